@@ -1,0 +1,366 @@
+"""Float64 CPU oracle for the sLSTM forward (channelwise mix='diag') and its Newton solve.
+
+TEST INFRASTRUCTURE. This module is the parity reference and the CPU baseline. Only the
+test suite, the smoke check in ``__graft_entry__`` and the ``cpu_baseline`` leg of the
+benchmark may import it; the product path (the HIP library and its binding) never does.
+It shares no code with the HIP path: nothing here is generated from, or feeds, the kernels.
+
+What it computes, and where each step is stated:
+
+* the cell f -- "xLSTM: Extended Long Short-Term Memory" (summary card), sLSTM step
+  pseudocode under "Key equations" (paper section 2.2, appendix A.2); the stabiliser,
+  stabilised gates and running-max recurrence from the educational reimplementation page
+  ("xLSTM -- a from-scratch, educational reimplementation"), section "Exponential gating +
+  the stabilizer (the crux)". Read-out h = o * c / n as in the paper's sLSTM step; the
+  floored read-out of the educational page is a declared deviation and is not used.
+* channelwise recurrence (mix='diag'): one recurrent weight per gate and feature, R of
+  shape (4, d_h), so each feature is an independent 4-state recurrence with a 4x4
+  Jacobian -- "sLSTM in this library", section "Cell" (mix table).
+* state layout (B, T, 4, d_h) with slots (c, n, m, h), hidden slot 3 -- same section.
+* gate order (z, i, f, o) in P, R and W_x -- order of the pre-activations in the paper's
+  sLSTM step pseudocode.
+* Newton ("Alg. 1"): residual F_t = s_t - f(s_{t-1}), linearise, solve the
+  block-bidiagonal system, update; K iterations; the initial state is prepended as s_0;
+  residual early stop and the divergence rule max|F| > 1 after K -- "Layout" page
+  (pararnn-torch structure), "Current surface (0.17)"; "sLSTM in this library", "API
+  notes".
+* the block-bidiagonal solve: Delta_1 = -F_1, Delta_t = A_t Delta_{t-1} - F_t, done here by
+  plain block forward substitution (a sequential loop), and on tiny inputs by a dense
+  LAPACK solve of the assembled system.
+* input projection P = W_x x + b ("W_x is a GEMM" -- "sLSTM in this library", "API
+  notes").
+
+Readings where the pages are silent (each listed in the design notes):
+
+* initial Newton iterate: the exact trajectory of the cell with the recurrent term
+  R * h_{t-1} removed from the pre-activations ("warm start"); a zero iterate is kept as
+  an option.
+* max tie-break: a >= i_tilde takes the forget branch; the Jacobian uses that branch.
+* early stop: stop before solving when max|F| < tol; ``iters`` counts applied updates.
+
+All arithmetic is float64.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+FORGET_EXP = "exp"
+FORGET_SIGMOID = "sigmoid"
+INIT_WARM = "warm"
+INIT_ZERO = "zero"
+
+# slot indices of the state (c, n, m, h) and gate indices of P and R (z, i, f, o)
+C, N, M, H = 0, 1, 2, 3
+GZ, GI, GF, GO = 0, 1, 2, 3
+
+
+# ---------------------------------------------------------------------------------------
+# scalar nonlinearities (float64, written to stay finite for any finite argument)
+# ---------------------------------------------------------------------------------------
+def _softplus(x):
+    return np.logaddexp(0.0, x)
+
+
+def sigmoid(x):
+    """sigma(x) = 1 / (1 + e^{-x}), computed as exp(-softplus(-x))."""
+    return np.exp(-_softplus(-x))
+
+
+def log_forget(f_tilde, forget):
+    """log f_t and its derivative d log f / d f_tilde.
+
+    Exponential forget gate: log f = f_tilde. Sigmoid forget gate: log f = log sigma(f_tilde)
+    = -softplus(-f_tilde), derivative sigma(-f_tilde). Both forms are allowed by the paper
+    (summary card, "Method" item 1; the educational page writes the stabiliser in terms of
+    log f so it covers both).
+    """
+    if forget == FORGET_EXP:
+        return f_tilde, np.ones_like(f_tilde)
+    if forget == FORGET_SIGMOID:
+        return -_softplus(-f_tilde), sigmoid(-f_tilde)
+    raise ValueError(f"unknown forget mode {forget!r}")
+
+
+# ---------------------------------------------------------------------------------------
+# the cell f and its 4x4 Jacobian
+# ---------------------------------------------------------------------------------------
+def cell(prev, p, r, forget, with_jacobian=False):
+    """One stabilised sLSTM step per feature (mix='diag').
+
+    prev : (..., 4, d) previous state (c', n', m', h')
+    p    : (..., 4, d) gate pre-activations from the input, gates (z, i, f, o)
+    r    : (4, d) channelwise recurrent weights
+    returns next state (..., 4, d) and, if asked, A = d next / d prev of shape (..., 4, 4, d)
+    with A[..., row, col, :] = d next[row] / d prev[col].
+
+    Equations (sLSTM step pseudocode, summary card; stabiliser from the educational page):
+      pre-activation  x~ = p_x + r_x h'                 for x in (z, i, f, o)
+      z = tanh z~,  o = sigma(o~),  l = log f(f~)
+      a = l + m',  m = max(a, i~)                         (stabiliser, running max)
+      i' = exp(i~ - m),  f' = exp(a - m)                  (both in (0, 1])
+      c = f' c' + i' z,  n = f' n' + i',  h = o c / n
+    """
+    c0, n0, m0, h0 = prev[..., C, :], prev[..., N, :], prev[..., M, :], prev[..., H, :]
+    zt = p[..., GZ, :] + r[GZ] * h0
+    it = p[..., GI, :] + r[GI] * h0
+    ft = p[..., GF, :] + r[GF] * h0
+    ot = p[..., GO, :] + r[GO] * h0
+    z = np.tanh(zt)
+    o = sigmoid(ot)
+    lf, dlf = log_forget(ft, forget)
+    a = lf + m0
+    beta = a >= it  # tie -> forget branch
+    m = np.where(beta, a, it)
+    ig = np.exp(it - m)
+    fg = np.exp(a - m)
+    c = fg * c0 + ig * z
+    n = fg * n0 + ig
+    h = o * c / n
+    nxt = np.stack([c, n, m, h], axis=-2)
+    if not with_jacobian:
+        return nxt
+
+    b = beta.astype(np.float64)
+    # derivatives of the stabiliser and of the two stabilised gates
+    dm_dm = b
+    dm_dh = b * dlf * r[GF] + (1.0 - b) * r[GI]
+    dig_dm = -b * ig
+    dig_dh = ig * (r[GI] - dm_dh)
+    dfg_dm = (1.0 - b) * fg
+    dfg_dh = fg * (dlf * r[GF] - dm_dh)
+    dz_dh = (1.0 - z * z) * r[GZ]
+    do_dh = o * (1.0 - o) * r[GO]
+
+    zero = np.zeros_like(c)
+    # rows c and n (c' and n' do not enter the gates)
+    dc = [fg, zero, c0 * dfg_dm + z * dig_dm, c0 * dfg_dh + z * dig_dh + ig * dz_dh]
+    dn = [zero, fg, n0 * dfg_dm + dig_dm, n0 * dfg_dh + dig_dh]
+    dmr = [zero, zero, dm_dm, dm_dh]
+    # row h = o c / n by the quotient rule, plus the output-gate term on h'
+    dh = [(o / n) * dc[k] - (o * c / (n * n)) * dn[k] for k in range(4)]
+    dh[H] = dh[H] + (c / n) * do_dh
+    A = np.stack([np.stack(row, axis=-2) for row in (dc, dn, dmr, dh)], axis=-3)
+    return nxt, A
+
+
+def gate_values(prev, p, r, forget):
+    """Stabilised gates (i', f') and the stabiliser m of one step, for invariant checks."""
+    h0, m0 = prev[..., H, :], prev[..., M, :]
+    it = p[..., GI, :] + r[GI] * h0
+    ft = p[..., GF, :] + r[GF] * h0
+    lf, _ = log_forget(ft, forget)
+    a = lf + m0
+    m = np.where(a >= it, a, it)
+    return np.exp(it - m), np.exp(a - m), m, a, it
+
+
+# ---------------------------------------------------------------------------------------
+# sequential forward and the unstabilised form
+# ---------------------------------------------------------------------------------------
+def _state0(state0, B, d):
+    if state0 is None:
+        return np.zeros((B, 4, d))
+    return np.asarray(state0, dtype=np.float64)
+
+
+def sequential(P, R, state0, forget):
+    """s_t = f(s_{t-1}) for t = 1..T from s_0 = state0 (zeros when None).
+
+    P (B, T, 4, d), R (4, d), state0 (B, 4, d) -> states (B, T, 4, d).
+    The step loop the 'sequential' solver runs ("sLSTM in this library", "API notes").
+    """
+    P = np.asarray(P, dtype=np.float64)
+    R = np.asarray(R, dtype=np.float64)
+    B, T, _, d = P.shape
+    s = _state0(state0, B, d)
+    out = np.empty((B, T, 4, d))
+    for t in range(T):
+        s = cell(s, P[:, t], R, forget)
+        out[:, t] = s
+    return out
+
+
+def unstabilised_hidden(P, R, forget):
+    """h from the unstabilised recurrence, zero initial state.
+
+    c_t = f_t c_{t-1} + i_t z_t, n_t = f_t n_{t-1} + i_t, h_t = o_t c_t / n_t with
+    i_t = exp(i~), f_t = exp(f~) or sigma(f~). The paper states that the stabilised and
+    unstabilised forms give identical outputs (summary card, "Method" item 1). Overflows
+    for long sequences; used only on short ones.
+    """
+    P = np.asarray(P, dtype=np.float64)
+    R = np.asarray(R, dtype=np.float64)
+    B, T, _, d = P.shape
+    c = np.zeros((B, d))
+    n = np.zeros((B, d))
+    h = np.zeros((B, d))
+    hs = np.empty((B, T, d))
+    cs = np.empty((B, T, d))
+    ns = np.empty((B, T, d))
+    for t in range(T):
+        pt = P[:, t]
+        z = np.tanh(pt[:, GZ] + R[GZ] * h)
+        i = np.exp(pt[:, GI] + R[GI] * h)
+        ft = pt[:, GF] + R[GF] * h
+        f = np.exp(ft) if forget == FORGET_EXP else sigmoid(ft)
+        o = sigmoid(pt[:, GO] + R[GO] * h)
+        c = f * c + i * z
+        n = f * n + i
+        h = o * c / n
+        hs[:, t], cs[:, t], ns[:, t] = h, c, n
+    return hs, cs, ns
+
+
+# ---------------------------------------------------------------------------------------
+# Newton
+# ---------------------------------------------------------------------------------------
+def warm_start(P, state0, forget):
+    """Initial Newton iterate: the exact trajectory with R * h_{t-1} dropped.
+
+    Reading (the pages give no initial guess): with the recurrent term removed every
+    pre-activation is known up front, so the trajectory is the sequential recurrence with
+    R = 0, started from state0's (c, n, m). The h slot is o c / n with o = sigma(p_o).
+    """
+    P = np.asarray(P, dtype=np.float64)
+    return sequential(P, np.zeros((4, P.shape[-1])), state0, forget)
+
+
+def _shifted(S, state0):
+    """Previous states s_{t-1} for t = 1..T, with state0 prepended as s_0."""
+    B, T, _, d = S.shape
+    prev = np.empty_like(S)
+    prev[:, 0] = _state0(state0, B, d)
+    prev[:, 1:] = S[:, :-1]
+    return prev
+
+
+def residual(S, P, R, state0, forget, with_jacobian=True):
+    """F_t = s_t - f(s_{t-1}) and A_t = df/ds' at s_{t-1}, for t = 1..T.
+
+    S, P (B, T, 4, d) -> F (B, T, 4, d), A (B, T, 4, 4, d)  (the scan_block4 layout)
+    """
+    prev = _shifted(S, state0)
+    if with_jacobian:
+        fs, A = cell(prev, P, R, forget, with_jacobian=True)
+        return S - fs, A
+    return S - cell(prev, P, R, forget), None
+
+
+def max_abs(F):
+    """max |F| over all entries; a non-finite entry counts as +inf."""
+    F = np.asarray(F)
+    if F.size == 0:
+        return 0.0
+    a = np.abs(F)
+    return float(np.max(np.where(np.isfinite(a), a, np.inf)))
+
+
+def forward_substitution(A, rhs):
+    """Solve the lower block-bidiagonal system by block forward substitution.
+
+    x_1 = rhs_1,  x_t = A_t x_{t-1} + rhs_t  (A_1 is not used: s_0 is fixed).
+    A (B, T, 4, 4, d), rhs (B, T, 4, d) -> x (B, T, 4, d).
+    """
+    B, T, _, d = rhs.shape
+    x = np.empty_like(rhs)
+    x[:, 0] = rhs[:, 0]
+    for t in range(1, T):
+        x[:, t] = np.einsum("bijd,bjd->bid", A[:, t], x[:, t - 1]) + rhs[:, t]
+    return x
+
+
+def dense_solve_lane(A_lane, F_lane):
+    """Dense LAPACK solve of one lane's Newton system (tiny inputs only).
+
+    A_lane (T, 4, 4), F_lane (T, 4). Assembles the 4T x 4T matrix with identity blocks on
+    the diagonal and -A_t below it, and solves  J Delta = -F.
+    """
+    T = F_lane.shape[0]
+    J = np.eye(4 * T)
+    for t in range(1, T):
+        J[4 * t:4 * t + 4, 4 * (t - 1):4 * t] = -A_lane[t]
+    return np.linalg.solve(J, -F_lane.reshape(-1)).reshape(T, 4)
+
+
+@dataclass
+class NewtonStats:
+    iters: int = 0
+    converged: bool = False
+    diverged: bool = False
+    nonfinite: bool = False
+    max_abs_F: list = field(default_factory=list)  # entry k: max|F| after k updates
+
+
+def newton_flags(e_final, tol):
+    """Divergence when max|F| > 1 (or non-finite) after the last iterate; convergence
+    when an early-stop tolerance is set and met ("Layout", "Current surface (0.17)")."""
+    nonfinite = not np.isfinite(e_final)
+    diverged = nonfinite or e_final > 1.0
+    converged = (tol > 0) and (not nonfinite) and e_final < tol
+    return converged, diverged, nonfinite
+
+
+def newton(P, R, state0, forget, max_iters, tol=0.0, init=INIT_WARM, return_history=False):
+    """Newton solve of the sLSTM recurrence over all T steps at once.
+
+    For k = 0 .. max_iters-1: F, A at the current iterate; e_k = max|F|; stop before the
+    solve when tol > 0 and e_k < tol; Delta from the block-bidiagonal system; S += Delta.
+    Finally e = max|F| at the last iterate and the flags.
+    Returns (S, NewtonStats) and, with return_history, the list of iterates S^0..S^iters.
+    """
+    P = np.asarray(P, dtype=np.float64)
+    R = np.asarray(R, dtype=np.float64)
+    B, T, _, d = P.shape
+    if init == INIT_WARM:
+        S = warm_start(P, state0, forget)
+    elif init == INIT_ZERO:
+        S = np.zeros((B, T, 4, d))
+    else:
+        raise ValueError(f"unknown init {init!r}")
+    stats = NewtonStats()
+    hist = [S.copy()] if return_history else None
+    with np.errstate(all="ignore"):
+        stopped = False
+        for _ in range(max_iters):
+            F, A = residual(S, P, R, state0, forget)
+            e = max_abs(F)
+            stats.max_abs_F.append(e)
+            if tol > 0 and e < tol:
+                stopped = True
+                break
+            S = S + forward_substitution(A, -F)
+            stats.iters += 1
+            if return_history:
+                hist.append(S.copy())
+        if not stopped:
+            F, _ = residual(S, P, R, state0, forget, with_jacobian=False)
+            stats.max_abs_F.append(max_abs(F))
+    e_final = stats.max_abs_F[-1]
+    stats.converged, stats.diverged, stats.nonfinite = newton_flags(e_final, tol)
+    if return_history:
+        return S, stats, hist
+    return S, stats
+
+
+# ---------------------------------------------------------------------------------------
+# input projection
+# ---------------------------------------------------------------------------------------
+def input_projection(x, W, bias):
+    """P[b, t, g, j] = sum_k x[b, t, k] W[g, j, k] + bias[g, j]   (gates g = z, i, f, o).
+
+    x (B, T, d_in), W (4, d_h, d_in), bias (4, d_h) -> P (B, T, 4, d_h), float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    bias = np.asarray(bias, dtype=np.float64)
+    B, T, d_in = x.shape
+    g, d_h, _ = W.shape
+    P = x.reshape(B * T, d_in) @ W.reshape(g * d_h, d_in).T
+    return P.reshape(B, T, g, d_h) + bias
+
+
+def hidden(S):
+    """The hidden slot (B, T, d_h) of a state tensor (hidden slot 3)."""
+    return np.asarray(S)[..., H, :]

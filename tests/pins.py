@@ -1,0 +1,358 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix.
+
+Each pin takes the oracle module as an argument so that the mutation test can run the same
+pins against copies of the oracle with planted mistakes. A pin returns nothing and raises
+AssertionError when the oracle disagrees.
+"""
+from __future__ import annotations
+
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------------------------------
+# golden worked examples
+# ---------------------------------------------------------------------------------------
+def _value(expr: str) -> float:
+    """Evaluate a golden-file entry: rationals, ln(), atanh() and + - * /."""
+    ns = {"ln": lambda v: math.log(float(v)), "atanh": lambda v: math.atanh(float(v)),
+          "__builtins__": {}}
+    expr = expr.strip()
+    try:
+        return float(Fraction(expr))
+    except ValueError:
+        pass
+    # rationals inside function calls are evaluated as floats
+    return float(eval(expr, ns, {}))  # noqa: S307 -- our own fixture files
+
+
+def load_golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        g = json.load(f)
+    conv = lambda a: np.vectorize(_value, otypes=[float])(np.array(a, dtype=object))  # noqa: E731
+    P = conv(g["P"])[None]           # (1, T, 4, 1)
+    R = conv(g["R"])                 # (4, 1)
+    S = conv(g["expected_states"])[None]
+    gates = conv(g["expected_gates_i_f"])
+    return g, P, R, S, gates
+
+
+GOLDEN_FILES = ["slstm_exp_forget_r0.json", "slstm_sigmoid_forget_r0.json",
+                "slstm_exp_forget_recurrent.json"]
+
+
+def pin_golden_sequential(ref):
+    for name in GOLDEN_FILES:
+        g, P, R, S, _ = load_golden(name)
+        got = ref.sequential(P, R, None, g["forget"])
+        np.testing.assert_allclose(got, S, rtol=1e-13, atol=1e-14, err_msg=name)
+
+
+def pin_golden_gates(ref):
+    for name in GOLDEN_FILES:
+        g, P, R, S, gates = load_golden(name)
+        prev = np.concatenate([np.zeros((1, 1, 4, 1)), S[:, :-1]], axis=1)
+        ig, fg, m, _, _ = ref.gate_values(prev, P, R, g["forget"])
+        np.testing.assert_allclose(ig[0, :, 0], gates[:, 0], rtol=1e-13, err_msg=name)
+        np.testing.assert_allclose(fg[0, :, 0], gates[:, 1], rtol=1e-13, err_msg=name)
+        np.testing.assert_allclose(m[0, :, 0], S[0, :, 2, 0], rtol=1e-13, atol=1e-15, err_msg=name)
+
+
+# ---------------------------------------------------------------------------------------
+# small seeded problems (drawn here so the pins do not depend on the workload module)
+# ---------------------------------------------------------------------------------------
+def small_problem(seed, B=2, T=64, d=16, forget="exp", forget_bias=3.0, r_scale=0.5):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = rng.standard_normal((B, T, d))
+    W = rng.standard_normal((4, d, d)) / np.sqrt(d)
+    R = rng.uniform(-r_scale, r_scale, size=(4, d))
+    P = np.einsum("btk,gjk->btgj", x, W)
+    P[:, :, 2, :] += forget_bias
+    return P, R
+
+
+def pin_unstabilised_equivalence(ref):
+    """Stabilised and unstabilised forms give the same h (summary card, 'Method' item 1)."""
+    for forget, seed in (("exp", 1), ("sigmoid", 2)):
+        P, R = small_problem(seed, forget=forget)
+        h_stab = ref.hidden(ref.sequential(P, R, None, forget))
+        h_raw, c_raw, n_raw = ref.unstabilised_hidden(P, R, forget)
+        assert np.all(np.isfinite(h_raw))
+        np.testing.assert_allclose(h_stab, h_raw, rtol=1e-11, atol=1e-13, err_msg=forget)
+        # the stabilised c, n are the unstabilised ones scaled by exp(-m)
+        S = ref.sequential(P, R, None, forget)
+        np.testing.assert_allclose(S[..., 0, :], c_raw * np.exp(-S[..., 2, :]), rtol=1e-10,
+                                   atol=1e-300, err_msg=forget)
+        np.testing.assert_allclose(S[..., 1, :], n_raw * np.exp(-S[..., 2, :]), rtol=1e-10,
+                                   err_msg=forget)
+
+
+def pin_stabiliser_invariants(ref):
+    """Along a sequential trajectory: i', f' in (0, 1], max(i', f') = 1 exactly, n > 0,
+    |c| <= n, |h| < 1 (educational page, stabiliser section; the exponent arguments stay
+    at or below zero)."""
+    for forget, seed, fb in (("exp", 3, 3.0), ("sigmoid", 4, 3.0), ("exp", 5, -2.0)):
+        P, R = small_problem(seed, T=96, forget=forget, forget_bias=fb)
+        P[:, ::7, 1, :] *= 8.0  # input-gate spikes so both branches are taken
+        S = ref.sequential(P, R, None, forget)
+        prev = np.concatenate([np.zeros_like(S[:, :1]), S[:, :-1]], axis=1)
+        ig, fg, m, a, it = ref.gate_values(prev, P, R, forget)
+        assert np.all(ig > 0) and np.all(ig <= 1) and np.all(fg > 0) and np.all(fg <= 1)
+        assert np.all(np.maximum(ig, fg) == 1.0)
+        np.testing.assert_array_equal(m, np.maximum(a, it))
+        assert np.any(it > a) and np.any(a > it), "both branches should be exercised"
+        c, n, h = S[..., 0, :], S[..., 1, :], S[..., 3, :]
+        assert np.all(n > 0) and np.all(np.abs(c) <= n * (1 + 1e-15)) and np.all(np.abs(h) < 1)
+
+
+def pin_zero_state_closed_forms(ref):
+    """With z constant over time and zero initial state, c_t = z n_t for all t, so
+    h_t = o_t z whatever the gates do."""
+    P, R = small_problem(6, T=40)
+    R[0] = 0.0  # r_z = 0 keeps z constant
+    P[:, :, 0, :] = P[:, :1, 0, :]
+    S = ref.sequential(P, R, None, "exp")
+    z = np.tanh(P[:, 0, 0, :])
+    hprev = np.concatenate([np.zeros_like(S[:, :1, 3]), S[:, :-1, 3]], axis=1)
+    o = 1.0 / (1.0 + np.exp(-(P[:, :, 3, :] + R[3] * hprev)))
+    np.testing.assert_allclose(S[..., 3, :], o * z[:, None, :], rtol=1e-12, atol=1e-15)
+
+
+def pin_maxplus_closed_form(ref):
+    """The stabiliser of the R-free trajectory solves m_t = max(l_t + m_{t-1}, i~_t), whose
+    closed form is max(m_0 + sum_{u<=t} l_u, max_s (i~_s + sum_{s<u<=t} l_u))."""
+    for forget, seed in (("exp", 7), ("sigmoid", 8)):
+        P, R = small_problem(seed, T=50, forget=forget, forget_bias=0.5)
+        state0 = np.zeros((2, 4, 16))
+        state0[:, 2, :] = np.linspace(-3, 3, 16)
+        S0 = ref.warm_start(P, state0, forget)
+        lf, _ = ref.log_forget(P[:, :, 2, :], forget)
+        it = P[:, :, 1, :]
+        T = P.shape[1]
+        for t in range(T):
+            cand = [state0[:, 2, :] + lf[:, :t + 1].sum(axis=1)]
+            for s in range(t + 1):
+                cand.append(it[:, s] + lf[:, s + 1:t + 1].sum(axis=1))
+            np.testing.assert_allclose(S0[:, t, 2, :], np.max(cand, axis=0), rtol=1e-12,
+                                       atol=1e-12)
+
+
+def pin_warm_start_is_solution_when_r_zero(ref):
+    """With R = 0 the warm start is the sequential solution: F^0 = 0 up to rounding."""
+    P, R = small_problem(9)
+    R0 = np.zeros_like(R)
+    S0 = ref.warm_start(P, None, "exp")
+    np.testing.assert_allclose(S0, ref.sequential(P, R0, None, "exp"), rtol=0, atol=0)
+    F, _ = ref.residual(S0, P, R0, None, "exp", with_jacobian=False)
+    assert ref.max_abs(F) == 0.0
+
+
+def pin_jacobian_finite_differences(ref):
+    """Analytic 4x4 Jacobian against central differences, away from branch ties."""
+    for forget, seed in (("exp", 10), ("sigmoid", 11)):
+        rng = np.random.Generator(np.random.PCG64(seed))
+        d = 64
+        prev = np.stack([rng.uniform(-2, 2, d), np.exp(rng.uniform(-1, 2, d)),
+                         rng.uniform(-3, 3, d), rng.uniform(-0.9, 0.9, d)])[None]
+        prev[0, 0] = np.clip(prev[0, 0], -prev[0, 1], prev[0, 1])
+        p = rng.standard_normal((1, 4, d)) * 2.0
+        r = rng.uniform(-0.5, 0.5, (4, d))
+        _, A = ref.cell(prev, p, r, forget, with_jacobian=True)
+        _, _, _, a, it = ref.gate_values(prev, p, r, forget)
+        ok = np.abs(a - it)[0] > 1e-3
+        assert ok.sum() > d // 2
+        eps = 1e-6
+        for col in range(4):
+            e = np.zeros_like(prev)
+            e[0, col] = eps
+            num = (ref.cell(prev + e, p, r, forget) - ref.cell(prev - e, p, r, forget)) / (2 * eps)
+            np.testing.assert_allclose(A[0, :, col][:, ok], num[0][:, ok], rtol=1e-6, atol=1e-8,
+                                       err_msg=f"{forget} column {col}")
+        # structural zeros of the channelwise cell
+        for row, col in ((0, 1), (1, 0), (2, 0), (2, 1)):
+            assert np.all(A[0, row, col] == 0)
+
+
+def pin_jacobian_at_ties(ref):
+    """At an exact tie a = i~ the forget branch is taken, and the Jacobian is that branch's
+    one-sided derivative: the forward difference in m' (which moves a above i~)."""
+    for forget in ("exp", "sigmoid"):
+        rng = np.random.Generator(np.random.PCG64(21))
+        d = 16
+        prev = np.stack([rng.uniform(-1, 1, d), np.exp(rng.uniform(0, 1, d)),
+                         rng.uniform(-3, 3, d), rng.uniform(-0.9, 0.9, d)])[None]
+        r = rng.uniform(-0.5, 0.5, (4, d))
+        r[1] = 0.0  # i~ = p_i exactly
+        p = rng.standard_normal((1, 4, d))
+        lf, _ = ref.log_forget(p[:, 2] + r[2] * prev[:, 3], forget)
+        p[:, 1] = lf + prev[:, 2]  # a == i~ bit for bit
+        _, A = ref.cell(prev, p, r, forget, with_jacobian=True)
+        eps = 1e-7
+        e = np.zeros_like(prev)
+        e[0, 2] = eps
+        fwd = (ref.cell(prev + e, p, r, forget) - ref.cell(prev, p, r, forget)) / eps
+        np.testing.assert_allclose(A[0, :, 2], fwd[0], rtol=1e-5, atol=1e-6, err_msg=forget)
+        np.testing.assert_array_equal(A[0, 2, 2], 1.0)
+
+
+def pin_forward_substitution_closed_form(ref):
+    """x_t = a x_{t-1} + 1 with scalar-times-identity A_t: x_t = (1 - a^t) / (1 - a)."""
+    T, d = 30, 3
+    a = np.array([0.5, -0.8, 0.9])
+    A = np.zeros((1, T, 4, 4, d))
+    for i in range(4):
+        A[0, :, i, i, :] = a
+    rhs = np.ones((1, T, 4, d))
+    x = ref.forward_substitution(A, rhs)
+    t = np.arange(1, T + 1)[:, None]
+    expect = (1 - a[None, :] ** t) / (1 - a[None, :])
+    for i in range(4):
+        np.testing.assert_allclose(x[0, :, i, :], expect, rtol=1e-13)
+
+
+def pin_forward_substitution_vs_dense_lu(ref):
+    """Block forward substitution against a dense LAPACK solve of the assembled system,
+    at Jacobians of a real iterate (tiny workload shape)."""
+    P, R = small_problem(12)
+    S = ref.warm_start(P, None, "exp")
+    F, A = ref.residual(S, P, R, None, "exp")
+    D = ref.forward_substitution(A, -F)
+    for b in range(2):
+        for j in (0, 5, 15):
+            dense = ref.dense_solve_lane(A[b, :, :, :, j], F[b, :, :, j])
+            np.testing.assert_allclose(D[b, :, :, j], dense, rtol=1e-10, atol=1e-12)
+
+
+def pin_scan_bracketing(ref):
+    """The affine maps compose associatively: a tree-ordered reduction of (A_t, r_t) gives
+    the same final x_T as forward substitution."""
+    rng = np.random.Generator(np.random.PCG64(13))
+    T, d = 37, 5
+    A = rng.uniform(-0.5, 0.5, (1, T, 4, 4, d))
+    r = rng.standard_normal((1, T, 4, d))
+    x = ref.forward_substitution(A, r)
+
+    def compose(first, second):  # apply first, then second
+        A1, b1 = first
+        A2, b2 = second
+        return np.einsum("ijd,jkd->ikd", A2, A1), np.einsum("ijd,jd->id", A2, b1) + b2
+
+    maps = [(np.zeros((4, 4, d)), r[0, 0])] + [(A[0, t], r[0, t]) for t in range(1, T)]
+    while len(maps) > 1:  # pairwise tree reduction
+        nxt = [compose(maps[i], maps[i + 1]) for i in range(0, len(maps) - 1, 2)]
+        if len(maps) % 2:
+            nxt.append(maps[-1])
+        maps = nxt
+    np.testing.assert_allclose(maps[0][1], x[0, -1], rtol=1e-12, atol=1e-12)
+
+
+def pin_newton_prefix_exactness(ref):
+    """From the zero iterate, k Newton updates make the first k steps exact (s_0 is fixed
+    and a step is exact once its predecessor is)."""
+    P, R = small_problem(14, T=24, d=8)
+    seq = ref.sequential(P, R, None, "exp")
+    for k in (1, 2, 3, 5):
+        S, st = ref.newton(P, R, None, "exp", k, init="zero")
+        assert st.iters == k
+        np.testing.assert_allclose(S[:, :k], seq[:, :k], rtol=1e-9, atol=1e-12, err_msg=f"k={k}")
+
+
+def pin_newton_k_equals_t(ref):
+    """K = T Newton iterations reproduce the sequential recurrence (same forward either
+    way: 'sLSTM in this library', 'API notes', solver modes)."""
+    P, R = small_problem(15, T=16, d=8)
+    S, st = ref.newton(P, R, None, "exp", 16, init="zero")
+    seq = ref.sequential(P, R, None, "exp")
+    np.testing.assert_allclose(S, seq, rtol=1e-9, atol=1e-12)
+    S, st = ref.newton(P, R, None, "exp", 16, init="warm")
+    np.testing.assert_allclose(S, seq, rtol=1e-12, atol=1e-13)
+
+
+def pin_newton_quadratic(ref):
+    """Near the solution max|F| roughly squares per iteration, and the warm-started solve
+    converges to the sequential trajectory."""
+    P, R = small_problem(16, B=2, T=256, d=16)
+    S, st = ref.newton(P, R, None, "exp", 4)
+    e = st.max_abs_F
+    floor = 16 * np.finfo(np.float64).eps * np.max(np.abs(S))  # rounding floor of |F|
+    assert len(e) == 5 and e[0] < 1.0
+    for k in range(3):
+        assert e[k + 1] < 10 * e[k] ** 2 + floor, e
+    assert e[2] > floor and e[-1] <= floor
+    np.testing.assert_allclose(S, ref.sequential(P, R, None, "exp"), rtol=1e-10, atol=1e-12)
+
+
+def pin_early_stop_and_flags(ref):
+    """Early stop before the solve once max|F| < tol; divergence when max|F| > 1 or
+    non-finite after the last iterate ('Layout', 'Current surface (0.17)')."""
+    P, R = small_problem(17, T=128, forget="sigmoid")
+    S, st = ref.newton(P, R, None, "sigmoid", 8, tol=1e-5)
+    assert st.converged and not st.diverged
+    assert st.max_abs_F[st.iters] < 1e-5 and all(e >= 1e-5 for e in st.max_abs_F[:st.iters])
+    assert len(st.max_abs_F) == st.iters + 1
+    # the divergence rule itself: max|F| > 1 after the last iterate, or non-finite
+    for e, tol, want in ((0.5, 0.0, (False, False, False)), (1.0, 0.0, (False, False, False)),
+                         (1.5, 0.0, (False, True, False)), (3e-6, 1e-5, (True, False, False)),
+                         (2e-5, 1e-5, (False, False, False)), (np.inf, 0.0, (False, True, True)),
+                         (np.nan, 1e-5, (False, True, True))):
+        assert tuple(ref.newton_flags(e, tol)) == want, (e, tol)
+    # a NaN in the inputs gives a non-finite residual and the divergence flag
+    Pn = P.copy()
+    Pn[0, 5, 1, 3] = np.nan
+    _, st = ref.newton(Pn, R, None, "sigmoid", 3)
+    assert st.diverged and st.nonfinite
+    # the zero iterate overflows on a long exponential-forget sequence
+    P2, R2 = small_problem(18, B=2, T=1024, d=32)
+    _, st = ref.newton(P2, R2, None, "exp", 3, init="zero")
+    assert st.diverged
+
+
+def pin_input_projection(ref):
+    """P = W_x x + b: one-hot weight rows pick single input features into the right gate
+    and feature slots; small sizes against an explicit triple loop."""
+    B, T, d_in, d_h = 2, 3, 5, 4
+    rng = np.random.Generator(np.random.PCG64(19))
+    x = rng.standard_normal((B, T, d_in))
+    W = np.zeros((4, d_h, d_in))
+    picks = {}
+    for g in range(4):
+        for j in range(d_h):
+            k = (3 * g + j) % d_in
+            W[g, j, k] = g + 1.0
+            picks[g, j] = k
+    bias = rng.standard_normal((4, d_h))
+    P = ref.input_projection(x, W, bias)
+    assert P.shape == (B, T, 4, d_h)
+    for (g, j), k in picks.items():
+        np.testing.assert_allclose(P[:, :, g, j], (g + 1.0) * x[:, :, k] + bias[g, j], rtol=1e-15)
+    W = rng.standard_normal((4, d_h, d_in))
+    P = ref.input_projection(x, W, bias)
+    for b in range(B):
+        for t in range(T):
+            for g in range(4):
+                for j in range(d_h):
+                    acc = bias[g, j]
+                    for k in range(d_in):
+                        acc += x[b, t, k] * W[g, j, k]
+                    assert abs(P[b, t, g, j] - acc) < 1e-12
+
+
+def pin_state0_chunking(ref):
+    """The final state carries a sequence: forward(T) = forward(T/2) then forward(T/2)
+    from the carried state ('fused kernels prepend h0', 'Layout' page)."""
+    P, R = small_problem(20, T=64)
+    full = ref.sequential(P, R, None, "exp")
+    first = ref.sequential(P[:, :32], R, None, "exp")
+    second = ref.sequential(P[:, 32:], R, first[:, -1], "exp")
+    np.testing.assert_allclose(np.concatenate([first, second], axis=1), full, rtol=0, atol=0)
+    S, st = ref.newton(P[:, 32:], R, first[:, -1], "exp", 6)
+    np.testing.assert_allclose(S, full[:, 32:], rtol=1e-11, atol=1e-13)
+
+
+ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

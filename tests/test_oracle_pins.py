@@ -1,0 +1,67 @@
+"""The float64 oracle against golden worked examples, closed forms, invariants, textbook
+routines and brute force (CPU only). Also checks that planted mistakes in a copy of the
+oracle are caught by at least one pin."""
+import importlib.util
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import pins
+from oracle import slstm_ref
+
+ORACLE_SRC = os.path.join(os.path.dirname(slstm_ref.__file__), "slstm_ref.py")
+
+
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    pin(slstm_ref)
+
+
+# Each mutation: (label, original text, replacement). A mutation that no pin notices would
+# mean the pins leave that part of the oracle unchecked.
+MUTATIONS = [
+    ("gate order i<->f", "it = p[..., GI, :] + r[GI] * h0\n    ft = p[..., GF, :] + r[GF] * h0\n    ot",
+     "it = p[..., GF, :] + r[GF] * h0\n    ft = p[..., GI, :] + r[GI] * h0\n    ot"),
+    ("dropped input term in c", "c = fg * c0 + ig * z\n", "c = fg * c0\n"),
+    ("wrong sign in stabiliser gate", "ig = np.exp(it - m)\n    fg = np.exp(a - m)\n    c =",
+     "ig = np.exp(m - it)\n    fg = np.exp(a - m)\n    c ="),
+    ("tie to input branch", "beta = a >= it  # tie", "beta = a > it  # tie"),
+    ("read-out floor variant", "h = o * c / n\n    nxt", "h = o * c / np.maximum(np.abs(n), 1.0)\n    nxt"),
+    ("quotient rule sign", "- (o * c / (n * n)) * dn[k]", "+ (o * c / (n * n)) * dn[k]"),
+    ("missing output-gate term", "dh[H] = dh[H] + (c / n) * do_dh", "dh[H] = dh[H]"),
+    ("sigmoid-forget derivative", "return -_softplus(-f_tilde), sigmoid(-f_tilde)",
+     "return -_softplus(-f_tilde), sigmoid(f_tilde)"),
+    ("transposed Jacobian in the solve", 'np.einsum("bijd,bjd->bid", A[:, t], x[:, t - 1])',
+     'np.einsum("bjid,bjd->bid", A[:, t], x[:, t - 1])'),
+    ("off-by-one state shift", "prev[:, 1:] = S[:, :-1]", "prev[:, 1:] = S[:, 1:]"),
+    ("transposed weight", "P = x.reshape(B * T, d_in) @ W.reshape(g * d_h, d_in).T",
+     "P = x.reshape(B * T, d_in) @ W.transpose(0, 2, 1).reshape(g * d_h, d_in).T"),
+    ("early stop after the solve", "if tol > 0 and e < tol:\n                stopped = True",
+     "if tol > 0 and e < tol * 1e-30:\n                stopped = True"),
+    ("divergence threshold", "diverged = nonfinite or e_final > 1.0", "diverged = nonfinite or e_final > 10.0"),
+]
+
+
+def _mutant(label, old, new):
+    src = open(ORACLE_SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {label!r} not found exactly once"
+    spec = importlib.util.spec_from_loader(f"mutant_{abs(hash(label))}", loader=None)
+    mod = importlib.util.module_from_spec(spec)
+    sys.modules[spec.name] = mod
+    exec(compile(src.replace(old, new), f"<mutant {label}>", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("label,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(label, old, new):
+    mod = _mutant(label, old, new)
+    caught = []
+    with np.errstate(all="ignore"):
+        for pin in pins.ALL_PINS:
+            try:
+                pin(mod)
+            except (AssertionError, FloatingPointError, ValueError, IndexError):
+                caught.append(pin.__name__)
+    assert caught, f"no pin notices the planted mistake {label!r}"
