@@ -1,0 +1,201 @@
+/*
+ * slstm.h -- C ABI of the MI355X (gfx950) sLSTM forward library: channelwise recurrence
+ * (mix='diag'), state (c, n, m, h) per feature, solved in parallel over time by Newton's
+ * method with a 4x4 affine scan, or step by step.
+ *
+ * Sources (the pages the method is described on):
+ *  [SL]  pararnn-torch docs, "sLSTM in this library": sections "Cell" (state layout
+ *        (B, T, 4, d_h) = (c, n, m, h), hidden slot 3; mix='diag' = channelwise R of shape
+ *        (4, d_h), a 4x4 Jacobian per feature), "API notes" (Newton / sequential solver
+ *        modes, T = 1 decode step, W_x applied as a GEMM), "Outputs".
+ *  [LY]  pararnn-torch docs, "Layout": "Current surface (0.17)" (fused kernels prepend h0;
+ *        NewtonStats; residual early stop; divergence error when max|F| > 1 after K),
+ *        "Naming" (scan_block4 for the (B, T, 4, 4, d) layout).
+ *  [XL]  "xLSTM: Extended Long Short-Term Memory" summary card, "Key equations": the sLSTM
+ *        step pseudocode (paper section 2.2, appendix A.2), gate order (z, i, f, o).
+ *  [ED]  "xLSTM -- a from-scratch, educational reimplementation", section "Exponential gating
+ *        + the stabilizer (the crux)": stabiliser m_t and the stabilised gates.
+ *
+ * Conventions shared by every entry point:
+ *  - All tensors are dense, row-major, in device memory owned by the caller. The library never
+ *    allocates, frees or keeps a pointer after a call returns (workspaces are caller memory).
+ *  - Layouts (feature index innermost):
+ *      P        (B, T, 4, d_h)      gate pre-activations, gates (z, i, f, o); float32 or bf16
+ *      R        (4, d_h)  float32   channelwise recurrent weights, same gate order
+ *      state0   (B, 4, d_h) float32 initial state, slots (c, n, m, h); NULL means all zeros
+ *      states   (B, T, 4, d_h) float32, slots (c, n, m, h); states[:, T-1] is the final state
+ *      h_out    (B, T, d_h) float32, the hidden slot; optional (NULL skips it)
+ *      A        (B, T, 4, 4, d_h) float32, A[b,t,row,col,j] = d s_t[row] / d s_{t-1}[col]
+ *  - Every call enqueues work on `stream` (a hipStream_t; NULL is the default stream) and
+ *    returns without waiting, unless stated otherwise.
+ *  - Status: negative values mean invalid input or a HIP failure and that no output is valid;
+ *    slstm_last_error() then describes the problem (per thread). Positive values report a
+ *    solver outcome with outputs written.
+ *  - Alignment: states, h_out, A, rhs/x and workspaces 16-byte aligned; P 4-byte (float32) or
+ *    2-byte (bf16); x and W_x of the input projection 16-byte aligned.
+ */
+#ifndef SLSTM_H
+#define SLSTM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SLSTM_OK = 0,
+  SLSTM_DIVERGED = 1,   /* Newton: finite max|F| > 1 after the last iterate ([LY]) */
+  SLSTM_NONFINITE = 2,  /* Newton: residual of the last iterate is NaN or infinite */
+  SLSTM_EINVAL = -1,    /* invalid argument */
+  SLSTM_EWORKSPACE = -2,/* workspace smaller than required */
+  SLSTM_EHIP = -3       /* a HIP runtime call or kernel launch failed */
+} slstm_status;
+
+typedef enum { SLSTM_F32 = 0, SLSTM_BF16 = 1 } slstm_dtype;
+
+/* forget gate: log f = f~ (exponential) or log sigma(f~) (sigmoid) ([XL] "Method"; [ED]) */
+typedef enum { SLSTM_FORGET_EXP = 0, SLSTM_FORGET_SIGMOID = 1 } slstm_forget;
+
+/* initial Newton iterate: the trajectory with the recurrent term R h_{t-1} dropped, or zeros */
+typedef enum { SLSTM_INIT_WARM = 0, SLSTM_INIT_ZERO = 1 } slstm_init;
+
+#define SLSTM_MAX_ITERS 64
+
+/* Newton bookkeeping ([LY] NewtonStats). max_abs_F[k] = max |F| over all (b, t, slot, j) at
+ * the iterate after k updates, k = 0 .. iters; entries past `iters` are 0. A non-finite
+ * residual is recorded as +inf. */
+typedef struct {
+  int32_t iters;      /* updates applied */
+  int32_t converged;  /* tol > 0 and max_abs_F[iters] < tol */
+  int32_t diverged;   /* max_abs_F[iters] > 1 or not finite */
+  int32_t nonfinite;  /* max_abs_F[iters] not finite */
+  float max_abs_F[SLSTM_MAX_ITERS + 1];
+} slstm_newton_stats;
+
+const char* slstm_status_string(slstm_status s);
+/* Detail of the last negative status returned on the calling thread ("" if none). */
+const char* slstm_last_error(void);
+
+/* Bytes of device workspace slstm_newton_forward needs for these sizes (0 if invalid). */
+size_t slstm_newton_workspace_bytes(int B, int T, int d_h);
+
+/*
+ * Newton-parallel forward ([SL] "API notes": solver='newton'; [LY] "Current surface"): the
+ * whole sequence s_1..s_T of the recurrence s_t = f(s_{t-1}, P_t) with s_0 = state0, where f
+ * is the stabilised sLSTM step of [XL]/[ED] with channelwise R:
+ *   x~ = p_x + r_x h'; z = tanh z~; o = sigma(o~); l = f~ or log sigma(f~);
+ *   a = l + m'; m = max(a, i~) (a tie takes a); i' = e^{i~ - m}; f' = e^{a - m};
+ *   c = f' c' + i' z; n = f' n' + i'; h = o c / n.
+ * Each iteration k evaluates F_t = s_t - f(s_{t-1}) and A_t = df/ds' at every step; if
+ * tol > 0 and max|F| < tol it stops before solving; otherwise it solves
+ *   Delta_1 = -F_1, Delta_t = A_t Delta_{t-1} - F_t     (block-bidiagonal system)
+ * by a 4x4 affine scan and sets s <- s + Delta. After max_iters updates (or the stop) the
+ * residual of the final iterate gives the flags.
+ *
+ *  P, P_dtype   gate pre-activations (B, T, 4, d_h), float32 or bf16
+ *  R            (4, d_h); state0 (B, 4, d_h) or NULL
+ *  states       output (B, T, 4, d_h); also the Newton iterate while solving
+ *  h_out        optional output (B, T, d_h)
+ *  fmode        forget-gate form; max_iters in 1..64; tol >= 0 (0: fixed iteration count)
+ *  init         SLSTM_INIT_WARM (default reading) or SLSTM_INIT_ZERO
+ *  workspace    >= slstm_newton_workspace_bytes(B, T, d_h) bytes of device memory; holds the
+ *               Jacobians, the right-hand sides / Newton steps and the solver control block
+ *               (later readable with slstm_newton_read_stats)
+ *  stats        NULL: fully asynchronous, returns SLSTM_OK once everything is enqueued.
+ *               non-NULL: waits for the stream, fills *stats and returns SLSTM_DIVERGED or
+ *               SLSTM_NONFINITE when the flags say so (outputs are still written).
+ */
+slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const float* R,
+                                  const float* state0, float* states, float* h_out, int B, int T,
+                                  int d_h, slstm_forget fmode, int max_iters, float tol,
+                                  slstm_init init, void* workspace, size_t workspace_bytes,
+                                  void* stream, slstm_newton_stats* stats);
+
+/* Waits for `stream` and copies the stats of the last slstm_newton_forward that used this
+ * workspace into *stats; returns the status that call would have returned with stats. */
+slstm_status slstm_newton_read_stats(const void* workspace, size_t workspace_bytes, void* stream,
+                                     slstm_newton_stats* stats);
+
+/*
+ * Sequential forward ([SL] "API notes": solver='sequential'; at T = 1 the decode step):
+ * s_t = f(s_{t-1}, P_t) for t = 1..T, one thread per lane (b, j). Same arguments and layouts
+ * as slstm_newton_forward; needs no workspace.
+ */
+slstm_status slstm_sequential_forward(const void* P, slstm_dtype P_dtype, const float* R,
+                                      const float* state0, float* states, float* h_out, int B,
+                                      int T, int d_h, slstm_forget fmode, void* stream);
+
+/*
+ * Input projection on the MFMA matrix cores ([SL] "API notes": W_x is a GEMM; [XL]
+ * pre-activations W x + b):  P[b,t,g,j] = sum_k x[b,t,k] W_x[g,j,k] + bias[g,j].
+ *  x (B, T, d_in) and W_x (4, d_h, d_in) in bf16 (xw_dtype must be SLSTM_BF16), bias (4, d_h)
+ *  float32 (NULL: no bias), P (B, T, 4, d_h) float32 output. d_in must be a multiple of 8.
+ *  Accumulates in float32.
+ */
+slstm_status slstm_input_projection(const void* x, const void* W_x, const float* bias, float* P,
+                                    int B, int T, int d_in, int d_h, slstm_dtype xw_dtype,
+                                    void* stream);
+
+/*
+ * One residual + Jacobian evaluation (the first half of a Newton iteration, [LY]):
+ *   rhs_t = f(s_{t-1}, P_t) - s_t = -F_t and A_t = df/ds' at s_{t-1}, for t = 1..T, s_0 = state0.
+ *  states (B, T, 4, d_h) is the iterate; A (B, T, 4, 4, d_h) and rhs (B, T, 4, d_h) are outputs.
+ *  max_abs_F: device pointer to one float, overwritten with max |F| (NaN counted as +inf).
+ */
+slstm_status slstm_residual_jacobian(const void* P, slstm_dtype P_dtype, const float* R,
+                                     const float* state0, const float* states, float* A,
+                                     float* rhs, float* max_abs_F, int B, int T, int d_h,
+                                     slstm_forget fmode, void* stream);
+
+/* Workspace bytes of slstm_scan_block4 (0 if invalid). */
+size_t slstm_scan_block4_workspace_bytes(int B, int T, int d_h);
+
+/*
+ * Associative scan over 4x4 affine maps in the scan_block4 layout ([LY] "Naming"; the (J, r)
+ * monoid of [SL] "Packed sequences"): x_1 = rhs_1, x_t = A_t x_{t-1} + rhs_t, per lane (b, j).
+ * A at the first step is not read as a multiplier (x_0 = 0). A (B, T, 4, 4, d_h), rhs and x
+ * (B, T, 4, d_h); x may be the same buffer as rhs.
+ */
+slstm_status slstm_scan_block4(const float* A, const float* rhs, float* x, int B, int T, int d_h,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes of slstm_warm_start (0 if invalid). */
+size_t slstm_warm_start_workspace_bytes(int B, int T, int d_h);
+
+/*
+ * The initial Newton iterate: the exact trajectory of the cell with R h_{t-1} dropped from the
+ * pre-activations, from state0's (c, n, m) (a reading: the pages give no initial guess).
+ * Writes states (B, T, 4, d_h) with h = sigma(p_o) c / n.
+ */
+slstm_status slstm_warm_start(const void* P, slstm_dtype P_dtype, const float* state0,
+                              float* states, int B, int T, int d_h, slstm_forget fmode,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Kernel timing with HIP events recorded on the launching stream around every kernel the
+ * library launches, for measurement. Off by default; process-wide; not thread-safe.
+ * slstm_profile_read waits for the recorded events and returns the summed duration (ms) and
+ * the launch count of one kernel kind since the last reset.
+ */
+typedef enum {
+  SLSTM_KERNEL_WARM_START = 0,
+  SLSTM_KERNEL_RESIDUAL_JACOBIAN = 1,
+  SLSTM_KERNEL_SCAN_BLOCK4 = 2,
+  SLSTM_KERNEL_UPDATE = 3,
+  SLSTM_KERNEL_FINAL_RESIDUAL = 4,
+  SLSTM_KERNEL_INPUT_PROJECTION = 5,
+  SLSTM_KERNEL_SEQUENTIAL = 6,
+  SLSTM_KERNEL_KINDS = 7
+} slstm_kernel_kind;
+
+slstm_status slstm_profile_enable(int on);
+slstm_status slstm_profile_reset(void);
+slstm_status slstm_profile_read(slstm_kernel_kind kind, double* total_ms, int* launches);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLSTM_H */

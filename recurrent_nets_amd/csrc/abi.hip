@@ -1,0 +1,405 @@
+// C ABI of the library: argument checks, workspace layout, the Newton driver and timing.
+// The solver loop follows "Layout" (pararnn-torch docs), "Current surface (0.17)":
+// initial state prepended, residual early stop, flags after the last iterate.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <random>
+#include <vector>
+
+#include "../../include/slstm.h"
+#include "common.h"
+#include "kernels.h"
+
+using slstm::Control;
+using slstm::i64;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+slstm_status fail(slstm_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+#define HIP_TRY(expr)                                                                     \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess)                                                                 \
+      return fail(SLSTM_EHIP, "%s failed: %s", #expr, hipGetErrorString(e_));             \
+  } while (0)
+
+// Launch epochs tag the look-back words of every scan launch. The sequence starts at a random
+// point so that words left in recycled device memory by another process do not match.
+std::atomic<uint32_t> g_epoch{[] {
+  std::random_device rd;
+  return static_cast<uint32_t>(rd());
+}()};
+
+uint32_t next_epoch() {
+  uint32_t e;
+  do {
+    e = g_epoch.fetch_add(1u) + 1u;
+  } while (e == 0u);
+  return e;
+}
+
+// ---- kernel timing ------------------------------------------------------------------------
+struct ProfRec {
+  hipEvent_t a, b;
+  int kind;
+};
+struct Profiler {
+  bool on = false;
+  std::vector<ProfRec> recs;
+  std::vector<ProfRec> pool;
+  hipError_t acquire(ProfRec& r) {
+    if (!pool.empty()) {
+      r = pool.back();
+      pool.pop_back();
+      return hipSuccess;
+    }
+    hipError_t e = hipEventCreate(&r.a);
+    if (e != hipSuccess) return e;
+    return hipEventCreate(&r.b);
+  }
+};
+Profiler g_prof;
+
+template <class F>
+hipError_t timed(slstm_kernel_kind kind, hipStream_t s, F&& launch) {
+  if (!g_prof.on) return launch();
+  ProfRec r;
+  hipError_t e = g_prof.acquire(r);
+  if (e != hipSuccess) return e;
+  r.kind = kind;
+  e = hipEventRecord(r.a, s);
+  if (e != hipSuccess) return e;
+  e = launch();
+  if (e != hipSuccess) return e;
+  e = hipEventRecord(r.b, s);
+  if (e == hipSuccess) g_prof.recs.push_back(r);
+  return e;
+}
+
+// ---- argument checks and workspace layout ----------------------------------------------------
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+slstm_status check_dims(int B, int T, int d) {
+  if (B < 1 || T < 1 || d < 1) return fail(SLSTM_EINVAL, "B, T, d_h must be >= 1 (got %d, %d, %d)", B, T, d);
+  // the largest tensor, A, has B*T*16*d floats; keep every element offset well inside int64
+  const double elems = 16.0 * B * T * d;
+  if (elems > 4.0e15) return fail(SLSTM_EINVAL, "sizes too large");
+  return SLSTM_OK;
+}
+
+struct NewtonLayout {
+  size_t ctl, desc, A, rhs, total;
+};
+
+NewtonLayout newton_layout(int B, int T, int d) {
+  NewtonLayout L;
+  const size_t desc_words = std::max(slstm::scan_desc_words(B, T, d), slstm::warm_desc_words(B, T, d));
+  const size_t n_state = static_cast<size_t>(B) * T * 4 * d;
+  L.ctl = 0;
+  L.desc = align_up(sizeof(Control));
+  L.A = align_up(L.desc + desc_words * 8);
+  L.rhs = align_up(L.A + 4 * n_state * sizeof(float));
+  L.total = align_up(L.rhs + n_state * sizeof(float));
+  return L;
+}
+
+struct ScanLayout {
+  size_t ctl, desc, total;
+};
+
+ScanLayout scan_layout(size_t desc_words) {
+  ScanLayout L;
+  L.ctl = 0;
+  L.desc = align_up(sizeof(Control));
+  L.total = align_up(L.desc + desc_words * 8);
+  return L;
+}
+
+template <class T>
+T* at(void* base, size_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(base) + off);
+}
+
+slstm_status check_common(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
+                          const float* states, const float* h_out, int B, int T, int d,
+                          slstm_forget fmode) {
+  slstm_status s = check_dims(B, T, d);
+  if (s != SLSTM_OK) return s;
+  if (P == nullptr || R == nullptr || states == nullptr)
+    return fail(SLSTM_EINVAL, "P, R and states must not be NULL");
+  if (P_dtype != SLSTM_F32 && P_dtype != SLSTM_BF16) return fail(SLSTM_EINVAL, "unknown P dtype %d", (int)P_dtype);
+  if (fmode != SLSTM_FORGET_EXP && fmode != SLSTM_FORGET_SIGMOID)
+    return fail(SLSTM_EINVAL, "unknown forget mode %d", (int)fmode);
+  if (!aligned(P, P_dtype == SLSTM_F32 ? 4 : 2) || !aligned(R, 4) || !aligned(state0, 4))
+    return fail(SLSTM_EINVAL, "P, R or state0 misaligned");
+  if (!aligned(states, 16) || !aligned(h_out, 16)) return fail(SLSTM_EINVAL, "states and h_out must be 16-byte aligned");
+  return SLSTM_OK;
+}
+
+slstm_status stats_from_control(const Control& c, slstm_newton_stats* st) {
+  std::memset(st, 0, sizeof(*st));
+  st->iters = c.iters;
+  st->converged = c.converged;
+  st->diverged = c.diverged;
+  st->nonfinite = c.nonfinite;
+  for (int k = 0; k <= c.iters && k <= SLSTM_MAX_ITERS; ++k) {
+    float v;
+    std::memcpy(&v, &c.err_bits[k], 4);
+    st->max_abs_F[k] = v;
+  }
+  if (c.nonfinite) return SLSTM_NONFINITE;
+  if (c.diverged) return SLSTM_DIVERGED;
+  return SLSTM_OK;
+}
+
+__global__ void store_u32_kernel(unsigned int* p, unsigned int v) { *p = v; }
+
+}  // namespace
+
+extern "C" {
+
+const char* slstm_status_string(slstm_status s) {
+  switch (s) {
+    case SLSTM_OK: return "ok";
+    case SLSTM_DIVERGED: return "diverged: max|F| > 1 after the last Newton iterate";
+    case SLSTM_NONFINITE: return "non-finite residual after the last Newton iterate";
+    case SLSTM_EINVAL: return "invalid argument";
+    case SLSTM_EWORKSPACE: return "workspace too small";
+    case SLSTM_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+const char* slstm_last_error(void) { return g_err; }
+
+size_t slstm_newton_workspace_bytes(int B, int T, int d_h) {
+  if (check_dims(B, T, d_h) != SLSTM_OK) return 0;
+  return newton_layout(B, T, d_h).total;
+}
+
+slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const float* R,
+                                  const float* state0, float* states, float* h_out, int B, int T,
+                                  int d_h, slstm_forget fmode, int max_iters, float tol,
+                                  slstm_init init, void* workspace, size_t workspace_bytes,
+                                  void* stream, slstm_newton_stats* stats) {
+  g_err[0] = '\0';
+  slstm_status s = check_common(P, P_dtype, R, state0, states, h_out, B, T, d_h, fmode);
+  if (s != SLSTM_OK) return s;
+  if (max_iters < 1 || max_iters > SLSTM_MAX_ITERS)
+    return fail(SLSTM_EINVAL, "max_iters must be in 1..%d (got %d)", SLSTM_MAX_ITERS, max_iters);
+  if (!(tol >= 0.0f) || std::isinf(tol)) return fail(SLSTM_EINVAL, "tol must be finite and >= 0");
+  if (init != SLSTM_INIT_WARM && init != SLSTM_INIT_ZERO) return fail(SLSTM_EINVAL, "unknown init %d", (int)init);
+  if (workspace == nullptr || !aligned(workspace, kAlign))
+    return fail(SLSTM_EINVAL, "workspace must be non-NULL and 256-byte aligned");
+  const NewtonLayout L = newton_layout(B, T, d_h);
+  if (workspace_bytes < L.total)
+    return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf16 = P_dtype == SLSTM_BF16;
+  const bool sig = fmode == SLSTM_FORGET_SIGMOID;
+  Control* ctl = at<Control>(workspace, L.ctl);
+  auto* desc = at<unsigned long long>(workspace, L.desc);
+  float* A = at<float>(workspace, L.A);
+  float* rhs = at<float>(workspace, L.rhs);
+  const i64 n_state = static_cast<i64>(B) * T * 4 * d_h;
+
+  HIP_TRY(slstm::launch_init_control(ctl, st));
+  if (init == SLSTM_INIT_WARM) {
+    const uint32_t ep = next_epoch();
+    HIP_TRY(timed(SLSTM_KERNEL_WARM_START, st, [&] {
+      return slstm::launch_warm_start(P, bf16, state0, states, B, T, d_h, sig, desc, &ctl->ticket_warm, ep, st);
+    }));
+  } else {
+    HIP_TRY(slstm::launch_zero(states, n_state, st));
+  }
+  for (int k = 0; k < max_iters; ++k) {
+    HIP_TRY(timed(SLSTM_KERNEL_RESIDUAL_JACOBIAN, st, [&] {
+      return slstm::launch_residual(P, bf16, R, state0, states, A, rhs, B, T, d_h, sig, ctl,
+                                    &ctl->err_bits[k], true, st);
+    }));
+    const uint32_t ep = next_epoch();
+    HIP_TRY(timed(SLSTM_KERNEL_SCAN_BLOCK4, st, [&] {
+      return slstm::launch_scan_block4(A, rhs, rhs, B, T, d_h, desc, &ctl->ticket_scan, ep, ctl, k, tol, st);
+    }));
+    HIP_TRY(timed(SLSTM_KERNEL_UPDATE, st, [&] { return slstm::launch_update(states, rhs, n_state, ctl, k, st); }));
+  }
+  HIP_TRY(timed(SLSTM_KERNEL_FINAL_RESIDUAL, st, [&] {
+    return slstm::launch_residual(P, bf16, R, state0, states, nullptr, nullptr, B, T, d_h, sig, ctl,
+                                  &ctl->err_bits[max_iters], false, st);
+  }));
+  HIP_TRY(slstm::launch_finalize(ctl, tol, st));
+  if (h_out != nullptr) HIP_TRY(slstm::launch_hidden(states, h_out, B, T, d_h, st));
+  if (stats == nullptr) return SLSTM_OK;
+  Control host;
+  HIP_TRY(hipMemcpyAsync(&host, ctl, sizeof(Control), hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipStreamSynchronize(st));
+  return stats_from_control(host, stats);
+}
+
+slstm_status slstm_newton_read_stats(const void* workspace, size_t workspace_bytes, void* stream,
+                                     slstm_newton_stats* stats) {
+  g_err[0] = '\0';
+  if (workspace == nullptr || stats == nullptr || workspace_bytes < sizeof(Control))
+    return fail(SLSTM_EINVAL, "workspace and stats must be valid");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Control host;
+  HIP_TRY(hipMemcpyAsync(&host, workspace, sizeof(Control), hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipStreamSynchronize(st));
+  return stats_from_control(host, stats);
+}
+
+slstm_status slstm_sequential_forward(const void* P, slstm_dtype P_dtype, const float* R,
+                                      const float* state0, float* states, float* h_out, int B,
+                                      int T, int d_h, slstm_forget fmode, void* stream) {
+  g_err[0] = '\0';
+  slstm_status s = check_common(P, P_dtype, R, state0, states, h_out, B, T, d_h, fmode);
+  if (s != SLSTM_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HIP_TRY(timed(SLSTM_KERNEL_SEQUENTIAL, st, [&] {
+    return slstm::launch_sequential(P, P_dtype == SLSTM_BF16, R, state0, states, h_out, B, T, d_h,
+                                    fmode == SLSTM_FORGET_SIGMOID, st);
+  }));
+  return SLSTM_OK;
+}
+
+slstm_status slstm_input_projection(const void* x, const void* W_x, const float* bias, float* P,
+                                    int B, int T, int d_in, int d_h, slstm_dtype xw_dtype,
+                                    void* stream) {
+  g_err[0] = '\0';
+  slstm_status s = check_dims(B, T, d_h);
+  if (s != SLSTM_OK) return s;
+  if (d_in < 8 || d_in % 8 != 0) return fail(SLSTM_EINVAL, "d_in must be a positive multiple of 8 (got %d)", d_in);
+  if (xw_dtype != SLSTM_BF16) return fail(SLSTM_EINVAL, "the input projection takes bf16 x and W_x");
+  if (x == nullptr || W_x == nullptr || P == nullptr) return fail(SLSTM_EINVAL, "x, W_x and P must not be NULL");
+  if (!aligned(x, 16) || !aligned(W_x, 16) || !aligned(P, 4) || !aligned(bias, 4))
+    return fail(SLSTM_EINVAL, "x and W_x must be 16-byte aligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const i64 M = static_cast<i64>(B) * T;
+  HIP_TRY(timed(SLSTM_KERNEL_INPUT_PROJECTION, st, [&] {
+    return slstm::launch_gemm_bf16(x, W_x, bias, P, M, 4 * d_h, d_in, st);
+  }));
+  return SLSTM_OK;
+}
+
+slstm_status slstm_residual_jacobian(const void* P, slstm_dtype P_dtype, const float* R,
+                                     const float* state0, const float* states, float* A,
+                                     float* rhs, float* max_abs_F, int B, int T, int d_h,
+                                     slstm_forget fmode, void* stream) {
+  g_err[0] = '\0';
+  slstm_status s = check_common(P, P_dtype, R, state0, states, nullptr, B, T, d_h, fmode);
+  if (s != SLSTM_OK) return s;
+  if (A == nullptr || rhs == nullptr || max_abs_F == nullptr)
+    return fail(SLSTM_EINVAL, "A, rhs and max_abs_F must not be NULL");
+  if (!aligned(A, 16) || !aligned(rhs, 16) || !aligned(max_abs_F, 4)) return fail(SLSTM_EINVAL, "A or rhs misaligned");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  unsigned int* err = reinterpret_cast<unsigned int*>(max_abs_F);
+  store_u32_kernel<<<1, 1, 0, st>>>(err, 0u);
+  HIP_TRY(hipGetLastError());
+  HIP_TRY(timed(SLSTM_KERNEL_RESIDUAL_JACOBIAN, st, [&] {
+    return slstm::launch_residual(P, P_dtype == SLSTM_BF16, R, state0, states, A, rhs, B, T, d_h,
+                                  fmode == SLSTM_FORGET_SIGMOID, nullptr, err, true, st);
+  }));
+  return SLSTM_OK;
+}
+
+size_t slstm_scan_block4_workspace_bytes(int B, int T, int d_h) {
+  if (check_dims(B, T, d_h) != SLSTM_OK) return 0;
+  return scan_layout(slstm::scan_desc_words(B, T, d_h)).total;
+}
+
+slstm_status slstm_scan_block4(const float* A, const float* rhs, float* x, int B, int T, int d_h,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = '\0';
+  slstm_status s = check_dims(B, T, d_h);
+  if (s != SLSTM_OK) return s;
+  if (A == nullptr || rhs == nullptr || x == nullptr) return fail(SLSTM_EINVAL, "A, rhs and x must not be NULL");
+  if (!aligned(A, 4) || !aligned(rhs, 4) || !aligned(x, 4)) return fail(SLSTM_EINVAL, "A, rhs or x misaligned");
+  if (workspace == nullptr || !aligned(workspace, kAlign)) return fail(SLSTM_EINVAL, "workspace must be 256-byte aligned");
+  const ScanLayout L = scan_layout(slstm::scan_desc_words(B, T, d_h));
+  if (workspace_bytes < L.total) return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Control* ctl = at<Control>(workspace, L.ctl);
+  HIP_TRY(slstm::launch_init_control(ctl, st));
+  const uint32_t ep = next_epoch();
+  HIP_TRY(timed(SLSTM_KERNEL_SCAN_BLOCK4, st, [&] {
+    return slstm::launch_scan_block4(A, rhs, x, B, T, d_h, at<unsigned long long>(workspace, L.desc),
+                                     &ctl->ticket_scan, ep, nullptr, 0, 0.0f, st);
+  }));
+  return SLSTM_OK;
+}
+
+size_t slstm_warm_start_workspace_bytes(int B, int T, int d_h) {
+  if (check_dims(B, T, d_h) != SLSTM_OK) return 0;
+  return scan_layout(slstm::warm_desc_words(B, T, d_h)).total;
+}
+
+slstm_status slstm_warm_start(const void* P, slstm_dtype P_dtype, const float* state0,
+                              float* states, int B, int T, int d_h, slstm_forget fmode,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = '\0';
+  static const float kDummyR = 0.0f;  // R is not used by the warm start; the shared check wants one
+  slstm_status s = check_common(P, P_dtype, &kDummyR, state0, states, nullptr, B, T, d_h, fmode);
+  if (s != SLSTM_OK) return s;
+  if (workspace == nullptr || !aligned(workspace, kAlign)) return fail(SLSTM_EINVAL, "workspace must be 256-byte aligned");
+  const ScanLayout L = scan_layout(slstm::warm_desc_words(B, T, d_h));
+  if (workspace_bytes < L.total) return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Control* ctl = at<Control>(workspace, L.ctl);
+  HIP_TRY(slstm::launch_init_control(ctl, st));
+  const uint32_t ep = next_epoch();
+  HIP_TRY(timed(SLSTM_KERNEL_WARM_START, st, [&] {
+    return slstm::launch_warm_start(P, P_dtype == SLSTM_BF16, state0, states, B, T, d_h,
+                                    fmode == SLSTM_FORGET_SIGMOID, at<unsigned long long>(workspace, L.desc),
+                                    &ctl->ticket_warm, ep, st);
+  }));
+  return SLSTM_OK;
+}
+
+slstm_status slstm_profile_enable(int on) {
+  g_prof.on = on != 0;
+  return SLSTM_OK;
+}
+
+slstm_status slstm_profile_reset(void) {
+  for (auto& r : g_prof.recs) g_prof.pool.push_back(r);
+  g_prof.recs.clear();
+  return SLSTM_OK;
+}
+
+slstm_status slstm_profile_read(slstm_kernel_kind kind, double* total_ms, int* launches) {
+  g_err[0] = '\0';
+  if (total_ms == nullptr || launches == nullptr) return fail(SLSTM_EINVAL, "NULL output");
+  double sum = 0.0;
+  int n = 0;
+  for (auto& r : g_prof.recs) {
+    if (r.kind != static_cast<int>(kind)) continue;
+    HIP_TRY(hipEventSynchronize(r.b));
+    float ms = 0.0f;
+    HIP_TRY(hipEventElapsedTime(&ms, r.a, r.b));
+    sum += ms;
+    ++n;
+  }
+  *total_ms = sum;
+  *launches = n;
+  return SLSTM_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,83 @@
+// Shared device helpers for the sLSTM Newton kernels (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace slstm {
+
+constexpr int kWave = 64;
+
+// 64-bit element offsets: the Jacobian tensor of a large layer exceeds 2^32 floats.
+typedef long long i64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// Load one gate pre-activation, stored as float32 or bfloat16.
+template <bool BF16>
+__device__ __forceinline__ float load_p(const void* __restrict__ P, i64 idx) {
+  if constexpr (BF16) {
+    return bf16_to_f32(static_cast<const uint16_t*>(P)[idx]);
+  } else {
+    return static_cast<const float*>(P)[idx];
+  }
+}
+
+// |x| for the residual maximum; NaN counts as +inf so that a max reduction cannot drop it.
+__device__ __forceinline__ float abs_nan_inf(float x) {
+  float a = fabsf(x);
+  return (a == a) ? a : __int_as_float(0x7f800000);
+}
+
+// Device-wide running maximum of non-negative floats (bit patterns order like the values).
+__device__ __forceinline__ void atomic_max_nonneg(unsigned int* dst, float v) {
+  atomicMax(dst, __float_as_uint(v));
+}
+
+// ---- DPP quad permutations (lanes grouped in fours) ---------------------------------------
+// quad_perm selector: lane k of each quad reads lane sel[k] of the same quad.
+template <int S0, int S1, int S2, int S3>
+__device__ __forceinline__ float quad_perm(float v) {
+  constexpr int ctrl = S0 | (S1 << 2) | (S2 << 4) | (S3 << 6);
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), ctrl,
+                                                    0xf, 0xf, false));
+}
+
+// ---- wave / block maximum --------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+  return v;
+}
+
+// ---- epoch-tagged words for the decoupled look-back -------------------------------------------
+// Each published float travels in a 64-bit word whose high half is the launch's epoch. A reader
+// accepts a word only when its tag matches, so every word validates itself: no flag-after-data
+// ordering is needed, and stale words from earlier launches are never mistaken for new ones.
+__device__ __forceinline__ void tag_store(unsigned long long* p, float v, uint32_t epoch) {
+  unsigned long long w = (static_cast<unsigned long long>(epoch) << 32) | __float_as_uint(v);
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool tag_load(const unsigned long long* p, uint32_t epoch, float& v) {
+  unsigned long long w = __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+  v = __uint_as_float(static_cast<uint32_t>(w));
+  return static_cast<uint32_t>(w >> 32) == epoch;
+}
+
+// Solver control block kept at the start of the workspace.
+struct Control {
+  unsigned int err_bits[72];  // max|F| after k updates (float bits; NaN stored as +inf)
+  int iters;                  // Newton updates applied
+  int stopped;                // early stop taken
+  int converged;
+  int diverged;
+  int nonfinite;
+  unsigned int ticket_warm;   // work tickets of the look-back kernels (self-resetting)
+  unsigned int ticket_scan;
+  int pad[49];
+};
+static_assert(sizeof(Control) == 512, "control block layout");
+
+}  // namespace slstm

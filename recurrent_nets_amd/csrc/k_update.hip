@@ -1,0 +1,103 @@
+// Kernel (c) and the solver's control kernels.
+//
+// update:    s <- s + Delta over all (b, t, slot, j) (the Newton step, Delta from the scan);
+//            records the number of applied updates. Skipped once the solver has stopped.
+// init:      clears the control block (residual maxima, counters, flags) at the start of a
+//            solve; a plain fill kernel, so the whole solve can be replayed from a graph.
+// finalize:  flags from the residual of the last iterate: divergence when max|F| > 1 or it is
+//            not finite, convergence when a tolerance is set and met ("Layout" page of the
+//            pararnn-torch docs, "Current surface (0.17)": NewtonStats, residual early stop,
+//            divergence error when max|F| > 1 after K).
+// hidden:    copies the hidden slot (slot 3) of the states into a (B, T, d) output.
+#include "common.h"
+#include "kernels.h"
+
+namespace slstm {
+
+constexpr int kUpdBlock = 256;
+
+__global__ __launch_bounds__(kUpdBlock) void update_kernel(float4* __restrict__ S,
+                                                           const float4* __restrict__ D, i64 n4,
+                                                           Control* __restrict__ ctl, int k_iter) {
+  if (ctl->stopped) return;
+  const i64 stride = static_cast<i64>(gridDim.x) * kUpdBlock;
+  for (i64 i = static_cast<i64>(blockIdx.x) * kUpdBlock + threadIdx.x; i < n4; i += stride) {
+    float4 s = S[i];
+    const float4 dl = D[i];
+    s.x += dl.x;
+    s.y += dl.y;
+    s.z += dl.z;
+    s.w += dl.w;
+    S[i] = s;
+  }
+  if (blockIdx.x == 0 && threadIdx.x == 0) ctl->iters = k_iter + 1;
+}
+
+__global__ void init_control_kernel(Control* __restrict__ ctl) {
+  unsigned int* w = reinterpret_cast<unsigned int*>(ctl);
+  for (int i = threadIdx.x; i < static_cast<int>(sizeof(Control) / 4); i += blockDim.x) w[i] = 0u;
+}
+
+__global__ void finalize_kernel(Control* __restrict__ ctl, float tol) {
+  const float e = __uint_as_float(ctl->err_bits[ctl->iters]);
+  const bool finite = e == e && e != INFINITY;
+  ctl->nonfinite = finite ? 0 : 1;
+  ctl->diverged = (!finite || e > 1.0f) ? 1 : 0;
+  ctl->converged = (tol > 0.0f && finite && e < tol) ? 1 : 0;
+}
+
+__global__ __launch_bounds__(kUpdBlock) void hidden_kernel(const float* __restrict__ S,
+                                                           float* __restrict__ h, i64 rows, int d) {
+  // rows = B*T; one (b, t) row of d features per grid-stride step
+  const i64 n = rows * d;
+  const i64 stride = static_cast<i64>(gridDim.x) * kUpdBlock;
+  for (i64 i = static_cast<i64>(blockIdx.x) * kUpdBlock + threadIdx.x; i < n; i += stride) {
+    const i64 row = i / d;
+    const i64 j = i - row * d;
+    h[i] = S[(row * 4 + 3) * d + j];
+  }
+}
+
+__global__ __launch_bounds__(kUpdBlock) void zero_kernel(float4* __restrict__ p, i64 n4) {
+  const i64 stride = static_cast<i64>(gridDim.x) * kUpdBlock;
+  for (i64 i = static_cast<i64>(blockIdx.x) * kUpdBlock + threadIdx.x; i < n4; i += stride)
+    p[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+}
+
+static unsigned int stream_grid(i64 n) {
+  // enough blocks to fill 256 CUs several times over; the kernels stride the rest
+  const i64 want = (n + kUpdBlock - 1) / kUpdBlock;
+  return static_cast<unsigned int>(want < 8192 ? (want > 0 ? want : 1) : 8192);
+}
+
+hipError_t launch_update(float* S, const float* D, i64 n_floats, Control* ctl, int k_iter,
+                         hipStream_t stream) {
+  const i64 n4 = n_floats / 4;
+  update_kernel<<<stream_grid(n4), kUpdBlock, 0, stream>>>(
+      reinterpret_cast<float4*>(S), reinterpret_cast<const float4*>(D), n4, ctl, k_iter);
+  return hipGetLastError();
+}
+
+hipError_t launch_init_control(Control* ctl, hipStream_t stream) {
+  init_control_kernel<<<1, 128, 0, stream>>>(ctl);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(Control* ctl, float tol, hipStream_t stream) {
+  finalize_kernel<<<1, 1, 0, stream>>>(ctl, tol);
+  return hipGetLastError();
+}
+
+hipError_t launch_hidden(const float* S, float* h, int B, int T, int d, hipStream_t stream) {
+  const i64 rows = static_cast<i64>(B) * T;
+  hidden_kernel<<<stream_grid(rows * d), kUpdBlock, 0, stream>>>(S, h, rows, d);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero(float* p, i64 n_floats, hipStream_t stream) {
+  const i64 n4 = n_floats / 4;
+  zero_kernel<<<stream_grid(n4), kUpdBlock, 0, stream>>>(reinterpret_cast<float4*>(p), n4);
+  return hipGetLastError();
+}
+
+}  // namespace slstm

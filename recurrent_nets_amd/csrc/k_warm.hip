@@ -1,0 +1,278 @@
+// Initial Newton iterate: the exact trajectory of the sLSTM cell with the recurrent term
+// R h_{t-1} removed from the pre-activations. (The pages give no initial guess; with the
+// recurrent term dropped every gate is known up front, and this trajectory is the plainest
+// starting point that the stabilised equations admit.)
+//
+// With R dropped, step t is the map (m, c, n) -> (m', c', n'):
+//   m' = max(l_t + m, i~_t),  c' = e^{l_t + m - m'} c + e^{i~_t - m'} z_t,
+//   n' = e^{l_t + m - m'} n + e^{i~_t - m'}
+// (stabiliser and stabilised gates: educational reimplementation page, "Exponential gating +
+// the stabilizer (the crux)"; z = tanh, l = f~ or log sigma(f~)). A run of steps composes to
+// the same shape, held in log space relative to the run's start as (L, E, cz, nz):
+//   L  = sum of the l over the run,
+//   E  = max over steps s of e_s, with e_s = i~_s - (l_1 + ... + l_s) the log weight of the
+//        input at s seen from the run's start (a (max, +) scan),
+//   cz = sum_s e^{e_s - E} z_s,  nz = sum_s e^{e_s - E},
+// and it acts on a carried (m, c, n) as
+//   x = max(m, E),  c_out = e^{m - x} c + e^{E - x} cz,  n_out likewise,  m_out = L + x.
+// Referencing the exponents to the run's start keeps every exponent that carries weight of
+// order one: sums of l (which grow by about f~ per step) enter only m_out, never an
+// exponent, so a float32 carry is as accurate as the plain step loop.
+// Composition (X first, then Y): L = L_X + L_Y, E = max(E_X, E_Y - L_X),
+//   cz = e^{E_X - E} cz_X + e^{E_Y - L_X - E} cz_Y, nz likewise. One step: (l, i~ - l, z, 1).
+//
+// Same decomposition as the 4x4 scan: a tile of 64 lanes x 4*TSUB steps per workgroup,
+// per-thread sequential sub-chunks, a DPP quad scan of sub-chunk aggregates, tile
+// aggregates and carries staged in LDS, and a decoupled look-back across tiles along T. The
+// re-run from each carry writes the states (c, n, m, h) with h = sigma(p_o) c / n.
+#include "cell.h"
+#include "kernels.h"
+
+namespace slstm {
+
+constexpr int kWarmBlock = 256;
+constexpr int kWarmTSub = 16;
+constexpr int kWarmTile = 4 * kWarmTSub;
+constexpr int kWarmWords = 8;  // per lane and tile: carry (m, c, n, -), aggregate (L, E, cz, nz)
+
+struct LogAgg {
+  float L, E, cz, nz;
+};
+
+__device__ __forceinline__ float exp_or_zero(float e, float x) {
+  // e^{x} for an exponent built from E; an empty run has E = -inf and weight zero
+  return (e == -INFINITY) ? 0.0f : expf(x);
+}
+
+// X first, then Y
+__device__ __forceinline__ LogAgg compose(const LogAgg& X, const LogAgg& Y) {
+  LogAgg o;
+  o.L = X.L + Y.L;
+  const float ey = Y.E - X.L;
+  o.E = fmaxf(X.E, ey);
+  const float wx = exp_or_zero(X.E, X.E - o.E);
+  const float wy = exp_or_zero(Y.E, ey - o.E);
+  o.cz = fmaf(wx, X.cz, wy * Y.cz);
+  o.nz = fmaf(wx, X.nz, wy * Y.nz);
+  return o;
+}
+
+// apply a run to a carried (m, c, n)
+__device__ __forceinline__ void apply(const LogAgg& X, float& m, float& c, float& n) {
+  const float x = fmaxf(m, X.E);
+  const float wc = expf(m - x);
+  const float wz = exp_or_zero(X.E, X.E - x);
+  c = fmaf(wc, c, wz * X.cz);
+  n = fmaf(wc, n, wz * X.nz);
+  m = X.L + x;
+}
+
+__device__ __forceinline__ LogAgg quad_perm_agg_m1(const LogAgg& X) {
+  return {quad_perm<0, 0, 1, 2>(X.L), quad_perm<0, 0, 1, 2>(X.E), quad_perm<0, 0, 1, 2>(X.cz),
+          quad_perm<0, 0, 1, 2>(X.nz)};
+}
+__device__ __forceinline__ LogAgg quad_perm_agg_m2(const LogAgg& X) {
+  return {quad_perm<0, 1, 0, 1>(X.L), quad_perm<0, 1, 0, 1>(X.E), quad_perm<0, 1, 0, 1>(X.cz),
+          quad_perm<0, 1, 0, 1>(X.nz)};
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
+    const void* __restrict__ P, const float* __restrict__ state0, float* __restrict__ S, int B,
+    int T, int d, int sig_forget, int n_lg, int n_tt, unsigned long long* __restrict__ desc,
+    unsigned int* __restrict__ ticket, uint32_t epoch) {
+  __shared__ unsigned int s_ticket;
+  __shared__ LogAgg s_agg[64];
+  __shared__ float s_carry[64][3];
+
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    const unsigned int total = static_cast<unsigned int>(n_lg) * n_tt;
+    const unsigned int tk = atomicAdd(ticket, 1u);
+    if (tk == total - 1) atomicExch(ticket, 0u);
+    s_ticket = tk;
+  }
+  __syncthreads();
+  const unsigned int tk = s_ticket;
+  const int tt = static_cast<int>(tk / n_lg);
+  const int lg = static_cast<int>(tk % n_lg);
+
+  const int wave = tid >> 6;
+  const int l = tid & 63;
+  const int sc = l & 3;
+  const int lane_in_tile = wave * 16 + (l >> 2);
+  const i64 n_lanes = static_cast<i64>(B) * d;
+  const i64 n_lanes_pad = static_cast<i64>(n_lg) * 64;
+  const i64 lane = static_cast<i64>(lg) * 64 + lane_in_tile;
+  const bool valid = lane < n_lanes;
+  const int b = valid ? static_cast<int>(lane / d) : 0;
+  const int j = valid ? static_cast<int>(lane % d) : 0;
+  const int t_start = tt * kWarmTile + sc * kWarmTSub;
+  const i64 dd = d;
+  const bool sig = sig_forget != 0;
+
+  // ---- level 1: gates of the sub-chunk, folded into one aggregate ----
+  float lf[kWarmTSub], it[kWarmTSub], zz[kWarmTSub], oo[kWarmTSub];
+#pragma unroll
+  for (int u = 0; u < kWarmTSub; ++u) {
+    const int t = t_start + u;
+    if (valid && t < T) {
+      const i64 base = (static_cast<i64>(b) * T + t) * 4 * dd + j;
+      const float pz = load_p<BF16>(P, base);
+      const float pi = load_p<BF16>(P, base + dd);
+      const float pf = load_p<BF16>(P, base + 2 * dd);
+      const float po = load_p<BF16>(P, base + 3 * dd);
+      zz[u] = tanhf(pz);
+      oo[u] = sigmoidf(po);
+      it[u] = pi;
+      lf[u] = sig ? log_sigmoidf(pf) : pf;
+    } else {
+      zz[u] = 0.0f;
+      oo[u] = 0.0f;
+      it[u] = -INFINITY;  // padding step: m -> m, c -> c, n -> n
+      lf[u] = 0.0f;
+    }
+  }
+  LogAgg agg = {0.0f, -INFINITY, 0.0f, 0.0f};
+#pragma unroll
+  for (int u = 0; u < kWarmTSub; ++u) {
+    // one step as a run: L = l, E = i~ - l, cz = z, nz = 1
+    const LogAgg stp = {lf[u], it[u] - lf[u], zz[u], 1.0f};
+    agg = compose(agg, stp);
+  }
+
+  // ---- level 2: quad scan (DPP) ----
+  {
+    const LogAgg p1 = quad_perm_agg_m1(agg);
+    if (sc >= 1) agg = compose(p1, agg);
+    const LogAgg p2 = quad_perm_agg_m2(agg);
+    if (sc >= 2) agg = compose(p2, agg);
+  }
+  if (sc == 3) s_agg[lane_in_tile] = agg;
+  __syncthreads();
+
+  // ---- level 3: decoupled look-back ----
+  if (wave == 0) {
+    const i64 my_lane = static_cast<i64>(lg) * 64 + l;
+    const LogAgg tile = s_agg[l];
+    auto word = [&](int t_tile, int w) {
+      return desc + (static_cast<i64>(t_tile) * kWarmWords + w) * n_lanes_pad + my_lane;
+    };
+    // state entering the sequence (slots c, n, m of state0; zeros without one)
+    float m0 = 0.0f, c0 = 0.0f, n0 = 0.0f;
+    if (state0 != nullptr && my_lane < n_lanes) {
+      const int bl = static_cast<int>(my_lane / d), jl = static_cast<int>(my_lane % d);
+      const float* s0 = state0 + static_cast<i64>(bl) * 4 * dd + jl;
+      c0 = s0[0];
+      n0 = s0[dd];
+      m0 = s0[2 * dd];
+    }
+    float cm = m0, cc = c0, cn = n0;
+    if (tt > 0) {
+      LogAgg acc = {0.0f, -INFINITY, 0.0f, 0.0f};
+      bool published = false;
+      int p = tt - 1;
+      while (true) {
+        float xm, xc, xn;
+        const bool inc = tag_load(word(p, 0), epoch, xm) & tag_load(word(p, 1), epoch, xc) &
+                         tag_load(word(p, 2), epoch, xn);
+        if (inc) {
+          apply(acc, xm, xc, xn);
+          cm = xm;
+          cc = xc;
+          cn = xn;
+          break;
+        }
+        if (!published) {
+          tag_store(word(tt, 4), tile.L, epoch);
+          tag_store(word(tt, 5), tile.E, epoch);
+          tag_store(word(tt, 6), tile.cz, epoch);
+          tag_store(word(tt, 7), tile.nz, epoch);
+          published = true;
+        }
+        LogAgg pa;
+        const bool ok = tag_load(word(p, 4), epoch, pa.L) & tag_load(word(p, 5), epoch, pa.E) &
+                        tag_load(word(p, 6), epoch, pa.cz) & tag_load(word(p, 7), epoch, pa.nz);
+        if (ok) {
+          acc = compose(pa, acc);
+          if (--p < 0) {
+            apply(acc, cm, cc, cn);  // from the state entering the sequence
+            break;
+          }
+          continue;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    s_carry[l][0] = cm;
+    s_carry[l][1] = cc;
+    s_carry[l][2] = cn;
+    float em = cm, ec = cc, en = cn;
+    apply(tile, em, ec, en);
+    tag_store(word(tt, 0), em, epoch);
+    tag_store(word(tt, 1), ec, epoch);
+    tag_store(word(tt, 2), en, epoch);
+  }
+  __syncthreads();
+
+  // ---- re-run each sub-chunk from its carry, writing the states ----
+  const float cm = s_carry[lane_in_tile][0];
+  const float cc = s_carry[lane_in_tile][1];
+  const float cn = s_carry[lane_in_tile][2];
+  float em = cm, ec = cc, en = cn;
+  apply(agg, em, ec, en);  // inclusive: end of this sub-chunk
+  float m = quad_perm<0, 0, 1, 2>(em);
+  float c = quad_perm<0, 0, 1, 2>(ec);
+  float n = quad_perm<0, 0, 1, 2>(en);
+  if (sc == 0) {
+    m = cm;
+    c = cc;
+    n = cn;
+  }
+#pragma unroll
+  for (int u = 0; u < kWarmTSub; ++u) {
+    const int t = t_start + u;
+    if (valid && t < T) {
+      const float a = lf[u] + m;
+      const float mn = (a >= it[u]) ? a : it[u];
+      const float ig = expf(it[u] - mn);
+      const float fg = expf(a - mn);
+      c = fmaf(fg, c, ig * zz[u]);
+      n = fmaf(fg, n, ig);
+      m = mn;
+      float* sp = S + (static_cast<i64>(b) * T + t) * 4 * dd + j;
+      sp[0] = c;
+      sp[dd] = n;
+      sp[2 * dd] = m;
+      sp[3 * dd] = oo[u] * c / n;
+    }
+  }
+}
+
+size_t warm_desc_words(int B, int T, int d) {
+  const i64 n_lg = (static_cast<i64>(B) * d + 63) / 64;
+  const i64 n_tt = (T + kWarmTile - 1) / kWarmTile;
+  return static_cast<size_t>(n_tt * kWarmWords * n_lg * 64);
+}
+
+hipError_t launch_warm_start(const void* P, bool p_bf16, const float* state0, float* S, int B,
+                             int T, int d, bool sig_forget, unsigned long long* desc,
+                             unsigned int* ticket, uint32_t epoch, hipStream_t stream) {
+  const i64 n_lg = (static_cast<i64>(B) * d + 63) / 64;
+  const i64 n_tt = (T + kWarmTile - 1) / kWarmTile;
+  const i64 blocks = n_lg * n_tt;
+  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>(blocks));
+  const int sig = sig_forget ? 1 : 0;
+  if (p_bf16)
+    warm_start_kernel<true><<<grid, kWarmBlock, 0, stream>>>(P, state0, S, B, T, d, sig,
+                                                             static_cast<int>(n_lg), static_cast<int>(n_tt),
+                                                             desc, ticket, epoch);
+  else
+    warm_start_kernel<false><<<grid, kWarmBlock, 0, stream>>>(P, state0, S, B, T, d, sig,
+                                                              static_cast<int>(n_lg), static_cast<int>(n_tt),
+                                                              desc, ticket, epoch);
+  return hipGetLastError();
+}
+
+}  // namespace slstm

@@ -1,0 +1,322 @@
+"""Python binding of the sLSTM HIP library (ctypes over the C ABI in include/slstm.h).
+
+Argument marshalling only: every step of the computation runs in the library's kernels.
+PyTorch supplies device memory and the current stream. Importing torch first makes the
+library bind to the HIP runtime torch has already loaded (same SONAME), so torch's streams
+are valid handles for it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+
+import torch
+
+from . import build as _build
+
+# enums of include/slstm.h
+OK, DIVERGED, NONFINITE, EINVAL, EWORKSPACE, EHIP = 0, 1, 2, -1, -2, -3
+F32, BF16 = 0, 1
+FORGET = {"exp": 0, "sigmoid": 1}
+INIT = {"warm": 0, "zero": 1}
+MAX_ITERS = 64
+KERNELS = {"warm_start": 0, "residual_jacobian": 1, "scan_block4": 2, "update": 3,
+           "final_residual": 4, "input_projection": 5, "sequential": 6}
+
+EXPORTED = [
+    "slstm_status_string", "slstm_last_error", "slstm_newton_workspace_bytes",
+    "slstm_newton_forward", "slstm_newton_read_stats", "slstm_sequential_forward",
+    "slstm_input_projection", "slstm_residual_jacobian", "slstm_scan_block4_workspace_bytes",
+    "slstm_scan_block4", "slstm_warm_start_workspace_bytes", "slstm_warm_start",
+    "slstm_profile_enable", "slstm_profile_reset", "slstm_profile_read",
+]
+
+
+class NewtonDivergenceError(RuntimeError):
+    """Raised when max|F| > 1 (or is not finite) after the last Newton iterate."""
+
+
+class SlstmError(RuntimeError):
+    pass
+
+
+class _Stats(ctypes.Structure):
+    _fields_ = [("iters", ctypes.c_int32), ("converged", ctypes.c_int32),
+                ("diverged", ctypes.c_int32), ("nonfinite", ctypes.c_int32),
+                ("max_abs_F", ctypes.c_float * (MAX_ITERS + 1))]
+
+
+@dataclass
+class NewtonStats:
+    iters: int = 0
+    converged: bool = False
+    diverged: bool = False
+    nonfinite: bool = False
+    max_abs_F: list = field(default_factory=list)  # entry k: max|F| after k updates
+    status: int = OK
+
+    @classmethod
+    def _from(cls, s: _Stats, status: int) -> "NewtonStats":
+        return cls(s.iters, bool(s.converged), bool(s.diverged), bool(s.nonfinite),
+                   [float(s.max_abs_F[k]) for k in range(s.iters + 1)], status)
+
+
+_LIB = None
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+
+
+def lib_path() -> str:
+    return _build.lib_path()
+
+
+def load(path: str | None = None):
+    """Load the built library (once). Raises when it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = path or lib_path()
+    if not os.path.exists(path):
+        raise ImportError(f"the HIP library is not built ({path} missing); run "
+                          f"`python -m recurrent_nets_amd.build` first")
+    L = ctypes.CDLL(path)
+    L.slstm_status_string.restype = ctypes.c_char_p
+    L.slstm_status_string.argtypes = [_i]
+    L.slstm_last_error.restype = ctypes.c_char_p
+    for name in ("slstm_newton_workspace_bytes", "slstm_scan_block4_workspace_bytes",
+                 "slstm_warm_start_workspace_bytes"):
+        getattr(L, name).restype = _sz
+        getattr(L, name).argtypes = [_i, _i, _i]
+    L.slstm_newton_forward.restype = _i
+    L.slstm_newton_forward.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
+                                       _vp, _sz, _vp, ctypes.POINTER(_Stats)]
+    L.slstm_newton_read_stats.restype = _i
+    L.slstm_newton_read_stats.argtypes = [_vp, _sz, _vp, ctypes.POINTER(_Stats)]
+    L.slstm_sequential_forward.restype = _i
+    L.slstm_sequential_forward.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]
+    L.slstm_input_projection.restype = _i
+    L.slstm_input_projection.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
+    L.slstm_residual_jacobian.restype = _i
+    L.slstm_residual_jacobian.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]
+    L.slstm_scan_block4.restype = _i
+    L.slstm_scan_block4.argtypes = [_vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp]
+    L.slstm_warm_start.restype = _i
+    L.slstm_warm_start.argtypes = [_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]
+    L.slstm_profile_enable.restype = _i
+    L.slstm_profile_enable.argtypes = [_i]
+    L.slstm_profile_reset.restype = _i
+    L.slstm_profile_read.restype = _i
+    L.slstm_profile_read.argtypes = [_i, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i)]
+    _LIB = L
+    return L
+
+
+def _check(status: int, what: str) -> int:
+    if status < 0:
+        L = load()
+        raise SlstmError(f"{what}: {L.slstm_status_string(status).decode()}: "
+                         f"{L.slstm_last_error().decode()}")
+    return status
+
+
+# ---- marshalling helpers ---------------------------------------------------------------------
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(t, name, dtypes):
+    if t is None:
+        return
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must be one of {dtypes}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _p_dtype(P):
+    return BF16 if P.dtype == torch.bfloat16 else F32
+
+
+def _shape_check(P, R, state0):
+    if P.dim() != 4 or P.shape[2] != 4:
+        raise ValueError(f"P must be (B, T, 4, d_h), got {tuple(P.shape)}")
+    B, T, _, d = P.shape
+    if tuple(R.shape) != (4, d):
+        raise ValueError(f"R must be (4, {d}), got {tuple(R.shape)}")
+    if state0 is not None and tuple(state0.shape) != (B, 4, d):
+        raise ValueError(f"state0 must be ({B}, 4, {d}), got {tuple(state0.shape)}")
+    return B, T, d
+
+
+def newton_workspace_bytes(B: int, T: int, d_h: int) -> int:
+    return int(load().slstm_newton_workspace_bytes(B, T, d_h))
+
+
+def alloc_workspace(nbytes: int, device=None) -> torch.Tensor:
+    # torch's caching allocator returns blocks aligned well beyond 256 bytes
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device or "cuda")
+
+
+def newton_forward(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, init="warm",
+                   states=None, h_out=None, want_hidden=True, workspace=None, stream=None,
+                   stats=True, raise_on_divergence=True):
+    """Newton-parallel forward. Returns (states (B,T,4,d_h), h (B,T,d_h) or None, NewtonStats
+    or None). With stats=False the call is asynchronous and returns no stats."""
+    L = load()
+    _dev(P, "P", (torch.float32, torch.bfloat16))
+    _dev(R, "R", (torch.float32,))
+    _dev(state0, "state0", (torch.float32,))
+    B, T, d = _shape_check(P, R, state0)
+    if states is None:
+        states = torch.empty((B, T, 4, d), dtype=torch.float32, device=P.device)
+    if want_hidden and h_out is None:
+        h_out = torch.empty((B, T, d), dtype=torch.float32, device=P.device)
+    _dev(states, "states", (torch.float32,))
+    _dev(h_out, "h_out", (torch.float32,))
+    need = L.slstm_newton_workspace_bytes(B, T, d)
+    if workspace is None:
+        workspace = alloc_workspace(need, P.device)
+    st = _Stats() if stats else None
+    status = L.slstm_newton_forward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
+                                    _ptr(h_out), B, T, d, FORGET[forget], int(max_iters),
+                                    float(tol), INIT[init], _ptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _stream(stream),
+                                    ctypes.byref(st) if st is not None else None)
+    _check(status, "slstm_newton_forward")
+    out_stats = NewtonStats._from(st, status) if st is not None else None
+    if raise_on_divergence and status in (DIVERGED, NONFINITE):
+        raise NewtonDivergenceError(
+            f"{L.slstm_status_string(status).decode()} (max|F| = {out_stats.max_abs_F[-1]:.3g})")
+    return states, h_out, out_stats
+
+
+def read_stats(workspace, stream=None) -> NewtonStats:
+    L = load()
+    st = _Stats()
+    status = L.slstm_newton_read_stats(_ptr(workspace), workspace.numel(), _stream(stream),
+                                       ctypes.byref(st))
+    _check(status, "slstm_newton_read_stats")
+    return NewtonStats._from(st, status)
+
+
+def sequential_forward(P, R, state0=None, forget="exp", states=None, h_out=None,
+                       want_hidden=True, stream=None):
+    """Step-by-step forward (also the T=1 decode step). Returns (states, h or None)."""
+    L = load()
+    _dev(P, "P", (torch.float32, torch.bfloat16))
+    _dev(R, "R", (torch.float32,))
+    _dev(state0, "state0", (torch.float32,))
+    B, T, d = _shape_check(P, R, state0)
+    if states is None:
+        states = torch.empty((B, T, 4, d), dtype=torch.float32, device=P.device)
+    if want_hidden and h_out is None:
+        h_out = torch.empty((B, T, d), dtype=torch.float32, device=P.device)
+    _dev(states, "states", (torch.float32,))
+    _dev(h_out, "h_out", (torch.float32,))
+    status = L.slstm_sequential_forward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
+                                        _ptr(h_out), B, T, d, FORGET[forget], _stream(stream))
+    _check(status, "slstm_sequential_forward")
+    return states, h_out
+
+
+def input_projection(x, W, bias=None, out=None, stream=None):
+    """P = x W^T + bias on MFMA. x (B,T,d_in) bf16, W (4,d_h,d_in) bf16, bias (4,d_h) f32."""
+    L = load()
+    _dev(x, "x", (torch.bfloat16,))
+    _dev(W, "W_x", (torch.bfloat16,))
+    _dev(bias, "bias", (torch.float32,))
+    B, T, d_in = x.shape
+    g, d, d_in2 = W.shape
+    if g != 4 or d_in2 != d_in:
+        raise ValueError(f"W_x must be (4, d_h, {d_in}), got {tuple(W.shape)}")
+    if bias is not None and tuple(bias.shape) != (4, d):
+        raise ValueError(f"bias must be (4, {d})")
+    if out is None:
+        out = torch.empty((B, T, 4, d), dtype=torch.float32, device=x.device)
+    _dev(out, "P", (torch.float32,))
+    status = L.slstm_input_projection(_ptr(x), _ptr(W), _ptr(bias), _ptr(out), B, T, d_in, d,
+                                      BF16, _stream(stream))
+    _check(status, "slstm_input_projection")
+    return out
+
+
+def residual_jacobian(P, R, states, state0=None, forget="exp", stream=None):
+    """One residual + Jacobian evaluation. Returns (A (B,T,4,4,d), rhs = -F (B,T,4,d),
+    max|F| as a 1-element device tensor)."""
+    L = load()
+    _dev(P, "P", (torch.float32, torch.bfloat16))
+    _dev(R, "R", (torch.float32,))
+    _dev(state0, "state0", (torch.float32,))
+    _dev(states, "states", (torch.float32,))
+    B, T, d = _shape_check(P, R, state0)
+    A = torch.empty((B, T, 4, 4, d), dtype=torch.float32, device=P.device)
+    rhs = torch.empty((B, T, 4, d), dtype=torch.float32, device=P.device)
+    err = torch.empty((1,), dtype=torch.float32, device=P.device)
+    status = L.slstm_residual_jacobian(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
+                                       _ptr(A), _ptr(rhs), _ptr(err), B, T, d, FORGET[forget],
+                                       _stream(stream))
+    _check(status, "slstm_residual_jacobian")
+    return A, rhs, err
+
+
+def scan_block4(A, rhs, out=None, workspace=None, stream=None):
+    """x_1 = rhs_1, x_t = A_t x_{t-1} + rhs_t per lane. A (B,T,4,4,d), rhs (B,T,4,d).
+    ``out`` may be ``rhs`` itself (in place)."""
+    L = load()
+    _dev(A, "A", (torch.float32,))
+    _dev(rhs, "rhs", (torch.float32,))
+    B, T, _, d = rhs.shape
+    if tuple(A.shape) != (B, T, 4, 4, d):
+        raise ValueError("A must be (B, T, 4, 4, d) matching rhs")
+    if out is None:
+        out = torch.empty_like(rhs)
+    _dev(out, "out", (torch.float32,))
+    need = L.slstm_scan_block4_workspace_bytes(B, T, d)
+    if workspace is None:
+        workspace = alloc_workspace(need, rhs.device)
+    status = L.slstm_scan_block4(_ptr(A), _ptr(rhs), _ptr(out), B, T, d, _ptr(workspace),
+                                 workspace.numel(), _stream(stream))
+    _check(status, "slstm_scan_block4")
+    return out
+
+
+def warm_start(P, state0=None, forget="exp", out=None, workspace=None, stream=None):
+    """The R-free trajectory used as the initial Newton iterate. Returns states (B,T,4,d)."""
+    L = load()
+    _dev(P, "P", (torch.float32, torch.bfloat16))
+    _dev(state0, "state0", (torch.float32,))
+    B, T, _, d = P.shape
+    if out is None:
+        out = torch.empty((B, T, 4, d), dtype=torch.float32, device=P.device)
+    need = L.slstm_warm_start_workspace_bytes(B, T, d)
+    if workspace is None:
+        workspace = alloc_workspace(need, P.device)
+    status = L.slstm_warm_start(_ptr(P), _p_dtype(P), _ptr(state0), _ptr(out), B, T, d,
+                                FORGET[forget], _ptr(workspace), workspace.numel(),
+                                _stream(stream))
+    _check(status, "slstm_warm_start")
+    return out
+
+
+def profile_enable(on: bool = True):
+    load().slstm_profile_enable(1 if on else 0)
+
+
+def profile_reset():
+    load().slstm_profile_reset()
+
+
+def profile_read(kind: str):
+    """(summed milliseconds, launch count) of one kernel kind since the last reset."""
+    ms = ctypes.c_double()
+    n = ctypes.c_int()
+    _check(load().slstm_profile_read(KERNELS[kind], ctypes.byref(ms), ctypes.byref(n)),
+           "slstm_profile_read")
+    return ms.value, n.value

@@ -1,0 +1,98 @@
+"""The C-ABI library on the host: it loads, exports every function include/slstm.h declares,
+and its argument checks and workspace sizing behave as documented (no GPU work is done)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import torch  # noqa: F401  (binds the library to the HIP runtime torch loads)
+from recurrent_nets_amd import slstm
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "slstm.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(slstm_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(slstm.lib_path()):
+        pytest.fail("library not built: run `python -m recurrent_nets_amd.build`")
+    return slstm.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    declared = _declared()
+    assert len(declared) >= 15
+    missing = [n for n in declared if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(declared) == set(slstm.EXPORTED)
+
+
+def test_status_strings(lib):
+    for s in (0, 1, 2, -1, -2, -3):
+        assert lib.slstm_status_string(s).decode()
+    assert lib.slstm_status_string(99).decode() == "unknown status"
+
+
+def test_workspace_sizes(lib):
+    # Jacobians (64 B) + right-hand sides (16 B) per state element, plus look-back words
+    B, T, d = 128, 2048, 1024
+    n = lib.slstm_newton_workspace_bytes(B, T, d)
+    assert n >= 80 * B * T * d
+    assert n < 90 * B * T * d
+    assert lib.slstm_newton_workspace_bytes(0, 1, 1) == 0
+    assert lib.slstm_newton_workspace_bytes(1, -1, 1) == 0
+    assert lib.slstm_scan_block4_workspace_bytes(2, 64, 16) > 0
+    assert lib.slstm_warm_start_workspace_bytes(2, 64, 16) > 0
+    # tiny shapes still get a control block and one tile of look-back words
+    assert lib.slstm_newton_workspace_bytes(1, 1, 1) >= 512
+
+
+def _fwd(lib, **kw):
+    args = dict(P=ctypes.c_void_p(256), dt=0, R=ctypes.c_void_p(256), s0=None,
+                S=ctypes.c_void_p(256), h=None, B=2, T=64, d=16, fm=0, K=3, tol=0.0, init=0,
+                ws=ctypes.c_void_p(4096), wsb=1 << 30, stream=None, stats=None)
+    args.update(kw)
+    return lib.slstm_newton_forward(*args.values())
+
+
+def test_argument_checks_return_einval(lib):
+    # every call below is rejected on the host before any device work
+    assert _fwd(lib, B=0) == slstm.EINVAL
+    assert _fwd(lib, K=0) == slstm.EINVAL
+    assert _fwd(lib, K=65) == slstm.EINVAL
+    assert _fwd(lib, tol=-1.0) == slstm.EINVAL
+    assert _fwd(lib, tol=float("nan")) == slstm.EINVAL
+    assert _fwd(lib, fm=7) == slstm.EINVAL
+    assert _fwd(lib, dt=5) == slstm.EINVAL
+    assert _fwd(lib, init=3) == slstm.EINVAL
+    assert _fwd(lib, P=None) == slstm.EINVAL
+    assert _fwd(lib, S=ctypes.c_void_p(260)) == slstm.EINVAL      # states not 16-byte aligned
+    assert _fwd(lib, ws=ctypes.c_void_p(4096 + 16)) == slstm.EINVAL  # workspace not 256-aligned
+    assert "256-byte" in lib.slstm_last_error().decode()
+    assert _fwd(lib, wsb=100) == slstm.EWORKSPACE
+    assert "needed" in lib.slstm_last_error().decode()
+    s = lib.slstm_input_projection(ctypes.c_void_p(256), ctypes.c_void_p(256), None,
+                                   ctypes.c_void_p(256), 2, 3, 12, 4, 1, None)
+    assert s == slstm.EINVAL and "multiple of 8" in lib.slstm_last_error().decode()
+    s = lib.slstm_input_projection(ctypes.c_void_p(256), ctypes.c_void_p(256), None,
+                                   ctypes.c_void_p(256), 2, 3, 16, 4, 0, None)
+    assert s == slstm.EINVAL  # float32 x / W_x are not taken
+    s = lib.slstm_scan_block4(ctypes.c_void_p(256), ctypes.c_void_p(256), ctypes.c_void_p(256),
+                              2, 64, 16, ctypes.c_void_p(4096), 10, None)
+    assert s == slstm.EWORKSPACE
+    s = lib.slstm_sequential_forward(None, 0, ctypes.c_void_p(256), None, ctypes.c_void_p(256),
+                                     None, 2, 64, 16, 0, None)
+    assert s == slstm.EINVAL
+
+
+def test_binding_refuses_host_tensors():
+    P = torch.zeros((1, 2, 4, 3))
+    R = torch.zeros((4, 3))
+    with pytest.raises(ValueError):
+        slstm.newton_forward(P, R)

@@ -1,0 +1,165 @@
+"""End-to-end GPU parity of the Newton and sequential forwards against the float64 oracle:
+h within the bar, identical iteration counts and flags; edge shapes; divergence; early stop;
+sequence carrying through the final state."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import lanes, slstm_ref as ref
+from parity import H_TOL_BF16, H_TOL_F32, case, h_rel_err, to_np
+from workloads import by_name, draw_preactivation_inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _run_both(gpu_lib, P, R, state0, forget, K, tol=0.0, init="warm"):
+    S, h, st = gpu_lib.newton_forward(P.to(DEV), R.to(DEV),
+                                      None if state0 is None else state0.to(DEV), forget,
+                                      K, tol, init, raise_on_divergence=False)
+    torch.cuda.synchronize()
+    S_ref, st_ref = ref.newton(to_np(P), to_np(R), None if state0 is None else to_np(state0),
+                               forget, K, tol=tol, init=init)
+    return S, h, st, S_ref, st_ref
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4, 8, 16, 32, 64])
+def test_tiny_fixed_k_sweep(gpu_lib, K):
+    w = by_name("tiny_b2_t64_d16")
+    case(f"newton {w.name} K={K}")
+    inp = draw_preactivation_inputs(w)
+    S, h, st, S_ref, st_ref = _run_both(gpu_lib, inp["P"], inp["R"], None, w.forget, K)
+    assert h_rel_err(h, S_ref[..., 3, :]) < H_TOL_F32
+    assert torch.equal(h, S[..., 3, :])
+    assert st.iters == st_ref.iters == K
+    assert st.diverged == st_ref.diverged is False
+    assert st.converged == st_ref.converged is False
+    assert len(st.max_abs_F) == K + 1
+
+
+def test_mid_workload_full_size(gpu_lib):
+    w = by_name("mid_b8_t1024_d256")
+    case(f"newton {w.name} full size K={w.max_iters}")
+    inp = draw_preactivation_inputs(w)
+    S, h, st = gpu_lib.newton_forward(inp["P"].to(DEV), inp["R"].to(DEV), None, w.forget,
+                                      w.max_iters, w.tol)
+    torch.cuda.synchronize()
+    S_ref, st_ref = lanes.newton_lanes(inp["P"], inp["R"], None, w.forget, w.max_iters, w.tol)
+    h_ref = S_ref[:, :, 3].reshape(w.B, w.d_h, w.T).transpose(0, 2, 1)
+    assert h_rel_err(h, h_ref) < H_TOL_F32
+    assert st.iters == st_ref.iters and st.diverged == st_ref.diverged
+    # and against the sequential recurrence: the K=3 Newton iterate is converged here
+    seq = lanes.sequential_lanes(inp["P"], inp["R"], None, w.forget)
+    h_seq = seq[:, :, 3].reshape(w.B, w.d_h, w.T).transpose(0, 2, 1)
+    assert h_rel_err(h, h_seq) < H_TOL_F32
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (1, 2, 3), (3, 33, 65), (2, 257, 20), (1, 70, 64)])
+@pytest.mark.parametrize("forget", ["exp", "sigmoid"])
+def test_edge_shapes(gpu_lib, shape, forget):
+    B, T, d = shape
+    case(f"newton edge B={B} T={T} d={d} {forget}")
+    rng = np.random.Generator(np.random.PCG64(B * 1000 + T * 10 + d))
+    P = rng.standard_normal((B, T, 4, d))
+    P[:, :, 2] += 3.0
+    R = rng.uniform(-0.5, 0.5, (4, d))
+    s0 = np.zeros((B, 4, d))
+    s0[:, 0] = rng.uniform(-0.3, 0.3, (B, d))
+    s0[:, 1] = rng.uniform(0.5, 1.5, (B, d))
+    s0[:, 2] = rng.uniform(-1, 1, (B, d))
+    s0[:, 3] = rng.uniform(-0.5, 0.5, (B, d))
+    Pt = torch.from_numpy(P.astype(np.float32))
+    Rt = torch.from_numpy(R.astype(np.float32))
+    s0t = torch.from_numpy(s0.astype(np.float32))
+    S, h, st, S_ref, st_ref = _run_both(gpu_lib, Pt, Rt, s0t, forget, 6)
+    assert h_rel_err(h, S_ref[..., 3, :]) < H_TOL_F32
+    assert st.iters == st_ref.iters and st.diverged == st_ref.diverged
+    Ss, hs = gpu_lib.sequential_forward(Pt.to(DEV), Rt.to(DEV), s0t.to(DEV), forget)
+    torch.cuda.synchronize()
+    seq_ref = ref.sequential(to_np(Pt), to_np(Rt), to_np(s0t), forget)
+    assert h_rel_err(hs, seq_ref[..., 3, :]) < H_TOL_F32
+
+
+@pytest.mark.parametrize("name", ["tiny_b2_t64_d16", "mid_b8_t1024_d256"])
+def test_sequential_full_size(gpu_lib, name):
+    w = by_name(name)
+    case(f"sequential {name}")
+    inp = draw_preactivation_inputs(w)
+    S, h = gpu_lib.sequential_forward(inp["P"].to(DEV), inp["R"].to(DEV), None, w.forget)
+    torch.cuda.synchronize()
+    seq = lanes.sequential_lanes(inp["P"], inp["R"], None, w.forget)
+    h_seq = seq[:, :, 3].reshape(w.B, w.d_h, w.T).transpose(0, 2, 1)
+    assert h_rel_err(h, h_seq) < H_TOL_F32
+    assert torch.equal(h, S[..., 3, :])
+
+
+def test_zero_guess_diverges_on_both_sides(gpu_lib):
+    # the zero iterate overflows on a long exponential-forget sequence
+    w = by_name("mid_b8_t1024_d256")
+    case("newton zero init B=2 T=1024 d=32 K=3")
+    inp = draw_preactivation_inputs(w, B=2)
+    P = inp["P"][..., :32].contiguous()
+    R = inp["R"][:, :32].contiguous()
+    S, h, st, S_ref, st_ref = _run_both(gpu_lib, P, R, None, "exp", 3, init="zero")
+    assert st_ref.diverged and st.diverged
+    assert st.nonfinite == st_ref.nonfinite
+
+
+def test_nan_input_gives_nonfinite(gpu_lib):
+    w = by_name("tiny_b2_t64_d16")
+    case("newton NaN input")
+    inp = draw_preactivation_inputs(w)
+    P = inp["P"].clone()
+    P[1, 17, 1, 5] = float("nan")
+    S, h, st, S_ref, st_ref = _run_both(gpu_lib, P, inp["R"], None, w.forget, 3)
+    assert st.diverged and st.nonfinite and st_ref.diverged and st_ref.nonfinite
+    assert st.status == gpu_lib.NONFINITE
+    with pytest.raises(gpu_lib.NewtonDivergenceError):
+        gpu_lib.newton_forward(P.to(DEV), inp["R"].to(DEV), None, w.forget, 3)
+
+
+@pytest.mark.parametrize("B,T,d", [(2, 4096, 64), (1, 1000, 16)])
+def test_early_stop_sigmoid_bf16(gpu_lib, B, T, d):
+    w = by_name("sigmoid_bf16p_b16_t4096_d1024")
+    case(f"newton early stop {w.name} B={B} T={T} d={d}")
+    inp = draw_preactivation_inputs(w, B=B, T=T)
+    P = inp["P"][..., :d].contiguous()
+    R = inp["R"][:, :d].contiguous()
+    S, h, st, S_ref, st_ref = _run_both(gpu_lib, P, R, None, w.forget, w.max_iters, w.tol)
+    assert st_ref.converged and st.converged
+    assert st.iters == st_ref.iters
+    assert h_rel_err(h, S_ref[..., 3, :]) < H_TOL_BF16
+    # the GPU's residual history tracks the oracle's until the rounding floor
+    for k in range(st.iters):
+        assert st.max_abs_F[k] == pytest.approx(st_ref.max_abs_F[k], rel=0.05, abs=2e-5)
+
+
+def test_state_carry_across_calls(gpu_lib):
+    w = by_name("tiny_b2_t64_d16")
+    case("newton state carry T=64 as 32 + 32")
+    inp = draw_preactivation_inputs(w)
+    P = inp["P"].to(DEV)
+    R = inp["R"].to(DEV)
+    S_full, h_full, _ = gpu_lib.newton_forward(P, R, None, w.forget, 8)
+    S1, _, _ = gpu_lib.newton_forward(P[:, :32].contiguous(), R, None, w.forget, 8)
+    S2, h2, _ = gpu_lib.newton_forward(P[:, 32:].contiguous(), R, S1[:, -1].contiguous(), w.forget, 8)
+    torch.cuda.synchronize()
+    assert h_rel_err(h2, h_full[:, 32:]) < H_TOL_F32
+    Sq1, _ = gpu_lib.sequential_forward(P[:, :32].contiguous(), R, None, w.forget)
+    Sq2, hq2 = gpu_lib.sequential_forward(P[:, 32:].contiguous(), R, Sq1[:, -1].contiguous(), w.forget)
+    Sq, hq = gpu_lib.sequential_forward(P, R, None, w.forget)
+    torch.cuda.synchronize()
+    assert torch.equal(hq2, hq[:, 32:])
+
+
+def test_async_stats_readback(gpu_lib):
+    w = by_name("tiny_b2_t64_d16")
+    case("newton async + read_stats")
+    inp = draw_preactivation_inputs(w)
+    ws = torch.empty(gpu_lib.newton_workspace_bytes(w.B, w.T, w.d_h), dtype=torch.uint8, device=DEV)
+    S, h, st = gpu_lib.newton_forward(inp["P"].to(DEV), inp["R"].to(DEV), None, w.forget, 4,
+                                      workspace=ws, stats=False)
+    assert st is None
+    st = gpu_lib.read_stats(ws)
+    assert st.iters == 4 and not st.diverged and len(st.max_abs_F) == 5

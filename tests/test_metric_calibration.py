@@ -1,0 +1,60 @@
+"""Calibration of the h error metric against plain float32 arithmetic (CPU only).
+
+The bar on h is a relative error of 1e-4 for float32 state. Element-wise relative error needs
+a floor, since h crosses zero. This test runs the sLSTM recurrence as a plain float32 step
+loop -- the most direct float32 evaluation there is -- against the float64 oracle and shows
+that a floor of 1e-3 asks for more than float32 can deliver on the sigmoid-forget workload,
+while a floor of 1e-2 leaves a margin of several times under 1e-4.
+"""
+import numpy as np
+
+from oracle import slstm_ref as ref
+from parity import H_FLOOR
+from workloads import by_name, draw_preactivation_inputs
+
+f32 = np.float32
+
+
+def _float32_step_loop(P, R, forget):
+    P = P.astype(f32)
+    R = R.astype(f32)
+    B, T, _, d = P.shape
+    c = np.zeros((B, d), f32)
+    n = np.zeros((B, d), f32)
+    m = np.zeros((B, d), f32)
+    h = np.zeros((B, d), f32)
+    hs = np.empty((B, T, d), f32)
+    for t in range(T):
+        p = P[:, t]
+        z = np.tanh(p[:, 0] + R[0] * h)
+        it = p[:, 1] + R[1] * h
+        ft = p[:, 2] + R[2] * h
+        o = f32(1) / (f32(1) + np.exp(-(p[:, 3] + R[3] * h)))
+        lf = ft if forget == "exp" else (-np.logaddexp(f32(0), -ft)).astype(f32)
+        a = lf + m
+        mn = np.where(a >= it, a, it)
+        ig = np.exp(it - mn)
+        fg = np.exp(a - mn)
+        c = fg * c + ig * z
+        n = fg * n + ig
+        m = mn
+        h = o * c / n
+        hs[:, t] = h
+    return hs
+
+
+def _rel(a, b, floor):
+    return float(np.max(np.abs(a - b) / np.maximum(np.abs(b), floor)))
+
+
+def test_float32_meets_the_bar_only_with_the_chosen_floor():
+    w = by_name("sigmoid_bf16p_b16_t4096_d1024")
+    inp = draw_preactivation_inputs(w, B=2, T=4096)
+    P = inp["P"].double().numpy()[..., :256]
+    R = inp["R"].double().numpy()[:, :256]
+    h64 = ref.hidden(ref.sequential(P, R, None, w.forget))
+    with np.errstate(all="ignore"):
+        h32 = _float32_step_loop(P, R, w.forget)
+    assert _rel(h32, h64, 1e-3) > 1e-4      # a 1e-3 floor is beyond float32 here
+    assert _rel(h32, h64, H_FLOOR) < 3e-5   # the chosen floor: float32 passes with margin
+    assert float(np.max(np.abs(h32 - h64))) < 1e-6
