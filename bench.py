@@ -1,0 +1,341 @@
+#!/usr/bin/env python3
+"""Throughput of the Newton-parallel sLSTM forward on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input. For the
+full-layer workload (B=128, T=2048, d_in=d_h=1024, bf16 x and W_x):
+    bf16 MFMA input projection -> Newton forward (warm start, K x [residual + Jacobian,
+    4x4 scan, update], final residual, flags, h and final-state outputs) -> a T=1
+    sequential decode step at B=128 continuing from the final state (its own projection).
+For workloads whose solver input is P the step is the Newton forward alone.
+
+Prints ONE JSON line on stdout. Timing: W untimed warm-up steps, then exactly K steps
+between two device synchronisations, wall clock. Per-kernel durations come from HIP events
+the library records on the launching stream during the timed steps; the dominant kernel's
+algorithmic bytes per launch over its mean duration give the roofline figure. The CPU
+baseline times the float64 oracle on a bounded lane sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 10] [--warmup 2] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sLSTM Newton forward state-elems/s (B·T·d_h) + % HBM roofline, 1 MI355X"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------------------------------
+# algorithmic work per launch
+# ---------------------------------------------------------------------------------------
+# The solver's Jacobian planes: the 12 entries of each 4x4 block that are not structural
+# zeros of the channelwise cell ((c,n'), (n,c'), (m,c'), (m,n') are identically zero).
+JAC_BYTES = 12 * 4
+
+
+def kernel_work(w, n_e, p_bytes):
+    """Algorithmic bytes per launch of each kernel kind: every operand of every state
+    element read once and every result written once (per element: P p_bytes, a state 16,
+    a right-hand side / Newton step 16, the Jacobian JAC_BYTES)."""
+    return {
+        "warm_start": ("hbm", n_e * (p_bytes + 16)),                        # P in, S out
+        "residual_jacobian": ("hbm", n_e * (p_bytes + 16 + JAC_BYTES + 16)),  # P, S in; A, rhs out
+        "scan_block4": ("hbm", n_e * (JAC_BYTES + 16 + 16)),                # A, rhs in; Delta out
+        "update": ("hbm", n_e * 48),                                        # S, Delta in; S out
+        "final_residual": ("hbm", n_e * (p_bytes + 16)),                    # P, S in
+    }
+
+
+def source_sha(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "residual_jacobian": ["recurrent_nets_amd/csrc/k_residual.hip", "recurrent_nets_amd/csrc/cell.h",
+                          "recurrent_nets_amd/csrc/common.h"],
+    "scan_block4": ["recurrent_nets_amd/csrc/k_scan.hip", "recurrent_nets_amd/csrc/common.h"],
+    "update": ["recurrent_nets_amd/csrc/k_update.hip", "recurrent_nets_amd/csrc/common.h"],
+    "warm_start": ["recurrent_nets_amd/csrc/k_warm.hip", "recurrent_nets_amd/csrc/cell.h",
+                   "recurrent_nets_amd/csrc/common.h"],
+    "input_projection": ["recurrent_nets_amd/csrc/k_gemm.hip", "recurrent_nets_amd/csrc/common.h"],
+}
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when they were
+    taken on another workload or on an older version of the kernel's source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        data = json.load(f)
+    rec = data.get(kernel)
+    if not rec or rec.get("workload") != workload:
+        return None
+    if rec.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------------------
+# CPU baseline: the float64 oracle on a lane sample
+# ---------------------------------------------------------------------------------------
+_CPU = {}
+
+
+def _cpu_block(args):
+    from threadpoolctl import threadpool_limits
+    import numpy as np
+    from oracle import slstm_ref as ref
+    b, j0, j1 = args
+    w = _CPU["w"]
+    with threadpool_limits(1):
+        if "x" in _CPU:
+            x = _CPU["x"][b:b + 1].astype(np.float64)
+            P = ref.input_projection(x, _CPU["W"][:, j0:j1], _CPU["bias"][:, j0:j1])
+        else:
+            P = _CPU["P"][b:b + 1, :, :, j0:j1]
+        _, st = ref.newton(P, _CPU["R"][:, j0:j1], None, w.forget, w.max_iters, tol=w.tol)
+    return st.iters
+
+
+def cpu_baseline(w, host, lanes_wanted):
+    import multiprocessing as mp
+    import numpy as np
+    import torch
+    workers = max(1, min(16, os.cpu_count() or 1))
+    block = 256
+    per_b = w.d_h // block if w.d_h >= block else 1
+    blk = min(block, w.d_h)
+    tasks = []
+    for b in range(w.B):
+        for k in range(per_b):
+            tasks.append((b, k * blk, (k + 1) * blk))
+            if len(tasks) * blk >= lanes_wanted:
+                break
+        if len(tasks) * blk >= lanes_wanted:
+            break
+    n_lanes = len(tasks) * blk
+    _CPU.clear()
+    _CPU["w"] = w
+    _CPU["R"] = host["R"].double().numpy()
+    if "x" in host:
+        rows = sorted({t[0] for t in tasks})
+        xs = np.zeros((w.B, w.T, w.d_in), dtype=np.float32)
+        xs[rows] = host["x"][rows].float().numpy()
+        _CPU["x"] = xs
+        _CPU["W"] = host["W"].double().numpy()
+        _CPU["bias"] = host["bias"].double().numpy()
+    else:
+        _CPU["P"] = host["P"].double().numpy()
+    ctx = mp.get_context("fork")
+    t0 = time.perf_counter()
+    with ctx.Pool(processes=min(workers, len(tasks))) as pool:
+        pool.map(_cpu_block, tasks, chunksize=1)
+    dt = time.perf_counter() - t0
+    _CPU.clear()
+    elems = n_lanes * w.T
+    what = ("input projection + " if "x" in host else "") + f"Newton K={w.max_iters}"
+    return {"value": elems / dt, "unit": "state-elems/s", "cores": min(workers, len(tasks)),
+            "kind": "oracle",
+            "sample": f"{n_lanes} of {w.lanes} lanes (b, j) x full T={w.T}: float64 {what}, "
+                      f"{elems} state elements in {dt:.2f} s wall on {min(workers, len(tasks))} "
+                      f"single-threaded processes"}
+
+
+# ---------------------------------------------------------------------------------------
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="layer_b128_t2048_d1024")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-lanes", type=int, default=4096)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain device copy of 4 GiB (counter calibration runs)")
+    ap.add_argument("--no-sequential-context", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: this build runs the whole Newton solve on a single "
+              f"MI355X (requested --gpus {args.gpus}, WORLD_SIZE {world}). Multi-GPU runs are "
+              f"not part of it.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from recurrent_nets_amd import slstm
+    from workloads import by_name, draw_decode_inputs, draw_layer_inputs, draw_preactivation_inputs
+
+    w = by_name(args.workload)
+    dev = torch.device("cuda:0")
+    slstm.load()
+    log(f"[bench] workload {w.name}: generating inputs")
+    t_gen = time.perf_counter()
+    if w.on_gpu_gemm:
+        host = draw_layer_inputs(w)
+        x = host["x"].to(dev)
+        W = host["W"].to(dev)
+        bias = host["bias"].to(dev)
+        R = host["R"].to(dev)
+        P = torch.empty((w.B, w.T, 4, w.d_h), dtype=torch.float32, device=dev)
+        x_dec = draw_decode_inputs(w).to(dev)
+        P_dec = torch.empty((w.decode_batch, 1, 4, w.d_h), dtype=torch.float32, device=dev)
+        S_dec = torch.empty((w.decode_batch, 1, 4, w.d_h), dtype=torch.float32, device=dev)
+        H_dec = torch.empty((w.decode_batch, 1, w.d_h), dtype=torch.float32, device=dev)
+        p_bytes = 16
+    else:
+        host = draw_preactivation_inputs(w)
+        P = host["P"].to(dev)
+        R = host["R"].to(dev)
+        p_bytes = 8 if w.p_dtype == "bf16" else 16
+    log(f"[bench] inputs ready in {time.perf_counter() - t_gen:.1f} s")
+    S = torch.empty((w.B, w.T, 4, w.d_h), dtype=torch.float32, device=dev)
+    H = torch.empty((w.B, w.T, w.d_h), dtype=torch.float32, device=dev)
+    FS = torch.empty((w.B, 4, w.d_h), dtype=torch.float32, device=dev)
+    ws = slstm.alloc_workspace(slstm.newton_workspace_bytes(w.B, w.T, w.d_h), dev)
+    log(f"[bench] device memory in use {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+
+    if args.copy_calibration:
+        src = torch.empty(2**30, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        log("[bench] copy calibration: 3 copies of 4 GiB done")
+
+    def step():
+        if w.on_gpu_gemm:
+            slstm.input_projection(x, W, bias, out=P)
+        slstm.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, "warm", states=S, h_out=H,
+                             final_state=FS, workspace=ws, stats=False)
+        if w.on_gpu_gemm:
+            slstm.input_projection(x_dec, W, bias, out=P_dec)
+            slstm.sequential_forward(P_dec, R, FS, w.forget, states=S_dec, h_out=H_dec)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        log(f"[bench] warm-up step {i + 1}/{args.warmup} done")
+    st = slstm.read_stats(ws)
+    log(f"[bench] solver: iters {st.iters}, max|F| {['%.2e' % e for e in st.max_abs_F]}, "
+        f"diverged {st.diverged}")
+
+    torch.cuda.synchronize()
+    slstm.profile_reset()
+    slstm.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    slstm.profile_enable(False)
+    ms_per_step = (t1 - t0) * 1000.0 / args.steps
+    log(f"[bench] {args.steps} timed steps: {ms_per_step:.3f} ms/step")
+
+    n_e = w.state_elems
+    work = kernel_work(w, n_e, p_bytes)
+    kernels = {}
+    for kind, (bound, nbytes) in work.items():
+        d = slstm.profile_durations(kind)
+        if not d:
+            continue
+        avg = sum(d) / len(d)
+        kernels[kind] = {"launches": len(d), "avg_ms": avg, "total_ms_per_step": sum(d) / args.steps,
+                         "bytes_per_launch": nbytes, "GB_s": nbytes / (avg * 1e-3) / 1e9}
+    if w.on_gpu_gemm:
+        d = slstm.profile_durations("input_projection")
+        big = d[0::2]
+        small = d[1::2]
+        M, N, K = w.B * w.T, 4 * w.d_h, w.d_in
+        flops = 2.0 * M * N * K
+        avg = sum(big) / len(big)
+        kernels["input_projection"] = {"launches": len(big), "avg_ms": avg,
+                                       "total_ms_per_step": sum(big) / args.steps,
+                                       "flops_per_launch": flops,
+                                       "bytes_per_launch": M * K * 2 + N * K * 2 + M * N * 4,
+                                       "TFLOP_s": flops / (avg * 1e-3) / 1e12}
+        seqd = slstm.profile_durations("sequential")
+        kernels["decode"] = {"launches": len(seqd) + len(small),
+                             "total_ms_per_step": (sum(seqd) + sum(small)) / args.steps}
+    dominant = max((k for k in kernels if k in work), key=lambda k: kernels[k]["total_ms_per_step"])
+    dk = kernels[dominant]
+    achieved = dk["GB_s"]
+    traffic = measured_traffic(dominant, w.name)
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": traffic}
+
+    # whole-step roofline: every kernel at its own bound
+    t_roof = 0.0
+    for kind, k in kernels.items():
+        if kind in work:
+            t_roof += k["launches"] / args.steps * k["bytes_per_launch"] / (HBM_PEAK_GBS * 1e9)
+        elif kind == "input_projection":
+            t_roof += max(k["flops_per_launch"] / (BF16_PEAK_TFLOPS * 1e12),
+                          k["bytes_per_launch"] / (HBM_PEAK_GBS * 1e9))
+    value = n_e / (ms_per_step * 1e-3)
+
+    context = {"step_roofline_frac": round(t_roof / (ms_per_step * 1e-3), 4),
+               "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                               for kk, vv in v.items()} for k, v in kernels.items()},
+               "solver": {"iters": st.iters, "max_abs_F": st.max_abs_F, "diverged": st.diverged}}
+    if w.on_gpu_gemm:
+        gk = kernels["input_projection"]
+        context["gemm"] = {"TFLOP_s": round(gk["TFLOP_s"], 1), "peak": BF16_PEAK_TFLOPS,
+                           "frac": round(gk["TFLOP_s"] / BF16_PEAK_TFLOPS, 4),
+                           "traffic": measured_traffic("input_projection", w.name)}
+
+    if not args.no_sequential_context:
+        # the lane-parallel sequential forward on the same P, for context (not the metric)
+        slstm.sequential_forward(P, R, None, w.forget, states=S, h_out=H)
+        torch.cuda.synchronize()
+        reps = 5
+        ts = time.perf_counter()
+        for _ in range(reps):
+            slstm.sequential_forward(P, R, None, w.forget, states=S, h_out=H)
+        torch.cuda.synchronize()
+        seq_ms = (time.perf_counter() - ts) * 1000.0 / reps
+        context["sequential_forward"] = {"ms": round(seq_ms, 3),
+                                         "state_elems_per_s": n_e / (seq_ms * 1e-3)}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU baseline: float64 oracle on {args.cpu_lanes} lanes")
+        cpu = cpu_baseline(w, host, args.cpu_lanes)
+        log(f"[bench] CPU baseline: {cpu['value']:.3e} state-elems/s on {cpu['cores']} cores")
+
+    config = {"workload": w.name, "B": w.B, "T": w.T, "d_in": w.d_in, "d_h": w.d_h,
+              "newton_iters": w.max_iters, "tol": w.tol, "forget_gate": w.forget,
+              "preactivations": ("bf16 x, W_x -> float32 P on MFMA" if w.on_gpu_gemm else w.p_dtype),
+              "decode_batch": w.decode_batch, "init": "warm", "state_dtype": "f32"}
+    line = {"metric": METRIC, "value": value, "unit": "state-elems/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+            "data": "synthetic (seeded; shapes and distributions of the workload)",
+            "config": config, "roofline": roofline, "cpu_baseline": cpu, "context": context}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

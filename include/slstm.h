@@ -25,6 +25,9 @@
  *      state0   (B, 4, d_h) float32 initial state, slots (c, n, m, h); NULL means all zeros
  *      states   (B, T, 4, d_h) float32, slots (c, n, m, h); states[:, T-1] is the final state
  *      h_out    (B, T, d_h) float32, the hidden slot; optional (NULL skips it)
+ *      final_state (B, 4, d_h) float32, the last step's state (c, n, m, h) as a contiguous
+ *               tensor, ready to be the next call's state0 ([SL] "Outputs": return_hidden adds
+ *               the final state); optional (NULL skips it)
  *      A        (B, T, 4, 4, d_h) float32, A[b,t,row,col,j] = d s_t[row] / d s_{t-1}[col]
  *  - Every call enqueues work on `stream` (a hipStream_t; NULL is the default stream) and
  *    returns without waiting, unless stated otherwise.
@@ -97,7 +100,7 @@ size_t slstm_newton_workspace_bytes(int B, int T, int d_h);
  *  P, P_dtype   gate pre-activations (B, T, 4, d_h), float32 or bf16
  *  R            (4, d_h); state0 (B, 4, d_h) or NULL
  *  states       output (B, T, 4, d_h); also the Newton iterate while solving
- *  h_out        optional output (B, T, d_h)
+ *  h_out        optional output (B, T, d_h); final_state optional output (B, 4, d_h)
  *  fmode        forget-gate form; max_iters in 1..64; tol >= 0 (0: fixed iteration count)
  *  init         SLSTM_INIT_WARM (default reading) or SLSTM_INIT_ZERO
  *  workspace    >= slstm_newton_workspace_bytes(B, T, d_h) bytes of device memory; holds the
@@ -108,8 +111,9 @@ size_t slstm_newton_workspace_bytes(int B, int T, int d_h);
  *               SLSTM_NONFINITE when the flags say so (outputs are still written).
  */
 slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const float* R,
-                                  const float* state0, float* states, float* h_out, int B, int T,
-                                  int d_h, slstm_forget fmode, int max_iters, float tol,
+                                  const float* state0, float* states, float* h_out,
+                                  float* final_state, int B, int T, int d_h, slstm_forget fmode,
+                                  int max_iters, float tol,
                                   slstm_init init, void* workspace, size_t workspace_bytes,
                                   void* stream, slstm_newton_stats* stats);
 
@@ -124,8 +128,9 @@ slstm_status slstm_newton_read_stats(const void* workspace, size_t workspace_byt
  * as slstm_newton_forward; needs no workspace.
  */
 slstm_status slstm_sequential_forward(const void* P, slstm_dtype P_dtype, const float* R,
-                                      const float* state0, float* states, float* h_out, int B,
-                                      int T, int d_h, slstm_forget fmode, void* stream);
+                                      const float* state0, float* states, float* h_out,
+                                      float* final_state, int B, int T, int d_h,
+                                      slstm_forget fmode, void* stream);
 
 /*
  * Input projection on the MFMA matrix cores ([SL] "API notes": W_x is a GEMM; [XL]
@@ -193,6 +198,10 @@ typedef enum {
 slstm_status slstm_profile_enable(int on);
 slstm_status slstm_profile_reset(void);
 slstm_status slstm_profile_read(slstm_kernel_kind kind, double* total_ms, int* launches);
+/* The individual durations (ms, in launch order) of one kernel kind since the last reset:
+ * writes min(count, capacity) values to out_ms and the full count to *launches. */
+slstm_status slstm_profile_durations(slstm_kernel_kind kind, double* out_ms, int capacity,
+                                     int* launches);
 
 #ifdef __cplusplus
 }

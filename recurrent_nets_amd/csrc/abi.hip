@@ -98,6 +98,10 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 slstm_status check_dims(int B, int T, int d) {
   if (B < 1 || T < 1 || d < 1) return fail(SLSTM_EINVAL, "B, T, d_h must be >= 1 (got %d, %d, %d)", B, T, d);
+  // grid limits of the kernels' launch shapes (batch and time on grid dimensions of <= 65535
+  // blocks) and 32-bit byte offsets inside one tile's rows (a scan tile spans 2 KiB * d_h)
+  if (B > 65535 || T > (1 << 22) || d > (1 << 20))
+    return fail(SLSTM_EINVAL, "B <= 65535, T <= 4194304 and d_h <= 1048576 required (got %d, %d, %d)", B, T, d);
   // the largest tensor, A, has B*T*16*d floats; keep every element offset well inside int64
   const double elems = 16.0 * B * T * d;
   if (elems > 4.0e15) return fail(SLSTM_EINVAL, "sizes too large");
@@ -110,7 +114,7 @@ struct NewtonLayout {
 
 NewtonLayout newton_layout(int B, int T, int d) {
   NewtonLayout L;
-  const size_t desc_words = std::max(slstm::scan_desc_words(B, T, d), slstm::warm_desc_words(B, T, d));
+  const size_t desc_words = std::max(slstm::scan_desc_words(B, T, d, true), slstm::warm_desc_words(B, T, d));
   const size_t n_state = static_cast<size_t>(B) * T * 4 * d;
   L.ctl = 0;
   L.desc = align_up(sizeof(Control));
@@ -138,8 +142,8 @@ T* at(void* base, size_t off) {
 }
 
 slstm_status check_common(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
-                          const float* states, const float* h_out, int B, int T, int d,
-                          slstm_forget fmode) {
+                          const float* states, const float* h_out, const float* final_state, int B,
+                          int T, int d, slstm_forget fmode) {
   slstm_status s = check_dims(B, T, d);
   if (s != SLSTM_OK) return s;
   if (P == nullptr || R == nullptr || states == nullptr)
@@ -149,7 +153,8 @@ slstm_status check_common(const void* P, slstm_dtype P_dtype, const float* R, co
     return fail(SLSTM_EINVAL, "unknown forget mode %d", (int)fmode);
   if (!aligned(P, P_dtype == SLSTM_F32 ? 4 : 2) || !aligned(R, 4) || !aligned(state0, 4))
     return fail(SLSTM_EINVAL, "P, R or state0 misaligned");
-  if (!aligned(states, 16) || !aligned(h_out, 16)) return fail(SLSTM_EINVAL, "states and h_out must be 16-byte aligned");
+  if (!aligned(states, 16) || !aligned(h_out, 16) || !aligned(final_state, 16))
+    return fail(SLSTM_EINVAL, "states, h_out and final_state must be 16-byte aligned");
   return SLSTM_OK;
 }
 
@@ -173,6 +178,23 @@ __global__ void store_u32_kernel(unsigned int* p, unsigned int v) { *p = v; }
 
 }  // namespace
 
+namespace slstm {
+
+int look_back_anchor_stride(long long n_lane_groups) {
+  static int resident = [] {
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+      int v = 0;
+      if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
+    }
+    return 2 * cus;  // two look-back workgroups fit on a compute unit
+  }();
+  long long s = (resident + n_lane_groups - 1) / n_lane_groups;
+  return static_cast<int>(s < 1 ? 1 : (s > 8 ? 8 : s));
+}
+
+}  // namespace slstm
+
 extern "C" {
 
 const char* slstm_status_string(slstm_status s) {
@@ -195,12 +217,13 @@ size_t slstm_newton_workspace_bytes(int B, int T, int d_h) {
 }
 
 slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const float* R,
-                                  const float* state0, float* states, float* h_out, int B, int T,
-                                  int d_h, slstm_forget fmode, int max_iters, float tol,
+                                  const float* state0, float* states, float* h_out,
+                                  float* final_state, int B, int T, int d_h, slstm_forget fmode,
+                                  int max_iters, float tol,
                                   slstm_init init, void* workspace, size_t workspace_bytes,
                                   void* stream, slstm_newton_stats* stats) {
   g_err[0] = '\0';
-  slstm_status s = check_common(P, P_dtype, R, state0, states, h_out, B, T, d_h, fmode);
+  slstm_status s = check_common(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, fmode);
   if (s != SLSTM_OK) return s;
   if (max_iters < 1 || max_iters > SLSTM_MAX_ITERS)
     return fail(SLSTM_EINVAL, "max_iters must be in 1..%d (got %d)", SLSTM_MAX_ITERS, max_iters);
@@ -233,20 +256,22 @@ slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const floa
   for (int k = 0; k < max_iters; ++k) {
     HIP_TRY(timed(SLSTM_KERNEL_RESIDUAL_JACOBIAN, st, [&] {
       return slstm::launch_residual(P, bf16, R, state0, states, A, rhs, B, T, d_h, sig, ctl,
-                                    &ctl->err_bits[k], true, st);
+                                    &ctl->err_bits[k], slstm::ResidualMode::kSparse, st);
     }));
     const uint32_t ep = next_epoch();
     HIP_TRY(timed(SLSTM_KERNEL_SCAN_BLOCK4, st, [&] {
-      return slstm::launch_scan_block4(A, rhs, rhs, B, T, d_h, desc, &ctl->ticket_scan, ep, ctl, k, tol, st);
+      return slstm::launch_scan_block4(A, rhs, rhs, B, T, d_h, true, desc, &ctl->ticket_scan, ep, ctl, k,
+                                       tol, st);
     }));
     HIP_TRY(timed(SLSTM_KERNEL_UPDATE, st, [&] { return slstm::launch_update(states, rhs, n_state, ctl, k, st); }));
   }
   HIP_TRY(timed(SLSTM_KERNEL_FINAL_RESIDUAL, st, [&] {
     return slstm::launch_residual(P, bf16, R, state0, states, nullptr, nullptr, B, T, d_h, sig, ctl,
-                                  &ctl->err_bits[max_iters], false, st);
+                                  &ctl->err_bits[max_iters], slstm::ResidualMode::kNone, st);
   }));
   HIP_TRY(slstm::launch_finalize(ctl, tol, st));
-  if (h_out != nullptr) HIP_TRY(slstm::launch_hidden(states, h_out, B, T, d_h, st));
+  if (h_out != nullptr || final_state != nullptr)
+    HIP_TRY(slstm::launch_outputs(states, h_out, final_state, B, T, d_h, st));
   if (stats == nullptr) return SLSTM_OK;
   Control host;
   HIP_TRY(hipMemcpyAsync(&host, ctl, sizeof(Control), hipMemcpyDeviceToHost, st));
@@ -267,15 +292,16 @@ slstm_status slstm_newton_read_stats(const void* workspace, size_t workspace_byt
 }
 
 slstm_status slstm_sequential_forward(const void* P, slstm_dtype P_dtype, const float* R,
-                                      const float* state0, float* states, float* h_out, int B,
-                                      int T, int d_h, slstm_forget fmode, void* stream) {
+                                      const float* state0, float* states, float* h_out,
+                                      float* final_state, int B, int T, int d_h,
+                                      slstm_forget fmode, void* stream) {
   g_err[0] = '\0';
-  slstm_status s = check_common(P, P_dtype, R, state0, states, h_out, B, T, d_h, fmode);
+  slstm_status s = check_common(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, fmode);
   if (s != SLSTM_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   HIP_TRY(timed(SLSTM_KERNEL_SEQUENTIAL, st, [&] {
-    return slstm::launch_sequential(P, P_dtype == SLSTM_BF16, R, state0, states, h_out, B, T, d_h,
-                                    fmode == SLSTM_FORGET_SIGMOID, st);
+    return slstm::launch_sequential(P, P_dtype == SLSTM_BF16, R, state0, states, h_out, final_state,
+                                    B, T, d_h, fmode == SLSTM_FORGET_SIGMOID, st);
   }));
   return SLSTM_OK;
 }
@@ -304,7 +330,7 @@ slstm_status slstm_residual_jacobian(const void* P, slstm_dtype P_dtype, const f
                                      float* rhs, float* max_abs_F, int B, int T, int d_h,
                                      slstm_forget fmode, void* stream) {
   g_err[0] = '\0';
-  slstm_status s = check_common(P, P_dtype, R, state0, states, nullptr, B, T, d_h, fmode);
+  slstm_status s = check_common(P, P_dtype, R, state0, states, nullptr, nullptr, B, T, d_h, fmode);
   if (s != SLSTM_OK) return s;
   if (A == nullptr || rhs == nullptr || max_abs_F == nullptr)
     return fail(SLSTM_EINVAL, "A, rhs and max_abs_F must not be NULL");
@@ -315,14 +341,14 @@ slstm_status slstm_residual_jacobian(const void* P, slstm_dtype P_dtype, const f
   HIP_TRY(hipGetLastError());
   HIP_TRY(timed(SLSTM_KERNEL_RESIDUAL_JACOBIAN, st, [&] {
     return slstm::launch_residual(P, P_dtype == SLSTM_BF16, R, state0, states, A, rhs, B, T, d_h,
-                                  fmode == SLSTM_FORGET_SIGMOID, nullptr, err, true, st);
+                                  fmode == SLSTM_FORGET_SIGMOID, nullptr, err, slstm::ResidualMode::kDense, st);
   }));
   return SLSTM_OK;
 }
 
 size_t slstm_scan_block4_workspace_bytes(int B, int T, int d_h) {
   if (check_dims(B, T, d_h) != SLSTM_OK) return 0;
-  return scan_layout(slstm::scan_desc_words(B, T, d_h)).total;
+  return scan_layout(slstm::scan_desc_words(B, T, d_h, false)).total;
 }
 
 slstm_status slstm_scan_block4(const float* A, const float* rhs, float* x, int B, int T, int d_h,
@@ -333,14 +359,14 @@ slstm_status slstm_scan_block4(const float* A, const float* rhs, float* x, int B
   if (A == nullptr || rhs == nullptr || x == nullptr) return fail(SLSTM_EINVAL, "A, rhs and x must not be NULL");
   if (!aligned(A, 4) || !aligned(rhs, 4) || !aligned(x, 4)) return fail(SLSTM_EINVAL, "A, rhs or x misaligned");
   if (workspace == nullptr || !aligned(workspace, kAlign)) return fail(SLSTM_EINVAL, "workspace must be 256-byte aligned");
-  const ScanLayout L = scan_layout(slstm::scan_desc_words(B, T, d_h));
+  const ScanLayout L = scan_layout(slstm::scan_desc_words(B, T, d_h, false));
   if (workspace_bytes < L.total) return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
   hipStream_t st = static_cast<hipStream_t>(stream);
   Control* ctl = at<Control>(workspace, L.ctl);
   HIP_TRY(slstm::launch_init_control(ctl, st));
   const uint32_t ep = next_epoch();
   HIP_TRY(timed(SLSTM_KERNEL_SCAN_BLOCK4, st, [&] {
-    return slstm::launch_scan_block4(A, rhs, x, B, T, d_h, at<unsigned long long>(workspace, L.desc),
+    return slstm::launch_scan_block4(A, rhs, x, B, T, d_h, false, at<unsigned long long>(workspace, L.desc),
                                      &ctl->ticket_scan, ep, nullptr, 0, 0.0f, st);
   }));
   return SLSTM_OK;
@@ -356,7 +382,7 @@ slstm_status slstm_warm_start(const void* P, slstm_dtype P_dtype, const float* s
                               void* workspace, size_t workspace_bytes, void* stream) {
   g_err[0] = '\0';
   static const float kDummyR = 0.0f;  // R is not used by the warm start; the shared check wants one
-  slstm_status s = check_common(P, P_dtype, &kDummyR, state0, states, nullptr, B, T, d_h, fmode);
+  slstm_status s = check_common(P, P_dtype, &kDummyR, state0, states, nullptr, nullptr, B, T, d_h, fmode);
   if (s != SLSTM_OK) return s;
   if (workspace == nullptr || !aligned(workspace, kAlign)) return fail(SLSTM_EINVAL, "workspace must be 256-byte aligned");
   const ScanLayout L = scan_layout(slstm::warm_desc_words(B, T, d_h));
@@ -398,6 +424,25 @@ slstm_status slstm_profile_read(slstm_kernel_kind kind, double* total_ms, int* l
     ++n;
   }
   *total_ms = sum;
+  *launches = n;
+  return SLSTM_OK;
+}
+
+slstm_status slstm_profile_durations(slstm_kernel_kind kind, double* out_ms, int capacity,
+                                     int* launches) {
+  g_err[0] = '\0';
+  if (launches == nullptr || (capacity > 0 && out_ms == nullptr)) return fail(SLSTM_EINVAL, "NULL output");
+  int n = 0;
+  for (auto& r : g_prof.recs) {
+    if (r.kind != static_cast<int>(kind)) continue;
+    if (n < capacity) {
+      HIP_TRY(hipEventSynchronize(r.b));
+      float ms = 0.0f;
+      HIP_TRY(hipEventElapsedTime(&ms, r.a, r.b));
+      out_ms[n] = ms;
+    }
+    ++n;
+  }
   *launches = n;
   return SLSTM_OK;
 }

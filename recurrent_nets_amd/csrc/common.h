@@ -24,6 +24,33 @@ __device__ __forceinline__ float load_p(const void* __restrict__ P, i64 idx) {
   }
 }
 
+// ---- buffer resources -------------------------------------------------------------------------
+// A buffer resource holds a wave-uniform base address in scalar registers; each access adds a
+// 32-bit per-lane byte offset (one VGPR) and a wave-uniform byte offset (an SGPR). Kernels that
+// issue many loads from rows at uniform strides keep one VGPR per stream instead of a 64-bit
+// address per load. The third descriptor word is the raw-buffer setting of the gfx9 family.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), -1,
+                                           0x00020000);
+}
+__device__ __forceinline__ float buf_ld(rsrc_t r, unsigned voff_bytes, unsigned soff_bytes) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, voff_bytes, soff_bytes, 0));
+}
+__device__ __forceinline__ void buf_st(float v, rsrc_t r, unsigned voff_bytes, unsigned soff_bytes) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, voff_bytes, soff_bytes, 0);
+}
+// gate pre-activation at element offsets (lane part, uniform part) of a float32 or bf16 tensor
+template <bool BF16>
+__device__ __forceinline__ float buf_ld_p(rsrc_t r, unsigned voff_elems, unsigned soff_elems) {
+  if constexpr (BF16) {
+    return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, 2u * voff_elems, 2u * soff_elems, 0));
+  } else {
+    return buf_ld(r, 4u * voff_elems, 4u * soff_elems);
+  }
+}
+
 // |x| for the residual maximum; NaN counts as +inf so that a max reduction cannot drop it.
 __device__ __forceinline__ float abs_nan_inf(float x) {
   float a = fabsf(x);
@@ -65,6 +92,14 @@ __device__ __forceinline__ bool tag_load(const unsigned long long* p, uint32_t e
   v = __uint_as_float(static_cast<uint32_t>(w));
   return static_cast<uint32_t>(w >> 32) == epoch;
 }
+
+// Anchor stride of the look-back along T: tiles of one lane group are n_lg work tickets
+// apart, so when the lane groups outnumber the workgroups resident on the GPU a predecessor
+// has finished before its successor starts and a plain chain (stride 1) never waits. With few
+// lane groups several tiles of a chain run at once, and every stride-th tile anchors the
+// chain, so a tile waits on at most one anchor and on aggregates published before any wait.
+// A function of the shape and the device alone, so results stay reproducible.
+int look_back_anchor_stride(long long n_lane_groups);
 
 // Solver control block kept at the start of the workspace.
 struct Control {

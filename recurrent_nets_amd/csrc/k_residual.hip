@@ -6,126 +6,149 @@
 // the per-feature 4x4 Jacobian in the scan_block4 layout (B, T, 4, 4, d), "Naming").
 // The maximum of |F| over the launch is folded into one device word (NaN counts as +inf).
 //
-// Mapping: one thread owns one lane and a chunk of CHUNK consecutive steps; consecutive
-// threads are consecutive lanes, so every load and store of a wave covers 64 consecutive
-// features of one (b, t, plane) row. The previous state of a chunk's first step is the one
-// halo read; after that each state is loaded once and reused as the next step's s'.
+// Jacobian planes written:
+//   kJacDense   all 16 planes of each 4x4 block;
+//   kJacSparse  the 12 planes that are not structural zeros of the channelwise cell
+//               ((c, n'), (n, c'), (m, c'), (m, n') are never written); the Newton solver's
+//               scan reads exactly these;
+//   kJacNone    no Jacobian and no right-hand side: the residual maximum only.
+//
+// Mapping: grid (feature tiles of 64, groups of 4 time chunks, batch). Each wave owns 64
+// consecutive features of one batch row and one chunk of kResChunk consecutive steps, so
+// (b, t) are wave-uniform: every access is a scalar row base plus a 32-bit lane offset, and
+// every load or store of a wave covers 256 contiguous bytes of one (b, t, plane) row. The
+// previous state of a chunk's first step is the one halo read; after that each state is
+// loaded once and reused as the next step's s'.
 #include "cell.h"
 #include "kernels.h"
 
 namespace slstm {
 
 constexpr int kResChunk = 16;
-constexpr int kResUnroll = 2;
-constexpr int kResBlock = 256;
+constexpr int kResWaves = 4;
+constexpr int kResBlock = kResWaves * kWave;
 
-template <bool BF16, bool JAC>
-__global__ __launch_bounds__(kResBlock, 4) void residual_kernel(
+enum { kJacNone = 0, kJacSparse = 1, kJacDense = 2 };
+
+// row-major 4x4 positions written in the sparse form (all but the four structural zeros)
+__device__ constexpr int kSparsePlanes[12] = {0, 2, 3, 5, 6, 7, 10, 11, 12, 13, 14, 15};
+
+template <bool BF16, int JMODE>
+__global__ __launch_bounds__(kResBlock, 2) void residual_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
-    const float* __restrict__ S, float* __restrict__ A, float* __restrict__ rhs, int B, int T,
-    int d, int n_chunks, int sig_forget, const Control* __restrict__ ctl,
+    const float* __restrict__ S, float* __restrict__ A, float* __restrict__ rhs, int T, int d,
+    int n_chunks, int sig_forget, const Control* __restrict__ ctl,
     unsigned int* __restrict__ err_dst) {
   if (ctl != nullptr && ctl->stopped) return;
-  const i64 n_lanes = static_cast<i64>(B) * d;
-  const i64 g = static_cast<i64>(blockIdx.x) * kResBlock + threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l = threadIdx.x & (kWave - 1);
+  const int b = blockIdx.z;
+  const int chunk = blockIdx.y * kResWaves + wave;
+  const unsigned j = blockIdx.x * kWave + l;
   float fmax_local = 0.0f;
-  if (g < n_lanes * n_chunks) {
-    const i64 lane = g % n_lanes;
-    const int ch = static_cast<int>(g / n_lanes);
-    const int b = static_cast<int>(lane / d);
-    const int j = static_cast<int>(lane % d);
-    const int t0 = ch * kResChunk;
+  if (chunk < n_chunks && j < static_cast<unsigned>(d)) {
+    const unsigned ud = static_cast<unsigned>(d);
+    const int t0 = chunk * kResChunk;
     const int t1 = min(T, t0 + kResChunk);
-    const float rz = R[j], ri = R[d + j], rf = R[2 * d + j], ro = R[3 * d + j];
+    const float rz = R[j], ri = R[ud + j], rf = R[2 * ud + j], ro = R[3 * ud + j];
     const bool sig = sig_forget != 0;
-    const i64 d4 = 4 * static_cast<i64>(d);
-    const i64 lane_base = static_cast<i64>(b) * T * d4 + j;  // (b, t=0, slot 0, j)
+    const i64 row4 = 4 * static_cast<i64>(d);  // floats per (b, t) row of a state tensor
+    const float* Sb = S + static_cast<i64>(b) * T * row4;
     CellIn pv;
     if (t0 == 0) {
       if (state0 != nullptr) {
-        const float* s0 = state0 + static_cast<i64>(b) * d4 + j;
-        pv = {s0[0], s0[d], s0[2 * d], s0[3 * d]};
+        const float* s0 = state0 + static_cast<i64>(b) * row4;
+        pv = {s0[j], s0[ud + j], s0[2 * ud + j], s0[3 * ud + j]};
       } else {
         pv = {0.0f, 0.0f, 0.0f, 0.0f};
       }
     } else {
-      const float* sp = S + lane_base + static_cast<i64>(t0 - 1) * d4;
-      pv = {sp[0], sp[d], sp[2 * d], sp[3 * d]};
+      const float* sp = Sb + static_cast<i64>(t0 - 1) * row4;
+      pv = {sp[j], sp[ud + j], sp[2 * ud + j], sp[3 * ud + j]};
     }
-    for (int tb = t0; tb < t1; tb += kResUnroll) {
-      float pg[kResUnroll][4], st[kResUnroll][4];
-      // issue every load of the group before any arithmetic
+    // next step's operands are loaded one step ahead
+    float pn[4], sn[4];
+    auto load_step = [&](int t, float (&pg)[4], float (&st)[4]) {
+      const i64 row = static_cast<i64>(b) * T + t;
 #pragma unroll
-      for (int u = 0; u < kResUnroll; ++u) {
-        const int t = tb + u;
-        const i64 base = lane_base + static_cast<i64>(t) * d4;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          pg[u][k] = (t < t1) ? load_p<BF16>(P, base + k * d) : 0.0f;
-          st[u][k] = (t < t1) ? S[base + k * d] : 0.0f;
-        }
+      for (int k = 0; k < 4; ++k) {
+        pg[k] = load_p<BF16>(P, row * row4 + k * ud + j);
+        st[k] = Sb[static_cast<i64>(t) * row4 + k * ud + j];
       }
+    };
+    load_step(t0, pn, sn);
+    for (int t = t0; t < t1; ++t) {
+      float pg[4], st[4];
 #pragma unroll
-      for (int u = 0; u < kResUnroll; ++u) {
-        const int t = tb + u;
-        if (t < t1) {
-          float f[4], Aj[16];
-          cell_step<JAC>(pv, pg[u][0], pg[u][1], pg[u][2], pg[u][3], rz, ri, rf, ro, sig, f, Aj);
-          const i64 base = lane_base + static_cast<i64>(t) * d4;
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float F = st[u][k] - f[k];
-            fmax_local = fmaxf(fmax_local, abs_nan_inf(F));
-            if constexpr (JAC) rhs[base + k * d] = -F;
-          }
-          if constexpr (JAC) {
-            float* Ap = A + (static_cast<i64>(b) * T + t) * 16 * static_cast<i64>(d) + j;
-#pragma unroll
-            for (int e = 0; e < 16; ++e) Ap[static_cast<i64>(e) * d] = Aj[e];
-          }
-          pv = {st[u][0], st[u][1], st[u][2], st[u][3]};
-        }
+      for (int k = 0; k < 4; ++k) {
+        pg[k] = pn[k];
+        st[k] = sn[k];
       }
+      if (t + 1 < t1) load_step(t + 1, pn, sn);
+      float f[4], Aj[16];
+      cell_step<JMODE != kJacNone>(pv, pg[0], pg[1], pg[2], pg[3], rz, ri, rf, ro, sig, f, Aj);
+      const i64 row = static_cast<i64>(b) * T + t;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float F = st[k] - f[k];
+        fmax_local = fmaxf(fmax_local, abs_nan_inf(F));
+        if constexpr (JMODE != kJacNone) rhs[row * row4 + k * ud + j] = -F;
+      }
+      if constexpr (JMODE == kJacDense) {
+        float* Ap = A + row * 16 * static_cast<i64>(d);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) Ap[e * ud + j] = Aj[e];
+      } else if constexpr (JMODE == kJacSparse) {
+        float* Ap = A + row * 16 * static_cast<i64>(d);
+#pragma unroll
+        for (int q = 0; q < 12; ++q) Ap[kSparsePlanes[q] * ud + j] = Aj[kSparsePlanes[q]];
+      }
+      pv = {st[0], st[1], st[2], st[3]};
     }
   }
   // block maximum, then one device-wide atomic per block
-  __shared__ float s_max[kResBlock / kWave];
+  __shared__ float s_max[kResWaves];
   const float wm = wave_max(fmax_local);
-  if ((threadIdx.x & (kWave - 1)) == 0) s_max[threadIdx.x / kWave] = wm;
+  if (l == 0) s_max[wave] = wm;
   __syncthreads();
   if (threadIdx.x == 0) {
     float m = s_max[0];
 #pragma unroll
-    for (int w = 1; w < kResBlock / kWave; ++w) m = fmaxf(m, s_max[w]);
+    for (int w = 1; w < kResWaves; ++w) m = fmaxf(m, s_max[w]);
     atomic_max_nonneg(err_dst, m);
   }
+}
+
+template <bool BF16>
+static void launch_mode(int mode, dim3 grid, hipStream_t stream, const void* P, const float* R,
+                        const float* state0, const float* S, float* A, float* rhs, int T, int d,
+                        int n_chunks, int sig, const Control* ctl, unsigned int* err_dst) {
+  if (mode == kJacDense)
+    residual_kernel<BF16, kJacDense><<<grid, kResBlock, 0, stream>>>(P, R, state0, S, A, rhs, T, d,
+                                                                      n_chunks, sig, ctl, err_dst);
+  else if (mode == kJacSparse)
+    residual_kernel<BF16, kJacSparse><<<grid, kResBlock, 0, stream>>>(P, R, state0, S, A, rhs, T, d,
+                                                                       n_chunks, sig, ctl, err_dst);
+  else
+    residual_kernel<BF16, kJacNone><<<grid, kResBlock, 0, stream>>>(P, R, state0, S, nullptr, nullptr,
+                                                                     T, d, n_chunks, sig, ctl, err_dst);
 }
 
 hipError_t launch_residual(const void* P, bool p_bf16, const float* R, const float* state0,
                            const float* S, float* A, float* rhs, int B, int T, int d,
                            bool sig_forget, const Control* ctl, unsigned int* err_dst,
-                           bool with_jacobian, hipStream_t stream) {
+                           ResidualMode mode, hipStream_t stream) {
   const int n_chunks = (T + kResChunk - 1) / kResChunk;
-  const i64 threads = static_cast<i64>(B) * d * n_chunks;
-  const i64 blocks = (threads + kResBlock - 1) / kResBlock;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  const dim3 grid(static_cast<unsigned>(blocks));
+  const unsigned gx = static_cast<unsigned>((d + kWave - 1) / kWave);
+  const unsigned gy = static_cast<unsigned>((n_chunks + kResWaves - 1) / kResWaves);
+  if (B > 65535 || gy > 65535u) return hipErrorInvalidValue;
+  const dim3 grid(gx, gy, static_cast<unsigned>(B));
   const int sig = sig_forget ? 1 : 0;
-  if (with_jacobian) {
-    if (p_bf16)
-      residual_kernel<true, true><<<grid, kResBlock, 0, stream>>>(P, R, state0, S, A, rhs, B, T, d,
-                                                                  n_chunks, sig, ctl, err_dst);
-    else
-      residual_kernel<false, true><<<grid, kResBlock, 0, stream>>>(P, R, state0, S, A, rhs, B, T, d,
-                                                                   n_chunks, sig, ctl, err_dst);
-  } else {
-    if (p_bf16)
-      residual_kernel<true, false><<<grid, kResBlock, 0, stream>>>(P, R, state0, S, nullptr, nullptr,
-                                                                   B, T, d, n_chunks, sig, ctl, err_dst);
-    else
-      residual_kernel<false, false><<<grid, kResBlock, 0, stream>>>(
-          P, R, state0, S, nullptr, nullptr, B, T, d, n_chunks, sig, ctl, err_dst);
-  }
+  const int m = mode == ResidualMode::kDense ? kJacDense : (mode == ResidualMode::kSparse ? kJacSparse : kJacNone);
+  if (p_bf16)
+    launch_mode<true>(m, grid, stream, P, R, state0, S, A, rhs, T, d, n_chunks, sig, ctl, err_dst);
+  else
+    launch_mode<false>(m, grid, stream, P, R, state0, S, A, rhs, T, d, n_chunks, sig, ctl, err_dst);
   return hipGetLastError();
 }
 

@@ -6,9 +6,11 @@
 //
 // Each step is the map x -> A x + r; maps compose as (A2, r2) o (A1, r1) = (A2 A1, A2 r1 + r2).
 //
-// Work decomposition (one workgroup = 4 waves = one tile of 64 lanes x 4*TSUB steps):
-//   * lane   = flattened (b, j); a tile covers 64 consecutive lanes, so each load of the tile
-//              reads 256 contiguous bytes of one (b, t, plane) row;
+// Work decomposition (one workgroup = 4 waves = one tile of 64 features of one batch row x
+// 4*TSUB steps):
+//   * lane   = (b, j); a tile covers 64 consecutive features of one batch row, so each load
+//              of the tile reads 256 contiguous bytes of one (b, t, plane) row, and b is
+//              uniform over the workgroup (scalar row bases, 32-bit lane offsets);
 //   * thread = one lane and one sub-chunk of TSUB steps; a wave holds 16 lanes x 4
 //              consecutive sub-chunks, the 4 sub-chunks of a lane forming one quad.
 // Level 1: every thread composes its sub-chunk sequentially in registers (A and r stay in
@@ -16,30 +18,27 @@
 // Level 2: inclusive scan of the 4 sub-chunk aggregates inside each quad with DPP quad
 //          permutations; the tile aggregate of each lane is staged in LDS.
 // Level 3: decoupled look-back across tiles along T: wave 0 (one thread per lane) publishes
-//          the tile aggregate, walks back over predecessor tiles until it meets an inclusive
-//          value, and stages the resulting carry in LDS. Tiles take work tickets in launch
-//          order, so a predecessor always holds a smaller ticket and is running or done.
-// Finally every thread re-runs its sub-chunk from its carry (16 FMA per step) and stores x.
+//          the tile aggregate, folds its predecessors' aggregates down to the nearest anchor
+//          tile, applies the anchor's inclusive value and stages the carry in LDS. The fold
+//          order is fixed, so results are bitwise reproducible. Tiles take work tickets in
+//          launch order, so a predecessor always holds a smaller ticket and is running or done.
+// Finally every thread re-runs its sub-chunk from its carry and stores x.
 // x may alias rhs: each thread reads its rhs values before writing the same addresses.
+//
+// SPARSE: the sLSTM Jacobian has four structural zeros ((c, n'), (n, c'), (m, c'), (m, n'));
+// the Newton solver's scan reads only the other 12 planes and multiplies with them alone
+// (48 instead of 64 FMA per 4x4 product). The dense form serves arbitrary 4x4 maps.
 #include "common.h"
 #include "kernels.h"
 
 namespace slstm {
 
 constexpr int kScanBlock = 256;
-constexpr int kScanTSub = 8;
-constexpr int kScanTile = 4 * kScanTSub;
-constexpr int kScanWords = 24;  // per lane and tile: x_end (4), M (16), v (4)
+constexpr int kScanTSubSparse = 8;  // sub-chunk length of the Newton solver's sparse scan
+constexpr int kScanTSubDense = 4;   // and of the dense scan (16 values per step in registers)
+constexpr int kScanWords = 24;      // per lane and tile: x_end (4), M (16), v (4)
 
-// C = X Y for row-major 4x4 matrices
-__device__ __forceinline__ void mat4_mul(const float X[16], const float Y[16], float C[16]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      C[4 * i + k] = fmaf(X[4 * i + 0], Y[k],
-                          fmaf(X[4 * i + 1], Y[4 + k], fmaf(X[4 * i + 2], Y[8 + k], X[4 * i + 3] * Y[12 + k])));
-}
+__device__ constexpr int kSpPlane[12] = {0, 2, 3, 5, 6, 7, 10, 11, 12, 13, 14, 15};
 
 // y = X v + w
 __device__ __forceinline__ void mat4_vec(const float X[16], const float v[4], const float w[4],
@@ -49,16 +48,55 @@ __device__ __forceinline__ void mat4_vec(const float X[16], const float v[4], co
     y[i] = fmaf(X[4 * i + 0], v[0], fmaf(X[4 * i + 1], v[1], fmaf(X[4 * i + 2], v[2], fmaf(X[4 * i + 3], v[3], w[i]))));
 }
 
-// (M, v) <- (M, v) o (Mp, vp): apply (Mp, vp) first, then (M, v)
+// Y <- A Y with A given by its 12 non-structural entries (order of kSpPlane); in place,
+// column by column (column k of A Y needs only column k of Y)
+__device__ __forceinline__ void sp_mul_left(const float a[12], float Y[16]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float y0 = Y[k], y1 = Y[4 + k], y2 = Y[8 + k], y3 = Y[12 + k];
+    Y[k] = fmaf(a[0], y0, fmaf(a[1], y2, a[2] * y3));
+    Y[4 + k] = fmaf(a[3], y1, fmaf(a[4], y2, a[5] * y3));
+    Y[8 + k] = fmaf(a[6], y2, a[7] * y3);
+    Y[12 + k] = fmaf(a[8], y0, fmaf(a[9], y1, fmaf(a[10], y2, a[11] * y3)));
+  }
+}
+
+// Y <- X Y for a dense X; in place, column by column
+__device__ __forceinline__ void mat4_mul_left(const float X[16], float Y[16]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float y0 = Y[k], y1 = Y[4 + k], y2 = Y[8 + k], y3 = Y[12 + k];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      Y[4 * i + k] = fmaf(X[4 * i], y0, fmaf(X[4 * i + 1], y1, fmaf(X[4 * i + 2], y2, X[4 * i + 3] * y3)));
+  }
+}
+
+// y = A v + w, A sparse
+__device__ __forceinline__ void sp_vec(const float a[12], const float v[4], const float w[4],
+                                       float y[4]) {
+  y[0] = fmaf(a[0], v[0], fmaf(a[1], v[2], fmaf(a[2], v[3], w[0])));
+  y[1] = fmaf(a[3], v[1], fmaf(a[4], v[2], fmaf(a[5], v[3], w[1])));
+  y[2] = fmaf(a[6], v[2], fmaf(a[7], v[3], w[2]));
+  y[3] = fmaf(a[8], v[0], fmaf(a[9], v[1], fmaf(a[10], v[2], fmaf(a[11], v[3], w[3]))));
+}
+
+// (M, v) <- (M, v) o (Mp, vp): apply (Mp, vp) first, then (M, v). In place, row by row: the
+// new v needs the old M, and row i of the new M needs only row i of the old M.
 __device__ __forceinline__ void compose_after(float M[16], float v[4], const float Mp[16],
                                               const float vp[4]) {
-  float Mn[16], vn[4];
-  mat4_mul(M, Mp, Mn);
-  mat4_vec(M, vp, v, vn);
 #pragma unroll
-  for (int e = 0; e < 16; ++e) M[e] = Mn[e];
+  for (int i = 0; i < 4; ++i)
+    v[i] = fmaf(M[4 * i], vp[0], fmaf(M[4 * i + 1], vp[1], fmaf(M[4 * i + 2], vp[2], fmaf(M[4 * i + 3], vp[3], v[i]))));
 #pragma unroll
-  for (int e = 0; e < 4; ++e) v[e] = vn[e];
+  for (int i = 0; i < 4; ++i) {
+    float row[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      row[k] = fmaf(M[4 * i], Mp[k], fmaf(M[4 * i + 1], Mp[4 + k], fmaf(M[4 * i + 2], Mp[8 + k], M[4 * i + 3] * Mp[12 + k])));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) M[4 * i + k] = row[k];
+  }
 }
 
 template <int S0, int S1, int S2, int S3>
@@ -70,10 +108,12 @@ __device__ __forceinline__ void quad_perm_map(const float M[16], const float v[4
   for (int e = 0; e < 4; ++e) vp[e] = quad_perm<S0, S1, S2, S3>(v[e]);
 }
 
-__global__ __launch_bounds__(kScanBlock) void scan_block4_kernel(
-    const float* __restrict__ A, const float* rhs, float* x, int B, int T, int d, int n_lg,
-    int n_tt, unsigned long long* __restrict__ desc, unsigned int* __restrict__ ticket,
-    uint32_t epoch, Control* ctl, int k_iter, float tol) {
+template <bool SPARSE, int TSUB>
+__global__ __launch_bounds__(kScanBlock, 2) void scan_block4_kernel(
+    const float* __restrict__ A, const float* rhs, float* x, int T, int d, int n_jt, int n_lg,
+    int n_tt, int anchor_stride, unsigned long long* __restrict__ desc,
+    unsigned int* __restrict__ ticket, uint32_t epoch, Control* ctl, int k_iter, float tol) {
+  constexpr int NA = SPARSE ? 12 : 16;
   if (ctl != nullptr) {
     if (ctl->stopped) return;
     if (tol > 0.0f && __uint_as_float(ctl->err_bits[k_iter]) < tol) {
@@ -97,59 +137,81 @@ __global__ __launch_bounds__(kScanBlock) void scan_block4_kernel(
     s_ticket = tk;
   }
   __syncthreads();
-  const unsigned int tk = s_ticket;
+  const unsigned int tk = __builtin_amdgcn_readfirstlane(s_ticket);
   const int tt = static_cast<int>(tk / n_lg);
   const int lg = static_cast<int>(tk % n_lg);
+  const int b = lg / n_jt;
+  const int jt = lg - b * n_jt;
 
   const int wave = tid >> 6;
   const int l = tid & 63;
   const int sc = l & 3;
   const int lane_in_tile = wave * 16 + (l >> 2);
-  const i64 n_lanes = static_cast<i64>(B) * d;
+  const unsigned j = static_cast<unsigned>(jt * 64 + lane_in_tile);
+  const unsigned ud = static_cast<unsigned>(d);
+  const bool valid = j < ud;
+  const int t_tile = tt * 4 * TSUB;
+  const int t_start = t_tile + sc * TSUB;
   const i64 n_lanes_pad = static_cast<i64>(n_lg) * 64;
-  const i64 lane = static_cast<i64>(lg) * 64 + lane_in_tile;
-  const bool valid = lane < n_lanes;
-  const int b = valid ? static_cast<int>(lane / d) : 0;
-  const int j = valid ? static_cast<int>(lane % d) : 0;
-  const int t_start = tt * kScanTile + sc * kScanTSub;
-  const i64 dd = d;
+  // scalar bases of this tile's rows, 32-bit lane offsets within them
+  const rsrc_t rsA = make_rsrc(A + (static_cast<i64>(b) * T + t_tile) * 16 * static_cast<i64>(d));
+  const rsrc_t rsR = make_rsrc(rhs + (static_cast<i64>(b) * T + t_tile) * 4 * static_cast<i64>(d));
+  const rsrc_t rsX = make_rsrc(x + (static_cast<i64>(b) * T + t_tile) * 4 * static_cast<i64>(d));
+  const unsigned a_lane = 4u * (static_cast<unsigned>(sc * TSUB) * 16u * ud + j);  // bytes
+  const unsigned r_lane = 4u * (static_cast<unsigned>(sc * TSUB) * 4u * ud + j);
+  const unsigned row_b = 4u * ud;  // bytes per plane row
 
   // ---- level 1: load the sub-chunk and compose it ----
-  float a[kScanTSub][16], r[kScanTSub][4];
+  float a[TSUB][NA], r[TSUB][4];
 #pragma unroll
-  for (int u = 0; u < kScanTSub; ++u) {
+  for (int u = 0; u < TSUB; ++u) {
     const int t = t_start + u;
     if (valid && t < T) {
-      const float* Ap = A + (static_cast<i64>(b) * T + t) * 16 * dd + j;
-      const float* rp = rhs + (static_cast<i64>(b) * T + t) * 4 * dd + j;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) a[u][e] = Ap[e * dd];
+      for (int e = 0; e < NA; ++e) {
+        const unsigned plane = SPARSE ? kSpPlane[e] : e;
+        a[u][e] = buf_ld(rsA, a_lane, (u * 16u + plane) * row_b);
+      }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) r[u][e] = rp[e * dd];
+      for (int e = 0; e < 4; ++e) r[u][e] = buf_ld(rsR, r_lane, (u * 4u + e) * row_b);
       if (t == 0) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) a[u][e] = 0.0f;  // x_0 = 0: the first map is constant
+        for (int e = 0; e < NA; ++e) a[u][e] = 0.0f;  // x_0 = 0: the first map is constant
       }
     } else {
+      // identity map
 #pragma unroll
-      for (int e = 0; e < 16; ++e) a[u][e] = (e % 5 == 0) ? 1.0f : 0.0f;  // identity map
+      for (int e = 0; e < NA; ++e) {
+        const int plane = SPARSE ? kSpPlane[e] : e;
+        a[u][e] = (plane % 5 == 0) ? 1.0f : 0.0f;
+      }
 #pragma unroll
       for (int e = 0; e < 4; ++e) r[u][e] = 0.0f;
     }
   }
   float M[16], v[4];
+  if constexpr (SPARSE) {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) M[e] = a[0][e];
+    for (int e = 0; e < 16; ++e) M[e] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 12; ++e) M[kSpPlane[e]] = a[0][e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) M[e] = a[0][e];
+  }
 #pragma unroll
   for (int e = 0; e < 4; ++e) v[e] = r[0][e];
 #pragma unroll
-  for (int u = 1; u < kScanTSub; ++u) {
+  for (int u = 1; u < TSUB; ++u) {
     // (M, v) <- (a_u, r_u) o (M, v)
-    float Mn[16], vn[4];
-    mat4_mul(a[u], M, Mn);
-    mat4_vec(a[u], v, r[u], vn);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) M[e] = Mn[e];
+    float vn[4];
+    if constexpr (SPARSE) {
+      sp_mul_left(a[u], M);
+      sp_vec(a[u], v, r[u], vn);
+    } else {
+      mat4_mul_left(a[u], M);
+      mat4_vec(a[u], v, r[u], vn);
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) v[e] = vn[e];
   }
@@ -170,63 +232,61 @@ __global__ __launch_bounds__(kScanBlock) void scan_block4_kernel(
   }
   __syncthreads();
 
-  // ---- level 3: decoupled look-back, one thread per lane of the tile ----
+  // ---- level 3: look-back across tiles, one thread per lane of the tile ----
+  // Fixed dataflow, so results do not depend on scheduling: tiles whose index is a multiple
+  // of the anchor stride publish their inclusive value; the others publish their aggregate
+  // before waiting. A tile folds the aggregates of its predecessors down to the nearest
+  // anchor, always in the same order, and applies the anchor's inclusive value.
   if (wave == 0) {
     const i64 my_lane = static_cast<i64>(lg) * 64 + l;
-    float Mt[16], vt[4], carry[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int e = 0; e < 16; ++e) Mt[e] = s_agg[l][e];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) vt[e] = s_agg[l][16 + e];
+    float carry[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     auto word = [&](int tile, int w) {
       return desc + (static_cast<i64>(tile) * kScanWords + w) * n_lanes_pad + my_lane;
     };
+    const bool anchor = (tt % anchor_stride) == 0;
+    if (!anchor) {
+#pragma unroll
+      for (int e = 0; e < 20; ++e) tag_store(word(tt, 4 + e), s_agg[l][e], epoch);
+    }
     if (tt > 0) {
-      // accumulated map of the tiles between the one being inspected and this one
+      const int a = ((tt - 1) / anchor_stride) * anchor_stride;  // nearest anchor below
+      // accumulated map of the tiles a+1 .. tt-1
       float Macc[16], vacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int e = 0; e < 16; ++e) Macc[e] = (e % 5 == 0) ? 1.0f : 0.0f;
-      bool published = false;
-      int p = tt - 1;
-      while (true) {
-        float xin[4];
-        bool inc = true;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) inc &= tag_load(word(p, e), epoch, xin[e]);
-        if (inc) {
-          mat4_vec(Macc, xin, vacc, carry);
-          break;
-        }
-        if (!published) {
-          // let successors look past this tile while it waits
-#pragma unroll
-          for (int e = 0; e < 16; ++e) tag_store(word(tt, 4 + e), Mt[e], epoch);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) tag_store(word(tt, 20 + e), vt[e], epoch);
-          published = true;
-        }
+      for (int p = tt - 1; p > a; --p) {
         float Mp[16], vp[4];
-        bool agg = true;
+        while (true) {
+          bool ok = true;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) agg &= tag_load(word(p, 4 + e), epoch, Mp[e]);
+          for (int e = 0; e < 16; ++e) ok &= tag_load(word(p, 4 + e), epoch, Mp[e]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) agg &= tag_load(word(p, 20 + e), epoch, vp[e]);
-        if (agg) {
-          compose_after(Macc, vacc, Mp, vp);
-          if (--p < 0) {  // walked past the first tile: x before it is zero
-#pragma unroll
-            for (int e = 0; e < 4; ++e) carry[e] = vacc[e];
-            break;
-          }
-          continue;
+          for (int e = 0; e < 4; ++e) ok &= tag_load(word(p, 20 + e), epoch, vp[e]);
+          if (ok) break;
+          __builtin_amdgcn_s_sleep(2);
         }
+        compose_after(Macc, vacc, Mp, vp);
+      }
+      float xin[4];
+      while (true) {
+        bool ok = true;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ok &= tag_load(word(a, e), epoch, xin[e]);
+        if (ok) break;
         __builtin_amdgcn_s_sleep(2);
       }
+      mat4_vec(Macc, xin, vacc, carry);
     }
-    float xend[4];
-    mat4_vec(Mt, carry, vt, xend);
+    if (anchor) {
+      // inclusive value at the end of this tile: x_end = M_tile carry + v_tile
 #pragma unroll
-    for (int e = 0; e < 4; ++e) tag_store(word(tt, e), xend[e], epoch);
+      for (int i = 0; i < 4; ++i) {
+        const float xe = fmaf(s_agg[l][4 * i], carry[0],
+                              fmaf(s_agg[l][4 * i + 1], carry[1],
+                                   fmaf(s_agg[l][4 * i + 2], carry[2], fmaf(s_agg[l][4 * i + 3], carry[3], s_agg[l][16 + i]))));
+        tag_store(word(tt, i), xe, epoch);
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) s_carry[l][e] = carry[e];
   }
@@ -243,36 +303,53 @@ __global__ __launch_bounds__(kScanBlock) void scan_block4_kernel(
     if (sc == 0) xs[e] = cin[e];
   }
 #pragma unroll
-  for (int u = 0; u < kScanTSub; ++u) {
+  for (int u = 0; u < TSUB; ++u) {
     const int t = t_start + u;
     float xn[4];
-    mat4_vec(a[u], xs, r[u], xn);
+    if constexpr (SPARSE)
+      sp_vec(a[u], xs, r[u], xn);
+    else
+      mat4_vec(a[u], xs, r[u], xn);
 #pragma unroll
     for (int e = 0; e < 4; ++e) xs[e] = xn[e];
     if (valid && t < T) {
-      float* xp = x + (static_cast<i64>(b) * T + t) * 4 * dd + j;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) xp[e * dd] = xs[e];
+      for (int e = 0; e < 4; ++e) buf_st(xs[e], rsX, r_lane, (u * 4u + e) * row_b);
     }
   }
 }
 
-size_t scan_desc_words(int B, int T, int d) {
-  const i64 n_lg = (static_cast<i64>(B) * d + 63) / 64;
-  const i64 n_tt = (T + kScanTile - 1) / kScanTile;
+static void scan_grid(int B, int T, int d, int tile, i64& n_jt, i64& n_lg, i64& n_tt) {
+  n_jt = (d + 63) / 64;
+  n_lg = static_cast<i64>(B) * n_jt;
+  n_tt = (T + tile - 1) / tile;
+}
+
+size_t scan_desc_words(int B, int T, int d, bool sparse) {
+  i64 n_jt, n_lg, n_tt;
+  scan_grid(B, T, d, 4 * (sparse ? kScanTSubSparse : kScanTSubDense), n_jt, n_lg, n_tt);
   return static_cast<size_t>(n_tt * kScanWords * n_lg * 64);
 }
 
 hipError_t launch_scan_block4(const float* A, const float* rhs, float* x, int B, int T, int d,
-                              unsigned long long* desc, unsigned int* ticket, uint32_t epoch,
-                              Control* ctl, int k_iter, float tol, hipStream_t stream) {
-  const i64 n_lg = (static_cast<i64>(B) * d + 63) / 64;
-  const i64 n_tt = (T + kScanTile - 1) / kScanTile;
+                              bool sparse, unsigned long long* desc, unsigned int* ticket,
+                              uint32_t epoch, Control* ctl, int k_iter, float tol,
+                              hipStream_t stream) {
+  const int tile = 4 * (sparse ? kScanTSubSparse : kScanTSubDense);
+  i64 n_jt, n_lg, n_tt;
+  scan_grid(B, T, d, tile, n_jt, n_lg, n_tt);
   const i64 blocks = n_lg * n_tt;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  scan_block4_kernel<<<dim3(static_cast<unsigned>(blocks)), kScanBlock, 0, stream>>>(
-      A, rhs, x, B, T, d, static_cast<int>(n_lg), static_cast<int>(n_tt), desc, ticket, epoch, ctl,
-      k_iter, tol);
+  const int stride = look_back_anchor_stride(n_lg);
+  const dim3 grid(static_cast<unsigned>(blocks));
+  if (sparse)
+    scan_block4_kernel<true, kScanTSubSparse><<<grid, kScanBlock, 0, stream>>>(
+        A, rhs, x, T, d, static_cast<int>(n_jt), static_cast<int>(n_lg), static_cast<int>(n_tt), stride,
+        desc, ticket, epoch, ctl, k_iter, tol);
+  else
+    scan_block4_kernel<false, kScanTSubDense><<<grid, kScanBlock, 0, stream>>>(
+        A, rhs, x, T, d, static_cast<int>(n_jt), static_cast<int>(n_lg), static_cast<int>(n_tt), stride,
+        desc, ticket, epoch, ctl, k_iter, tol);
   return hipGetLastError();
 }
 

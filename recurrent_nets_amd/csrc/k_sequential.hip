@@ -17,7 +17,8 @@ constexpr int kSeqGroup = 4;
 template <bool BF16>
 __global__ __launch_bounds__(kSeqBlock) void sequential_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
-    float* __restrict__ S, float* __restrict__ h_out, int B, int T, int d, int sig_forget) {
+    float* __restrict__ S, float* __restrict__ h_out, float* __restrict__ final_state, int B,
+    int T, int d, int sig_forget) {
   const i64 lane = static_cast<i64>(blockIdx.x) * kSeqBlock + threadIdx.x;
   if (lane >= static_cast<i64>(B) * d) return;
   const int b = static_cast<int>(lane / d);
@@ -66,21 +67,28 @@ __global__ __launch_bounds__(kSeqBlock) void sequential_kernel(
 #pragma unroll
       for (int k = 0; k < 4; ++k) cur[u][k] = nxt[u][k];
   }
+  if (final_state != nullptr) {
+    float* fs = final_state + static_cast<i64>(b) * d4 + j;
+    fs[0] = pv.c;
+    fs[dd] = pv.n;
+    fs[2 * dd] = pv.m;
+    fs[3 * dd] = pv.h;
+  }
 }
 
 hipError_t launch_sequential(const void* P, bool p_bf16, const float* R, const float* state0,
-                             float* S, float* h_out, int B, int T, int d, bool sig_forget,
-                             hipStream_t stream) {
+                             float* S, float* h_out, float* final_state, int B, int T, int d,
+                             bool sig_forget, hipStream_t stream) {
   const i64 lanes = static_cast<i64>(B) * d;
   const i64 blocks = (lanes + kSeqBlock - 1) / kSeqBlock;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const int sig = sig_forget ? 1 : 0;
   if (p_bf16)
     sequential_kernel<true><<<dim3(static_cast<unsigned>(blocks)), kSeqBlock, 0, stream>>>(
-        P, R, state0, S, h_out, B, T, d, sig);
+        P, R, state0, S, h_out, final_state, B, T, d, sig);
   else
     sequential_kernel<false><<<dim3(static_cast<unsigned>(blocks)), kSeqBlock, 0, stream>>>(
-        P, R, state0, S, h_out, B, T, d, sig);
+        P, R, state0, S, h_out, final_state, B, T, d, sig);
   return hipGetLastError();
 }
 

@@ -8,7 +8,8 @@
 //            not finite, convergence when a tolerance is set and met ("Layout" page of the
 //            pararnn-torch docs, "Current surface (0.17)": NewtonStats, residual early stop,
 //            divergence error when max|F| > 1 after K).
-// hidden:    copies the hidden slot (slot 3) of the states into a (B, T, d) output.
+// outputs:   copies the hidden slot (slot 3) of the states into a (B, T, d) output and the
+//            last step's state into a contiguous (B, 4, d) output.
 #include "common.h"
 #include "kernels.h"
 
@@ -48,13 +49,25 @@ __global__ void finalize_kernel(Control* __restrict__ ctl, float tol) {
 
 __global__ __launch_bounds__(kUpdBlock) void hidden_kernel(const float* __restrict__ S,
                                                            float* __restrict__ h, i64 rows, int d) {
-  // rows = B*T; one (b, t) row of d features per grid-stride step
+  // rows = B*T; element i of h is feature i % d of row i / d
   const i64 n = rows * d;
   const i64 stride = static_cast<i64>(gridDim.x) * kUpdBlock;
   for (i64 i = static_cast<i64>(blockIdx.x) * kUpdBlock + threadIdx.x; i < n; i += stride) {
     const i64 row = i / d;
     const i64 j = i - row * d;
     h[i] = S[(row * 4 + 3) * d + j];
+  }
+}
+
+__global__ __launch_bounds__(kUpdBlock) void final_state_kernel(const float* __restrict__ S,
+                                                                float* __restrict__ out, int B,
+                                                                int T, int d) {
+  const i64 n = static_cast<i64>(B) * 4 * d;  // (b, slot, j) of the last step
+  for (i64 i = static_cast<i64>(blockIdx.x) * kUpdBlock + threadIdx.x; i < n;
+       i += static_cast<i64>(gridDim.x) * kUpdBlock) {
+    const i64 b = i / (4 * static_cast<i64>(d));
+    const i64 rest = i - b * 4 * d;
+    out[i] = S[(b * T + (T - 1)) * 4 * d + rest];
   }
 }
 
@@ -88,9 +101,18 @@ hipError_t launch_finalize(Control* ctl, float tol, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_hidden(const float* S, float* h, int B, int T, int d, hipStream_t stream) {
-  const i64 rows = static_cast<i64>(B) * T;
-  hidden_kernel<<<stream_grid(rows * d), kUpdBlock, 0, stream>>>(S, h, rows, d);
+hipError_t launch_outputs(const float* S, float* h, float* final_state, int B, int T, int d,
+                          hipStream_t stream) {
+  if (h != nullptr) {
+    const i64 rows = static_cast<i64>(B) * T;
+    hidden_kernel<<<stream_grid(rows * d), kUpdBlock, 0, stream>>>(S, h, rows, d);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (final_state != nullptr) {
+    final_state_kernel<<<stream_grid(static_cast<i64>(B) * 4 * d), kUpdBlock, 0, stream>>>(
+        S, final_state, B, T, d);
+  }
   return hipGetLastError();
 }
 

@@ -21,10 +21,11 @@
 // Composition (X first, then Y): L = L_X + L_Y, E = max(E_X, E_Y - L_X),
 //   cz = e^{E_X - E} cz_X + e^{E_Y - L_X - E} cz_Y, nz likewise. One step: (l, i~ - l, z, 1).
 //
-// Same decomposition as the 4x4 scan: a tile of 64 lanes x 4*TSUB steps per workgroup,
-// per-thread sequential sub-chunks, a DPP quad scan of sub-chunk aggregates, tile
-// aggregates and carries staged in LDS, and a decoupled look-back across tiles along T. The
-// re-run from each carry writes the states (c, n, m, h) with h = sigma(p_o) c / n.
+// Same decomposition as the 4x4 scan: a tile of 64 features of one batch row x 4*TSUB steps
+// per workgroup, per-thread sequential sub-chunks, a DPP quad scan of sub-chunk aggregates,
+// tile aggregates and carries staged in LDS, and a decoupled look-back across tiles along T
+// with the same fixed, anchored dataflow. The re-run from each carry writes the states
+// (c, n, m, h) with h = sigma(p_o) c / n.
 #include "cell.h"
 #include "kernels.h"
 
@@ -78,9 +79,9 @@ __device__ __forceinline__ LogAgg quad_perm_agg_m2(const LogAgg& X) {
 
 template <bool BF16>
 __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
-    const void* __restrict__ P, const float* __restrict__ state0, float* __restrict__ S, int B,
-    int T, int d, int sig_forget, int n_lg, int n_tt, unsigned long long* __restrict__ desc,
-    unsigned int* __restrict__ ticket, uint32_t epoch) {
+    const void* __restrict__ P, const float* __restrict__ state0, float* __restrict__ S, int T,
+    int d, int sig_forget, int n_jt, int n_lg, int n_tt, int anchor_stride,
+    unsigned long long* __restrict__ desc, unsigned int* __restrict__ ticket, uint32_t epoch) {
   __shared__ unsigned int s_ticket;
   __shared__ LogAgg s_agg[64];
   __shared__ float s_carry[64][3];
@@ -93,23 +94,27 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
     s_ticket = tk;
   }
   __syncthreads();
-  const unsigned int tk = s_ticket;
+  const unsigned int tk = __builtin_amdgcn_readfirstlane(s_ticket);
   const int tt = static_cast<int>(tk / n_lg);
   const int lg = static_cast<int>(tk % n_lg);
+  const int b = lg / n_jt;
+  const int jt = lg - b * n_jt;
 
   const int wave = tid >> 6;
   const int l = tid & 63;
   const int sc = l & 3;
   const int lane_in_tile = wave * 16 + (l >> 2);
-  const i64 n_lanes = static_cast<i64>(B) * d;
+  const unsigned ud = static_cast<unsigned>(d);
+  const unsigned j = static_cast<unsigned>(jt * 64 + lane_in_tile);
+  const bool valid = j < ud;
+  const int t_tile = tt * kWarmTile;
+  const int t_start = t_tile + sc * kWarmTSub;
   const i64 n_lanes_pad = static_cast<i64>(n_lg) * 64;
-  const i64 lane = static_cast<i64>(lg) * 64 + lane_in_tile;
-  const bool valid = lane < n_lanes;
-  const int b = valid ? static_cast<int>(lane / d) : 0;
-  const int j = valid ? static_cast<int>(lane % d) : 0;
-  const int t_start = tt * kWarmTile + sc * kWarmTSub;
-  const i64 dd = d;
   const bool sig = sig_forget != 0;
+  // scalar bases of this tile's rows, 32-bit lane offsets within them
+  const i64 tile_row = (static_cast<i64>(b) * T + t_tile) * 4 * static_cast<i64>(d);
+  float* Sb = S + tile_row;
+  const unsigned lane_off = static_cast<unsigned>(sc * kWarmTSub) * 4u * ud + j;
 
   // ---- level 1: gates of the sub-chunk, folded into one aggregate ----
   float lf[kWarmTSub], it[kWarmTSub], zz[kWarmTSub], oo[kWarmTSub];
@@ -117,11 +122,11 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
   for (int u = 0; u < kWarmTSub; ++u) {
     const int t = t_start + u;
     if (valid && t < T) {
-      const i64 base = (static_cast<i64>(b) * T + t) * 4 * dd + j;
-      const float pz = load_p<BF16>(P, base);
-      const float pi = load_p<BF16>(P, base + dd);
-      const float pf = load_p<BF16>(P, base + 2 * dd);
-      const float po = load_p<BF16>(P, base + 3 * dd);
+      const unsigned o = lane_off + u * 4u * ud;
+      const float pz = load_p<BF16>(P, tile_row + o);
+      const float pi = load_p<BF16>(P, tile_row + o + ud);
+      const float pf = load_p<BF16>(P, tile_row + o + 2 * ud);
+      const float po = load_p<BF16>(P, tile_row + o + 3 * ud);
       zz[u] = tanhf(pz);
       oo[u] = sigmoidf(po);
       it[u] = pi;
@@ -155,63 +160,58 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
   if (wave == 0) {
     const i64 my_lane = static_cast<i64>(lg) * 64 + l;
     const LogAgg tile = s_agg[l];
-    auto word = [&](int t_tile, int w) {
-      return desc + (static_cast<i64>(t_tile) * kWarmWords + w) * n_lanes_pad + my_lane;
+    auto word = [&](int tile_idx, int w) {
+      return desc + (static_cast<i64>(tile_idx) * kWarmWords + w) * n_lanes_pad + my_lane;
     };
     // state entering the sequence (slots c, n, m of state0; zeros without one)
     float m0 = 0.0f, c0 = 0.0f, n0 = 0.0f;
-    if (state0 != nullptr && my_lane < n_lanes) {
-      const int bl = static_cast<int>(my_lane / d), jl = static_cast<int>(my_lane % d);
-      const float* s0 = state0 + static_cast<i64>(bl) * 4 * dd + jl;
-      c0 = s0[0];
-      n0 = s0[dd];
-      m0 = s0[2 * dd];
+    const unsigned jl = static_cast<unsigned>(jt * 64 + l);
+    if (state0 != nullptr && jl < ud) {
+      const float* s0 = state0 + static_cast<i64>(b) * 4 * static_cast<i64>(d);
+      c0 = s0[jl];
+      n0 = s0[ud + jl];
+      m0 = s0[2 * ud + jl];
     }
     float cm = m0, cc = c0, cn = n0;
+    // fixed dataflow (results independent of scheduling): anchors publish their carry out,
+    // the tiles in between their run aggregate before waiting; a tile folds the aggregates
+    // down to the nearest anchor in a fixed order and applies it to the anchor's carry out
+    const bool anchor = (tt % anchor_stride) == 0;
+    if (!anchor) {
+      tag_store(word(tt, 4), tile.L, epoch);
+      tag_store(word(tt, 5), tile.E, epoch);
+      tag_store(word(tt, 6), tile.cz, epoch);
+      tag_store(word(tt, 7), tile.nz, epoch);
+    }
     if (tt > 0) {
-      LogAgg acc = {0.0f, -INFINITY, 0.0f, 0.0f};
-      bool published = false;
-      int p = tt - 1;
-      while (true) {
-        float xm, xc, xn;
-        const bool inc = tag_load(word(p, 0), epoch, xm) & tag_load(word(p, 1), epoch, xc) &
-                         tag_load(word(p, 2), epoch, xn);
-        if (inc) {
-          apply(acc, xm, xc, xn);
-          cm = xm;
-          cc = xc;
-          cn = xn;
-          break;
-        }
-        if (!published) {
-          tag_store(word(tt, 4), tile.L, epoch);
-          tag_store(word(tt, 5), tile.E, epoch);
-          tag_store(word(tt, 6), tile.cz, epoch);
-          tag_store(word(tt, 7), tile.nz, epoch);
-          published = true;
-        }
+      const int a = ((tt - 1) / anchor_stride) * anchor_stride;
+      LogAgg acc = {0.0f, -INFINITY, 0.0f, 0.0f};  // runs a+1 .. tt-1, composed
+      for (int p = tt - 1; p > a; --p) {
         LogAgg pa;
-        const bool ok = tag_load(word(p, 4), epoch, pa.L) & tag_load(word(p, 5), epoch, pa.E) &
-                        tag_load(word(p, 6), epoch, pa.cz) & tag_load(word(p, 7), epoch, pa.nz);
-        if (ok) {
-          acc = compose(pa, acc);
-          if (--p < 0) {
-            apply(acc, cm, cc, cn);  // from the state entering the sequence
-            break;
-          }
-          continue;
-        }
-        __builtin_amdgcn_s_sleep(2);
+        while (!(tag_load(word(p, 4), epoch, pa.L) & tag_load(word(p, 5), epoch, pa.E) &
+                 tag_load(word(p, 6), epoch, pa.cz) & tag_load(word(p, 7), epoch, pa.nz)))
+          __builtin_amdgcn_s_sleep(2);
+        acc = compose(pa, acc);
       }
+      float xm, xc, xn;
+      while (!(tag_load(word(a, 0), epoch, xm) & tag_load(word(a, 1), epoch, xc) &
+               tag_load(word(a, 2), epoch, xn)))
+        __builtin_amdgcn_s_sleep(2);
+      apply(acc, xm, xc, xn);
+      cm = xm;
+      cc = xc;
+      cn = xn;
     }
     s_carry[l][0] = cm;
     s_carry[l][1] = cc;
     s_carry[l][2] = cn;
-    float em = cm, ec = cc, en = cn;
-    apply(tile, em, ec, en);
-    tag_store(word(tt, 0), em, epoch);
-    tag_store(word(tt, 1), ec, epoch);
-    tag_store(word(tt, 2), en, epoch);
+    if (anchor) {
+      float em = cm, ec = cc, en = cn;
+      apply(tile, em, ec, en);
+      tag_store(word(tt, 0), em, epoch);
+      tag_store(word(tt, 1), ec, epoch);
+      tag_store(word(tt, 2), en, epoch);
+    }
   }
   __syncthreads();
 
@@ -240,38 +240,45 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
       c = fmaf(fg, c, ig * zz[u]);
       n = fmaf(fg, n, ig);
       m = mn;
-      float* sp = S + (static_cast<i64>(b) * T + t) * 4 * dd + j;
-      sp[0] = c;
-      sp[dd] = n;
-      sp[2 * dd] = m;
-      sp[3 * dd] = oo[u] * c / n;
+      const unsigned o = lane_off + u * 4u * ud;
+      Sb[o] = c;
+      Sb[o + ud] = n;
+      Sb[o + 2 * ud] = m;
+      Sb[o + 3 * ud] = oo[u] * c / n;
     }
   }
 }
 
+static void warm_grid(int B, int T, int d, i64& n_jt, i64& n_lg, i64& n_tt) {
+  n_jt = (d + 63) / 64;
+  n_lg = static_cast<i64>(B) * n_jt;
+  n_tt = (T + kWarmTile - 1) / kWarmTile;
+}
+
 size_t warm_desc_words(int B, int T, int d) {
-  const i64 n_lg = (static_cast<i64>(B) * d + 63) / 64;
-  const i64 n_tt = (T + kWarmTile - 1) / kWarmTile;
+  i64 n_jt, n_lg, n_tt;
+  warm_grid(B, T, d, n_jt, n_lg, n_tt);
   return static_cast<size_t>(n_tt * kWarmWords * n_lg * 64);
 }
 
 hipError_t launch_warm_start(const void* P, bool p_bf16, const float* state0, float* S, int B,
                              int T, int d, bool sig_forget, unsigned long long* desc,
                              unsigned int* ticket, uint32_t epoch, hipStream_t stream) {
-  const i64 n_lg = (static_cast<i64>(B) * d + 63) / 64;
-  const i64 n_tt = (T + kWarmTile - 1) / kWarmTile;
+  i64 n_jt, n_lg, n_tt;
+  warm_grid(B, T, d, n_jt, n_lg, n_tt);
   const i64 blocks = n_lg * n_tt;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks));
   const int sig = sig_forget ? 1 : 0;
+  const int stride = look_back_anchor_stride(n_lg);
   if (p_bf16)
-    warm_start_kernel<true><<<grid, kWarmBlock, 0, stream>>>(P, state0, S, B, T, d, sig,
+    warm_start_kernel<true><<<grid, kWarmBlock, 0, stream>>>(P, state0, S, T, d, sig, static_cast<int>(n_jt),
                                                              static_cast<int>(n_lg), static_cast<int>(n_tt),
-                                                             desc, ticket, epoch);
+                                                             stride, desc, ticket, epoch);
   else
-    warm_start_kernel<false><<<grid, kWarmBlock, 0, stream>>>(P, state0, S, B, T, d, sig,
+    warm_start_kernel<false><<<grid, kWarmBlock, 0, stream>>>(P, state0, S, T, d, sig, static_cast<int>(n_jt),
                                                               static_cast<int>(n_lg), static_cast<int>(n_tt),
-                                                              desc, ticket, epoch);
+                                                              stride, desc, ticket, epoch);
   return hipGetLastError();
 }
 

@@ -8,15 +8,19 @@
 
 namespace slstm {
 
+// Jacobian planes the residual kernel writes: all 16, the 12 non-structural ones, or none
+enum class ResidualMode { kDense, kSparse, kNone };
+
 hipError_t launch_residual(const void* P, bool p_bf16, const float* R, const float* state0,
                            const float* S, float* A, float* rhs, int B, int T, int d,
                            bool sig_forget, const Control* ctl, unsigned int* err_dst,
-                           bool with_jacobian, hipStream_t stream);
+                           ResidualMode mode, hipStream_t stream);
 
-size_t scan_desc_words(int B, int T, int d);
+size_t scan_desc_words(int B, int T, int d, bool sparse);
 hipError_t launch_scan_block4(const float* A, const float* rhs, float* x, int B, int T, int d,
-                              unsigned long long* desc, unsigned int* ticket, uint32_t epoch,
-                              Control* ctl, int k_iter, float tol, hipStream_t stream);
+                              bool sparse, unsigned long long* desc, unsigned int* ticket,
+                              uint32_t epoch, Control* ctl, int k_iter, float tol,
+                              hipStream_t stream);
 
 size_t warm_desc_words(int B, int T, int d);
 hipError_t launch_warm_start(const void* P, bool p_bf16, const float* state0, float* S, int B,
@@ -27,12 +31,13 @@ hipError_t launch_update(float* S, const float* D, i64 n_floats, Control* ctl, i
                          hipStream_t stream);
 hipError_t launch_init_control(Control* ctl, hipStream_t stream);
 hipError_t launch_finalize(Control* ctl, float tol, hipStream_t stream);
-hipError_t launch_hidden(const float* S, float* h, int B, int T, int d, hipStream_t stream);
+hipError_t launch_outputs(const float* S, float* h, float* final_state, int B, int T, int d,
+                          hipStream_t stream);
 hipError_t launch_zero(float* p, i64 n_floats, hipStream_t stream);
 
 hipError_t launch_sequential(const void* P, bool p_bf16, const float* R, const float* state0,
-                             float* S, float* h_out, int B, int T, int d, bool sig_forget,
-                             hipStream_t stream);
+                             float* S, float* h_out, float* final_state, int B, int T, int d,
+                             bool sig_forget, hipStream_t stream);
 
 hipError_t launch_gemm_bf16(const void* X, const void* W, const float* bias, float* C, i64 M,
                             int N, int K, hipStream_t stream);

@@ -30,6 +30,7 @@ EXPORTED = [
     "slstm_input_projection", "slstm_residual_jacobian", "slstm_scan_block4_workspace_bytes",
     "slstm_scan_block4", "slstm_warm_start_workspace_bytes", "slstm_warm_start",
     "slstm_profile_enable", "slstm_profile_reset", "slstm_profile_read",
+    "slstm_profile_durations",
 ]
 
 
@@ -88,12 +89,12 @@ def load(path: str | None = None):
         getattr(L, name).restype = _sz
         getattr(L, name).argtypes = [_i, _i, _i]
     L.slstm_newton_forward.restype = _i
-    L.slstm_newton_forward.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i,
-                                       _vp, _sz, _vp, ctypes.POINTER(_Stats)]
+    L.slstm_newton_forward.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
+                                       _i, _vp, _sz, _vp, ctypes.POINTER(_Stats)]
     L.slstm_newton_read_stats.restype = _i
     L.slstm_newton_read_stats.argtypes = [_vp, _sz, _vp, ctypes.POINTER(_Stats)]
     L.slstm_sequential_forward.restype = _i
-    L.slstm_sequential_forward.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]
+    L.slstm_sequential_forward.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp]
     L.slstm_input_projection.restype = _i
     L.slstm_input_projection.argtypes = [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
     L.slstm_residual_jacobian.restype = _i
@@ -107,6 +108,8 @@ def load(path: str | None = None):
     L.slstm_profile_reset.restype = _i
     L.slstm_profile_read.restype = _i
     L.slstm_profile_read.argtypes = [_i, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_i)]
+    L.slstm_profile_durations.restype = _i
+    L.slstm_profile_durations.argtypes = [_i, ctypes.POINTER(ctypes.c_double), _i, ctypes.POINTER(_i)]
     _LIB = L
     return L
 
@@ -165,10 +168,11 @@ def alloc_workspace(nbytes: int, device=None) -> torch.Tensor:
 
 
 def newton_forward(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, init="warm",
-                   states=None, h_out=None, want_hidden=True, workspace=None, stream=None,
-                   stats=True, raise_on_divergence=True):
+                   states=None, h_out=None, want_hidden=True, final_state=None, workspace=None,
+                   stream=None, stats=True, raise_on_divergence=True):
     """Newton-parallel forward. Returns (states (B,T,4,d_h), h (B,T,d_h) or None, NewtonStats
-    or None). With stats=False the call is asynchronous and returns no stats."""
+    or None). With stats=False the call is asynchronous and returns no stats. A given
+    ``final_state`` (B,4,d_h) tensor receives the last step's state."""
     L = load()
     _dev(P, "P", (torch.float32, torch.bfloat16))
     _dev(R, "R", (torch.float32,))
@@ -180,12 +184,14 @@ def newton_forward(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, init="
         h_out = torch.empty((B, T, d), dtype=torch.float32, device=P.device)
     _dev(states, "states", (torch.float32,))
     _dev(h_out, "h_out", (torch.float32,))
+    _dev(final_state, "final_state", (torch.float32,))
     need = L.slstm_newton_workspace_bytes(B, T, d)
     if workspace is None:
         workspace = alloc_workspace(need, P.device)
     st = _Stats() if stats else None
     status = L.slstm_newton_forward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
-                                    _ptr(h_out), B, T, d, FORGET[forget], int(max_iters),
+                                    _ptr(h_out), _ptr(final_state), B, T, d, FORGET[forget],
+                                    int(max_iters),
                                     float(tol), INIT[init], _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream),
                                     ctypes.byref(st) if st is not None else None)
@@ -207,8 +213,9 @@ def read_stats(workspace, stream=None) -> NewtonStats:
 
 
 def sequential_forward(P, R, state0=None, forget="exp", states=None, h_out=None,
-                       want_hidden=True, stream=None):
-    """Step-by-step forward (also the T=1 decode step). Returns (states, h or None)."""
+                       want_hidden=True, final_state=None, stream=None):
+    """Step-by-step forward (also the T=1 decode step). Returns (states, h or None). A given
+    ``final_state`` (B,4,d_h) tensor receives the last step's state."""
     L = load()
     _dev(P, "P", (torch.float32, torch.bfloat16))
     _dev(R, "R", (torch.float32,))
@@ -220,8 +227,10 @@ def sequential_forward(P, R, state0=None, forget="exp", states=None, h_out=None,
         h_out = torch.empty((B, T, d), dtype=torch.float32, device=P.device)
     _dev(states, "states", (torch.float32,))
     _dev(h_out, "h_out", (torch.float32,))
+    _dev(final_state, "final_state", (torch.float32,))
     status = L.slstm_sequential_forward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
-                                        _ptr(h_out), B, T, d, FORGET[forget], _stream(stream))
+                                        _ptr(h_out), _ptr(final_state), B, T, d, FORGET[forget],
+                                        _stream(stream))
     _check(status, "slstm_sequential_forward")
     return states, h_out
 
@@ -320,3 +329,14 @@ def profile_read(kind: str):
     _check(load().slstm_profile_read(KERNELS[kind], ctypes.byref(ms), ctypes.byref(n)),
            "slstm_profile_read")
     return ms.value, n.value
+
+
+def profile_durations(kind: str):
+    """Every launch duration (ms, launch order) of one kernel kind since the last reset."""
+    L = load()
+    n = ctypes.c_int()
+    _check(L.slstm_profile_durations(KERNELS[kind], None, 0, ctypes.byref(n)), "slstm_profile_durations")
+    buf = (ctypes.c_double * max(n.value, 1))()
+    _check(L.slstm_profile_durations(KERNELS[kind], buf, n.value, ctypes.byref(n)),
+           "slstm_profile_durations")
+    return [buf[i] for i in range(n.value)]

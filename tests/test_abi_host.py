@@ -55,7 +55,7 @@ def test_workspace_sizes(lib):
 
 def _fwd(lib, **kw):
     args = dict(P=ctypes.c_void_p(256), dt=0, R=ctypes.c_void_p(256), s0=None,
-                S=ctypes.c_void_p(256), h=None, B=2, T=64, d=16, fm=0, K=3, tol=0.0, init=0,
+                S=ctypes.c_void_p(256), h=None, fin=None, B=2, T=64, d=16, fm=0, K=3, tol=0.0, init=0,
                 ws=ctypes.c_void_p(4096), wsb=1 << 30, stream=None, stats=None)
     args.update(kw)
     return lib.slstm_newton_forward(*args.values())
@@ -73,6 +73,7 @@ def test_argument_checks_return_einval(lib):
     assert _fwd(lib, init=3) == slstm.EINVAL
     assert _fwd(lib, P=None) == slstm.EINVAL
     assert _fwd(lib, S=ctypes.c_void_p(260)) == slstm.EINVAL      # states not 16-byte aligned
+    assert _fwd(lib, fin=ctypes.c_void_p(264)) == slstm.EINVAL    # final_state not 16-byte aligned
     assert _fwd(lib, ws=ctypes.c_void_p(4096 + 16)) == slstm.EINVAL  # workspace not 256-aligned
     assert "256-byte" in lib.slstm_last_error().decode()
     assert _fwd(lib, wsb=100) == slstm.EWORKSPACE
@@ -87,7 +88,7 @@ def test_argument_checks_return_einval(lib):
                               2, 64, 16, ctypes.c_void_p(4096), 10, None)
     assert s == slstm.EWORKSPACE
     s = lib.slstm_sequential_forward(None, 0, ctypes.c_void_p(256), None, ctypes.c_void_p(256),
-                                     None, 2, 64, 16, 0, None)
+                                     None, None, 2, 64, 16, 0, None)
     assert s == slstm.EINVAL
 
 

@@ -69,15 +69,35 @@ def test_scan_block4(gpu_lib, shape, inplace):
     assert float(np.max(np.abs(x - x_ref))) < 2e-5 * max(1.0, float(np.max(np.abs(x_ref))))
 
 
-def test_scan_block4_is_deterministic(gpu_lib):
-    case("scan_block4 determinism B=4 T=8192 d=96")
-    A, r = random_scan_operands(3, 4, 8192, 96)
+@pytest.mark.parametrize("shape", [(4, 8192, 96), (64, 256, 512)])
+def test_scan_block4_is_deterministic(gpu_lib, shape):
+    # few lane groups (anchored look-back) and many (plain chain): bitwise equal reruns
+    B, T, d = shape
+    case(f"scan_block4 determinism B={B} T={T} d={d}")
+    A, r = random_scan_operands(3, B, T, d)
     At = torch.from_numpy(A.astype(np.float32)).to(DEV)
     rt = torch.from_numpy(r.astype(np.float32)).to(DEV)
     first = gpu_lib.scan_block4(At, rt)
     for _ in range(5):
         again = gpu_lib.scan_block4(At, rt)
         assert torch.equal(first, again)
+    x_ref = ref.forward_substitution(A[:1, :, :, :, :8].astype(np.float32).astype(np.float64),
+                                     r[:1, :, :, :8].astype(np.float32).astype(np.float64))
+    assert float(np.max(np.abs(to_np(first[:1, :, :, :8]) - x_ref))) < 2e-5 * max(1.0, float(np.max(np.abs(x_ref))))
+
+
+def test_warm_start_and_newton_are_deterministic(gpu_lib):
+    w = by_name("sigmoid_bf16p_b16_t4096_d1024")
+    case("warm start / newton determinism B=2 T=4096 d=1024")
+    inp = draw_preactivation_inputs(w, B=2, T=4096)
+    P = inp["P"].to(DEV)
+    R = inp["R"].to(DEV)
+    w0 = gpu_lib.warm_start(P, None, w.forget)
+    S0, h0, st0 = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, w.tol)
+    for _ in range(3):
+        assert torch.equal(w0, gpu_lib.warm_start(P, None, w.forget))
+        S1, h1, st1 = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, w.tol)
+        assert torch.equal(S0, S1) and st0.max_abs_F == st1.max_abs_F
 
 
 @pytest.mark.parametrize("name,B,T", [("tiny_b2_t64_d16", None, None), ("mid_b8_t1024_d256", 2, 1024),

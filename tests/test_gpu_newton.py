@@ -142,14 +142,18 @@ def test_state_carry_across_calls(gpu_lib):
     P = inp["P"].to(DEV)
     R = inp["R"].to(DEV)
     S_full, h_full, _ = gpu_lib.newton_forward(P, R, None, w.forget, 8)
-    S1, _, _ = gpu_lib.newton_forward(P[:, :32].contiguous(), R, None, w.forget, 8)
-    S2, h2, _ = gpu_lib.newton_forward(P[:, 32:].contiguous(), R, S1[:, -1].contiguous(), w.forget, 8)
+    fin1 = torch.empty((w.B, 4, w.d_h), dtype=torch.float32, device=DEV)
+    S1, _, _ = gpu_lib.newton_forward(P[:, :32].contiguous(), R, None, w.forget, 8, final_state=fin1)
+    S2, h2, _ = gpu_lib.newton_forward(P[:, 32:].contiguous(), R, fin1, w.forget, 8)
     torch.cuda.synchronize()
+    assert torch.equal(fin1, S1[:, -1])
     assert h_rel_err(h2, h_full[:, 32:]) < H_TOL_F32
-    Sq1, _ = gpu_lib.sequential_forward(P[:, :32].contiguous(), R, None, w.forget)
-    Sq2, hq2 = gpu_lib.sequential_forward(P[:, 32:].contiguous(), R, Sq1[:, -1].contiguous(), w.forget)
+    fq1 = torch.empty((w.B, 4, w.d_h), dtype=torch.float32, device=DEV)
+    Sq1, _ = gpu_lib.sequential_forward(P[:, :32].contiguous(), R, None, w.forget, final_state=fq1)
+    Sq2, hq2 = gpu_lib.sequential_forward(P[:, 32:].contiguous(), R, fq1, w.forget)
     Sq, hq = gpu_lib.sequential_forward(P, R, None, w.forget)
     torch.cuda.synchronize()
+    assert torch.equal(fq1, Sq1[:, -1])
     assert torch.equal(hq2, hq[:, 32:])
 
 
