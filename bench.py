@@ -57,6 +57,7 @@ def kernel_work(w, n_e, p_bytes):
         "scan_block4": ("hbm", n_e * (JAC_BYTES + 16 + 16)),                # A, rhs in; Delta out
         "update": ("hbm", n_e * 48),                                        # S, Delta in; S out
         "final_residual": ("hbm", n_e * (p_bytes + 16)),                    # P, S in
+        "newton_iteration": ("hbm", n_e * (p_bytes + 16 + 16)),             # P, S_k in; S_k+1 out
     }
 
 
@@ -71,7 +72,10 @@ def source_sha(paths):
 KERNEL_SOURCES = {
     "residual_jacobian": ["recurrent_nets_amd/csrc/k_residual.hip", "recurrent_nets_amd/csrc/cell.h",
                           "recurrent_nets_amd/csrc/common.h"],
-    "scan_block4": ["recurrent_nets_amd/csrc/k_scan.hip", "recurrent_nets_amd/csrc/common.h"],
+    "scan_block4": ["recurrent_nets_amd/csrc/k_scan.hip", "recurrent_nets_amd/csrc/affine4.h",
+                    "recurrent_nets_amd/csrc/common.h"],
+    "newton_iteration": ["recurrent_nets_amd/csrc/k_newton_fused.hip", "recurrent_nets_amd/csrc/affine4.h",
+                         "recurrent_nets_amd/csrc/cell.h", "recurrent_nets_amd/csrc/common.h"],
     "update": ["recurrent_nets_amd/csrc/k_update.hip", "recurrent_nets_amd/csrc/common.h"],
     "warm_start": ["recurrent_nets_amd/csrc/k_warm.hip", "recurrent_nets_amd/csrc/cell.h",
                    "recurrent_nets_amd/csrc/common.h"],
@@ -172,6 +176,8 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain device copy of 4 GiB (counter calibration runs)")
     ap.add_argument("--no-sequential-context", action="store_true")
+    ap.add_argument("--schedule", default="fused", choices=["fused", "layered"])
+    ap.add_argument("--no-layered-context", action="store_true")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -211,8 +217,6 @@ def main():
     S = torch.empty((w.B, w.T, 4, w.d_h), dtype=torch.float32, device=dev)
     H = torch.empty((w.B, w.T, w.d_h), dtype=torch.float32, device=dev)
     FS = torch.empty((w.B, 4, w.d_h), dtype=torch.float32, device=dev)
-    ws = slstm.alloc_workspace(slstm.newton_workspace_bytes(w.B, w.T, w.d_h), dev)
-    log(f"[bench] device memory in use {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
 
     if args.copy_calibration:
         src = torch.empty(2**30, dtype=torch.float32, device=dev)
@@ -224,87 +228,109 @@ def main():
         del src, dst
         log("[bench] copy calibration: 3 copies of 4 GiB done")
 
-    def step():
-        if w.on_gpu_gemm:
-            slstm.input_projection(x, W, bias, out=P)
-        slstm.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, "warm", states=S, h_out=H,
-                             final_state=FS, workspace=ws, stats=False)
-        if w.on_gpu_gemm:
-            slstm.input_projection(x_dec, W, bias, out=P_dec)
-            slstm.sequential_forward(P_dec, R, FS, w.forget, states=S_dec, h_out=H_dec)
-
-    for i in range(args.warmup):
-        step()
-        torch.cuda.synchronize()
-        log(f"[bench] warm-up step {i + 1}/{args.warmup} done")
-    st = slstm.read_stats(ws)
-    log(f"[bench] solver: iters {st.iters}, max|F| {['%.2e' % e for e in st.max_abs_F]}, "
-        f"diverged {st.diverged}")
-
-    torch.cuda.synchronize()
-    slstm.profile_reset()
-    slstm.profile_enable(True)
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    slstm.profile_enable(False)
-    ms_per_step = (t1 - t0) * 1000.0 / args.steps
-    log(f"[bench] {args.steps} timed steps: {ms_per_step:.3f} ms/step")
-
     n_e = w.state_elems
     work = kernel_work(w, n_e, p_bytes)
-    kernels = {}
-    for kind, (bound, nbytes) in work.items():
-        d = slstm.profile_durations(kind)
-        if not d:
-            continue
-        avg = sum(d) / len(d)
-        kernels[kind] = {"launches": len(d), "avg_ms": avg, "total_ms_per_step": sum(d) / args.steps,
-                         "bytes_per_launch": nbytes, "GB_s": nbytes / (avg * 1e-3) / 1e9}
-    if w.on_gpu_gemm:
-        d = slstm.profile_durations("input_projection")
-        big = d[0::2]
-        small = d[1::2]
-        M, N, K = w.B * w.T, 4 * w.d_h, w.d_in
-        flops = 2.0 * M * N * K
-        avg = sum(big) / len(big)
-        kernels["input_projection"] = {"launches": len(big), "avg_ms": avg,
-                                       "total_ms_per_step": sum(big) / args.steps,
-                                       "flops_per_launch": flops,
-                                       "bytes_per_launch": M * K * 2 + N * K * 2 + M * N * 4,
-                                       "TFLOP_s": flops / (avg * 1e-3) / 1e12}
-        seqd = slstm.profile_durations("sequential")
-        kernels["decode"] = {"launches": len(seqd) + len(small),
-                             "total_ms_per_step": (sum(seqd) + sum(small)) / args.steps}
-    dominant = max((k for k in kernels if k in work), key=lambda k: kernels[k]["total_ms_per_step"])
-    dk = kernels[dominant]
-    achieved = dk["GB_s"]
-    traffic = measured_traffic(dominant, w.name)
-    roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": traffic}
 
-    # whole-step roofline: every kernel at its own bound
-    t_roof = 0.0
-    for kind, k in kernels.items():
-        if kind in work:
-            t_roof += k["launches"] / args.steps * k["bytes_per_launch"] / (HBM_PEAK_GBS * 1e9)
-        elif kind == "input_projection":
-            t_roof += max(k["flops_per_launch"] / (BF16_PEAK_TFLOPS * 1e12),
-                          k["bytes_per_launch"] / (HBM_PEAK_GBS * 1e9))
+    def timed_run(schedule, steps, warmup):
+        ws = slstm.alloc_workspace(slstm.newton_workspace_bytes(w.B, w.T, w.d_h, schedule), dev)
+
+        def step():
+            if w.on_gpu_gemm:
+                slstm.input_projection(x, W, bias, out=P)
+            slstm.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, "warm", states=S, h_out=H,
+                                 final_state=FS, workspace=ws, stats=False, schedule=schedule)
+            if w.on_gpu_gemm:
+                slstm.input_projection(x_dec, W, bias, out=P_dec)
+                slstm.sequential_forward(P_dec, R, FS, w.forget, states=S_dec, h_out=H_dec)
+
+        for i in range(warmup):
+            step()
+            torch.cuda.synchronize()
+            log(f"[bench] {schedule}: warm-up step {i + 1}/{warmup} done")
+        st = slstm.read_stats(ws)
+        log(f"[bench] {schedule}: solver iters {st.iters}, max|F| {['%.2e' % e for e in st.max_abs_F]}, "
+            f"diverged {st.diverged}; device memory {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
+        torch.cuda.synchronize()
+        slstm.profile_reset()
+        slstm.profile_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        slstm.profile_enable(False)
+        ms = (t1 - t0) * 1000.0 / steps
+        log(f"[bench] {schedule}: {steps} timed steps, {ms:.3f} ms/step")
+        kernels = {}
+        for kind, (bound, nbytes) in work.items():
+            d = slstm.profile_durations(kind)
+            if not d:
+                continue
+            avg = sum(d) / len(d)
+            kernels[kind] = {"launches": len(d), "avg_ms": avg, "total_ms_per_step": sum(d) / steps,
+                             "bytes_per_launch": nbytes, "GB_s": nbytes / (avg * 1e-3) / 1e9}
+        if w.on_gpu_gemm:
+            d = slstm.profile_durations("input_projection")
+            big = d[0::2]
+            small = d[1::2]
+            M, N, K = w.B * w.T, 4 * w.d_h, w.d_in
+            flops = 2.0 * M * N * K
+            avg = sum(big) / len(big)
+            kernels["input_projection"] = {"launches": len(big), "avg_ms": avg,
+                                           "total_ms_per_step": sum(big) / steps,
+                                           "flops_per_launch": flops,
+                                           "bytes_per_launch": M * K * 2 + N * K * 2 + M * N * 4,
+                                           "TFLOP_s": flops / (avg * 1e-3) / 1e12}
+            seqd = slstm.profile_durations("sequential")
+            kernels["decode"] = {"launches": len(seqd) + len(small),
+                                 "total_ms_per_step": (sum(seqd) + sum(small)) / steps}
+        del ws
+        torch.cuda.empty_cache()
+        return ms, kernels, st
+
+    def roofline_of(kernels, steps, ms):
+        dominant = max((k for k in kernels if k in work), key=lambda k: kernels[k]["total_ms_per_step"])
+        achieved = kernels[dominant]["GB_s"]
+        roof = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(dominant, w.name)}
+        # whole-step roofline: every kernel at its own bound
+        t_roof = 0.0
+        for kind, k in kernels.items():
+            if kind in work:
+                t_roof += k["launches"] / steps * k["bytes_per_launch"] / (HBM_PEAK_GBS * 1e9)
+            elif kind == "input_projection":
+                t_roof += max(k["flops_per_launch"] / (BF16_PEAK_TFLOPS * 1e12),
+                              k["bytes_per_launch"] / (HBM_PEAK_GBS * 1e9))
+        return roof, t_roof / (ms * 1e-3)
+
+    def rounded(kernels):
+        return {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+                for k, v in kernels.items()}
+
+    ms_per_step, kernels, st = timed_run(args.schedule, args.steps, args.warmup)
+    roofline, step_frac = roofline_of(kernels, args.steps, ms_per_step)
     value = n_e / (ms_per_step * 1e-3)
-
-    context = {"step_roofline_frac": round(t_roof / (ms_per_step * 1e-3), 4),
-               "kernels": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
-                               for kk, vv in v.items()} for k, v in kernels.items()},
+    context = {"schedule": args.schedule, "step_roofline_frac": round(step_frac, 4),
+               "kernels": rounded(kernels),
                "solver": {"iters": st.iters, "max_abs_F": st.max_abs_F, "diverged": st.diverged}}
     if w.on_gpu_gemm:
         gk = kernels["input_projection"]
         context["gemm"] = {"TFLOP_s": round(gk["TFLOP_s"], 1), "peak": BF16_PEAK_TFLOPS,
                            "frac": round(gk["TFLOP_s"] / BF16_PEAK_TFLOPS, 4),
                            "traffic": measured_traffic("input_projection", w.name)}
+    if not args.no_layered_context and args.schedule != "layered":
+        # the layered schedule: kernels (a) residual + Jacobian, (b) scan, (c) update
+        lsteps = max(2, args.steps // 2)
+        lms, lkernels, _ = timed_run("layered", lsteps, 1)
+        lroof, _ = roofline_of(lkernels, lsteps, lms)
+        a, b = lkernels["residual_jacobian"], lkernels["scan_block4"]
+        ab_gbs = (a["bytes_per_launch"] + b["bytes_per_launch"]) / ((a["avg_ms"] + b["avg_ms"]) * 1e-3) / 1e9
+        context["layered"] = {"ms_per_step": round(lms, 4), "state_elems_per_s": n_e / (lms * 1e-3),
+                              "roofline": lroof,
+                              "residual_plus_scan": {"achieved": round(ab_gbs, 1), "peak": HBM_PEAK_GBS,
+                                                     "unit": "GB/s", "frac": round(ab_gbs / HBM_PEAK_GBS, 4)},
+                              "kernels": rounded(lkernels)}
 
     if not args.no_sequential_context:
         # the lane-parallel sequential forward on the same P, for context (not the metric)

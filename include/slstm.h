@@ -64,6 +64,14 @@ typedef enum { SLSTM_FORGET_EXP = 0, SLSTM_FORGET_SIGMOID = 1 } slstm_forget;
 /* initial Newton iterate: the trajectory with the recurrent term R h_{t-1} dropped, or zeros */
 typedef enum { SLSTM_INIT_WARM = 0, SLSTM_INIT_ZERO = 1 } slstm_init;
 
+/* How a Newton iteration is laid out in kernels (same iterates up to float32 rounding):
+ *  SLSTM_SCHEDULE_FUSED    one kernel per iteration: residual, Jacobian, scan and update in
+ *                          registers; reads P and the iterate, writes the next iterate
+ *                          (double-buffered in the workspace);
+ *  SLSTM_SCHEDULE_LAYERED  three kernels per iteration: (a) residual + Jacobian to HBM in the
+ *                          scan_block4 layout, (b) the 4x4 affine scan, (c) the update. */
+typedef enum { SLSTM_SCHEDULE_FUSED = 0, SLSTM_SCHEDULE_LAYERED = 1 } slstm_schedule;
+
 #define SLSTM_MAX_ITERS 64
 
 /* Newton bookkeeping ([LY] NewtonStats). max_abs_F[k] = max |F| over all (b, t, slot, j) at
@@ -81,8 +89,9 @@ const char* slstm_status_string(slstm_status s);
 /* Detail of the last negative status returned on the calling thread ("" if none). */
 const char* slstm_last_error(void);
 
-/* Bytes of device workspace slstm_newton_forward needs for these sizes (0 if invalid). */
-size_t slstm_newton_workspace_bytes(int B, int T, int d_h);
+/* Bytes of device workspace slstm_newton_forward needs for these sizes and schedule (0 if
+ * invalid). */
+size_t slstm_newton_workspace_bytes(int B, int T, int d_h, slstm_schedule schedule);
 
 /*
  * Newton-parallel forward ([SL] "API notes": solver='newton'; [LY] "Current surface"): the
@@ -103,9 +112,11 @@ size_t slstm_newton_workspace_bytes(int B, int T, int d_h);
  *  h_out        optional output (B, T, d_h); final_state optional output (B, 4, d_h)
  *  fmode        forget-gate form; max_iters in 1..64; tol >= 0 (0: fixed iteration count)
  *  init         SLSTM_INIT_WARM (default reading) or SLSTM_INIT_ZERO
- *  workspace    >= slstm_newton_workspace_bytes(B, T, d_h) bytes of device memory; holds the
- *               Jacobians, the right-hand sides / Newton steps and the solver control block
- *               (later readable with slstm_newton_read_stats)
+ *  schedule     SLSTM_SCHEDULE_FUSED or SLSTM_SCHEDULE_LAYERED (see above)
+ *  workspace    >= slstm_newton_workspace_bytes(B, T, d_h, schedule) bytes of device memory;
+ *               holds the solver control block (later readable with slstm_newton_read_stats)
+ *               and look-back words, plus the second iterate buffer (fused) or the Jacobians
+ *               and right-hand sides / Newton steps (layered)
  *  stats        NULL: fully asynchronous, returns SLSTM_OK once everything is enqueued.
  *               non-NULL: waits for the stream, fills *stats and returns SLSTM_DIVERGED or
  *               SLSTM_NONFINITE when the flags say so (outputs are still written).
@@ -113,9 +124,9 @@ size_t slstm_newton_workspace_bytes(int B, int T, int d_h);
 slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const float* R,
                                   const float* state0, float* states, float* h_out,
                                   float* final_state, int B, int T, int d_h, slstm_forget fmode,
-                                  int max_iters, float tol,
-                                  slstm_init init, void* workspace, size_t workspace_bytes,
-                                  void* stream, slstm_newton_stats* stats);
+                                  int max_iters, float tol, slstm_init init,
+                                  slstm_schedule schedule, void* workspace,
+                                  size_t workspace_bytes, void* stream, slstm_newton_stats* stats);
 
 /* Waits for `stream` and copies the stats of the last slstm_newton_forward that used this
  * workspace into *stats; returns the status that call would have returned with stats. */
@@ -192,7 +203,8 @@ typedef enum {
   SLSTM_KERNEL_FINAL_RESIDUAL = 4,
   SLSTM_KERNEL_INPUT_PROJECTION = 5,
   SLSTM_KERNEL_SEQUENTIAL = 6,
-  SLSTM_KERNEL_KINDS = 7
+  SLSTM_KERNEL_NEWTON_ITERATION = 7,
+  SLSTM_KERNEL_KINDS = 8
 } slstm_kernel_kind;
 
 slstm_status slstm_profile_enable(int on);

@@ -109,18 +109,28 @@ slstm_status check_dims(int B, int T, int d) {
 }
 
 struct NewtonLayout {
-  size_t ctl, desc, A, rhs, total;
+  size_t ctl, desc, A, rhs, S2, total;
 };
 
-NewtonLayout newton_layout(int B, int T, int d) {
+// control block, look-back words, then either the second iterate buffer (fused) or the
+// Jacobians and right-hand sides (layered)
+NewtonLayout newton_layout(int B, int T, int d, slstm_schedule schedule) {
   NewtonLayout L;
-  const size_t desc_words = std::max(slstm::scan_desc_words(B, T, d, true), slstm::warm_desc_words(B, T, d));
   const size_t n_state = static_cast<size_t>(B) * T * 4 * d;
   L.ctl = 0;
   L.desc = align_up(sizeof(Control));
-  L.A = align_up(L.desc + desc_words * 8);
-  L.rhs = align_up(L.A + 4 * n_state * sizeof(float));
-  L.total = align_up(L.rhs + n_state * sizeof(float));
+  if (schedule == SLSTM_SCHEDULE_FUSED) {
+    const size_t desc_words = std::max(slstm::fused_desc_words(B, T, d), slstm::warm_desc_words(B, T, d));
+    L.S2 = align_up(L.desc + desc_words * 8);
+    L.A = L.rhs = 0;
+    L.total = align_up(L.S2 + n_state * sizeof(float));
+  } else {
+    const size_t desc_words = std::max(slstm::scan_desc_words(B, T, d, true), slstm::warm_desc_words(B, T, d));
+    L.A = align_up(L.desc + desc_words * 8);
+    L.rhs = align_up(L.A + 4 * n_state * sizeof(float));
+    L.S2 = 0;
+    L.total = align_up(L.rhs + n_state * sizeof(float));
+  }
   return L;
 }
 
@@ -211,17 +221,18 @@ const char* slstm_status_string(slstm_status s) {
 
 const char* slstm_last_error(void) { return g_err; }
 
-size_t slstm_newton_workspace_bytes(int B, int T, int d_h) {
+size_t slstm_newton_workspace_bytes(int B, int T, int d_h, slstm_schedule schedule) {
   if (check_dims(B, T, d_h) != SLSTM_OK) return 0;
-  return newton_layout(B, T, d_h).total;
+  if (schedule != SLSTM_SCHEDULE_FUSED && schedule != SLSTM_SCHEDULE_LAYERED) return 0;
+  return newton_layout(B, T, d_h, schedule).total;
 }
 
 slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const float* R,
                                   const float* state0, float* states, float* h_out,
                                   float* final_state, int B, int T, int d_h, slstm_forget fmode,
-                                  int max_iters, float tol,
-                                  slstm_init init, void* workspace, size_t workspace_bytes,
-                                  void* stream, slstm_newton_stats* stats) {
+                                  int max_iters, float tol, slstm_init init,
+                                  slstm_schedule schedule, void* workspace,
+                                  size_t workspace_bytes, void* stream, slstm_newton_stats* stats) {
   g_err[0] = '\0';
   slstm_status s = check_common(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, fmode);
   if (s != SLSTM_OK) return s;
@@ -229,9 +240,11 @@ slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const floa
     return fail(SLSTM_EINVAL, "max_iters must be in 1..%d (got %d)", SLSTM_MAX_ITERS, max_iters);
   if (!(tol >= 0.0f) || std::isinf(tol)) return fail(SLSTM_EINVAL, "tol must be finite and >= 0");
   if (init != SLSTM_INIT_WARM && init != SLSTM_INIT_ZERO) return fail(SLSTM_EINVAL, "unknown init %d", (int)init);
+  if (schedule != SLSTM_SCHEDULE_FUSED && schedule != SLSTM_SCHEDULE_LAYERED)
+    return fail(SLSTM_EINVAL, "unknown schedule %d", (int)schedule);
   if (workspace == nullptr || !aligned(workspace, kAlign))
     return fail(SLSTM_EINVAL, "workspace must be non-NULL and 256-byte aligned");
-  const NewtonLayout L = newton_layout(B, T, d_h);
+  const NewtonLayout L = newton_layout(B, T, d_h, schedule);
   if (workspace_bytes < L.total)
     return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
 
@@ -240,38 +253,64 @@ slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const floa
   const bool sig = fmode == SLSTM_FORGET_SIGMOID;
   Control* ctl = at<Control>(workspace, L.ctl);
   auto* desc = at<unsigned long long>(workspace, L.desc);
-  float* A = at<float>(workspace, L.A);
-  float* rhs = at<float>(workspace, L.rhs);
   const i64 n_state = static_cast<i64>(B) * T * 4 * d_h;
+
+  // iterate buffers: the layered schedule updates `states` in place; the fused one alternates
+  // between `states` and a workspace buffer, arranged so that iterate max_iters lands in
+  // `states` (iterate k lives in buf[k % 2])
+  float* buf[2] = {states, states};
+  if (schedule == SLSTM_SCHEDULE_FUSED) {
+    float* other = at<float>(workspace, L.S2);
+    buf[0] = (max_iters % 2 == 0) ? states : other;
+    buf[1] = (max_iters % 2 == 0) ? other : states;
+  }
 
   HIP_TRY(slstm::launch_init_control(ctl, st));
   if (init == SLSTM_INIT_WARM) {
     const uint32_t ep = next_epoch();
     HIP_TRY(timed(SLSTM_KERNEL_WARM_START, st, [&] {
-      return slstm::launch_warm_start(P, bf16, state0, states, B, T, d_h, sig, desc, &ctl->ticket_warm, ep, st);
+      return slstm::launch_warm_start(P, bf16, state0, buf[0], B, T, d_h, sig, desc, &ctl->ticket_warm, ep, st);
     }));
   } else {
-    HIP_TRY(slstm::launch_zero(states, n_state, st));
+    HIP_TRY(slstm::launch_zero(buf[0], n_state, st));
   }
-  for (int k = 0; k < max_iters; ++k) {
-    HIP_TRY(timed(SLSTM_KERNEL_RESIDUAL_JACOBIAN, st, [&] {
-      return slstm::launch_residual(P, bf16, R, state0, states, A, rhs, B, T, d_h, sig, ctl,
-                                    &ctl->err_bits[k], slstm::ResidualMode::kSparse, st);
-    }));
-    const uint32_t ep = next_epoch();
-    HIP_TRY(timed(SLSTM_KERNEL_SCAN_BLOCK4, st, [&] {
-      return slstm::launch_scan_block4(A, rhs, rhs, B, T, d_h, true, desc, &ctl->ticket_scan, ep, ctl, k,
-                                       tol, st);
-    }));
-    HIP_TRY(timed(SLSTM_KERNEL_UPDATE, st, [&] { return slstm::launch_update(states, rhs, n_state, ctl, k, st); }));
+  if (schedule == SLSTM_SCHEDULE_FUSED) {
+    for (int k = 0; k < max_iters; ++k) {
+      const uint32_t ep = next_epoch();
+      HIP_TRY(timed(SLSTM_KERNEL_NEWTON_ITERATION, st, [&] {
+        return slstm::launch_newton_iteration(P, bf16, R, state0, buf[k % 2], buf[(k + 1) % 2], B, T, d_h,
+                                              sig, desc, &ctl->ticket_scan, ep, ctl, k, tol, st);
+      }));
+    }
+  } else {
+    float* A = at<float>(workspace, L.A);
+    float* rhs = at<float>(workspace, L.rhs);
+    for (int k = 0; k < max_iters; ++k) {
+      HIP_TRY(timed(SLSTM_KERNEL_RESIDUAL_JACOBIAN, st, [&] {
+        return slstm::launch_residual(P, bf16, R, state0, states, A, rhs, B, T, d_h, sig, ctl,
+                                      &ctl->err_bits[k], slstm::ResidualMode::kSparse, -1, tol, st);
+      }));
+      const uint32_t ep = next_epoch();
+      HIP_TRY(timed(SLSTM_KERNEL_SCAN_BLOCK4, st, [&] {
+        return slstm::launch_scan_block4(A, rhs, rhs, B, T, d_h, true, desc, &ctl->ticket_scan, ep, ctl, k,
+                                         tol, st);
+      }));
+      HIP_TRY(timed(SLSTM_KERNEL_UPDATE, st, [&] { return slstm::launch_update(states, rhs, n_state, ctl, k, st); }));
+    }
   }
+  // residual of the last iterate (the fused schedule first checks whether the iterate before it
+  // already met the tolerance)
+  const int chk = (schedule == SLSTM_SCHEDULE_FUSED) ? max_iters - 1 : -1;
   HIP_TRY(timed(SLSTM_KERNEL_FINAL_RESIDUAL, st, [&] {
-    return slstm::launch_residual(P, bf16, R, state0, states, nullptr, nullptr, B, T, d_h, sig, ctl,
-                                  &ctl->err_bits[max_iters], slstm::ResidualMode::kNone, st);
+    return slstm::launch_residual(P, bf16, R, state0, buf[max_iters % 2], nullptr, nullptr, B, T, d_h, sig,
+                                  ctl, &ctl->err_bits[max_iters], slstm::ResidualMode::kNone, chk, tol, st,
+                                  h_out);
   }));
+  if (schedule == SLSTM_SCHEDULE_FUSED)
+    HIP_TRY(slstm::launch_select_iterate(ctl, buf[0], buf[1], states, n_state, st));
   HIP_TRY(slstm::launch_finalize(ctl, tol, st));
   if (h_out != nullptr || final_state != nullptr)
-    HIP_TRY(slstm::launch_outputs(states, h_out, final_state, B, T, d_h, st));
+    HIP_TRY(slstm::launch_outputs(states, h_out, final_state, B, T, d_h, ctl, st));
   if (stats == nullptr) return SLSTM_OK;
   Control host;
   HIP_TRY(hipMemcpyAsync(&host, ctl, sizeof(Control), hipMemcpyDeviceToHost, st));
@@ -341,7 +380,8 @@ slstm_status slstm_residual_jacobian(const void* P, slstm_dtype P_dtype, const f
   HIP_TRY(hipGetLastError());
   HIP_TRY(timed(SLSTM_KERNEL_RESIDUAL_JACOBIAN, st, [&] {
     return slstm::launch_residual(P, P_dtype == SLSTM_BF16, R, state0, states, A, rhs, B, T, d_h,
-                                  fmode == SLSTM_FORGET_SIGMOID, nullptr, err, slstm::ResidualMode::kDense, st);
+                                  fmode == SLSTM_FORGET_SIGMOID, nullptr, err, slstm::ResidualMode::kDense, -1,
+                                  0.0f, st);
   }));
   return SLSTM_OK;
 }

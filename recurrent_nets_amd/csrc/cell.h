@@ -18,12 +18,23 @@ struct CellIn {
   float c, n, m, h;  // previous state
 };
 
-// sigma(x) = 1 / (1 + e^-x)
-__device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + expf(-x)); }
+// Transcendentals on the hardware units, from their defining identities. Each is within a
+// few units in the last place of float32 where its value carries weight (absolute error
+// around 1e-7 where it is small), which is well inside the state's float32 rounding floor.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
-// log sigma(x) = -softplus(-x), written so that it stays finite for any finite x.
+// e^x = 2^(x log2 e) (v_exp_f32)
+__device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+// 1 / x (v_rcp_f32)
+__device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
+// sigma(x) = 1 / (1 + e^-x)
+__device__ __forceinline__ float sigmoidf(float x) { return rcp_fast(1.0f + exp_fast(-x)); }
+// tanh x = 1 - 2 / (1 + e^{2x})
+__device__ __forceinline__ float tanh_fast(float x) { return 1.0f - 2.0f * rcp_fast(1.0f + exp_fast(2.0f * x)); }
+// log sigma(x) = -softplus(-x) = -(max(-x, 0) + ln(1 + e^{-|x|})), finite for any finite x
 __device__ __forceinline__ float log_sigmoidf(float x) {
-  return -(fmaxf(-x, 0.0f) + log1pf(expf(-fabsf(x))));
+  return -(fmaxf(-x, 0.0f) + kLn2 * __builtin_amdgcn_logf(1.0f + exp_fast(-fabsf(x))));
 }
 
 // One step. Writes the next state s[4] = (c, n, m, h); with JAC also A[16] row-major
@@ -36,7 +47,7 @@ __device__ __forceinline__ void cell_step(const CellIn& pv, float pz, float pi, 
   const float it = fmaf(ri, pv.h, pi);
   const float ft = fmaf(rf, pv.h, pf);
   const float ot = fmaf(ro, pv.h, po);
-  const float z = tanhf(zt);
+  const float z = tanh_fast(zt);
   const float o = sigmoidf(ot);
   float lf, dlf;
   if (sig_forget) {
@@ -49,11 +60,12 @@ __device__ __forceinline__ void cell_step(const CellIn& pv, float pz, float pi, 
   const float a = lf + pv.m;
   const bool beta = a >= it;
   const float m = beta ? a : it;
-  const float ig = expf(it - m);
-  const float fg = expf(a - m);
+  const float ig = exp_fast(it - m);
+  const float fg = exp_fast(a - m);
   const float c = fmaf(fg, pv.c, ig * z);
   const float n = fmaf(fg, pv.n, ig);
-  const float h = o * c / n;
+  const float rn = rcp_fast(n);
+  const float h = o * c * rn;
   s[0] = c;
   s[1] = n;
   s[2] = m;
@@ -73,15 +85,15 @@ __device__ __forceinline__ void cell_step(const CellIn& pv, float pz, float pi, 
     const float n_m = pv.n * dfg_dm + dig_dm;
     const float n_h = pv.n * dfg_dh + dig_dh;
     // row h = o c / n: (o/n) dc - (o c / n^2) dn, plus (c/n) do on h'
-    const float q1 = o / n;
-    const float q2 = h / n;
+    const float q1 = o * rn;
+    const float q2 = h * rn;
     A[0] = fg;     A[1] = 0.0f;   A[2] = c_m;   A[3] = c_h;
     A[4] = 0.0f;   A[5] = fg;     A[6] = n_m;   A[7] = n_h;
     A[8] = 0.0f;   A[9] = 0.0f;   A[10] = b;    A[11] = dm_dh;
     A[12] = q1 * fg;
     A[13] = -q2 * fg;
     A[14] = q1 * c_m - q2 * n_m;
-    A[15] = q1 * c_h - q2 * n_h + (c / n) * do_dh;
+    A[15] = q1 * c_h - q2 * n_h + (c * rn) * do_dh;
   }
 }
 

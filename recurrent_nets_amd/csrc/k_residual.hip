@@ -11,7 +11,8 @@
 //   kJacSparse  the 12 planes that are not structural zeros of the channelwise cell
 //               ((c, n'), (n, c'), (m, c'), (m, n') are never written); the Newton solver's
 //               scan reads exactly these;
-//   kJacNone    no Jacobian and no right-hand side: the residual maximum only.
+//   kJacNone    no Jacobian and no right-hand side: the residual maximum only (the pass over
+//               the final iterate, which also writes the hidden slot out when asked).
 //
 // Mapping: grid (feature tiles of 64, groups of 4 time chunks, batch). Each wave owns 64
 // consecutive features of one batch row and one chunk of kResChunk consecutive steps, so
@@ -37,9 +38,18 @@ template <bool BF16, int JMODE>
 __global__ __launch_bounds__(kResBlock, 2) void residual_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S, float* __restrict__ A, float* __restrict__ rhs, int T, int d,
-    int n_chunks, int sig_forget, const Control* __restrict__ ctl,
-    unsigned int* __restrict__ err_dst) {
-  if (ctl != nullptr && ctl->stopped) return;
+    int n_chunks, int sig_forget, Control* __restrict__ ctl, unsigned int* __restrict__ err_dst,
+    int stop_check_iter, float tol, float* __restrict__ h_out) {
+  if (ctl != nullptr) {
+    if (ctl->stopped) return;
+    if (stop_check_iter >= 0 && tol > 0.0f && __uint_as_float(ctl->err_bits[stop_check_iter]) < tol) {
+      if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {
+        ctl->stopped = 1;
+        ctl->iters = stop_check_iter;
+      }
+      return;
+    }
+  }
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int l = threadIdx.x & (kWave - 1);
   const int b = blockIdx.z;
@@ -103,6 +113,7 @@ __global__ __launch_bounds__(kResBlock, 2) void residual_kernel(
 #pragma unroll
         for (int q = 0; q < 12; ++q) Ap[kSparsePlanes[q] * ud + j] = Aj[kSparsePlanes[q]];
       }
+      if (h_out != nullptr) h_out[row * static_cast<i64>(d) + j] = st[3];
       pv = {st[0], st[1], st[2], st[3]};
     }
   }
@@ -122,22 +133,24 @@ __global__ __launch_bounds__(kResBlock, 2) void residual_kernel(
 template <bool BF16>
 static void launch_mode(int mode, dim3 grid, hipStream_t stream, const void* P, const float* R,
                         const float* state0, const float* S, float* A, float* rhs, int T, int d,
-                        int n_chunks, int sig, const Control* ctl, unsigned int* err_dst) {
+                        int n_chunks, int sig, Control* ctl, unsigned int* err_dst, int chk,
+                        float tol, float* h_out) {
   if (mode == kJacDense)
     residual_kernel<BF16, kJacDense><<<grid, kResBlock, 0, stream>>>(P, R, state0, S, A, rhs, T, d,
-                                                                      n_chunks, sig, ctl, err_dst);
+                                                                      n_chunks, sig, ctl, err_dst, chk, tol, h_out);
   else if (mode == kJacSparse)
     residual_kernel<BF16, kJacSparse><<<grid, kResBlock, 0, stream>>>(P, R, state0, S, A, rhs, T, d,
-                                                                       n_chunks, sig, ctl, err_dst);
+                                                                       n_chunks, sig, ctl, err_dst, chk, tol, h_out);
   else
     residual_kernel<BF16, kJacNone><<<grid, kResBlock, 0, stream>>>(P, R, state0, S, nullptr, nullptr,
-                                                                     T, d, n_chunks, sig, ctl, err_dst);
+                                                                     T, d, n_chunks, sig, ctl, err_dst, chk, tol, h_out);
 }
 
 hipError_t launch_residual(const void* P, bool p_bf16, const float* R, const float* state0,
                            const float* S, float* A, float* rhs, int B, int T, int d,
-                           bool sig_forget, const Control* ctl, unsigned int* err_dst,
-                           ResidualMode mode, hipStream_t stream) {
+                           bool sig_forget, Control* ctl, unsigned int* err_dst,
+                           ResidualMode mode, int stop_check_iter, float tol, hipStream_t stream,
+                           float* h_out) {
   const int n_chunks = (T + kResChunk - 1) / kResChunk;
   const unsigned gx = static_cast<unsigned>((d + kWave - 1) / kWave);
   const unsigned gy = static_cast<unsigned>((n_chunks + kResWaves - 1) / kResWaves);
@@ -146,9 +159,11 @@ hipError_t launch_residual(const void* P, bool p_bf16, const float* R, const flo
   const int sig = sig_forget ? 1 : 0;
   const int m = mode == ResidualMode::kDense ? kJacDense : (mode == ResidualMode::kSparse ? kJacSparse : kJacNone);
   if (p_bf16)
-    launch_mode<true>(m, grid, stream, P, R, state0, S, A, rhs, T, d, n_chunks, sig, ctl, err_dst);
+    launch_mode<true>(m, grid, stream, P, R, state0, S, A, rhs, T, d, n_chunks, sig, ctl, err_dst,
+                      stop_check_iter, tol, h_out);
   else
-    launch_mode<false>(m, grid, stream, P, R, state0, S, A, rhs, T, d, n_chunks, sig, ctl, err_dst);
+    launch_mode<false>(m, grid, stream, P, R, state0, S, A, rhs, T, d, n_chunks, sig, ctl, err_dst,
+                       stop_check_iter, tol, h_out);
   return hipGetLastError();
 }
 

@@ -28,6 +28,7 @@
 // SPARSE: the sLSTM Jacobian has four structural zeros ((c, n'), (n, c'), (m, c'), (m, n'));
 // the Newton solver's scan reads only the other 12 planes and multiplies with them alone
 // (48 instead of 64 FMA per 4x4 product). The dense form serves arbitrary 4x4 maps.
+#include "affine4.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -36,77 +37,7 @@ namespace slstm {
 constexpr int kScanBlock = 256;
 constexpr int kScanTSubSparse = 8;  // sub-chunk length of the Newton solver's sparse scan
 constexpr int kScanTSubDense = 4;   // and of the dense scan (16 values per step in registers)
-constexpr int kScanWords = 24;      // per lane and tile: x_end (4), M (16), v (4)
-
-__device__ constexpr int kSpPlane[12] = {0, 2, 3, 5, 6, 7, 10, 11, 12, 13, 14, 15};
-
-// y = X v + w
-__device__ __forceinline__ void mat4_vec(const float X[16], const float v[4], const float w[4],
-                                         float y[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    y[i] = fmaf(X[4 * i + 0], v[0], fmaf(X[4 * i + 1], v[1], fmaf(X[4 * i + 2], v[2], fmaf(X[4 * i + 3], v[3], w[i]))));
-}
-
-// Y <- A Y with A given by its 12 non-structural entries (order of kSpPlane); in place,
-// column by column (column k of A Y needs only column k of Y)
-__device__ __forceinline__ void sp_mul_left(const float a[12], float Y[16]) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float y0 = Y[k], y1 = Y[4 + k], y2 = Y[8 + k], y3 = Y[12 + k];
-    Y[k] = fmaf(a[0], y0, fmaf(a[1], y2, a[2] * y3));
-    Y[4 + k] = fmaf(a[3], y1, fmaf(a[4], y2, a[5] * y3));
-    Y[8 + k] = fmaf(a[6], y2, a[7] * y3);
-    Y[12 + k] = fmaf(a[8], y0, fmaf(a[9], y1, fmaf(a[10], y2, a[11] * y3)));
-  }
-}
-
-// Y <- X Y for a dense X; in place, column by column
-__device__ __forceinline__ void mat4_mul_left(const float X[16], float Y[16]) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const float y0 = Y[k], y1 = Y[4 + k], y2 = Y[8 + k], y3 = Y[12 + k];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      Y[4 * i + k] = fmaf(X[4 * i], y0, fmaf(X[4 * i + 1], y1, fmaf(X[4 * i + 2], y2, X[4 * i + 3] * y3)));
-  }
-}
-
-// y = A v + w, A sparse
-__device__ __forceinline__ void sp_vec(const float a[12], const float v[4], const float w[4],
-                                       float y[4]) {
-  y[0] = fmaf(a[0], v[0], fmaf(a[1], v[2], fmaf(a[2], v[3], w[0])));
-  y[1] = fmaf(a[3], v[1], fmaf(a[4], v[2], fmaf(a[5], v[3], w[1])));
-  y[2] = fmaf(a[6], v[2], fmaf(a[7], v[3], w[2]));
-  y[3] = fmaf(a[8], v[0], fmaf(a[9], v[1], fmaf(a[10], v[2], fmaf(a[11], v[3], w[3]))));
-}
-
-// (M, v) <- (M, v) o (Mp, vp): apply (Mp, vp) first, then (M, v). In place, row by row: the
-// new v needs the old M, and row i of the new M needs only row i of the old M.
-__device__ __forceinline__ void compose_after(float M[16], float v[4], const float Mp[16],
-                                              const float vp[4]) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    v[i] = fmaf(M[4 * i], vp[0], fmaf(M[4 * i + 1], vp[1], fmaf(M[4 * i + 2], vp[2], fmaf(M[4 * i + 3], vp[3], v[i]))));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float row[4];
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      row[k] = fmaf(M[4 * i], Mp[k], fmaf(M[4 * i + 1], Mp[4 + k], fmaf(M[4 * i + 2], Mp[8 + k], M[4 * i + 3] * Mp[12 + k])));
-#pragma unroll
-    for (int k = 0; k < 4; ++k) M[4 * i + k] = row[k];
-  }
-}
-
-template <int S0, int S1, int S2, int S3>
-__device__ __forceinline__ void quad_perm_map(const float M[16], const float v[4], float Mp[16],
-                                              float vp[4]) {
-#pragma unroll
-  for (int e = 0; e < 16; ++e) Mp[e] = quad_perm<S0, S1, S2, S3>(M[e]);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) vp[e] = quad_perm<S0, S1, S2, S3>(v[e]);
-}
+constexpr int kScanWords = kLookBackWords;
 
 template <bool SPARSE, int TSUB>
 __global__ __launch_bounds__(kScanBlock, 2) void scan_block4_kernel(
@@ -217,13 +148,7 @@ __global__ __launch_bounds__(kScanBlock, 2) void scan_block4_kernel(
   }
 
   // ---- level 2: inclusive scan of the quad's sub-chunk aggregates (DPP) ----
-  {
-    float Mp[16], vp[4];
-    quad_perm_map<0, 0, 1, 2>(M, v, Mp, vp);  // from sub-chunk sc - 1
-    if (sc >= 1) compose_after(M, v, Mp, vp);
-    quad_perm_map<0, 1, 0, 1>(M, v, Mp, vp);  // from sub-chunk sc - 2
-    if (sc >= 2) compose_after(M, v, Mp, vp);
-  }
+  quad_inclusive_scan(M, v, sc);
   if (sc == 3) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) s_agg[lane_in_tile][e] = M[e];
@@ -233,60 +158,10 @@ __global__ __launch_bounds__(kScanBlock, 2) void scan_block4_kernel(
   __syncthreads();
 
   // ---- level 3: look-back across tiles, one thread per lane of the tile ----
-  // Fixed dataflow, so results do not depend on scheduling: tiles whose index is a multiple
-  // of the anchor stride publish their inclusive value; the others publish their aggregate
-  // before waiting. A tile folds the aggregates of its predecessors down to the nearest
-  // anchor, always in the same order, and applies the anchor's inclusive value.
   if (wave == 0) {
-    const i64 my_lane = static_cast<i64>(lg) * 64 + l;
-    float carry[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    auto word = [&](int tile, int w) {
-      return desc + (static_cast<i64>(tile) * kScanWords + w) * n_lanes_pad + my_lane;
-    };
-    const bool anchor = (tt % anchor_stride) == 0;
-    if (!anchor) {
-#pragma unroll
-      for (int e = 0; e < 20; ++e) tag_store(word(tt, 4 + e), s_agg[l][e], epoch);
-    }
-    if (tt > 0) {
-      const int a = ((tt - 1) / anchor_stride) * anchor_stride;  // nearest anchor below
-      // accumulated map of the tiles a+1 .. tt-1
-      float Macc[16], vacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int e = 0; e < 16; ++e) Macc[e] = (e % 5 == 0) ? 1.0f : 0.0f;
-      for (int p = tt - 1; p > a; --p) {
-        float Mp[16], vp[4];
-        while (true) {
-          bool ok = true;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) ok &= tag_load(word(p, 4 + e), epoch, Mp[e]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ok &= tag_load(word(p, 20 + e), epoch, vp[e]);
-          if (ok) break;
-          __builtin_amdgcn_s_sleep(2);
-        }
-        compose_after(Macc, vacc, Mp, vp);
-      }
-      float xin[4];
-      while (true) {
-        bool ok = true;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ok &= tag_load(word(a, e), epoch, xin[e]);
-        if (ok) break;
-        __builtin_amdgcn_s_sleep(2);
-      }
-      mat4_vec(Macc, xin, vacc, carry);
-    }
-    if (anchor) {
-      // inclusive value at the end of this tile: x_end = M_tile carry + v_tile
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float xe = fmaf(s_agg[l][4 * i], carry[0],
-                              fmaf(s_agg[l][4 * i + 1], carry[1],
-                                   fmaf(s_agg[l][4 * i + 2], carry[2], fmaf(s_agg[l][4 * i + 3], carry[3], s_agg[l][16 + i]))));
-        tag_store(word(tt, i), xe, epoch);
-      }
-    }
+    float carry[4];
+    tile_look_back(s_agg[l], carry, desc, n_lanes_pad, static_cast<i64>(lg) * 64 + l, tt,
+                   anchor_stride, epoch);
 #pragma unroll
     for (int e = 0; e < 4; ++e) s_carry[l][e] = carry[e];
   }

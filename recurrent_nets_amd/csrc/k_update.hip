@@ -8,6 +8,8 @@
 //            not finite, convergence when a tolerance is set and met ("Layout" page of the
 //            pararnn-torch docs, "Current surface (0.17)": NewtonStats, residual early stop,
 //            divergence error when max|F| > 1 after K).
+// select:    copies the final iterate into the caller's states when an early stop left it in
+//            the fused schedule's other iterate buffer.
 // outputs:   copies the hidden slot (slot 3) of the states into a (B, T, d) output and the
 //            last step's state into a contiguous (B, 4, d) output.
 #include "common.h"
@@ -48,7 +50,10 @@ __global__ void finalize_kernel(Control* __restrict__ ctl, float tol) {
 }
 
 __global__ __launch_bounds__(kUpdBlock) void hidden_kernel(const float* __restrict__ S,
-                                                           float* __restrict__ h, i64 rows, int d) {
+                                                           float* __restrict__ h, i64 rows, int d,
+                                                           const Control* __restrict__ ctl) {
+  // the final residual pass writes h unless an early stop skipped it
+  if (ctl != nullptr && !ctl->stopped) return;
   // rows = B*T; element i of h is feature i % d of row i / d
   const i64 n = rows * d;
   const i64 stride = static_cast<i64>(gridDim.x) * kUpdBlock;
@@ -77,6 +82,16 @@ __global__ __launch_bounds__(kUpdBlock) void zero_kernel(float4* __restrict__ p,
     p[i] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 }
 
+__global__ __launch_bounds__(kUpdBlock) void select_iterate_kernel(const Control* __restrict__ ctl,
+                                                                   const float4* buf0,
+                                                                   const float4* buf1, float4* states,
+                                                                   i64 n4) {
+  const float4* src = (ctl->iters % 2 == 0) ? buf0 : buf1;
+  if (src == states) return;  // the final iterate is already in place
+  const i64 stride = static_cast<i64>(gridDim.x) * kUpdBlock;
+  for (i64 i = static_cast<i64>(blockIdx.x) * kUpdBlock + threadIdx.x; i < n4; i += stride) states[i] = src[i];
+}
+
 static unsigned int stream_grid(i64 n) {
   // enough blocks to fill 256 CUs several times over; the kernels stride the rest
   const i64 want = (n + kUpdBlock - 1) / kUpdBlock;
@@ -102,10 +117,10 @@ hipError_t launch_finalize(Control* ctl, float tol, hipStream_t stream) {
 }
 
 hipError_t launch_outputs(const float* S, float* h, float* final_state, int B, int T, int d,
-                          hipStream_t stream) {
+                          const Control* ctl, hipStream_t stream) {
   if (h != nullptr) {
     const i64 rows = static_cast<i64>(B) * T;
-    hidden_kernel<<<stream_grid(rows * d), kUpdBlock, 0, stream>>>(S, h, rows, d);
+    hidden_kernel<<<stream_grid(rows * d), kUpdBlock, 0, stream>>>(S, h, rows, d, ctl);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -113,6 +128,15 @@ hipError_t launch_outputs(const float* S, float* h, float* final_state, int B, i
     final_state_kernel<<<stream_grid(static_cast<i64>(B) * 4 * d), kUpdBlock, 0, stream>>>(
         S, final_state, B, T, d);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_select_iterate(const Control* ctl, const float* buf0, const float* buf1,
+                                 float* states, i64 n_floats, hipStream_t stream) {
+  const i64 n4 = n_floats / 4;
+  select_iterate_kernel<<<stream_grid(n4), kUpdBlock, 0, stream>>>(
+      ctl, reinterpret_cast<const float4*>(buf0), reinterpret_cast<const float4*>(buf1),
+      reinterpret_cast<float4*>(states), n4);
   return hipGetLastError();
 }
 

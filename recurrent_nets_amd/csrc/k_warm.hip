@@ -42,7 +42,7 @@ struct LogAgg {
 
 __device__ __forceinline__ float exp_or_zero(float e, float x) {
   // e^{x} for an exponent built from E; an empty run has E = -inf and weight zero
-  return (e == -INFINITY) ? 0.0f : expf(x);
+  return (e == -INFINITY) ? 0.0f : exp_fast(x);
 }
 
 // X first, then Y
@@ -61,7 +61,7 @@ __device__ __forceinline__ LogAgg compose(const LogAgg& X, const LogAgg& Y) {
 // apply a run to a carried (m, c, n)
 __device__ __forceinline__ void apply(const LogAgg& X, float& m, float& c, float& n) {
   const float x = fmaxf(m, X.E);
-  const float wc = expf(m - x);
+  const float wc = exp_fast(m - x);
   const float wz = exp_or_zero(X.E, X.E - x);
   c = fmaf(wc, c, wz * X.cz);
   n = fmaf(wc, n, wz * X.nz);
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
       const float pi = load_p<BF16>(P, tile_row + o + ud);
       const float pf = load_p<BF16>(P, tile_row + o + 2 * ud);
       const float po = load_p<BF16>(P, tile_row + o + 3 * ud);
-      zz[u] = tanhf(pz);
+      zz[u] = tanh_fast(pz);
       oo[u] = sigmoidf(po);
       it[u] = pi;
       lf[u] = sig ? log_sigmoidf(pf) : pf;
@@ -235,8 +235,8 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
     if (valid && t < T) {
       const float a = lf[u] + m;
       const float mn = (a >= it[u]) ? a : it[u];
-      const float ig = expf(it[u] - mn);
-      const float fg = expf(a - mn);
+      const float ig = exp_fast(it[u] - mn);
+      const float fg = exp_fast(a - mn);
       c = fmaf(fg, c, ig * zz[u]);
       n = fmaf(fg, n, ig);
       m = mn;
@@ -244,7 +244,7 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
       Sb[o] = c;
       Sb[o + ud] = n;
       Sb[o + 2 * ud] = m;
-      Sb[o + 3 * ud] = oo[u] * c / n;
+      Sb[o + 3 * ud] = oo[u] * c * rcp_fast(n);
     }
   }
 }

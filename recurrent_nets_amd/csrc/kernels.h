@@ -11,10 +11,25 @@ namespace slstm {
 // Jacobian planes the residual kernel writes: all 16, the 12 non-structural ones, or none
 enum class ResidualMode { kDense, kSparse, kNone };
 
+// With a control block and stop_check_iter >= 0, the launch first declares the iterate
+// stop_check_iter final (and does nothing else) when its residual maximum met tol. h_out
+// (kNone only, optional) receives the hidden slot of S.
 hipError_t launch_residual(const void* P, bool p_bf16, const float* R, const float* state0,
                            const float* S, float* A, float* rhs, int B, int T, int d,
-                           bool sig_forget, const Control* ctl, unsigned int* err_dst,
-                           ResidualMode mode, hipStream_t stream);
+                           bool sig_forget, Control* ctl, unsigned int* err_dst,
+                           ResidualMode mode, int stop_check_iter, float tol, hipStream_t stream,
+                           float* h_out = nullptr);
+
+size_t fused_desc_words(int B, int T, int d);
+hipError_t launch_newton_iteration(const void* P, bool p_bf16, const float* R, const float* state0,
+                                   const float* S_in, float* S_out, int B, int T, int d,
+                                   bool sig_forget, unsigned long long* desc, unsigned int* ticket,
+                                   uint32_t epoch, Control* ctl, int k_iter, float tol,
+                                   hipStream_t stream);
+// copies the final iterate into `states` when it ended in the other buffer (iterate k lives in
+// buf0 for even k, buf1 for odd k)
+hipError_t launch_select_iterate(const Control* ctl, const float* buf0, const float* buf1,
+                                 float* states, i64 n_floats, hipStream_t stream);
 
 size_t scan_desc_words(int B, int T, int d, bool sparse);
 hipError_t launch_scan_block4(const float* A, const float* rhs, float* x, int B, int T, int d,
@@ -31,8 +46,10 @@ hipError_t launch_update(float* S, const float* D, i64 n_floats, Control* ctl, i
                          hipStream_t stream);
 hipError_t launch_init_control(Control* ctl, hipStream_t stream);
 hipError_t launch_finalize(Control* ctl, float tol, hipStream_t stream);
+// hidden slot (unless the final residual pass already wrote it: then only after an early stop,
+// signalled by ctl) and final state
 hipError_t launch_outputs(const float* S, float* h, float* final_state, int B, int T, int d,
-                          hipStream_t stream);
+                          const Control* ctl, hipStream_t stream);
 hipError_t launch_zero(float* p, i64 n_floats, hipStream_t stream);
 
 hipError_t launch_sequential(const void* P, bool p_bf16, const float* R, const float* state0,

@@ -20,9 +20,10 @@ OK, DIVERGED, NONFINITE, EINVAL, EWORKSPACE, EHIP = 0, 1, 2, -1, -2, -3
 F32, BF16 = 0, 1
 FORGET = {"exp": 0, "sigmoid": 1}
 INIT = {"warm": 0, "zero": 1}
+SCHEDULE = {"fused": 0, "layered": 1}
 MAX_ITERS = 64
 KERNELS = {"warm_start": 0, "residual_jacobian": 1, "scan_block4": 2, "update": 3,
-           "final_residual": 4, "input_projection": 5, "sequential": 6}
+           "final_residual": 4, "input_projection": 5, "sequential": 6, "newton_iteration": 7}
 
 EXPORTED = [
     "slstm_status_string", "slstm_last_error", "slstm_newton_workspace_bytes",
@@ -84,13 +85,14 @@ def load(path: str | None = None):
     L.slstm_status_string.restype = ctypes.c_char_p
     L.slstm_status_string.argtypes = [_i]
     L.slstm_last_error.restype = ctypes.c_char_p
-    for name in ("slstm_newton_workspace_bytes", "slstm_scan_block4_workspace_bytes",
-                 "slstm_warm_start_workspace_bytes"):
+    for name in ("slstm_scan_block4_workspace_bytes", "slstm_warm_start_workspace_bytes"):
         getattr(L, name).restype = _sz
         getattr(L, name).argtypes = [_i, _i, _i]
+    L.slstm_newton_workspace_bytes.restype = _sz
+    L.slstm_newton_workspace_bytes.argtypes = [_i, _i, _i, _i]
     L.slstm_newton_forward.restype = _i
     L.slstm_newton_forward.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
-                                       _i, _vp, _sz, _vp, ctypes.POINTER(_Stats)]
+                                       _i, _i, _vp, _sz, _vp, ctypes.POINTER(_Stats)]
     L.slstm_newton_read_stats.restype = _i
     L.slstm_newton_read_stats.argtypes = [_vp, _sz, _vp, ctypes.POINTER(_Stats)]
     L.slstm_sequential_forward.restype = _i
@@ -158,8 +160,8 @@ def _shape_check(P, R, state0):
     return B, T, d
 
 
-def newton_workspace_bytes(B: int, T: int, d_h: int) -> int:
-    return int(load().slstm_newton_workspace_bytes(B, T, d_h))
+def newton_workspace_bytes(B: int, T: int, d_h: int, schedule: str = "fused") -> int:
+    return int(load().slstm_newton_workspace_bytes(B, T, d_h, SCHEDULE[schedule]))
 
 
 def alloc_workspace(nbytes: int, device=None) -> torch.Tensor:
@@ -169,10 +171,11 @@ def alloc_workspace(nbytes: int, device=None) -> torch.Tensor:
 
 def newton_forward(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, init="warm",
                    states=None, h_out=None, want_hidden=True, final_state=None, workspace=None,
-                   stream=None, stats=True, raise_on_divergence=True):
+                   stream=None, stats=True, raise_on_divergence=True, schedule="fused"):
     """Newton-parallel forward. Returns (states (B,T,4,d_h), h (B,T,d_h) or None, NewtonStats
     or None). With stats=False the call is asynchronous and returns no stats. A given
-    ``final_state`` (B,4,d_h) tensor receives the last step's state."""
+    ``final_state`` (B,4,d_h) tensor receives the last step's state. ``schedule`` is "fused"
+    (one kernel per iteration) or "layered" (residual + Jacobian, scan, update)."""
     L = load()
     _dev(P, "P", (torch.float32, torch.bfloat16))
     _dev(R, "R", (torch.float32,))
@@ -185,14 +188,14 @@ def newton_forward(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, init="
     _dev(states, "states", (torch.float32,))
     _dev(h_out, "h_out", (torch.float32,))
     _dev(final_state, "final_state", (torch.float32,))
-    need = L.slstm_newton_workspace_bytes(B, T, d)
+    need = L.slstm_newton_workspace_bytes(B, T, d, SCHEDULE[schedule])
     if workspace is None:
         workspace = alloc_workspace(need, P.device)
     st = _Stats() if stats else None
     status = L.slstm_newton_forward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
                                     _ptr(h_out), _ptr(final_state), B, T, d, FORGET[forget],
                                     int(max_iters),
-                                    float(tol), INIT[init], _ptr(workspace),
+                                    float(tol), INIT[init], SCHEDULE[schedule], _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream),
                                     ctypes.byref(st) if st is not None else None)
     _check(status, "slstm_newton_forward")

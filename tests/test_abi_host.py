@@ -42,21 +42,25 @@ def test_status_strings(lib):
 def test_workspace_sizes(lib):
     # Jacobians (64 B) + right-hand sides (16 B) per state element, plus look-back words
     B, T, d = 128, 2048, 1024
-    n = lib.slstm_newton_workspace_bytes(B, T, d)
+    n = lib.slstm_newton_workspace_bytes(B, T, d, 1)  # layered
     assert n >= 80 * B * T * d
     assert n < 90 * B * T * d
-    assert lib.slstm_newton_workspace_bytes(0, 1, 1) == 0
-    assert lib.slstm_newton_workspace_bytes(1, -1, 1) == 0
+    # fused: a second iterate buffer (16 B) and look-back words, no Jacobians
+    nf = lib.slstm_newton_workspace_bytes(B, T, d, 0)
+    assert 16 * B * T * d <= nf < 32 * B * T * d
+    assert lib.slstm_newton_workspace_bytes(B, T, d, 7) == 0
+    assert lib.slstm_newton_workspace_bytes(0, 1, 1, 0) == 0
+    assert lib.slstm_newton_workspace_bytes(1, -1, 1, 0) == 0
     assert lib.slstm_scan_block4_workspace_bytes(2, 64, 16) > 0
     assert lib.slstm_warm_start_workspace_bytes(2, 64, 16) > 0
     # tiny shapes still get a control block and one tile of look-back words
-    assert lib.slstm_newton_workspace_bytes(1, 1, 1) >= 512
+    assert lib.slstm_newton_workspace_bytes(1, 1, 1, 0) >= 512
 
 
 def _fwd(lib, **kw):
     args = dict(P=ctypes.c_void_p(256), dt=0, R=ctypes.c_void_p(256), s0=None,
                 S=ctypes.c_void_p(256), h=None, fin=None, B=2, T=64, d=16, fm=0, K=3, tol=0.0, init=0,
-                ws=ctypes.c_void_p(4096), wsb=1 << 30, stream=None, stats=None)
+                sched=0, ws=ctypes.c_void_p(4096), wsb=1 << 30, stream=None, stats=None)
     args.update(kw)
     return lib.slstm_newton_forward(*args.values())
 
@@ -71,6 +75,7 @@ def test_argument_checks_return_einval(lib):
     assert _fwd(lib, fm=7) == slstm.EINVAL
     assert _fwd(lib, dt=5) == slstm.EINVAL
     assert _fwd(lib, init=3) == slstm.EINVAL
+    assert _fwd(lib, sched=2) == slstm.EINVAL
     assert _fwd(lib, P=None) == slstm.EINVAL
     assert _fwd(lib, S=ctypes.c_void_p(260)) == slstm.EINVAL      # states not 16-byte aligned
     assert _fwd(lib, fin=ctypes.c_void_p(264)) == slstm.EINVAL    # final_state not 16-byte aligned

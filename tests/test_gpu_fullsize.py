@@ -20,6 +20,11 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
+@pytest.fixture(params=["fused", "layered"])
+def schedule(request):
+    return request.param
+
+
 def _gpu_h_at(h, lb, lj):
     """GPU hidden states (B, T, d) at sampled lanes -> (n, T)."""
     idx_b = torch.as_tensor(lb, device=h.device)
@@ -27,13 +32,13 @@ def _gpu_h_at(h, lb, lj):
     return h[idx_b, :, idx_j].detach().cpu().double().numpy()
 
 
-def test_sigmoid_bf16_workload_full_size(gpu_lib):
+def test_sigmoid_bf16_workload_full_size(gpu_lib, schedule):
     w = by_name("sigmoid_bf16p_b16_t4096_d1024")
     case(f"full size {w.name}: GPU Newton with early stop, oracle history over all lanes")
     inp = draw_preactivation_inputs(w, device=DEV)
     P = inp["P"].to(DEV)
     R = inp["R"].to(DEV)
-    S, h, st = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, w.tol)
+    S, h, st = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, schedule=schedule)
     torch.cuda.synchronize()
     assert st.converged and not st.diverged
     lb, lj = sample_lanes(w.B, w.d_h, 96, seed=1)
@@ -50,13 +55,13 @@ def test_sigmoid_bf16_workload_full_size(gpu_lib):
     assert err < H_TOL_BF16
 
 
-def test_long_context_workload_full_size(gpu_lib):
+def test_long_context_workload_full_size(gpu_lib, schedule):
     w = by_name("long_b4_t16384_d2048")
     case(f"full size {w.name}: GPU Newton K={w.max_iters}, oracle on sampled lanes")
     inp = draw_preactivation_inputs(w, device=DEV)
     P = inp["P"].to(DEV)
     R = inp["R"].to(DEV)
-    S, h, st = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, w.tol)
+    S, h, st = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, schedule=schedule)
     torch.cuda.synchronize()
     assert st.iters == w.max_iters and not st.diverged and not st.nonfinite
     # the residual of the last iterate sits at the float32 rounding floor of m (~ulp of max m)
@@ -76,7 +81,7 @@ def test_long_context_workload_full_size(gpu_lib):
     assert h_rel_err(_gpu_h_at(hs, lb, lj), seq[:, :, 3]) < H_TOL_F32
 
 
-def test_full_layer_workload_full_size(gpu_lib):
+def test_full_layer_workload_full_size(gpu_lib, schedule):
     w = by_name("layer_b128_t2048_d1024")
     case(f"full size {w.name}: MFMA projection + Newton K={w.max_iters}, oracle on sampled lanes")
     inp = draw_layer_inputs(w)
@@ -85,7 +90,7 @@ def test_full_layer_workload_full_size(gpu_lib):
     bias = inp["bias"].to(DEV)
     R = inp["R"].to(DEV)
     P = gpu_lib.input_projection(x, W, bias)
-    S, h, st = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, w.tol)
+    S, h, st = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, schedule=schedule)
     torch.cuda.synchronize()
     assert st.iters == w.max_iters and not st.diverged
     m_max = float(S[..., 2, :].abs().max())

@@ -86,17 +86,18 @@ def test_scan_block4_is_deterministic(gpu_lib, shape):
     assert float(np.max(np.abs(to_np(first[:1, :, :, :8]) - x_ref))) < 2e-5 * max(1.0, float(np.max(np.abs(x_ref))))
 
 
-def test_warm_start_and_newton_are_deterministic(gpu_lib):
+@pytest.mark.parametrize("schedule", ["fused", "layered"])
+def test_warm_start_and_newton_are_deterministic(gpu_lib, schedule):
     w = by_name("sigmoid_bf16p_b16_t4096_d1024")
-    case("warm start / newton determinism B=2 T=4096 d=1024")
+    case(f"warm start / newton determinism B=2 T=4096 d=1024 {schedule}")
     inp = draw_preactivation_inputs(w, B=2, T=4096)
     P = inp["P"].to(DEV)
     R = inp["R"].to(DEV)
     w0 = gpu_lib.warm_start(P, None, w.forget)
-    S0, h0, st0 = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, w.tol)
+    S0, h0, st0 = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, schedule=schedule)
     for _ in range(3):
         assert torch.equal(w0, gpu_lib.warm_start(P, None, w.forget))
-        S1, h1, st1 = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, w.tol)
+        S1, h1, st1 = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, schedule=schedule)
         assert torch.equal(S0, S1) and st0.max_abs_F == st1.max_abs_F
 
 

@@ -14,10 +14,16 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-def _run_both(gpu_lib, P, R, state0, forget, K, tol=0.0, init="warm"):
+@pytest.fixture(params=["fused", "layered"])
+def schedule(request):
+    """Both kernel schedules of a Newton iteration must meet the same bar."""
+    return request.param
+
+
+def _run_both(gpu_lib, P, R, state0, forget, K, tol=0.0, init="warm", schedule="fused"):
     S, h, st = gpu_lib.newton_forward(P.to(DEV), R.to(DEV),
                                       None if state0 is None else state0.to(DEV), forget,
-                                      K, tol, init, raise_on_divergence=False)
+                                      K, tol, init, raise_on_divergence=False, schedule=schedule)
     torch.cuda.synchronize()
     S_ref, st_ref = ref.newton(to_np(P), to_np(R), None if state0 is None else to_np(state0),
                                forget, K, tol=tol, init=init)
@@ -25,11 +31,11 @@ def _run_both(gpu_lib, P, R, state0, forget, K, tol=0.0, init="warm"):
 
 
 @pytest.mark.parametrize("K", [1, 2, 3, 4, 8, 16, 32, 64])
-def test_tiny_fixed_k_sweep(gpu_lib, K):
+def test_tiny_fixed_k_sweep(gpu_lib, K, schedule):
     w = by_name("tiny_b2_t64_d16")
     case(f"newton {w.name} K={K}")
     inp = draw_preactivation_inputs(w)
-    S, h, st, S_ref, st_ref = _run_both(gpu_lib, inp["P"], inp["R"], None, w.forget, K)
+    S, h, st, S_ref, st_ref = _run_both(gpu_lib, inp["P"], inp["R"], None, w.forget, K, schedule=schedule)
     assert h_rel_err(h, S_ref[..., 3, :]) < H_TOL_F32
     assert torch.equal(h, S[..., 3, :])
     assert st.iters == st_ref.iters == K
@@ -38,12 +44,12 @@ def test_tiny_fixed_k_sweep(gpu_lib, K):
     assert len(st.max_abs_F) == K + 1
 
 
-def test_mid_workload_full_size(gpu_lib):
+def test_mid_workload_full_size(gpu_lib, schedule):
     w = by_name("mid_b8_t1024_d256")
     case(f"newton {w.name} full size K={w.max_iters}")
     inp = draw_preactivation_inputs(w)
     S, h, st = gpu_lib.newton_forward(inp["P"].to(DEV), inp["R"].to(DEV), None, w.forget,
-                                      w.max_iters, w.tol)
+                                      w.max_iters, w.tol, schedule=schedule)
     torch.cuda.synchronize()
     S_ref, st_ref = lanes.newton_lanes(inp["P"], inp["R"], None, w.forget, w.max_iters, w.tol)
     h_ref = S_ref[:, :, 3].reshape(w.B, w.d_h, w.T).transpose(0, 2, 1)
@@ -57,7 +63,7 @@ def test_mid_workload_full_size(gpu_lib):
 
 @pytest.mark.parametrize("shape", [(1, 1, 1), (1, 2, 3), (3, 33, 65), (2, 257, 20), (1, 70, 64)])
 @pytest.mark.parametrize("forget", ["exp", "sigmoid"])
-def test_edge_shapes(gpu_lib, shape, forget):
+def test_edge_shapes(gpu_lib, shape, forget, schedule):
     B, T, d = shape
     case(f"newton edge B={B} T={T} d={d} {forget}")
     rng = np.random.Generator(np.random.PCG64(B * 1000 + T * 10 + d))
@@ -72,7 +78,7 @@ def test_edge_shapes(gpu_lib, shape, forget):
     Pt = torch.from_numpy(P.astype(np.float32))
     Rt = torch.from_numpy(R.astype(np.float32))
     s0t = torch.from_numpy(s0.astype(np.float32))
-    S, h, st, S_ref, st_ref = _run_both(gpu_lib, Pt, Rt, s0t, forget, 6)
+    S, h, st, S_ref, st_ref = _run_both(gpu_lib, Pt, Rt, s0t, forget, 6, schedule=schedule)
     assert h_rel_err(h, S_ref[..., 3, :]) < H_TOL_F32
     assert st.iters == st_ref.iters and st.diverged == st_ref.diverged
     Ss, hs = gpu_lib.sequential_forward(Pt.to(DEV), Rt.to(DEV), s0t.to(DEV), forget)
@@ -94,39 +100,39 @@ def test_sequential_full_size(gpu_lib, name):
     assert torch.equal(h, S[..., 3, :])
 
 
-def test_zero_guess_diverges_on_both_sides(gpu_lib):
+def test_zero_guess_diverges_on_both_sides(gpu_lib, schedule):
     # the zero iterate overflows on a long exponential-forget sequence
     w = by_name("mid_b8_t1024_d256")
     case("newton zero init B=2 T=1024 d=32 K=3")
     inp = draw_preactivation_inputs(w, B=2)
     P = inp["P"][..., :32].contiguous()
     R = inp["R"][:, :32].contiguous()
-    S, h, st, S_ref, st_ref = _run_both(gpu_lib, P, R, None, "exp", 3, init="zero")
+    S, h, st, S_ref, st_ref = _run_both(gpu_lib, P, R, None, "exp", 3, init="zero", schedule=schedule)
     assert st_ref.diverged and st.diverged
     assert st.nonfinite == st_ref.nonfinite
 
 
-def test_nan_input_gives_nonfinite(gpu_lib):
+def test_nan_input_gives_nonfinite(gpu_lib, schedule):
     w = by_name("tiny_b2_t64_d16")
     case("newton NaN input")
     inp = draw_preactivation_inputs(w)
     P = inp["P"].clone()
     P[1, 17, 1, 5] = float("nan")
-    S, h, st, S_ref, st_ref = _run_both(gpu_lib, P, inp["R"], None, w.forget, 3)
+    S, h, st, S_ref, st_ref = _run_both(gpu_lib, P, inp["R"], None, w.forget, 3, schedule=schedule)
     assert st.diverged and st.nonfinite and st_ref.diverged and st_ref.nonfinite
     assert st.status == gpu_lib.NONFINITE
     with pytest.raises(gpu_lib.NewtonDivergenceError):
-        gpu_lib.newton_forward(P.to(DEV), inp["R"].to(DEV), None, w.forget, 3)
+        gpu_lib.newton_forward(P.to(DEV), inp["R"].to(DEV), None, w.forget, 3, schedule=schedule)
 
 
 @pytest.mark.parametrize("B,T,d", [(2, 4096, 64), (1, 1000, 16)])
-def test_early_stop_sigmoid_bf16(gpu_lib, B, T, d):
+def test_early_stop_sigmoid_bf16(gpu_lib, B, T, d, schedule):
     w = by_name("sigmoid_bf16p_b16_t4096_d1024")
     case(f"newton early stop {w.name} B={B} T={T} d={d}")
     inp = draw_preactivation_inputs(w, B=B, T=T)
     P = inp["P"][..., :d].contiguous()
     R = inp["R"][:, :d].contiguous()
-    S, h, st, S_ref, st_ref = _run_both(gpu_lib, P, R, None, w.forget, w.max_iters, w.tol)
+    S, h, st, S_ref, st_ref = _run_both(gpu_lib, P, R, None, w.forget, w.max_iters, w.tol, schedule=schedule)
     assert st_ref.converged and st.converged
     assert st.iters == st_ref.iters
     assert h_rel_err(h, S_ref[..., 3, :]) < H_TOL_BF16
@@ -135,16 +141,17 @@ def test_early_stop_sigmoid_bf16(gpu_lib, B, T, d):
         assert st.max_abs_F[k] == pytest.approx(st_ref.max_abs_F[k], rel=0.05, abs=2e-5)
 
 
-def test_state_carry_across_calls(gpu_lib):
+def test_state_carry_across_calls(gpu_lib, schedule):
     w = by_name("tiny_b2_t64_d16")
     case("newton state carry T=64 as 32 + 32")
     inp = draw_preactivation_inputs(w)
     P = inp["P"].to(DEV)
     R = inp["R"].to(DEV)
-    S_full, h_full, _ = gpu_lib.newton_forward(P, R, None, w.forget, 8)
+    S_full, h_full, _ = gpu_lib.newton_forward(P, R, None, w.forget, 8, schedule=schedule)
     fin1 = torch.empty((w.B, 4, w.d_h), dtype=torch.float32, device=DEV)
-    S1, _, _ = gpu_lib.newton_forward(P[:, :32].contiguous(), R, None, w.forget, 8, final_state=fin1)
-    S2, h2, _ = gpu_lib.newton_forward(P[:, 32:].contiguous(), R, fin1, w.forget, 8)
+    S1, _, _ = gpu_lib.newton_forward(P[:, :32].contiguous(), R, None, w.forget, 8, final_state=fin1,
+                                      schedule=schedule)
+    S2, h2, _ = gpu_lib.newton_forward(P[:, 32:].contiguous(), R, fin1, w.forget, 8, schedule=schedule)
     torch.cuda.synchronize()
     assert torch.equal(fin1, S1[:, -1])
     assert h_rel_err(h2, h_full[:, 32:]) < H_TOL_F32
@@ -157,13 +164,45 @@ def test_state_carry_across_calls(gpu_lib):
     assert torch.equal(hq2, hq[:, 32:])
 
 
-def test_async_stats_readback(gpu_lib):
+def test_async_stats_readback(gpu_lib, schedule):
     w = by_name("tiny_b2_t64_d16")
     case("newton async + read_stats")
     inp = draw_preactivation_inputs(w)
-    ws = torch.empty(gpu_lib.newton_workspace_bytes(w.B, w.T, w.d_h), dtype=torch.uint8, device=DEV)
+    ws = torch.empty(gpu_lib.newton_workspace_bytes(w.B, w.T, w.d_h, schedule), dtype=torch.uint8,
+                     device=DEV)
     S, h, st = gpu_lib.newton_forward(inp["P"].to(DEV), inp["R"].to(DEV), None, w.forget, 4,
-                                      workspace=ws, stats=False)
+                                      workspace=ws, stats=False, schedule=schedule)
     assert st is None
     st = gpu_lib.read_stats(ws)
     assert st.iters == 4 and not st.diverged and len(st.max_abs_F) == 5
+
+
+def test_schedules_agree(gpu_lib):
+    """The fused and layered schedules compute the same iterates up to float32 rounding."""
+    w = by_name("mid_b8_t1024_d256")
+    case("fused vs layered, mid workload")
+    inp = draw_preactivation_inputs(w)
+    P = inp["P"].to(DEV)
+    R = inp["R"].to(DEV)
+    Sf, hf, stf = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, schedule="fused")
+    Sl, hl, stl = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, schedule="layered")
+    torch.cuda.synchronize()
+    assert stf.iters == stl.iters
+    assert h_rel_err(hf, hl) < H_TOL_F32
+    for k in range(stf.iters):
+        assert stf.max_abs_F[k] == pytest.approx(stl.max_abs_F[k], rel=1e-3, abs=1e-4)
+
+
+def test_early_stop_lands_in_either_buffer(gpu_lib):
+    """Fused schedule: an early stop after an odd or even number of updates leaves the result
+    in either iterate buffer; the returned states must be the stopped iterate either way."""
+    w = by_name("sigmoid_bf16p_b16_t4096_d1024")
+    inp = draw_preactivation_inputs(w, B=1, T=2048)
+    P = inp["P"][..., :64].contiguous()
+    R = inp["R"][:, :64].contiguous()
+    for K in (7, 8):
+        case(f"fused early stop, budget K={K}")
+        S, h, st, S_ref, st_ref = _run_both(gpu_lib, P, R, None, w.forget, K, w.tol, schedule="fused")
+        assert st.converged and st.iters == st_ref.iters < K
+        assert h_rel_err(h, S_ref[..., 3, :]) < H_TOL_BF16
+        assert torch.equal(h, S[..., 3, :])
