@@ -118,7 +118,7 @@ NewtonLayout newton_layout(int B, int T, int d, slstm_schedule schedule) {
   NewtonLayout L;
   const size_t n_state = static_cast<size_t>(B) * T * 4 * d;
   L.ctl = 0;
-  L.desc = align_up(sizeof(Control));
+  L.desc = align_up(slstm::kControlBytes);
   if (schedule == SLSTM_SCHEDULE_FUSED) {
     const size_t desc_words = std::max(slstm::fused_desc_words(B, T, d), slstm::warm_desc_words(B, T, d));
     L.S2 = align_up(L.desc + desc_words * 8);
@@ -141,7 +141,7 @@ struct ScanLayout {
 ScanLayout scan_layout(size_t desc_words) {
   ScanLayout L;
   L.ctl = 0;
-  L.desc = align_up(sizeof(Control));
+  L.desc = align_up(slstm::kControlBytes);
   L.total = align_up(L.desc + desc_words * 8);
   return L;
 }
@@ -190,15 +190,15 @@ __global__ void store_u32_kernel(unsigned int* p, unsigned int v) { *p = v; }
 
 namespace slstm {
 
-int look_back_anchor_stride(long long n_lane_groups) {
-  static int resident = [] {
-    int dev = 0, cus = 256;
-    if (hipGetDevice(&dev) == hipSuccess) {
-      int v = 0;
-      if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-    }
-    return 2 * cus;  // two look-back workgroups fit on a compute unit
+int look_back_anchor_stride(long long n_lane_groups, int wgs_per_cu) {
+  static int cus = [] {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      return v;
+    return 256;
   }();
+  const long long resident = static_cast<long long>(wgs_per_cu) * cus;
   long long s = (resident + n_lane_groups - 1) / n_lane_groups;
   return static_cast<int>(s < 1 ? 1 : (s > 8 ? 8 : s));
 }
@@ -269,7 +269,7 @@ slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const floa
   if (init == SLSTM_INIT_WARM) {
     const uint32_t ep = next_epoch();
     HIP_TRY(timed(SLSTM_KERNEL_WARM_START, st, [&] {
-      return slstm::launch_warm_start(P, bf16, state0, buf[0], B, T, d_h, sig, desc, &ctl->ticket_warm, ep, st);
+      return slstm::launch_warm_start(P, bf16, state0, buf[0], B, T, d_h, sig, desc, slstm::spread_of(ctl)->ticket[slstm::kTicketWarm][0], ep, st);
     }));
   } else {
     HIP_TRY(slstm::launch_zero(buf[0], n_state, st));
@@ -279,7 +279,7 @@ slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const floa
       const uint32_t ep = next_epoch();
       HIP_TRY(timed(SLSTM_KERNEL_NEWTON_ITERATION, st, [&] {
         return slstm::launch_newton_iteration(P, bf16, R, state0, buf[k % 2], buf[(k + 1) % 2], B, T, d_h,
-                                              sig, desc, &ctl->ticket_scan, ep, ctl, k, tol, st);
+                                              sig, desc, slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0], ep, ctl, k, tol, st);
       }));
     }
   } else {
@@ -288,11 +288,11 @@ slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const floa
     for (int k = 0; k < max_iters; ++k) {
       HIP_TRY(timed(SLSTM_KERNEL_RESIDUAL_JACOBIAN, st, [&] {
         return slstm::launch_residual(P, bf16, R, state0, states, A, rhs, B, T, d_h, sig, ctl,
-                                      &ctl->err_bits[k], slstm::ResidualMode::kSparse, -1, tol, st);
+                                      &slstm::spread_of(ctl)->err[0][k], slstm::kErrSlotWords, slstm::ResidualMode::kSparse, -1, tol, st);
       }));
       const uint32_t ep = next_epoch();
       HIP_TRY(timed(SLSTM_KERNEL_SCAN_BLOCK4, st, [&] {
-        return slstm::launch_scan_block4(A, rhs, rhs, B, T, d_h, true, desc, &ctl->ticket_scan, ep, ctl, k,
+        return slstm::launch_scan_block4(A, rhs, rhs, B, T, d_h, true, desc, slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0], ep, ctl, k,
                                          tol, st);
       }));
       HIP_TRY(timed(SLSTM_KERNEL_UPDATE, st, [&] { return slstm::launch_update(states, rhs, n_state, ctl, k, st); }));
@@ -303,7 +303,7 @@ slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const floa
   const int chk = (schedule == SLSTM_SCHEDULE_FUSED) ? max_iters - 1 : -1;
   HIP_TRY(timed(SLSTM_KERNEL_FINAL_RESIDUAL, st, [&] {
     return slstm::launch_residual(P, bf16, R, state0, buf[max_iters % 2], nullptr, nullptr, B, T, d_h, sig,
-                                  ctl, &ctl->err_bits[max_iters], slstm::ResidualMode::kNone, chk, tol, st,
+                                  ctl, &slstm::spread_of(ctl)->err[0][max_iters], slstm::kErrSlotWords, slstm::ResidualMode::kNone, chk, tol, st,
                                   h_out);
   }));
   if (schedule == SLSTM_SCHEDULE_FUSED)
@@ -380,7 +380,7 @@ slstm_status slstm_residual_jacobian(const void* P, slstm_dtype P_dtype, const f
   HIP_TRY(hipGetLastError());
   HIP_TRY(timed(SLSTM_KERNEL_RESIDUAL_JACOBIAN, st, [&] {
     return slstm::launch_residual(P, P_dtype == SLSTM_BF16, R, state0, states, A, rhs, B, T, d_h,
-                                  fmode == SLSTM_FORGET_SIGMOID, nullptr, err, slstm::ResidualMode::kDense, -1,
+                                  fmode == SLSTM_FORGET_SIGMOID, nullptr, err, 0, slstm::ResidualMode::kDense, -1,
                                   0.0f, st);
   }));
   return SLSTM_OK;
@@ -407,7 +407,7 @@ slstm_status slstm_scan_block4(const float* A, const float* rhs, float* x, int B
   const uint32_t ep = next_epoch();
   HIP_TRY(timed(SLSTM_KERNEL_SCAN_BLOCK4, st, [&] {
     return slstm::launch_scan_block4(A, rhs, x, B, T, d_h, false, at<unsigned long long>(workspace, L.desc),
-                                     &ctl->ticket_scan, ep, nullptr, 0, 0.0f, st);
+                                     slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0], ep, nullptr, 0, 0.0f, st);
   }));
   return SLSTM_OK;
 }
@@ -434,7 +434,7 @@ slstm_status slstm_warm_start(const void* P, slstm_dtype P_dtype, const float* s
   HIP_TRY(timed(SLSTM_KERNEL_WARM_START, st, [&] {
     return slstm::launch_warm_start(P, P_dtype == SLSTM_BF16, state0, states, B, T, d_h,
                                     fmode == SLSTM_FORGET_SIGMOID, at<unsigned long long>(workspace, L.desc),
-                                    &ctl->ticket_warm, ep, st);
+                                    slstm::spread_of(ctl)->ticket[slstm::kTicketWarm][0], ep, st);
   }));
   return SLSTM_OK;
 }

@@ -183,4 +183,111 @@ __device__ __forceinline__ void tile_look_back(const float* agg, float carry[4],
   }
 }
 
+// Broadcast lane K of each quad to the whole quad.
+template <int K>
+__device__ __forceinline__ float quad_bcast(float x) {
+  return quad_perm<K, K, K, K>(x);
+}
+
+// Row q (the lane's position in its quad) of the map held by lane 3 of the quad; every lane of
+// the wave must take part.
+__device__ __forceinline__ void quad_row_of_last(const float M[16], const float v[4], int q,
+                                                 float row[4], float& vq) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float x0 = quad_bcast<3>(M[k]), x1 = quad_bcast<3>(M[4 + k]);
+    const float x2 = quad_bcast<3>(M[8 + k]), x3 = quad_bcast<3>(M[12 + k]);
+    row[k] = q == 0 ? x0 : (q == 1 ? x1 : (q == 2 ? x2 : x3));
+  }
+  const float y0 = quad_bcast<3>(v[0]), y1 = quad_bcast<3>(v[1]);
+  const float y2 = quad_bcast<3>(v[2]), y3 = quad_bcast<3>(v[3]);
+  vq = q == 0 ? y0 : (q == 1 ? y1 : (q == 2 ? y2 : y3));
+}
+
+// The same look-back as tile_look_back, for one lane of a tile spread over the four threads of
+// a quad: thread q holds row q of the tile's aggregate (arow = M[q][0..3], av = v[q]) and
+// publishes, loads and composes only the words of row q; the rows it needs from the other
+// threads of its quad arrive by DPP. Returns the full carry in every thread of the quad. The
+// words and the fixed dataflow are those of tile_look_back. Every lane of the wave must take
+// part (the quad broadcasts run after the waits).
+//   pf_word: this thread's word of the anchor's inclusive value, loaded ahead of time
+//            (quad_look_back_prefetch); it costs no wait when it already carries the epoch.
+__device__ __forceinline__ unsigned long long quad_look_back_prefetch(
+    const unsigned long long* __restrict__ desc, i64 n_lanes_pad, i64 my_lane, int q, int tt,
+    int anchor_stride) {
+  if (tt == 0) return 0ull;
+  const int a = ((tt - 1) / anchor_stride) * anchor_stride;
+  return __hip_atomic_load(const_cast<unsigned long long*>(desc) + (static_cast<i64>(a) * kLookBackWords + q) * n_lanes_pad + my_lane,
+                           __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void quad_look_back(const float arow[4], float av, float carry[4],
+                                               unsigned long long* __restrict__ desc,
+                                               i64 n_lanes_pad, i64 my_lane, int q, int tt,
+                                               int anchor_stride, uint32_t epoch,
+                                               unsigned long long pf_word) {
+  auto word = [&](int tile, int w) {
+    return desc + (static_cast<i64>(tile) * kLookBackWords + w) * n_lanes_pad + my_lane;
+  };
+  const bool anchor = (tt % anchor_stride) == 0;
+  if (!anchor) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) tag_store(word(tt, 4 + 4 * q + k), arow[k], epoch);
+    tag_store(word(tt, 20 + q), av, epoch);
+  }
+  float cq = 0.0f;  // carry[q]
+  if (tt > 0) {
+    const int a = ((tt - 1) / anchor_stride) * anchor_stride;  // nearest anchor below
+    // row q of the accumulated map of the tiles a+1 .. tt-1
+    float mrow[4], vacc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) mrow[k] = (k == q) ? 1.0f : 0.0f;
+    for (int p = tt - 1; p > a; --p) {
+      float prow[4], pv;
+      while (true) {
+        bool ok = true;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) ok &= tag_load(word(p, 4 + 4 * q + k), epoch, prow[k]);
+        ok &= tag_load(word(p, 20 + q), epoch, pv);
+        if (ok) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      // (Macc, vacc) <- (Macc, vacc) o (Mp, vp), row q: sum_k Macc[q][k] (Mp[k][.], vp[k])
+      float nrow[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      float nv = vacc;
+      auto fold = [&](float mk, float r0, float r1, float r2, float r3, float vk) {
+        nrow[0] = fmaf(mk, r0, nrow[0]);
+        nrow[1] = fmaf(mk, r1, nrow[1]);
+        nrow[2] = fmaf(mk, r2, nrow[2]);
+        nrow[3] = fmaf(mk, r3, nrow[3]);
+        nv = fmaf(mk, vk, nv);
+      };
+      fold(mrow[0], quad_bcast<0>(prow[0]), quad_bcast<0>(prow[1]), quad_bcast<0>(prow[2]), quad_bcast<0>(prow[3]), quad_bcast<0>(pv));
+      fold(mrow[1], quad_bcast<1>(prow[0]), quad_bcast<1>(prow[1]), quad_bcast<1>(prow[2]), quad_bcast<1>(prow[3]), quad_bcast<1>(pv));
+      fold(mrow[2], quad_bcast<2>(prow[0]), quad_bcast<2>(prow[1]), quad_bcast<2>(prow[2]), quad_bcast<2>(prow[3]), quad_bcast<2>(pv));
+      fold(mrow[3], quad_bcast<3>(prow[0]), quad_bcast<3>(prow[1]), quad_bcast<3>(prow[2]), quad_bcast<3>(prow[3]), quad_bcast<3>(pv));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) mrow[k] = nrow[k];
+      vacc = nv;
+    }
+    // the anchor's inclusive value, element q
+    float xq = __uint_as_float(static_cast<uint32_t>(pf_word));
+    bool ok = static_cast<uint32_t>(pf_word >> 32) == epoch;
+    while (!ok) {
+      ok = tag_load(word(a, q), epoch, xq);
+      if (ok) break;
+      __builtin_amdgcn_s_sleep(2);
+    }
+    cq = fmaf(mrow[0], quad_bcast<0>(xq), fmaf(mrow[1], quad_bcast<1>(xq), fmaf(mrow[2], quad_bcast<2>(xq), fmaf(mrow[3], quad_bcast<3>(xq), vacc))));
+  }
+  carry[0] = quad_bcast<0>(cq);
+  carry[1] = quad_bcast<1>(cq);
+  carry[2] = quad_bcast<2>(cq);
+  carry[3] = quad_bcast<3>(cq);
+  if (anchor) {
+    const float xe = fmaf(arow[0], carry[0], fmaf(arow[1], carry[1], fmaf(arow[2], carry[2], fmaf(arow[3], carry[3], av))));
+    tag_store(word(tt, q), xe, epoch);
+  }
+}
+
 }  // namespace slstm

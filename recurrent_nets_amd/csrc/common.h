@@ -98,21 +98,83 @@ __device__ __forceinline__ bool tag_load(const unsigned long long* p, uint32_t e
 // has finished before its successor starts and a plain chain (stride 1) never waits. With few
 // lane groups several tiles of a chain run at once, and every stride-th tile anchors the
 // chain, so a tile waits on at most one anchor and on aggregates published before any wait.
-// A function of the shape and the device alone, so results stay reproducible.
-int look_back_anchor_stride(long long n_lane_groups);
+// A function of the shape, the kernel's residency (workgroups per compute unit) and the device
+// alone, so results stay reproducible.
+int look_back_anchor_stride(long long n_lane_groups, int wgs_per_cu);
 
-// Solver control block kept at the start of the workspace.
+// ---- spread counters ----------------------------------------------------------------------------
+// Device-scope atomics on one address serialise (about 10 ns apiece on MI355X), so a launch of
+// 2^18 workgroups that all touch one word spends milliseconds there. Work tickets and residual
+// maxima are therefore spread over kSpreadSlots words in separate cache lines.
+constexpr int kSpreadSlots = 64;   // one per lane of a wave: a reduction is a single wave load
+constexpr int kErrSlotWords = 128; // per slot one word per Newton iteration (slots 512 B apart)
+constexpr int kTicketWords = 64;   // ticket counters 256 B apart
+enum { kTicketWarm = 0, kTicketTiles = 1 };
+
+// Solver control block kept at the start of the workspace, followed by its Spread block.
 struct Control {
-  unsigned int err_bits[72];  // max|F| after k updates (float bits; NaN stored as +inf)
+  unsigned int err_bits[72];  // max|F| after k updates (float bits; NaN stored as +inf),
+                              // reduced from the slots when the solve is finalised
   int iters;                  // Newton updates applied
   int stopped;                // early stop taken
   int converged;
   int diverged;
   int nonfinite;
-  unsigned int ticket_warm;   // work tickets of the look-back kernels (self-resetting)
-  unsigned int ticket_scan;
-  int pad[49];
+  int pad[51];
 };
 static_assert(sizeof(Control) == 512, "control block layout");
+
+struct Spread {
+  unsigned int err[kSpreadSlots][kErrSlotWords];             // residual maxima per slot
+  unsigned int ticket[2][kSpreadSlots][kTicketWords];        // work counters (self-resetting)
+};
+constexpr size_t kControlBytes = sizeof(Control) + sizeof(Spread);
+
+__host__ __device__ inline Spread* spread_of(Control* c) {
+  return reinterpret_cast<Spread*>(reinterpret_cast<char*>(c) + sizeof(Control));
+}
+__host__ __device__ inline const Spread* spread_of(const Control* c) {
+  return reinterpret_cast<const Spread*>(reinterpret_cast<const char*>(c) + sizeof(Control));
+}
+
+// Residual maximum of iteration k over all slots. Every lane of the wave must take part; the
+// result is wave-uniform.
+__device__ __forceinline__ float err_reduced(const Control* c, int k) {
+  const unsigned int w = spread_of(c)->err[threadIdx.x & (kSpreadSlots - 1)][k];
+  return wave_max(__uint_as_float(w));
+}
+
+// Publish a (non-negative) residual maximum: into word err_base[slot * stride], slot chosen
+// by the caller. stride 0 folds every slot into the one word err_base.
+__device__ __forceinline__ void err_publish(unsigned int* err_base, int stride, unsigned int slot,
+                                            float v) {
+  atomic_max_nonneg(err_base + static_cast<i64>(slot % kSpreadSlots) * stride, v);
+}
+
+// Work tickets (thread 0 of a workgroup). Tiles are numbered (tt, lg): lane group lg of tile
+// row tt. Lane group lg draws from counter lg % n_ctr, which hands its tiles out in order of
+// tt; workgroup b draws from counter b % n_ctr. n_ctr divides n_lg, so each counter serves as
+// many workgroups as it has tiles, and a tile's predecessors along T (same lane group, smaller
+// tt) hold smaller tickets of the same counter: they have been taken by running workgroups, so
+// the look-back's waits always end, whatever order the hardware dispatches workgroups in.
+// The last ticket of a counter resets it for the next launch.
+__device__ __forceinline__ void take_ticket(unsigned int* counters, int n_ctr, int n_lg, int n_tt,
+                                            int& tt, int& lg) {
+  const int c = static_cast<int>(blockIdx.x % static_cast<unsigned>(n_ctr));
+  const int per = n_lg / n_ctr;  // lane groups per counter
+  unsigned int* ctr = counters + c * kTicketWords;
+  const unsigned int tk = atomicAdd(ctr, 1u);
+  if (tk == static_cast<unsigned int>(per) * n_tt - 1) atomicExch(ctr, 0u);
+  tt = static_cast<int>(tk / per);
+  lg = c + n_ctr * static_cast<int>(tk % per);
+}
+
+// number of ticket counters for n_lg lane groups: the largest power of two <= kSpreadSlots
+// that divides n_lg
+inline int ticket_counters(long long n_lg) {
+  int c = kSpreadSlots;
+  while (c > 1 && n_lg % c != 0) c >>= 1;
+  return c;
+}
 
 }  // namespace slstm

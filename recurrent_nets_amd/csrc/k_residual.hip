@@ -38,11 +38,11 @@ template <bool BF16, int JMODE>
 __global__ __launch_bounds__(kResBlock, 2) void residual_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S, float* __restrict__ A, float* __restrict__ rhs, int T, int d,
-    int n_chunks, int sig_forget, Control* __restrict__ ctl, unsigned int* __restrict__ err_dst,
-    int stop_check_iter, float tol, float* __restrict__ h_out) {
+    int n_chunks, int sig_forget, Control* __restrict__ ctl, unsigned int* __restrict__ err_base,
+    int err_stride, int stop_check_iter, float tol, float* __restrict__ h_out) {
   if (ctl != nullptr) {
     if (ctl->stopped) return;
-    if (stop_check_iter >= 0 && tol > 0.0f && __uint_as_float(ctl->err_bits[stop_check_iter]) < tol) {
+    if (stop_check_iter >= 0 && tol > 0.0f && err_reduced(ctl, stop_check_iter) < tol) {
       if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && threadIdx.x == 0) {
         ctl->stopped = 1;
         ctl->iters = stop_check_iter;
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(kResBlock, 2) void residual_kernel(
       pv = {st[0], st[1], st[2], st[3]};
     }
   }
-  // block maximum, then one device-wide atomic per block
+  // block maximum, then one device-wide atomic per block, into a slot of its own
   __shared__ float s_max[kResWaves];
   const float wm = wave_max(fmax_local);
   if (l == 0) s_max[wave] = wm;
@@ -126,29 +126,29 @@ __global__ __launch_bounds__(kResBlock, 2) void residual_kernel(
     float m = s_max[0];
 #pragma unroll
     for (int w = 1; w < kResWaves; ++w) m = fmaxf(m, s_max[w]);
-    atomic_max_nonneg(err_dst, m);
+    err_publish(err_base, err_stride, blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), m);
   }
 }
 
 template <bool BF16>
 static void launch_mode(int mode, dim3 grid, hipStream_t stream, const void* P, const float* R,
                         const float* state0, const float* S, float* A, float* rhs, int T, int d,
-                        int n_chunks, int sig, Control* ctl, unsigned int* err_dst, int chk,
-                        float tol, float* h_out) {
+                        int n_chunks, int sig, Control* ctl, unsigned int* err_base, int err_stride,
+                        int chk, float tol, float* h_out) {
   if (mode == kJacDense)
     residual_kernel<BF16, kJacDense><<<grid, kResBlock, 0, stream>>>(P, R, state0, S, A, rhs, T, d,
-                                                                      n_chunks, sig, ctl, err_dst, chk, tol, h_out);
+                                                                      n_chunks, sig, ctl, err_base, err_stride, chk, tol, h_out);
   else if (mode == kJacSparse)
     residual_kernel<BF16, kJacSparse><<<grid, kResBlock, 0, stream>>>(P, R, state0, S, A, rhs, T, d,
-                                                                       n_chunks, sig, ctl, err_dst, chk, tol, h_out);
+                                                                       n_chunks, sig, ctl, err_base, err_stride, chk, tol, h_out);
   else
     residual_kernel<BF16, kJacNone><<<grid, kResBlock, 0, stream>>>(P, R, state0, S, nullptr, nullptr,
-                                                                     T, d, n_chunks, sig, ctl, err_dst, chk, tol, h_out);
+                                                                     T, d, n_chunks, sig, ctl, err_base, err_stride, chk, tol, h_out);
 }
 
 hipError_t launch_residual(const void* P, bool p_bf16, const float* R, const float* state0,
                            const float* S, float* A, float* rhs, int B, int T, int d,
-                           bool sig_forget, Control* ctl, unsigned int* err_dst,
+                           bool sig_forget, Control* ctl, unsigned int* err_base, int err_stride,
                            ResidualMode mode, int stop_check_iter, float tol, hipStream_t stream,
                            float* h_out) {
   const int n_chunks = (T + kResChunk - 1) / kResChunk;
@@ -159,10 +159,10 @@ hipError_t launch_residual(const void* P, bool p_bf16, const float* R, const flo
   const int sig = sig_forget ? 1 : 0;
   const int m = mode == ResidualMode::kDense ? kJacDense : (mode == ResidualMode::kSparse ? kJacSparse : kJacNone);
   if (p_bf16)
-    launch_mode<true>(m, grid, stream, P, R, state0, S, A, rhs, T, d, n_chunks, sig, ctl, err_dst,
+    launch_mode<true>(m, grid, stream, P, R, state0, S, A, rhs, T, d, n_chunks, sig, ctl, err_base, err_stride,
                       stop_check_iter, tol, h_out);
   else
-    launch_mode<false>(m, grid, stream, P, R, state0, S, A, rhs, T, d, n_chunks, sig, ctl, err_dst,
+    launch_mode<false>(m, grid, stream, P, R, state0, S, A, rhs, T, d, n_chunks, sig, ctl, err_base, err_stride,
                        stop_check_iter, tol, h_out);
   return hipGetLastError();
 }

@@ -20,8 +20,8 @@
 // Level 3: decoupled look-back across tiles along T: wave 0 (one thread per lane) publishes
 //          the tile aggregate, folds its predecessors' aggregates down to the nearest anchor
 //          tile, applies the anchor's inclusive value and stages the carry in LDS. The fold
-//          order is fixed, so results are bitwise reproducible. Tiles take work tickets in
-//          launch order, so a predecessor always holds a smaller ticket and is running or done.
+//          order is fixed, so results are bitwise reproducible. Tiles take work tickets (take_ticket),
+//          so a predecessor always holds a smaller ticket and is running or done.
 // Finally every thread re-runs its sub-chunk from its carry and stores x.
 // x may alias rhs: each thread reads its rhs values before writing the same addresses.
 //
@@ -43,11 +43,11 @@ template <bool SPARSE, int TSUB>
 __global__ __launch_bounds__(kScanBlock, 2) void scan_block4_kernel(
     const float* __restrict__ A, const float* rhs, float* x, int T, int d, int n_jt, int n_lg,
     int n_tt, int anchor_stride, unsigned long long* __restrict__ desc,
-    unsigned int* __restrict__ ticket, uint32_t epoch, Control* ctl, int k_iter, float tol) {
+    unsigned int* __restrict__ tickets, int n_ctr, uint32_t epoch, Control* ctl, int k_iter, float tol) {
   constexpr int NA = SPARSE ? 12 : 16;
   if (ctl != nullptr) {
     if (ctl->stopped) return;
-    if (tol > 0.0f && __uint_as_float(ctl->err_bits[k_iter]) < tol) {
+    if (tol > 0.0f && err_reduced(ctl, k_iter) < tol) {
       // residual already below the tolerance: stop before solving
       if (blockIdx.x == 0 && threadIdx.x == 0) {
         ctl->stopped = 1;
@@ -56,21 +56,15 @@ __global__ __launch_bounds__(kScanBlock, 2) void scan_block4_kernel(
       return;
     }
   }
-  __shared__ unsigned int s_ticket;
+  __shared__ int s_tile[2];
   __shared__ float s_agg[64][21];
   __shared__ float s_carry[64][4];
 
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    const unsigned int total = static_cast<unsigned int>(n_lg) * n_tt;
-    const unsigned int tk = atomicAdd(ticket, 1u);
-    if (tk == total - 1) atomicExch(ticket, 0u);  // last ticket: reset for the next launch
-    s_ticket = tk;
-  }
+  if (tid == 0) take_ticket(tickets, n_ctr, n_lg, n_tt, s_tile[0], s_tile[1]);
   __syncthreads();
-  const unsigned int tk = __builtin_amdgcn_readfirstlane(s_ticket);
-  const int tt = static_cast<int>(tk / n_lg);
-  const int lg = static_cast<int>(tk % n_lg);
+  const int tt = __builtin_amdgcn_readfirstlane(s_tile[0]);
+  const int lg = __builtin_amdgcn_readfirstlane(s_tile[1]);
   const int b = lg / n_jt;
   const int jt = lg - b * n_jt;
 
@@ -207,7 +201,7 @@ size_t scan_desc_words(int B, int T, int d, bool sparse) {
 }
 
 hipError_t launch_scan_block4(const float* A, const float* rhs, float* x, int B, int T, int d,
-                              bool sparse, unsigned long long* desc, unsigned int* ticket,
+                              bool sparse, unsigned long long* desc, unsigned int* tickets,
                               uint32_t epoch, Control* ctl, int k_iter, float tol,
                               hipStream_t stream) {
   const int tile = 4 * (sparse ? kScanTSubSparse : kScanTSubDense);
@@ -215,16 +209,17 @@ hipError_t launch_scan_block4(const float* A, const float* rhs, float* x, int B,
   scan_grid(B, T, d, tile, n_jt, n_lg, n_tt);
   const i64 blocks = n_lg * n_tt;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  const int stride = look_back_anchor_stride(n_lg);
+  const int stride = look_back_anchor_stride(n_lg, 2);
+  const int n_ctr = ticket_counters(n_lg);
   const dim3 grid(static_cast<unsigned>(blocks));
   if (sparse)
     scan_block4_kernel<true, kScanTSubSparse><<<grid, kScanBlock, 0, stream>>>(
         A, rhs, x, T, d, static_cast<int>(n_jt), static_cast<int>(n_lg), static_cast<int>(n_tt), stride,
-        desc, ticket, epoch, ctl, k_iter, tol);
+        desc, tickets, n_ctr, epoch, ctl, k_iter, tol);
   else
     scan_block4_kernel<false, kScanTSubDense><<<grid, kScanBlock, 0, stream>>>(
         A, rhs, x, T, d, static_cast<int>(n_jt), static_cast<int>(n_lg), static_cast<int>(n_tt), stride,
-        desc, ticket, epoch, ctl, k_iter, tol);
+        desc, tickets, n_ctr, epoch, ctl, k_iter, tol);
   return hipGetLastError();
 }
 

@@ -18,6 +18,9 @@
 namespace slstm {
 
 constexpr int kUpdBlock = 256;
+// residual maxima reduced at the end of a solve: iterations 0 .. 64 (the largest iteration cap)
+constexpr int kFinalizeIters = 65;
+static_assert(kFinalizeIters <= kErrSlotWords && kFinalizeIters <= 72, "slot words per iteration");
 
 __global__ __launch_bounds__(kUpdBlock) void update_kernel(float4* __restrict__ S,
                                                            const float4* __restrict__ D, i64 n4,
@@ -36,13 +39,21 @@ __global__ __launch_bounds__(kUpdBlock) void update_kernel(float4* __restrict__ 
   if (blockIdx.x == 0 && threadIdx.x == 0) ctl->iters = k_iter + 1;
 }
 
-__global__ void init_control_kernel(Control* __restrict__ ctl) {
+__global__ __launch_bounds__(kUpdBlock) void init_control_kernel(Control* __restrict__ ctl) {
+  // the control block and its spread counters
   unsigned int* w = reinterpret_cast<unsigned int*>(ctl);
-  for (int i = threadIdx.x; i < static_cast<int>(sizeof(Control) / 4); i += blockDim.x) w[i] = 0u;
+  constexpr int n = static_cast<int>(kControlBytes / 4);
+  for (int i = blockIdx.x * kUpdBlock + threadIdx.x; i < n; i += gridDim.x * kUpdBlock) w[i] = 0u;
 }
 
-__global__ void finalize_kernel(Control* __restrict__ ctl, float tol) {
-  const float e = __uint_as_float(ctl->err_bits[ctl->iters]);
+// one wave per iteration k: the residual maximum reduced over the slots into err_bits[k];
+// the wave of the final iterate also sets the flags
+__global__ __launch_bounds__(kWave) void finalize_kernel(Control* __restrict__ ctl, float tol) {
+  const int k = blockIdx.x;
+  const float e = err_reduced(ctl, k);
+  if (threadIdx.x != 0) return;
+  ctl->err_bits[k] = __float_as_uint(e);
+  if (k != ctl->iters) return;
   const bool finite = e == e && e != INFINITY;
   ctl->nonfinite = finite ? 0 : 1;
   ctl->diverged = (!finite || e > 1.0f) ? 1 : 0;
@@ -107,12 +118,12 @@ hipError_t launch_update(float* S, const float* D, i64 n_floats, Control* ctl, i
 }
 
 hipError_t launch_init_control(Control* ctl, hipStream_t stream) {
-  init_control_kernel<<<1, 128, 0, stream>>>(ctl);
+  init_control_kernel<<<16, kUpdBlock, 0, stream>>>(ctl);
   return hipGetLastError();
 }
 
 hipError_t launch_finalize(Control* ctl, float tol, hipStream_t stream) {
-  finalize_kernel<<<1, 1, 0, stream>>>(ctl, tol);
+  finalize_kernel<<<kFinalizeIters, kWave, 0, stream>>>(ctl, tol);
   return hipGetLastError();
 }
 

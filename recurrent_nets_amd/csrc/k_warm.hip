@@ -81,22 +81,16 @@ template <bool BF16>
 __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
     const void* __restrict__ P, const float* __restrict__ state0, float* __restrict__ S, int T,
     int d, int sig_forget, int n_jt, int n_lg, int n_tt, int anchor_stride,
-    unsigned long long* __restrict__ desc, unsigned int* __restrict__ ticket, uint32_t epoch) {
-  __shared__ unsigned int s_ticket;
+    unsigned long long* __restrict__ desc, unsigned int* __restrict__ tickets, int n_ctr, uint32_t epoch) {
+  __shared__ int s_tile[2];
   __shared__ LogAgg s_agg[64];
   __shared__ float s_carry[64][3];
 
   const int tid = threadIdx.x;
-  if (tid == 0) {
-    const unsigned int total = static_cast<unsigned int>(n_lg) * n_tt;
-    const unsigned int tk = atomicAdd(ticket, 1u);
-    if (tk == total - 1) atomicExch(ticket, 0u);
-    s_ticket = tk;
-  }
+  if (tid == 0) take_ticket(tickets, n_ctr, n_lg, n_tt, s_tile[0], s_tile[1]);
   __syncthreads();
-  const unsigned int tk = __builtin_amdgcn_readfirstlane(s_ticket);
-  const int tt = static_cast<int>(tk / n_lg);
-  const int lg = static_cast<int>(tk % n_lg);
+  const int tt = __builtin_amdgcn_readfirstlane(s_tile[0]);
+  const int lg = __builtin_amdgcn_readfirstlane(s_tile[1]);
   const int b = lg / n_jt;
   const int jt = lg - b * n_jt;
 
@@ -263,22 +257,23 @@ size_t warm_desc_words(int B, int T, int d) {
 
 hipError_t launch_warm_start(const void* P, bool p_bf16, const float* state0, float* S, int B,
                              int T, int d, bool sig_forget, unsigned long long* desc,
-                             unsigned int* ticket, uint32_t epoch, hipStream_t stream) {
+                             unsigned int* tickets, uint32_t epoch, hipStream_t stream) {
   i64 n_jt, n_lg, n_tt;
   warm_grid(B, T, d, n_jt, n_lg, n_tt);
   const i64 blocks = n_lg * n_tt;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks));
   const int sig = sig_forget ? 1 : 0;
-  const int stride = look_back_anchor_stride(n_lg);
+  const int stride = look_back_anchor_stride(n_lg, 2);
+  const int n_ctr = ticket_counters(n_lg);
   if (p_bf16)
     warm_start_kernel<true><<<grid, kWarmBlock, 0, stream>>>(P, state0, S, T, d, sig, static_cast<int>(n_jt),
                                                              static_cast<int>(n_lg), static_cast<int>(n_tt),
-                                                             stride, desc, ticket, epoch);
+                                                             stride, desc, tickets, n_ctr, epoch);
   else
     warm_start_kernel<false><<<grid, kWarmBlock, 0, stream>>>(P, state0, S, T, d, sig, static_cast<int>(n_jt),
                                                               static_cast<int>(n_lg), static_cast<int>(n_tt),
-                                                              stride, desc, ticket, epoch);
+                                                              stride, desc, tickets, n_ctr, epoch);
   return hipGetLastError();
 }
 

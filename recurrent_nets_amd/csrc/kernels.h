@@ -8,22 +8,26 @@
 
 namespace slstm {
 
+// `tickets` arguments: the kSpreadSlots work counters of one kind (Spread::ticket[kind]), zero
+// before the launch and zero again after it.
+
 // Jacobian planes the residual kernel writes: all 16, the 12 non-structural ones, or none
 enum class ResidualMode { kDense, kSparse, kNone };
 
 // With a control block and stop_check_iter >= 0, the launch first declares the iterate
 // stop_check_iter final (and does nothing else) when its residual maximum met tol. h_out
-// (kNone only, optional) receives the hidden slot of S.
+// (kNone only, optional) receives the hidden slot of S. The residual maximum goes to
+// err_base[slot * err_stride] (see err_publish; stride 0 for a single word).
 hipError_t launch_residual(const void* P, bool p_bf16, const float* R, const float* state0,
                            const float* S, float* A, float* rhs, int B, int T, int d,
-                           bool sig_forget, Control* ctl, unsigned int* err_dst,
+                           bool sig_forget, Control* ctl, unsigned int* err_base, int err_stride,
                            ResidualMode mode, int stop_check_iter, float tol, hipStream_t stream,
                            float* h_out = nullptr);
 
 size_t fused_desc_words(int B, int T, int d);
 hipError_t launch_newton_iteration(const void* P, bool p_bf16, const float* R, const float* state0,
                                    const float* S_in, float* S_out, int B, int T, int d,
-                                   bool sig_forget, unsigned long long* desc, unsigned int* ticket,
+                                   bool sig_forget, unsigned long long* desc, unsigned int* tickets,
                                    uint32_t epoch, Control* ctl, int k_iter, float tol,
                                    hipStream_t stream);
 // copies the final iterate into `states` when it ended in the other buffer (iterate k lives in
@@ -33,14 +37,14 @@ hipError_t launch_select_iterate(const Control* ctl, const float* buf0, const fl
 
 size_t scan_desc_words(int B, int T, int d, bool sparse);
 hipError_t launch_scan_block4(const float* A, const float* rhs, float* x, int B, int T, int d,
-                              bool sparse, unsigned long long* desc, unsigned int* ticket,
+                              bool sparse, unsigned long long* desc, unsigned int* tickets,
                               uint32_t epoch, Control* ctl, int k_iter, float tol,
                               hipStream_t stream);
 
 size_t warm_desc_words(int B, int T, int d);
 hipError_t launch_warm_start(const void* P, bool p_bf16, const float* state0, float* S, int B,
                              int T, int d, bool sig_forget, unsigned long long* desc,
-                             unsigned int* ticket, uint32_t epoch, hipStream_t stream);
+                             unsigned int* tickets, uint32_t epoch, hipStream_t stream);
 
 hipError_t launch_update(float* S, const float* D, i64 n_floats, Control* ctl, int k_iter,
                          hipStream_t stream);
