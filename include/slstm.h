@@ -65,12 +65,27 @@ typedef enum { SLSTM_FORGET_EXP = 0, SLSTM_FORGET_SIGMOID = 1 } slstm_forget;
 typedef enum { SLSTM_INIT_WARM = 0, SLSTM_INIT_ZERO = 1 } slstm_init;
 
 /* How a Newton iteration is laid out in kernels (same iterates up to float32 rounding):
- *  SLSTM_SCHEDULE_FUSED    one kernel per iteration: residual, Jacobian, scan and update in
- *                          registers; reads P and the iterate, writes the next iterate
- *                          (double-buffered in the workspace);
- *  SLSTM_SCHEDULE_LAYERED  three kernels per iteration: (a) residual + Jacobian to HBM in the
- *                          scan_block4 layout, (b) the 4x4 affine scan, (c) the update. */
-typedef enum { SLSTM_SCHEDULE_FUSED = 0, SLSTM_SCHEDULE_LAYERED = 1 } slstm_schedule;
+ *  SLSTM_SCHEDULE_FUSED_SCAN   one kernel per iteration: residual, Jacobian, the 4x4 affine
+ *                              scan of the block-bidiagonal system and the update, all in
+ *                              registers; reads P and the iterate, writes the next iterate
+ *                              (double-buffered in the workspace);
+ *  SLSTM_SCHEDULE_FUSED_CHAIN  one kernel per iteration as above, but each tile of 8 steps
+ *                              solves its part of the system as a plain recurrence from the
+ *                              Newton step entering it, published by the tile before; no 4x4
+ *                              maps are composed. The last iteration also forms the final
+ *                              residual and h, so no separate pass over the states follows.
+ *                              Fast when there are many independent lanes, serial along T;
+ *  SLSTM_SCHEDULE_FUSED        FUSED_CHAIN when B * ceil(d_h / 256) is at least the GPU's
+ *                              compute-unit count, FUSED_SCAN otherwise;
+ *  SLSTM_SCHEDULE_LAYERED      three kernels per iteration: (a) residual + Jacobian to HBM in
+ *                              the scan_block4 layout, (b) the 4x4 affine scan, (c) the update.
+ * Each schedule's results are bitwise reproducible on a given device. */
+typedef enum {
+  SLSTM_SCHEDULE_FUSED = 0,
+  SLSTM_SCHEDULE_LAYERED = 1,
+  SLSTM_SCHEDULE_FUSED_SCAN = 2,
+  SLSTM_SCHEDULE_FUSED_CHAIN = 3
+} slstm_schedule;
 
 #define SLSTM_MAX_ITERS 64
 
@@ -103,7 +118,7 @@ size_t slstm_newton_workspace_bytes(int B, int T, int d_h, slstm_schedule schedu
  * Each iteration k evaluates F_t = s_t - f(s_{t-1}) and A_t = df/ds' at every step; if
  * tol > 0 and max|F| < tol it stops before solving; otherwise it solves
  *   Delta_1 = -F_1, Delta_t = A_t Delta_{t-1} - F_t     (block-bidiagonal system)
- * by a 4x4 affine scan and sets s <- s + Delta. After max_iters updates (or the stop) the
+ * by a 4x4 affine scan (or, FUSED_CHAIN, tile-serial recurrences) and sets s <- s + Delta. After max_iters updates (or the stop) the
  * residual of the final iterate gives the flags.
  *
  *  P, P_dtype   gate pre-activations (B, T, 4, d_h), float32 or bf16
@@ -112,7 +127,7 @@ size_t slstm_newton_workspace_bytes(int B, int T, int d_h, slstm_schedule schedu
  *  h_out        optional output (B, T, d_h); final_state optional output (B, 4, d_h)
  *  fmode        forget-gate form; max_iters in 1..64; tol >= 0 (0: fixed iteration count)
  *  init         SLSTM_INIT_WARM (default reading) or SLSTM_INIT_ZERO
- *  schedule     SLSTM_SCHEDULE_FUSED or SLSTM_SCHEDULE_LAYERED (see above)
+ *  schedule     one of the slstm_schedule values (see above)
  *  workspace    >= slstm_newton_workspace_bytes(B, T, d_h, schedule) bytes of device memory;
  *               holds the solver control block (later readable with slstm_newton_read_stats)
  *               and look-back words, plus the second iterate buffer (fused) or the Jacobians
@@ -178,16 +193,20 @@ slstm_status slstm_scan_block4(const float* A, const float* rhs, float* x, int B
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes of slstm_warm_start (0 if invalid). */
-size_t slstm_warm_start_workspace_bytes(int B, int T, int d_h);
+size_t slstm_warm_start_workspace_bytes(int B, int T, int d_h, slstm_schedule schedule);
 
 /*
  * The initial Newton iterate: the exact trajectory of the cell with R h_{t-1} dropped from the
  * pre-activations, from state0's (c, n, m) (a reading: the pages give no initial guess).
- * Writes states (B, T, 4, d_h) with h = sigma(p_o) c / n.
+ * Writes states (B, T, 4, d_h) with h = sigma(p_o) c / n. schedule picks the kernel form the
+ * Newton solver would use for it: SLSTM_SCHEDULE_FUSED_CHAIN runs tile-serial recurrences,
+ * SLSTM_SCHEDULE_FUSED_SCAN and SLSTM_SCHEDULE_LAYERED a log-space scan with look-back, and
+ * SLSTM_SCHEDULE_FUSED chooses as slstm_newton_forward does.
  */
 slstm_status slstm_warm_start(const void* P, slstm_dtype P_dtype, const float* state0,
                               float* states, int B, int T, int d_h, slstm_forget fmode,
-                              void* workspace, size_t workspace_bytes, void* stream);
+                              slstm_schedule schedule, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /*
  * Kernel timing with HIP events recorded on the launching stream around every kernel the

@@ -108,19 +108,52 @@ slstm_status check_dims(int B, int T, int d) {
   return SLSTM_OK;
 }
 
+int device_cus() {
+  static int cus = [] {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      return v;
+    return 256;
+  }();
+  return cus;
+}
+
+// the kernel layout a schedule resolves to for a shape
+enum class Form { kScan, kChain, kLayered };
+
+bool known_schedule(slstm_schedule s) {
+  return s == SLSTM_SCHEDULE_FUSED || s == SLSTM_SCHEDULE_LAYERED || s == SLSTM_SCHEDULE_FUSED_SCAN ||
+         s == SLSTM_SCHEDULE_FUSED_CHAIN;
+}
+
+Form newton_form(int B, int d, slstm_schedule s) {
+  switch (s) {
+    case SLSTM_SCHEDULE_LAYERED: return Form::kLayered;
+    case SLSTM_SCHEDULE_FUSED_SCAN: return Form::kScan;
+    case SLSTM_SCHEDULE_FUSED_CHAIN: return Form::kChain;
+    default:
+      // chains along T cost no waiting once the lane groups cover every compute unit
+      return slstm::chain_lane_groups(B, d) >= device_cus() ? Form::kChain : Form::kScan;
+  }
+}
+
 struct NewtonLayout {
   size_t ctl, desc, A, rhs, S2, total;
 };
 
 // control block, look-back words, then either the second iterate buffer (fused) or the
 // Jacobians and right-hand sides (layered)
-NewtonLayout newton_layout(int B, int T, int d, slstm_schedule schedule) {
+NewtonLayout newton_layout(int B, int T, int d, Form form) {
   NewtonLayout L;
   const size_t n_state = static_cast<size_t>(B) * T * 4 * d;
   L.ctl = 0;
   L.desc = align_up(slstm::kControlBytes);
-  if (schedule == SLSTM_SCHEDULE_FUSED) {
-    const size_t desc_words = std::max(slstm::fused_desc_words(B, T, d), slstm::warm_desc_words(B, T, d));
+  if (form != Form::kLayered) {
+    const bool chain = form == Form::kChain;
+    const size_t iter_words = chain ? slstm::chain_desc_words(B, T, d) : slstm::fused_desc_words(B, T, d);
+    const size_t desc_words = std::max(iter_words, chain ? slstm::warm_chain_desc_words(B, T, d)
+                                                         : slstm::warm_desc_words(B, T, d));
     L.S2 = align_up(L.desc + desc_words * 8);
     L.A = L.rhs = 0;
     L.total = align_up(L.S2 + n_state * sizeof(float));
@@ -132,6 +165,25 @@ NewtonLayout newton_layout(int B, int T, int d, slstm_schedule schedule) {
     L.total = align_up(L.rhs + n_state * sizeof(float));
   }
   return L;
+}
+
+// the warm start's kernel for a schedule: chains where the solver would use them
+bool warm_chain_form(int B, int d, slstm_schedule schedule) {
+  return newton_form(B, d, schedule) == Form::kChain;
+}
+
+size_t warm_desc_words_for(int B, int T, int d, bool chain) {
+  return chain ? slstm::warm_chain_desc_words(B, T, d) : slstm::warm_desc_words(B, T, d);
+}
+
+hipError_t launch_warm(const void* P, bool bf16, const float* state0, float* S, int B, int T, int d,
+                       bool sig, bool chain, unsigned long long* desc, Control* ctl, hipStream_t st) {
+  const uint32_t ep = next_epoch();
+  unsigned int* tickets = slstm::spread_of(ctl)->ticket[slstm::kTicketWarm][0];
+  return timed(SLSTM_KERNEL_WARM_START, st, [&] {
+    return chain ? slstm::launch_warm_chain(P, bf16, state0, S, B, T, d, sig, desc, tickets, ep, st)
+                 : slstm::launch_warm_start(P, bf16, state0, S, B, T, d, sig, desc, tickets, ep, st);
+  });
 }
 
 struct ScanLayout {
@@ -191,14 +243,7 @@ __global__ void store_u32_kernel(unsigned int* p, unsigned int v) { *p = v; }
 namespace slstm {
 
 int look_back_anchor_stride(long long n_lane_groups, int wgs_per_cu) {
-  static int cus = [] {
-    int dev = 0, v = 0;
-    if (hipGetDevice(&dev) == hipSuccess &&
-        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
-      return v;
-    return 256;
-  }();
-  const long long resident = static_cast<long long>(wgs_per_cu) * cus;
+  const long long resident = static_cast<long long>(wgs_per_cu) * device_cus();
   long long s = (resident + n_lane_groups - 1) / n_lane_groups;
   return static_cast<int>(s < 1 ? 1 : (s > 8 ? 8 : s));
 }
@@ -223,8 +268,8 @@ const char* slstm_last_error(void) { return g_err; }
 
 size_t slstm_newton_workspace_bytes(int B, int T, int d_h, slstm_schedule schedule) {
   if (check_dims(B, T, d_h) != SLSTM_OK) return 0;
-  if (schedule != SLSTM_SCHEDULE_FUSED && schedule != SLSTM_SCHEDULE_LAYERED) return 0;
-  return newton_layout(B, T, d_h, schedule).total;
+  if (!known_schedule(schedule)) return 0;
+  return newton_layout(B, T, d_h, newton_form(B, d_h, schedule)).total;
 }
 
 slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const float* R,
@@ -240,11 +285,11 @@ slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const floa
     return fail(SLSTM_EINVAL, "max_iters must be in 1..%d (got %d)", SLSTM_MAX_ITERS, max_iters);
   if (!(tol >= 0.0f) || std::isinf(tol)) return fail(SLSTM_EINVAL, "tol must be finite and >= 0");
   if (init != SLSTM_INIT_WARM && init != SLSTM_INIT_ZERO) return fail(SLSTM_EINVAL, "unknown init %d", (int)init);
-  if (schedule != SLSTM_SCHEDULE_FUSED && schedule != SLSTM_SCHEDULE_LAYERED)
-    return fail(SLSTM_EINVAL, "unknown schedule %d", (int)schedule);
+  if (!known_schedule(schedule)) return fail(SLSTM_EINVAL, "unknown schedule %d", (int)schedule);
   if (workspace == nullptr || !aligned(workspace, kAlign))
     return fail(SLSTM_EINVAL, "workspace must be non-NULL and 256-byte aligned");
-  const NewtonLayout L = newton_layout(B, T, d_h, schedule);
+  const Form form = newton_form(B, d_h, schedule);
+  const NewtonLayout L = newton_layout(B, T, d_h, form);
   if (workspace_bytes < L.total)
     return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
 
@@ -259,7 +304,7 @@ slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const floa
   // between `states` and a workspace buffer, arranged so that iterate max_iters lands in
   // `states` (iterate k lives in buf[k % 2])
   float* buf[2] = {states, states};
-  if (schedule == SLSTM_SCHEDULE_FUSED) {
+  if (form != Form::kLayered) {
     float* other = at<float>(workspace, L.S2);
     buf[0] = (max_iters % 2 == 0) ? states : other;
     buf[1] = (max_iters % 2 == 0) ? other : states;
@@ -267,19 +312,29 @@ slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const floa
 
   HIP_TRY(slstm::launch_init_control(ctl, st));
   if (init == SLSTM_INIT_WARM) {
-    const uint32_t ep = next_epoch();
-    HIP_TRY(timed(SLSTM_KERNEL_WARM_START, st, [&] {
-      return slstm::launch_warm_start(P, bf16, state0, buf[0], B, T, d_h, sig, desc, slstm::spread_of(ctl)->ticket[slstm::kTicketWarm][0], ep, st);
-    }));
+    HIP_TRY(launch_warm(P, bf16, state0, buf[0], B, T, d_h, sig, form == Form::kChain, desc, ctl, st));
   } else {
     HIP_TRY(slstm::launch_zero(buf[0], n_state, st));
   }
-  if (schedule == SLSTM_SCHEDULE_FUSED) {
+  unsigned int* tickets = slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0];
+  if (form == Form::kChain) {
+    for (int k = 0; k < max_iters; ++k) {
+      const uint32_t ep = next_epoch();
+      const bool last = k + 1 == max_iters;
+      HIP_TRY(timed(SLSTM_KERNEL_NEWTON_ITERATION, st, [&] {
+        return slstm::launch_newton_chain(P, bf16, R, state0, buf[k % 2], buf[(k + 1) % 2], last ? h_out : nullptr,
+                                          B, T, d_h, sig, desc, tickets, ep, ctl, k, tol, last, st);
+      }));
+    }
+    // the last launch formed the final residual and h; what remains of the stop rule is the
+    // check of the iterate before it
+    HIP_TRY(slstm::launch_settle(ctl, max_iters - 1, tol, st));
+  } else if (form == Form::kScan) {
     for (int k = 0; k < max_iters; ++k) {
       const uint32_t ep = next_epoch();
       HIP_TRY(timed(SLSTM_KERNEL_NEWTON_ITERATION, st, [&] {
         return slstm::launch_newton_iteration(P, bf16, R, state0, buf[k % 2], buf[(k + 1) % 2], B, T, d_h,
-                                              sig, desc, slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0], ep, ctl, k, tol, st);
+                                              sig, desc, tickets, ep, ctl, k, tol, st);
       }));
     }
   } else {
@@ -292,21 +347,22 @@ slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const floa
       }));
       const uint32_t ep = next_epoch();
       HIP_TRY(timed(SLSTM_KERNEL_SCAN_BLOCK4, st, [&] {
-        return slstm::launch_scan_block4(A, rhs, rhs, B, T, d_h, true, desc, slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0], ep, ctl, k,
-                                         tol, st);
+        return slstm::launch_scan_block4(A, rhs, rhs, B, T, d_h, true, desc, tickets, ep, ctl, k, tol, st);
       }));
       HIP_TRY(timed(SLSTM_KERNEL_UPDATE, st, [&] { return slstm::launch_update(states, rhs, n_state, ctl, k, st); }));
     }
   }
-  // residual of the last iterate (the fused schedule first checks whether the iterate before it
-  // already met the tolerance)
-  const int chk = (schedule == SLSTM_SCHEDULE_FUSED) ? max_iters - 1 : -1;
-  HIP_TRY(timed(SLSTM_KERNEL_FINAL_RESIDUAL, st, [&] {
-    return slstm::launch_residual(P, bf16, R, state0, buf[max_iters % 2], nullptr, nullptr, B, T, d_h, sig,
-                                  ctl, &slstm::spread_of(ctl)->err[0][max_iters], slstm::kErrSlotWords, slstm::ResidualMode::kNone, chk, tol, st,
-                                  h_out);
-  }));
-  if (schedule == SLSTM_SCHEDULE_FUSED)
+  if (form != Form::kChain) {
+    // residual of the last iterate (the scan form first checks whether the iterate before it
+    // already met the tolerance)
+    const int chk = (form == Form::kScan) ? max_iters - 1 : -1;
+    HIP_TRY(timed(SLSTM_KERNEL_FINAL_RESIDUAL, st, [&] {
+      return slstm::launch_residual(P, bf16, R, state0, buf[max_iters % 2], nullptr, nullptr, B, T, d_h, sig,
+                                    ctl, &slstm::spread_of(ctl)->err[0][max_iters], slstm::kErrSlotWords,
+                                    slstm::ResidualMode::kNone, chk, tol, st, h_out);
+    }));
+  }
+  if (form != Form::kLayered)
     HIP_TRY(slstm::launch_select_iterate(ctl, buf[0], buf[1], states, n_state, st));
   HIP_TRY(slstm::launch_finalize(ctl, tol, st));
   if (h_out != nullptr || final_state != nullptr)
@@ -412,30 +468,29 @@ slstm_status slstm_scan_block4(const float* A, const float* rhs, float* x, int B
   return SLSTM_OK;
 }
 
-size_t slstm_warm_start_workspace_bytes(int B, int T, int d_h) {
-  if (check_dims(B, T, d_h) != SLSTM_OK) return 0;
-  return scan_layout(slstm::warm_desc_words(B, T, d_h)).total;
+size_t slstm_warm_start_workspace_bytes(int B, int T, int d_h, slstm_schedule schedule) {
+  if (check_dims(B, T, d_h) != SLSTM_OK || !known_schedule(schedule)) return 0;
+  return scan_layout(warm_desc_words_for(B, T, d_h, warm_chain_form(B, d_h, schedule))).total;
 }
 
 slstm_status slstm_warm_start(const void* P, slstm_dtype P_dtype, const float* state0,
                               float* states, int B, int T, int d_h, slstm_forget fmode,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+                              slstm_schedule schedule, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   g_err[0] = '\0';
   static const float kDummyR = 0.0f;  // R is not used by the warm start; the shared check wants one
   slstm_status s = check_common(P, P_dtype, &kDummyR, state0, states, nullptr, nullptr, B, T, d_h, fmode);
   if (s != SLSTM_OK) return s;
+  if (!known_schedule(schedule)) return fail(SLSTM_EINVAL, "unknown schedule %d", (int)schedule);
   if (workspace == nullptr || !aligned(workspace, kAlign)) return fail(SLSTM_EINVAL, "workspace must be 256-byte aligned");
-  const ScanLayout L = scan_layout(slstm::warm_desc_words(B, T, d_h));
+  const bool chain = warm_chain_form(B, d_h, schedule);
+  const ScanLayout L = scan_layout(warm_desc_words_for(B, T, d_h, chain));
   if (workspace_bytes < L.total) return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
   hipStream_t st = static_cast<hipStream_t>(stream);
   Control* ctl = at<Control>(workspace, L.ctl);
   HIP_TRY(slstm::launch_init_control(ctl, st));
-  const uint32_t ep = next_epoch();
-  HIP_TRY(timed(SLSTM_KERNEL_WARM_START, st, [&] {
-    return slstm::launch_warm_start(P, P_dtype == SLSTM_BF16, state0, states, B, T, d_h,
-                                    fmode == SLSTM_FORGET_SIGMOID, at<unsigned long long>(workspace, L.desc),
-                                    slstm::spread_of(ctl)->ticket[slstm::kTicketWarm][0], ep, st);
-  }));
+  HIP_TRY(launch_warm(P, P_dtype == SLSTM_BF16, state0, states, B, T, d_h, fmode == SLSTM_FORGET_SIGMOID,
+                      chain, at<unsigned long long>(workspace, L.desc), ctl, st));
   return SLSTM_OK;
 }
 

@@ -60,6 +60,15 @@ __global__ __launch_bounds__(kWave) void finalize_kernel(Control* __restrict__ c
   ctl->converged = (tol > 0.0f && finite && e < tol) ? 1 : 0;
 }
 
+// one wave: the stop decision the next iteration's launch would have taken for iterate k
+__global__ __launch_bounds__(kWave) void settle_kernel(Control* __restrict__ ctl, int k, float tol) {
+  const float e = err_reduced(ctl, k);
+  if (threadIdx.x == 0 && !ctl->stopped && tol > 0.0f && e < tol) {
+    ctl->stopped = 1;
+    ctl->iters = k;
+  }
+}
+
 __global__ __launch_bounds__(kUpdBlock) void hidden_kernel(const float* __restrict__ S,
                                                            float* __restrict__ h, i64 rows, int d,
                                                            const Control* __restrict__ ctl) {
@@ -124,6 +133,11 @@ hipError_t launch_init_control(Control* ctl, hipStream_t stream) {
 
 hipError_t launch_finalize(Control* ctl, float tol, hipStream_t stream) {
   finalize_kernel<<<kFinalizeIters, kWave, 0, stream>>>(ctl, tol);
+  return hipGetLastError();
+}
+
+hipError_t launch_settle(Control* ctl, int k, float tol, hipStream_t stream) {
+  settle_kernel<<<1, kWave, 0, stream>>>(ctl, k, tol);
   return hipGetLastError();
 }
 

@@ -30,6 +30,17 @@ hipError_t launch_newton_iteration(const void* P, bool p_bf16, const float* R, c
                                    bool sig_forget, unsigned long long* desc, unsigned int* tickets,
                                    uint32_t epoch, Control* ctl, int k_iter, float tol,
                                    hipStream_t stream);
+// chain form of the fused iteration (256 features x 8 steps per tile); `last` also writes the
+// residual of the new iterate (slot k_iter + 1) and, if h_out is not NULL, its hidden slot
+long long chain_lane_groups(int B, int d);
+size_t chain_desc_words(int B, int T, int d);
+hipError_t launch_newton_chain(const void* P, bool p_bf16, const float* R, const float* state0,
+                               const float* S_in, float* S_out, float* h_out, int B, int T, int d,
+                               bool sig_forget, unsigned long long* carry, unsigned int* tickets,
+                               uint32_t epoch, Control* ctl, int k_iter, float tol, bool last,
+                               hipStream_t stream);
+// after the last chain iteration: declares iterate k final when its residual met tol
+hipError_t launch_settle(Control* ctl, int k, float tol, hipStream_t stream);
 // copies the final iterate into `states` when it ended in the other buffer (iterate k lives in
 // buf0 for even k, buf1 for odd k)
 hipError_t launch_select_iterate(const Control* ctl, const float* buf0, const float* buf1,
@@ -44,6 +55,11 @@ hipError_t launch_scan_block4(const float* A, const float* rhs, float* x, int B,
 size_t warm_desc_words(int B, int T, int d);
 hipError_t launch_warm_start(const void* P, bool p_bf16, const float* state0, float* S, int B,
                              int T, int d, bool sig_forget, unsigned long long* desc,
+                             unsigned int* tickets, uint32_t epoch, hipStream_t stream);
+
+size_t warm_chain_desc_words(int B, int T, int d);
+hipError_t launch_warm_chain(const void* P, bool p_bf16, const float* state0, float* S, int B,
+                             int T, int d, bool sig_forget, unsigned long long* carry,
                              unsigned int* tickets, uint32_t epoch, hipStream_t stream);
 
 hipError_t launch_update(float* S, const float* D, i64 n_floats, Control* ctl, int k_iter,

@@ -20,7 +20,7 @@ OK, DIVERGED, NONFINITE, EINVAL, EWORKSPACE, EHIP = 0, 1, 2, -1, -2, -3
 F32, BF16 = 0, 1
 FORGET = {"exp": 0, "sigmoid": 1}
 INIT = {"warm": 0, "zero": 1}
-SCHEDULE = {"fused": 0, "layered": 1}
+SCHEDULE = {"fused": 0, "layered": 1, "fused_scan": 2, "fused_chain": 3}
 MAX_ITERS = 64
 KERNELS = {"warm_start": 0, "residual_jacobian": 1, "scan_block4": 2, "update": 3,
            "final_residual": 4, "input_projection": 5, "sequential": 6, "newton_iteration": 7}
@@ -85,9 +85,10 @@ def load(path: str | None = None):
     L.slstm_status_string.restype = ctypes.c_char_p
     L.slstm_status_string.argtypes = [_i]
     L.slstm_last_error.restype = ctypes.c_char_p
-    for name in ("slstm_scan_block4_workspace_bytes", "slstm_warm_start_workspace_bytes"):
-        getattr(L, name).restype = _sz
-        getattr(L, name).argtypes = [_i, _i, _i]
+    L.slstm_scan_block4_workspace_bytes.restype = _sz
+    L.slstm_scan_block4_workspace_bytes.argtypes = [_i, _i, _i]
+    L.slstm_warm_start_workspace_bytes.restype = _sz
+    L.slstm_warm_start_workspace_bytes.argtypes = [_i, _i, _i, _i]
     L.slstm_newton_workspace_bytes.restype = _sz
     L.slstm_newton_workspace_bytes.argtypes = [_i, _i, _i, _i]
     L.slstm_newton_forward.restype = _i
@@ -104,7 +105,7 @@ def load(path: str | None = None):
     L.slstm_scan_block4.restype = _i
     L.slstm_scan_block4.argtypes = [_vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp]
     L.slstm_warm_start.restype = _i
-    L.slstm_warm_start.argtypes = [_vp, _i, _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]
+    L.slstm_warm_start.argtypes = [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp]
     L.slstm_profile_enable.restype = _i
     L.slstm_profile_enable.argtypes = [_i]
     L.slstm_profile_reset.restype = _i
@@ -175,7 +176,9 @@ def newton_forward(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, init="
     """Newton-parallel forward. Returns (states (B,T,4,d_h), h (B,T,d_h) or None, NewtonStats
     or None). With stats=False the call is asynchronous and returns no stats. A given
     ``final_state`` (B,4,d_h) tensor receives the last step's state. ``schedule`` is "fused"
-    (one kernel per iteration) or "layered" (residual + Jacobian, scan, update)."""
+    (one kernel per iteration; "fused_chain" when the lane groups cover the GPU, else
+    "fused_scan"), "fused_scan", "fused_chain" or "layered" (residual + Jacobian, scan,
+    update)."""
     L = load()
     _dev(P, "P", (torch.float32, torch.bfloat16))
     _dev(R, "R", (torch.float32,))
@@ -299,20 +302,23 @@ def scan_block4(A, rhs, out=None, workspace=None, stream=None):
     return out
 
 
-def warm_start(P, state0=None, forget="exp", out=None, workspace=None, stream=None):
-    """The R-free trajectory used as the initial Newton iterate. Returns states (B,T,4,d)."""
+def warm_start(P, state0=None, forget="exp", out=None, workspace=None, stream=None,
+               schedule="fused"):
+    """The R-free trajectory used as the initial Newton iterate. Returns states (B,T,4,d).
+    ``schedule`` picks the kernel form as in newton_forward ("fused_chain": tile-serial
+    recurrences; "fused_scan" / "layered": log-space scan with look-back)."""
     L = load()
     _dev(P, "P", (torch.float32, torch.bfloat16))
     _dev(state0, "state0", (torch.float32,))
     B, T, _, d = P.shape
     if out is None:
         out = torch.empty((B, T, 4, d), dtype=torch.float32, device=P.device)
-    need = L.slstm_warm_start_workspace_bytes(B, T, d)
+    need = L.slstm_warm_start_workspace_bytes(B, T, d, SCHEDULE[schedule])
     if workspace is None:
         workspace = alloc_workspace(need, P.device)
     status = L.slstm_warm_start(_ptr(P), _p_dtype(P), _ptr(state0), _ptr(out), B, T, d,
-                                FORGET[forget], _ptr(workspace), workspace.numel(),
-                                _stream(stream))
+                                FORGET[forget], SCHEDULE[schedule], _ptr(workspace),
+                                workspace.numel(), _stream(stream))
     _check(status, "slstm_warm_start")
     return out
 

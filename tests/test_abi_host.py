@@ -45,14 +45,19 @@ def test_workspace_sizes(lib):
     n = lib.slstm_newton_workspace_bytes(B, T, d, 1)  # layered
     assert n >= 80 * B * T * d
     assert n < 90 * B * T * d
-    # fused: a second iterate buffer (16 B) and look-back words, no Jacobians
-    nf = lib.slstm_newton_workspace_bytes(B, T, d, 0)
-    assert 16 * B * T * d <= nf < 32 * B * T * d
+    # fused forms: a second iterate buffer (16 B) and look-back words, no Jacobians; the chain
+    # form publishes 4 tagged words per lane and tile of 8 steps (4 B per state element)
+    for sched in (0, 2, 3):
+        nf = lib.slstm_newton_workspace_bytes(B, T, d, sched)
+        assert 16 * B * T * d <= nf < 32 * B * T * d
+    assert lib.slstm_newton_workspace_bytes(B, T, d, 3) < 21 * B * T * d
     assert lib.slstm_newton_workspace_bytes(B, T, d, 7) == 0
     assert lib.slstm_newton_workspace_bytes(0, 1, 1, 0) == 0
     assert lib.slstm_newton_workspace_bytes(1, -1, 1, 0) == 0
     assert lib.slstm_scan_block4_workspace_bytes(2, 64, 16) > 0
-    assert lib.slstm_warm_start_workspace_bytes(2, 64, 16) > 0
+    for sched in (0, 1, 2, 3):
+        assert lib.slstm_warm_start_workspace_bytes(2, 64, 16, sched) > 0
+    assert lib.slstm_warm_start_workspace_bytes(2, 64, 16, 9) == 0
     # tiny shapes still get a control block and one tile of look-back words
     assert lib.slstm_newton_workspace_bytes(1, 1, 1, 0) >= 512
 
@@ -75,7 +80,7 @@ def test_argument_checks_return_einval(lib):
     assert _fwd(lib, fm=7) == slstm.EINVAL
     assert _fwd(lib, dt=5) == slstm.EINVAL
     assert _fwd(lib, init=3) == slstm.EINVAL
-    assert _fwd(lib, sched=2) == slstm.EINVAL
+    assert _fwd(lib, sched=9) == slstm.EINVAL
     assert _fwd(lib, P=None) == slstm.EINVAL
     assert _fwd(lib, S=ctypes.c_void_p(260)) == slstm.EINVAL      # states not 16-byte aligned
     assert _fwd(lib, fin=ctypes.c_void_p(264)) == slstm.EINVAL    # final_state not 16-byte aligned

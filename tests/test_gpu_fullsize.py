@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-@pytest.fixture(params=["fused", "layered"])
+@pytest.fixture(params=["fused_scan", "fused_chain", "layered"])
 def schedule(request):
     return request.param
 

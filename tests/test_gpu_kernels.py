@@ -86,26 +86,27 @@ def test_scan_block4_is_deterministic(gpu_lib, shape):
     assert float(np.max(np.abs(to_np(first[:1, :, :, :8]) - x_ref))) < 2e-5 * max(1.0, float(np.max(np.abs(x_ref))))
 
 
-@pytest.mark.parametrize("schedule", ["fused", "layered"])
+@pytest.mark.parametrize("schedule", ["fused_scan", "fused_chain", "layered"])
 def test_warm_start_and_newton_are_deterministic(gpu_lib, schedule):
     w = by_name("sigmoid_bf16p_b16_t4096_d1024")
     case(f"warm start / newton determinism B=2 T=4096 d=1024 {schedule}")
     inp = draw_preactivation_inputs(w, B=2, T=4096)
     P = inp["P"].to(DEV)
     R = inp["R"].to(DEV)
-    w0 = gpu_lib.warm_start(P, None, w.forget)
+    w0 = gpu_lib.warm_start(P, None, w.forget, schedule=schedule)
     S0, h0, st0 = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, schedule=schedule)
     for _ in range(3):
-        assert torch.equal(w0, gpu_lib.warm_start(P, None, w.forget))
+        assert torch.equal(w0, gpu_lib.warm_start(P, None, w.forget, schedule=schedule))
         S1, h1, st1 = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, schedule=schedule)
         assert torch.equal(S0, S1) and st0.max_abs_F == st1.max_abs_F
 
 
+@pytest.mark.parametrize("form", ["fused_scan", "fused_chain"])
 @pytest.mark.parametrize("name,B,T", [("tiny_b2_t64_d16", None, None), ("mid_b8_t1024_d256", 2, 1024),
                                       ("sigmoid_bf16p_b16_t4096_d1024", 1, 700)])
-def test_warm_start(gpu_lib, name, B, T):
+def test_warm_start(gpu_lib, name, B, T, form):
     w = by_name(name)
-    case(f"warm_start {name} B={B} T={T}")
+    case(f"warm_start {name} B={B} T={T} {form}")
     inp = draw_preactivation_inputs(w, B, T)
     P = inp["P"]
     d = P.shape[-1]
@@ -114,7 +115,7 @@ def test_warm_start(gpu_lib, name, B, T):
     s0[:, 0] = rng.uniform(-0.5, 0.5, (P.shape[0], d))
     s0[:, 1] = rng.uniform(0.5, 2.0, (P.shape[0], d))
     s0[:, 2] = rng.uniform(-2, 2, (P.shape[0], d))
-    out = gpu_lib.warm_start(P.to(DEV), torch.from_numpy(s0).to(DEV), w.forget)
+    out = gpu_lib.warm_start(P.to(DEV), torch.from_numpy(s0).to(DEV), w.forget, schedule=form)
     torch.cuda.synchronize()
     S_ref = ref.warm_start(to_np(P), s0.astype(np.float64), w.forget)
     S = to_np(out)

@@ -14,9 +14,9 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda"
 
 
-@pytest.fixture(params=["fused", "layered"])
+@pytest.fixture(params=["fused_scan", "fused_chain", "layered"])
 def schedule(request):
-    """Both kernel schedules of a Newton iteration must meet the same bar."""
+    """Every kernel form of a Newton iteration must meet the same bar."""
     return request.param
 
 
@@ -177,32 +177,52 @@ def test_async_stats_readback(gpu_lib, schedule):
     assert st.iters == 4 and not st.diverged and len(st.max_abs_F) == 5
 
 
-def test_schedules_agree(gpu_lib):
-    """The fused and layered schedules compute the same iterates up to float32 rounding."""
+@pytest.mark.parametrize("form", ["fused_scan", "fused_chain"])
+def test_schedules_agree(gpu_lib, form):
+    """The fused forms and the layered schedule compute the same iterates up to float32
+    rounding."""
     w = by_name("mid_b8_t1024_d256")
-    case("fused vs layered, mid workload")
+    case(f"{form} vs layered, mid workload")
     inp = draw_preactivation_inputs(w)
     P = inp["P"].to(DEV)
     R = inp["R"].to(DEV)
-    Sf, hf, stf = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, schedule="fused")
+    Sf, hf, stf = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, schedule=form)
     Sl, hl, stl = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, schedule="layered")
     torch.cuda.synchronize()
     assert stf.iters == stl.iters
     assert h_rel_err(hf, hl) < H_TOL_F32
-    for k in range(stf.iters):
+    for k in range(stf.iters + 1):
         assert stf.max_abs_F[k] == pytest.approx(stl.max_abs_F[k], rel=1e-3, abs=1e-4)
 
 
-def test_early_stop_lands_in_either_buffer(gpu_lib):
-    """Fused schedule: an early stop after an odd or even number of updates leaves the result
+def test_fused_picks_a_form(gpu_lib):
+    """schedule="fused" resolves to one of the two fused forms, bit for bit."""
+    w = by_name("mid_b8_t1024_d256")
+    case("fused (automatic form) equals fused_scan or fused_chain")
+    inp = draw_preactivation_inputs(w)
+    P = inp["P"].to(DEV)
+    R = inp["R"].to(DEV)
+    outs = {s: gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, schedule=s)
+            for s in ("fused", "fused_scan", "fused_chain")}
+    torch.cuda.synchronize()
+    assert any(torch.equal(outs["fused"][0], outs[s][0]) for s in ("fused_scan", "fused_chain"))
+
+
+@pytest.mark.parametrize("form", ["fused_scan", "fused_chain"])
+def test_early_stop_lands_in_either_buffer(gpu_lib, form):
+    """Fused forms: an early stop after an odd or even number of updates leaves the result
     in either iterate buffer; the returned states must be the stopped iterate either way."""
     w = by_name("sigmoid_bf16p_b16_t4096_d1024")
     inp = draw_preactivation_inputs(w, B=1, T=2048)
     P = inp["P"][..., :64].contiguous()
     R = inp["R"][:, :64].contiguous()
-    for K in (7, 8):
-        case(f"fused early stop, budget K={K}")
-        S, h, st, S_ref, st_ref = _run_both(gpu_lib, P, R, None, w.forget, K, w.tol, schedule="fused")
-        assert st.converged and st.iters == st_ref.iters < K
+    # n: the iteration the oracle stops at. Budgets n and n + 1 make the stop fall on the last
+    # launch (the chain form decides it after its last iteration), 7 and 8 well before it.
+    n = ref.newton(to_np(P), to_np(R), None, w.forget, 8, tol=w.tol)[1].iters
+    assert 2 <= n < 6
+    for K in sorted({n, n + 1, n + 2, 7, 8}):
+        case(f"{form} early stop at {n}, budget K={K}")
+        S, h, st, S_ref, st_ref = _run_both(gpu_lib, P, R, None, w.forget, K, w.tol, schedule=form)
+        assert st.converged and st.iters == st_ref.iters == min(n, K)
         assert h_rel_err(h, S_ref[..., 3, :]) < H_TOL_BF16
         assert torch.equal(h, S[..., 3, :])
