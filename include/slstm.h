@@ -74,6 +74,10 @@ typedef enum { SLSTM_INIT_WARM = 0, SLSTM_INIT_ZERO = 1 } slstm_init;
  *                              Newton step entering it, published by the tile before; no 4x4
  *                              maps are composed. The last iteration also forms the final
  *                              residual and h, so no separate pass over the states follows.
+ *                              A fixed-count solve (tol = 0, max_iters <= 8) runs as ONE
+ *                              kernel: each tile keeps P and its iterate in registers through
+ *                              the warm start and all iterations (a wavefront along T), so P
+ *                              is read once and only the final states are written.
  *                              Fast when there are many independent lanes, serial along T;
  *  SLSTM_SCHEDULE_FUSED        FUSED_CHAIN when B * ceil(d_h / 256) is at least the GPU's
  *                              compute-unit count, FUSED_SCAN otherwise;
@@ -223,7 +227,8 @@ typedef enum {
   SLSTM_KERNEL_INPUT_PROJECTION = 5,
   SLSTM_KERNEL_SEQUENTIAL = 6,
   SLSTM_KERNEL_NEWTON_ITERATION = 7,
-  SLSTM_KERNEL_KINDS = 8
+  SLSTM_KERNEL_NEWTON_SOLVE = 8, /* the one-kernel fixed-count solve of the chain form */
+  SLSTM_KERNEL_KINDS = 9
 } slstm_kernel_kind;
 
 slstm_status slstm_profile_enable(int on);

@@ -157,6 +157,8 @@ NewtonLayout newton_layout(int B, int T, int d, Form form) {
     L.S2 = align_up(L.desc + desc_words * 8);
     L.A = L.rhs = 0;
     L.total = align_up(L.S2 + n_state * sizeof(float));
+    if (chain)  // the one-kernel solve keeps its words from L.desc on, in place of S2
+      L.total = std::max(L.total, align_up(L.desc + slstm::pipe_desc_words(B, T, d, slstm::kPipeMaxIters) * 8));
   } else {
     const size_t desc_words = std::max(slstm::scan_desc_words(B, T, d, true), slstm::warm_desc_words(B, T, d));
     L.A = align_up(L.desc + desc_words * 8);
@@ -238,6 +240,89 @@ slstm_status stats_from_control(const Control& c, slstm_newton_stats* st) {
 
 __global__ void store_u32_kernel(unsigned int* p, unsigned int v) { *p = v; }
 
+#define HIP_RET(expr)            \
+  do {                           \
+    hipError_t e_ = (expr);      \
+    if (e_ != hipSuccess) return e_; \
+  } while (0)
+
+// the solver as one launch per iteration (every schedule; the only way with an early stop)
+hipError_t iterate(const void* P, bool bf16, const float* R, const float* state0, float* states,
+                   float* h_out, int B, int T, int d_h, bool sig, int max_iters, float tol,
+                   slstm_init init, Form form, const NewtonLayout& L, void* workspace, Control* ctl,
+                   unsigned int* tickets, hipStream_t st) {
+  auto* desc = at<unsigned long long>(workspace, L.desc);
+  const i64 n_state = static_cast<i64>(B) * T * 4 * d_h;
+  // iterate buffers: the layered schedule updates `states` in place; the fused one alternates
+  // between `states` and a workspace buffer, arranged so that iterate max_iters lands in
+  // `states` (iterate k lives in buf[k % 2])
+  float* buf[2] = {states, states};
+  if (form != Form::kLayered) {
+    float* other = at<float>(workspace, L.S2);
+    buf[0] = (max_iters % 2 == 0) ? states : other;
+    buf[1] = (max_iters % 2 == 0) ? other : states;
+  }
+  if (init == SLSTM_INIT_WARM) {
+    HIP_RET(launch_warm(P, bf16, state0, buf[0], B, T, d_h, sig, form == Form::kChain, desc, ctl, st));
+  } else {
+    HIP_RET(slstm::launch_zero(buf[0], n_state, st));
+  }
+  if (form == Form::kChain) {
+    for (int k = 0; k < max_iters; ++k) {
+      const uint32_t ep = next_epoch();
+      const bool last = k + 1 == max_iters;
+      HIP_RET(timed(SLSTM_KERNEL_NEWTON_ITERATION, st, [&] {
+        return slstm::launch_newton_chain(P, bf16, R, state0, buf[k % 2], buf[(k + 1) % 2], last ? h_out : nullptr,
+                                          B, T, d_h, sig, desc, tickets, ep, ctl, k, tol, last, st);
+      }));
+    }
+    // the last launch formed the final residual and h; what remains of the stop rule is the
+    // check of the iterate before it
+    HIP_RET(slstm::launch_settle(ctl, max_iters - 1, tol, st));
+  } else if (form == Form::kScan) {
+    for (int k = 0; k < max_iters; ++k) {
+      const uint32_t ep = next_epoch();
+      HIP_RET(timed(SLSTM_KERNEL_NEWTON_ITERATION, st, [&] {
+        return slstm::launch_newton_iteration(P, bf16, R, state0, buf[k % 2], buf[(k + 1) % 2], B, T, d_h,
+                                              sig, desc, tickets, ep, ctl, k, tol, st);
+      }));
+    }
+  } else {
+    float* A = at<float>(workspace, L.A);
+    float* rhs = at<float>(workspace, L.rhs);
+    for (int k = 0; k < max_iters; ++k) {
+      HIP_RET(timed(SLSTM_KERNEL_RESIDUAL_JACOBIAN, st, [&] {
+        return slstm::launch_residual(P, bf16, R, state0, states, A, rhs, B, T, d_h, sig, ctl,
+                                      &slstm::spread_of(ctl)->err[0][k], slstm::kErrSlotWords, slstm::ResidualMode::kSparse, -1, tol, st);
+      }));
+      const uint32_t ep = next_epoch();
+      HIP_RET(timed(SLSTM_KERNEL_SCAN_BLOCK4, st, [&] {
+        return slstm::launch_scan_block4(A, rhs, rhs, B, T, d_h, true, desc, tickets, ep, ctl, k, tol, st);
+      }));
+      HIP_RET(timed(SLSTM_KERNEL_UPDATE, st, [&] { return slstm::launch_update(states, rhs, n_state, ctl, k, st); }));
+    }
+  }
+  if (form != Form::kChain) {
+    // residual of the last iterate (the scan form first checks whether the iterate before it
+    // already met the tolerance)
+    const int chk = (form == Form::kScan) ? max_iters - 1 : -1;
+    HIP_RET(timed(SLSTM_KERNEL_FINAL_RESIDUAL, st, [&] {
+      return slstm::launch_residual(P, bf16, R, state0, buf[max_iters % 2], nullptr, nullptr, B, T, d_h, sig,
+                                    ctl, &slstm::spread_of(ctl)->err[0][max_iters], slstm::kErrSlotWords,
+                                    slstm::ResidualMode::kNone, chk, tol, st, h_out);
+    }));
+  }
+  if (form != Form::kLayered)
+    HIP_RET(slstm::launch_select_iterate(ctl, buf[0], buf[1], states, n_state, st));
+  return hipSuccess;
+}
+#undef HIP_RET
+
+// fixed-count solves of the chain form run as one pipelined kernel
+bool pipe_solve(Form form, int max_iters, float tol) {
+  return form == Form::kChain && tol == 0.0f && max_iters <= slstm::kPipeMaxIters;
+}
+
 }  // namespace
 
 namespace slstm {
@@ -300,70 +385,19 @@ slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const floa
   auto* desc = at<unsigned long long>(workspace, L.desc);
   const i64 n_state = static_cast<i64>(B) * T * 4 * d_h;
 
-  // iterate buffers: the layered schedule updates `states` in place; the fused one alternates
-  // between `states` and a workspace buffer, arranged so that iterate max_iters lands in
-  // `states` (iterate k lives in buf[k % 2])
-  float* buf[2] = {states, states};
-  if (form != Form::kLayered) {
-    float* other = at<float>(workspace, L.S2);
-    buf[0] = (max_iters % 2 == 0) ? states : other;
-    buf[1] = (max_iters % 2 == 0) ? other : states;
-  }
-
   HIP_TRY(slstm::launch_init_control(ctl, st));
-  if (init == SLSTM_INIT_WARM) {
-    HIP_TRY(launch_warm(P, bf16, state0, buf[0], B, T, d_h, sig, form == Form::kChain, desc, ctl, st));
-  } else {
-    HIP_TRY(slstm::launch_zero(buf[0], n_state, st));
-  }
   unsigned int* tickets = slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0];
-  if (form == Form::kChain) {
-    for (int k = 0; k < max_iters; ++k) {
-      const uint32_t ep = next_epoch();
-      const bool last = k + 1 == max_iters;
-      HIP_TRY(timed(SLSTM_KERNEL_NEWTON_ITERATION, st, [&] {
-        return slstm::launch_newton_chain(P, bf16, R, state0, buf[k % 2], buf[(k + 1) % 2], last ? h_out : nullptr,
-                                          B, T, d_h, sig, desc, tickets, ep, ctl, k, tol, last, st);
-      }));
-    }
-    // the last launch formed the final residual and h; what remains of the stop rule is the
-    // check of the iterate before it
-    HIP_TRY(slstm::launch_settle(ctl, max_iters - 1, tol, st));
-  } else if (form == Form::kScan) {
-    for (int k = 0; k < max_iters; ++k) {
-      const uint32_t ep = next_epoch();
-      HIP_TRY(timed(SLSTM_KERNEL_NEWTON_ITERATION, st, [&] {
-        return slstm::launch_newton_iteration(P, bf16, R, state0, buf[k % 2], buf[(k + 1) % 2], B, T, d_h,
-                                              sig, desc, tickets, ep, ctl, k, tol, st);
-      }));
-    }
-  } else {
-    float* A = at<float>(workspace, L.A);
-    float* rhs = at<float>(workspace, L.rhs);
-    for (int k = 0; k < max_iters; ++k) {
-      HIP_TRY(timed(SLSTM_KERNEL_RESIDUAL_JACOBIAN, st, [&] {
-        return slstm::launch_residual(P, bf16, R, state0, states, A, rhs, B, T, d_h, sig, ctl,
-                                      &slstm::spread_of(ctl)->err[0][k], slstm::kErrSlotWords, slstm::ResidualMode::kSparse, -1, tol, st);
-      }));
-      const uint32_t ep = next_epoch();
-      HIP_TRY(timed(SLSTM_KERNEL_SCAN_BLOCK4, st, [&] {
-        return slstm::launch_scan_block4(A, rhs, rhs, B, T, d_h, true, desc, tickets, ep, ctl, k, tol, st);
-      }));
-      HIP_TRY(timed(SLSTM_KERNEL_UPDATE, st, [&] { return slstm::launch_update(states, rhs, n_state, ctl, k, st); }));
-    }
-  }
-  if (form != Form::kChain) {
-    // residual of the last iterate (the scan form first checks whether the iterate before it
-    // already met the tolerance)
-    const int chk = (form == Form::kScan) ? max_iters - 1 : -1;
-    HIP_TRY(timed(SLSTM_KERNEL_FINAL_RESIDUAL, st, [&] {
-      return slstm::launch_residual(P, bf16, R, state0, buf[max_iters % 2], nullptr, nullptr, B, T, d_h, sig,
-                                    ctl, &slstm::spread_of(ctl)->err[0][max_iters], slstm::kErrSlotWords,
-                                    slstm::ResidualMode::kNone, chk, tol, st, h_out);
+  if (pipe_solve(form, max_iters, tol)) {
+    // the whole fixed-count solve in one pass; it writes the final states, h and every residual
+    const uint32_t ep = next_epoch();
+    HIP_TRY(timed(SLSTM_KERNEL_NEWTON_SOLVE, st, [&] {
+      return slstm::launch_newton_pipe(P, bf16, R, state0, states, h_out, B, T, d_h, sig,
+                                       init == SLSTM_INIT_WARM, max_iters, desc, tickets, ep, ctl, st);
     }));
+  } else {
+    HIP_TRY(iterate(P, bf16, R, state0, states, h_out, B, T, d_h, sig, max_iters, tol, init, form, L,
+                    workspace, ctl, tickets, st));
   }
-  if (form != Form::kLayered)
-    HIP_TRY(slstm::launch_select_iterate(ctl, buf[0], buf[1], states, n_state, st));
   HIP_TRY(slstm::launch_finalize(ctl, tol, st));
   if (h_out != nullptr || final_state != nullptr)
     HIP_TRY(slstm::launch_outputs(states, h_out, final_state, B, T, d_h, ctl, st));
@@ -373,6 +407,7 @@ slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const floa
   HIP_TRY(hipStreamSynchronize(st));
   return stats_from_control(host, stats);
 }
+
 
 slstm_status slstm_newton_read_stats(const void* workspace, size_t workspace_bytes, void* stream,
                                      slstm_newton_stats* stats) {

@@ -39,6 +39,14 @@ hipError_t launch_newton_chain(const void* P, bool p_bf16, const float* R, const
                                bool sig_forget, unsigned long long* carry, unsigned int* tickets,
                                uint32_t epoch, Control* ctl, int k_iter, float tol, bool last,
                                hipStream_t stream);
+// a whole fixed-count solve of the chain form in one pipelined pass (warm or zero initial
+// iterate, 1 <= K <= kPipeMaxIters iterations, final residual and h); writes S_K to S_out
+constexpr int kPipeMaxIters = 8;
+size_t pipe_desc_words(int B, int T, int d, int K);
+hipError_t launch_newton_pipe(const void* P, bool p_bf16, const float* R, const float* state0,
+                              float* S_out, float* h_out, int B, int T, int d, bool sig_forget,
+                              bool warm, int K, unsigned long long* carry, unsigned int* tickets,
+                              uint32_t epoch, Control* ctl, hipStream_t stream);
 // after the last chain iteration: declares iterate k final when its residual met tol
 hipError_t launch_settle(Control* ctl, int k, float tol, hipStream_t stream);
 // copies the final iterate into `states` when it ended in the other buffer (iterate k lives in

@@ -23,7 +23,8 @@ INIT = {"warm": 0, "zero": 1}
 SCHEDULE = {"fused": 0, "layered": 1, "fused_scan": 2, "fused_chain": 3}
 MAX_ITERS = 64
 KERNELS = {"warm_start": 0, "residual_jacobian": 1, "scan_block4": 2, "update": 3,
-           "final_residual": 4, "input_projection": 5, "sequential": 6, "newton_iteration": 7}
+           "final_residual": 4, "input_projection": 5, "sequential": 6, "newton_iteration": 7,
+           "newton_solve": 8}
 
 EXPORTED = [
     "slstm_status_string", "slstm_last_error", "slstm_newton_workspace_bytes",

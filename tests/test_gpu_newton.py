@@ -7,7 +7,7 @@ import torch
 
 from oracle import lanes, slstm_ref as ref
 from parity import H_TOL_BF16, H_TOL_F32, case, h_rel_err, to_np
-from workloads import by_name, draw_preactivation_inputs
+from workloads import by_name, draw_preactivation_inputs, random_states
 
 pytestmark = pytest.mark.gpu
 
@@ -226,3 +226,37 @@ def test_early_stop_lands_in_either_buffer(gpu_lib, form):
         assert st.converged and st.iters == st_ref.iters == min(n, K)
         assert h_rel_err(h, S_ref[..., 3, :]) < H_TOL_BF16
         assert torch.equal(h, S[..., 3, :])
+
+
+@pytest.mark.parametrize("init", ["warm", "zero"])
+def test_one_kernel_solve_matches_iteration_kernels(gpu_lib, init):
+    """fused_chain with tol = 0 and K <= 8 runs the whole solve as one pipelined kernel; with a
+    tolerance that is never met it runs one kernel per iteration. Both form every value with
+    the same float32 operations in the same order, so they agree bit for bit (ragged T and d,
+    a random initial state)."""
+    w = by_name("mid_b8_t1024_d256")
+    inp = draw_preactivation_inputs(w, B=3, T=999)
+    P = inp["P"][..., :200].contiguous().to(DEV)
+    R = inp["R"][:, :200].contiguous().to(DEV)
+    s0 = torch.from_numpy(random_states(w.seed + 7, 3, 1, 200)[:, 0].astype(np.float32)).to(DEV)
+    for K in (1, 3, 8):
+        case(f"one-kernel solve vs per-iteration chain, init={init}, K={K}")
+        gpu_lib.profile_reset()
+        gpu_lib.profile_enable(True)
+        Sa, ha, sta = gpu_lib.newton_forward(P, R, s0, w.forget, K, 0.0, init, raise_on_divergence=False,
+                                             schedule="fused_chain")
+        n_solve = len(gpu_lib.profile_durations("newton_solve"))
+        Sb, hb, stb = gpu_lib.newton_forward(P, R, s0, w.forget, K, 1e-30, init, raise_on_divergence=False,
+                                             schedule="fused_chain")
+        n_iter = len(gpu_lib.profile_durations("newton_iteration"))
+        gpu_lib.profile_enable(False)
+        torch.cuda.synchronize()
+        assert n_solve == 1 and n_iter == K
+        assert sta.iters == stb.iters == K
+        # the zero guess diverges: NaN in the same places (its payload may come from either
+        # operand of a product, which the compiler may order differently), equal elsewhere
+        for a, b in ((Sa, Sb), (ha, hb)):
+            nan = torch.isnan(a)
+            assert torch.equal(nan, torch.isnan(b))
+            assert torch.equal(a[~nan], b[~nan])
+        assert np.array_equal(np.array(sta.max_abs_F), np.array(stb.max_abs_F), equal_nan=True)
