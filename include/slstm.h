@@ -74,7 +74,7 @@ typedef enum { SLSTM_INIT_WARM = 0, SLSTM_INIT_ZERO = 1 } slstm_init;
  *                              Newton step entering it, published by the tile before; no 4x4
  *                              maps are composed. The last iteration also forms the final
  *                              residual and h, so no separate pass over the states follows.
- *                              A fixed-count solve (tol = 0, max_iters <= 8) runs as ONE
+ *                              A fixed-count solve (tol = 0, max_iters <= 4) runs as ONE
  *                              kernel: each tile keeps P and its iterate in registers through
  *                              the warm start and all iterations (a wavefront along T), so P
  *                              is read once and only the final states are written.

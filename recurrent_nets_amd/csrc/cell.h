@@ -39,6 +39,14 @@ __device__ __forceinline__ float log_sigmoidf(float x) {
 
 // One step. Writes the next state s[4] = (c, n, m, h); with JAC also A[16] row-major
 // (A[4*row + col] = d s[row] / d prev[col]).
+//
+// m = max(a, i~) makes one of the two gates exactly e^0 = 1: with beta = (a >= i~) and
+// e = e^{-|a - i~|}, (i', f') = (e, 1) when beta and (1, e) otherwise. Both are bitwise the
+// values e^{i~ - m} and e^{a - m}, from one exponential. On the branch the max takes, the
+// derivatives of the c and n rows reduce to (with l' = dl/df~ and D = l' r_f - r_i)
+//   dc/dm' = e (beta ? -z : c'),   dn/dm' = e (beta ? -1 : n'),
+//   dc/dh' = D dc/dm' + i' dz/dh',  dn/dh' = D dn/dm',
+// and dm/dm' = beta, dm/dh' = beta ? l' r_f : r_i.
 template <bool JAC>
 __device__ __forceinline__ void cell_step(const CellIn& pv, float pz, float pi, float pf, float po,
                                           float rz, float ri, float rf, float ro, bool sig_forget,
@@ -60,8 +68,9 @@ __device__ __forceinline__ void cell_step(const CellIn& pv, float pz, float pi, 
   const float a = lf + pv.m;
   const bool beta = a >= it;
   const float m = beta ? a : it;
-  const float ig = exp_fast(it - m);
-  const float fg = exp_fast(a - m);
+  const float e = exp_fast(-fabsf(a - it));
+  const float ig = beta ? e : 1.0f;
+  const float fg = beta ? 1.0f : e;
   const float c = fmaf(fg, pv.c, ig * z);
   const float n = fmaf(fg, pv.n, ig);
   const float rn = rcp_fast(n);
@@ -71,29 +80,24 @@ __device__ __forceinline__ void cell_step(const CellIn& pv, float pz, float pi, 
   s[2] = m;
   s[3] = h;
   if constexpr (JAC) {
-    const float b = beta ? 1.0f : 0.0f;
-    const float dm_dh = beta ? dlf * rf : ri;
-    const float dig_dm = -b * ig;
-    const float dig_dh = ig * (ri - dm_dh);
-    const float dfg_dm = (1.0f - b) * fg;
-    const float dfg_dh = fg * (dlf * rf - dm_dh);
-    const float dz_dh = (1.0f - z * z) * rz;
-    const float do_dh = o * (1.0f - o) * ro;
-    // rows c and n
-    const float c_m = pv.c * dfg_dm + z * dig_dm;
-    const float c_h = pv.c * dfg_dh + z * dig_dh + ig * dz_dh;
-    const float n_m = pv.n * dfg_dm + dig_dm;
-    const float n_h = pv.n * dfg_dh + dig_dh;
+    const float lrf = dlf * rf;
+    const float D = lrf - ri;
+    const float c_m = e * (beta ? -z : pv.c);
+    const float n_m = e * (beta ? -1.0f : pv.n);
+    const float dz_dh = fmaf(-z, z, 1.0f) * rz;
+    const float do_dh = fmaf(-o, o, o) * ro;
+    const float c_h = fmaf(c_m, D, ig * dz_dh);
+    const float n_h = n_m * D;
     // row h = o c / n: (o/n) dc - (o c / n^2) dn, plus (c/n) do on h'
     const float q1 = o * rn;
     const float q2 = h * rn;
     A[0] = fg;     A[1] = 0.0f;   A[2] = c_m;   A[3] = c_h;
     A[4] = 0.0f;   A[5] = fg;     A[6] = n_m;   A[7] = n_h;
-    A[8] = 0.0f;   A[9] = 0.0f;   A[10] = b;    A[11] = dm_dh;
+    A[8] = 0.0f;   A[9] = 0.0f;   A[10] = beta ? 1.0f : 0.0f;   A[11] = beta ? lrf : ri;
     A[12] = q1 * fg;
     A[13] = -q2 * fg;
-    A[14] = q1 * c_m - q2 * n_m;
-    A[15] = q1 * c_h - q2 * n_h + (c * rn) * do_dh;
+    A[14] = fmaf(q1, c_m, -q2 * n_m);
+    A[15] = fmaf(q1, c_h, fmaf(-q2, n_h, (c * rn) * do_dh));
   }
 }
 

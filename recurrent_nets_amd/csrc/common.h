@@ -57,6 +57,21 @@ __device__ __forceinline__ float abs_nan_inf(float x) {
   return (a == a) ? a : __int_as_float(0x7f800000);
 }
 
+// Running maximum of |x| over float32 values with NaN counted as +inf, kept on the bit
+// patterns of |x| as unsigned integers: they order like the magnitudes, and every NaN pattern
+// (exponent all ones, mantissa non-zero) lies above +inf, so a single integer max per value
+// keeps the NaN; res_max_value maps the result to a float once.
+__device__ __forceinline__ unsigned int res_max(unsigned int acc, float x) {
+  return max(acc, __float_as_uint(x) & 0x7fffffffu);
+}
+__device__ __forceinline__ float res_max_value(unsigned int acc) {
+  return acc > 0x7f800000u ? __int_as_float(0x7f800000) : __uint_as_float(acc);
+}
+__device__ __forceinline__ unsigned int wave_max_u32(unsigned int v) {
+  for (int off = 32; off > 0; off >>= 1) v = max(v, static_cast<unsigned int>(__shfl_xor(static_cast<int>(v), off, 64)));
+  return v;
+}
+
 // Device-wide running maximum of non-negative floats (bit patterns order like the values).
 __device__ __forceinline__ void atomic_max_nonneg(unsigned int* dst, float v) {
   atomicMax(dst, __float_as_uint(v));

@@ -35,11 +35,11 @@ constexpr int kChainSteps = SLSTM_CHAIN_STEPS;  // steps per tile
 #define SLSTM_CHAIN_MIN_WAVES 3
 #endif
 
-template <bool BF16, bool LAST>
+template <bool BF16, bool LAST, bool SIG>
 __global__ __launch_bounds__(kChainBlock, SLSTM_CHAIN_MIN_WAVES) void newton_chain_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S_in, float* __restrict__ S_out, float* __restrict__ h_out, int T,
-    int d, int n_jt, int n_lg, int n_tt, int sig_forget, unsigned long long* __restrict__ carry,
+    int d, int n_jt, int n_lg, int n_tt, unsigned long long* __restrict__ carry,
     unsigned int* __restrict__ tickets, int n_ctr, uint32_t epoch, Control* __restrict__ ctl,
     int k_iter, float tol) {
   constexpr int TC = kChainSteps;
@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kChainBlock, SLSTM_CHAIN_MIN_WAVES) void newton_cha
   const i64 n_lanes = static_cast<i64>(n_lg) * kChainBlock;
   const i64 lane = static_cast<i64>(lg) * kChainBlock + tid;
   auto carry_word = [&](int tile, int e) { return carry + (static_cast<i64>(tile) * 4 + e) * n_lanes + lane; };
-  const bool sig = sig_forget != 0;
+  constexpr bool sig = SIG;  // forget-gate form, fixed per instantiation
 
   // Delta entering the tile, loaded now so that it arrives while the tile's operands do
   unsigned long long pf[4] = {0ull, 0ull, 0ull, 0ull};
@@ -121,7 +121,7 @@ __global__ __launch_bounds__(kChainBlock, SLSTM_CHAIN_MIN_WAVES) void newton_cha
   }
 
   float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // Delta of the current step
-  float fmax = 0.0f, fmax_new = 0.0f;
+  unsigned int fmax = 0u, fmax_new = 0u;
   CellIn pn = pv;  // S_k+1 before the step (last iteration only)
   float* h_tile = (LAST && h_out != nullptr) ? h_out + (static_cast<i64>(b) * T + t0) * static_cast<i64>(d) : nullptr;
   if (valid) {
@@ -135,7 +135,7 @@ __global__ __launch_bounds__(kChainBlock, SLSTM_CHAIN_MIN_WAVES) void newton_cha
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           r[k] = f[k] - sv[u][k];
-          fmax = fmaxf(fmax, abs_nan_inf(r[k]));
+          fmax = res_max(fmax, r[k]);
         }
         if (u == 0 && tt > 0) {
           // Delta entering the tile: the prefetched words, or wait until the tile before
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(kChainBlock, SLSTM_CHAIN_MIN_WAVES) void newton_cha
           float fn[4];
           cell_step<false>(pn, pg[u][0], pg[u][1], pg[u][2], pg[u][3], rz, ri, rf, ro, sig, fn, nullptr);
 #pragma unroll
-          for (int k = 0; k < 4; ++k) fmax_new = fmaxf(fmax_new, abs_nan_inf(sn[k] - fn[k]));
+          for (int k = 0; k < 4; ++k) fmax_new = res_max(fmax_new, sn[k] - fn[k]);
           if (h_tile != nullptr) h_tile[static_cast<i64>(u) * d + j] = sn[3];
           pn = {sn[0], sn[1], sn[2], sn[3]};
         }
@@ -194,17 +194,17 @@ __global__ __launch_bounds__(kChainBlock, SLSTM_CHAIN_MIN_WAVES) void newton_cha
 
   // residual maxima: waves fold theirs into the block's in LDS; the last to arrive publishes
   const int l = tid & (kWave - 1);
-  const float w0 = wave_max(fmax);
-  const float w1 = LAST ? wave_max(fmax_new) : 0.0f;
+  const unsigned int w0 = wave_max_u32(fmax);
+  const unsigned int w1 = LAST ? wave_max_u32(fmax_new) : 0u;
   if (l == 0) {
-    __hip_atomic_fetch_max(&s_err[0], __float_as_uint(w0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    if (LAST) __hip_atomic_fetch_max(&s_err[1], __float_as_uint(w1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_max(&s_err[0], w0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    if (LAST) __hip_atomic_fetch_max(&s_err[1], w1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
     if (__hip_atomic_fetch_add(&s_arrived, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP) == kChainBlock / kWave - 1) {
       err_publish(&spread_of(ctl)->err[0][k_iter], kErrSlotWords, blockIdx.x,
-                  __uint_as_float(__hip_atomic_load(&s_err[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)));
+                  res_max_value(__hip_atomic_load(&s_err[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)));
       if (LAST)
         err_publish(&spread_of(ctl)->err[0][k_iter + 1], kErrSlotWords, blockIdx.x,
-                    __uint_as_float(__hip_atomic_load(&s_err[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)));
+                    res_max_value(__hip_atomic_load(&s_err[1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)));
     }
   }
   if (blockIdx.x == 0 && tid == 0) ctl->iters = k_iter + 1;
@@ -237,19 +237,21 @@ hipError_t launch_newton_chain(const void* P, bool p_bf16, const float* R, const
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const int n_ctr = ticket_counters(n_lg);
   const dim3 grid(static_cast<unsigned>(blocks));
-  const int sig = sig_forget ? 1 : 0;
   const int a = static_cast<int>(n_jt), c = static_cast<int>(n_lg), e = static_cast<int>(n_tt);
-#define SLSTM_CHAIN_LAUNCH(BF, LS)                                                                      \
-  newton_chain_kernel<BF, LS><<<grid, kChainBlock, 0, stream>>>(P, R, state0, S_in, S_out, h_out, T, d, \
-                                                                a, c, e, sig, carry, tickets, n_ctr,  \
-                                                                epoch, ctl, k_iter, tol)
+#define SLSTM_CHAIN_LAUNCH(BF, LS, SG)                                                                      \
+  newton_chain_kernel<BF, LS, SG><<<grid, kChainBlock, 0, stream>>>(P, R, state0, S_in, S_out, h_out, T, d, \
+                                                                    a, c, e, carry, tickets, n_ctr,       \
+                                                                    epoch, ctl, k_iter, tol)
+#define SLSTM_CHAIN_LAUNCH_SIG(BF, LS) \
+  if (sig_forget) SLSTM_CHAIN_LAUNCH(BF, LS, true); else SLSTM_CHAIN_LAUNCH(BF, LS, false)
   if (p_bf16) {
-    if (last) SLSTM_CHAIN_LAUNCH(true, true);
-    else SLSTM_CHAIN_LAUNCH(true, false);
+    if (last) SLSTM_CHAIN_LAUNCH_SIG(true, true);
+    else SLSTM_CHAIN_LAUNCH_SIG(true, false);
   } else {
-    if (last) SLSTM_CHAIN_LAUNCH(false, true);
-    else SLSTM_CHAIN_LAUNCH(false, false);
+    if (last) SLSTM_CHAIN_LAUNCH_SIG(false, true);
+    else SLSTM_CHAIN_LAUNCH_SIG(false, false);
   }
+#undef SLSTM_CHAIN_LAUNCH_SIG
 #undef SLSTM_CHAIN_LAUNCH
   return hipGetLastError();
 }

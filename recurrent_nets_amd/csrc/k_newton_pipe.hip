@@ -32,20 +32,20 @@ namespace slstm {
 
 constexpr int kPipeBlock = 256;  // one feature per thread
 #ifndef SLSTM_PIPE_STEPS
-#define SLSTM_PIPE_STEPS 16
+#define SLSTM_PIPE_STEPS 14
 #endif
 #ifndef SLSTM_PIPE_MIN_WAVES
-#define SLSTM_PIPE_MIN_WAVES 2
+#define SLSTM_PIPE_MIN_WAVES 3
 #endif
 constexpr int kPipeSteps = SLSTM_PIPE_STEPS;  // steps per tile
 
 __host__ __device__ constexpr int pipe_words(int K) { return 4 + 4 * K; }
 
-template <bool BF16, bool WARM>
+template <bool BF16, bool WARM, bool SIG>
 __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     float* __restrict__ S_out, float* __restrict__ h_out, int T, int d, int n_jt, int n_lg,
-    int n_tt, int sig_forget, int K, unsigned long long* __restrict__ carry,
+    int n_tt, int K, unsigned long long* __restrict__ carry,
     unsigned int* __restrict__ tickets, int n_ctr, uint32_t epoch, Control* __restrict__ ctl) {
   constexpr int TC = kPipeSteps;
   __shared__ int s_tile[2];
@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_
       __builtin_amdgcn_s_sleep(2);
     }
   };
-  const bool sig = sig_forget != 0;
+  constexpr bool sig = SIG;  // forget-gate form, fixed per instantiation
 
   // ---- the tile's pre-activations, held for the whole solve ----
   const i64 tile_row = (static_cast<i64>(b) * T + t0) * 4 * static_cast<i64>(d);
@@ -89,9 +89,9 @@ __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_
 #pragma unroll
     for (int k = 0; k < 4; ++k) p[u][k] = 0.0f;
     if (valid && t0 + u < T) {
-      const unsigned o = u * 4u * ud + j;
+      // lane part j in the vector offset, step and gate parts in the scalar offset
 #pragma unroll
-      for (int k = 0; k < 4; ++k) p[u][k] = buf_ld_p<BF16>(rsP, o, k * ud);
+      for (int k = 0; k < 4; ++k) p[u][k] = buf_ld_p<BF16>(rsP, j, (4u * u + k) * ud);
     }
   }
   float rz = 0.0f, ri = 0.0f, rf = 0.0f, ro = 0.0f;
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_
   for (int k = 0; k < K; ++k) {
     CellIn pv = {hv[0], hv[1], hv[2], hv[3]};
     float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    float fmax = 0.0f;
+    unsigned int fmax = 0u;
     if (valid) {
 #pragma unroll
       for (int u = 0; u < TC; ++u) {
@@ -164,7 +164,7 @@ __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             r[e] = f[e] - s[u][e];
-            fmax = fmaxf(fmax, abs_nan_inf(r[e]));
+            fmax = res_max(fmax, r[e]);
           }
           if (u == 0 && wait) {
             // the Newton step entering the tile; the state before the tile in iterate k+1
@@ -195,36 +195,35 @@ __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_
         for (int e = 0; e < 4; ++e) tag_store(word(tt, 4 + 4 * k + e), x[e], epoch);
       }
     }
-    const float wm = wave_max(fmax);
-    if (l == 0) __hip_atomic_fetch_max(&s_err[k], __float_as_uint(wm), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    const unsigned int wm = wave_max_u32(fmax);
+    if (l == 0) __hip_atomic_fetch_max(&s_err[k], wm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 
   // ---- residual of S_K, and the outputs ----
-  float fmax = 0.0f;
+  unsigned int fmax = 0u;
   if (valid) {
     const rsrc_t rsO = make_rsrc(S_out + tile_row);
-    float* h_tile = h_out != nullptr ? h_out + (static_cast<i64>(b) * T + t0) * static_cast<i64>(d) : nullptr;
+    const rsrc_t rsH = make_rsrc(h_out != nullptr ? h_out + (static_cast<i64>(b) * T + t0) * static_cast<i64>(d) : S_out);
     CellIn pv = {hv[0], hv[1], hv[2], hv[3]};
 #pragma unroll
     for (int u = 0; u < TC; ++u) {
       if (t0 + u < T) {
         float f[4];
         cell_step<false>(pv, p[u][0], p[u][1], p[u][2], p[u][3], rz, ri, rf, ro, sig, f, nullptr);
-        const unsigned o = 4u * (u * 4u * ud + j);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          fmax = fmaxf(fmax, abs_nan_inf(s[u][e] - f[e]));
-          buf_st(s[u][e], rsO, o, 4u * e * ud);
+          fmax = res_max(fmax, s[u][e] - f[e]);
+          buf_st(s[u][e], rsO, 4u * j, 4u * (4u * u + e) * ud);
         }
-        if (h_tile != nullptr) h_tile[static_cast<i64>(u) * d + j] = s[u][3];
+        if (h_out != nullptr) buf_st(s[u][3], rsH, 4u * j, 4u * u * ud);
         pv = {s[u][0], s[u][1], s[u][2], s[u][3]};
       }
     }
   }
-  const float wm = wave_max(fmax);
-  if (l == 0) __hip_atomic_fetch_max(&s_err[K], __float_as_uint(wm), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  const unsigned int wm = wave_max_u32(fmax);
+  if (l == 0) __hip_atomic_fetch_max(&s_err[K], wm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   __syncthreads();
-  if (tid <= K) err_publish(&spread_of(ctl)->err[0][tid], kErrSlotWords, blockIdx.x, __uint_as_float(s_err[tid]));
+  if (tid <= K) err_publish(&spread_of(ctl)->err[0][tid], kErrSlotWords, blockIdx.x, res_max_value(s_err[tid]));
   if (blockIdx.x == 0 && tid == 0) ctl->iters = K;
 }
 
@@ -250,19 +249,21 @@ hipError_t launch_newton_pipe(const void* P, bool p_bf16, const float* R, const 
   if (blocks > 0x7fffffffLL || K < 1 || K > kPipeMaxIters) return hipErrorInvalidValue;
   const int n_ctr = ticket_counters(n_lg);
   const dim3 grid(static_cast<unsigned>(blocks));
-  const int sig = sig_forget ? 1 : 0;
   const int a = static_cast<int>(n_jt), c = static_cast<int>(n_lg), e = static_cast<int>(n_tt);
-#define SLSTM_PIPE_LAUNCH(BF, WM)                                                                    \
-  newton_pipe_kernel<BF, WM><<<grid, kPipeBlock, 0, stream>>>(P, R, state0, S_out, h_out, T, d, a, c, \
-                                                              e, sig, K, carry, tickets, n_ctr,      \
-                                                              epoch, ctl)
+#define SLSTM_PIPE_LAUNCH(BF, WM, SG)                                                                   \
+  newton_pipe_kernel<BF, WM, SG><<<grid, kPipeBlock, 0, stream>>>(P, R, state0, S_out, h_out, T, d, a, \
+                                                                  c, e, K, carry, tickets, n_ctr,      \
+                                                                  epoch, ctl)
+#define SLSTM_PIPE_LAUNCH_SIG(BF, WM) \
+  if (sig_forget) SLSTM_PIPE_LAUNCH(BF, WM, true); else SLSTM_PIPE_LAUNCH(BF, WM, false)
   if (p_bf16) {
-    if (warm) SLSTM_PIPE_LAUNCH(true, true);
-    else SLSTM_PIPE_LAUNCH(true, false);
+    if (warm) SLSTM_PIPE_LAUNCH_SIG(true, true);
+    else SLSTM_PIPE_LAUNCH_SIG(true, false);
   } else {
-    if (warm) SLSTM_PIPE_LAUNCH(false, true);
-    else SLSTM_PIPE_LAUNCH(false, false);
+    if (warm) SLSTM_PIPE_LAUNCH_SIG(false, true);
+    else SLSTM_PIPE_LAUNCH_SIG(false, false);
   }
+#undef SLSTM_PIPE_LAUNCH_SIG
 #undef SLSTM_PIPE_LAUNCH
   return hipGetLastError();
 }

@@ -28,10 +28,10 @@ constexpr int kWarmChainBlock = 256;  // one feature per thread
 #endif
 constexpr int kWarmChainSteps = SLSTM_WARM_CHAIN_STEPS;  // steps per tile
 
-template <bool BF16>
+template <bool BF16, bool SIG>
 __global__ __launch_bounds__(kWarmChainBlock, SLSTM_WARM_CHAIN_MIN_WAVES) void warm_chain_kernel(
     const void* __restrict__ P, const float* __restrict__ state0, float* __restrict__ S, int T,
-    int d, int sig_forget, int n_jt, int n_lg, int n_tt, unsigned long long* __restrict__ carry,
+    int d, int n_jt, int n_lg, int n_tt, unsigned long long* __restrict__ carry,
     unsigned int* __restrict__ tickets, int n_ctr, uint32_t epoch) {
   constexpr int TC = kWarmChainSteps;
   __shared__ int s_tile[2];
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(kWarmChainBlock, SLSTM_WARM_CHAIN_MIN_WAVES) void w
   const i64 n_lanes = static_cast<i64>(n_lg) * kWarmChainBlock;
   const i64 lane = static_cast<i64>(lg) * kWarmChainBlock + tid;
   auto carry_word = [&](int tile, int e) { return carry + (static_cast<i64>(tile) * 3 + e) * n_lanes + lane; };
-  const bool sig = sig_forget != 0;
+  constexpr bool sig = SIG;  // forget-gate form, fixed per instantiation
 
   // the state entering the tile: prefetched from the tile before, or state0
   unsigned long long pf[3] = {0ull, 0ull, 0ull};
@@ -144,15 +144,19 @@ hipError_t launch_warm_chain(const void* P, bool p_bf16, const float* state0, fl
   const i64 blocks = n_lg * n_tt;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks));
-  const int sig = sig_forget ? 1 : 0;
   const int n_ctr = ticket_counters(n_lg);
   const int a = static_cast<int>(n_jt), c = static_cast<int>(n_lg), e = static_cast<int>(n_tt);
-  if (p_bf16)
-    warm_chain_kernel<true><<<grid, kWarmChainBlock, 0, stream>>>(P, state0, S, T, d, sig, a, c, e, carry,
-                                                                   tickets, n_ctr, epoch);
-  else
-    warm_chain_kernel<false><<<grid, kWarmChainBlock, 0, stream>>>(P, state0, S, T, d, sig, a, c, e, carry,
-                                                                    tickets, n_ctr, epoch);
+#define SLSTM_WARM_LAUNCH(BF, SG)                                                                          \
+  warm_chain_kernel<BF, SG><<<grid, kWarmChainBlock, 0, stream>>>(P, state0, S, T, d, a, c, e, carry, tickets, \
+                                                                  n_ctr, epoch)
+  if (p_bf16) {
+    if (sig_forget) SLSTM_WARM_LAUNCH(true, true);
+    else SLSTM_WARM_LAUNCH(true, false);
+  } else {
+    if (sig_forget) SLSTM_WARM_LAUNCH(false, true);
+    else SLSTM_WARM_LAUNCH(false, false);
+  }
+#undef SLSTM_WARM_LAUNCH
   return hipGetLastError();
 }
 

@@ -41,7 +41,7 @@ hipError_t launch_newton_chain(const void* P, bool p_bf16, const float* R, const
                                hipStream_t stream);
 // a whole fixed-count solve of the chain form in one pipelined pass (warm or zero initial
 // iterate, 1 <= K <= kPipeMaxIters iterations, final residual and h); writes S_K to S_out
-constexpr int kPipeMaxIters = 8;
+constexpr int kPipeMaxIters = 4;
 size_t pipe_desc_words(int B, int T, int d, int K);
 hipError_t launch_newton_pipe(const void* P, bool p_bf16, const float* R, const float* state0,
                               float* S_out, float* h_out, int B, int T, int d, bool sig_forget,
