@@ -7,16 +7,19 @@
 // As a matrix product: C (M x N) = X (M x K) * W^T with M = B*T, N = 4*d_h, K = d_in; both
 // operands are K-contiguous, and C row-major is exactly P's (B, T, 4, d_h) layout.
 //
-// Block tile 256 x 256, K step 64, 512 threads = 8 waves in a 2 x 4 arrangement, each wave a
-// 128 x 64 sub-tile made of 4 x 2 v_mfma_f32_32x32x16_bf16 accumulators (128 accumulator
-// registers). Per 16-deep K slice a wave reads 6 KB of LDS for 8 MFMAs. Both operand tiles
-// are staged through LDS with a padded row stride, double-buffered: the global loads of K step
-// s+1 are in flight (in registers) while step s is multiplied, and one barrier per step
-// separates the two buffers. Rows past M or N read zero (buffer loads against the operand's
-// extent); a K tail is zeroed explicitly. The bias is added in the epilogue, so P is written
-// once. Workgroups are renumbered so that each of the 8 XCDs works through a contiguous range
-// of tiles, ordered in groups of row panels so that the tiles an XCD runs together share
-// their row and column panels in its L2.
+// Workgroup tile 256 x 128 (rows of x by rows of W_x), 4 waves in a 2 x 2 arrangement, each wave
+// a 128 x 64 sub-tile made of 4 x 2 v_mfma_f32_32x32x16_bf16 accumulators (128 registers), so
+// two workgroups share a compute unit and one's epilogue (the float32 P write, as large as the
+// arithmetic) overlaps the other's main loop. K advances 32 at a time through a three-stage
+// LDS ring (72 KiB) filled by direct global-to-LDS buffer loads: no staging registers and no LDS
+// stores in the instruction stream, two stages in flight while one is multiplied, one barrier
+// per step. LDS rows are 64 bytes (four 16-byte chunks of 8 bf16); chunk c of row r sits in
+// slot c ^ ((r >> 1) & 3), which keeps every 8-lane group of a fragment read on distinct banks.
+// Rows past M or N read zero (buffer loads against the tile's extent); a K tail is pointed
+// outside the extent, which also reads zero. The bias is added in the epilogue, so P is written
+// once. Workgroups are renumbered so that each of the 8 XCDs works through a contiguous range of
+// tiles, ordered in groups of row panels so that the tiles an XCD runs together share row and
+// column panels in its L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -24,31 +27,55 @@ namespace slstm {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kGemmBM = 256;
-constexpr int kGemmBN = 256;
-constexpr int kGemmBK = 64;
-constexpr int kGemmLds = kGemmBK + 8;  // padded row stride in bf16 elements
-constexpr int kGemmStage = (kGemmBM + kGemmBN) * kGemmLds;  // bf16 elements per LDS stage
-constexpr int kGemmThreads = 512;
-constexpr int kGemmGroupM = 8;
+constexpr int kGemmBN = 128;
+constexpr int kGemmBK = 32;
+constexpr int kGemmStages = 3;
+constexpr int kGemmThreads = 256;
+constexpr int kGemmRowBytes = kGemmBK * 2;                               // 64
+constexpr int kGemmStageBytes = (kGemmBM + kGemmBN) * kGemmRowBytes;     // 24 KiB
+constexpr int kGemmBlocksA = kGemmBM * kGemmRowBytes / 1024;             // 1 KiB loads: 16 for x
+constexpr int kGemmBlocks = kGemmStageBytes / 1024;                      // 24 per stage
+constexpr int kGemmBlocksPerWave = kGemmBlocks / (kGemmThreads / kWave);  // 6
+constexpr int kGemmGroupM = 4;
 constexpr int kXcds = 8;
-constexpr int kGemmLoads = kGemmBM * kGemmBK / 8 / kGemmThreads;  // 16-byte chunks per thread and operand
 // a byte offset beyond every tile extent: buffer loads there return zero, stores are dropped
 constexpr uint32_t kOutside = 0x80000000u;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 __device__ __forceinline__ rsrc_t make_rsrc_bytes(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
                                            static_cast<int>(bytes), 0x00020000);
 }
 
-__global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(const uint16_t* __restrict__ X,
+// slot of chunk c of row r in the swizzled LDS layout
+__device__ __forceinline__ uint32_t gemm_slot(uint32_t r, uint32_t c) { return c ^ ((r >> 1) & 3u); }
+
+// s_waitcnt on the vector-memory counter only (expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// one stage of the LDS ring: the x rows of the tile, then the W_x rows
+struct GemmStage {
+  unsigned char a[kGemmBM * kGemmRowBytes];
+  unsigned char b[kGemmBN * kGemmRowBytes];
+};
+
+__global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(const uint16_t* __restrict__ X,
                                                                   const uint16_t* __restrict__ W,
                                                                   const float* __restrict__ bias,
                                                                   float* __restrict__ C, int M, int N,
                                                                   int K, int tiles_m, int tiles_n) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kGemmStage];
+  // three separate objects, so that the compiler sees which stage a fragment read touches and
+  // waits only for the loads into that stage
+  __shared__ __attribute__((aligned(1024))) GemmStage st0;
+  __shared__ __attribute__((aligned(1024))) GemmStage st1;
+  __shared__ __attribute__((aligned(1024))) GemmStage st2;
 
   // ---- tile selection: XCD-contiguous ranges, grouped row panels ----
   const int nb = gridDim.x;
@@ -63,45 +90,39 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(const uint16
   const int tn = in_group / gsize;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
-  const int wm = wave >> 2;  // 0..1: 128-row half
-  const int wn = wave & 3;   // 0..3: 64-column quarter
-  const int lrow = lane & 31;
-  const int lk = (lane >> 5) * 8;
+  const int wm = wave >> 1;  // 0..1: 128-row half of the tile
+  const int wn = wave & 1;   // 0..1: 64-column half
 
   const i64 row0 = static_cast<i64>(tm) * kGemmBM;
   const i64 col0 = static_cast<i64>(tn) * kGemmBN;
-  // operand tiles as buffers: rows beyond M (N) fall outside the extent and read as zero
-  const uint32_t x_bytes = static_cast<uint32_t>(min<i64>(M - row0, kGemmBM) * K * 2);
-  const uint32_t w_bytes = static_cast<uint32_t>(min<i64>(N - col0, kGemmBN) * K * 2);
+  // extents of the operand tiles (uniform; integer selects keep them in scalar registers)
+  const int x_rows = (M - row0 < kGemmBM) ? static_cast<int>(M - row0) : kGemmBM;
+  const int w_rows = (N - col0 < kGemmBN) ? static_cast<int>(N - col0) : kGemmBN;
+  const uint32_t x_bytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x_rows) * static_cast<uint32_t>(K) * 2u);
+  const uint32_t w_bytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(w_rows) * static_cast<uint32_t>(K) * 2u);
   const rsrc_t rX = make_rsrc_bytes(X + row0 * K, x_bytes);
   const rsrc_t rW = make_rsrc_bytes(W + col0 * K, w_bytes);
 
-  u32x4 ra[kGemmLoads], rb[kGemmLoads];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < kGemmLoads; ++i) {
-      const int c = tid + kGemmThreads * i;
-      const int row = c >> 3;
-      const int gk = k0 + (c & 7) * 8;
-      // a K tail chunk is pointed past the extent, where the load returns zero
-      const uint32_t off = gk < K ? static_cast<uint32_t>((row * K + gk) * 2) : kOutside;
-      ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rX, off, 0, 0);
-      rb[i] = __builtin_amdgcn_raw_buffer_load_b128(rW, off, 0, 0);
-    }
+  // ---- global -> LDS: each wave fills 4 of the 16 x blocks and 2 of the 8 W_x blocks of a
+  //      stage (a block: 16 rows x 64 B, one 1 KiB direct load). Lane l fills slot l & 3 of row
+  //      l >> 2 of its block, i.e. fetches that row's chunk gemm_slot(row, slot) (the swizzle
+  //      is an involution). ----
+  const uint32_t lrow = static_cast<uint32_t>(lane) >> 2;
+  const uint32_t lslot = static_cast<uint32_t>(lane) & 3u;
+  auto load_block = [&](rsrc_t rs, unsigned char* dst_rows, int blk, int k0) {
+    const uint32_t r = static_cast<uint32_t>(blk * 16) + lrow;
+    const uint32_t c = gemm_slot(r, lslot);
+    const int gk = k0 + static_cast<int>(c) * 8;
+    const uint32_t off = gk < K ? (r * static_cast<uint32_t>(K) + static_cast<uint32_t>(gk)) * 2u : kOutside;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst_rows + blk * 1024), 16, off, 0, 0, 0);
   };
-  auto lstore = [&](int stage) {
-    uint16_t* sA = smem + stage * kGemmStage;
-    uint16_t* sB = sA + kGemmBM * kGemmLds;
+  auto issue = [&](GemmStage& stg, int k0) {
 #pragma unroll
-    for (int i = 0; i < kGemmLoads; ++i) {
-      const int c = tid + kGemmThreads * i;
-      const int row = c >> 3;
-      const int col = (c & 7) * 8;
-      *reinterpret_cast<u32x4*>(sA + row * kGemmLds + col) = ra[i];
-      *reinterpret_cast<u32x4*>(sB + row * kGemmLds + col) = rb[i];
-    }
+    for (int i = 0; i < 4; ++i) load_block(rX, stg.a, wave * 4 + i, k0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) load_block(rW, stg.b, wave * 2 + i, k0);
   };
 
   f32x16 acc[4][2];
@@ -112,51 +133,73 @@ __global__ __launch_bounds__(kGemmThreads, 1) void gemm_bf16_kernel(const uint16
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][jn][r] = 0.0f;
 
-  const int nk = (K + kGemmBK - 1) / kGemmBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * kGemmBK);
-    const uint16_t* sA = smem + cur * kGemmStage;
-    const uint16_t* sB = sA + kGemmBM * kGemmLds;
+  // fragment addresses within a stage: lane l reads row (l & 31) of a 32-row strip, chunk
+  // (kk / 8) + (l >> 5)
+  const uint32_t frow = static_cast<uint32_t>(lane) & 31u;
+  const uint32_t fhalf = static_cast<uint32_t>(lane) >> 5;
+  auto multiply = [&](const GemmStage& stg) {
 #pragma unroll
     for (int kk = 0; kk < kGemmBK; kk += 16) {
+      const uint32_t c = static_cast<uint32_t>(kk / 8) + fhalf;
       bf16x8 a[4], bm[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(sA + (wm * 128 + i * 32 + lrow) * kGemmLds + kk + lk);
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t r = static_cast<uint32_t>(wm * 128 + i * 32) + frow;
+        a[i] = *reinterpret_cast<const bf16x8*>(stg.a + r * kGemmRowBytes + (gemm_slot(r, c) << 4));
+      }
 #pragma unroll
-      for (int jn = 0; jn < 2; ++jn)
-        bm[jn] = *reinterpret_cast<const bf16x8*>(sB + (wn * 64 + jn * 32 + lrow) * kGemmLds + kk + lk);
+      for (int jn = 0; jn < 2; ++jn) {
+        const uint32_t r = static_cast<uint32_t>(wn * 64 + jn * 32) + frow;
+        bm[jn] = *reinterpret_cast<const bf16x8*>(stg.b + r * kGemmRowBytes + (gemm_slot(r, c) << 4));
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int jn = 0; jn < 2; ++jn)
           acc[i][jn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], bm[jn], acc[i][jn], 0, 0, 0);
     }
-    if (kt + 1 < nk) lstore(cur ^ 1);
+  };
+  // step q: wait for this wave's loads into stage q (those of stage q+1 may still be in flight),
+  // barrier (every wave's have landed; every wave is done with the stage of step q-1), refill
+  // that stage with step q+2, multiply stage q
+  const int nk = (K + kGemmBK - 1) / kGemmBK;
+  auto step = [&](int q, GemmStage& cur, GemmStage& refill) {
+    if (q + 1 < nk)
+      wait_vmcnt<kGemmBlocksPerWave>();
+    else
+      wait_vmcnt<0>();
     __syncthreads();
+    if (q + 2 < nk) issue(refill, (q + 2) * kGemmBK);
+    multiply(cur);
+  };
+  issue(st0, 0);
+  if (nk > 1) issue(st1, kGemmBK);
+  int q = 0;
+  for (; q + 3 <= nk; q += 3) {
+    step(q, st0, st2);
+    step(q + 1, st1, st0);
+    step(q + 2, st2, st1);
   }
+  if (q < nk) step(q, st0, st2);
+  if (q + 1 < nk) step(q + 1, st1, st0);
 
   // ---- epilogue: bias, float32 store. Accumulator r of lane l holds row
   //      8*(r/4) + 4*(l/32) + r%4 and column l%32 of its 32 x 32 tile. Stores go through a
   //      buffer over the output tile: rows past M fall outside its extent and are dropped,
   //      columns past N are pointed outside it. ----
-  const uint32_t c_bytes = static_cast<uint32_t>(min<i64>(M - row0, kGemmBM) * N * 4);
+  const uint32_t c_bytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x_rows) * static_cast<uint32_t>(N) * 4u);
   const rsrc_t rC = make_rsrc_bytes(C + row0 * N + col0, c_bytes);
   const int n_in = N - static_cast<int>(col0);  // columns of this tile inside C
 #pragma unroll
   for (int jn = 0; jn < 2; ++jn) {
-    const int nl = wn * 64 + jn * 32 + lrow;
+    const int nl = wn * 64 + jn * 32 + static_cast<int>(frow);
     const bool col_ok = nl < n_in;
     const float bn = (bias != nullptr && col_ok) ? bias[col0 + nl] : 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int ml = wm * 128 + i * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
+        const int ml = wm * 128 + i * 32 + (r >> 2) * 8 + static_cast<int>(fhalf) * 4 + (r & 3);
         const uint32_t off = col_ok ? static_cast<uint32_t>((ml * N + nl) * 4) : kOutside;
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][jn][r] + bn), rC, off, 0, 0);
       }
