@@ -4,9 +4,11 @@
 One step is one pass of the whole hot path over one batch of synthetic input. For the
 full-layer workload (B=128, T=2048, d_in=d_h=1024, bf16 x and W_x):
     bf16 MFMA input projection -> Newton forward (warm start, K x [residual + Jacobian,
-    4x4 scan, update], final residual, flags, h and final-state outputs) -> a T=1
-    sequential decode step at B=128 continuing from the final state (its own projection).
-For workloads whose solver input is P the step is the Newton forward alone.
+    block-bidiagonal solve, update], final residual, flags, h and final-state outputs) -> a
+    T=1 sequential decode step at B=128 continuing from the final state (its own projection).
+For workloads whose solver input is P the step is the Newton forward alone. The Newton
+forward runs in the schedule the library picks for the shape (--schedule fused); the scan
+form of the fused iteration and the layered schedule are timed after it as context.
 
 Prints ONE JSON line on stdout. Timing: W untimed warm-up steps, then exactly K steps
 between two device synchronisations, wall clock. Per-kernel durations come from HIP events
@@ -32,6 +34,10 @@ if ROOT not in sys.path:
 METRIC = "sLSTM Newton forward state-elems/s (B·T·d_h) + % HBM roofline, 1 MI355X"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
+# MI355X fp32 vector peak, published: 256 CUs x 4 SIMDs x 16 lanes x 2 (FMA) x 2 (packed
+# dual-rate fp32) x 2.4 GHz = 157.3 TFLOP/s. The library's kernels are built without packed
+# fp32 instructions, so 78.6 TFLOP/s is their ceiling for pure FMA streams.
+FP32_VECTOR_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
@@ -47,17 +53,34 @@ def log(*a):
 JAC_BYTES = 12 * 4
 
 
+def solve_flops_per_elem(K, sigmoid_forget):
+    """Floating-point operations of one state element of a whole Newton solve as the kernels
+    form them (an add, multiply, compare-select or max counts 1, an FMA 2, an exp2, log2 or
+    reciprocal 1): warm-start step 26, cell step 34, its Jacobian 31, residual and its maximum
+    8, the 4x4 recurrence (11 FMA) 22, the update 4; the sigmoid forget gate adds a log-sigmoid
+    to every step (6) and its derivative to every Jacobian (5)."""
+    sig = 1 if sigmoid_forget else 0
+    warm = 26 + 6 * sig
+    cell = 34 + 6 * sig
+    jac = 31 + 5 * sig
+    return warm + K * (cell + jac + 8 + 22 + 4) + (cell + 8)
+
+
 def kernel_work(w, n_e, p_bytes):
-    """Algorithmic bytes per launch of each kernel kind: every operand of every state
-    element read once and every result written once (per element: P p_bytes, a state 16,
-    a right-hand side / Newton step 16, the Jacobian JAC_BYTES)."""
+    """Algorithmic work per launch of each kernel kind. Bytes: every operand of every state
+    element read once and every result written once (per element: P p_bytes, a state 16, a
+    right-hand side / Newton step 16, the Jacobian JAC_BYTES, h 4). The one-kernel solve is
+    bound by its vector instructions, so its figure is the flop count of solve_flops_per_elem;
+    its bytes (P in; S_K and h out) are kept for the HBM view."""
     return {
-        "warm_start": ("hbm", n_e * (p_bytes + 16)),                        # P in, S out
-        "residual_jacobian": ("hbm", n_e * (p_bytes + 16 + JAC_BYTES + 16)),  # P, S in; A, rhs out
-        "scan_block4": ("hbm", n_e * (JAC_BYTES + 16 + 16)),                # A, rhs in; Delta out
-        "update": ("hbm", n_e * 48),                                        # S, Delta in; S out
-        "final_residual": ("hbm", n_e * (p_bytes + 16)),                    # P, S in
-        "newton_iteration": ("hbm", n_e * (p_bytes + 16 + 16)),             # P, S_k in; S_k+1 out
+        "warm_start": {"bound": "hbm", "bytes": n_e * (p_bytes + 16)},                        # P in, S out
+        "residual_jacobian": {"bound": "hbm", "bytes": n_e * (p_bytes + 16 + JAC_BYTES + 16)},  # P, S in; A, rhs out
+        "scan_block4": {"bound": "hbm", "bytes": n_e * (JAC_BYTES + 16 + 16)},                # A, rhs in; Delta out
+        "update": {"bound": "hbm", "bytes": n_e * 48},                                        # S, Delta in; S out
+        "final_residual": {"bound": "hbm", "bytes": n_e * (p_bytes + 16)},                    # P, S in
+        "newton_iteration": {"bound": "hbm", "bytes": n_e * (p_bytes + 16 + 16)},             # P, S_k in; S_k+1 out
+        "newton_solve": {"bound": "alu", "bytes": n_e * (p_bytes + 16 + 4),                   # P in; S_K, h out
+                         "flops": n_e * solve_flops_per_elem(w.max_iters, w.forget == "sigmoid")},
     }
 
 
@@ -76,6 +99,8 @@ KERNEL_SOURCES = {
                     "recurrent_nets_amd/csrc/common.h"],
     "newton_iteration": ["recurrent_nets_amd/csrc/k_newton_fused.hip", "recurrent_nets_amd/csrc/affine4.h",
                          "recurrent_nets_amd/csrc/cell.h", "recurrent_nets_amd/csrc/common.h"],
+    "newton_solve": ["recurrent_nets_amd/csrc/k_newton_pipe.hip", "recurrent_nets_amd/csrc/cell.h",
+                     "recurrent_nets_amd/csrc/common.h", "recurrent_nets_amd/csrc/kernels.h"],
     "update": ["recurrent_nets_amd/csrc/k_update.hip", "recurrent_nets_amd/csrc/common.h"],
     "warm_start": ["recurrent_nets_amd/csrc/k_warm.hip", "recurrent_nets_amd/csrc/cell.h",
                    "recurrent_nets_amd/csrc/common.h"],
@@ -172,12 +197,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="layer_b128_t2048_d1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-lanes", type=int, default=4096)
+    ap.add_argument("--cpu-lanes", type=int, default=40960)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain device copy of 4 GiB (counter calibration runs)")
     ap.add_argument("--no-sequential-context", action="store_true")
-    ap.add_argument("--schedule", default="fused", choices=["fused", "layered"])
-    ap.add_argument("--no-layered-context", action="store_true")
+    ap.add_argument("--schedule", default="fused", choices=["fused", "fused_scan", "fused_chain", "layered"])
+    ap.add_argument("--no-layered-context", action="store_true",
+                    help="skip the context runs of the scan form and the layered schedule")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -262,13 +288,16 @@ def main():
         ms = (t1 - t0) * 1000.0 / steps
         log(f"[bench] {schedule}: {steps} timed steps, {ms:.3f} ms/step")
         kernels = {}
-        for kind, (bound, nbytes) in work.items():
+        for kind, wk in work.items():
             d = slstm.profile_durations(kind)
             if not d:
                 continue
             avg = sum(d) / len(d)
             kernels[kind] = {"launches": len(d), "avg_ms": avg, "total_ms_per_step": sum(d) / steps,
-                             "bytes_per_launch": nbytes, "GB_s": nbytes / (avg * 1e-3) / 1e9}
+                             "bytes_per_launch": wk["bytes"], "GB_s": wk["bytes"] / (avg * 1e-3) / 1e9}
+            if "flops" in wk:
+                kernels[kind]["flops_per_launch"] = wk["flops"]
+                kernels[kind]["TFLOP_s"] = wk["flops"] / (avg * 1e-3) / 1e12
         if w.on_gpu_gemm:
             d = slstm.profile_durations("input_projection")
             big = d[0::2]
@@ -289,19 +318,35 @@ def main():
         return ms, kernels, st
 
     def roofline_of(kernels, steps, ms):
-        dominant = max((k for k in kernels if k in work), key=lambda k: kernels[k]["total_ms_per_step"])
-        achieved = kernels[dominant]["GB_s"]
-        roof = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": measured_traffic(dominant, w.name)}
+        dominant = max((k for k in kernels if k in work or k == "input_projection"),
+                       key=lambda k: kernels[k]["total_ms_per_step"])
+        k = kernels[dominant]
+        if dominant == "input_projection":
+            roof = {"bound": "mfma", "kernel": dominant, "achieved": round(k["TFLOP_s"], 1),
+                    "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(k["TFLOP_s"] / BF16_PEAK_TFLOPS, 4)}
+        elif work[dominant]["bound"] == "alu":
+            roof = {"bound": "alu", "kernel": dominant, "achieved": round(k["TFLOP_s"], 1),
+                    "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(k["TFLOP_s"] / FP32_VECTOR_PEAK_TFLOPS, 4),
+                    "hbm_view": {"achieved": round(k["GB_s"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                 "frac": round(k["GB_s"] / HBM_PEAK_GBS, 4)}}
+        else:
+            roof = {"bound": "hbm", "kernel": dominant, "achieved": round(k["GB_s"], 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(k["GB_s"] / HBM_PEAK_GBS, 4)}
+        roof["traffic"] = measured_traffic(dominant, w.name)
         # whole-step roofline: every kernel at its own bound
         t_roof = 0.0
-        for kind, k in kernels.items():
-            if kind in work:
-                t_roof += k["launches"] / steps * k["bytes_per_launch"] / (HBM_PEAK_GBS * 1e9)
-            elif kind == "input_projection":
-                t_roof += max(k["flops_per_launch"] / (BF16_PEAK_TFLOPS * 1e12),
-                              k["bytes_per_launch"] / (HBM_PEAK_GBS * 1e9))
+        for kind, kk in kernels.items():
+            per_step = kk["launches"] / steps
+            if kind == "input_projection":
+                t_roof += per_step * max(kk["flops_per_launch"] / (BF16_PEAK_TFLOPS * 1e12),
+                                         kk["bytes_per_launch"] / (HBM_PEAK_GBS * 1e9))
+            elif kind in work:
+                wk = work[kind]
+                t = wk["bytes"] / (HBM_PEAK_GBS * 1e9)
+                if "flops" in wk:
+                    t = max(t, wk["flops"] / (FP32_VECTOR_PEAK_TFLOPS * 1e12))
+                t_roof += per_step * t
         return roof, t_roof / (ms * 1e-3)
 
     def rounded(kernels):
@@ -319,6 +364,14 @@ def main():
         context["gemm"] = {"TFLOP_s": round(gk["TFLOP_s"], 1), "peak": BF16_PEAK_TFLOPS,
                            "frac": round(gk["TFLOP_s"] / BF16_PEAK_TFLOPS, 4),
                            "traffic": measured_traffic("input_projection", w.name)}
+    if not args.no_layered_context and args.schedule not in ("layered", "fused_scan"):
+        # the scan form of the fused iteration: residual, Jacobian, 4x4 affine scan with look-back
+        # and update in one kernel per iteration
+        ssteps = max(2, args.steps // 2)
+        sms, skernels, _ = timed_run("fused_scan", ssteps, 1)
+        sroof, _ = roofline_of(skernels, ssteps, sms)
+        context["fused_scan"] = {"ms_per_step": round(sms, 4), "state_elems_per_s": n_e / (sms * 1e-3),
+                                 "roofline": sroof, "kernels": rounded(skernels)}
     if not args.no_layered_context and args.schedule != "layered":
         # the layered schedule: kernels (a) residual + Jacobian, (b) scan, (c) update
         lsteps = max(2, args.steps // 2)
