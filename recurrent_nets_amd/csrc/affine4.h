@@ -91,98 +91,6 @@ __device__ __forceinline__ void quad_inclusive_scan(float M[16], float v[4], int
 
 constexpr int kLookBackWords = 24;  // per lane and tile: x_end (4), M (16), v (4)
 
-// Look-back along T for one lane of a tile (called by one thread per lane, lane l of the tile).
-// agg (20 floats: M row-major, then v) is the tile's composed map; returns in carry the value
-// entering the tile (x before the tile's first step; zero before the first tile).
-//
-// Fixed dataflow, so results do not depend on scheduling: tiles whose index is a multiple of
-// the anchor stride publish their inclusive value x_end = M carry + v; the others publish
-// their aggregate before waiting. A tile folds its predecessors' aggregates down to the nearest
-// anchor, always in the same order, and applies the anchor's inclusive value. Words are
-// epoch-tagged (see tag_store); the words of tile t for lane L sit at
-// desc[(t * kLookBackWords + w) * n_lanes_pad + L].
-// The words of the anchor's inclusive value can be loaded ahead of time (look_back_prefetch):
-// when they already carry this launch's epoch the wait costs nothing.
-struct LookBackPrefetch {
-  unsigned long long w[4];
-};
-
-__device__ __forceinline__ LookBackPrefetch look_back_prefetch(const unsigned long long* __restrict__ desc,
-                                                               i64 n_lanes_pad, i64 my_lane, int tt,
-                                                               int anchor_stride) {
-  LookBackPrefetch pf = {{0ull, 0ull, 0ull, 0ull}};
-  if (tt > 0) {
-    const int a = ((tt - 1) / anchor_stride) * anchor_stride;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      pf.w[e] = __hip_atomic_load(const_cast<unsigned long long*>(desc) + (static_cast<i64>(a) * kLookBackWords + e) * n_lanes_pad + my_lane,
-                                  __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  return pf;
-}
-
-__device__ __forceinline__ void tile_look_back(const float* agg, float carry[4],
-                                               unsigned long long* __restrict__ desc,
-                                               i64 n_lanes_pad, i64 my_lane, int tt,
-                                               int anchor_stride, uint32_t epoch,
-                                               const LookBackPrefetch* pf = nullptr) {
-  auto word = [&](int tile, int w) {
-    return desc + (static_cast<i64>(tile) * kLookBackWords + w) * n_lanes_pad + my_lane;
-  };
-#pragma unroll
-  for (int e = 0; e < 4; ++e) carry[e] = 0.0f;
-  const bool anchor = (tt % anchor_stride) == 0;
-  if (!anchor) {
-#pragma unroll
-    for (int e = 0; e < 20; ++e) tag_store(word(tt, 4 + e), agg[e], epoch);
-  }
-  if (tt > 0) {
-    const int a = ((tt - 1) / anchor_stride) * anchor_stride;  // nearest anchor below
-    // accumulated map of the tiles a+1 .. tt-1
-    float Macc[16], vacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int e = 0; e < 16; ++e) Macc[e] = (e % 5 == 0) ? 1.0f : 0.0f;
-    for (int p = tt - 1; p > a; --p) {
-      float Mp[16], vp[4];
-      while (true) {
-        bool ok = true;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) ok &= tag_load(word(p, 4 + e), epoch, Mp[e]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ok &= tag_load(word(p, 20 + e), epoch, vp[e]);
-        if (ok) break;
-        __builtin_amdgcn_s_sleep(2);
-      }
-      compose_after(Macc, vacc, Mp, vp);
-    }
-    float xin[4];
-    bool ok = pf != nullptr;
-    if (ok) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        xin[e] = __uint_as_float(static_cast<uint32_t>(pf->w[e]));
-        ok &= static_cast<uint32_t>(pf->w[e] >> 32) == epoch;
-      }
-    }
-    while (!ok) {
-      ok = true;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ok &= tag_load(word(a, e), epoch, xin[e]);
-      if (ok) break;
-      __builtin_amdgcn_s_sleep(2);
-    }
-    mat4_vec(Macc, xin, vacc, carry);
-  }
-  if (anchor) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float xe = fmaf(agg[4 * i], carry[0],
-                            fmaf(agg[4 * i + 1], carry[1], fmaf(agg[4 * i + 2], carry[2], fmaf(agg[4 * i + 3], carry[3], agg[16 + i]))));
-      tag_store(word(tt, i), xe, epoch);
-    }
-  }
-}
-
 // Broadcast lane K of each quad to the whole quad.
 template <int K>
 __device__ __forceinline__ float quad_bcast(float x) {
@@ -204,12 +112,20 @@ __device__ __forceinline__ void quad_row_of_last(const float M[16], const float 
   vq = q == 0 ? y0 : (q == 1 ? y1 : (q == 2 ? y2 : y3));
 }
 
-// The same look-back as tile_look_back, for one lane of a tile spread over the four threads of
-// a quad: thread q holds row q of the tile's aggregate (arow = M[q][0..3], av = v[q]) and
-// publishes, loads and composes only the words of row q; the rows it needs from the other
-// threads of its quad arrive by DPP. Returns the full carry in every thread of the quad. The
-// words and the fixed dataflow are those of tile_look_back. Every lane of the wave must take
-// part (the quad broadcasts run after the waits).
+// Look-back along T for one lane of a tile, spread over the four threads of a quad: thread q
+// holds row q of the tile's composed map (arow = M[q][0..3], av = v[q]) and publishes, loads and
+// folds only the words of row q; the rows it needs from the other threads of its quad arrive by
+// DPP. Returns in carry, in every thread of the quad, the value entering the tile (x before the
+// tile's first step; zero before the first tile). Every lane of the wave must take part (the
+// quad broadcasts run after the waits).
+//
+// Fixed dataflow, so results do not depend on scheduling: tiles whose index is a multiple of
+// the anchor stride publish their inclusive value x_end = M carry + v; the others publish their
+// aggregate (M, v) before waiting. A tile folds its predecessors' aggregates down to the nearest
+// anchor, always in the same order, and applies the anchor's inclusive value. Words are
+// epoch-tagged (see tag_store); the word w of tile t for lane L sits at
+// desc[(t * kLookBackWords + w) * n_lanes_pad + L]: w = 0..3 the inclusive value, 4 + 4 i + k
+// the entry (i, k) of M, 20 + i the entry i of v.
 //   pf_word: this thread's word of the anchor's inclusive value, loaded ahead of time
 //            (quad_look_back_prefetch); it costs no wait when it already carries the epoch.
 __device__ __forceinline__ unsigned long long quad_look_back_prefetch(

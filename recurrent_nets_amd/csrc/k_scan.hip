@@ -16,12 +16,13 @@
 // Level 1: every thread composes its sub-chunk sequentially in registers (A and r stay in
 //          registers for the whole kernel, so each byte is read from HBM once).
 // Level 2: inclusive scan of the 4 sub-chunk aggregates inside each quad with DPP quad
-//          permutations; the tile aggregate of each lane is staged in LDS.
-// Level 3: decoupled look-back across tiles along T: wave 0 (one thread per lane) publishes
-//          the tile aggregate, folds its predecessors' aggregates down to the nearest anchor
-//          tile, applies the anchor's inclusive value and stages the carry in LDS. The fold
-//          order is fixed, so results are bitwise reproducible. Tiles take work tickets (take_ticket),
-//          so a predecessor always holds a smaller ticket and is running or done.
+//          permutations; lane 3 of the quad then holds the tile aggregate of its feature.
+// Level 3: decoupled look-back across tiles along T, spread over the quad (quad_look_back):
+//          each thread publishes, loads and folds one row of the 4x4 maps and receives the
+//          other rows by DPP, so every wave runs the look-back of its own 16 features with no
+//          LDS staging and no barrier. The fold order is fixed, so results are bitwise
+//          reproducible. Tiles take work tickets (take_ticket), so a predecessor always holds a
+//          smaller ticket and is running or done.
 // Finally every thread re-runs its sub-chunk from its carry and stores x.
 // x may alias rhs: each thread reads its rhs values before writing the same addresses.
 //
@@ -35,12 +36,18 @@
 namespace slstm {
 
 constexpr int kScanBlock = 256;
-constexpr int kScanTSubSparse = 8;  // sub-chunk length of the Newton solver's sparse scan
+#ifndef SLSTM_SCAN_TSUB
+#define SLSTM_SCAN_TSUB 6
+#endif
+#ifndef SLSTM_SCAN_MIN_WAVES
+#define SLSTM_SCAN_MIN_WAVES 3
+#endif
+constexpr int kScanTSubSparse = SLSTM_SCAN_TSUB;  // sub-chunk length of the Newton solver's sparse scan
 constexpr int kScanTSubDense = 4;   // and of the dense scan (16 values per step in registers)
 constexpr int kScanWords = kLookBackWords;
 
 template <bool SPARSE, int TSUB>
-__global__ __launch_bounds__(kScanBlock, 2) void scan_block4_kernel(
+__global__ __launch_bounds__(kScanBlock, SLSTM_SCAN_MIN_WAVES) void scan_block4_kernel(
     const float* __restrict__ A, const float* rhs, float* x, int T, int d, int n_jt, int n_lg,
     int n_tt, int anchor_stride, unsigned long long* __restrict__ desc,
     unsigned int* __restrict__ tickets, int n_ctr, uint32_t epoch, Control* ctl, int k_iter, float tol) {
@@ -57,8 +64,6 @@ __global__ __launch_bounds__(kScanBlock, 2) void scan_block4_kernel(
     }
   }
   __shared__ int s_tile[2];
-  __shared__ float s_agg[64][21];
-  __shared__ float s_carry[64][4];
 
   const int tid = threadIdx.x;
   if (tid == 0) take_ticket(tickets, n_ctr, n_lg, n_tt, s_tile[0], s_tile[1]);
@@ -70,6 +75,7 @@ __global__ __launch_bounds__(kScanBlock, 2) void scan_block4_kernel(
 
   const int wave = tid >> 6;
   const int l = tid & 63;
+  (void)wave;
   const int sc = l & 3;
   const int lane_in_tile = wave * 16 + (l >> 2);
   const unsigned j = static_cast<unsigned>(jt * 64 + lane_in_tile);
@@ -85,6 +91,9 @@ __global__ __launch_bounds__(kScanBlock, 2) void scan_block4_kernel(
   const unsigned a_lane = 4u * (static_cast<unsigned>(sc * TSUB) * 16u * ud + j);  // bytes
   const unsigned r_lane = 4u * (static_cast<unsigned>(sc * TSUB) * 4u * ud + j);
   const unsigned row_b = 4u * ud;  // bytes per plane row
+  const i64 my_lane = static_cast<i64>(lg) * 64 + lane_in_tile;
+  // this thread's word of the look-back anchor, loaded now so that it arrives meanwhile
+  const unsigned long long pf = quad_look_back_prefetch(desc, n_lanes_pad, my_lane, sc, tt, anchor_stride);
 
   // ---- level 1: load the sub-chunk and compose it ----
   float a[TSUB][NA], r[TSUB][4];
@@ -143,28 +152,17 @@ __global__ __launch_bounds__(kScanBlock, 2) void scan_block4_kernel(
 
   // ---- level 2: inclusive scan of the quad's sub-chunk aggregates (DPP) ----
   quad_inclusive_scan(M, v, sc);
-  if (sc == 3) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) s_agg[lane_in_tile][e] = M[e];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s_agg[lane_in_tile][16 + e] = v[e];
-  }
-  __syncthreads();
 
-  // ---- level 3: look-back across tiles, one thread per lane of the tile ----
-  if (wave == 0) {
-    float carry[4];
-    tile_look_back(s_agg[l], carry, desc, n_lanes_pad, static_cast<i64>(lg) * 64 + l, tt,
-                   anchor_stride, epoch);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) s_carry[l][e] = carry[e];
+  // ---- level 3: look-back across tiles, spread over the quad ----
+  float cin[4];
+  {
+    float arow[4], av;
+    quad_row_of_last(M, v, sc, arow, av);
+    quad_look_back(arow, av, cin, desc, n_lanes_pad, my_lane, sc, tt, anchor_stride, epoch, pf);
   }
-  __syncthreads();
 
   // ---- re-run each sub-chunk from its carry ----
-  float cin[4], xe[4], xs[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) cin[e] = s_carry[lane_in_tile][e];
+  float xe[4], xs[4];
   mat4_vec(M, cin, v, xe);  // value at the end of this sub-chunk
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -209,7 +207,7 @@ hipError_t launch_scan_block4(const float* A, const float* rhs, float* x, int B,
   scan_grid(B, T, d, tile, n_jt, n_lg, n_tt);
   const i64 blocks = n_lg * n_tt;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  const int stride = look_back_anchor_stride(n_lg, 2);
+  const int stride = look_back_anchor_stride(n_lg, SLSTM_SCAN_MIN_WAVES);
   const int n_ctr = ticket_counters(n_lg);
   const dim3 grid(static_cast<unsigned>(blocks));
   if (sparse)
