@@ -29,6 +29,12 @@ What it computes, and where each step is stated:
   LAPACK solve of the assembled system.
 * input projection P = W_x x + b ("W_x is a GEMM" -- "sLSTM in this library", "API
   notes").
+* backward ("sLSTM in this library", section "Backward": the adjoint is one reverse scan of
+  the transposed Jacobians, then the cell's vector-Jacobian product for the gradients of R
+  and W_x): lam_T = g_T, lam_t = g_t + A_{t+1}^T lam_{t+1}; per step the gate Jacobian
+  G_t = d s_t / d x~_t gives dP_t = G_t^T lam_t, dR = sum dP_t * h_{t-1}, dstate0 = A_1^T lam_1.
+  Written here as a plain reverse loop, and on tiny inputs as a dense LAPACK solve of the
+  transposed system.
 
 Readings where the pages are silent (each listed in the design notes):
 
@@ -86,6 +92,40 @@ def log_forget(f_tilde, forget):
 # ---------------------------------------------------------------------------------------
 # the cell f and its 4x4 Jacobian
 # ---------------------------------------------------------------------------------------
+def preactivations(prev, p, r):
+    """Gate pre-activations x~ = p_x + r_x h' for x in (z, i, f, o) (channelwise R)."""
+    h0 = prev[..., H, :]
+    zt = p[..., GZ, :] + r[GZ] * h0
+    it = p[..., GI, :] + r[GI] * h0
+    ft = p[..., GF, :] + r[GF] * h0
+    ot = p[..., GO, :] + r[GO] * h0
+    return zt, it, ft, ot
+
+
+def _step(prev, p, r, forget):
+    """The intermediate values of one step, shared by the state, its Jacobian and the gate
+    Jacobian (equations in ``cell``)."""
+    c0, n0, m0 = prev[..., C, :], prev[..., N, :], prev[..., M, :]
+    zt, it, ft, ot = preactivations(prev, p, r)
+    z = np.tanh(zt)
+    o = sigmoid(ot)
+    lf, dlf = log_forget(ft, forget)
+    a = lf + m0
+    beta = a >= it  # tie -> forget branch
+    m = np.where(beta, a, it)
+    ig = np.exp(it - m)
+    fg = np.exp(a - m)
+    c = fg * c0 + ig * z
+    n = fg * n0 + ig
+    h = o * c / n  # read-out
+    return {"z": z, "o": o, "dlf": dlf, "beta": beta, "m": m, "ig": ig, "fg": fg, "c": c, "n": n, "h": h}
+
+
+def _quotient_row(o, c, n, dc, dn):
+    """Derivatives of h = o c / n through c and n (quotient rule), one per column."""
+    return [(o / n) * dc[k] - (o * c / (n * n)) * dn[k] for k in range(len(dc))]
+
+
 def cell(prev, p, r, forget, with_jacobian=False):
     """One stabilised sLSTM step per feature (mix='diag').
 
@@ -102,23 +142,10 @@ def cell(prev, p, r, forget, with_jacobian=False):
       i' = exp(i~ - m),  f' = exp(a - m)                  (both in (0, 1])
       c = f' c' + i' z,  n = f' n' + i',  h = o c / n
     """
-    c0, n0, m0, h0 = prev[..., C, :], prev[..., N, :], prev[..., M, :], prev[..., H, :]
-    zt = p[..., GZ, :] + r[GZ] * h0
-    it = p[..., GI, :] + r[GI] * h0
-    ft = p[..., GF, :] + r[GF] * h0
-    ot = p[..., GO, :] + r[GO] * h0
-    z = np.tanh(zt)
-    o = sigmoid(ot)
-    lf, dlf = log_forget(ft, forget)
-    a = lf + m0
-    beta = a >= it  # tie -> forget branch
-    m = np.where(beta, a, it)
-    ig = np.exp(it - m)
-    fg = np.exp(a - m)
-    c = fg * c0 + ig * z
-    n = fg * n0 + ig
-    h = o * c / n
-    nxt = np.stack([c, n, m, h], axis=-2)
+    v = _step(prev, p, r, forget)
+    c0, n0 = prev[..., C, :], prev[..., N, :]
+    z, o, dlf, beta, ig, fg, c, n = v["z"], v["o"], v["dlf"], v["beta"], v["ig"], v["fg"], v["c"], v["n"]
+    nxt = np.stack([c, n, v["m"], v["h"]], axis=-2)
     if not with_jacobian:
         return nxt
 
@@ -139,10 +166,40 @@ def cell(prev, p, r, forget, with_jacobian=False):
     dn = [zero, fg, n0 * dfg_dm + dig_dm, n0 * dfg_dh + dig_dh]
     dmr = [zero, zero, dm_dm, dm_dh]
     # row h = o c / n by the quotient rule, plus the output-gate term on h'
-    dh = [(o / n) * dc[k] - (o * c / (n * n)) * dn[k] for k in range(4)]
+    dh = _quotient_row(o, c, n, dc, dn)
     dh[H] = dh[H] + (c / n) * do_dh
     A = np.stack([np.stack(row, axis=-2) for row in (dc, dn, dmr, dh)], axis=-3)
     return nxt, A
+
+
+def gate_jacobian(prev, p, r, forget):
+    """G = d next / d x~ of one step, x~ = p + r h' the gate pre-activations (z, i, f, o).
+
+    Shape (..., 4, 4, d) with G[..., slot, gate, :] = d next[slot] / d x~[gate]. The state
+    enters the gates only through h', so the h' column of the state Jacobian is G r. Same
+    equations as ``cell``, differentiated in the pre-activations on the branch the max takes:
+      m = max(l(f~) + m', i~):  dm/di~ = 1 - beta,  dm/df~ = beta l'(f~)
+      i' = exp(i~ - m):         di'/di~ = i' (1 - dm/di~),  di'/df~ = -i' dm/df~
+      f' = exp(l + m' - m):     df'/di~ = -f' dm/di~,       df'/df~ = f' (l' - dm/df~)
+      c = f' c' + i' z,  n = f' n' + i',  h = o c / n,  z = tanh z~,  o = sigma(o~)
+    """
+    v = _step(prev, p, r, forget)
+    c0, n0 = prev[..., C, :], prev[..., N, :]
+    z, o, dlf, beta, ig, fg, c, n = v["z"], v["o"], v["dlf"], v["beta"], v["ig"], v["fg"], v["c"], v["n"]
+    b = beta.astype(np.float64)
+    dm_di = 1.0 - b
+    dm_df = b * dlf
+    dig_di = ig * (1.0 - dm_di)
+    dig_df = -ig * dm_df
+    dfg_di = -fg * dm_di
+    dfg_df = fg * (dlf - dm_df)
+    zero = np.zeros_like(c)
+    dc = [ig * (1.0 - z * z), c0 * dfg_di + z * dig_di, c0 * dfg_df + z * dig_df, zero]
+    dn = [zero, n0 * dfg_di + dig_di, n0 * dfg_df + dig_df, zero]
+    dmr = [zero, dm_di, dm_df, zero]
+    dh = _quotient_row(o, c, n, dc, dn)
+    dh[GO] = dh[GO] + (c / n) * o * (1.0 - o)
+    return np.stack([np.stack(row, axis=-2) for row in (dc, dn, dmr, dh)], axis=-3)
 
 
 def gate_values(prev, p, r, forget):
@@ -282,6 +339,57 @@ def dense_solve_lane(A_lane, F_lane):
     for t in range(1, T):
         J[4 * t:4 * t + 4, 4 * (t - 1):4 * t] = -A_lane[t]
     return np.linalg.solve(J, -F_lane.reshape(-1)).reshape(T, 4)
+
+
+def backward(P, R, state0, S, g, forget, return_adjoint=False):
+    """Gradients through the recurrence of a loss L whose direct derivative with respect to the
+    states is g = dL/dS.
+
+    P, S, g (B, T, 4, d): pre-activations, the forward states s_1..s_T (the solution) and the
+    direct gradient; R (4, d); state0 (B, 4, d) or None. Returns dP (B, T, 4, d), dR (4, d),
+    dstate0 (B, 4, d), and with return_adjoint the adjoint lam (B, T, 4, d), lam_t = dL/ds_t.
+
+    "sLSTM in this library", section "Backward": the reverse recurrence
+      lam_T = g_T,  lam_t = g_t + A_{t+1}^T lam_{t+1}     (A_{t+1} = d s_{t+1} / d s_t)
+    then per step the cell's vector-Jacobian product with the gate Jacobian G_t:
+      dP_t = G_t^T lam_t,  dR = sum over b and t of dP_t * h_{t-1},  dstate0 = A_1^T lam_1.
+    """
+    P = np.asarray(P, dtype=np.float64)
+    R = np.asarray(R, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    g = np.asarray(g, dtype=np.float64)
+    B, T, _, d = P.shape
+    prev = _shifted(S, state0)
+    dP = np.empty_like(P)
+    dR = np.zeros((4, d))
+    lam_all = np.empty_like(S)
+    lam = g[:, T - 1].copy()
+    for t in range(T - 1, -1, -1):
+        lam_all[:, t] = lam
+        _, A = cell(prev[:, t], P[:, t], R, forget, with_jacobian=True)
+        G = gate_jacobian(prev[:, t], P[:, t], R, forget)
+        delta = np.einsum("bsgd,bsd->bgd", G, lam)
+        dP[:, t] = delta
+        dR += np.sum(delta * prev[:, t, H][:, None, :], axis=0)
+        lam_prev = np.einsum("bsjd,bsd->bjd", A, lam)
+        lam = g[:, t - 1] + lam_prev if t > 0 else lam_prev
+    if return_adjoint:
+        return dP, dR, lam, lam_all
+    return dP, dR, lam
+
+
+def dense_adjoint_lane(A_lane, g_lane):
+    """Dense LAPACK solve of one lane's adjoint system (tiny inputs only).
+
+    A_lane (T, 4, 4) with A_lane[t] = d s_t / d s_{t-1}, g_lane (T, 4). The forward Newton
+    system J x = r has identity blocks on the diagonal and -A_t below it; the adjoint solves
+    J^T lam = g.
+    """
+    T = g_lane.shape[0]
+    J = np.eye(4 * T)
+    for t in range(1, T):
+        J[4 * t:4 * t + 4, 4 * (t - 1):4 * t] = -A_lane[t]
+    return np.linalg.solve(J.T, g_lane.reshape(-1)).reshape(T, 4)
 
 
 @dataclass

@@ -355,4 +355,69 @@ def pin_state0_chunking(ref):
     np.testing.assert_allclose(S, full[:, 32:], rtol=1e-11, atol=1e-13)
 
 
+def _backward_problem(seed, forget, B=2, T=10, d=3):
+    P, R = small_problem(seed, B=B, T=T, d=d, forget=forget)
+    rng = np.random.default_rng(seed + 1)
+    s0 = np.stack([rng.uniform(-0.5, 0.5, (B, d)), rng.uniform(0.5, 2.0, (B, d)),
+                   rng.uniform(-2.0, 2.0, (B, d)), rng.uniform(-0.9, 0.9, (B, d))], axis=1)
+    g = rng.standard_normal((B, T, 4, d))
+    return P, R, s0, g
+
+
+def pin_backward_finite_differences(ref):
+    """The backward is the gradient of L = sum(g * S(P, R, state0)) with S the sequential
+    solution: central differences in float64 on entries of P, every entry of R, and entries of
+    state0, for both forget-gate forms ("sLSTM in this library", "Backward")."""
+    for seed, forget in ((41, "exp"), (43, "sigmoid")):
+        P, R, s0, g = _backward_problem(seed, forget)
+        S = ref.sequential(P, R, s0, forget)
+        dP, dR, ds0 = ref.backward(P, R, s0, S, g, forget)
+
+        def loss(P_, R_, s_):
+            return float(np.sum(g * ref.sequential(P_, R_, s_, forget)))
+
+        eps = 1e-6
+        scale = max(1.0, float(np.max(np.abs(dP))), float(np.max(np.abs(dR))))
+
+        def fd(which, idx):
+            args_p = [P.copy(), R.copy(), s0.copy()]
+            args_m = [P.copy(), R.copy(), s0.copy()]
+            args_p[which][idx] += eps
+            args_m[which][idx] -= eps
+            return (loss(*args_p) - loss(*args_m)) / (2 * eps)
+
+        for idx in [(0, 0, 0, 0), (1, 5, 2, 1), (0, 9, 3, 2), (1, 3, 1, 0), (0, 7, 0, 2)]:
+            assert abs(fd(0, idx) - dP[idx]) < 1e-6 * scale, (forget, "P", idx)
+        for gi in range(4):
+            for j in range(R.shape[1]):
+                assert abs(fd(1, (gi, j)) - dR[gi, j]) < 1e-6 * scale, (forget, "R", gi, j)
+        for idx in [(0, 0, 1), (1, 2, 2), (0, 3, 0), (1, 1, 2)]:
+            assert abs(fd(2, idx) - ds0[idx]) < 1e-6 * scale, (forget, "state0", idx)
+
+
+def pin_backward_adjoint_dense(ref):
+    """The reverse recurrence solves the transposed block-bidiagonal system: its adjoint equals a
+    dense LAPACK solve of J^T lam = g for every lane (J the forward Newton matrix)."""
+    P, R, s0, g = _backward_problem(47, "exp", T=12)
+    S = ref.sequential(P, R, s0, "exp")
+    _, A = ref.residual(S, P, R, s0, "exp")
+    _, _, _, lam = ref.backward(P, R, s0, S, g, "exp", return_adjoint=True)
+    for b in range(P.shape[0]):
+        for j in range(P.shape[-1]):
+            dense = ref.dense_adjoint_lane(A[b, :, :, :, j], g[b, :, :, j])
+            np.testing.assert_allclose(lam[b, :, :, j], dense, rtol=1e-10, atol=1e-12)
+
+
+def pin_gate_jacobian_h_column(ref):
+    """h' enters the cell only through the gate pre-activations x~ = p + r h', so the h' column
+    of the state Jacobian is G r (G = d next / d x~), to rounding."""
+    for forget in ("exp", "sigmoid"):
+        P, R = small_problem(53, T=8, forget=forget)
+        S = ref.sequential(P, R, None, forget)
+        prev = S[:, :-1]
+        _, A = ref.cell(prev, P[:, 1:], R, forget, with_jacobian=True)
+        G = ref.gate_jacobian(prev, P[:, 1:], R, forget)
+        np.testing.assert_allclose(A[..., :, 3, :], np.einsum("btsgd,gd->btsd", G, R), rtol=1e-12, atol=1e-14)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

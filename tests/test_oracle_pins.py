@@ -28,7 +28,7 @@ MUTATIONS = [
     ("wrong sign in stabiliser gate", "ig = np.exp(it - m)\n    fg = np.exp(a - m)\n    c =",
      "ig = np.exp(m - it)\n    fg = np.exp(a - m)\n    c ="),
     ("tie to input branch", "beta = a >= it  # tie", "beta = a > it  # tie"),
-    ("read-out floor variant", "h = o * c / n\n    nxt", "h = o * c / np.maximum(np.abs(n), 1.0)\n    nxt"),
+    ("read-out floor variant", "h = o * c / n  # read-out", "h = o * c / np.maximum(np.abs(n), 1.0)  # read-out"),
     ("quotient rule sign", "- (o * c / (n * n)) * dn[k]", "+ (o * c / (n * n)) * dn[k]"),
     ("missing output-gate term", "dh[H] = dh[H] + (c / n) * do_dh", "dh[H] = dh[H]"),
     ("sigmoid-forget derivative", "return -_softplus(-f_tilde), sigmoid(-f_tilde)",
@@ -41,6 +41,13 @@ MUTATIONS = [
     ("early stop after the solve", "if tol > 0 and e < tol:\n                stopped = True",
      "if tol > 0 and e < tol * 1e-30:\n                stopped = True"),
     ("divergence threshold", "diverged = nonfinite or e_final > 1.0", "diverged = nonfinite or e_final > 10.0"),
+    ("backward: transposed gate Jacobian", 'np.einsum("bsgd,bsd->bgd", G, lam)', 'np.einsum("bgsd,bsd->bgd", G, lam)'),
+    ("backward: dropped direct gradient", "lam = g[:, t - 1] + lam_prev if t > 0 else lam_prev",
+     "lam = lam_prev"),
+    ("backward: dR against h_t", "dR += np.sum(delta * prev[:, t, H][:, None, :], axis=0)",
+     "dR += np.sum(delta * S[:, t, H][:, None, :], axis=0)"),
+    ("gate Jacobian: forget derivative", "dfg_df = fg * (dlf - dm_df)", "dfg_df = fg * (1.0 - dm_df)"),
+    ("gate Jacobian: output-gate term", "dh[GO] = dh[GO] + (c / n) * o * (1.0 - o)", "dh[GO] = dh[GO]"),
 ]
 
 
