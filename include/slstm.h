@@ -212,6 +212,38 @@ slstm_status slstm_warm_start(const void* P, slstm_dtype P_dtype, const float* s
                               slstm_schedule schedule, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/* Workspace bytes of slstm_backward (0 if invalid). */
+size_t slstm_backward_workspace_bytes(int B, int T, int d_h, slstm_schedule schedule);
+
+/*
+ * Gradients through the recurrence ("sLSTM in this library", section "Backward"): the adjoint
+ * lam_t = dL/ds_t, from lam_{T-1} = g_{T-1} and lam_t = g_t + A_{t+1}^T lam_{t+1} (A_t the 4x4
+ * Jacobian of step t with respect to the state before it), then per step the vector-Jacobian
+ * product of the cell with respect to its pre-activations.
+ *   P (B, T, 4, d_h) f32 or bf16, R (4, d_h), state0 (B, 4, d_h) or NULL (zeros): as given to
+ *     the forward call.
+ *   states (B, T, 4, d_h) f32: the forward solution s_1..s_T (slots c, n, m, h), as the Newton
+ *     or the sequential forward wrote it. 16-byte aligned.
+ *   g_states (B, T, 4, d_h) or NULL: dL/d states.  g_h (B, T, d_h) or NULL: dL/d h, added to
+ *     slot 3.  g_final (B, 4, d_h) or NULL: dL/d of the final state, added at step T-1. A NULL
+ *     gradient counts as zeros.
+ *   dP (B, T, 4, d_h) f32, written: dL/dP per gate (z, i, f, o). P = W_x x + bias, so the
+ *     gradients of W_x, x and the bias are products of dP with x and W_x and a sum of dP.
+ *   dR (4, d_h) f32, written: dL/dR = sum over b, t of dP[b, t, g, j] * h_{t-1}[b, j], with
+ *     h_0 taken from state0.
+ *   dstate0 (B, 4, d_h) f32 or NULL, written: dL/d state0 (at the zero state if state0 is NULL).
+ * schedule: SLSTM_SCHEDULE_FUSED and SLSTM_SCHEDULE_FUSED_CHAIN run one kernel of tile-serial
+ * reverse chains along T (and a fixed-order sum of dR over the batch); other values are
+ * rejected. The workspace (slstm_backward_workspace_bytes, 256-byte aligned) is the caller's;
+ * results are bitwise reproducible. Negative status: nothing valid was written. Outputs must
+ * not alias inputs.
+ */
+slstm_status slstm_backward(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
+                            const float* states, const float* g_states, const float* g_h,
+                            const float* g_final, float* dP, float* dR, float* dstate0, int B,
+                            int T, int d_h, slstm_forget fmode, slstm_schedule schedule,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /*
  * Kernel timing with HIP events recorded on the launching stream around every kernel the
  * library launches, for measurement. Off by default; process-wide; not thread-safe.
@@ -228,7 +260,8 @@ typedef enum {
   SLSTM_KERNEL_SEQUENTIAL = 6,
   SLSTM_KERNEL_NEWTON_ITERATION = 7,
   SLSTM_KERNEL_NEWTON_SOLVE = 8, /* the one-kernel fixed-count solve of the chain form */
-  SLSTM_KERNEL_KINDS = 9
+  SLSTM_KERNEL_BACKWARD = 9,     /* the adjoint and cell VJP pass of slstm_backward */
+  SLSTM_KERNEL_KINDS = 10
 } slstm_kernel_kind;
 
 slstm_status slstm_profile_enable(int on);

@@ -378,6 +378,24 @@ def backward(P, R, state0, S, g, forget, return_adjoint=False):
     return dP, dR, lam
 
 
+def branch_margin(P, R, state0, S, forget):
+    """Distance |a - i~| of every step from the tie of the running maximum m = max(a, i~), and
+    the scale |a| + |i~|, at the states S; each (B, T, d).
+
+    The state is continuous where the maximum switches branch but its derivatives are not, so
+    a backward computed in another precision agrees with this one only on lanes whose margins
+    all exceed that precision's rounding of a and i~ (the tie reading: a >= i~ takes the
+    forget branch).
+    """
+    P = np.asarray(P, dtype=np.float64)
+    R = np.asarray(R, dtype=np.float64)
+    prev = _shifted(np.asarray(S, dtype=np.float64), state0)
+    _, it, ft, _ = preactivations(prev, P, R)
+    lf, _ = log_forget(ft, forget)
+    a = lf + prev[..., M, :]
+    return np.abs(a - it), np.abs(a) + np.abs(it)
+
+
 def dense_adjoint_lane(A_lane, g_lane):
     """Dense LAPACK solve of one lane's adjoint system (tiny inputs only).
 

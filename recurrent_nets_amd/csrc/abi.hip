@@ -323,6 +323,24 @@ bool pipe_solve(Form form, int max_iters, float tol) {
   return form == Form::kChain && tol == 0.0f && max_iters <= slstm::kPipeMaxIters;
 }
 
+// control block, the chains' words, then the per-batch-row dR sums
+struct BackwardLayout {
+  size_t ctl, desc, rows, total;
+};
+
+BackwardLayout backward_layout(int B, int T, int d) {
+  BackwardLayout L;
+  L.ctl = 0;
+  L.desc = align_up(slstm::kControlBytes);
+  L.rows = align_up(L.desc + slstm::backward_desc_words(B, T, d) * 8);
+  L.total = align_up(L.rows + static_cast<size_t>(B) * 4 * d * sizeof(float));
+  return L;
+}
+
+bool backward_schedule(slstm_schedule s) {
+  return s == SLSTM_SCHEDULE_FUSED || s == SLSTM_SCHEDULE_FUSED_CHAIN;
+}
+
 }  // namespace
 
 namespace slstm {
@@ -526,6 +544,44 @@ slstm_status slstm_warm_start(const void* P, slstm_dtype P_dtype, const float* s
   HIP_TRY(slstm::launch_init_control(ctl, st));
   HIP_TRY(launch_warm(P, P_dtype == SLSTM_BF16, state0, states, B, T, d_h, fmode == SLSTM_FORGET_SIGMOID,
                       chain, at<unsigned long long>(workspace, L.desc), ctl, st));
+  return SLSTM_OK;
+}
+
+size_t slstm_backward_workspace_bytes(int B, int T, int d_h, slstm_schedule schedule) {
+  if (check_dims(B, T, d_h) != SLSTM_OK || !backward_schedule(schedule)) return 0;
+  return backward_layout(B, T, d_h).total;
+}
+
+slstm_status slstm_backward(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
+                            const float* states, const float* g_states, const float* g_h,
+                            const float* g_final, float* dP, float* dR, float* dstate0, int B,
+                            int T, int d_h, slstm_forget fmode, slstm_schedule schedule,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = '\0';
+  slstm_status s = check_common(P, P_dtype, R, state0, states, nullptr, nullptr, B, T, d_h, fmode);
+  if (s != SLSTM_OK) return s;
+  if (dP == nullptr || dR == nullptr) return fail(SLSTM_EINVAL, "dP and dR must not be NULL");
+  if (!aligned(dP, 16) || !aligned(dR, 4) || !aligned(dstate0, 4) || !aligned(g_states, 4) ||
+      !aligned(g_h, 4) || !aligned(g_final, 4))
+    return fail(SLSTM_EINVAL, "dP must be 16-byte aligned; gradients and dR, dstate0 4-byte aligned");
+  if (!known_schedule(schedule)) return fail(SLSTM_EINVAL, "unknown schedule %d", (int)schedule);
+  if (!backward_schedule(schedule))
+    return fail(SLSTM_EINVAL, "the backward pass runs as chains: schedule FUSED or FUSED_CHAIN");
+  if (workspace == nullptr || !aligned(workspace, kAlign))
+    return fail(SLSTM_EINVAL, "workspace must be non-NULL and 256-byte aligned");
+  const BackwardLayout L = backward_layout(B, T, d_h);
+  if (workspace_bytes < L.total)
+    return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Control* ctl = at<Control>(workspace, L.ctl);
+  HIP_TRY(slstm::launch_init_control(ctl, st));
+  const uint32_t ep = next_epoch();
+  HIP_TRY(timed(SLSTM_KERNEL_BACKWARD, st, [&] {
+    return slstm::launch_backward_chain(P, P_dtype == SLSTM_BF16, R, state0, states, g_states, g_h, g_final, dP,
+                                        dR, dstate0, at<float>(workspace, L.rows), B, T, d_h,
+                                        fmode == SLSTM_FORGET_SIGMOID, at<unsigned long long>(workspace, L.desc),
+                                        slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0], ep, st);
+  }));
   return SLSTM_OK;
 }
 

@@ -101,4 +101,57 @@ __device__ __forceinline__ void cell_step(const CellIn& pv, float pz, float pi, 
   }
 }
 
+// Vector-Jacobian product of one step at the state before it (pv) and its pre-activations:
+// given lam = dL/ds for the state the step produces, returns dx = dL/dx~ for the gate
+// pre-activations (z, i, f, o) (= dL/dP of the step) and lam_prev = dL/ds' = A^T lam. The
+// backward of "sLSTM in this library", section "Backward", one step of it:
+//   h = o c / n folds into the c and n adjoints: lc = lam_c + (o/n) lam_h, ln = lam_n - (h/n) lam_h,
+//   c = f' c' + i' z, n = f' n' + i':  dL/df' = lc c' + ln n',  dL/di' = lc z + ln,  dL/dz = lc i'
+//   one of (i', f') is 1 and the other e = e^{-|a - i~|} (see cell_step); with
+//   w = beta ? e dL/di' : -e dL/df', the stabiliser m = max(a, i~) gives
+//   dL/di~ = w + (1 - beta) lam_m,  dL/da = -w + beta lam_m  (a = l(f~) + m')
+//   dL/dz~ = dL/dz (1 - z^2),  dL/do~ = (c/n) lam_h o (1 - o),  dL/df~ = dL/da l'(f~)
+//   lam_prev = (lc f', ln f', dL/da, sum_x r_x dL/dx~)   (h' enters only through x~ = p + r h')
+__device__ __forceinline__ void cell_vjp(const CellIn& pv, float pz, float pi, float pf, float po,
+                                         float rz, float ri, float rf, float ro, bool sig_forget,
+                                         const float lam[4], float dx[4], float lam_prev[4]) {
+  const float zt = fmaf(rz, pv.h, pz);
+  const float it = fmaf(ri, pv.h, pi);
+  const float ft = fmaf(rf, pv.h, pf);
+  const float ot = fmaf(ro, pv.h, po);
+  const float z = tanh_fast(zt);
+  const float o = sigmoidf(ot);
+  float lf, dlf;
+  if (sig_forget) {
+    lf = log_sigmoidf(ft);
+    dlf = sigmoidf(-ft);
+  } else {
+    lf = ft;
+    dlf = 1.0f;
+  }
+  const float a = lf + pv.m;
+  const bool beta = a >= it;
+  const float e = exp_fast(-fabsf(a - it));
+  const float ig = beta ? e : 1.0f;
+  const float fg = beta ? 1.0f : e;
+  const float c = fmaf(fg, pv.c, ig * z);
+  const float n = fmaf(fg, pv.n, ig);
+  const float rn = rcp_fast(n);
+  const float cn = c * rn;
+  const float lc = fmaf(o * rn, lam[3], lam[0]);
+  const float ln = fmaf(-o * cn * rn, lam[3], lam[1]);
+  const float lfg = fmaf(lc, pv.c, ln * pv.n);
+  const float lig = fmaf(lc, z, ln);
+  const float w = beta ? e * lig : -e * lfg;
+  const float da = beta ? lam[2] - w : -w;
+  dx[0] = lc * ig * fmaf(-z, z, 1.0f);
+  dx[1] = beta ? w : w + lam[2];
+  dx[2] = da * dlf;
+  dx[3] = cn * lam[3] * fmaf(-o, o, o);
+  lam_prev[0] = lc * fg;
+  lam_prev[1] = ln * fg;
+  lam_prev[2] = da;
+  lam_prev[3] = fmaf(rz, dx[0], fmaf(ri, dx[1], fmaf(rf, dx[2], ro * dx[3])));
+}
+
 }  // namespace slstm

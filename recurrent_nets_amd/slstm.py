@@ -24,7 +24,7 @@ SCHEDULE = {"fused": 0, "layered": 1, "fused_scan": 2, "fused_chain": 3}
 MAX_ITERS = 64
 KERNELS = {"warm_start": 0, "residual_jacobian": 1, "scan_block4": 2, "update": 3,
            "final_residual": 4, "input_projection": 5, "sequential": 6, "newton_iteration": 7,
-           "newton_solve": 8}
+           "newton_solve": 8, "backward": 9}
 
 EXPORTED = [
     "slstm_status_string", "slstm_last_error", "slstm_newton_workspace_bytes",
@@ -32,7 +32,7 @@ EXPORTED = [
     "slstm_input_projection", "slstm_residual_jacobian", "slstm_scan_block4_workspace_bytes",
     "slstm_scan_block4", "slstm_warm_start_workspace_bytes", "slstm_warm_start",
     "slstm_profile_enable", "slstm_profile_reset", "slstm_profile_read",
-    "slstm_profile_durations",
+    "slstm_profile_durations", "slstm_backward_workspace_bytes", "slstm_backward",
 ]
 
 
@@ -107,6 +107,11 @@ def load(path: str | None = None):
     L.slstm_scan_block4.argtypes = [_vp, _vp, _vp, _i, _i, _i, _vp, _sz, _vp]
     L.slstm_warm_start.restype = _i
     L.slstm_warm_start.argtypes = [_vp, _i, _vp, _vp, _i, _i, _i, _i, _i, _vp, _sz, _vp]
+    L.slstm_backward_workspace_bytes.restype = _sz
+    L.slstm_backward_workspace_bytes.argtypes = [_i, _i, _i, _i]
+    L.slstm_backward.restype = _i
+    L.slstm_backward.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
+                                 _i, _i, _vp, _sz, _vp]
     L.slstm_profile_enable.restype = _i
     L.slstm_profile_enable.argtypes = [_i]
     L.slstm_profile_reset.restype = _i
@@ -322,6 +327,46 @@ def warm_start(P, state0=None, forget="exp", out=None, workspace=None, stream=No
                                 workspace.numel(), _stream(stream))
     _check(status, "slstm_warm_start")
     return out
+
+
+def backward_workspace_bytes(B: int, T: int, d_h: int, schedule: str = "fused") -> int:
+    return int(load().slstm_backward_workspace_bytes(B, T, d_h, SCHEDULE[schedule]))
+
+
+def backward(P, R, states, state0=None, g_states=None, g_h=None, g_final=None, forget="exp",
+             dP=None, dR=None, dstate0=None, want_dstate0=True, workspace=None, stream=None,
+             schedule="fused"):
+    """Gradients through the recurrence at the forward solution ``states`` (B,T,4,d_h).
+    g_states (B,T,4,d_h), g_h (B,T,d_h) and g_final (B,4,d_h) are the loss's direct gradients
+    (None: zeros). Returns (dP (B,T,4,d_h), dR (4,d_h), dstate0 (B,4,d_h) or None)."""
+    L = load()
+    _dev(P, "P", (torch.float32, torch.bfloat16))
+    _dev(R, "R", (torch.float32,))
+    _dev(state0, "state0", (torch.float32,))
+    B, T, d = _shape_check(P, R, state0)
+    for name, t, shape in (("states", states, (B, T, 4, d)), ("g_states", g_states, (B, T, 4, d)),
+                           ("g_h", g_h, (B, T, d)), ("g_final", g_final, (B, 4, d))):
+        _dev(t, name, (torch.float32,))
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {shape}, got {tuple(t.shape)}")
+    if dP is None:
+        dP = torch.empty((B, T, 4, d), dtype=torch.float32, device=P.device)
+    if dR is None:
+        dR = torch.empty((4, d), dtype=torch.float32, device=P.device)
+    if want_dstate0 and dstate0 is None:
+        dstate0 = torch.empty((B, 4, d), dtype=torch.float32, device=P.device)
+    _dev(dP, "dP", (torch.float32,))
+    _dev(dR, "dR", (torch.float32,))
+    _dev(dstate0, "dstate0", (torch.float32,))
+    need = L.slstm_backward_workspace_bytes(B, T, d, SCHEDULE[schedule])
+    if workspace is None:
+        workspace = alloc_workspace(need, P.device)
+    status = L.slstm_backward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
+                              _ptr(g_states), _ptr(g_h), _ptr(g_final), _ptr(dP), _ptr(dR),
+                              _ptr(dstate0), B, T, d, FORGET[forget], SCHEDULE[schedule],
+                              _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(status, "slstm_backward")
+    return dP, dR, dstate0
 
 
 def profile_enable(on: bool = True):

@@ -41,6 +41,31 @@ def h_rel_err(h_gpu, h_ref) -> float:
     return float(np.max(np.abs(g - r) / np.maximum(np.abs(r), H_FLOOR)))
 
 
+# Bar on the gradients of the backward pass (dP, dR, dstate0), float32 arithmetic in the kernel
+# against the float64 oracle at the same inputs: the largest error relative to the tensor's
+# largest value. The adjoint recurrence multiplies by A_t^T, whose c and n rows scale by the
+# forget gate f' <= 1, so per-step rounding (a few float32 ulps) does not grow along T; dR adds
+# B*T products in float32, about sqrt(B*T) ulps of its largest term. 1e-4 leaves a wide margin
+# over both at every workload size.
+GRAD_TOL = 1e-4
+
+
+def grad_rel_err(gpu, ref, keep=None) -> float:
+    """max |gpu - ref| / max |ref| over the elements where ``keep`` (broadcastable) is True."""
+    g = to_np(gpu)
+    r = to_np(ref)
+    assert g.shape == r.shape, (g.shape, r.shape)
+    if keep is not None:
+        keep = np.broadcast_to(keep, g.shape)
+        g, r = g[keep], r[keep]
+    if g.size == 0:
+        return 0.0
+    if not np.all(np.isfinite(g)):
+        return float("inf")
+    scale = float(np.max(np.abs(r)))
+    return float(np.max(np.abs(g - r))) / max(scale, 1e-30)
+
+
 def lanes_to_btd(S_lanes, lane_b, lane_j, B, d):
     """(n, T, 4) per-lane oracle states -> dict keyed by (b, j)."""
     return {(int(b), int(j)): S_lanes[k] for k, (b, j) in enumerate(zip(lane_b, lane_j))}

@@ -103,3 +103,23 @@ def random_scan_operands(seed: int, B: int, T: int, d: int, scale: float = 0.45)
     A = rng.uniform(-scale, scale, size=(B, T, 4, 4, d))
     r = rng.standard_normal((B, T, 4, d))
     return A, r
+
+
+def random_cotangents(seed: int, B: int, T: int, d: int):
+    """Direct loss gradients for a backward pass, each ~ N(0, 1) in float32: with respect to
+    the states (B, T, 4, d), the hidden states (B, T, d) and the final state (B, 4, d)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    g_states = rng.standard_normal((B, T, 4, d)).astype(np.float32)
+    g_h = rng.standard_normal((B, T, d)).astype(np.float32)
+    g_final = rng.standard_normal((B, 4, d)).astype(np.float32)
+    return g_states, g_h, g_final
+
+
+def random_cotangents_device(seed: int, B: int, T: int, d: int, device):
+    """random_cotangents' distributions drawn on ``device`` by torch's seeded generator."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    g_states = torch.randn((B, T, 4, d), generator=gen, device=device)
+    g_h = torch.randn((B, T, d), generator=gen, device=device)
+    g_final = torch.randn((B, 4, d), generator=gen, device=device)
+    return g_states, g_h, g_final
