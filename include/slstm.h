@@ -232,9 +232,10 @@ size_t slstm_backward_workspace_bytes(int B, int T, int d_h, slstm_schedule sche
  *   dR (4, d_h) f32, written: dL/dR = sum over b, t of dP[b, t, g, j] * h_{t-1}[b, j], with
  *     h_0 taken from state0.
  *   dstate0 (B, 4, d_h) f32 or NULL, written: dL/d state0 (at the zero state if state0 is NULL).
- * schedule: SLSTM_SCHEDULE_FUSED and SLSTM_SCHEDULE_FUSED_CHAIN run one kernel of tile-serial
- * reverse chains along T (and a fixed-order sum of dR over the batch); other values are
- * rejected. The workspace (slstm_backward_workspace_bytes, 256-byte aligned) is the caller's;
+ * schedule: SLSTM_SCHEDULE_FUSED and SLSTM_SCHEDULE_FUSED_SCAN run one kernel that scans the
+ * maps y -> A_t^T (g_t + y) along T with a look-back across tiles (parallel along T at any
+ * batch size); SLSTM_SCHEDULE_FUSED_CHAIN runs tile-serial reverse chains instead;
+ * SLSTM_SCHEDULE_LAYERED is rejected. Two small kernels then sum dR in a fixed order. The workspace (slstm_backward_workspace_bytes, 256-byte aligned) is the caller's;
  * results are bitwise reproducible. Negative status: nothing valid was written. Outputs must
  * not alias inputs.
  */

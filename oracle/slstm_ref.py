@@ -380,7 +380,8 @@ def backward(P, R, state0, S, g, forget, return_adjoint=False):
 
 def branch_margin(P, R, state0, S, forget):
     """Distance |a - i~| of every step from the tie of the running maximum m = max(a, i~), and
-    the scale |a| + |i~|, at the states S; each (B, T, d).
+    the scale |l| + |m'| + |i~| of the operands that form it (a = l + m'), at the states S;
+    each (B, T, d).
 
     The state is continuous where the maximum switches branch but its derivatives are not, so
     a backward computed in another precision agrees with this one only on lanes whose margins
@@ -393,7 +394,7 @@ def branch_margin(P, R, state0, S, forget):
     _, it, ft, _ = preactivations(prev, P, R)
     lf, _ = log_forget(ft, forget)
     a = lf + prev[..., M, :]
-    return np.abs(a - it), np.abs(a) + np.abs(it)
+    return np.abs(a - it), np.abs(lf) + np.abs(prev[..., M, :]) + np.abs(it)
 
 
 def dense_adjoint_lane(A_lane, g_lane):

@@ -323,22 +323,30 @@ bool pipe_solve(Form form, int max_iters, float tol) {
   return form == Form::kChain && tol == 0.0f && max_iters <= slstm::kPipeMaxIters;
 }
 
-// control block, the chains' words, then the per-batch-row dR sums
+// control block, the look-back words, then the dR rows and their chunk sums
 struct BackwardLayout {
   size_t ctl, desc, rows, total;
 };
 
-BackwardLayout backward_layout(int B, int T, int d) {
+bool backward_schedule(slstm_schedule s) {
+  return s == SLSTM_SCHEDULE_FUSED || s == SLSTM_SCHEDULE_FUSED_SCAN || s == SLSTM_SCHEDULE_FUSED_CHAIN;
+}
+
+// The backward's scan form measured at least as fast as its chains at every shape tried on
+// MI355X (B = 128 with 512 lane groups included): one VJP pass per step costs about as much as
+// the chain's, and the look-back words shrink to the anchors' values when the lane groups
+// cover the GPU. Chains on request only.
+bool backward_scan_form(int /*B*/, int /*d*/, slstm_schedule s) {
+  return s != SLSTM_SCHEDULE_FUSED_CHAIN;
+}
+
+BackwardLayout backward_layout(int B, int T, int d, bool scan) {
   BackwardLayout L;
   L.ctl = 0;
   L.desc = align_up(slstm::kControlBytes);
-  L.rows = align_up(L.desc + slstm::backward_desc_words(B, T, d) * 8);
-  L.total = align_up(L.rows + static_cast<size_t>(B) * 4 * d * sizeof(float));
+  L.rows = align_up(L.desc + slstm::backward_desc_words(B, T, d, scan) * 8);
+  L.total = align_up(L.rows + slstm::backward_row_floats(B, T, d, scan) * sizeof(float));
   return L;
-}
-
-bool backward_schedule(slstm_schedule s) {
-  return s == SLSTM_SCHEDULE_FUSED || s == SLSTM_SCHEDULE_FUSED_CHAIN;
 }
 
 }  // namespace
@@ -549,7 +557,7 @@ slstm_status slstm_warm_start(const void* P, slstm_dtype P_dtype, const float* s
 
 size_t slstm_backward_workspace_bytes(int B, int T, int d_h, slstm_schedule schedule) {
   if (check_dims(B, T, d_h) != SLSTM_OK || !backward_schedule(schedule)) return 0;
-  return backward_layout(B, T, d_h).total;
+  return backward_layout(B, T, d_h, backward_scan_form(B, d_h, schedule)).total;
 }
 
 slstm_status slstm_backward(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
@@ -566,10 +574,11 @@ slstm_status slstm_backward(const void* P, slstm_dtype P_dtype, const float* R, 
     return fail(SLSTM_EINVAL, "dP must be 16-byte aligned; gradients and dR, dstate0 4-byte aligned");
   if (!known_schedule(schedule)) return fail(SLSTM_EINVAL, "unknown schedule %d", (int)schedule);
   if (!backward_schedule(schedule))
-    return fail(SLSTM_EINVAL, "the backward pass runs as chains: schedule FUSED or FUSED_CHAIN");
+    return fail(SLSTM_EINVAL, "the backward pass has fused forms only: schedule FUSED, FUSED_SCAN or FUSED_CHAIN");
   if (workspace == nullptr || !aligned(workspace, kAlign))
     return fail(SLSTM_EINVAL, "workspace must be non-NULL and 256-byte aligned");
-  const BackwardLayout L = backward_layout(B, T, d_h);
+  const bool scan = backward_scan_form(B, d_h, schedule);
+  const BackwardLayout L = backward_layout(B, T, d_h, scan);
   if (workspace_bytes < L.total)
     return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -577,10 +586,10 @@ slstm_status slstm_backward(const void* P, slstm_dtype P_dtype, const float* R, 
   HIP_TRY(slstm::launch_init_control(ctl, st));
   const uint32_t ep = next_epoch();
   HIP_TRY(timed(SLSTM_KERNEL_BACKWARD, st, [&] {
-    return slstm::launch_backward_chain(P, P_dtype == SLSTM_BF16, R, state0, states, g_states, g_h, g_final, dP,
-                                        dR, dstate0, at<float>(workspace, L.rows), B, T, d_h,
-                                        fmode == SLSTM_FORGET_SIGMOID, at<unsigned long long>(workspace, L.desc),
-                                        slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0], ep, st);
+    return slstm::launch_backward(P, P_dtype == SLSTM_BF16, R, state0, states, g_states, g_h, g_final, dP, dR,
+                                  dstate0, at<float>(workspace, L.rows), B, T, d_h,
+                                  fmode == SLSTM_FORGET_SIGMOID, scan, at<unsigned long long>(workspace, L.desc),
+                                  slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0], ep, st);
   }));
   return SLSTM_OK;
 }

@@ -1,20 +1,31 @@
 // Backward of the forward recurrence s_t = f(s_{t-1}, P_t) ("sLSTM in this library", section
-// "Backward": one reverse pass of the transposed Jacobians, then the cell's vector-Jacobian
-// product for the gradients of R and W_x), chain form.
+// "Backward": the adjoint is one reverse scan of the transposed Jacobians, then the cell's
+// vector-Jacobian product gives the gradients of R and W_x).
 //
 // Per lane (b, j), with g_t the direct gradient of the loss with respect to the state s_t:
 //   lam_{T-1} = g_{T-1} (+ the gradient of the final state),  lam_t = g_t + A_{t+1}^T lam_{t+1}
 //   dP_t = G_t^T lam_t,  dR = sum over b and t of dP_t * h_{t-1},  dstate0 = A_0^T lam_0
 // (A_t = d s_t / d s_{t-1}, G_t = d s_t / d x~_t; cell_vjp forms both products at once from
-// the stored state before the step.)
+// the stored state before the step.) The value y_t = A_t^T lam_t handed from step t to step
+// t-1 obeys the affine recurrence y_{t-1} = A_t^T (g_t + y_t), run from t = T-1 down to 0.
 //
-// A thread owns one feature and kBackSteps consecutive steps and runs them from the last to the
-// first; the adjoint entering its tile from the tile after it (A^T lam of that tile's first
-// step) and the running sum of the tile's dR contributions come as epoch-tagged words (see
-// tag_store). Tiles take tickets from the last tile along T to the first, so the tile a tile
-// waits on holds an earlier ticket of the same counter and runs. The first tile along T holds
-// the lane's dR over all of T; it writes it per batch row, and a second kernel sums the batch
-// rows in a fixed order. Every value is formed in one fixed order: bitwise reproducible.
+// Two layouts, as for the forward solve:
+// * chains: a thread owns one feature and kBackSteps consecutive steps and runs them from the
+//   last to the first; y entering its tile (from the tile after it) and the running sum of the
+//   lane's dR contributions come as epoch-tagged words (see tag_store). Tiles take tickets
+//   from the last tile along T to the first, so the tile a tile waits on holds an earlier
+//   ticket of the same counter and runs. The first tile along T holds the lane's dR over all
+//   of T and writes it per batch row. No waiting once the lane groups cover the GPU.
+// * scan: the four threads of a quad hold four consecutive sub-chunks of one feature (the
+//   last in time first), compose their steps' maps y -> A_t^T (g_t + y) into one affine map,
+//   scan the maps across the quad and look back across tiles (quad_look_back, tiles in reverse
+//   order of time), then run their steps again from the y entering them. Parallel along T for
+//   few lane groups; each tile writes its dR contributions per batch row and tile.
+// The per-row dR sums are added in a fixed order by two small kernels. Every value is formed
+// in one fixed order: bitwise reproducible.
+#include <algorithm>
+
+#include "affine4.h"
 #include "cell.h"
 #include "kernels.h"
 
@@ -172,57 +183,299 @@ __global__ __launch_bounds__(kBackBlock, SLSTM_BACK_MIN_WAVES) void backward_cha
   }
 }
 
-// dR[g, j] = sum over batch rows b of dR_rows[b, g, j], in order of b
-__global__ __launch_bounds__(256) void sum_rows_kernel(const float* __restrict__ rows, float* __restrict__ out,
-                                                       int B, int n) {
+// ---- scan form ------------------------------------------------------------------------------
+#ifndef SLSTM_BACK_SCAN_TSUB
+#define SLSTM_BACK_SCAN_TSUB 4
+#endif
+#ifndef SLSTM_BACK_SCAN_MIN_WAVES
+#define SLSTM_BACK_SCAN_MIN_WAVES 3
+#endif
+constexpr int kBackScanBlock = 256;  // 4 waves x 16 features x 4 sub-chunks
+constexpr int kBackScanTSub = SLSTM_BACK_SCAN_TSUB;
+
+template <bool BF16, bool SIG, int TSUB>
+__global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void backward_scan_kernel(
+    const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
+    const float* __restrict__ S, const float* __restrict__ g, const float* __restrict__ g_h,
+    const float* __restrict__ g_final, float* __restrict__ dP, float* __restrict__ dstate0,
+    float* __restrict__ dR_rows, int T, int d, int n_jt, int n_lg, int n_tt, int anchor_stride,
+    unsigned long long* __restrict__ desc, unsigned int* __restrict__ tickets, int n_ctr,
+    uint32_t epoch) {
+  constexpr bool sig = SIG;
+  __shared__ int s_tile[2];
+  const int tid = threadIdx.x;
+  if (tid == 0) take_ticket(tickets, n_ctr, n_lg, n_tt, s_tile[0], s_tile[1]);
+  __syncthreads();
+  // tickets (and the look-back) run from the last tile along T to the first
+  const int tr = __builtin_amdgcn_readfirstlane(s_tile[0]);
+  const int lg = __builtin_amdgcn_readfirstlane(s_tile[1]);
+  const int tt = n_tt - 1 - tr;
+  const int b = lg / n_jt;
+  const int jt = lg - b * n_jt;
+
+  // quad position q holds sub-chunk 3 - q: the quad scans in reverse order of time
+  const int l = tid & 63;
+  const int q = l & 3;
+  const int sc = 3 - q;
+  const int lane_in_tile = (tid >> 6) * 16 + (l >> 2);
+  const unsigned ud = static_cast<unsigned>(d);
+  const unsigned j = static_cast<unsigned>(jt * 64 + lane_in_tile);
+  const bool valid = j < ud;
+  const int t_tile = tt * 4 * TSUB;
+  const int t_start = t_tile + sc * TSUB;
+  const i64 n_lanes_pad = static_cast<i64>(n_lg) * 64;
+  const i64 my_lane = static_cast<i64>(lg) * 64 + lane_in_tile;
+  const i64 tile_row = (static_cast<i64>(b) * T + t_tile) * 4 * static_cast<i64>(d);
+  const rsrc_t rsP = make_rsrc(static_cast<const char*>(P) + tile_row * (BF16 ? 2 : 4));
+  const rsrc_t rsS = make_rsrc(S + tile_row);
+  const rsrc_t rsD = make_rsrc(dP + tile_row);
+  const unsigned lane_off = static_cast<unsigned>(sc * TSUB) * 4u * ud + j;  // elements
+
+  const unsigned long long pf = quad_look_back_prefetch(desc, n_lanes_pad, my_lane, q, tr, anchor_stride);
+
+  float pg[TSUB][4], sv[TSUB][4], gs[TSUB][4];
+#pragma unroll
+  for (int u = 0; u < TSUB; ++u) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      pg[u][k] = 0.0f;
+      sv[u][k] = 0.0f;
+      gs[u][k] = 0.0f;
+    }
+    const int t = t_start + u;
+    if (valid && t < T) {
+      const unsigned o = lane_off + u * 4u * ud;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        pg[u][k] = buf_ld_p<BF16>(rsP, o, k * ud);
+        sv[u][k] = buf_ld(rsS, 4u * o, 4u * k * ud);
+      }
+      const i64 row = static_cast<i64>(b) * T + t;
+      if (g != nullptr) {
+        const float* gr = g + row * 4 * static_cast<i64>(d);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) gs[u][k] = gr[k * ud + j];
+      }
+      if (g_h != nullptr) gs[u][3] += g_h[row * static_cast<i64>(d) + j];
+      if (g_final != nullptr && t == T - 1) {
+        const float* gf = g_final + static_cast<i64>(b) * 4 * static_cast<i64>(d);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) gs[u][k] += gf[k * ud + j];
+      }
+    }
+  }
+  float rz = 0.0f, ri = 0.0f, rf = 0.0f, ro = 0.0f;
+  // the state before the sub-chunk: the last step of the sub-chunk before it in time (held by
+  // the next thread of the quad), the step before the tile, or the initial state
+  CellIn pv0 = {quad_perm<1, 2, 3, 3>(sv[TSUB - 1][0]), quad_perm<1, 2, 3, 3>(sv[TSUB - 1][1]),
+                quad_perm<1, 2, 3, 3>(sv[TSUB - 1][2]), quad_perm<1, 2, 3, 3>(sv[TSUB - 1][3])};
+  if (valid) {
+    rz = R[j];
+    ri = R[ud + j];
+    rf = R[2 * ud + j];
+    ro = R[3 * ud + j];
+    if (sc == 0) {
+      if (t_start == 0) {
+        pv0 = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (state0 != nullptr) {
+          const float* s0 = state0 + static_cast<i64>(b) * 4 * static_cast<i64>(d);
+          pv0 = {s0[j], s0[ud + j], s0[2 * ud + j], s0[3 * ud + j]};
+        }
+      } else if (t_start < T) {
+        const float* sp = S + (static_cast<i64>(b) * T + t_start - 1) * 4 * static_cast<i64>(d);
+        pv0 = {sp[j], sp[ud + j], sp[2 * ud + j], sp[3 * ud + j]};
+      }
+    }
+  }
+
+  // ---- the sub-chunk's map y -> (M y + v), its steps composed from the last to the first ----
+  float M[16], v[4];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) M[e] = (e % 5 == 0) ? 1.0f : 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] = 0.0f;
+#pragma unroll
+  for (int u = TSUB - 1; u >= 0; --u) {
+    const int t = t_start + u;
+    if (valid && t < T) {
+      const CellIn pv = (u == 0) ? pv0 : CellIn{sv[u - 1][0], sv[u - 1][1], sv[u - 1][2], sv[u - 1][3]};
+      float f[4], A[16], At[16];
+      cell_step<true>(pv, pg[u][0], pg[u][1], pg[u][2], pg[u][3], rz, ri, rf, ro, sig, f, A);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) At[4 * r + c] = A[4 * c + r];
+      // (M, v) <- (A^T M, A^T (v + g_t))
+      const float w[4] = {v[0] + gs[u][0], v[1] + gs[u][1], v[2] + gs[u][2], v[3] + gs[u][3]};
+      const float zero[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      mat4_vec(At, w, zero, v);
+      mat4_mul_left(At, M);
+    }
+  }
+
+  // ---- quad scan of the sub-chunk maps, then the look-back across tiles ----
+  quad_inclusive_scan(M, v, q);
+  float carry[4];
+  {
+    float arow[4], av;
+    quad_row_of_last(M, v, q, arow, av);
+    quad_look_back(arow, av, carry, desc, n_lanes_pad, my_lane, q, tr, anchor_stride, epoch, pf);
+  }
+  // y entering the sub-chunk: the inclusive value of the thread before in the quad
+  float y[4];
+  {
+    float xe[4];
+    mat4_vec(M, carry, v, xe);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y[e] = quad_perm<0, 0, 1, 2>(xe[e]);
+      if (q == 0) y[e] = carry[e];
+    }
+  }
+
+  // ---- the steps again, from the last to the first, with the adjoint ----
+  float dr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int u = TSUB - 1; u >= 0; --u) {
+    const int t = t_start + u;
+    if (valid && t < T) {
+      const CellIn pv = (u == 0) ? pv0 : CellIn{sv[u - 1][0], sv[u - 1][1], sv[u - 1][2], sv[u - 1][3]};
+      float lam[4], dx[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) lam[e] = gs[u][e] + y[e];
+      cell_vjp(pv, pg[u][0], pg[u][1], pg[u][2], pg[u][3], rz, ri, rf, ro, sig, lam, dx, y);
+      const unsigned o = lane_off + u * 4u * ud;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        buf_st(dx[e], rsD, 4u * o, 4u * e * ud);
+        dr[e] = fmaf(dx[e], pv.h, dr[e]);
+      }
+    }
+  }
+  // the tile's dR over the quad, summed in order of time (sub-chunks 3, 2, 1, 0 = q 0..3)
+  float tot[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e)
+    tot[e] = ((quad_bcast<0>(dr[e]) + quad_bcast<1>(dr[e])) + quad_bcast<2>(dr[e])) + quad_bcast<3>(dr[e]);
+  if (valid && q == 0) {
+    float* rows = dR_rows + (static_cast<i64>(b) * n_tt + tt) * 4 * static_cast<i64>(d);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) rows[e * ud + j] = tot[e];
+  }
+  if (valid && t_start == 0 && dstate0 != nullptr) {
+    float* ds = dstate0 + static_cast<i64>(b) * 4 * static_cast<i64>(d);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) ds[e * ud + j] = y[e];
+  }
+}
+
+// ---- fixed-order sum of the dR rows -------------------------------------------------------------
+// rows summed per thread in the first level: at least 32, and at most 4096 chunks
+static i64 row_chunk(i64 rows) { return std::max<i64>(32, (rows + 4095) / 4096); }
+
+// part[c, i] = sum of rows[r, i] over the rows r of chunk c, in order of r
+__global__ __launch_bounds__(256) void sum_row_chunks_kernel(const float* __restrict__ rows,
+                                                             float* __restrict__ part, int n_rows,
+                                                             int chunk, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int r0 = blockIdx.y * chunk;
+  const int r1 = min(r0 + chunk, n_rows);
+  float acc = 0.0f;
+  for (int r = r0; r < r1; ++r) acc += rows[static_cast<i64>(r) * n + i];
+  part[static_cast<i64>(blockIdx.y) * n + i] = acc;
+}
+
+// out[i] = sum of part[c, i] over the chunks c, in order of c
+__global__ __launch_bounds__(256) void sum_chunks_kernel(const float* __restrict__ part,
+                                                         float* __restrict__ out, int n_chunks, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   float acc = 0.0f;
-  for (int b = 0; b < B; ++b) acc += rows[static_cast<i64>(b) * n + i];
+  for (int c = 0; c < n_chunks; ++c) acc += part[static_cast<i64>(c) * n + i];
   out[i] = acc;
 }
 
-static void back_grid(int B, int T, int d, i64& n_jt, i64& n_lg, i64& n_tt) {
-  n_jt = (d + kBackBlock - 1) / kBackBlock;
-  n_lg = static_cast<i64>(B) * n_jt;
-  n_tt = (T + kBackSteps - 1) / kBackSteps;
-}
+// ---- sizes and launch ---------------------------------------------------------------------------
+struct BackGrid {
+  i64 n_jt, n_lg, n_tt, rows;
+};
 
-size_t backward_desc_words(int B, int T, int d) {
-  i64 n_jt, n_lg, n_tt;
-  back_grid(B, T, d, n_jt, n_lg, n_tt);
-  return static_cast<size_t>(n_tt * kBackWords * n_lg * kBackBlock);
-}
-
-hipError_t launch_backward_chain(const void* P, bool p_bf16, const float* R, const float* state0,
-                                 const float* S, const float* g, const float* g_h,
-                                 const float* g_final, float* dP, float* dR, float* dstate0,
-                                 float* dR_rows, int B, int T, int d, bool sig_forget,
-                                 unsigned long long* carry, unsigned int* tickets, uint32_t epoch,
-                                 hipStream_t stream) {
-  i64 n_jt, n_lg, n_tt;
-  back_grid(B, T, d, n_jt, n_lg, n_tt);
-  const i64 blocks = n_lg * n_tt;
-  if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  const int n_ctr = ticket_counters(n_lg);
-  const dim3 grid(static_cast<unsigned>(blocks));
-  const int a = static_cast<int>(n_jt), c = static_cast<int>(n_lg), e = static_cast<int>(n_tt);
-#define SLSTM_BACK_LAUNCH(BF, SG)                                                                         \
-  backward_chain_kernel<BF, SG><<<grid, kBackBlock, 0, stream>>>(P, R, state0, S, g, g_h, g_final, dP,    \
-                                                                 dstate0, dR_rows, T, d, a, c, e, carry, \
-                                                                 tickets, n_ctr, epoch)
-  if (p_bf16) {
-    if (sig_forget) SLSTM_BACK_LAUNCH(true, true);
-    else SLSTM_BACK_LAUNCH(true, false);
+static BackGrid back_grid(int B, int T, int d, bool scan) {
+  BackGrid g;
+  if (scan) {
+    g.n_jt = (d + 63) / 64;
+    g.n_tt = (T + 4 * kBackScanTSub - 1) / (4 * kBackScanTSub);
+    g.rows = static_cast<i64>(B) * g.n_tt;
   } else {
-    if (sig_forget) SLSTM_BACK_LAUNCH(false, true);
-    else SLSTM_BACK_LAUNCH(false, false);
+    g.n_jt = (d + kBackBlock - 1) / kBackBlock;
+    g.n_tt = (T + kBackSteps - 1) / kBackSteps;
+    g.rows = B;
   }
+  g.n_lg = static_cast<i64>(B) * g.n_jt;
+  return g;
+}
+
+size_t backward_desc_words(int B, int T, int d, bool scan) {
+  const BackGrid g = back_grid(B, T, d, scan);
+  return static_cast<size_t>(scan ? g.n_tt * kLookBackWords * g.n_lg * 64 : g.n_tt * kBackWords * g.n_lg * kBackBlock);
+}
+
+size_t backward_row_floats(int B, int T, int d, bool scan) {
+  const BackGrid g = back_grid(B, T, d, scan);
+  const i64 chunk = row_chunk(g.rows);
+  const i64 chunks = (g.rows + chunk - 1) / chunk;
+  return static_cast<size_t>((g.rows + chunks) * 4 * static_cast<i64>(d));
+}
+
+hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const float* state0,
+                           const float* S, const float* g, const float* g_h, const float* g_final,
+                           float* dP, float* dR, float* dstate0, float* rows, int B, int T, int d,
+                           bool sig_forget, bool scan, unsigned long long* desc,
+                           unsigned int* tickets, uint32_t epoch, hipStream_t stream) {
+  const BackGrid gr = back_grid(B, T, d, scan);
+  const i64 blocks = gr.n_lg * gr.n_tt;
+  const i64 chunk = row_chunk(gr.rows);
+  const i64 chunks = (gr.rows + chunk - 1) / chunk;
+  if (blocks > 0x7fffffffLL || gr.rows > 0x7fffffffLL) return hipErrorInvalidValue;
+  const int n_ctr = ticket_counters(gr.n_lg);
+  const dim3 grid(static_cast<unsigned>(blocks));
+  const int a = static_cast<int>(gr.n_jt), c = static_cast<int>(gr.n_lg), e = static_cast<int>(gr.n_tt);
+  if (scan) {
+    const int stride = look_back_anchor_stride(gr.n_lg, SLSTM_BACK_SCAN_MIN_WAVES);
+#define SLSTM_BACK_LAUNCH(BF, SG)                                                                                  \
+  backward_scan_kernel<BF, SG, kBackScanTSub><<<grid, kBackScanBlock, 0, stream>>>(                                \
+      P, R, state0, S, g, g_h, g_final, dP, dstate0, rows, T, d, a, c, e, stride, desc, tickets, n_ctr, epoch)
+    if (p_bf16) {
+      if (sig_forget) SLSTM_BACK_LAUNCH(true, true);
+      else SLSTM_BACK_LAUNCH(true, false);
+    } else {
+      if (sig_forget) SLSTM_BACK_LAUNCH(false, true);
+      else SLSTM_BACK_LAUNCH(false, false);
+    }
 #undef SLSTM_BACK_LAUNCH
+  } else {
+#define SLSTM_BACK_LAUNCH(BF, SG)                                                                                  \
+  backward_chain_kernel<BF, SG><<<grid, kBackBlock, 0, stream>>>(P, R, state0, S, g, g_h, g_final, dP, dstate0, \
+                                                                 rows, T, d, a, c, e, desc, tickets, n_ctr, epoch)
+    if (p_bf16) {
+      if (sig_forget) SLSTM_BACK_LAUNCH(true, true);
+      else SLSTM_BACK_LAUNCH(true, false);
+    } else {
+      if (sig_forget) SLSTM_BACK_LAUNCH(false, true);
+      else SLSTM_BACK_LAUNCH(false, false);
+    }
+#undef SLSTM_BACK_LAUNCH
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int n = 4 * d;
-  sum_rows_kernel<<<(n + 255) / 256, 256, 0, stream>>>(dR_rows, dR, B, n);
+  float* part = rows + gr.rows * n;
+  sum_row_chunks_kernel<<<dim3((n + 255) / 256, static_cast<unsigned>(chunks)), 256, 0, stream>>>(
+      rows, part, static_cast<int>(gr.rows), static_cast<int>(chunk), n);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  sum_chunks_kernel<<<(n + 255) / 256, 256, 0, stream>>>(part, dR, static_cast<int>(chunks), n);
   return hipGetLastError();
 }
 

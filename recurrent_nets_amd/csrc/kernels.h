@@ -70,15 +70,15 @@ hipError_t launch_warm_chain(const void* P, bool p_bf16, const float* state0, fl
                              int T, int d, bool sig_forget, unsigned long long* carry,
                              unsigned int* tickets, uint32_t epoch, hipStream_t stream);
 
-// backward chains (adjoint + cell VJP, tiles from the last along T to the first), then the
-// fixed-order batch sum of dR from dR_rows (B, 4, d)
-size_t backward_desc_words(int B, int T, int d);
-hipError_t launch_backward_chain(const void* P, bool p_bf16, const float* R, const float* state0,
-                                 const float* S, const float* g, const float* g_h,
-                                 const float* g_final, float* dP, float* dR, float* dstate0,
-                                 float* dR_rows, int B, int T, int d, bool sig_forget,
-                                 unsigned long long* carry, unsigned int* tickets, uint32_t epoch,
-                                 hipStream_t stream);
+// backward (adjoint + cell VJP) as chains or as a scan along T, then the fixed-order sum of
+// dR over its rows; rows holds backward_row_floats floats
+size_t backward_desc_words(int B, int T, int d, bool scan);
+size_t backward_row_floats(int B, int T, int d, bool scan);
+hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const float* state0,
+                           const float* S, const float* g, const float* g_h, const float* g_final,
+                           float* dP, float* dR, float* dstate0, float* rows, int B, int T, int d,
+                           bool sig_forget, bool scan, unsigned long long* desc,
+                           unsigned int* tickets, uint32_t epoch, hipStream_t stream);
 
 hipError_t launch_update(float* S, const float* D, i64 n_floats, Control* ctl, int k_iter,
                          hipStream_t stream);

@@ -17,8 +17,8 @@ from workloads import by_name, draw_preactivation_inputs, random_cotangents, ran
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-# a lane is decided when |a - i~| > MARGIN * (1 + |a| + |i~|) at every step: float32 forms a
-# and i~ to about 4e-7 of that scale
+# a lane is decided when |a - i~| > MARGIN * (1 + |l| + |m'| + |i~|) at every step: float32
+# forms a = l + m' and i~ to within a few units in the last place (1.2e-7) of that scale
 MARGIN = 1e-5
 
 
@@ -90,29 +90,35 @@ def _compare(P, R, s0, S, forget, got, want, tol=GRAD_TOL, max_undecided=0.05):
 SHAPES = [(1, 1, 1), (2, 64, 16), (3, 33, 65), (2, 257, 20), (1, 70, 300), (4, 9, 256)]
 
 
+@pytest.fixture(params=["fused_scan", "fused_chain"])
+def schedule(request):
+    """Both kernel forms of the backward must meet the same bar."""
+    return request.param
+
+
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("forget", ["exp", "sigmoid"])
 @pytest.mark.parametrize("p_dtype", ["f32", "bf16"])
-def test_backward_matches_oracle(gpu_lib, shape, forget, p_dtype):
+def test_backward_matches_oracle(gpu_lib, shape, forget, p_dtype, schedule):
     B, T, d = shape
-    case(f"backward B={B} T={T} d={d} {forget} P {p_dtype}")
+    case(f"backward {schedule} B={B} T={T} d={d} {forget} P {p_dtype}")
     P, R, s0, S = _problem(B * 7919 + T * 31 + d, B, T, d, forget, p_dtype, with_state0=True)
     gs, gh, gf = (torch.from_numpy(a) for a in random_cotangents(B + T + d, B, T, d))
-    got = _gpu(gpu_lib, P, R, s0, S, gs, gh, gf, forget)
+    got = _gpu(gpu_lib, P, R, s0, S, gs, gh, gf, forget, schedule=schedule)
     want = _oracle(P, R, s0, S, gs, gh, gf, forget)
     _compare(P, R, s0, S, forget, got, want)
 
 
 @pytest.mark.parametrize("which", ["states", "h", "final", "none"])
-def test_backward_optional_gradients(gpu_lib, which):
+def test_backward_optional_gradients(gpu_lib, which, schedule):
     B, T, d = 2, 40, 48
-    case(f"backward with only the {which} gradient")
+    case(f"backward {schedule} with only the {which} gradient")
     P, R, s0, S = _problem(5, B, T, d, "exp", "f32", with_state0=False)
     gs, gh, gf = (torch.from_numpy(a) for a in random_cotangents(6, B, T, d))
     gs = gs if which == "states" else None
     gh = gh if which == "h" else None
     gf = gf if which == "final" else None
-    got = _gpu(gpu_lib, P, R, None, S, gs, gh, gf, "exp")
+    got = _gpu(gpu_lib, P, R, None, S, gs, gh, gf, "exp", schedule=schedule)
     if which == "none":
         assert all(bool((t == 0).all()) for t in got)
         return
@@ -131,28 +137,52 @@ def test_backward_without_dstate0(gpu_lib):
     assert torch.equal(dP, dP2) and torch.equal(dR, dR2)
 
 
-def test_backward_bitwise_reproducible(gpu_lib):
+def test_backward_bitwise_reproducible(gpu_lib, schedule):
     B, T, d = 16, 300, 512
-    case(f"backward reproducibility B={B} T={T} d={d}")
+    case(f"backward {schedule} reproducibility B={B} T={T} d={d}")
     P, R, s0, S = _problem(11, B, T, d, "exp", "f32", with_state0=True)
     gs, gh, gf = (torch.from_numpy(a) for a in random_cotangents(12, B, T, d))
-    ws = gpu_lib.alloc_workspace(gpu_lib.backward_workspace_bytes(B, T, d))
-    a = _gpu(gpu_lib, P, R, s0, S, gs, gh, gf, "exp", workspace=ws)
-    b = _gpu(gpu_lib, P, R, s0, S, gs, gh, gf, "exp", workspace=ws)
-    c = _gpu(gpu_lib, P, R, s0, S, gs, gh, gf, "exp")
+    ws = gpu_lib.alloc_workspace(gpu_lib.backward_workspace_bytes(B, T, d, schedule))
+    a = _gpu(gpu_lib, P, R, s0, S, gs, gh, gf, "exp", workspace=ws, schedule=schedule)
+    b = _gpu(gpu_lib, P, R, s0, S, gs, gh, gf, "exp", workspace=ws, schedule=schedule)
+    c = _gpu(gpu_lib, P, R, s0, S, gs, gh, gf, "exp", schedule=schedule)
     for x, y, z in zip(a, b, c):
         assert torch.equal(x, y) and torch.equal(x, z)
 
 
-def test_backward_mid_workload_full_size(gpu_lib):
+def test_backward_forms_agree(gpu_lib):
+    """The two forms order their float32 sums differently but agree to rounding."""
+    B, T, d = 3, 200, 96
+    case(f"backward forms agree B={B} T={T} d={d}")
+    P, R, s0, S = _problem(13, B, T, d, "sigmoid", "f32", with_state0=True)
+    gs, gh, gf = (torch.from_numpy(a) for a in random_cotangents(14, B, T, d))
+    a = _gpu(gpu_lib, P, R, s0, S, gs, gh, gf, "sigmoid", schedule="fused_scan")
+    b = _gpu(gpu_lib, P, R, s0, S, gs, gh, gf, "sigmoid", schedule="fused_chain")
+    for x, y in zip(a, b):
+        assert grad_rel_err(x, y) < 1e-5
+
+
+def test_backward_fused_picks_a_form(gpu_lib):
+    B, T, d = 2, 64, 128
+    P, R, s0, S = _problem(15, B, T, d, "exp", "f32", with_state0=False)
+    gs, gh, gf = (torch.from_numpy(a) for a in random_cotangents(16, B, T, d))
+    a = _gpu(gpu_lib, P, R, None, S, gs, gh, gf, "exp", schedule="fused")
+    # the default form of the backward is the scan
+    b = _gpu(gpu_lib, P, R, None, S, gs, gh, gf, "exp", schedule="fused_scan")
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
+
+
+@pytest.mark.parametrize("sched", ["fused_scan", "fused_chain"])
+def test_backward_mid_workload_full_size(gpu_lib, sched):
     """The mid workload (B=8, T=1024, d=256) at its full size on its own trajectory."""
     w = by_name("mid_b8_t1024_d256")
-    case(f"backward {w.name} full size")
+    case(f"backward {sched} {w.name} full size")
     inp = draw_preactivation_inputs(w)
     P, R = inp["P"], inp["R"]
     S = torch.from_numpy(ref.sequential(to_np(P), to_np(R), None, w.forget).astype(np.float32))
     gs, gh, gf = (torch.from_numpy(a) for a in random_cotangents(w.seed + 7, w.B, w.T, w.d_h))
-    got = _gpu(gpu_lib, P, R, None, S, gs, gh, gf, w.forget)
+    got = _gpu(gpu_lib, P, R, None, S, gs, gh, gf, w.forget, schedule=sched)
     want = _oracle(P, R, None, S, gs, gh, gf, w.forget)
     _compare(P, R, None, S, w.forget, got, want)
 
@@ -168,11 +198,13 @@ def test_backward_rejects_bad_arguments(gpu_lib):
     assert gpu_lib.backward_workspace_bytes(1, 4, 8, "layered") == 0
 
 
-def test_backward_layer_workload_full_size(gpu_lib):
-    """B=128, T=2048, d=1024, the shape the benchmark times. The states are the GPU's Newton
-    solve, with the oracle's own trajectory written over the lanes the oracle checks: every
-    batch row of three features (which fixes dR there) and 64 sampled lanes."""
-    w = by_name("layer_b128_t2048_d1024")
+@pytest.mark.parametrize("name", ["layer_b128_t2048_d1024", "sigmoid_bf16p_b16_t4096_d1024",
+                                  "long_b4_t16384_d2048"])
+def test_backward_workload_full_size(gpu_lib, name):
+    """Full workload sizes in the default (scan) form, and chains at the layer's size. The states are the GPU's Newton solve, with the
+    oracle's own trajectory written over the lanes the oracle checks: every batch row of three
+    features (which fixes dR there) and 64 sampled lanes."""
+    w = by_name(name)
     B, T, d = w.B, w.T, w.d_h
     case(f"backward {w.name} full size, sampled lanes")
     inp = draw_preactivation_inputs(w, device=DEV)
@@ -189,8 +221,8 @@ def test_backward_layer_workload_full_size(gpu_lib):
     lane4 = lambda t: t[ib, :, :, ij].permute(1, 2, 0).unsqueeze(0).cpu()  # noqa: E731
     subs = {"features": (feat(P), R[:, js].cpu()), "lanes": (lane4(P), R[:, ij].cpu())}
     S_ref = {}
-    for name, (Ps, Rs) in subs.items():
-        S_ref[name] = torch.from_numpy(ref.sequential(to_np(Ps), to_np(Rs), None, w.forget).astype(np.float32))
+    for part, (Ps, Rs) in subs.items():
+        S_ref[part] = torch.from_numpy(ref.sequential(to_np(Ps), to_np(Rs), None, w.forget).astype(np.float32))
     S[..., js] = S_ref["features"].to(DEV)
     S[ib, :, :, ij] = S_ref["lanes"][0].permute(2, 0, 1).to(DEV)
 
@@ -198,20 +230,26 @@ def test_backward_layer_workload_full_size(gpu_lib):
     dP, dR, ds0 = gpu_lib.backward(P, R, S, None, gs, gh, gf, w.forget)
     torch.cuda.synchronize()
     assert torch.isfinite(dP).all() and torch.isfinite(dR).all() and torch.isfinite(ds0).all()
+    if B >= 128:
+        # chains agree with the scan to rounding
+        cP, cR, c0 = gpu_lib.backward(P, R, S, None, gs, gh, gf, w.forget, schedule="fused_chain")
+        torch.cuda.synchronize()
+        assert grad_rel_err(cP, dP) < 1e-5 and grad_rel_err(cR, dR) < 1e-5 and grad_rel_err(c0, ds0) < 1e-5
+        del cP, cR, c0
 
     grads = {"features": (feat(gs), gh[:, :, js].cpu(), gf[:, :, js].cpu()),
              "lanes": (lane4(gs), gh[ib, :, ij].T.unsqueeze(0).cpu(), gf[ib, :, ij].T.unsqueeze(0).cpu())}
     got = {"features": (feat(dP), dR[:, js].cpu(), ds0[:, :, js].cpu()),
            "lanes": (lane4(dP), None, ds0[ib, :, ij].T.unsqueeze(0).cpu())}
-    for name, (Ps, Rs) in subs.items():
-        want = _oracle(Ps, Rs, None, S_ref[name], *grads[name], w.forget)
-        keep = _decided_lanes(to_np(Ps), to_np(Rs), None, to_np(S_ref[name]), w.forget)
+    for part, (Ps, Rs) in subs.items():
+        want = _oracle(Ps, Rs, None, S_ref[part], *grads[part], w.forget)
+        keep = _decided_lanes(to_np(Ps), to_np(Rs), None, to_np(S_ref[part]), w.forget)
         assert 1.0 - keep.mean() <= 0.05
-        dP_g, dR_g, ds0_g = got[name]
+        dP_g, dR_g, ds0_g = got[part]
         errs = [grad_rel_err(dP_g, want[0], keep[:, None, None, :]),
                 grad_rel_err(ds0_g, want[2], keep[:, None, :])]
         if dR_g is not None:
             errs.append(grad_rel_err(dR_g, want[1], np.all(keep, axis=0)[None, :]))
-        print(f"layer full size backward ({name}): rel err {['%.2e' % e for e in errs]}, "
+        print(f"{w.name} full size backward ({part}): rel err {['%.2e' % e for e in errs]}, "
               f"undecided {int((~keep).sum())}/{keep.size}")
         assert max(errs) < GRAD_TOL
