@@ -81,6 +81,7 @@ def kernel_work(w, n_e, p_bytes):
         "newton_iteration": {"bound": "hbm", "bytes": n_e * (p_bytes + 16 + 16)},             # P, S_k in; S_k+1 out
         "newton_solve": {"bound": "alu", "bytes": n_e * (p_bytes + 16 + 4),                   # P in; S_K, h out
                          "flops": n_e * solve_flops_per_elem(w.max_iters, w.forget == "sigmoid")},
+        "backward": {"bound": "hbm", "bytes": n_e * (p_bytes + 16 + 4 + 16)},                 # P, S, dL/dh in; dP out
     }
 
 
@@ -105,6 +106,9 @@ KERNEL_SOURCES = {
     "warm_start": ["recurrent_nets_amd/csrc/k_warm.hip", "recurrent_nets_amd/csrc/cell.h",
                    "recurrent_nets_amd/csrc/common.h"],
     "input_projection": ["recurrent_nets_amd/csrc/k_gemm.hip", "recurrent_nets_amd/csrc/common.h"],
+    "backward": ["recurrent_nets_amd/csrc/k_backward.hip", "recurrent_nets_amd/csrc/affine4.h",
+                 "recurrent_nets_amd/csrc/cell.h", "recurrent_nets_amd/csrc/common.h",
+                 "recurrent_nets_amd/csrc/kernels.h"],
 }
 
 
@@ -204,6 +208,8 @@ def main():
     ap.add_argument("--schedule", default="fused", choices=["fused", "fused_scan", "fused_chain", "layered"])
     ap.add_argument("--no-layered-context", action="store_true",
                     help="skip the context runs of the scan form and the layered schedule")
+    ap.add_argument("--no-backward-context", action="store_true",
+                    help="skip the context run of the backward pass at the forward solution")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -384,6 +390,45 @@ def main():
                               "residual_plus_scan": {"achieved": round(ab_gbs, 1), "peak": HBM_PEAK_GBS,
                                                      "unit": "GB/s", "frac": round(ab_gbs / HBM_PEAK_GBS, 4)},
                               "kernels": rounded(lkernels)}
+
+    if not args.no_backward_context:
+        # the backward pass at the forward solution for a loss on h (dL/dh ~ N(0, 1) and a
+        # final-state gradient): dP, dR, dstate0; not part of the metric
+        from workloads import random_cotangents_device
+        _, g_h, g_fin = random_cotangents_device(w.seed + 99, w.B, w.T, w.d_h, dev)
+        dP = torch.empty((w.B, w.T, 4, w.d_h), dtype=torch.float32, device=dev)
+        dR = torch.empty((4, w.d_h), dtype=torch.float32, device=dev)
+        d0 = torch.empty((w.B, 4, w.d_h), dtype=torch.float32, device=dev)
+        bws = slstm.alloc_workspace(slstm.backward_workspace_bytes(w.B, w.T, w.d_h), dev)
+
+        def bwd():
+            slstm.backward(P, R, S, None, None, g_h, g_fin, w.forget, dP=dP, dR=dR, dstate0=d0, workspace=bws)
+
+        bwd()
+        torch.cuda.synchronize()
+        reps = max(3, args.steps // 2)
+        slstm.profile_reset()
+        slstm.profile_enable(True)
+        tb = time.perf_counter()
+        for _ in range(reps):
+            bwd()
+        torch.cuda.synchronize()
+        b_ms = (time.perf_counter() - tb) * 1000.0 / reps
+        slstm.profile_enable(False)
+        bd = slstm.profile_durations("backward")
+        bk = sum(bd) / len(bd)
+        gbs = work["backward"]["bytes"] / (bk * 1e-3) / 1e9
+        log(f"[bench] backward: {b_ms:.3f} ms per call, kernels {bk:.3f} ms, {gbs:.0f} GB/s algorithmic")
+        context["backward"] = {"ms": round(b_ms, 4), "state_elems_per_s": n_e / (b_ms * 1e-3),
+                               "gradients_in": "dL/dh, dL/d final state", "form": "scan",
+                               "roofline": {"bound": "hbm", "kernel": "backward", "achieved": round(gbs, 1),
+                                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                            "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                            "traffic": measured_traffic("backward", w.name)},
+                               "kernel_avg_ms": round(bk, 4),
+                               "bytes_per_launch": work["backward"]["bytes"]}
+        del dP, dR, d0, bws, g_h, g_fin
+        torch.cuda.empty_cache()
 
     if not args.no_sequential_context:
         # the lane-parallel sequential forward on the same P, for context (not the metric)

@@ -41,7 +41,8 @@ constexpr int kBackBlock = 256;  // one feature per thread
 constexpr int kBackSteps = SLSTM_BACK_STEPS;  // steps per tile
 constexpr int kBackWords = 8;                 // per lane and tile: adjoint (4), running dR (4)
 
-template <bool BF16, bool SIG>
+// GS: a gradient with respect to the states is given (else only dL/dh and the final state's)
+template <bool BF16, bool SIG, bool GS>
 __global__ __launch_bounds__(kBackBlock, SLSTM_BACK_MIN_WAVES) void backward_chain_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S, const float* __restrict__ g, const float* __restrict__ g_h,
@@ -84,6 +85,8 @@ __global__ __launch_bounds__(kBackBlock, SLSTM_BACK_MIN_WAVES) void backward_cha
   const rsrc_t rsP = make_rsrc(static_cast<const char*>(P) + row * 4 * static_cast<i64>(d) * (BF16 ? 2 : 4));
   const rsrc_t rsS = make_rsrc(S + row * 4 * static_cast<i64>(d));
   const rsrc_t rsD = make_rsrc(dP + row * 4 * static_cast<i64>(d));
+  const rsrc_t rsG = make_rsrc(GS ? g + row * 4 * static_cast<i64>(d) : g);
+  const rsrc_t rsH = make_rsrc(g_h != nullptr ? g_h + row * static_cast<i64>(d) : g_h);
   float p[TC][4], s[TC][4], gs[TC][4];
 #pragma unroll
   for (int u = 0; u < TC; ++u) {
@@ -99,12 +102,11 @@ __global__ __launch_bounds__(kBackBlock, SLSTM_BACK_MIN_WAVES) void backward_cha
         p[u][k] = buf_ld_p<BF16>(rsP, j, (4u * u + k) * ud);
         s[u][k] = buf_ld(rsS, 4u * j, 4u * (4u * u + k) * ud);
       }
-      if (g != nullptr) {
-        const float* gr = g + (row + u) * 4 * static_cast<i64>(d);
+      if constexpr (GS) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) gs[u][k] = gr[k * ud + j];
+        for (int k = 0; k < 4; ++k) gs[u][k] = buf_ld(rsG, 4u * j, 4u * (4u * u + k) * ud);
       }
-      if (g_h != nullptr) gs[u][3] += g_h[(row + u) * static_cast<i64>(d) + j];
+      if (g_h != nullptr) gs[u][3] += buf_ld(rsH, 4u * j, 4u * u * ud);
     }
   }
   // the state before the tile
@@ -184,16 +186,20 @@ __global__ __launch_bounds__(kBackBlock, SLSTM_BACK_MIN_WAVES) void backward_cha
 }
 
 // ---- scan form ------------------------------------------------------------------------------
+// Sub-chunk length and waves per SIMD: the quad scan and look-back cost a fixed number of
+// instructions per sub-chunk, so longer sub-chunks spend fewer per step; 8 steps at 2 waves per
+// SIMD (the sub-chunk's P, states and gradients in registers, no spills) measured fastest on
+// MI355X at every shape tried (4 steps at 3 waves: 5% slower at B=128, 30% at B=4).
 #ifndef SLSTM_BACK_SCAN_TSUB
-#define SLSTM_BACK_SCAN_TSUB 4
+#define SLSTM_BACK_SCAN_TSUB 8
 #endif
 #ifndef SLSTM_BACK_SCAN_MIN_WAVES
-#define SLSTM_BACK_SCAN_MIN_WAVES 3
+#define SLSTM_BACK_SCAN_MIN_WAVES 2
 #endif
 constexpr int kBackScanBlock = 256;  // 4 waves x 16 features x 4 sub-chunks
 constexpr int kBackScanTSub = SLSTM_BACK_SCAN_TSUB;
 
-template <bool BF16, bool SIG, int TSUB>
+template <bool BF16, bool SIG, bool GS, int TSUB>
 __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void backward_scan_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S, const float* __restrict__ g, const float* __restrict__ g_h,
@@ -229,6 +235,8 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
   const rsrc_t rsP = make_rsrc(static_cast<const char*>(P) + tile_row * (BF16 ? 2 : 4));
   const rsrc_t rsS = make_rsrc(S + tile_row);
   const rsrc_t rsD = make_rsrc(dP + tile_row);
+  const rsrc_t rsG = make_rsrc(GS ? g + tile_row : g);
+  const rsrc_t rsH = make_rsrc(g_h != nullptr ? g_h + (static_cast<i64>(b) * T + t_tile) * static_cast<i64>(d) : g_h);
   const unsigned lane_off = static_cast<unsigned>(sc * TSUB) * 4u * ud + j;  // elements
 
   const unsigned long long pf = quad_look_back_prefetch(desc, n_lanes_pad, my_lane, q, tr, anchor_stride);
@@ -250,13 +258,11 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
         pg[u][k] = buf_ld_p<BF16>(rsP, o, k * ud);
         sv[u][k] = buf_ld(rsS, 4u * o, 4u * k * ud);
       }
-      const i64 row = static_cast<i64>(b) * T + t;
-      if (g != nullptr) {
-        const float* gr = g + row * 4 * static_cast<i64>(d);
+      if constexpr (GS) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) gs[u][k] = gr[k * ud + j];
+        for (int k = 0; k < 4; ++k) gs[u][k] = buf_ld(rsG, 4u * o, 4u * k * ud);
       }
-      if (g_h != nullptr) gs[u][3] += g_h[row * static_cast<i64>(d) + j];
+      if (g_h != nullptr) gs[u][3] += buf_ld(rsH, 4u * (static_cast<unsigned>(sc * TSUB + u) * ud + j), 0);
       if (g_final != nullptr && t == T - 1) {
         const float* gf = g_final + static_cast<i64>(b) * 4 * static_cast<i64>(d);
 #pragma unroll
@@ -367,11 +373,17 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
 #pragma unroll
     for (int e = 0; e < 4; ++e) ds[e * ud + j] = y[e];
   }
+
 }
 
 // ---- fixed-order sum of the dR rows -------------------------------------------------------------
-// rows summed per thread in the first level: at least 32, and at most 4096 chunks
-static i64 row_chunk(i64 rows) { return std::max<i64>(32, (rows + 4095) / 4096); }
+// rows summed per thread in the first level: about the square root of the row count, so that
+// both levels have short loops (a multiple of 8, for the unrolled loads)
+static i64 row_chunk(i64 rows) {
+  i64 c = 8;
+  while (c * c < rows) c += 8;
+  return c;
+}
 
 // part[c, i] = sum of rows[r, i] over the rows r of chunk c, in order of r
 __global__ __launch_bounds__(256) void sum_row_chunks_kernel(const float* __restrict__ rows,
@@ -382,6 +394,7 @@ __global__ __launch_bounds__(256) void sum_row_chunks_kernel(const float* __rest
   const int r0 = blockIdx.y * chunk;
   const int r1 = min(r0 + chunk, n_rows);
   float acc = 0.0f;
+#pragma unroll 8
   for (int r = r0; r < r1; ++r) acc += rows[static_cast<i64>(r) * n + i];
   part[static_cast<i64>(blockIdx.y) * n + i] = acc;
 }
@@ -392,6 +405,7 @@ __global__ __launch_bounds__(256) void sum_chunks_kernel(const float* __restrict
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   float acc = 0.0f;
+#pragma unroll 8
   for (int c = 0; c < n_chunks; ++c) acc += part[static_cast<i64>(c) * n + i];
   out[i] = acc;
 }
@@ -441,32 +455,44 @@ hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const flo
   const int n_ctr = ticket_counters(gr.n_lg);
   const dim3 grid(static_cast<unsigned>(blocks));
   const int a = static_cast<int>(gr.n_jt), c = static_cast<int>(gr.n_lg), e = static_cast<int>(gr.n_tt);
+  const bool gs = g != nullptr;
+  // one instantiation per P dtype, forget-gate form and presence of the state gradient
+#define SLSTM_BACK_DISPATCH                                   \
+  do {                                                        \
+    if (p_bf16) {                                             \
+      if (sig_forget) {                                       \
+        if (gs) SLSTM_BACK_LAUNCH(true, true, true);          \
+        else SLSTM_BACK_LAUNCH(true, true, false);            \
+      } else {                                                \
+        if (gs) SLSTM_BACK_LAUNCH(true, false, true);         \
+        else SLSTM_BACK_LAUNCH(true, false, false);           \
+      }                                                       \
+    } else {                                                  \
+      if (sig_forget) {                                       \
+        if (gs) SLSTM_BACK_LAUNCH(false, true, true);         \
+        else SLSTM_BACK_LAUNCH(false, true, false);           \
+      } else {                                                \
+        if (gs) SLSTM_BACK_LAUNCH(false, false, true);        \
+        else SLSTM_BACK_LAUNCH(false, false, false);          \
+      }                                                       \
+    }                                                         \
+  } while (0)
   if (scan) {
     const int stride = look_back_anchor_stride(gr.n_lg, SLSTM_BACK_SCAN_MIN_WAVES);
-#define SLSTM_BACK_LAUNCH(BF, SG)                                                                                  \
-  backward_scan_kernel<BF, SG, kBackScanTSub><<<grid, kBackScanBlock, 0, stream>>>(                                \
+#define SLSTM_BACK_LAUNCH(BF, SG, GS)                                                                              \
+  backward_scan_kernel<BF, SG, GS, kBackScanTSub><<<grid, kBackScanBlock, 0, stream>>>(                            \
       P, R, state0, S, g, g_h, g_final, dP, dstate0, rows, T, d, a, c, e, stride, desc, tickets, n_ctr, epoch)
-    if (p_bf16) {
-      if (sig_forget) SLSTM_BACK_LAUNCH(true, true);
-      else SLSTM_BACK_LAUNCH(true, false);
-    } else {
-      if (sig_forget) SLSTM_BACK_LAUNCH(false, true);
-      else SLSTM_BACK_LAUNCH(false, false);
-    }
+    SLSTM_BACK_DISPATCH;
 #undef SLSTM_BACK_LAUNCH
   } else {
-#define SLSTM_BACK_LAUNCH(BF, SG)                                                                                  \
-  backward_chain_kernel<BF, SG><<<grid, kBackBlock, 0, stream>>>(P, R, state0, S, g, g_h, g_final, dP, dstate0, \
-                                                                 rows, T, d, a, c, e, desc, tickets, n_ctr, epoch)
-    if (p_bf16) {
-      if (sig_forget) SLSTM_BACK_LAUNCH(true, true);
-      else SLSTM_BACK_LAUNCH(true, false);
-    } else {
-      if (sig_forget) SLSTM_BACK_LAUNCH(false, true);
-      else SLSTM_BACK_LAUNCH(false, false);
-    }
+#define SLSTM_BACK_LAUNCH(BF, SG, GS)                                                                      \
+  backward_chain_kernel<BF, SG, GS><<<grid, kBackBlock, 0, stream>>>(P, R, state0, S, g, g_h, g_final, dP, \
+                                                                     dstate0, rows, T, d, a, c, e, desc,      \
+                                                                     tickets, n_ctr, epoch)
+    SLSTM_BACK_DISPATCH;
 #undef SLSTM_BACK_LAUNCH
   }
+#undef SLSTM_BACK_DISPATCH
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int n = 4 * d;
