@@ -227,10 +227,14 @@ size_t slstm_backward_workspace_bytes(int B, int T, int d_h, slstm_schedule sche
  *   g_states (B, T, 4, d_h) or NULL: dL/d states.  g_h (B, T, d_h) or NULL: dL/d h, added to
  *     slot 3.  g_final (B, 4, d_h) or NULL: dL/d of the final state, added at step T-1. A NULL
  *     gradient counts as zeros.
- *   dP (B, T, 4, d_h) f32, written: dL/dP per gate (z, i, f, o). P = W_x x + bias, so the
- *     gradients of W_x, x and the bias are products of dP with x and W_x and a sum of dP.
+ *   dP (B, T, 4, d_h), written: dL/dP per gate (z, i, f, o), float32 (dP_dtype SLSTM_F32) or
+ *     rounded to bfloat16, nearest even (SLSTM_BF16, the operand of
+ *     slstm_input_projection_backward). P = W_x x + bias, so the gradients of W_x and x are
+ *     products of dP with x and W_x.
  *   dR (4, d_h) f32, written: dL/dR = sum over b, t of dP[b, t, g, j] * h_{t-1}[b, j], with
  *     h_0 taken from state0.
+ *   dbias (4, d_h) f32 or NULL, written: dL/dbias = sum over b, t of dP[b, t, g, j] (from the
+ *     float32 values).
  *   dstate0 (B, 4, d_h) f32 or NULL, written: dL/d state0 (at the zero state if state0 is NULL).
  * schedule: SLSTM_SCHEDULE_FUSED and SLSTM_SCHEDULE_FUSED_SCAN run one kernel that scans the
  * maps y -> A_t^T (g_t + y) along T with a look-back across tiles (parallel along T at any
@@ -241,9 +245,34 @@ size_t slstm_backward_workspace_bytes(int B, int T, int d_h, slstm_schedule sche
  */
 slstm_status slstm_backward(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
                             const float* states, const float* g_states, const float* g_h,
-                            const float* g_final, float* dP, float* dR, float* dstate0, int B,
-                            int T, int d_h, slstm_forget fmode, slstm_schedule schedule,
-                            void* workspace, size_t workspace_bytes, void* stream);
+                            const float* g_final, void* dP, slstm_dtype dP_dtype, float* dR,
+                            float* dbias, float* dstate0, int B, int T, int d_h, slstm_forget fmode,
+                            slstm_schedule schedule, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* Workspace bytes of slstm_input_projection_backward (0 if invalid). */
+size_t slstm_input_projection_backward_workspace_bytes(int B, int T, int d_in, int d_h);
+
+/*
+ * Gradients of the input projection P = x W_x^T + bias ("sLSTM in this library", "API notes":
+ * W_x is a GEMM; "Backward": the gradient of W_x follows from the cell's VJP by a GEMM):
+ *   dW_x[g, j, k] = sum over b, t of dP[b, t, g, j] x[b, t, k]   (dW_x = dP^T x)
+ *   dx[b, t, k]   = sum over g, j of dP[b, t, g, j] W_x[g, j, k]  (dx = dP W_x)
+ * (the bias gradient is slstm_backward's dbias).
+ *   x (B, T, d_in) bf16, W_x (4, d_h, d_in) bf16: as given to slstm_input_projection.
+ *   dP (B, T, 4, d_h), f32 (rounded to bfloat16, nearest even, for the products) or bf16
+ *     (dP_dtype), as slstm_backward writes it.
+ *   dx (B, T, d_in) f32 or NULL; dW_x (4, d_h, d_in) f32 or NULL: written when non-NULL.
+ * Both products run on the bf16 MFMA units with float32 accumulation; dW_x, whose reduction
+ * runs over all B*T rows, splits that range over workgroups and adds the partial products in a
+ * fixed order (bitwise reproducible). d_in must be a positive multiple of 8; 16-byte aligned
+ * x, W_x and dP. The workspace (slstm_input_projection_backward_workspace_bytes, 256-byte
+ * aligned) holds the bfloat16 transposes of dP, x and W_x and the partial products.
+ */
+slstm_status slstm_input_projection_backward(const void* x, const void* W_x, const void* dP,
+                                             slstm_dtype dP_dtype, float* dx, float* dW_x, int B,
+                                             int T, int d_in, int d_h, void* workspace,
+                                             size_t workspace_bytes, void* stream);
 
 /*
  * Kernel timing with HIP events recorded on the launching stream around every kernel the
@@ -262,7 +291,9 @@ typedef enum {
   SLSTM_KERNEL_NEWTON_ITERATION = 7,
   SLSTM_KERNEL_NEWTON_SOLVE = 8, /* the one-kernel fixed-count solve of the chain form */
   SLSTM_KERNEL_BACKWARD = 9,     /* the adjoint and cell VJP pass of slstm_backward */
-  SLSTM_KERNEL_KINDS = 10
+  SLSTM_KERNEL_WEIGHT_GRADIENT = 10, /* slstm_input_projection_backward's dW_x product */
+  SLSTM_KERNEL_INPUT_GRADIENT = 11,  /* slstm_input_projection_backward's dx product */
+  SLSTM_KERNEL_KINDS = 12
 } slstm_kernel_kind;
 
 slstm_status slstm_profile_enable(int on);

@@ -28,7 +28,7 @@ What it computes, and where each step is stated:
   plain block forward substitution (a sequential loop), and on tiny inputs by a dense
   LAPACK solve of the assembled system.
 * input projection P = W_x x + b ("W_x is a GEMM" -- "sLSTM in this library", "API
-  notes").
+  notes"), and its gradients dW_x = dP^T x, dx = dP W_x, dbias = sum of dP.
 * backward ("sLSTM in this library", section "Backward": the adjoint is one reverse scan of
   the transposed Jacobians, then the cell's vector-Jacobian product for the gradients of R
   and W_x): lam_T = g_T, lam_t = g_t + A_{t+1}^T lam_{t+1}; per step the gate Jacobian
@@ -486,6 +486,24 @@ def input_projection(x, W, bias):
     g, d_h, _ = W.shape
     P = x.reshape(B * T, d_in) @ W.reshape(g * d_h, d_in).T
     return P.reshape(B, T, g, d_h) + bias
+
+
+def input_projection_backward(x, W, dP):
+    """Gradients of a loss L through P = x W^T + bias, given dP = dL/dP (B, T, 4, d_h):
+    dW[g, j, k] = sum_{b,t} dP[b, t, g, j] x[b, t, k], dx[b, t, k] = sum_{g,j} dP[b, t, g, j]
+    W[g, j, k], dbias[g, j] = sum_{b,t} dP[b, t, g, j]. ("sLSTM in this library", "Backward":
+    the gradient of W_x follows from the cell's VJP by a GEMM.) Returns (dW, dx, dbias), float64.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    W = np.asarray(W, dtype=np.float64)
+    dP = np.asarray(dP, dtype=np.float64)
+    B, T, d_in = x.shape
+    g, d_h, _ = W.shape
+    dP2 = dP.reshape(B * T, g * d_h)
+    dW = (dP2.T @ x.reshape(B * T, d_in)).reshape(g, d_h, d_in)
+    dx = (dP2 @ W.reshape(g * d_h, d_in)).reshape(B, T, d_in)
+    dbias = dP2.sum(axis=0).reshape(g, d_h)
+    return dW, dx, dbias
 
 
 def hidden(S):

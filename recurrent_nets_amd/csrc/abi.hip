@@ -3,6 +3,7 @@
 // initial state prepended, residual early stop, flags after the last iterate.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -349,6 +350,36 @@ BackwardLayout backward_layout(int B, int T, int d, bool scan) {
   return L;
 }
 
+// workspace of the input projection's backward: bfloat16 operands with the reduction dimension
+// padded to whole 16-byte chunks, then the split-K partial products of dW_x
+struct ProjBackLayout {
+  i64 k_bt, k_4d;  // padded reduction lengths of dW_x (B*T) and dx (4*d_h)
+  int splits;
+  size_t dPb, WT, dPT, xT, part, total;
+};
+
+i64 pad8(i64 v) { return (v + 7) / 8 * 8; }
+
+ProjBackLayout proj_back_layout(int B, int T, int d_in, int d_h) {
+  ProjBackLayout L;
+  const i64 bt = static_cast<i64>(B) * T;
+  const i64 n4 = 4 * static_cast<i64>(d_h);
+  L.k_bt = pad8(bt);
+  L.k_4d = pad8(n4);
+  // enough workgroups for two per compute unit, each split at least 32 K steps long
+  const int tiles = slstm::gemm_tiles(n4, d_in);
+  int want = (2 * device_cus() + tiles - 1) / tiles;
+  want = std::min<i64>(want, std::max<i64>(1, L.k_bt / 1024));
+  L.splits = slstm::gemm_splits_for(n4, d_in, static_cast<int>(L.k_bt), std::min(want, 64));
+  L.dPb = 0;
+  L.WT = align_up(L.dPb + static_cast<size_t>(bt * L.k_4d) * 2);
+  L.dPT = align_up(L.WT + static_cast<size_t>(d_in * L.k_4d) * 2);
+  L.xT = align_up(L.dPT + static_cast<size_t>(n4 * L.k_bt) * 2);
+  L.part = align_up(L.xT + static_cast<size_t>(d_in * L.k_bt) * 2);
+  L.total = align_up(L.part + (L.splits > 1 ? static_cast<size_t>(L.splits) * n4 * d_in * 4 : 0));
+  return L;
+}
+
 }  // namespace
 
 namespace slstm {
@@ -562,16 +593,18 @@ size_t slstm_backward_workspace_bytes(int B, int T, int d_h, slstm_schedule sche
 
 slstm_status slstm_backward(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
                             const float* states, const float* g_states, const float* g_h,
-                            const float* g_final, float* dP, float* dR, float* dstate0, int B,
-                            int T, int d_h, slstm_forget fmode, slstm_schedule schedule,
-                            void* workspace, size_t workspace_bytes, void* stream) {
+                            const float* g_final, void* dP, slstm_dtype dP_dtype, float* dR,
+                            float* dbias, float* dstate0, int B, int T, int d_h, slstm_forget fmode,
+                            slstm_schedule schedule, void* workspace, size_t workspace_bytes,
+                            void* stream) {
   g_err[0] = '\0';
   slstm_status s = check_common(P, P_dtype, R, state0, states, nullptr, nullptr, B, T, d_h, fmode);
   if (s != SLSTM_OK) return s;
   if (dP == nullptr || dR == nullptr) return fail(SLSTM_EINVAL, "dP and dR must not be NULL");
-  if (!aligned(dP, 16) || !aligned(dR, 4) || !aligned(dstate0, 4) || !aligned(g_states, 4) ||
-      !aligned(g_h, 4) || !aligned(g_final, 4))
-    return fail(SLSTM_EINVAL, "dP must be 16-byte aligned; gradients and dR, dstate0 4-byte aligned");
+  if (dP_dtype != SLSTM_F32 && dP_dtype != SLSTM_BF16) return fail(SLSTM_EINVAL, "unknown dP dtype %d", (int)dP_dtype);
+  if (!aligned(dP, 16) || !aligned(dR, 4) || !aligned(dbias, 4) || !aligned(dstate0, 4) ||
+      !aligned(g_states, 4) || !aligned(g_h, 4) || !aligned(g_final, 4))
+    return fail(SLSTM_EINVAL, "dP must be 16-byte aligned; gradients and dR, dbias, dstate0 4-byte aligned");
   if (!known_schedule(schedule)) return fail(SLSTM_EINVAL, "unknown schedule %d", (int)schedule);
   if (!backward_schedule(schedule))
     return fail(SLSTM_EINVAL, "the backward pass has fused forms only: schedule FUSED, FUSED_SCAN or FUSED_CHAIN");
@@ -586,11 +619,71 @@ slstm_status slstm_backward(const void* P, slstm_dtype P_dtype, const float* R, 
   HIP_TRY(slstm::launch_init_control(ctl, st));
   const uint32_t ep = next_epoch();
   HIP_TRY(timed(SLSTM_KERNEL_BACKWARD, st, [&] {
-    return slstm::launch_backward(P, P_dtype == SLSTM_BF16, R, state0, states, g_states, g_h, g_final, dP, dR,
-                                  dstate0, at<float>(workspace, L.rows), B, T, d_h,
+    return slstm::launch_backward(P, P_dtype == SLSTM_BF16, R, state0, states, g_states, g_h, g_final, dP,
+                                  dP_dtype == SLSTM_BF16, dR, dbias, dstate0, at<float>(workspace, L.rows), B, T, d_h,
                                   fmode == SLSTM_FORGET_SIGMOID, scan, at<unsigned long long>(workspace, L.desc),
                                   slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0], ep, st);
   }));
+  return SLSTM_OK;
+}
+
+size_t slstm_input_projection_backward_workspace_bytes(int B, int T, int d_in, int d_h) {
+  if (check_dims(B, T, d_h) != SLSTM_OK || d_in < 8 || d_in % 8 != 0) return 0;
+  return proj_back_layout(B, T, d_in, d_h).total;
+}
+
+slstm_status slstm_input_projection_backward(const void* x, const void* W_x, const void* dP,
+                                             slstm_dtype dP_dtype, float* dx, float* dW_x, int B,
+                                             int T, int d_in, int d_h, void* workspace,
+                                             size_t workspace_bytes, void* stream) {
+  g_err[0] = '\0';
+  slstm_status s = check_dims(B, T, d_h);
+  if (s != SLSTM_OK) return s;
+  if (d_in < 8 || d_in % 8 != 0) return fail(SLSTM_EINVAL, "d_in must be a positive multiple of 8 (got %d)", d_in);
+  if (dP_dtype != SLSTM_F32 && dP_dtype != SLSTM_BF16) return fail(SLSTM_EINVAL, "unknown dP dtype %d", (int)dP_dtype);
+  if (dP == nullptr || (dW_x != nullptr && x == nullptr) || (dx != nullptr && W_x == nullptr))
+    return fail(SLSTM_EINVAL, "dP, and x for dW_x and W_x for dx, must not be NULL");
+  if (!aligned(x, 16) || !aligned(W_x, 16) || !aligned(dP, 16) || !aligned(dx, 4) || !aligned(dW_x, 4))
+    return fail(SLSTM_EINVAL, "x, W_x and dP must be 16-byte aligned");
+  if (workspace == nullptr || !aligned(workspace, kAlign))
+    return fail(SLSTM_EINVAL, "workspace must be non-NULL and 256-byte aligned");
+  const ProjBackLayout L = proj_back_layout(B, T, d_in, d_h);
+  if (workspace_bytes < L.total)
+    return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool f32 = dP_dtype == SLSTM_F32;
+  const i64 bt = static_cast<i64>(B) * T;
+  const int n4 = 4 * d_h;
+  if (dW_x != nullptr) {
+    uint16_t* dPT = at<uint16_t>(workspace, L.dPT);
+    uint16_t* xT = at<uint16_t>(workspace, L.xT);
+    float* part = at<float>(workspace, L.part);
+    HIP_TRY(timed(SLSTM_KERNEL_WEIGHT_GRADIENT, st, [&]() -> hipError_t {
+      hipError_t e = slstm::launch_transpose_bf16(dP, f32, dPT, bt, n4, L.k_bt, st);
+      if (e != hipSuccess) return e;
+      e = slstm::launch_transpose_bf16(x, false, xT, bt, d_in, L.k_bt, st);
+      if (e != hipSuccess) return e;
+      if (L.splits == 1) return slstm::launch_gemm_bf16(dPT, xT, nullptr, dW_x, n4, d_in, static_cast<int>(L.k_bt), st, 1);
+      e = slstm::launch_gemm_bf16(dPT, xT, nullptr, part, n4, d_in, static_cast<int>(L.k_bt), st, L.splits);
+      if (e != hipSuccess) return e;
+      return slstm::launch_sum_splits(part, dW_x, L.splits, static_cast<i64>(n4) * d_in, st);
+    }));
+  }
+  if (dx != nullptr) {
+    uint16_t* WT = at<uint16_t>(workspace, L.WT);
+    HIP_TRY(timed(SLSTM_KERNEL_INPUT_GRADIENT, st, [&]() -> hipError_t {
+      hipError_t e = slstm::launch_transpose_bf16(W_x, false, WT, n4, d_in, L.k_4d, st);
+      if (e != hipSuccess) return e;
+      const void* A = dP;
+      if (f32 || L.k_4d != n4) {
+        uint16_t* dPb = at<uint16_t>(workspace, L.dPb);
+        e = slstm::launch_pad_bf16(dP, f32, dPb, bt, n4, static_cast<int>(L.k_4d), st);
+        if (e != hipSuccess) return e;
+        A = dPb;
+      }
+      return slstm::launch_gemm_bf16(A, WT, nullptr, dx, bt, d_in, static_cast<int>(L.k_4d), st, 1);
+    }));
+  }
   return SLSTM_OK;
 }
 

@@ -14,6 +14,14 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
+// float32 -> bfloat16, round to nearest, ties to even (add half an ulp of the kept part, less
+// one unless the kept part is odd, then truncate); NaN stays a quiet NaN
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  const uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  return static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
 // Load one gate pre-activation, stored as float32 or bfloat16.
 template <bool BF16>
 __device__ __forceinline__ float load_p(const void* __restrict__ P, i64 idx) {

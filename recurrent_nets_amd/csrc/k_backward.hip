@@ -4,25 +4,26 @@
 //
 // Per lane (b, j), with g_t the direct gradient of the loss with respect to the state s_t:
 //   lam_{T-1} = g_{T-1} (+ the gradient of the final state),  lam_t = g_t + A_{t+1}^T lam_{t+1}
-//   dP_t = G_t^T lam_t,  dR = sum over b and t of dP_t * h_{t-1},  dstate0 = A_0^T lam_0
+//   dP_t = G_t^T lam_t,  dR = sum over b and t of dP_t * h_{t-1},  dbias = sum of dP_t,
+//   dstate0 = A_0^T lam_0
 // (A_t = d s_t / d s_{t-1}, G_t = d s_t / d x~_t; cell_vjp forms both products at once from
 // the stored state before the step.) The value y_t = A_t^T lam_t handed from step t to step
 // t-1 obeys the affine recurrence y_{t-1} = A_t^T (g_t + y_t), run from t = T-1 down to 0.
 //
 // Two layouts, as for the forward solve:
 // * chains: a thread owns one feature and kBackSteps consecutive steps and runs them from the
-//   last to the first; y entering its tile (from the tile after it) and the running sum of the
-//   lane's dR contributions come as epoch-tagged words (see tag_store). Tiles take tickets
-//   from the last tile along T to the first, so the tile a tile waits on holds an earlier
-//   ticket of the same counter and runs. The first tile along T holds the lane's dR over all
-//   of T and writes it per batch row. No waiting once the lane groups cover the GPU.
+//   last to the first; y entering its tile (from the tile after it) comes as four epoch-tagged
+//   words (see tag_store). Tiles take tickets from the last tile along T to the first, so the
+//   tile a tile waits on holds an earlier ticket of the same counter and runs.
 // * scan: the four threads of a quad hold four consecutive sub-chunks of one feature (the
 //   last in time first), compose their steps' maps y -> A_t^T (g_t + y) into one affine map,
 //   scan the maps across the quad and look back across tiles (quad_look_back, tiles in reverse
-//   order of time), then run their steps again from the y entering them. Parallel along T for
-//   few lane groups; each tile writes its dR contributions per batch row and tile.
-// The per-row dR sums are added in a fixed order by two small kernels. Every value is formed
-// in one fixed order: bitwise reproducible.
+//   order of time), then run their steps again from the y entering them. Parallel along T at
+//   any batch size.
+// Each tile writes its lane's sums of dP_t h_{t-1} and of dP_t (a row of 8 d floats per batch
+// row and tile), and two small kernels add the rows in a fixed order into dR and dbias. dP is
+// written as float32 or, for the bf16 weight-gradient GEMMs, rounded to bfloat16. Every value
+// is formed in one fixed order: bitwise reproducible.
 #include <algorithm>
 
 #include "affine4.h"
@@ -39,15 +40,23 @@ constexpr int kBackBlock = 256;  // one feature per thread
 #define SLSTM_BACK_MIN_WAVES 3
 #endif
 constexpr int kBackSteps = SLSTM_BACK_STEPS;  // steps per tile
-constexpr int kBackWords = 8;                 // per lane and tile: adjoint (4), running dR (4)
+constexpr int kBackWords = 4;                 // per lane and tile: y entering the tile before
+
+// dP of one step: float32, or bfloat16 rounded to nearest even
+__device__ __forceinline__ void store_dp(float v, bool bf16, rsrc_t r, unsigned elem_lane, unsigned elem_uniform) {
+  if (bf16)
+    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_rne(v), r, 2u * elem_lane, 2u * elem_uniform, 0);
+  else
+    buf_st(v, r, 4u * elem_lane, 4u * elem_uniform);
+}
 
 // GS: a gradient with respect to the states is given (else only dL/dh and the final state's)
 template <bool BF16, bool SIG, bool GS>
 __global__ __launch_bounds__(kBackBlock, SLSTM_BACK_MIN_WAVES) void backward_chain_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S, const float* __restrict__ g, const float* __restrict__ g_h,
-    const float* __restrict__ g_final, float* __restrict__ dP, float* __restrict__ dstate0,
-    float* __restrict__ dR_rows, int T, int d, int n_jt, int n_lg, int n_tt,
+    const float* __restrict__ g_final, void* __restrict__ dP, int dp_bf16, float* __restrict__ dstate0,
+    float* __restrict__ sum_rows, int T, int d, int n_jt, int n_lg, int n_tt,
     unsigned long long* __restrict__ carry, unsigned int* __restrict__ tickets, int n_ctr,
     uint32_t epoch) {
   constexpr int TC = kBackSteps;
@@ -84,7 +93,8 @@ __global__ __launch_bounds__(kBackBlock, SLSTM_BACK_MIN_WAVES) void backward_cha
   const i64 row = static_cast<i64>(b) * T + t0;
   const rsrc_t rsP = make_rsrc(static_cast<const char*>(P) + row * 4 * static_cast<i64>(d) * (BF16 ? 2 : 4));
   const rsrc_t rsS = make_rsrc(S + row * 4 * static_cast<i64>(d));
-  const rsrc_t rsD = make_rsrc(dP + row * 4 * static_cast<i64>(d));
+  const bool dpb = dp_bf16 != 0;
+  const rsrc_t rsD = make_rsrc(static_cast<char*>(dP) + row * 4 * static_cast<i64>(d) * (dpb ? 2 : 4));
   const rsrc_t rsG = make_rsrc(GS ? g + row * 4 * static_cast<i64>(d) : g);
   const rsrc_t rsH = make_rsrc(g_h != nullptr ? g_h + row * static_cast<i64>(d) : g_h);
   float p[TC][4], s[TC][4], gs[TC][4];
@@ -122,8 +132,8 @@ __global__ __launch_bounds__(kBackBlock, SLSTM_BACK_MIN_WAVES) void backward_cha
   }
   const float rz = R[j], ri = R[ud + j], rf = R[2 * ud + j], ro = R[3 * ud + j];
 
-  // the adjoint contribution entering from after the tile, and the running dR
-  float lin[4] = {0.0f, 0.0f, 0.0f, 0.0f}, dr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  // the adjoint contribution entering from after the tile
+  float lin[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   if (tt + 1 < n_tt) {
     bool ok = true;
     float v[kBackWords];
@@ -140,10 +150,7 @@ __global__ __launch_bounds__(kBackBlock, SLSTM_BACK_MIN_WAVES) void backward_cha
       for (int e = 0; e < kBackWords; ++e) ok &= tag_load(word(tt + 1, e), epoch, v[e]);
     }
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      lin[e] = v[e];
-      dr[e] = v[4 + e];
-    }
+    for (int e = 0; e < 4; ++e) lin[e] = v[e];
   } else if (g_final != nullptr) {
     const float* gf = g_final + static_cast<i64>(b) * 4 * static_cast<i64>(d);
 #pragma unroll
@@ -151,6 +158,7 @@ __global__ __launch_bounds__(kBackBlock, SLSTM_BACK_MIN_WAVES) void backward_cha
   }
 
   // ---- the steps of the tile, last to first ----
+  float dr[4] = {0.0f, 0.0f, 0.0f, 0.0f}, db[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int u = TC - 1; u >= 0; --u) {
     if (u < n_in) {
@@ -161,27 +169,25 @@ __global__ __launch_bounds__(kBackBlock, SLSTM_BACK_MIN_WAVES) void backward_cha
       cell_vjp(pv, p[u][0], p[u][1], p[u][2], p[u][3], rz, ri, rf, ro, sig, lam, dx, lin);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        buf_st(dx[e], rsD, 4u * j, 4u * (4u * u + e) * ud);
+        store_dp(dx[e], dpb, rsD, j, (4u * u + e) * ud);
         dr[e] = fmaf(dx[e], pv.h, dr[e]);
+        db[e] += dx[e];
       }
     }
   }
-
   if (tt > 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      tag_store(word(tt, e), lin[e], epoch);
-      tag_store(word(tt, 4 + e), dr[e], epoch);
-    }
-  } else {
-    if (dstate0 != nullptr) {
-      float* ds = dstate0 + static_cast<i64>(b) * 4 * static_cast<i64>(d);
+    for (int e = 0; e < 4; ++e) tag_store(word(tt, e), lin[e], epoch);
+  } else if (dstate0 != nullptr) {
+    float* ds = dstate0 + static_cast<i64>(b) * 4 * static_cast<i64>(d);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) ds[e * ud + j] = lin[e];
-    }
-    float* rows = dR_rows + static_cast<i64>(b) * 4 * static_cast<i64>(d);
+    for (int e = 0; e < 4; ++e) ds[e * ud + j] = lin[e];
+  }
+  float* rows = sum_rows + (static_cast<i64>(b) * n_tt + tt) * 8 * static_cast<i64>(d);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) rows[e * ud + j] = dr[e];
+  for (int e = 0; e < 4; ++e) {
+    rows[e * ud + j] = dr[e];
+    rows[(4 + e) * ud + j] = db[e];
   }
 }
 
@@ -203,8 +209,8 @@ template <bool BF16, bool SIG, bool GS, int TSUB>
 __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void backward_scan_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S, const float* __restrict__ g, const float* __restrict__ g_h,
-    const float* __restrict__ g_final, float* __restrict__ dP, float* __restrict__ dstate0,
-    float* __restrict__ dR_rows, int T, int d, int n_jt, int n_lg, int n_tt, int anchor_stride,
+    const float* __restrict__ g_final, void* __restrict__ dP, int dp_bf16, float* __restrict__ dstate0,
+    float* __restrict__ sum_rows, int T, int d, int n_jt, int n_lg, int n_tt, int anchor_stride,
     unsigned long long* __restrict__ desc, unsigned int* __restrict__ tickets, int n_ctr,
     uint32_t epoch) {
   constexpr bool sig = SIG;
@@ -234,7 +240,8 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
   const i64 tile_row = (static_cast<i64>(b) * T + t_tile) * 4 * static_cast<i64>(d);
   const rsrc_t rsP = make_rsrc(static_cast<const char*>(P) + tile_row * (BF16 ? 2 : 4));
   const rsrc_t rsS = make_rsrc(S + tile_row);
-  const rsrc_t rsD = make_rsrc(dP + tile_row);
+  const bool dpb = dp_bf16 != 0;
+  const rsrc_t rsD = make_rsrc(static_cast<char*>(dP) + tile_row * (dpb ? 2 : 4));
   const rsrc_t rsG = make_rsrc(GS ? g + tile_row : g);
   const rsrc_t rsH = make_rsrc(g_h != nullptr ? g_h + (static_cast<i64>(b) * T + t_tile) * static_cast<i64>(d) : g_h);
   const unsigned lane_off = static_cast<unsigned>(sc * TSUB) * 4u * ud + j;  // elements
@@ -340,7 +347,7 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
   }
 
   // ---- the steps again, from the last to the first, with the adjoint ----
-  float dr[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float dr[4] = {0.0f, 0.0f, 0.0f, 0.0f}, db[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int u = TSUB - 1; u >= 0; --u) {
     const int t = t_start + u;
@@ -353,20 +360,23 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
       const unsigned o = lane_off + u * 4u * ud;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        buf_st(dx[e], rsD, 4u * o, 4u * e * ud);
+        store_dp(dx[e], dpb, rsD, o, e * ud);
         dr[e] = fmaf(dx[e], pv.h, dr[e]);
+        db[e] += dx[e];
       }
     }
   }
-  // the tile's dR over the quad, summed in order of time (sub-chunks 3, 2, 1, 0 = q 0..3)
-  float tot[4];
+  // the tile's sums over the quad, in order of time (sub-chunks 3, 2, 1, 0 = q 0..3)
+  float tot[8];
 #pragma unroll
-  for (int e = 0; e < 4; ++e)
+  for (int e = 0; e < 4; ++e) {
     tot[e] = ((quad_bcast<0>(dr[e]) + quad_bcast<1>(dr[e])) + quad_bcast<2>(dr[e])) + quad_bcast<3>(dr[e]);
+    tot[4 + e] = ((quad_bcast<0>(db[e]) + quad_bcast<1>(db[e])) + quad_bcast<2>(db[e])) + quad_bcast<3>(db[e]);
+  }
   if (valid && q == 0) {
-    float* rows = dR_rows + (static_cast<i64>(b) * n_tt + tt) * 4 * static_cast<i64>(d);
+    float* rows = sum_rows + (static_cast<i64>(b) * n_tt + tt) * 8 * static_cast<i64>(d);
 #pragma unroll
-    for (int e = 0; e < 4; ++e) rows[e * ud + j] = tot[e];
+    for (int e = 0; e < 8; ++e) rows[e * ud + j] = tot[e];
   }
   if (valid && t_start == 0 && dstate0 != nullptr) {
     float* ds = dstate0 + static_cast<i64>(b) * 4 * static_cast<i64>(d);
@@ -399,15 +409,18 @@ __global__ __launch_bounds__(256) void sum_row_chunks_kernel(const float* __rest
   part[static_cast<i64>(blockIdx.y) * n + i] = acc;
 }
 
-// out[i] = sum of part[c, i] over the chunks c, in order of c
+// sum of part[c, i] over the chunks c, in order of c: into out0[i] for i < n0, else into
+// out1[i - n0] (skipped when out1 is null)
 __global__ __launch_bounds__(256) void sum_chunks_kernel(const float* __restrict__ part,
-                                                         float* __restrict__ out, int n_chunks, int n) {
+                                                         float* __restrict__ out0, float* __restrict__ out1,
+                                                         int n_chunks, int n0, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= n) return;
+  if (i >= n || (i >= n0 && out1 == nullptr)) return;
   float acc = 0.0f;
 #pragma unroll 8
   for (int c = 0; c < n_chunks; ++c) acc += part[static_cast<i64>(c) * n + i];
-  out[i] = acc;
+  if (i < n0) out0[i] = acc;
+  else out1[i - n0] = acc;
 }
 
 // ---- sizes and launch ---------------------------------------------------------------------------
@@ -424,7 +437,7 @@ static BackGrid back_grid(int B, int T, int d, bool scan) {
   } else {
     g.n_jt = (d + kBackBlock - 1) / kBackBlock;
     g.n_tt = (T + kBackSteps - 1) / kBackSteps;
-    g.rows = B;
+    g.rows = static_cast<i64>(B) * g.n_tt;
   }
   g.n_lg = static_cast<i64>(B) * g.n_jt;
   return g;
@@ -439,14 +452,15 @@ size_t backward_row_floats(int B, int T, int d, bool scan) {
   const BackGrid g = back_grid(B, T, d, scan);
   const i64 chunk = row_chunk(g.rows);
   const i64 chunks = (g.rows + chunk - 1) / chunk;
-  return static_cast<size_t>((g.rows + chunks) * 4 * static_cast<i64>(d));
+  return static_cast<size_t>((g.rows + chunks) * 8 * static_cast<i64>(d));
 }
 
 hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const float* state0,
                            const float* S, const float* g, const float* g_h, const float* g_final,
-                           float* dP, float* dR, float* dstate0, float* rows, int B, int T, int d,
-                           bool sig_forget, bool scan, unsigned long long* desc,
-                           unsigned int* tickets, uint32_t epoch, hipStream_t stream) {
+                           void* dP, bool dp_bf16, float* dR, float* dbias, float* dstate0,
+                           float* rows, int B, int T, int d, bool sig_forget, bool scan,
+                           unsigned long long* desc, unsigned int* tickets, uint32_t epoch,
+                           hipStream_t stream) {
   const BackGrid gr = back_grid(B, T, d, scan);
   const i64 blocks = gr.n_lg * gr.n_tt;
   const i64 chunk = row_chunk(gr.rows);
@@ -456,6 +470,7 @@ hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const flo
   const dim3 grid(static_cast<unsigned>(blocks));
   const int a = static_cast<int>(gr.n_jt), c = static_cast<int>(gr.n_lg), e = static_cast<int>(gr.n_tt);
   const bool gs = g != nullptr;
+  const int dpb = dp_bf16 ? 1 : 0;
   // one instantiation per P dtype, forget-gate form and presence of the state gradient
 #define SLSTM_BACK_DISPATCH                                   \
   do {                                                        \
@@ -481,13 +496,13 @@ hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const flo
     const int stride = look_back_anchor_stride(gr.n_lg, SLSTM_BACK_SCAN_MIN_WAVES);
 #define SLSTM_BACK_LAUNCH(BF, SG, GS)                                                                              \
   backward_scan_kernel<BF, SG, GS, kBackScanTSub><<<grid, kBackScanBlock, 0, stream>>>(                            \
-      P, R, state0, S, g, g_h, g_final, dP, dstate0, rows, T, d, a, c, e, stride, desc, tickets, n_ctr, epoch)
+      P, R, state0, S, g, g_h, g_final, dP, dpb, dstate0, rows, T, d, a, c, e, stride, desc, tickets, n_ctr, epoch)
     SLSTM_BACK_DISPATCH;
 #undef SLSTM_BACK_LAUNCH
   } else {
 #define SLSTM_BACK_LAUNCH(BF, SG, GS)                                                                      \
   backward_chain_kernel<BF, SG, GS><<<grid, kBackBlock, 0, stream>>>(P, R, state0, S, g, g_h, g_final, dP, \
-                                                                     dstate0, rows, T, d, a, c, e, desc,      \
+                                                                     dpb, dstate0, rows, T, d, a, c, e, desc, \
                                                                      tickets, n_ctr, epoch)
     SLSTM_BACK_DISPATCH;
 #undef SLSTM_BACK_LAUNCH
@@ -495,13 +510,13 @@ hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const flo
 #undef SLSTM_BACK_DISPATCH
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int n = 4 * d;
+  const int n = 8 * d;
   float* part = rows + gr.rows * n;
   sum_row_chunks_kernel<<<dim3((n + 255) / 256, static_cast<unsigned>(chunks)), 256, 0, stream>>>(
       rows, part, static_cast<int>(gr.rows), static_cast<int>(chunk), n);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  sum_chunks_kernel<<<(n + 255) / 256, 256, 0, stream>>>(part, dR, static_cast<int>(chunks), n);
+  sum_chunks_kernel<<<(n + 255) / 256, 256, 0, stream>>>(part, dR, dbias, static_cast<int>(chunks), 4 * d, n);
   return hipGetLastError();
 }
 

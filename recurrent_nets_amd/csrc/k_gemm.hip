@@ -17,7 +17,9 @@
 // slot c ^ ((r >> 1) & 3), which keeps every 8-lane group of a fragment read on distinct banks.
 // Rows past M or N read zero (buffer loads against the tile's extent); a K tail is pointed
 // outside the extent, which also reads zero. The bias is added in the epilogue, so P is written
-// once. Workgroups are renumbered so that each of the 8 XCDs works through a contiguous range of
+// once. The same kernel serves the weight-gradient products of the backward pass, whose
+// reduction length (B*T) is long and whose output is small: there the K range is split over
+// gridDim.y and each split writes its partial product to its own slice of C. Workgroups are renumbered so that each of the 8 XCDs works through a contiguous range of
 // tiles, ordered in groups of row panels so that the tiles an XCD runs together share row and
 // column panels in its L2.
 #include "common.h"
@@ -70,7 +72,8 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(const uint16
                                                                   const uint16_t* __restrict__ W,
                                                                   const float* __restrict__ bias,
                                                                   float* __restrict__ C, int M, int N,
-                                                                  int K, int tiles_m, int tiles_n) {
+                                                                  int K, int tiles_m, int tiles_n,
+                                                                  int k_split, i64 c_split) {
   // three separate objects, so that the compiler sees which stage a fragment read touches and
   // waits only for the loads into that stage
   __shared__ __attribute__((aligned(1024))) GemmStage st0;
@@ -97,13 +100,16 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(const uint16
 
   const i64 row0 = static_cast<i64>(tm) * kGemmBM;
   const i64 col0 = static_cast<i64>(tn) * kGemmBN;
+  // this split's range of K: [kb, kb + kl)
+  const int kb = static_cast<int>(blockIdx.y) * k_split;
+  const int kl = min(k_split, K - kb);
   // extents of the operand tiles (uniform; integer selects keep them in scalar registers)
   const int x_rows = (M - row0 < kGemmBM) ? static_cast<int>(M - row0) : kGemmBM;
   const int w_rows = (N - col0 < kGemmBN) ? static_cast<int>(N - col0) : kGemmBN;
-  const uint32_t x_bytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x_rows) * static_cast<uint32_t>(K) * 2u);
-  const uint32_t w_bytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(w_rows) * static_cast<uint32_t>(K) * 2u);
-  const rsrc_t rX = make_rsrc_bytes(X + row0 * K, x_bytes);
-  const rsrc_t rW = make_rsrc_bytes(W + col0 * K, w_bytes);
+  const uint32_t x_bytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x_rows) * static_cast<uint32_t>(K) * 2u - static_cast<uint32_t>(kb) * 2u);
+  const uint32_t w_bytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(w_rows) * static_cast<uint32_t>(K) * 2u - static_cast<uint32_t>(kb) * 2u);
+  const rsrc_t rX = make_rsrc_bytes(X + row0 * K + kb, x_bytes);
+  const rsrc_t rW = make_rsrc_bytes(W + col0 * K + kb, w_bytes);
 
   // ---- global -> LDS: each wave fills 4 of the 16 x blocks and 2 of the 8 W_x blocks of a
   //      stage (a block: 16 rows x 64 B, one 1 KiB direct load). Lane l fills slot l & 3 of row
@@ -115,7 +121,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(const uint16
     const uint32_t r = static_cast<uint32_t>(blk * 16) + lrow;
     const uint32_t c = gemm_slot(r, lslot);
     const int gk = k0 + static_cast<int>(c) * 8;
-    const uint32_t off = gk < K ? (r * static_cast<uint32_t>(K) + static_cast<uint32_t>(gk)) * 2u : kOutside;
+    const uint32_t off = gk < kl ? (r * static_cast<uint32_t>(K) + static_cast<uint32_t>(gk)) * 2u : kOutside;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(dst_rows + blk * 1024), 16, off, 0, 0, 0);
   };
   auto issue = [&](GemmStage& stg, int k0) {
@@ -162,7 +168,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(const uint16
   // step q: wait for this wave's loads into stage q (those of stage q+1 may still be in flight),
   // barrier (every wave's have landed; every wave is done with the stage of step q-1), refill
   // that stage with step q+2, multiply stage q
-  const int nk = (K + kGemmBK - 1) / kGemmBK;
+  const int nk = (kl + kGemmBK - 1) / kGemmBK;
   auto step = [&](int q, GemmStage& cur, GemmStage& refill) {
     if (q + 1 < nk)
       wait_vmcnt<kGemmBlocksPerWave>();
@@ -188,7 +194,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(const uint16
   //      buffer over the output tile: rows past M fall outside its extent and are dropped,
   //      columns past N are pointed outside it. ----
   const uint32_t c_bytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x_rows) * static_cast<uint32_t>(N) * 4u);
-  const rsrc_t rC = make_rsrc_bytes(C + row0 * N + col0, c_bytes);
+  const rsrc_t rC = make_rsrc_bytes(C + static_cast<i64>(blockIdx.y) * c_split + row0 * N + col0, c_bytes);
   const int n_in = N - static_cast<int>(col0);  // columns of this tile inside C
 #pragma unroll
   for (int jn = 0; jn < 2; ++jn) {
@@ -207,19 +213,41 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(const uint16
   }
 }
 
+int gemm_tiles(i64 M, int N) {
+  return static_cast<int>(((M + kGemmBM - 1) / kGemmBM) * ((N + kGemmBN - 1) / kGemmBN));
+}
+
 hipError_t launch_gemm_bf16(const void* X, const void* W, const float* bias, float* C, i64 M,
-                            int N, int K, hipStream_t stream) {
+                            int N, int K, hipStream_t stream, int splits) {
   const i64 tiles_m = (M + kGemmBM - 1) / kGemmBM;
   const i64 tiles_n = (N + kGemmBN - 1) / kGemmBN;
   const i64 blocks = tiles_m * tiles_n;
   // operand and output tiles are addressed with 32-bit byte offsets below kOutside
   if (blocks > 0x7fffffffLL || M > 0x7fffffffLL || static_cast<i64>(kGemmBM) * K * 2 >= kOutside ||
-      static_cast<i64>(kGemmBM) * N * 4 >= kOutside)
+      static_cast<i64>(kGemmBM) * N * 4 >= kOutside || splits < 1 || splits > 65535)
     return hipErrorInvalidValue;
-  gemm_bf16_kernel<<<dim3(static_cast<unsigned>(blocks)), kGemmThreads, 0, stream>>>(
+  // K range per split: a whole number of K steps; every split gets at least one
+  const int k_split = ((K + splits - 1) / splits + kGemmBK - 1) / kGemmBK * kGemmBK;
+  const int used = (K + k_split - 1) / k_split;
+  if (used != splits) return hipErrorInvalidValue;
+  gemm_bf16_kernel<<<dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(splits)), kGemmThreads, 0, stream>>>(
       static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W), bias, C, static_cast<int>(M),
-      N, K, static_cast<int>(tiles_m), static_cast<int>(tiles_n));
+      N, K, static_cast<int>(tiles_m), static_cast<int>(tiles_n), k_split, M * static_cast<i64>(N));
   return hipGetLastError();
+}
+
+int gemm_splits_for(i64 M, int N, int K, int want) {
+  // the number of splits launch_gemm_bf16 accepts closest to want (each split a whole number of
+  // K steps, none empty)
+  int s = want < 1 ? 1 : want;
+  while (s > 1) {
+    const int k_split = ((K + s - 1) / s + kGemmBK - 1) / kGemmBK * kGemmBK;
+    if ((K + k_split - 1) / k_split == s) break;
+    --s;
+  }
+  (void)M;
+  (void)N;
+  return s;
 }
 
 }  // namespace slstm

@@ -70,15 +70,16 @@ hipError_t launch_warm_chain(const void* P, bool p_bf16, const float* state0, fl
                              int T, int d, bool sig_forget, unsigned long long* carry,
                              unsigned int* tickets, uint32_t epoch, hipStream_t stream);
 
-// backward (adjoint + cell VJP) as chains or as a scan along T, then the fixed-order sum of
-// dR over its rows; rows holds backward_row_floats floats
+// backward (adjoint + cell VJP) as chains or as a scan along T, then the fixed-order sums of
+// dR and dbias over the tiles' rows; rows holds backward_row_floats floats
 size_t backward_desc_words(int B, int T, int d, bool scan);
 size_t backward_row_floats(int B, int T, int d, bool scan);
 hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const float* state0,
                            const float* S, const float* g, const float* g_h, const float* g_final,
-                           float* dP, float* dR, float* dstate0, float* rows, int B, int T, int d,
-                           bool sig_forget, bool scan, unsigned long long* desc,
-                           unsigned int* tickets, uint32_t epoch, hipStream_t stream);
+                           void* dP, bool dp_bf16, float* dR, float* dbias, float* dstate0,
+                           float* rows, int B, int T, int d, bool sig_forget, bool scan,
+                           unsigned long long* desc, unsigned int* tickets, uint32_t epoch,
+                           hipStream_t stream);
 
 hipError_t launch_update(float* S, const float* D, i64 n_floats, Control* ctl, int k_iter,
                          hipStream_t stream);
@@ -94,7 +95,19 @@ hipError_t launch_sequential(const void* P, bool p_bf16, const float* R, const f
                              float* S, float* h_out, float* final_state, int B, int T, int d,
                              bool sig_forget, hipStream_t stream);
 
+// C = X W^T (+ bias) in bf16 MFMA with float32 accumulation; X (M x K), W (N x K), both
+// K-contiguous. With splits > 1 the K range is split and split s writes its partial product to
+// C + s * M * N (bias must then be null); gemm_splits_for gives an accepted split count.
 hipError_t launch_gemm_bf16(const void* X, const void* W, const float* bias, float* C, i64 M,
-                            int N, int K, hipStream_t stream);
+                            int N, int K, hipStream_t stream, int splits = 1);
+int gemm_tiles(i64 M, int N);
+int gemm_splits_for(i64 M, int N, int K, int want);
+
+// operand preparation for the weight-gradient products (bfloat16, rounded to nearest even)
+hipError_t launch_transpose_bf16(const void* src, bool src_f32, uint16_t* dst, i64 rows, int cols,
+                                 i64 ld, hipStream_t stream);
+hipError_t launch_pad_bf16(const void* src, bool src_f32, uint16_t* dst, i64 rows, int cols, int ld,
+                           hipStream_t stream);
+hipError_t launch_sum_splits(const float* part, float* out, int splits, i64 n, hipStream_t stream);
 
 }  // namespace slstm

@@ -24,7 +24,7 @@ SCHEDULE = {"fused": 0, "layered": 1, "fused_scan": 2, "fused_chain": 3}
 MAX_ITERS = 64
 KERNELS = {"warm_start": 0, "residual_jacobian": 1, "scan_block4": 2, "update": 3,
            "final_residual": 4, "input_projection": 5, "sequential": 6, "newton_iteration": 7,
-           "newton_solve": 8, "backward": 9}
+           "newton_solve": 8, "backward": 9, "weight_gradient": 10, "input_gradient": 11}
 
 EXPORTED = [
     "slstm_status_string", "slstm_last_error", "slstm_newton_workspace_bytes",
@@ -33,6 +33,7 @@ EXPORTED = [
     "slstm_scan_block4", "slstm_warm_start_workspace_bytes", "slstm_warm_start",
     "slstm_profile_enable", "slstm_profile_reset", "slstm_profile_read",
     "slstm_profile_durations", "slstm_backward_workspace_bytes", "slstm_backward",
+    "slstm_input_projection_backward_workspace_bytes", "slstm_input_projection_backward",
 ]
 
 
@@ -110,8 +111,13 @@ def load(path: str | None = None):
     L.slstm_backward_workspace_bytes.restype = _sz
     L.slstm_backward_workspace_bytes.argtypes = [_i, _i, _i, _i]
     L.slstm_backward.restype = _i
-    L.slstm_backward.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
-                                 _i, _i, _vp, _sz, _vp]
+    L.slstm_backward.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp,
+                                 _i, _i, _i, _i, _i, _vp, _sz, _vp]
+    L.slstm_input_projection_backward_workspace_bytes.restype = _sz
+    L.slstm_input_projection_backward_workspace_bytes.argtypes = [_i, _i, _i, _i]
+    L.slstm_input_projection_backward.restype = _i
+    L.slstm_input_projection_backward.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _vp,
+                                                  _sz, _vp]
     L.slstm_profile_enable.restype = _i
     L.slstm_profile_enable.argtypes = [_i]
     L.slstm_profile_reset.restype = _i
@@ -335,10 +341,12 @@ def backward_workspace_bytes(B: int, T: int, d_h: int, schedule: str = "fused") 
 
 def backward(P, R, states, state0=None, g_states=None, g_h=None, g_final=None, forget="exp",
              dP=None, dR=None, dstate0=None, want_dstate0=True, workspace=None, stream=None,
-             schedule="fused"):
+             schedule="fused", dP_dtype=torch.float32, dbias=None, want_dbias=False):
     """Gradients through the recurrence at the forward solution ``states`` (B,T,4,d_h).
     g_states (B,T,4,d_h), g_h (B,T,d_h) and g_final (B,4,d_h) are the loss's direct gradients
-    (None: zeros). Returns (dP (B,T,4,d_h), dR (4,d_h), dstate0 (B,4,d_h) or None)."""
+    (None: zeros). dP is float32 or bfloat16 (``dP_dtype``). Returns (dP (B,T,4,d_h),
+    dR (4,d_h), dstate0 (B,4,d_h) or None), and dbias (4,d_h) last when ``want_dbias`` or a
+    ``dbias`` tensor is given."""
     L = load()
     _dev(P, "P", (torch.float32, torch.bfloat16))
     _dev(R, "R", (torch.float32,))
@@ -350,23 +358,61 @@ def backward(P, R, states, state0=None, g_states=None, g_h=None, g_final=None, f
         if t is not None and tuple(t.shape) != shape:
             raise ValueError(f"{name} must be {shape}, got {tuple(t.shape)}")
     if dP is None:
-        dP = torch.empty((B, T, 4, d), dtype=torch.float32, device=P.device)
+        dP = torch.empty((B, T, 4, d), dtype=dP_dtype, device=P.device)
+    if want_dbias and dbias is None:
+        dbias = torch.empty((4, d), dtype=torch.float32, device=P.device)
     if dR is None:
         dR = torch.empty((4, d), dtype=torch.float32, device=P.device)
     if want_dstate0 and dstate0 is None:
         dstate0 = torch.empty((B, 4, d), dtype=torch.float32, device=P.device)
-    _dev(dP, "dP", (torch.float32,))
+    _dev(dP, "dP", (torch.float32, torch.bfloat16))
     _dev(dR, "dR", (torch.float32,))
+    _dev(dbias, "dbias", (torch.float32,))
     _dev(dstate0, "dstate0", (torch.float32,))
     need = L.slstm_backward_workspace_bytes(B, T, d, SCHEDULE[schedule])
     if workspace is None:
         workspace = alloc_workspace(need, P.device)
     status = L.slstm_backward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
-                              _ptr(g_states), _ptr(g_h), _ptr(g_final), _ptr(dP), _ptr(dR),
+                              _ptr(g_states), _ptr(g_h), _ptr(g_final), _ptr(dP),
+                              BF16 if dP.dtype == torch.bfloat16 else F32, _ptr(dR), _ptr(dbias),
                               _ptr(dstate0), B, T, d, FORGET[forget], SCHEDULE[schedule],
                               _ptr(workspace), workspace.numel(), _stream(stream))
     _check(status, "slstm_backward")
+    if dbias is not None:
+        return dP, dR, dstate0, dbias
     return dP, dR, dstate0
+
+
+def input_projection_backward_workspace_bytes(B: int, T: int, d_in: int, d_h: int) -> int:
+    return int(load().slstm_input_projection_backward_workspace_bytes(B, T, d_in, d_h))
+
+
+def input_projection_backward(x, W, dP, dx=None, dW=None, want_dx=True, want_dW=True,
+                              workspace=None, stream=None):
+    """dW_x = dP^T x and dx = dP W_x on MFMA (bf16 operands, float32 results). x (B,T,d_in) bf16,
+    W (4,d_h,d_in) bf16, dP (B,T,4,d_h) float32 or bf16. Returns (dx or None, dW or None)."""
+    L = load()
+    _dev(x, "x", (torch.bfloat16,))
+    _dev(W, "W_x", (torch.bfloat16,))
+    _dev(dP, "dP", (torch.float32, torch.bfloat16))
+    B, T, d_in = x.shape
+    g, d, d_in2 = W.shape
+    if g != 4 or d_in2 != d_in or tuple(dP.shape) != (B, T, 4, d):
+        raise ValueError(f"shapes: x {tuple(x.shape)}, W_x {tuple(W.shape)}, dP {tuple(dP.shape)}")
+    if want_dx and dx is None:
+        dx = torch.empty((B, T, d_in), dtype=torch.float32, device=x.device)
+    if want_dW and dW is None:
+        dW = torch.empty((4, d, d_in), dtype=torch.float32, device=x.device)
+    _dev(dx, "dx", (torch.float32,))
+    _dev(dW, "dW", (torch.float32,))
+    need = L.slstm_input_projection_backward_workspace_bytes(B, T, d_in, d)
+    if workspace is None:
+        workspace = alloc_workspace(need, x.device)
+    status = L.slstm_input_projection_backward(
+        _ptr(x), _ptr(W), _ptr(dP), BF16 if dP.dtype == torch.bfloat16 else F32, _ptr(dx), _ptr(dW),
+        B, T, d_in, d, _ptr(workspace), workspace.numel(), _stream(stream))
+    _check(status, "slstm_input_projection_backward")
+    return dx, dW
 
 
 def profile_enable(on: bool = True):

@@ -343,6 +343,33 @@ def pin_input_projection(ref):
                     assert abs(P[b, t, g, j] - acc) < 1e-12
 
 
+def pin_input_projection_backward(ref):
+    """dW, dx, dbias of L = sum dP * input_projection(x, W, b): L is linear in each of W, x and
+    b, so a central difference along any direction E equals <grad, E> up to rounding; and an
+    explicit loop on one entry of each."""
+    B, T, d_in, d_h = 2, 3, 5, 4
+    rng = np.random.Generator(np.random.PCG64(23))
+    x = rng.standard_normal((B, T, d_in))
+    W = rng.standard_normal((4, d_h, d_in))
+    b = rng.standard_normal((4, d_h))
+    dP = rng.standard_normal((B, T, 4, d_h))
+    dW, dx, db = ref.input_projection_backward(x, W, dP)
+    assert dW.shape == W.shape and dx.shape == x.shape and db.shape == b.shape
+    L = lambda x_, W_, b_: float(np.sum(dP * ref.input_projection(x_, W_, b_)))  # noqa: E731
+    for grad, arg in ((dW, 1), (dx, 0), (db, 2)):
+        E = rng.standard_normal(grad.shape)
+        args_p = [x, W, b]
+        args_m = [x, W, b]
+        args_p[arg] = args_p[arg] + 0.5 * E
+        args_m[arg] = args_m[arg] - 0.5 * E
+        fd = L(*args_p) - L(*args_m)
+        assert abs(fd - float(np.sum(grad * E))) < 1e-10 * (1.0 + abs(fd))
+    g, j, k, bb, t = 2, 3, 4, 1, 2
+    assert abs(dW[g, j, k] - sum(dP[p, s, g, j] * x[p, s, k] for p in range(B) for s in range(T))) < 1e-12
+    assert abs(dx[bb, t, k] - sum(dP[bb, t, q, i] * W[q, i, k] for q in range(4) for i in range(d_h))) < 1e-12
+    assert abs(db[g, j] - sum(dP[p, s, g, j] for p in range(B) for s in range(T))) < 1e-12
+
+
 def pin_state0_chunking(ref):
     """The final state carries a sequence: forward(T) = forward(T/2) then forward(T/2)
     from the carried state ('fused kernels prepend h0', 'Layout' page)."""

@@ -60,13 +60,13 @@ def test_workspace_sizes(lib):
     assert lib.slstm_warm_start_workspace_bytes(2, 64, 16, 9) == 0
     # tiny shapes still get a control block and one tile of look-back words
     assert lib.slstm_newton_workspace_bytes(1, 1, 1, 0) >= 512
-    # backward chains: 8 tagged words per lane and tile of 8 steps (8 B per state element) and
-    # per-batch-row dR sums; scan: 24 words per lane and tile of 32 steps (6 B) and one dR row
-    # per batch row and tile (0.5 B)
+    # backward chains: 4 tagged words per lane and tile of 8 steps (4 B per state element) and a
+    # row of 8 sums per lane and tile (4 B); scan: 24 words per lane and tile of 32 steps (6 B)
+    # and a row of 8 sums per lane and tile (1 B)
     nb = lib.slstm_backward_workspace_bytes(B, T, d, 3)
     assert 8 * B * T * d <= nb < 9 * B * T * d
     ns = lib.slstm_backward_workspace_bytes(B, T, d, 2)
-    assert 6 * B * T * d <= ns < 7 * B * T * d
+    assert 7 * B * T * d <= ns < 8 * B * T * d
     assert lib.slstm_backward_workspace_bytes(B, T, d, 0) == ns
     assert lib.slstm_backward_workspace_bytes(B, T, d, 1) == 0
     assert lib.slstm_backward_workspace_bytes(0, T, d, 0) == 0
@@ -115,7 +115,7 @@ def test_argument_checks_return_einval(lib):
 def _bwd(lib, **kw):
     args = dict(P=ctypes.c_void_p(256), dt=0, R=ctypes.c_void_p(256), s0=None,
                 S=ctypes.c_void_p(256), gs=None, gh=None, gf=None, dP=ctypes.c_void_p(256),
-                dR=ctypes.c_void_p(256), ds0=None, B=2, T=64, d=16, fm=0, sched=0,
+                dpt=0, dR=ctypes.c_void_p(256), db=None, ds0=None, B=2, T=64, d=16, fm=0, sched=0,
                 ws=ctypes.c_void_p(4096), wsb=1 << 30, stream=None)
     args.update(kw)
     return lib.slstm_backward(*args.values())
@@ -129,6 +129,8 @@ def test_backward_argument_checks(lib):
     assert _bwd(lib, dP=ctypes.c_void_p(264)) == slstm.EINVAL   # dP not 16-byte aligned
     assert _bwd(lib, gh=ctypes.c_void_p(258)) == slstm.EINVAL   # g_h misaligned
     assert _bwd(lib, fm=2) == slstm.EINVAL
+    assert _bwd(lib, dpt=3) == slstm.EINVAL
+    assert _bwd(lib, db=ctypes.c_void_p(258)) == slstm.EINVAL
     assert _bwd(lib, sched=1) == slstm.EINVAL
     assert "fused forms only" in lib.slstm_last_error().decode()
     assert _bwd(lib, sched=9) == slstm.EINVAL

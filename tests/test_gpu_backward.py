@@ -253,3 +253,89 @@ def test_backward_workload_full_size(gpu_lib, name):
         print(f"{w.name} full size backward ({part}): rel err {['%.2e' % e for e in errs]}, "
               f"undecided {int((~keep).sum())}/{keep.size}")
         assert max(errs) < GRAD_TOL
+
+
+# ---- dbias, bf16 dP and the input projection's gradients ----------------------------------------
+def test_backward_dbias_and_bf16_dP(gpu_lib, schedule):
+    B, T, d = 3, 75, 40
+    case(f"backward {schedule} dbias and bf16 dP B={B} T={T} d={d}")
+    P, R, s0, S = _problem(17, B, T, d, "exp", "f32", with_state0=True)
+    gs, gh, gf = (torch.from_numpy(a) for a in random_cotangents(18, B, T, d))
+    on = lambda t: t.to(DEV)  # noqa: E731
+    dP, dR, ds0, db = gpu_lib.backward(on(P), on(R), on(S), on(s0), on(gs), on(gh), on(gf), "exp",
+                                       schedule=schedule, want_dbias=True)
+    dPb, dRb, ds0b, dbb = gpu_lib.backward(on(P), on(R), on(S), on(s0), on(gs), on(gh), on(gf), "exp",
+                                           schedule=schedule, dP_dtype=torch.bfloat16, want_dbias=True)
+    torch.cuda.synchronize()
+    want = _oracle(P, R, s0, S, gs, gh, gf, "exp")
+    keep = _decided_lanes(to_np(P), to_np(R), to_np(s0), to_np(S), "exp")
+    _, _, db_ref = ref.input_projection_backward(np.zeros((B, T, 8)), np.zeros((4, d, 8)), want[0])
+    assert grad_rel_err(db, db_ref, np.all(keep, axis=0)[None, :]) < GRAD_TOL
+    # the bf16 output is the float32 dP rounded to nearest even; everything else is unchanged
+    assert torch.equal(dPb, dP.to(torch.bfloat16))
+    assert torch.equal(dRb, dR) and torch.equal(ds0b, ds0) and torch.equal(dbb, db)
+
+
+PROJ_SHAPES = [(2, 5, 8, 4), (3, 7, 24, 5), (1, 130, 40, 20), (2, 300, 72, 66)]
+
+
+@pytest.mark.parametrize("shape", PROJ_SHAPES)
+@pytest.mark.parametrize("dp_dtype", ["bf16", "f32"])
+def test_input_projection_backward_matches_oracle(gpu_lib, shape, dp_dtype):
+    """dW_x = dP^T x and dx = dP W_x. With bf16 dP both sides multiply the same bf16 values and
+    only the float32 accumulation differs (bar 1e-4); float32 dP is rounded to bf16 on the GPU
+    (the bf16 bar, 2e-2)."""
+    B, T, d_in, d_h = shape
+    case(f"input projection backward B={B} T={T} d_in={d_in} d_h={d_h} dP {dp_dtype}")
+    rng = np.random.Generator(np.random.PCG64(B * 1000 + T + d_in + d_h))
+    x = torch.from_numpy(rng.standard_normal((B, T, d_in)).astype(np.float32)).to(torch.bfloat16)
+    W = torch.from_numpy((rng.standard_normal((4, d_h, d_in)) / np.sqrt(d_in)).astype(np.float32)).to(torch.bfloat16)
+    dP = torch.from_numpy(rng.standard_normal((B, T, 4, d_h)).astype(np.float32))
+    if dp_dtype == "bf16":
+        dP = dP.to(torch.bfloat16)
+    dx, dW = gpu_lib.input_projection_backward(x.to(DEV), W.to(DEV), dP.to(DEV))
+    torch.cuda.synchronize()
+    dW_ref, dx_ref, _ = ref.input_projection_backward(to_np(x), to_np(W), to_np(dP))
+    tol = GRAD_TOL if dp_dtype == "bf16" else 2e-2
+    e_w, e_x = grad_rel_err(dW, dW_ref), grad_rel_err(dx, dx_ref)
+    print(f"input projection backward rel err: dW {e_w:.2e}, dx {e_x:.2e}")
+    assert e_w < tol and e_x < tol
+    # each output alone, and reproducible
+    dx2, none = gpu_lib.input_projection_backward(x.to(DEV), W.to(DEV), dP.to(DEV), want_dW=False)
+    none2, dW2 = gpu_lib.input_projection_backward(x.to(DEV), W.to(DEV), dP.to(DEV), want_dx=False)
+    torch.cuda.synchronize()
+    assert none is None and none2 is None
+    assert torch.equal(dx, dx2) and torch.equal(dW, dW2)
+
+
+def test_input_projection_backward_layer_full_size(gpu_lib):
+    """x (128, 2048, 1024), W_x (4, 1024, 1024), bf16 dP: sampled entries of dW_x (each a sum
+    over all 262,144 rows) and sampled rows of dx against the oracle on those entries."""
+    w = by_name("layer_b128_t2048_d1024")
+    B, T, d_in, d = w.B, w.T, w.d_in, w.d_h
+    case(f"input projection backward {w.name} full size")
+    from workloads import draw_layer_inputs
+    inp = draw_layer_inputs(w)
+    x, W = inp["x"].to(DEV), inp["W"].to(DEV)
+    dP = random_cotangents_device(w.seed + 21, B, T, d, DEV)[0].to(torch.bfloat16)
+    dx, dW = gpu_lib.input_projection_backward(x, W, dP)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(5))
+    gj = [(int(rng.integers(4)), int(rng.integers(d))) for _ in range(24)] + [(0, 0), (3, d - 1)]
+    ks = rng.integers(0, d_in, size=8).tolist() + [0, d_in - 1]
+    # the oracle on sub-problems: one (gate, feature) column of dP against the sampled columns of
+    # x gives dW[g, j, ks]; one row of dP against all of W_x gives dx[b, t]
+    xs = to_np(x[:, :, ks].cpu())
+    errs = []
+    for g, j in gj:
+        col = to_np(dP[:, :, g:g + 1, j:j + 1].cpu())
+        want, _, _ = ref.input_projection_backward(xs, np.zeros((1, 1, len(ks))), col)
+        got = to_np(dW[g, j, ks])
+        errs.append(grad_rel_err(got, want[0, 0]))
+    rows = [(int(rng.integers(B)), int(rng.integers(T))) for _ in range(12)] + [(0, 0), (B - 1, T - 1)]
+    Wn = to_np(W.cpu())
+    for b, t in rows:
+        _, want, _ = ref.input_projection_backward(np.zeros((1, 1, d_in)), Wn, to_np(dP[b:b + 1, t:t + 1].cpu()))
+        errs.append(grad_rel_err(dx[b, t], want[0, 0]))
+    print(f"input projection backward full size: max rel err {max(errs):.2e}")
+    assert max(errs) < GRAD_TOL

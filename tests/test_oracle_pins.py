@@ -46,6 +46,10 @@ MUTATIONS = [
      "lam = lam_prev"),
     ("backward: dR against h_t", "dR += np.sum(delta * prev[:, t, H][:, None, :], axis=0)",
      "dR += np.sum(delta * S[:, t, H][:, None, :], axis=0)"),
+    ("weight gradient: transposed operand", "dW = (dP2.T @ x.reshape(B * T, d_in)).reshape(g, d_h, d_in)",
+     "dW = (dP2.T @ x.reshape(B * T, d_in)[::-1]).reshape(g, d_h, d_in)"),
+    ("input gradient: gate rows swapped", "dx = (dP2 @ W.reshape(g * d_h, d_in)).reshape(B, T, d_in)",
+     "dx = (dP2 @ W[::-1].reshape(g * d_h, d_in)).reshape(B, T, d_in)"),
     ("gate Jacobian: forget derivative", "dfg_df = fg * (dlf - dm_df)", "dfg_df = fg * (1.0 - dm_df)"),
     ("gate Jacobian: output-gate term", "dh[GO] = dh[GO] + (c / n) * o * (1.0 - o)", "dh[GO] = dh[GO]"),
 ]
