@@ -81,7 +81,7 @@ def kernel_work(w, n_e, p_bytes):
         "newton_iteration": {"bound": "hbm", "bytes": n_e * (p_bytes + 16 + 16)},             # P, S_k in; S_k+1 out
         "newton_solve": {"bound": "alu", "bytes": n_e * (p_bytes + 16 + 4),                   # P in; S_K, h out
                          "flops": n_e * solve_flops_per_elem(w.max_iters, w.forget == "sigmoid")},
-        "backward": {"bound": "hbm", "bytes": n_e * (p_bytes + 16 + 4 + 16)},                 # P, S, dL/dh in; dP out
+        "backward": {"bound": "hbm", "bytes": n_e * (p_bytes + 16 + 4 + 8)},                  # P, S, dL/dh in; bf16 dP out
     }
 
 
@@ -393,16 +393,25 @@ def main():
 
     if not args.no_backward_context:
         # the backward pass at the forward solution for a loss on h (dL/dh ~ N(0, 1) and a
-        # final-state gradient): dP, dR, dstate0; not part of the metric
+        # final-state gradient): dP (bf16), dR, dbias, dstate0, and for the full layer dW_x and
+        # dx from the input projection's backward; not part of the metric
         from workloads import random_cotangents_device
         _, g_h, g_fin = random_cotangents_device(w.seed + 99, w.B, w.T, w.d_h, dev)
-        dP = torch.empty((w.B, w.T, 4, w.d_h), dtype=torch.float32, device=dev)
+        dP = torch.empty((w.B, w.T, 4, w.d_h), dtype=torch.bfloat16, device=dev)
         dR = torch.empty((4, w.d_h), dtype=torch.float32, device=dev)
+        db = torch.empty((4, w.d_h), dtype=torch.float32, device=dev)
         d0 = torch.empty((w.B, 4, w.d_h), dtype=torch.float32, device=dev)
         bws = slstm.alloc_workspace(slstm.backward_workspace_bytes(w.B, w.T, w.d_h), dev)
+        if w.on_gpu_gemm:
+            dx = torch.empty((w.B, w.T, w.d_in), dtype=torch.float32, device=dev)
+            dW = torch.empty((4, w.d_h, w.d_in), dtype=torch.float32, device=dev)
+            pws = slstm.alloc_workspace(slstm.input_projection_backward_workspace_bytes(w.B, w.T, w.d_in, w.d_h), dev)
 
         def bwd():
-            slstm.backward(P, R, S, None, None, g_h, g_fin, w.forget, dP=dP, dR=dR, dstate0=d0, workspace=bws)
+            slstm.backward(P, R, S, None, None, g_h, g_fin, w.forget, dP=dP, dR=dR, dstate0=d0, dbias=db,
+                           workspace=bws)
+            if w.on_gpu_gemm:
+                slstm.input_projection_backward(x, W, dP, dx=dx, dW=dW, workspace=pws)
 
         bwd()
         torch.cuda.synchronize()
@@ -418,16 +427,28 @@ def main():
         bd = slstm.profile_durations("backward")
         bk = sum(bd) / len(bd)
         gbs = work["backward"]["bytes"] / (bk * 1e-3) / 1e9
-        log(f"[bench] backward: {b_ms:.3f} ms per call, kernels {bk:.3f} ms, {gbs:.0f} GB/s algorithmic")
+        log(f"[bench] backward: {b_ms:.3f} ms per call, recurrence kernels {bk:.3f} ms, {gbs:.0f} GB/s algorithmic")
         context["backward"] = {"ms": round(b_ms, 4), "state_elems_per_s": n_e / (b_ms * 1e-3),
                                "gradients_in": "dL/dh, dL/d final state", "form": "scan",
-                               "roofline": {"bound": "hbm", "kernel": "backward", "achieved": round(gbs, 1),
-                                            "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                            "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                            "traffic": measured_traffic("backward", w.name)},
-                               "kernel_avg_ms": round(bk, 4),
-                               "bytes_per_launch": work["backward"]["bytes"]}
-        del dP, dR, d0, bws, g_h, g_fin
+                               "recurrence": {"kernel_avg_ms": round(bk, 4),
+                                              "bytes_per_launch": work["backward"]["bytes"],
+                                              "roofline": {"bound": "hbm", "kernel": "backward",
+                                                           "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                                                           "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                                           "traffic": measured_traffic("backward", w.name)}}}
+        if w.on_gpu_gemm:
+            flops = 2.0 * w.B * w.T * 4 * w.d_h * w.d_in
+            for kind in ("weight_gradient", "input_gradient"):
+                kd = slstm.profile_durations(kind)
+                kavg = sum(kd) / len(kd)
+                tf = flops / (kavg * 1e-3) / 1e12
+                context["backward"][kind] = {"ms": round(kavg, 4), "flops_per_launch": flops,
+                                             "roofline": {"bound": "mfma", "achieved": round(tf, 1),
+                                                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                                          "frac": round(tf / BF16_PEAK_TFLOPS, 4)}}
+                log(f"[bench] backward {kind}: {kavg:.3f} ms, {tf:.0f} TFLOP/s (operand transposes included)")
+            del dx, dW, pws
+        del dP, dR, db, d0, bws, g_h, g_fin
         torch.cuda.empty_cache()
 
     if not args.no_sequential_context:

@@ -366,9 +366,13 @@ ProjBackLayout proj_back_layout(int B, int T, int d_in, int d_h) {
   const i64 n4 = 4 * static_cast<i64>(d_h);
   L.k_bt = pad8(bt);
   L.k_4d = pad8(n4);
-  // enough workgroups for two per compute unit, each split at least 32 K steps long
+  // enough workgroups for SLSTM_DW_WAVES rounds of two per compute unit, each split at least
+  // 32 K steps long
+#ifndef SLSTM_DW_WAVES
+#define SLSTM_DW_WAVES 1
+#endif
   const int tiles = slstm::gemm_tiles(n4, d_in);
-  int want = (2 * device_cus() + tiles - 1) / tiles;
+  int want = (SLSTM_DW_WAVES * 2 * device_cus() + tiles - 1) / tiles;
   want = std::min<i64>(want, std::max<i64>(1, L.k_bt / 1024));
   L.splits = slstm::gemm_splits_for(n4, d_in, static_cast<int>(L.k_bt), std::min(want, 64));
   L.dPb = 0;

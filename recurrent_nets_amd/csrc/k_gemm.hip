@@ -18,8 +18,10 @@
 // Rows past M or N read zero (buffer loads against the tile's extent); a K tail is pointed
 // outside the extent, which also reads zero. The bias is added in the epilogue, so P is written
 // once. The same kernel serves the weight-gradient products of the backward pass, whose
-// reduction length (B*T) is long and whose output is small: there the K range is split over
-// gridDim.y and each split writes its partial product to its own slice of C. Workgroups are renumbered so that each of the 8 XCDs works through a contiguous range of
+// reduction length (B*T) is long and whose output is small: there the K range is split and each
+// split writes its partial product to its own slice of C. Splits are numbered with the tiles,
+// split-major, so each XCD's contiguous range of work covers one K range: the workgroups an XCD
+// runs together read the same K slices of their row and column panels from its L2. Workgroups are renumbered so that each of the 8 XCDs works through a contiguous range of
 // tiles, ordered in groups of row panels so that the tiles an XCD runs together share row and
 // column panels in its L2.
 #include "common.h"
@@ -83,7 +85,10 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(const uint16
   // ---- tile selection: XCD-contiguous ranges, grouped row panels ----
   const int nb = gridDim.x;
   const int bid = blockIdx.x;
-  const int logical = (nb % kXcds == 0) ? (bid % kXcds) * (nb / kXcds) + bid / kXcds : bid;
+  const int logical_all = (nb % kXcds == 0) ? (bid % kXcds) * (nb / kXcds) + bid / kXcds : bid;
+  const int n_tiles = tiles_m * tiles_n;
+  const int split = logical_all / n_tiles;
+  const int logical = logical_all - split * n_tiles;
   const int per_group = kGemmGroupM * tiles_n;
   const int group = logical / per_group;
   const int in_group = logical % per_group;
@@ -101,7 +106,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(const uint16
   const i64 row0 = static_cast<i64>(tm) * kGemmBM;
   const i64 col0 = static_cast<i64>(tn) * kGemmBN;
   // this split's range of K: [kb, kb + kl)
-  const int kb = static_cast<int>(blockIdx.y) * k_split;
+  const int kb = split * k_split;
   const int kl = min(k_split, K - kb);
   // extents of the operand tiles (uniform; integer selects keep them in scalar registers)
   const int x_rows = (M - row0 < kGemmBM) ? static_cast<int>(M - row0) : kGemmBM;
@@ -194,7 +199,7 @@ __global__ __launch_bounds__(kGemmThreads, 2) void gemm_bf16_kernel(const uint16
   //      buffer over the output tile: rows past M fall outside its extent and are dropped,
   //      columns past N are pointed outside it. ----
   const uint32_t c_bytes = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(x_rows) * static_cast<uint32_t>(N) * 4u);
-  const rsrc_t rC = make_rsrc_bytes(C + static_cast<i64>(blockIdx.y) * c_split + row0 * N + col0, c_bytes);
+  const rsrc_t rC = make_rsrc_bytes(C + static_cast<i64>(split) * c_split + row0 * N + col0, c_bytes);
   const int n_in = N - static_cast<int>(col0);  // columns of this tile inside C
 #pragma unroll
   for (int jn = 0; jn < 2; ++jn) {
@@ -221,16 +226,16 @@ hipError_t launch_gemm_bf16(const void* X, const void* W, const float* bias, flo
                             int N, int K, hipStream_t stream, int splits) {
   const i64 tiles_m = (M + kGemmBM - 1) / kGemmBM;
   const i64 tiles_n = (N + kGemmBN - 1) / kGemmBN;
-  const i64 blocks = tiles_m * tiles_n;
+  const i64 blocks = tiles_m * tiles_n * splits;
   // operand and output tiles are addressed with 32-bit byte offsets below kOutside
-  if (blocks > 0x7fffffffLL || M > 0x7fffffffLL || static_cast<i64>(kGemmBM) * K * 2 >= kOutside ||
-      static_cast<i64>(kGemmBM) * N * 4 >= kOutside || splits < 1 || splits > 65535)
+  if (splits < 1 || blocks > 0x7fffffffLL || M > 0x7fffffffLL || static_cast<i64>(kGemmBM) * K * 2 >= kOutside ||
+      static_cast<i64>(kGemmBM) * N * 4 >= kOutside)
     return hipErrorInvalidValue;
   // K range per split: a whole number of K steps; every split gets at least one
   const int k_split = ((K + splits - 1) / splits + kGemmBK - 1) / kGemmBK * kGemmBK;
   const int used = (K + k_split - 1) / k_split;
   if (used != splits) return hipErrorInvalidValue;
-  gemm_bf16_kernel<<<dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(splits)), kGemmThreads, 0, stream>>>(
+  gemm_bf16_kernel<<<dim3(static_cast<unsigned>(blocks)), kGemmThreads, 0, stream>>>(
       static_cast<const uint16_t*>(X), static_cast<const uint16_t*>(W), bias, C, static_cast<int>(M),
       N, K, static_cast<int>(tiles_m), static_cast<int>(tiles_n), k_split, M * static_cast<i64>(N));
   return hipGetLastError();

@@ -24,32 +24,85 @@ __device__ __forceinline__ float load_elem(const void* src, i64 idx) {
   }
 }
 
-// dst[c, r] = src[r, c] for a rows x cols source; dst rows are ld long, r >= rows is zero.
-// Grid: x over 64-row bands of dst's columns (source rows, padding included), y over 64-column
-// bands of the source. Reads and writes are each 64 consecutive elements per wave.
+// dst[c, r] = src[r, c] for a rows x cols source; dst rows are ld long (ld a multiple of 8),
+// r >= rows is zero. Grid: x over 64-row bands of the source (dst's columns, padding included),
+// y over 64-column bands. A 64 x 64 tile goes through LDS as bfloat16: loads of 16 bytes along
+// the source rows (scalar loads where the rows are not whole 16-byte chunks), then each thread
+// gathers two adjacent columns of 8 consecutive rows (8 LDS words) and writes two 16-byte chunks
+// of dst rows.
 template <bool SRC_F32>
 __global__ __launch_bounds__(256) void transpose_bf16_kernel(const void* __restrict__ src,
                                                              uint16_t* __restrict__ dst, i64 rows,
                                                              int cols, i64 ld) {
-  __shared__ float tile[kTile][kTile + 1];
-  const int tx = threadIdx.x & 63;
-  const int ty = threadIdx.x >> 6;  // 0..3
+  constexpr int kLdsRow = kTile + 8;  // 144-byte rows: 16-byte aligned, spread over banks
+  __shared__ __attribute__((aligned(16))) uint16_t tile[kTile][kLdsRow];
+  const int tid = threadIdx.x;
   const i64 r0 = static_cast<i64>(blockIdx.x) * kTile;
   const int c0 = static_cast<int>(blockIdx.y) * kTile;
+  if constexpr (SRC_F32) {
+    const float* s = static_cast<const float*>(src);
 #pragma unroll
-  for (int k = 0; k < kTile / 4; ++k) {
-    const int rr = ty + 4 * k;
-    const i64 r = r0 + rr;
-    const int c = c0 + tx;
-    tile[rr][tx] = (r < rows && c < cols) ? load_elem<SRC_F32>(src, r * cols + c) : 0.0f;
+    for (int k = 0; k < 4; ++k) {
+      const int q = tid + 256 * k;  // 1024 chunks of 4
+      const int rr = q >> 4, cc = (q & 15) * 4;
+      const i64 r = r0 + rr;
+      const int c = c0 + cc;
+      float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (r < rows) {
+        if (c + 4 <= cols && (cols & 3) == 0) {
+          const float4 f = *reinterpret_cast<const float4*>(s + r * cols + c);
+          v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (c + e < cols) v[e] = s[r * cols + c + e];
+        }
+      }
+      uint2 packed;
+      packed.x = static_cast<uint32_t>(f32_to_bf16_rne(v[0])) | (static_cast<uint32_t>(f32_to_bf16_rne(v[1])) << 16);
+      packed.y = static_cast<uint32_t>(f32_to_bf16_rne(v[2])) | (static_cast<uint32_t>(f32_to_bf16_rne(v[3])) << 16);
+      *reinterpret_cast<uint2*>(&tile[rr][cc]) = packed;
+    }
+  } else {
+    const uint16_t* s = static_cast<const uint16_t*>(src);
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int q = tid + 256 * k;  // 512 chunks of 8
+      const int rr = q >> 3, cc = (q & 7) * 8;
+      const i64 r = r0 + rr;
+      const int c = c0 + cc;
+      uint4 v = {0u, 0u, 0u, 0u};
+      if (r < rows) {
+        if (c + 8 <= cols && (cols & 7) == 0) {
+          v = *reinterpret_cast<const uint4*>(s + r * cols + c);
+        } else {
+          uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (c + e < cols) w[e >> 1] |= static_cast<uint32_t>(s[r * cols + c + e]) << (16 * (e & 1));
+          v = {w[0], w[1], w[2], w[3]};
+        }
+      }
+      *reinterpret_cast<uint4*>(&tile[rr][cc]) = v;
+    }
   }
   __syncthreads();
+  // thread: columns cc, cc + 1 of the tile (two dst rows), source rows rq .. rq + 7
+  const int cc = 2 * (tid >> 3);
+  const int rq = (tid & 7) * 8;
+  uint32_t lo[4], hi[4];
 #pragma unroll
-  for (int k = 0; k < kTile / 4; ++k) {
-    const int cc = ty + 4 * k;
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t a = *reinterpret_cast<const uint32_t*>(&tile[rq + 2 * i][cc]);
+    const uint32_t b = *reinterpret_cast<const uint32_t*>(&tile[rq + 2 * i + 1][cc]);
+    lo[i] = (a & 0xffffu) | (b << 16);            // column cc, rows rq + 2i, rq + 2i + 1
+    hi[i] = (a >> 16) | (b & 0xffff0000u);        // column cc + 1
+  }
+  const i64 r = r0 + rq;
+  if (r < ld) {
     const int c = c0 + cc;
-    const i64 r = r0 + tx;
-    if (c < cols && r < ld) dst[static_cast<i64>(c) * ld + r] = f32_to_bf16_rne(tile[tx][cc]);
+    if (c < cols) *reinterpret_cast<uint4*>(dst + static_cast<i64>(c) * ld + r) = {lo[0], lo[1], lo[2], lo[3]};
+    if (c + 1 < cols) *reinterpret_cast<uint4*>(dst + static_cast<i64>(c + 1) * ld + r) = {hi[0], hi[1], hi[2], hi[3]};
   }
 }
 
@@ -80,7 +133,7 @@ hipError_t launch_transpose_bf16(const void* src, bool src_f32, uint16_t* dst, i
                                  i64 ld, hipStream_t stream) {
   const i64 gx = (ld + kTile - 1) / kTile;
   const i64 gy = (cols + kTile - 1) / kTile;
-  if (gx > 0x7fffffffLL || gy > 65535 || ld < rows) return hipErrorInvalidValue;
+  if (gx > 0x7fffffffLL || gy > 65535 || ld < rows || ld % 8 != 0) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(gx), static_cast<unsigned>(gy));
   if (src_f32)
     transpose_bf16_kernel<true><<<grid, 256, 0, stream>>>(src, dst, rows, cols, ld);
