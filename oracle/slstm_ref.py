@@ -54,6 +54,12 @@ import numpy as np
 
 FORGET_EXP = "exp"
 FORGET_SIGMOID = "sigmoid"
+# A forget-gate name may carry the read-out variant after a slash: "exp/floored",
+# "sigmoid/floored" select h = o c / max(|n|, e^{-m}, READOUT_FLOOR) (the educational page,
+# "Exponential gating + the stabilizer (the crux)" and "Implementation notes / deviations"
+# item 1) instead of the paper's h = o c / n.
+FLOORED = "/floored"
+READOUT_FLOOR = 1e-6
 INIT_WARM = "warm"
 INIT_ZERO = "zero"
 
@@ -74,6 +80,14 @@ def sigmoid(x):
     return np.exp(-_softplus(-x))
 
 
+def cell_mode(forget):
+    """(forget-gate form, floored read-out?) of a cell-mode name such as "sigmoid/floored"."""
+    base, _, variant = forget.partition("/")
+    if variant not in ("", "floored"):
+        raise ValueError(f"unknown read-out variant {variant!r}")
+    return base, variant == "floored"
+
+
 def log_forget(f_tilde, forget):
     """log f_t and its derivative d log f / d f_tilde.
 
@@ -82,6 +96,7 @@ def log_forget(f_tilde, forget):
     (summary card, "Method" item 1; the educational page writes the stabiliser in terms of
     log f so it covers both).
     """
+    forget, _ = cell_mode(forget)
     if forget == FORGET_EXP:
         return f_tilde, np.ones_like(f_tilde)
     if forget == FORGET_SIGMOID:
@@ -117,13 +132,31 @@ def _step(prev, p, r, forget):
     fg = np.exp(a - m)
     c = fg * c0 + ig * z
     n = fg * n0 + ig
-    h = o * c / n  # read-out
-    return {"z": z, "o": o, "dlf": dlf, "beta": beta, "m": m, "ig": ig, "fg": fg, "c": c, "n": n, "h": h}
+    D, dD_dn, dD_dm = _readout_denominator(n, m, cell_mode(forget)[1])
+    h = o * c / D  # read-out
+    return {"z": z, "o": o, "dlf": dlf, "beta": beta, "m": m, "ig": ig, "fg": fg, "c": c, "n": n, "h": h,
+            "D": D, "dD_dn": dD_dn, "dD_dm": dD_dm}
 
 
-def _quotient_row(o, c, n, dc, dn):
-    """Derivatives of h = o c / n through c and n (quotient rule), one per column."""
-    return [(o / n) * dc[k] - (o * c / (n * n)) * dn[k] for k in range(len(dc))]
+def _readout_denominator(n, m, floored):
+    """D of the read-out h = o c / D and its derivatives in n and m: D = n (the paper's sLSTM
+    step), or D = max(|n|, e^{-m}, READOUT_FLOOR) with the derivative of the branch the max
+    takes (ties go to |n|, then to e^{-m})."""
+    if not floored:
+        return n, np.ones_like(n), np.zeros_like(n)
+    an = np.abs(n)
+    em = np.exp(-m)
+    on_n = (an >= em) & (an >= READOUT_FLOOR)
+    on_m = ~on_n & (em >= READOUT_FLOOR)
+    D = np.where(on_n, an, np.where(on_m, em, READOUT_FLOOR))
+    return D, np.where(on_n, np.sign(n), 0.0), np.where(on_m, -em, 0.0)
+
+
+def _readout_row(v, dc, dn, dm):
+    """Derivatives of h = o c / D(n, m) through c, n and m (quotient rule), one per column."""
+    o, c, D = v["o"], v["c"], v["D"]
+    q = o * c / (D * D)
+    return [(o / D) * dc[k] - q * (v["dD_dn"] * dn[k] + v["dD_dm"] * dm[k]) for k in range(len(dc))]
 
 
 def cell(prev, p, r, forget, with_jacobian=False):
@@ -141,6 +174,7 @@ def cell(prev, p, r, forget, with_jacobian=False):
       a = l + m',  m = max(a, i~)                         (stabiliser, running max)
       i' = exp(i~ - m),  f' = exp(a - m)                  (both in (0, 1])
       c = f' c' + i' z,  n = f' n' + i',  h = o c / n
+    (h = o c / max(|n|, e^{-m}, READOUT_FLOOR) for a "/floored" cell mode).
     """
     v = _step(prev, p, r, forget)
     c0, n0 = prev[..., C, :], prev[..., N, :]
@@ -165,9 +199,9 @@ def cell(prev, p, r, forget, with_jacobian=False):
     dc = [fg, zero, c0 * dfg_dm + z * dig_dm, c0 * dfg_dh + z * dig_dh + ig * dz_dh]
     dn = [zero, fg, n0 * dfg_dm + dig_dm, n0 * dfg_dh + dig_dh]
     dmr = [zero, zero, dm_dm, dm_dh]
-    # row h = o c / n by the quotient rule, plus the output-gate term on h'
-    dh = _quotient_row(o, c, n, dc, dn)
-    dh[H] = dh[H] + (c / n) * do_dh
+    # row h = o c / D by the quotient rule, plus the output-gate term on h'
+    dh = _readout_row(v, dc, dn, dmr)
+    dh[H] = dh[H] + (c / v["D"]) * do_dh
     A = np.stack([np.stack(row, axis=-2) for row in (dc, dn, dmr, dh)], axis=-3)
     return nxt, A
 
@@ -197,8 +231,8 @@ def gate_jacobian(prev, p, r, forget):
     dc = [ig * (1.0 - z * z), c0 * dfg_di + z * dig_di, c0 * dfg_df + z * dig_df, zero]
     dn = [zero, n0 * dfg_di + dig_di, n0 * dfg_df + dig_df, zero]
     dmr = [zero, dm_di, dm_df, zero]
-    dh = _quotient_row(o, c, n, dc, dn)
-    dh[GO] = dh[GO] + (c / n) * o * (1.0 - o)
+    dh = _readout_row(v, dc, dn, dmr)
+    dh[GO] = dh[GO] + (c / v["D"]) * o * (1.0 - o)
     return np.stack([np.stack(row, axis=-2) for row in (dc, dn, dmr, dh)], axis=-3)
 
 
@@ -239,13 +273,15 @@ def sequential(P, R, state0, forget):
     return out
 
 
-def unstabilised_hidden(P, R, forget):
+def unstabilised_hidden(P, R, forget, floored=False):
     """h from the unstabilised recurrence, zero initial state.
 
     c_t = f_t c_{t-1} + i_t z_t, n_t = f_t n_{t-1} + i_t, h_t = o_t c_t / n_t with
     i_t = exp(i~), f_t = exp(f~) or sigma(f~). The paper states that the stabilised and
-    unstabilised forms give identical outputs (summary card, "Method" item 1). Overflows
-    for long sequences; used only on short ones.
+    unstabilised forms give identical outputs (summary card, "Method" item 1). With floored,
+    h_t = o_t c_t / max(|n_t|, 1): the floor e^{-m} of the stabilised read-out is 1 in the
+    unstabilised domain (educational page, "Implementation notes / deviations" item 1).
+    Overflows for long sequences; used only on short ones.
     """
     P = np.asarray(P, dtype=np.float64)
     R = np.asarray(R, dtype=np.float64)
@@ -261,11 +297,11 @@ def unstabilised_hidden(P, R, forget):
         z = np.tanh(pt[:, GZ] + R[GZ] * h)
         i = np.exp(pt[:, GI] + R[GI] * h)
         ft = pt[:, GF] + R[GF] * h
-        f = np.exp(ft) if forget == FORGET_EXP else sigmoid(ft)
+        f = np.exp(ft) if cell_mode(forget)[0] == FORGET_EXP else sigmoid(ft)
         o = sigmoid(pt[:, GO] + R[GO] * h)
         c = f * c + i * z
         n = f * n + i
-        h = o * c / n
+        h = o * c / (np.maximum(np.abs(n), 1.0) if floored else n)
         hs[:, t], cs[:, t], ns[:, t] = h, c, n
     return hs, cs, ns
 

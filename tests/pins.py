@@ -93,6 +93,23 @@ def pin_unstabilised_equivalence(ref):
                                    err_msg=forget)
 
 
+def pin_floored_readout_unstabilised(ref):
+    """The floored read-out h = o c / max(|n|, e^{-m}) is the unstabilised o c / max(|n|, 1)
+    (the floor e^{-m} is 1 in the unstabilised domain), recurrent term included; on inputs
+    where the floor is active (input pre-activations shifted down, so n < e^{-m} early on),
+    and there it differs from the paper's o c / n."""
+    for forget, seed in (("exp", 61), ("sigmoid", 62)):
+        P, R = small_problem(seed, T=24, forget=forget)
+        P[:, :, 1, :] -= 2.0
+        S = ref.sequential(P, R, None, forget + ref.FLOORED)
+        h_raw, _, _ = ref.unstabilised_hidden(P, R, forget, floored=True)
+        np.testing.assert_allclose(ref.hidden(S), h_raw, rtol=1e-11, atol=1e-13, err_msg=forget)
+        active = np.abs(S[..., 1, :]) < np.exp(-S[..., 2, :])
+        assert active.mean() > 0.02, forget
+        h_exact = ref.hidden(ref.sequential(P, R, None, forget))
+        assert np.max(np.abs(h_exact - ref.hidden(S))) > 1e-3, forget
+
+
 def pin_stabiliser_invariants(ref):
     """Along a sequential trajectory: i', f' in (0, 1], max(i', f') = 1 exactly, n > 0,
     |c| <= n, |h| < 1 (educational page, stabiliser section; the exponent arguments stay
@@ -155,7 +172,7 @@ def pin_warm_start_is_solution_when_r_zero(ref):
 
 def pin_jacobian_finite_differences(ref):
     """Analytic 4x4 Jacobian against central differences, away from branch ties."""
-    for forget, seed in (("exp", 10), ("sigmoid", 11)):
+    for forget, seed in (("exp", 10), ("sigmoid", 11), ("exp/floored", 12), ("sigmoid/floored", 13)):
         rng = np.random.Generator(np.random.PCG64(seed))
         d = 64
         prev = np.stack([rng.uniform(-2, 2, d), np.exp(rng.uniform(-1, 2, d)),
@@ -166,6 +183,13 @@ def pin_jacobian_finite_differences(ref):
         _, A = ref.cell(prev, p, r, forget, with_jacobian=True)
         _, _, _, a, it = ref.gate_values(prev, p, r, forget)
         ok = np.abs(a - it)[0] > 1e-3
+        if forget.endswith(ref.FLOORED):
+            # away from the read-out's own branch switch |n| = e^{-m}, and with the floor active
+            # on some features
+            nxt = ref.cell(prev, p, r, forget)[0]
+            gap = np.abs(np.abs(nxt[1]) - np.exp(-nxt[2]))
+            ok &= gap > 1e-3
+            assert np.sum(ok & (np.abs(nxt[1]) < np.exp(-nxt[2]))) > 4, forget
         assert ok.sum() > d // 2
         eps = 1e-6
         for col in range(4):
@@ -382,10 +406,10 @@ def pin_state0_chunking(ref):
     np.testing.assert_allclose(S, full[:, 32:], rtol=1e-11, atol=1e-13)
 
 
-def _backward_problem(seed, forget, B=2, T=10, d=3):
-    P, R = small_problem(seed, B=B, T=T, d=d, forget=forget)
+def _backward_problem(seed, forget, B=2, T=10, d=3, n_range=(0.5, 2.0)):
+    P, R = small_problem(seed, B=B, T=T, d=d, forget=forget.split("/")[0])
     rng = np.random.default_rng(seed + 1)
-    s0 = np.stack([rng.uniform(-0.5, 0.5, (B, d)), rng.uniform(0.5, 2.0, (B, d)),
+    s0 = np.stack([rng.uniform(-0.5, 0.5, (B, d)), rng.uniform(*n_range, (B, d)),
                    rng.uniform(-2.0, 2.0, (B, d)), rng.uniform(-0.9, 0.9, (B, d))], axis=1)
     g = rng.standard_normal((B, T, 4, d))
     return P, R, s0, g
@@ -395,9 +419,13 @@ def pin_backward_finite_differences(ref):
     """The backward is the gradient of L = sum(g * S(P, R, state0)) with S the sequential
     solution: central differences in float64 on entries of P, every entry of R, and entries of
     state0, for both forget-gate forms ("sLSTM in this library", "Backward")."""
-    for seed, forget in ((41, "exp"), (43, "sigmoid")):
-        P, R, s0, g = _backward_problem(seed, forget)
+    for seed, forget in ((41, "exp"), (43, "sigmoid"), (45, "exp/floored"), (46, "sigmoid/floored")):
+        P, R, s0, g = _backward_problem(seed, forget, n_range=(0.02, 0.3) if "/" in forget else (0.5, 2.0))
+        if "/" in forget:
+            P[:, :, 1, :] -= 1.5  # small input gates keep the floor active on some steps
         S = ref.sequential(P, R, s0, forget)
+        if "/" in forget:
+            assert np.any(np.abs(S[..., 1, :]) < np.exp(-S[..., 2, :])), forget
         dP, dR, ds0 = ref.backward(P, R, s0, S, g, forget)
 
         def loss(P_, R_, s_):
@@ -438,8 +466,9 @@ def pin_backward_adjoint_dense(ref):
 def pin_gate_jacobian_h_column(ref):
     """h' enters the cell only through the gate pre-activations x~ = p + r h', so the h' column
     of the state Jacobian is G r (G = d next / d x~), to rounding."""
-    for forget in ("exp", "sigmoid"):
-        P, R = small_problem(53, T=8, forget=forget)
+    for forget in ("exp", "sigmoid", "exp/floored", "sigmoid/floored"):
+        P, R = small_problem(53, T=8, forget=forget.split("/")[0])
+        P[:, :, 1, :] -= 1.5
         S = ref.sequential(P, R, None, forget)
         prev = S[:, :-1]
         _, A = ref.cell(prev, P[:, 1:], R, forget, with_jacobian=True)

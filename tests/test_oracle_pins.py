@@ -28,9 +28,10 @@ MUTATIONS = [
     ("wrong sign in stabiliser gate", "ig = np.exp(it - m)\n    fg = np.exp(a - m)\n    c =",
      "ig = np.exp(m - it)\n    fg = np.exp(a - m)\n    c ="),
     ("tie to input branch", "beta = a >= it  # tie", "beta = a > it  # tie"),
-    ("read-out floor variant", "h = o * c / n  # read-out", "h = o * c / np.maximum(np.abs(n), 1.0)  # read-out"),
-    ("quotient rule sign", "- (o * c / (n * n)) * dn[k]", "+ (o * c / (n * n)) * dn[k]"),
-    ("missing output-gate term", "dh[H] = dh[H] + (c / n) * do_dh", "dh[H] = dh[H]"),
+    ("read-out floor variant", "return n, np.ones_like(n), np.zeros_like(n)",
+     "return np.maximum(np.abs(n), 1.0), np.ones_like(n), np.zeros_like(n)"),
+    ("quotient rule sign", "- q * (v[\"dD_dn\"] * dn[k]", "+ q * (v[\"dD_dn\"] * dn[k]"),
+    ("missing output-gate term", "dh[H] = dh[H] + (c / v[\"D\"]) * do_dh", "dh[H] = dh[H]"),
     ("sigmoid-forget derivative", "return -_softplus(-f_tilde), sigmoid(-f_tilde)",
      "return -_softplus(-f_tilde), sigmoid(f_tilde)"),
     ("transposed Jacobian in the solve", 'np.einsum("bijd,bjd->bid", A[:, t], x[:, t - 1])',
@@ -46,12 +47,16 @@ MUTATIONS = [
      "lam = lam_prev"),
     ("backward: dR against h_t", "dR += np.sum(delta * prev[:, t, H][:, None, :], axis=0)",
      "dR += np.sum(delta * S[:, t, H][:, None, :], axis=0)"),
+    ("floored read-out: floor e^{+m}", "    em = np.exp(-m)\n", "    em = np.exp(m)\n"),
+    ("floored read-out: m derivative dropped", "np.where(on_m, -em, 0.0)", "np.where(on_m, 0.0 * em, 0.0)"),
+    ("floored read-out: n branch without the floor", "on_n = (an >= em) & (an >= READOUT_FLOOR)",
+     "on_n = an >= READOUT_FLOOR"),
     ("weight gradient: transposed operand", "dW = (dP2.T @ x.reshape(B * T, d_in)).reshape(g, d_h, d_in)",
      "dW = (dP2.T @ x.reshape(B * T, d_in)[::-1]).reshape(g, d_h, d_in)"),
     ("input gradient: gate rows swapped", "dx = (dP2 @ W.reshape(g * d_h, d_in)).reshape(B, T, d_in)",
      "dx = (dP2 @ W[::-1].reshape(g * d_h, d_in)).reshape(B, T, d_in)"),
     ("gate Jacobian: forget derivative", "dfg_df = fg * (dlf - dm_df)", "dfg_df = fg * (1.0 - dm_df)"),
-    ("gate Jacobian: output-gate term", "dh[GO] = dh[GO] + (c / n) * o * (1.0 - o)", "dh[GO] = dh[GO]"),
+    ("gate Jacobian: output-gate term", "dh[GO] = dh[GO] + (c / v[\"D\"]) * o * (1.0 - o)", "dh[GO] = dh[GO]"),
 ]
 
 
