@@ -58,8 +58,16 @@ typedef enum {
 
 typedef enum { SLSTM_F32 = 0, SLSTM_BF16 = 1 } slstm_dtype;
 
-/* forget gate: log f = f~ (exponential) or log sigma(f~) (sigmoid) ([XL] "Method"; [ED]) */
-typedef enum { SLSTM_FORGET_EXP = 0, SLSTM_FORGET_SIGMOID = 1 } slstm_forget;
+/* forget gate: log f = f~ (exponential) or log sigma(f~) (sigmoid) ([XL] "Method"; [ED]).
+ * SLSTM_READOUT_FLOORED may be OR-ed into every argument of this type: the read-out becomes
+ * h = o c / max(|n|, e^{-m}, 1e-6), the stabilised read-out of [ED] ("Exponential gating + the
+ * stabilizer (the crux)", with the 1e-6 floor of its "Implementation notes / deviations" item 1,
+ * read as a lower bound), instead of the paper's h = o c / n. Any other bit is rejected. */
+typedef enum {
+  SLSTM_FORGET_EXP = 0,
+  SLSTM_FORGET_SIGMOID = 1,
+  SLSTM_READOUT_FLOORED = 0x100
+} slstm_forget;
 
 /* initial Newton iterate: the trajectory with the recurrent term R h_{t-1} dropped, or zeros */
 typedef enum { SLSTM_INIT_WARM = 0, SLSTM_INIT_ZERO = 1 } slstm_init;

@@ -180,12 +180,12 @@ size_t warm_desc_words_for(int B, int T, int d, bool chain) {
 }
 
 hipError_t launch_warm(const void* P, bool bf16, const float* state0, float* S, int B, int T, int d,
-                       bool sig, bool chain, unsigned long long* desc, Control* ctl, hipStream_t st) {
+                       int cm, bool chain, unsigned long long* desc, Control* ctl, hipStream_t st) {
   const uint32_t ep = next_epoch();
   unsigned int* tickets = slstm::spread_of(ctl)->ticket[slstm::kTicketWarm][0];
   return timed(SLSTM_KERNEL_WARM_START, st, [&] {
-    return chain ? slstm::launch_warm_chain(P, bf16, state0, S, B, T, d, sig, desc, tickets, ep, st)
-                 : slstm::launch_warm_start(P, bf16, state0, S, B, T, d, sig, desc, tickets, ep, st);
+    return chain ? slstm::launch_warm_chain(P, bf16, state0, S, B, T, d, cm, desc, tickets, ep, st)
+                 : slstm::launch_warm_start(P, bf16, state0, S, B, T, d, cm, desc, tickets, ep, st);
   });
 }
 
@@ -206,6 +206,19 @@ T* at(void* base, size_t off) {
   return reinterpret_cast<T*>(static_cast<char*>(base) + off);
 }
 
+// the kernels' cell mode: bit 0 sigmoid forget gate, bit 1 floored read-out
+bool known_cell_mode(slstm_forget f) {
+  const int v = static_cast<int>(f);
+  const int base = v & ~static_cast<int>(SLSTM_READOUT_FLOORED);
+  return base == SLSTM_FORGET_EXP || base == SLSTM_FORGET_SIGMOID;
+}
+
+int cell_mode_of(slstm_forget f) {
+  const int v = static_cast<int>(f);
+  return ((v & ~static_cast<int>(SLSTM_READOUT_FLOORED)) == SLSTM_FORGET_SIGMOID ? slstm::kCellSigmoid : 0) |
+         ((v & SLSTM_READOUT_FLOORED) ? slstm::kCellFloored : 0);
+}
+
 slstm_status check_common(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
                           const float* states, const float* h_out, const float* final_state, int B,
                           int T, int d, slstm_forget fmode) {
@@ -214,8 +227,7 @@ slstm_status check_common(const void* P, slstm_dtype P_dtype, const float* R, co
   if (P == nullptr || R == nullptr || states == nullptr)
     return fail(SLSTM_EINVAL, "P, R and states must not be NULL");
   if (P_dtype != SLSTM_F32 && P_dtype != SLSTM_BF16) return fail(SLSTM_EINVAL, "unknown P dtype %d", (int)P_dtype);
-  if (fmode != SLSTM_FORGET_EXP && fmode != SLSTM_FORGET_SIGMOID)
-    return fail(SLSTM_EINVAL, "unknown forget mode %d", (int)fmode);
+  if (!known_cell_mode(fmode)) return fail(SLSTM_EINVAL, "unknown forget mode %d", (int)fmode);
   if (!aligned(P, P_dtype == SLSTM_F32 ? 4 : 2) || !aligned(R, 4) || !aligned(state0, 4))
     return fail(SLSTM_EINVAL, "P, R or state0 misaligned");
   if (!aligned(states, 16) || !aligned(h_out, 16) || !aligned(final_state, 16))
@@ -249,7 +261,7 @@ __global__ void store_u32_kernel(unsigned int* p, unsigned int v) { *p = v; }
 
 // the solver as one launch per iteration (every schedule; the only way with an early stop)
 hipError_t iterate(const void* P, bool bf16, const float* R, const float* state0, float* states,
-                   float* h_out, int B, int T, int d_h, bool sig, int max_iters, float tol,
+                   float* h_out, int B, int T, int d_h, int cm, int max_iters, float tol,
                    slstm_init init, Form form, const NewtonLayout& L, void* workspace, Control* ctl,
                    unsigned int* tickets, hipStream_t st) {
   auto* desc = at<unsigned long long>(workspace, L.desc);
@@ -264,7 +276,7 @@ hipError_t iterate(const void* P, bool bf16, const float* R, const float* state0
     buf[1] = (max_iters % 2 == 0) ? other : states;
   }
   if (init == SLSTM_INIT_WARM) {
-    HIP_RET(launch_warm(P, bf16, state0, buf[0], B, T, d_h, sig, form == Form::kChain, desc, ctl, st));
+    HIP_RET(launch_warm(P, bf16, state0, buf[0], B, T, d_h, cm, form == Form::kChain, desc, ctl, st));
   } else {
     HIP_RET(slstm::launch_zero(buf[0], n_state, st));
   }
@@ -274,7 +286,7 @@ hipError_t iterate(const void* P, bool bf16, const float* R, const float* state0
       const bool last = k + 1 == max_iters;
       HIP_RET(timed(SLSTM_KERNEL_NEWTON_ITERATION, st, [&] {
         return slstm::launch_newton_chain(P, bf16, R, state0, buf[k % 2], buf[(k + 1) % 2], last ? h_out : nullptr,
-                                          B, T, d_h, sig, desc, tickets, ep, ctl, k, tol, last, st);
+                                          B, T, d_h, cm, desc, tickets, ep, ctl, k, tol, last, st);
       }));
     }
     // the last launch formed the final residual and h; what remains of the stop rule is the
@@ -285,7 +297,7 @@ hipError_t iterate(const void* P, bool bf16, const float* R, const float* state0
       const uint32_t ep = next_epoch();
       HIP_RET(timed(SLSTM_KERNEL_NEWTON_ITERATION, st, [&] {
         return slstm::launch_newton_iteration(P, bf16, R, state0, buf[k % 2], buf[(k + 1) % 2], B, T, d_h,
-                                              sig, desc, tickets, ep, ctl, k, tol, st);
+                                              cm, desc, tickets, ep, ctl, k, tol, st);
       }));
     }
   } else {
@@ -293,7 +305,7 @@ hipError_t iterate(const void* P, bool bf16, const float* R, const float* state0
     float* rhs = at<float>(workspace, L.rhs);
     for (int k = 0; k < max_iters; ++k) {
       HIP_RET(timed(SLSTM_KERNEL_RESIDUAL_JACOBIAN, st, [&] {
-        return slstm::launch_residual(P, bf16, R, state0, states, A, rhs, B, T, d_h, sig, ctl,
+        return slstm::launch_residual(P, bf16, R, state0, states, A, rhs, B, T, d_h, cm, ctl,
                                       &slstm::spread_of(ctl)->err[0][k], slstm::kErrSlotWords, slstm::ResidualMode::kSparse, -1, tol, st);
       }));
       const uint32_t ep = next_epoch();
@@ -308,7 +320,7 @@ hipError_t iterate(const void* P, bool bf16, const float* R, const float* state0
     // already met the tolerance)
     const int chk = (form == Form::kScan) ? max_iters - 1 : -1;
     HIP_RET(timed(SLSTM_KERNEL_FINAL_RESIDUAL, st, [&] {
-      return slstm::launch_residual(P, bf16, R, state0, buf[max_iters % 2], nullptr, nullptr, B, T, d_h, sig,
+      return slstm::launch_residual(P, bf16, R, state0, buf[max_iters % 2], nullptr, nullptr, B, T, d_h, cm,
                                     ctl, &slstm::spread_of(ctl)->err[0][max_iters], slstm::kErrSlotWords,
                                     slstm::ResidualMode::kNone, chk, tol, st, h_out);
     }));
@@ -441,7 +453,7 @@ slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const floa
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool bf16 = P_dtype == SLSTM_BF16;
-  const bool sig = fmode == SLSTM_FORGET_SIGMOID;
+  const int cm = cell_mode_of(fmode);
   Control* ctl = at<Control>(workspace, L.ctl);
   auto* desc = at<unsigned long long>(workspace, L.desc);
   const i64 n_state = static_cast<i64>(B) * T * 4 * d_h;
@@ -452,11 +464,11 @@ slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const floa
     // the whole fixed-count solve in one pass; it writes the final states, h and every residual
     const uint32_t ep = next_epoch();
     HIP_TRY(timed(SLSTM_KERNEL_NEWTON_SOLVE, st, [&] {
-      return slstm::launch_newton_pipe(P, bf16, R, state0, states, h_out, B, T, d_h, sig,
+      return slstm::launch_newton_pipe(P, bf16, R, state0, states, h_out, B, T, d_h, cm,
                                        init == SLSTM_INIT_WARM, max_iters, desc, tickets, ep, ctl, st);
     }));
   } else {
-    HIP_TRY(iterate(P, bf16, R, state0, states, h_out, B, T, d_h, sig, max_iters, tol, init, form, L,
+    HIP_TRY(iterate(P, bf16, R, state0, states, h_out, B, T, d_h, cm, max_iters, tol, init, form, L,
                     workspace, ctl, tickets, st));
   }
   HIP_TRY(slstm::launch_finalize(ctl, tol, st));
@@ -492,7 +504,7 @@ slstm_status slstm_sequential_forward(const void* P, slstm_dtype P_dtype, const 
   hipStream_t st = static_cast<hipStream_t>(stream);
   HIP_TRY(timed(SLSTM_KERNEL_SEQUENTIAL, st, [&] {
     return slstm::launch_sequential(P, P_dtype == SLSTM_BF16, R, state0, states, h_out, final_state,
-                                    B, T, d_h, fmode == SLSTM_FORGET_SIGMOID, st);
+                                    B, T, d_h, cell_mode_of(fmode), st);
   }));
   return SLSTM_OK;
 }
@@ -532,7 +544,7 @@ slstm_status slstm_residual_jacobian(const void* P, slstm_dtype P_dtype, const f
   HIP_TRY(hipGetLastError());
   HIP_TRY(timed(SLSTM_KERNEL_RESIDUAL_JACOBIAN, st, [&] {
     return slstm::launch_residual(P, P_dtype == SLSTM_BF16, R, state0, states, A, rhs, B, T, d_h,
-                                  fmode == SLSTM_FORGET_SIGMOID, nullptr, err, 0, slstm::ResidualMode::kDense, -1,
+                                  cell_mode_of(fmode), nullptr, err, 0, slstm::ResidualMode::kDense, -1,
                                   0.0f, st);
   }));
   return SLSTM_OK;
@@ -585,7 +597,7 @@ slstm_status slstm_warm_start(const void* P, slstm_dtype P_dtype, const float* s
   hipStream_t st = static_cast<hipStream_t>(stream);
   Control* ctl = at<Control>(workspace, L.ctl);
   HIP_TRY(slstm::launch_init_control(ctl, st));
-  HIP_TRY(launch_warm(P, P_dtype == SLSTM_BF16, state0, states, B, T, d_h, fmode == SLSTM_FORGET_SIGMOID,
+  HIP_TRY(launch_warm(P, P_dtype == SLSTM_BF16, state0, states, B, T, d_h, cell_mode_of(fmode),
                       chain, at<unsigned long long>(workspace, L.desc), ctl, st));
   return SLSTM_OK;
 }
@@ -625,7 +637,7 @@ slstm_status slstm_backward(const void* P, slstm_dtype P_dtype, const float* R, 
   HIP_TRY(timed(SLSTM_KERNEL_BACKWARD, st, [&] {
     return slstm::launch_backward(P, P_dtype == SLSTM_BF16, R, state0, states, g_states, g_h, g_final, dP,
                                   dP_dtype == SLSTM_BF16, dR, dbias, dstate0, at<float>(workspace, L.rows), B, T, d_h,
-                                  fmode == SLSTM_FORGET_SIGMOID, scan, at<unsigned long long>(workspace, L.desc),
+                                  cell_mode_of(fmode), scan, at<unsigned long long>(workspace, L.desc),
                                   slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0], ep, st);
   }));
   return SLSTM_OK;

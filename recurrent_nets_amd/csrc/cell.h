@@ -7,8 +7,13 @@
 //   z = tanh z~, o = sigma(o~), l = f~ (exponential forget gate) or log sigma(f~) (sigmoid)
 //   a = l + m', m = max(a, i~) (ties take a), i' = exp(i~ - m), f' = exp(a - m)
 //   c = f' c' + i' z, n = f' n' + i', h = o c / n
+// or, with the floored read-out of the educational page (same section, and its deviations
+// item 1), h = o c / max(|n|, e^{-m}, 1e-6).
 // The 4x4 Jacobian A = d(c, n, m, h) / d(c', n', m', h') is the analytic derivative of these
-// equations, on the branch the max takes; (c, n', m) rows have structural zeros.
+// equations, on the branch each max takes; (c, n', m) rows have structural zeros.
+//
+// The cell mode of a kernel is an int: bit 0 the sigmoid forget gate (else exponential), bit 1
+// the floored read-out.
 #pragma once
 #include "common.h"
 
@@ -37,6 +42,32 @@ __device__ __forceinline__ float log_sigmoidf(float x) {
   return -(fmaxf(-x, 0.0f) + kLn2 * __builtin_amdgcn_logf(1.0f + exp_fast(-fabsf(x))));
 }
 
+// Expands LAUNCH(CM) with the compile-time cell mode CM equal to the runtime value cell_mode.
+#define SLSTM_CELL_MODE_DISPATCH(cell_mode, LAUNCH) \
+  switch (cell_mode) {                              \
+    case 0: LAUNCH(0); break;                       \
+    case 1: LAUNCH(1); break;                       \
+    case 2: LAUNCH(2); break;                       \
+    default: LAUNCH(3); break;                      \
+  }
+constexpr float kReadoutFloor = 1e-6f;
+
+// Denominator D of the read-out h = o c / D: returns 1 / D and the derivatives dD/dn, dD/dm.
+// D = n, or (floored) max(|n|, e^{-m}, 1e-6) on the branch the max takes (ties go to |n|, then
+// to e^{-m}).
+struct Readout {
+  float rD, dn, dm;
+};
+__device__ __forceinline__ Readout readout(float n, float m, bool floored) {
+  if (!floored) return {rcp_fast(n), 1.0f, 0.0f};
+  const float an = fabsf(n);
+  const float em = exp_fast(-m);
+  const bool on_n = an >= em && an >= kReadoutFloor;
+  const bool on_m = !on_n && em >= kReadoutFloor;
+  const float D = on_n ? an : (on_m ? em : kReadoutFloor);
+  return {rcp_fast(D), on_n ? copysignf(1.0f, n) : 0.0f, on_m ? -em : 0.0f};
+}
+
 // One step. Writes the next state s[4] = (c, n, m, h); with JAC also A[16] row-major
 // (A[4*row + col] = d s[row] / d prev[col]).
 //
@@ -46,11 +77,12 @@ __device__ __forceinline__ float log_sigmoidf(float x) {
 // derivatives of the c and n rows reduce to (with l' = dl/df~ and D = l' r_f - r_i)
 //   dc/dm' = e (beta ? -z : c'),   dn/dm' = e (beta ? -1 : n'),
 //   dc/dh' = D dc/dm' + i' dz/dh',  dn/dh' = D dn/dm',
-// and dm/dm' = beta, dm/dh' = beta ? l' r_f : r_i.
+// and dm/dm' = beta, dm/dh' = beta ? l' r_f : r_i. The h row is the quotient rule through c
+// and through the read-out's denominator D(n, m).
 template <bool JAC>
 __device__ __forceinline__ void cell_step(const CellIn& pv, float pz, float pi, float pf, float po,
                                           float rz, float ri, float rf, float ro, bool sig_forget,
-                                          float s[4], float A[16]) {
+                                          bool floored, float s[4], float A[16]) {
   const float zt = fmaf(rz, pv.h, pz);
   const float it = fmaf(ri, pv.h, pi);
   const float ft = fmaf(rf, pv.h, pf);
@@ -73,7 +105,8 @@ __device__ __forceinline__ void cell_step(const CellIn& pv, float pz, float pi, 
   const float fg = beta ? 1.0f : e;
   const float c = fmaf(fg, pv.c, ig * z);
   const float n = fmaf(fg, pv.n, ig);
-  const float rn = rcp_fast(n);
+  const Readout rdn = readout(n, m, floored);
+  const float rn = rdn.rD;
   const float h = o * c * rn;
   s[0] = c;
   s[1] = n;
@@ -88,16 +121,23 @@ __device__ __forceinline__ void cell_step(const CellIn& pv, float pz, float pi, 
     const float do_dh = fmaf(-o, o, o) * ro;
     const float c_h = fmaf(c_m, D, ig * dz_dh);
     const float n_h = n_m * D;
-    // row h = o c / n: (o/n) dc - (o c / n^2) dn, plus (c/n) do on h'
+    // row h = o c / D: (o/D) dc - (o c / D^2) (D_n dn + D_m dm), plus (c/D) do on h'
     const float q1 = o * rn;
     const float q2 = h * rn;
     A[0] = fg;     A[1] = 0.0f;   A[2] = c_m;   A[3] = c_h;
     A[4] = 0.0f;   A[5] = fg;     A[6] = n_m;   A[7] = n_h;
     A[8] = 0.0f;   A[9] = 0.0f;   A[10] = beta ? 1.0f : 0.0f;   A[11] = beta ? lrf : ri;
     A[12] = q1 * fg;
-    A[13] = -q2 * fg;
-    A[14] = fmaf(q1, c_m, -q2 * n_m);
-    A[15] = fmaf(q1, c_h, fmaf(-q2, n_h, (c * rn) * do_dh));
+    if (!floored) {
+      A[13] = -q2 * fg;
+      A[14] = fmaf(q1, c_m, -q2 * n_m);
+      A[15] = fmaf(q1, c_h, fmaf(-q2, n_h, (c * rn) * do_dh));
+    } else {
+      const float qn = q2 * rdn.dn, qm = q2 * rdn.dm;
+      A[13] = -qn * fg;
+      A[14] = fmaf(q1, c_m, fmaf(-qn, n_m, -qm * A[10]));
+      A[15] = fmaf(q1, c_h, fmaf(-qn, n_h, fmaf(-qm, A[11], (c * rn) * do_dh)));
+    }
   }
 }
 
@@ -105,7 +145,8 @@ __device__ __forceinline__ void cell_step(const CellIn& pv, float pz, float pi, 
 // given lam = dL/ds for the state the step produces, returns dx = dL/dx~ for the gate
 // pre-activations (z, i, f, o) (= dL/dP of the step) and lam_prev = dL/ds' = A^T lam. The
 // backward of "sLSTM in this library", section "Backward", one step of it:
-//   h = o c / n folds into the c and n adjoints: lc = lam_c + (o/n) lam_h, ln = lam_n - (h/n) lam_h,
+//   h = o c / D folds into the c, n and m adjoints: lc = lam_c + (o/D) lam_h,
+//   ln = lam_n - (h/D) D_n lam_h, lam_m += -(h/D) D_m lam_h (D = n: D_n = 1, D_m = 0),
 //   c = f' c' + i' z, n = f' n' + i':  dL/df' = lc c' + ln n',  dL/di' = lc z + ln,  dL/dz = lc i'
 //   one of (i', f') is 1 and the other e = e^{-|a - i~|} (see cell_step); with
 //   w = beta ? e dL/di' : -e dL/df', the stabiliser m = max(a, i~) gives
@@ -114,7 +155,7 @@ __device__ __forceinline__ void cell_step(const CellIn& pv, float pz, float pi, 
 //   lam_prev = (lc f', ln f', dL/da, sum_x r_x dL/dx~)   (h' enters only through x~ = p + r h')
 __device__ __forceinline__ void cell_vjp(const CellIn& pv, float pz, float pi, float pf, float po,
                                          float rz, float ri, float rf, float ro, bool sig_forget,
-                                         const float lam[4], float dx[4], float lam_prev[4]) {
+                                         bool floored, const float lam[4], float dx[4], float lam_prev[4]) {
   const float zt = fmaf(rz, pv.h, pz);
   const float it = fmaf(ri, pv.h, pi);
   const float ft = fmaf(rf, pv.h, pf);
@@ -136,16 +177,19 @@ __device__ __forceinline__ void cell_vjp(const CellIn& pv, float pz, float pi, f
   const float fg = beta ? 1.0f : e;
   const float c = fmaf(fg, pv.c, ig * z);
   const float n = fmaf(fg, pv.n, ig);
-  const float rn = rcp_fast(n);
+  const Readout rdn = readout(n, beta ? a : it, floored);
+  const float rn = rdn.rD;
   const float cn = c * rn;
   const float lc = fmaf(o * rn, lam[3], lam[0]);
-  const float ln = fmaf(-o * cn * rn, lam[3], lam[1]);
+  const float hq = -o * cn * rn;  // -(h / D)
+  const float ln = floored ? fmaf(hq * rdn.dn, lam[3], lam[1]) : fmaf(hq, lam[3], lam[1]);
+  const float lm = floored ? fmaf(hq * rdn.dm, lam[3], lam[2]) : lam[2];
   const float lfg = fmaf(lc, pv.c, ln * pv.n);
   const float lig = fmaf(lc, z, ln);
   const float w = beta ? e * lig : -e * lfg;
-  const float da = beta ? lam[2] - w : -w;
+  const float da = beta ? lm - w : -w;
   dx[0] = lc * ig * fmaf(-z, z, 1.0f);
-  dx[1] = beta ? w : w + lam[2];
+  dx[1] = beta ? w : w + lm;
   dx[2] = da * dlf;
   dx[3] = cn * lam[3] * fmaf(-o, o, o);
   lam_prev[0] = lc * fg;

@@ -32,6 +32,11 @@ __device__ __forceinline__ float load_p(const void* __restrict__ P, i64 idx) {
   }
 }
 
+// Cell mode of the kernels: bit 0 the sigmoid forget gate (else exponential), bit 1 the floored
+// read-out h = o c / max(|n|, e^{-m}, 1e-6) (else h = o c / n).
+constexpr int kCellSigmoid = 1;
+constexpr int kCellFloored = 2;
+
 // ---- buffer resources -------------------------------------------------------------------------
 // A buffer resource holds a wave-uniform base address in scalar registers; each access adds a
 // 32-bit per-lane byte offset (one VGPR) and a wave-uniform byte offset (an SGPR). Kernels that

@@ -51,7 +51,7 @@ __device__ __forceinline__ void store_dp(float v, bool bf16, rsrc_t r, unsigned 
 }
 
 // GS: a gradient with respect to the states is given (else only dL/dh and the final state's)
-template <bool BF16, bool SIG, bool GS>
+template <bool BF16, int CM, bool GS>
 __global__ __launch_bounds__(kBackBlock, SLSTM_BACK_MIN_WAVES) void backward_chain_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S, const float* __restrict__ g, const float* __restrict__ g_h,
@@ -60,7 +60,8 @@ __global__ __launch_bounds__(kBackBlock, SLSTM_BACK_MIN_WAVES) void backward_cha
     unsigned long long* __restrict__ carry, unsigned int* __restrict__ tickets, int n_ctr,
     uint32_t epoch) {
   constexpr int TC = kBackSteps;
-  constexpr bool sig = SIG;
+  constexpr bool sig = (CM & kCellSigmoid) != 0;   // forget-gate form and read-out,
+  constexpr bool floored = (CM & kCellFloored) != 0;  // fixed per instantiation
   __shared__ int s_tile[2];
   const int tid = threadIdx.x;
   if (tid == 0) take_ticket(tickets, n_ctr, n_lg, n_tt, s_tile[0], s_tile[1]);
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(kBackBlock, SLSTM_BACK_MIN_WAVES) void backward_cha
 #pragma unroll
       for (int e = 0; e < 4; ++e) lam[e] = gs[u][e] + lin[e];
       const CellIn pv = (u == 0) ? halo : CellIn{s[u - 1][0], s[u - 1][1], s[u - 1][2], s[u - 1][3]};
-      cell_vjp(pv, p[u][0], p[u][1], p[u][2], p[u][3], rz, ri, rf, ro, sig, lam, dx, lin);
+      cell_vjp(pv, p[u][0], p[u][1], p[u][2], p[u][3], rz, ri, rf, ro, sig, floored, lam, dx, lin);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         store_dp(dx[e], dpb, rsD, j, (4u * u + e) * ud);
@@ -205,7 +206,7 @@ __global__ __launch_bounds__(kBackBlock, SLSTM_BACK_MIN_WAVES) void backward_cha
 constexpr int kBackScanBlock = 256;  // 4 waves x 16 features x 4 sub-chunks
 constexpr int kBackScanTSub = SLSTM_BACK_SCAN_TSUB;
 
-template <bool BF16, bool SIG, bool GS, int TSUB>
+template <bool BF16, int CM, bool GS, int TSUB>
 __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void backward_scan_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S, const float* __restrict__ g, const float* __restrict__ g_h,
@@ -213,7 +214,8 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
     float* __restrict__ sum_rows, int T, int d, int n_jt, int n_lg, int n_tt, int anchor_stride,
     unsigned long long* __restrict__ desc, unsigned int* __restrict__ tickets, int n_ctr,
     uint32_t epoch) {
-  constexpr bool sig = SIG;
+  constexpr bool sig = (CM & kCellSigmoid) != 0;   // forget-gate form and read-out,
+  constexpr bool floored = (CM & kCellFloored) != 0;  // fixed per instantiation
   __shared__ int s_tile[2];
   const int tid = threadIdx.x;
   if (tid == 0) take_ticket(tickets, n_ctr, n_lg, n_tt, s_tile[0], s_tile[1]);
@@ -313,7 +315,7 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
     if (valid && t < T) {
       const CellIn pv = (u == 0) ? pv0 : CellIn{sv[u - 1][0], sv[u - 1][1], sv[u - 1][2], sv[u - 1][3]};
       float f[4], A[16], At[16];
-      cell_step<true>(pv, pg[u][0], pg[u][1], pg[u][2], pg[u][3], rz, ri, rf, ro, sig, f, A);
+      cell_step<true>(pv, pg[u][0], pg[u][1], pg[u][2], pg[u][3], rz, ri, rf, ro, sig, floored, f, A);
 #pragma unroll
       for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
       float lam[4], dx[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) lam[e] = gs[u][e] + y[e];
-      cell_vjp(pv, pg[u][0], pg[u][1], pg[u][2], pg[u][3], rz, ri, rf, ro, sig, lam, dx, y);
+      cell_vjp(pv, pg[u][0], pg[u][1], pg[u][2], pg[u][3], rz, ri, rf, ro, sig, floored, lam, dx, y);
       const unsigned o = lane_off + u * 4u * ud;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -458,7 +460,7 @@ size_t backward_row_floats(int B, int T, int d, bool scan) {
 hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const float* state0,
                            const float* S, const float* g, const float* g_h, const float* g_final,
                            void* dP, bool dp_bf16, float* dR, float* dbias, float* dstate0,
-                           float* rows, int B, int T, int d, bool sig_forget, bool scan,
+                           float* rows, int B, int T, int d, int cell_mode, bool scan,
                            unsigned long long* desc, unsigned int* tickets, uint32_t epoch,
                            hipStream_t stream) {
   const BackGrid gr = back_grid(B, T, d, scan);
@@ -471,42 +473,40 @@ hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const flo
   const int a = static_cast<int>(gr.n_jt), c = static_cast<int>(gr.n_lg), e = static_cast<int>(gr.n_tt);
   const bool gs = g != nullptr;
   const int dpb = dp_bf16 ? 1 : 0;
-  // one instantiation per P dtype, forget-gate form and presence of the state gradient
-#define SLSTM_BACK_DISPATCH                                   \
-  do {                                                        \
-    if (p_bf16) {                                             \
-      if (sig_forget) {                                       \
-        if (gs) SLSTM_BACK_LAUNCH(true, true, true);          \
-        else SLSTM_BACK_LAUNCH(true, true, false);            \
-      } else {                                                \
-        if (gs) SLSTM_BACK_LAUNCH(true, false, true);         \
-        else SLSTM_BACK_LAUNCH(true, false, false);           \
-      }                                                       \
-    } else {                                                  \
-      if (sig_forget) {                                       \
-        if (gs) SLSTM_BACK_LAUNCH(false, true, true);         \
-        else SLSTM_BACK_LAUNCH(false, true, false);           \
-      } else {                                                \
-        if (gs) SLSTM_BACK_LAUNCH(false, false, true);        \
-        else SLSTM_BACK_LAUNCH(false, false, false);          \
-      }                                                       \
-    }                                                         \
+  // one instantiation per P dtype, cell mode and presence of the state gradient
+#define SLSTM_BACK_TT(CM_) SLSTM_BACK_LAUNCH(true, CM_, true)
+#define SLSTM_BACK_TF(CM_) SLSTM_BACK_LAUNCH(true, CM_, false)
+#define SLSTM_BACK_FT(CM_) SLSTM_BACK_LAUNCH(false, CM_, true)
+#define SLSTM_BACK_FF(CM_) SLSTM_BACK_LAUNCH(false, CM_, false)
+#define SLSTM_BACK_DISPATCH                                                   \
+  do {                                                                        \
+    if (p_bf16) {                                                             \
+      if (gs) { SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_BACK_TT) }          \
+      else { SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_BACK_TF) }             \
+    } else {                                                                  \
+      if (gs) { SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_BACK_FT) }          \
+      else { SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_BACK_FF) }             \
+    }                                                                         \
   } while (0)
   if (scan) {
     const int stride = look_back_anchor_stride(gr.n_lg, SLSTM_BACK_SCAN_MIN_WAVES);
-#define SLSTM_BACK_LAUNCH(BF, SG, GS)                                                                              \
-  backward_scan_kernel<BF, SG, GS, kBackScanTSub><<<grid, kBackScanBlock, 0, stream>>>(                            \
+#define SLSTM_BACK_LAUNCH(BF, CM_, GS)                                                                             \
+  backward_scan_kernel<BF, CM_, GS, kBackScanTSub><<<grid, kBackScanBlock, 0, stream>>>(                           \
       P, R, state0, S, g, g_h, g_final, dP, dpb, dstate0, rows, T, d, a, c, e, stride, desc, tickets, n_ctr, epoch)
     SLSTM_BACK_DISPATCH;
 #undef SLSTM_BACK_LAUNCH
   } else {
-#define SLSTM_BACK_LAUNCH(BF, SG, GS)                                                                      \
-  backward_chain_kernel<BF, SG, GS><<<grid, kBackBlock, 0, stream>>>(P, R, state0, S, g, g_h, g_final, dP, \
-                                                                     dpb, dstate0, rows, T, d, a, c, e, desc, \
-                                                                     tickets, n_ctr, epoch)
+#define SLSTM_BACK_LAUNCH(BF, CM_, GS)                                                                      \
+  backward_chain_kernel<BF, CM_, GS><<<grid, kBackBlock, 0, stream>>>(P, R, state0, S, g, g_h, g_final, dP, \
+                                                                      dpb, dstate0, rows, T, d, a, c, e, desc, \
+                                                                      tickets, n_ctr, epoch)
     SLSTM_BACK_DISPATCH;
 #undef SLSTM_BACK_LAUNCH
   }
+#undef SLSTM_BACK_TT
+#undef SLSTM_BACK_TF
+#undef SLSTM_BACK_FT
+#undef SLSTM_BACK_FF
 #undef SLSTM_BACK_DISPATCH
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;

@@ -35,7 +35,7 @@ constexpr int kChainSteps = SLSTM_CHAIN_STEPS;  // steps per tile
 #define SLSTM_CHAIN_MIN_WAVES 3
 #endif
 
-template <bool BF16, bool LAST, bool SIG>
+template <bool BF16, bool LAST, int CM>
 __global__ __launch_bounds__(kChainBlock, SLSTM_CHAIN_MIN_WAVES) void newton_chain_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S_in, float* __restrict__ S_out, float* __restrict__ h_out, int T,
@@ -74,7 +74,8 @@ __global__ __launch_bounds__(kChainBlock, SLSTM_CHAIN_MIN_WAVES) void newton_cha
   const i64 n_lanes = static_cast<i64>(n_lg) * kChainBlock;
   const i64 lane = static_cast<i64>(lg) * kChainBlock + tid;
   auto carry_word = [&](int tile, int e) { return carry + (static_cast<i64>(tile) * 4 + e) * n_lanes + lane; };
-  constexpr bool sig = SIG;  // forget-gate form, fixed per instantiation
+  constexpr bool sig = (CM & kCellSigmoid) != 0;   // forget-gate form and read-out,
+  constexpr bool floored = (CM & kCellFloored) != 0;  // fixed per instantiation
 
   // Delta entering the tile, loaded now so that it arrives while the tile's operands do
   unsigned long long pf[4] = {0ull, 0ull, 0ull, 0ull};
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(kChainBlock, SLSTM_CHAIN_MIN_WAVES) void newton_cha
       const int t = t0 + u;
       if (t < T) {
         float f[4], A[16];
-        cell_step<true>(pv, pg[u][0], pg[u][1], pg[u][2], pg[u][3], rz, ri, rf, ro, sig, f, A);
+        cell_step<true>(pv, pg[u][0], pg[u][1], pg[u][2], pg[u][3], rz, ri, rf, ro, sig, floored, f, A);
         float r[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -177,7 +178,7 @@ __global__ __launch_bounds__(kChainBlock, SLSTM_CHAIN_MIN_WAVES) void newton_cha
         }
         if constexpr (LAST) {
           float fn[4];
-          cell_step<false>(pn, pg[u][0], pg[u][1], pg[u][2], pg[u][3], rz, ri, rf, ro, sig, fn, nullptr);
+          cell_step<false>(pn, pg[u][0], pg[u][1], pg[u][2], pg[u][3], rz, ri, rf, ro, sig, floored, fn, nullptr);
 #pragma unroll
           for (int k = 0; k < 4; ++k) fmax_new = res_max(fmax_new, sn[k] - fn[k]);
           if (h_tile != nullptr) h_tile[static_cast<i64>(u) * d + j] = sn[3];
@@ -228,7 +229,7 @@ size_t chain_desc_words(int B, int T, int d) {
 
 hipError_t launch_newton_chain(const void* P, bool p_bf16, const float* R, const float* state0,
                                const float* S_in, float* S_out, float* h_out, int B, int T, int d,
-                               bool sig_forget, unsigned long long* carry, unsigned int* tickets,
+                               int cell_mode, unsigned long long* carry, unsigned int* tickets,
                                uint32_t epoch, Control* ctl, int k_iter, float tol, bool last,
                                hipStream_t stream) {
   i64 n_jt, n_lg, n_tt;
@@ -238,20 +239,25 @@ hipError_t launch_newton_chain(const void* P, bool p_bf16, const float* R, const
   const int n_ctr = ticket_counters(n_lg);
   const dim3 grid(static_cast<unsigned>(blocks));
   const int a = static_cast<int>(n_jt), c = static_cast<int>(n_lg), e = static_cast<int>(n_tt);
-#define SLSTM_CHAIN_LAUNCH(BF, LS, SG)                                                                      \
-  newton_chain_kernel<BF, LS, SG><<<grid, kChainBlock, 0, stream>>>(P, R, state0, S_in, S_out, h_out, T, d, \
-                                                                    a, c, e, carry, tickets, n_ctr,       \
-                                                                    epoch, ctl, k_iter, tol)
-#define SLSTM_CHAIN_LAUNCH_SIG(BF, LS) \
-  if (sig_forget) SLSTM_CHAIN_LAUNCH(BF, LS, true); else SLSTM_CHAIN_LAUNCH(BF, LS, false)
+#define SLSTM_CHAIN_LAUNCH(BF, LS, CM_)                                                                      \
+  newton_chain_kernel<BF, LS, CM_><<<grid, kChainBlock, 0, stream>>>(P, R, state0, S_in, S_out, h_out, T, d, \
+                                                                     a, c, e, carry, tickets, n_ctr,       \
+                                                                     epoch, ctl, k_iter, tol)
+#define SLSTM_CHAIN_TT(CM_) SLSTM_CHAIN_LAUNCH(true, true, CM_)
+#define SLSTM_CHAIN_TF(CM_) SLSTM_CHAIN_LAUNCH(true, false, CM_)
+#define SLSTM_CHAIN_FT(CM_) SLSTM_CHAIN_LAUNCH(false, true, CM_)
+#define SLSTM_CHAIN_FF(CM_) SLSTM_CHAIN_LAUNCH(false, false, CM_)
   if (p_bf16) {
-    if (last) SLSTM_CHAIN_LAUNCH_SIG(true, true);
-    else SLSTM_CHAIN_LAUNCH_SIG(true, false);
+    if (last) { SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_CHAIN_TT) }
+    else { SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_CHAIN_TF) }
   } else {
-    if (last) SLSTM_CHAIN_LAUNCH_SIG(false, true);
-    else SLSTM_CHAIN_LAUNCH_SIG(false, false);
+    if (last) { SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_CHAIN_FT) }
+    else { SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_CHAIN_FF) }
   }
-#undef SLSTM_CHAIN_LAUNCH_SIG
+#undef SLSTM_CHAIN_TT
+#undef SLSTM_CHAIN_TF
+#undef SLSTM_CHAIN_FT
+#undef SLSTM_CHAIN_FF
 #undef SLSTM_CHAIN_LAUNCH
   return hipGetLastError();
 }

@@ -66,10 +66,10 @@ __device__ __forceinline__ void load_sub_chunk(rsrc_t rsP, rsrc_t rsS, unsigned 
 // residual r = f(s') - s and the 12 Jacobian entries of one step (zero map at t = 0: the
 // initial state is data, not an unknown)
 __device__ __forceinline__ void step_terms(const CellIn& pv, const float pg[4], const float sv[4],
-                                           float rz, float ri, float rf, float ro, bool sig, int t,
+                                           float rz, float ri, float rf, float ro, bool sig, bool floored, int t,
                                            float a[12], float r[4]) {
   float f[4], Aj[16];
-  cell_step<true>(pv, pg[0], pg[1], pg[2], pg[3], rz, ri, rf, ro, sig, f, Aj);
+  cell_step<true>(pv, pg[0], pg[1], pg[2], pg[3], rz, ri, rf, ro, sig, floored, f, Aj);
 #pragma unroll
   for (int k = 0; k < 4; ++k) r[k] = f[k] - sv[k];
 #pragma unroll
@@ -80,7 +80,7 @@ template <bool BF16, int TSUB>
 __global__ __launch_bounds__(kFusedBlock, SLSTM_FUSED_MIN_WAVES) void newton_iter_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S_in, float* __restrict__ S_out, int T, int d, int n_jt, int n_lg,
-    int n_tt, int anchor_stride, int sig_forget, unsigned long long* __restrict__ desc,
+    int n_tt, int anchor_stride, int cell_mode, unsigned long long* __restrict__ desc,
     unsigned int* __restrict__ tickets, int n_ctr, uint32_t epoch, Control* __restrict__ ctl,
     int k_iter, float tol) {
   if (ctl->stopped) return;
@@ -117,7 +117,8 @@ __global__ __launch_bounds__(kFusedBlock, SLSTM_FUSED_MIN_WAVES) void newton_ite
   const int t_start = t_tile + sc * TSUB;
   const i64 n_lanes_pad = static_cast<i64>(n_lg) * 64;
   const i64 my_lane = static_cast<i64>(lg) * 64 + lane_in_tile;
-  const bool sig = sig_forget != 0;
+  const bool sig = (cell_mode & kCellSigmoid) != 0;
+  const bool floored = (cell_mode & kCellFloored) != 0;
   // scalar bases of this tile's rows; 32-bit lane offsets (elements) within them
   const i64 tile_row = (static_cast<i64>(b) * T + t_tile) * 4 * static_cast<i64>(d);
   const rsrc_t rsP = make_rsrc(static_cast<const char*>(P) + tile_row * (BF16 ? 2 : 4));
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(kFusedBlock, SLSTM_FUSED_MIN_WAVES) void newton_ite
     const int t = t_start + u;
     float a[12], r[4];
     if (valid && t < T) {
-      step_terms(pv, pg[u], sv[u], rz, ri, rf, ro, sig, t, a, r);
+      step_terms(pv, pg[u], sv[u], rz, ri, rf, ro, sig, floored, t, a, r);
 #pragma unroll
       for (int k = 0; k < 4; ++k) fmax_local = fmaxf(fmax_local, abs_nan_inf(r[k]));
       pv = {sv[u][0], sv[u][1], sv[u][2], sv[u][3]};
@@ -257,7 +258,7 @@ size_t fused_desc_words(int B, int T, int d) {
 
 hipError_t launch_newton_iteration(const void* P, bool p_bf16, const float* R, const float* state0,
                                    const float* S_in, float* S_out, int B, int T, int d,
-                                   bool sig_forget, unsigned long long* desc, unsigned int* tickets,
+                                   int cell_mode, unsigned long long* desc, unsigned int* tickets,
                                    uint32_t epoch, Control* ctl, int k_iter, float tol,
                                    hipStream_t stream) {
   i64 n_jt, n_lg, n_tt;
@@ -267,7 +268,7 @@ hipError_t launch_newton_iteration(const void* P, bool p_bf16, const float* R, c
   const int stride = look_back_anchor_stride(n_lg, SLSTM_FUSED_MIN_WAVES);
   const int n_ctr = ticket_counters(n_lg);
   const dim3 grid(static_cast<unsigned>(blocks));
-  const int sig = sig_forget ? 1 : 0;
+  const int sig = cell_mode;
   if (p_bf16)
     newton_iter_kernel<true, kFusedTSub><<<grid, kFusedBlock, 0, stream>>>(
         P, R, state0, S_in, S_out, T, d, static_cast<int>(n_jt), static_cast<int>(n_lg),

@@ -41,7 +41,7 @@ constexpr int kPipeSteps = SLSTM_PIPE_STEPS;  // steps per tile
 
 __host__ __device__ constexpr int pipe_words(int K) { return 4 + 4 * K; }
 
-template <bool BF16, bool WARM, bool SIG>
+template <bool BF16, bool WARM, int CM>
 __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     float* __restrict__ S_out, float* __restrict__ h_out, int T, int d, int n_jt, int n_lg,
@@ -78,7 +78,8 @@ __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_
       __builtin_amdgcn_s_sleep(2);
     }
   };
-  constexpr bool sig = SIG;  // forget-gate form, fixed per instantiation
+  constexpr bool sig = (CM & kCellSigmoid) != 0;   // forget-gate form and read-out,
+  constexpr bool floored = (CM & kCellFloored) != 0;  // fixed per instantiation
 
   // ---- the tile's pre-activations, held for the whole solve ----
   const i64 tile_row = (static_cast<i64>(b) * T + t0) * 4 * static_cast<i64>(d);
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_
       c = fmaf(fg, c, ig * s[u][0]);
       n = fmaf(fg, n, ig);
       m = mn;
-      const float h = s[u][3] * c * rcp_fast(n);
+      const float h = s[u][3] * c * readout(n, m, floored).rD;
       s[u][0] = c;
       s[u][1] = n;
       s[u][2] = m;
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_
         const int t = t0 + u;
         if (t < T) {
           float f[4], A[16], r[4];
-          cell_step<true>(pv, p[u][0], p[u][1], p[u][2], p[u][3], rz, ri, rf, ro, sig, f, A);
+          cell_step<true>(pv, p[u][0], p[u][1], p[u][2], p[u][3], rz, ri, rf, ro, sig, floored, f, A);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             r[e] = f[e] - s[u][e];
@@ -209,7 +210,7 @@ __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_
     for (int u = 0; u < TC; ++u) {
       if (t0 + u < T) {
         float f[4];
-        cell_step<false>(pv, p[u][0], p[u][1], p[u][2], p[u][3], rz, ri, rf, ro, sig, f, nullptr);
+        cell_step<false>(pv, p[u][0], p[u][1], p[u][2], p[u][3], rz, ri, rf, ro, sig, floored, f, nullptr);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           fmax = res_max(fmax, s[u][e] - f[e]);
@@ -240,7 +241,7 @@ size_t pipe_desc_words(int B, int T, int d, int K) {
 }
 
 hipError_t launch_newton_pipe(const void* P, bool p_bf16, const float* R, const float* state0,
-                              float* S_out, float* h_out, int B, int T, int d, bool sig_forget,
+                              float* S_out, float* h_out, int B, int T, int d, int cell_mode,
                               bool warm, int K, unsigned long long* carry, unsigned int* tickets,
                               uint32_t epoch, Control* ctl, hipStream_t stream) {
   i64 n_jt, n_lg, n_tt;
@@ -250,20 +251,25 @@ hipError_t launch_newton_pipe(const void* P, bool p_bf16, const float* R, const 
   const int n_ctr = ticket_counters(n_lg);
   const dim3 grid(static_cast<unsigned>(blocks));
   const int a = static_cast<int>(n_jt), c = static_cast<int>(n_lg), e = static_cast<int>(n_tt);
-#define SLSTM_PIPE_LAUNCH(BF, WM, SG)                                                                   \
-  newton_pipe_kernel<BF, WM, SG><<<grid, kPipeBlock, 0, stream>>>(P, R, state0, S_out, h_out, T, d, a, \
-                                                                  c, e, K, carry, tickets, n_ctr,      \
-                                                                  epoch, ctl)
-#define SLSTM_PIPE_LAUNCH_SIG(BF, WM) \
-  if (sig_forget) SLSTM_PIPE_LAUNCH(BF, WM, true); else SLSTM_PIPE_LAUNCH(BF, WM, false)
+#define SLSTM_PIPE_LAUNCH(BF, WM, CM_)                                                                   \
+  newton_pipe_kernel<BF, WM, CM_><<<grid, kPipeBlock, 0, stream>>>(P, R, state0, S_out, h_out, T, d, a, \
+                                                                   c, e, K, carry, tickets, n_ctr,      \
+                                                                   epoch, ctl)
+#define SLSTM_PIPE_TT(CM_) SLSTM_PIPE_LAUNCH(true, true, CM_)
+#define SLSTM_PIPE_TF(CM_) SLSTM_PIPE_LAUNCH(true, false, CM_)
+#define SLSTM_PIPE_FT(CM_) SLSTM_PIPE_LAUNCH(false, true, CM_)
+#define SLSTM_PIPE_FF(CM_) SLSTM_PIPE_LAUNCH(false, false, CM_)
   if (p_bf16) {
-    if (warm) SLSTM_PIPE_LAUNCH_SIG(true, true);
-    else SLSTM_PIPE_LAUNCH_SIG(true, false);
+    if (warm) { SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_PIPE_TT) }
+    else { SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_PIPE_TF) }
   } else {
-    if (warm) SLSTM_PIPE_LAUNCH_SIG(false, true);
-    else SLSTM_PIPE_LAUNCH_SIG(false, false);
+    if (warm) { SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_PIPE_FT) }
+    else { SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_PIPE_FF) }
   }
-#undef SLSTM_PIPE_LAUNCH_SIG
+#undef SLSTM_PIPE_TT
+#undef SLSTM_PIPE_TF
+#undef SLSTM_PIPE_FT
+#undef SLSTM_PIPE_FF
 #undef SLSTM_PIPE_LAUNCH
   return hipGetLastError();
 }

@@ -38,7 +38,7 @@ template <bool BF16, int JMODE>
 __global__ __launch_bounds__(kResBlock, 2) void residual_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S, float* __restrict__ A, float* __restrict__ rhs, int T, int d,
-    int n_chunks, int sig_forget, Control* __restrict__ ctl, unsigned int* __restrict__ err_base,
+    int n_chunks, int cell_mode, Control* __restrict__ ctl, unsigned int* __restrict__ err_base,
     int err_stride, int stop_check_iter, float tol, float* __restrict__ h_out) {
   if (ctl != nullptr) {
     if (ctl->stopped) return;
@@ -61,7 +61,8 @@ __global__ __launch_bounds__(kResBlock, 2) void residual_kernel(
     const int t0 = chunk * kResChunk;
     const int t1 = min(T, t0 + kResChunk);
     const float rz = R[j], ri = R[ud + j], rf = R[2 * ud + j], ro = R[3 * ud + j];
-    const bool sig = sig_forget != 0;
+    const bool sig = (cell_mode & kCellSigmoid) != 0;
+    const bool floored = (cell_mode & kCellFloored) != 0;
     const i64 row4 = 4 * static_cast<i64>(d);  // floats per (b, t) row of a state tensor
     const float* Sb = S + static_cast<i64>(b) * T * row4;
     CellIn pv;
@@ -96,7 +97,7 @@ __global__ __launch_bounds__(kResBlock, 2) void residual_kernel(
       }
       if (t + 1 < t1) load_step(t + 1, pn, sn);
       float f[4], Aj[16];
-      cell_step<JMODE != kJacNone>(pv, pg[0], pg[1], pg[2], pg[3], rz, ri, rf, ro, sig, f, Aj);
+      cell_step<JMODE != kJacNone>(pv, pg[0], pg[1], pg[2], pg[3], rz, ri, rf, ro, sig, floored, f, Aj);
       const i64 row = static_cast<i64>(b) * T + t;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -148,7 +149,7 @@ static void launch_mode(int mode, dim3 grid, hipStream_t stream, const void* P, 
 
 hipError_t launch_residual(const void* P, bool p_bf16, const float* R, const float* state0,
                            const float* S, float* A, float* rhs, int B, int T, int d,
-                           bool sig_forget, Control* ctl, unsigned int* err_base, int err_stride,
+                           int cell_mode, Control* ctl, unsigned int* err_base, int err_stride,
                            ResidualMode mode, int stop_check_iter, float tol, hipStream_t stream,
                            float* h_out) {
   const int n_chunks = (T + kResChunk - 1) / kResChunk;
@@ -156,7 +157,7 @@ hipError_t launch_residual(const void* P, bool p_bf16, const float* R, const flo
   const unsigned gy = static_cast<unsigned>((n_chunks + kResWaves - 1) / kResWaves);
   if (B > 65535 || gy > 65535u) return hipErrorInvalidValue;
   const dim3 grid(gx, gy, static_cast<unsigned>(B));
-  const int sig = sig_forget ? 1 : 0;
+  const int sig = cell_mode;
   const int m = mode == ResidualMode::kDense ? kJacDense : (mode == ResidualMode::kSparse ? kJacSparse : kJacNone);
   if (p_bf16)
     launch_mode<true>(m, grid, stream, P, R, state0, S, A, rhs, T, d, n_chunks, sig, ctl, err_base, err_stride,

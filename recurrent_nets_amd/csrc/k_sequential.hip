@@ -18,7 +18,7 @@ template <bool BF16>
 __global__ __launch_bounds__(kSeqBlock) void sequential_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     float* __restrict__ S, float* __restrict__ h_out, float* __restrict__ final_state, int B,
-    int T, int d, int sig_forget) {
+    int T, int d, int cell_mode) {
   const i64 lane = static_cast<i64>(blockIdx.x) * kSeqBlock + threadIdx.x;
   if (lane >= static_cast<i64>(B) * d) return;
   const int b = static_cast<int>(lane / d);
@@ -26,7 +26,8 @@ __global__ __launch_bounds__(kSeqBlock) void sequential_kernel(
   const i64 dd = d;
   const i64 d4 = 4 * dd;
   const float rz = R[j], ri = R[dd + j], rf = R[2 * dd + j], ro = R[3 * dd + j];
-  const bool sig = sig_forget != 0;
+  const bool sig = (cell_mode & kCellSigmoid) != 0;
+  const bool floored = (cell_mode & kCellFloored) != 0;
   CellIn pv = {0.0f, 0.0f, 0.0f, 0.0f};
   if (state0 != nullptr) {
     const float* s0 = state0 + static_cast<i64>(b) * d4 + j;
@@ -51,7 +52,7 @@ __global__ __launch_bounds__(kSeqBlock) void sequential_kernel(
       const int t = tg + u;
       if (t < T) {
         float s[4];
-        cell_step<false>(pv, cur[u][0], cur[u][1], cur[u][2], cur[u][3], rz, ri, rf, ro, sig, s,
+        cell_step<false>(pv, cur[u][0], cur[u][1], cur[u][2], cur[u][3], rz, ri, rf, ro, sig, floored, s,
                          nullptr);
         float* sp = S + lane_base + static_cast<i64>(t) * d4;
         sp[0] = s[0];
@@ -78,11 +79,11 @@ __global__ __launch_bounds__(kSeqBlock) void sequential_kernel(
 
 hipError_t launch_sequential(const void* P, bool p_bf16, const float* R, const float* state0,
                              float* S, float* h_out, float* final_state, int B, int T, int d,
-                             bool sig_forget, hipStream_t stream) {
+                             int cell_mode, hipStream_t stream) {
   const i64 lanes = static_cast<i64>(B) * d;
   const i64 blocks = (lanes + kSeqBlock - 1) / kSeqBlock;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  const int sig = sig_forget ? 1 : 0;
+  const int sig = cell_mode;
   if (p_bf16)
     sequential_kernel<true><<<dim3(static_cast<unsigned>(blocks)), kSeqBlock, 0, stream>>>(
         P, R, state0, S, h_out, final_state, B, T, d, sig);

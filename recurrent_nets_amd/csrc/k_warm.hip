@@ -25,7 +25,7 @@
 // per workgroup, per-thread sequential sub-chunks, a DPP quad scan of sub-chunk aggregates,
 // tile aggregates and carries staged in LDS, and a decoupled look-back across tiles along T
 // with the same fixed, anchored dataflow. The re-run from each carry writes the states
-// (c, n, m, h) with h = sigma(p_o) c / n.
+// (c, n, m, h) with h = sigma(p_o) c / n (or the floored read-out, see cell.h).
 #include "cell.h"
 #include "kernels.h"
 
@@ -80,7 +80,7 @@ __device__ __forceinline__ LogAgg quad_perm_agg_m2(const LogAgg& X) {
 template <bool BF16>
 __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
     const void* __restrict__ P, const float* __restrict__ state0, float* __restrict__ S, int T,
-    int d, int sig_forget, int n_jt, int n_lg, int n_tt, int anchor_stride,
+    int d, int cell_mode, int n_jt, int n_lg, int n_tt, int anchor_stride,
     unsigned long long* __restrict__ desc, unsigned int* __restrict__ tickets, int n_ctr, uint32_t epoch) {
   __shared__ int s_tile[2];
   __shared__ LogAgg s_agg[64];
@@ -104,7 +104,8 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
   const int t_tile = tt * kWarmTile;
   const int t_start = t_tile + sc * kWarmTSub;
   const i64 n_lanes_pad = static_cast<i64>(n_lg) * 64;
-  const bool sig = sig_forget != 0;
+  const bool sig = (cell_mode & kCellSigmoid) != 0;
+  const bool floored = (cell_mode & kCellFloored) != 0;
   // scalar bases of this tile's rows, 32-bit lane offsets within them
   const i64 tile_row = (static_cast<i64>(b) * T + t_tile) * 4 * static_cast<i64>(d);
   float* Sb = S + tile_row;
@@ -238,7 +239,7 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
       Sb[o] = c;
       Sb[o + ud] = n;
       Sb[o + 2 * ud] = m;
-      Sb[o + 3 * ud] = oo[u] * c * rcp_fast(n);
+      Sb[o + 3 * ud] = oo[u] * c * readout(n, m, floored).rD;
     }
   }
 }
@@ -256,14 +257,14 @@ size_t warm_desc_words(int B, int T, int d) {
 }
 
 hipError_t launch_warm_start(const void* P, bool p_bf16, const float* state0, float* S, int B,
-                             int T, int d, bool sig_forget, unsigned long long* desc,
+                             int T, int d, int cell_mode, unsigned long long* desc,
                              unsigned int* tickets, uint32_t epoch, hipStream_t stream) {
   i64 n_jt, n_lg, n_tt;
   warm_grid(B, T, d, n_jt, n_lg, n_tt);
   const i64 blocks = n_lg * n_tt;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(blocks));
-  const int sig = sig_forget ? 1 : 0;
+  const int sig = cell_mode;
   const int stride = look_back_anchor_stride(n_lg, 2);
   const int n_ctr = ticket_counters(n_lg);
   if (p_bf16)

@@ -28,7 +28,7 @@ constexpr int kWarmChainBlock = 256;  // one feature per thread
 #endif
 constexpr int kWarmChainSteps = SLSTM_WARM_CHAIN_STEPS;  // steps per tile
 
-template <bool BF16, bool SIG>
+template <bool BF16, int CM>
 __global__ __launch_bounds__(kWarmChainBlock, SLSTM_WARM_CHAIN_MIN_WAVES) void warm_chain_kernel(
     const void* __restrict__ P, const float* __restrict__ state0, float* __restrict__ S, int T,
     int d, int n_jt, int n_lg, int n_tt, unsigned long long* __restrict__ carry,
@@ -49,7 +49,8 @@ __global__ __launch_bounds__(kWarmChainBlock, SLSTM_WARM_CHAIN_MIN_WAVES) void w
   const i64 n_lanes = static_cast<i64>(n_lg) * kWarmChainBlock;
   const i64 lane = static_cast<i64>(lg) * kWarmChainBlock + tid;
   auto carry_word = [&](int tile, int e) { return carry + (static_cast<i64>(tile) * 3 + e) * n_lanes + lane; };
-  constexpr bool sig = SIG;  // forget-gate form, fixed per instantiation
+  constexpr bool sig = (CM & kCellSigmoid) != 0;   // forget-gate form and read-out,
+  constexpr bool floored = (CM & kCellFloored) != 0;  // fixed per instantiation
 
   // the state entering the tile: prefetched from the tile before, or state0
   unsigned long long pf[3] = {0ull, 0ull, 0ull};
@@ -114,7 +115,7 @@ __global__ __launch_bounds__(kWarmChainBlock, SLSTM_WARM_CHAIN_MIN_WAVES) void w
       buf_st(c, rsS, o, 0);
       buf_st(n, rsS, o, 4u * ud);
       buf_st(m, rsS, o, 8u * ud);
-      buf_st(oo[u] * c * rcp_fast(n), rsS, o, 12u * ud);
+      buf_st(oo[u] * c * readout(n, m, floored).rD, rsS, o, 12u * ud);
     }
   }
   if (tt + 1 < n_tt) {
@@ -137,7 +138,7 @@ size_t warm_chain_desc_words(int B, int T, int d) {
 }
 
 hipError_t launch_warm_chain(const void* P, bool p_bf16, const float* state0, float* S, int B,
-                             int T, int d, bool sig_forget, unsigned long long* carry,
+                             int T, int d, int cell_mode, unsigned long long* carry,
                              unsigned int* tickets, uint32_t epoch, hipStream_t stream) {
   i64 n_jt, n_lg, n_tt;
   warm_chain_grid(B, T, d, n_jt, n_lg, n_tt);
@@ -146,16 +147,18 @@ hipError_t launch_warm_chain(const void* P, bool p_bf16, const float* state0, fl
   const dim3 grid(static_cast<unsigned>(blocks));
   const int n_ctr = ticket_counters(n_lg);
   const int a = static_cast<int>(n_jt), c = static_cast<int>(n_lg), e = static_cast<int>(n_tt);
-#define SLSTM_WARM_LAUNCH(BF, SG)                                                                          \
-  warm_chain_kernel<BF, SG><<<grid, kWarmChainBlock, 0, stream>>>(P, state0, S, T, d, a, c, e, carry, tickets, \
-                                                                  n_ctr, epoch)
+#define SLSTM_WARM_LAUNCH(BF, CM_)                                                                          \
+  warm_chain_kernel<BF, CM_><<<grid, kWarmChainBlock, 0, stream>>>(P, state0, S, T, d, a, c, e, carry, tickets, \
+                                                                   n_ctr, epoch)
+#define SLSTM_WARM_T(CM_) SLSTM_WARM_LAUNCH(true, CM_)
+#define SLSTM_WARM_F(CM_) SLSTM_WARM_LAUNCH(false, CM_)
   if (p_bf16) {
-    if (sig_forget) SLSTM_WARM_LAUNCH(true, true);
-    else SLSTM_WARM_LAUNCH(true, false);
+    SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_WARM_T)
   } else {
-    if (sig_forget) SLSTM_WARM_LAUNCH(false, true);
-    else SLSTM_WARM_LAUNCH(false, false);
+    SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_WARM_F)
   }
+#undef SLSTM_WARM_T
+#undef SLSTM_WARM_F
 #undef SLSTM_WARM_LAUNCH
   return hipGetLastError();
 }

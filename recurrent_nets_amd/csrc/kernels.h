@@ -20,14 +20,14 @@ enum class ResidualMode { kDense, kSparse, kNone };
 // err_base[slot * err_stride] (see err_publish; stride 0 for a single word).
 hipError_t launch_residual(const void* P, bool p_bf16, const float* R, const float* state0,
                            const float* S, float* A, float* rhs, int B, int T, int d,
-                           bool sig_forget, Control* ctl, unsigned int* err_base, int err_stride,
+                           int cell_mode, Control* ctl, unsigned int* err_base, int err_stride,
                            ResidualMode mode, int stop_check_iter, float tol, hipStream_t stream,
                            float* h_out = nullptr);
 
 size_t fused_desc_words(int B, int T, int d);
 hipError_t launch_newton_iteration(const void* P, bool p_bf16, const float* R, const float* state0,
                                    const float* S_in, float* S_out, int B, int T, int d,
-                                   bool sig_forget, unsigned long long* desc, unsigned int* tickets,
+                                   int cell_mode, unsigned long long* desc, unsigned int* tickets,
                                    uint32_t epoch, Control* ctl, int k_iter, float tol,
                                    hipStream_t stream);
 // chain form of the fused iteration (256 features x 8 steps per tile); `last` also writes the
@@ -36,7 +36,7 @@ long long chain_lane_groups(int B, int d);
 size_t chain_desc_words(int B, int T, int d);
 hipError_t launch_newton_chain(const void* P, bool p_bf16, const float* R, const float* state0,
                                const float* S_in, float* S_out, float* h_out, int B, int T, int d,
-                               bool sig_forget, unsigned long long* carry, unsigned int* tickets,
+                               int cell_mode, unsigned long long* carry, unsigned int* tickets,
                                uint32_t epoch, Control* ctl, int k_iter, float tol, bool last,
                                hipStream_t stream);
 // a whole fixed-count solve of the chain form in one pipelined pass (warm or zero initial
@@ -44,7 +44,7 @@ hipError_t launch_newton_chain(const void* P, bool p_bf16, const float* R, const
 constexpr int kPipeMaxIters = 4;
 size_t pipe_desc_words(int B, int T, int d, int K);
 hipError_t launch_newton_pipe(const void* P, bool p_bf16, const float* R, const float* state0,
-                              float* S_out, float* h_out, int B, int T, int d, bool sig_forget,
+                              float* S_out, float* h_out, int B, int T, int d, int cell_mode,
                               bool warm, int K, unsigned long long* carry, unsigned int* tickets,
                               uint32_t epoch, Control* ctl, hipStream_t stream);
 // after the last chain iteration: declares iterate k final when its residual met tol
@@ -62,12 +62,12 @@ hipError_t launch_scan_block4(const float* A, const float* rhs, float* x, int B,
 
 size_t warm_desc_words(int B, int T, int d);
 hipError_t launch_warm_start(const void* P, bool p_bf16, const float* state0, float* S, int B,
-                             int T, int d, bool sig_forget, unsigned long long* desc,
+                             int T, int d, int cell_mode, unsigned long long* desc,
                              unsigned int* tickets, uint32_t epoch, hipStream_t stream);
 
 size_t warm_chain_desc_words(int B, int T, int d);
 hipError_t launch_warm_chain(const void* P, bool p_bf16, const float* state0, float* S, int B,
-                             int T, int d, bool sig_forget, unsigned long long* carry,
+                             int T, int d, int cell_mode, unsigned long long* carry,
                              unsigned int* tickets, uint32_t epoch, hipStream_t stream);
 
 // backward (adjoint + cell VJP) as chains or as a scan along T, then the fixed-order sums of
@@ -77,7 +77,7 @@ size_t backward_row_floats(int B, int T, int d, bool scan);
 hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const float* state0,
                            const float* S, const float* g, const float* g_h, const float* g_final,
                            void* dP, bool dp_bf16, float* dR, float* dbias, float* dstate0,
-                           float* rows, int B, int T, int d, bool sig_forget, bool scan,
+                           float* rows, int B, int T, int d, int cell_mode, bool scan,
                            unsigned long long* desc, unsigned int* tickets, uint32_t epoch,
                            hipStream_t stream);
 
@@ -93,7 +93,7 @@ hipError_t launch_zero(float* p, i64 n_floats, hipStream_t stream);
 
 hipError_t launch_sequential(const void* P, bool p_bf16, const float* R, const float* state0,
                              float* S, float* h_out, float* final_state, int B, int T, int d,
-                             bool sig_forget, hipStream_t stream);
+                             int cell_mode, hipStream_t stream);
 
 // C = X W^T (+ bias) in bf16 MFMA with float32 accumulation; X (M x K), W (N x K), both
 // K-contiguous. With splits > 1 the K range is split and split s writes its partial product to

@@ -19,6 +19,7 @@ from . import build as _build
 OK, DIVERGED, NONFINITE, EINVAL, EWORKSPACE, EHIP = 0, 1, 2, -1, -2, -3
 F32, BF16 = 0, 1
 FORGET = {"exp": 0, "sigmoid": 1}
+READOUT = {"exact": 0, "floored": 0x100}  # OR-ed into the forget argument (SLSTM_READOUT_FLOORED)
 INIT = {"warm": 0, "zero": 1}
 SCHEDULE = {"fused": 0, "layered": 1, "fused_scan": 2, "fused_chain": 3}
 MAX_ITERS = 64
@@ -153,6 +154,11 @@ def _dev(t, name, dtypes):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _fmode(forget, readout):
+    """The C forget argument: the forget-gate form with the read-out variant OR-ed in."""
+    return FORGET[forget] | READOUT[readout]
+
+
 def _stream(stream):
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -184,13 +190,15 @@ def alloc_workspace(nbytes: int, device=None) -> torch.Tensor:
 
 def newton_forward(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, init="warm",
                    states=None, h_out=None, want_hidden=True, final_state=None, workspace=None,
-                   stream=None, stats=True, raise_on_divergence=True, schedule="fused"):
+                   stream=None, stats=True, raise_on_divergence=True, schedule="fused",
+                   readout="exact"):
     """Newton-parallel forward. Returns (states (B,T,4,d_h), h (B,T,d_h) or None, NewtonStats
     or None). With stats=False the call is asynchronous and returns no stats. A given
     ``final_state`` (B,4,d_h) tensor receives the last step's state. ``schedule`` is "fused"
     (one kernel per iteration; "fused_chain" when the lane groups cover the GPU, else
     "fused_scan"), "fused_scan", "fused_chain" or "layered" (residual + Jacobian, scan,
-    update)."""
+    update). ``readout`` is "exact" (h = o c / n) or "floored" (h = o c / max(|n|, e^{-m},
+    1e-6)); every function taking ``forget`` takes it too."""
     L = load()
     _dev(P, "P", (torch.float32, torch.bfloat16))
     _dev(R, "R", (torch.float32,))
@@ -208,7 +216,7 @@ def newton_forward(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, init="
         workspace = alloc_workspace(need, P.device)
     st = _Stats() if stats else None
     status = L.slstm_newton_forward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
-                                    _ptr(h_out), _ptr(final_state), B, T, d, FORGET[forget],
+                                    _ptr(h_out), _ptr(final_state), B, T, d, _fmode(forget, readout),
                                     int(max_iters),
                                     float(tol), INIT[init], SCHEDULE[schedule], _ptr(workspace),
                                     workspace.numel() * workspace.element_size(), _stream(stream),
@@ -231,7 +239,7 @@ def read_stats(workspace, stream=None) -> NewtonStats:
 
 
 def sequential_forward(P, R, state0=None, forget="exp", states=None, h_out=None,
-                       want_hidden=True, final_state=None, stream=None):
+                       want_hidden=True, final_state=None, stream=None, readout="exact"):
     """Step-by-step forward (also the T=1 decode step). Returns (states, h or None). A given
     ``final_state`` (B,4,d_h) tensor receives the last step's state."""
     L = load()
@@ -247,7 +255,7 @@ def sequential_forward(P, R, state0=None, forget="exp", states=None, h_out=None,
     _dev(h_out, "h_out", (torch.float32,))
     _dev(final_state, "final_state", (torch.float32,))
     status = L.slstm_sequential_forward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
-                                        _ptr(h_out), _ptr(final_state), B, T, d, FORGET[forget],
+                                        _ptr(h_out), _ptr(final_state), B, T, d, _fmode(forget, readout),
                                         _stream(stream))
     _check(status, "slstm_sequential_forward")
     return states, h_out
@@ -274,7 +282,7 @@ def input_projection(x, W, bias=None, out=None, stream=None):
     return out
 
 
-def residual_jacobian(P, R, states, state0=None, forget="exp", stream=None):
+def residual_jacobian(P, R, states, state0=None, forget="exp", stream=None, readout="exact"):
     """One residual + Jacobian evaluation. Returns (A (B,T,4,4,d), rhs = -F (B,T,4,d),
     max|F| as a 1-element device tensor)."""
     L = load()
@@ -287,7 +295,7 @@ def residual_jacobian(P, R, states, state0=None, forget="exp", stream=None):
     rhs = torch.empty((B, T, 4, d), dtype=torch.float32, device=P.device)
     err = torch.empty((1,), dtype=torch.float32, device=P.device)
     status = L.slstm_residual_jacobian(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
-                                       _ptr(A), _ptr(rhs), _ptr(err), B, T, d, FORGET[forget],
+                                       _ptr(A), _ptr(rhs), _ptr(err), B, T, d, _fmode(forget, readout),
                                        _stream(stream))
     _check(status, "slstm_residual_jacobian")
     return A, rhs, err
@@ -315,7 +323,7 @@ def scan_block4(A, rhs, out=None, workspace=None, stream=None):
 
 
 def warm_start(P, state0=None, forget="exp", out=None, workspace=None, stream=None,
-               schedule="fused"):
+               schedule="fused", readout="exact"):
     """The R-free trajectory used as the initial Newton iterate. Returns states (B,T,4,d).
     ``schedule`` picks the kernel form as in newton_forward ("fused_chain": tile-serial
     recurrences; "fused_scan" / "layered": log-space scan with look-back)."""
@@ -329,7 +337,7 @@ def warm_start(P, state0=None, forget="exp", out=None, workspace=None, stream=No
     if workspace is None:
         workspace = alloc_workspace(need, P.device)
     status = L.slstm_warm_start(_ptr(P), _p_dtype(P), _ptr(state0), _ptr(out), B, T, d,
-                                FORGET[forget], SCHEDULE[schedule], _ptr(workspace),
+                                _fmode(forget, readout), SCHEDULE[schedule], _ptr(workspace),
                                 workspace.numel(), _stream(stream))
     _check(status, "slstm_warm_start")
     return out
@@ -341,7 +349,8 @@ def backward_workspace_bytes(B: int, T: int, d_h: int, schedule: str = "fused") 
 
 def backward(P, R, states, state0=None, g_states=None, g_h=None, g_final=None, forget="exp",
              dP=None, dR=None, dstate0=None, want_dstate0=True, workspace=None, stream=None,
-             schedule="fused", dP_dtype=torch.float32, dbias=None, want_dbias=False):
+             schedule="fused", dP_dtype=torch.float32, dbias=None, want_dbias=False,
+             readout="exact"):
     """Gradients through the recurrence at the forward solution ``states`` (B,T,4,d_h).
     g_states (B,T,4,d_h), g_h (B,T,d_h) and g_final (B,4,d_h) are the loss's direct gradients
     (None: zeros). dP is float32 or bfloat16 (``dP_dtype``). Returns (dP (B,T,4,d_h),
@@ -375,7 +384,7 @@ def backward(P, R, states, state0=None, g_states=None, g_h=None, g_final=None, f
     status = L.slstm_backward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
                               _ptr(g_states), _ptr(g_h), _ptr(g_final), _ptr(dP),
                               BF16 if dP.dtype == torch.bfloat16 else F32, _ptr(dR), _ptr(dbias),
-                              _ptr(dstate0), B, T, d, FORGET[forget], SCHEDULE[schedule],
+                              _ptr(dstate0), B, T, d, _fmode(forget, readout), SCHEDULE[schedule],
                               _ptr(workspace), workspace.numel(), _stream(stream))
     _check(status, "slstm_backward")
     if dbias is not None:

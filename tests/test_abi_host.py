@@ -88,6 +88,11 @@ def test_argument_checks_return_einval(lib):
     assert _fwd(lib, tol=-1.0) == slstm.EINVAL
     assert _fwd(lib, tol=float("nan")) == slstm.EINVAL
     assert _fwd(lib, fm=7) == slstm.EINVAL
+    assert _fwd(lib, fm=0x200) == slstm.EINVAL                    # unknown flag bit
+    assert _fwd(lib, fm=0x102) == slstm.EINVAL                    # floored flag, unknown gate
+    # the floored read-out flag passes the argument checks (then the workspace check fails)
+    assert _fwd(lib, fm=0x101, wsb=100) == slstm.EWORKSPACE
+    assert _fwd(lib, fm=0x100, wsb=100) == slstm.EWORKSPACE
     assert _fwd(lib, dt=5) == slstm.EINVAL
     assert _fwd(lib, init=3) == slstm.EINVAL
     assert _fwd(lib, sched=9) == slstm.EINVAL
