@@ -29,6 +29,11 @@ What it computes, and where each step is stated:
   LAPACK solve of the assembled system.
 * input projection P = W_x x + b ("W_x is a GEMM" -- "sLSTM in this library", "API
   notes"), and its gradients dW_x = dP^T x, dx = dP W_x, dbias = sum of dP.
+* packed sequences ("sLSTM in this library", "Packed sequences"): with cu_seqlens (S + 1
+  exclusive prefix offsets) the time axis of a (1, N, ...) problem holds S sequences one after
+  the other, each started from its own state0[s] (state0 is (S, 4, d)); at a sequence start the
+  previous state is that state0 and the step's Jacobian with respect to the state before it is
+  zero (the head flag of the segmented scan), so no value crosses a sequence boundary.
 * backward ("sLSTM in this library", section "Backward": the adjoint is one reverse scan of
   the transposed Jacobians, then the cell's vector-Jacobian product for the gradients of R
   and W_x): lam_T = g_T, lam_t = g_t + A_{t+1}^T lam_{t+1}; per step the gate Jacobian
@@ -256,18 +261,45 @@ def _state0(state0, B, d):
     return np.asarray(state0, dtype=np.float64)
 
 
-def sequential(P, R, state0, forget):
+def sequence_starts(cu_seqlens, T):
+    """{t: s} for the first step t of every non-empty packed sequence s (cu_seqlens: S + 1
+    non-decreasing offsets from 0 to T)."""
+    cu = [int(v) for v in cu_seqlens]
+    if cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu, cu[1:])):
+        raise ValueError("cu_seqlens must rise from 0 to T")
+    return {cu[s]: s for s in range(len(cu) - 1) if cu[s] < cu[s + 1]}
+
+
+def final_states(S, state0, cu_seqlens):
+    """Last state of every packed sequence (S_seq, 4, d); an empty sequence keeps its state0."""
+    cu = [int(v) for v in cu_seqlens]
+    n_seq, d = len(cu) - 1, S.shape[-1]
+    s0 = _state0(state0, n_seq, d)
+    return np.stack([S[0, cu[s + 1] - 1] if cu[s + 1] > cu[s] else s0[s] for s in range(n_seq)])
+
+
+def sequential(P, R, state0, forget, cu_seqlens=None):
     """s_t = f(s_{t-1}) for t = 1..T from s_0 = state0 (zeros when None).
 
     P (B, T, 4, d), R (4, d), state0 (B, 4, d) -> states (B, T, 4, d).
     The step loop the 'sequential' solver runs ("sLSTM in this library", "API notes").
+    Packed (cu_seqlens given, B = 1, state0 (S, 4, d)): the state restarts from state0[s] at
+    the first step of sequence s.
     """
     P = np.asarray(P, dtype=np.float64)
     R = np.asarray(R, dtype=np.float64)
     B, T, _, d = P.shape
-    s = _state0(state0, B, d)
     out = np.empty((B, T, 4, d))
+    if cu_seqlens is None:
+        s = _state0(state0, B, d)
+        starts = {}
+    else:
+        starts = sequence_starts(cu_seqlens, T)
+        s0 = _state0(state0, len(cu_seqlens) - 1, d)
+        s = np.zeros((B, 4, d))
     for t in range(T):
+        if t in starts:
+            s = s0[starts[t]][None]
         s = cell(s, P[:, t], R, forget)
         out[:, t] = s
     return out
@@ -309,7 +341,7 @@ def unstabilised_hidden(P, R, forget, floored=False):
 # ---------------------------------------------------------------------------------------
 # Newton
 # ---------------------------------------------------------------------------------------
-def warm_start(P, state0, forget):
+def warm_start(P, state0, forget, cu_seqlens=None):
     """Initial Newton iterate: the exact trajectory with R * h_{t-1} dropped.
 
     Reading (the pages give no initial guess): with the recurrent term removed every
@@ -317,26 +349,36 @@ def warm_start(P, state0, forget):
     R = 0, started from state0's (c, n, m). The h slot is o c / n with o = sigma(p_o).
     """
     P = np.asarray(P, dtype=np.float64)
-    return sequential(P, np.zeros((4, P.shape[-1])), state0, forget)
+    return sequential(P, np.zeros((4, P.shape[-1])), state0, forget, cu_seqlens)
 
 
-def _shifted(S, state0):
-    """Previous states s_{t-1} for t = 1..T, with state0 prepended as s_0."""
+def _shifted(S, state0, cu_seqlens=None):
+    """Previous states s_{t-1} for t = 1..T, with state0 prepended as s_0 (packed: state0[s]
+    at the first step of sequence s)."""
     B, T, _, d = S.shape
     prev = np.empty_like(S)
-    prev[:, 0] = _state0(state0, B, d)
     prev[:, 1:] = S[:, :-1]
+    if cu_seqlens is None:
+        prev[:, 0] = _state0(state0, B, d)
+    else:
+        s0 = _state0(state0, len(cu_seqlens) - 1, d)
+        for t, s in sequence_starts(cu_seqlens, T).items():
+            prev[:, t] = s0[s]
     return prev
 
 
-def residual(S, P, R, state0, forget, with_jacobian=True):
+def residual(S, P, R, state0, forget, with_jacobian=True, cu_seqlens=None):
     """F_t = s_t - f(s_{t-1}) and A_t = df/ds' at s_{t-1}, for t = 1..T.
 
     S, P (B, T, 4, d) -> F (B, T, 4, d), A (B, T, 4, 4, d)  (the scan_block4 layout)
+    Packed: A is zero at every sequence start (the state before it is data).
     """
-    prev = _shifted(S, state0)
+    prev = _shifted(S, state0, cu_seqlens)
     if with_jacobian:
         fs, A = cell(prev, P, R, forget, with_jacobian=True)
+        if cu_seqlens is not None:
+            for t in sequence_starts(cu_seqlens, S.shape[1]):
+                A[:, t] = 0.0
         return S - fs, A
     return S - cell(prev, P, R, forget), None
 
@@ -377,7 +419,7 @@ def dense_solve_lane(A_lane, F_lane):
     return np.linalg.solve(J, -F_lane.reshape(-1)).reshape(T, 4)
 
 
-def backward(P, R, state0, S, g, forget, return_adjoint=False):
+def backward(P, R, state0, S, g, forget, return_adjoint=False, cu_seqlens=None, g_final=None):
     """Gradients through the recurrence of a loss L whose direct derivative with respect to the
     states is g = dL/dS.
 
@@ -389,13 +431,31 @@ def backward(P, R, state0, S, g, forget, return_adjoint=False):
       lam_T = g_T,  lam_t = g_t + A_{t+1}^T lam_{t+1}     (A_{t+1} = d s_{t+1} / d s_t)
     then per step the cell's vector-Jacobian product with the gate Jacobian G_t:
       dP_t = G_t^T lam_t,  dR = sum over b and t of dP_t * h_{t-1},  dstate0 = A_1^T lam_1.
+    g_final (B, 4, d), or (S, 4, d) when packed, is a gradient with respect to the final
+    state(s), added at the last step (of each sequence). Packed (cu_seqlens, B = 1): the
+    adjoint of the step before a sequence start takes nothing from that start, whose A^T lam
+    is dstate0[s] instead; an empty sequence passes g_final[s] to dstate0[s].
     """
     P = np.asarray(P, dtype=np.float64)
     R = np.asarray(R, dtype=np.float64)
     S = np.asarray(S, dtype=np.float64)
-    g = np.asarray(g, dtype=np.float64)
+    g = np.array(g, dtype=np.float64)
     B, T, _, d = P.shape
-    prev = _shifted(S, state0)
+    prev = _shifted(S, state0, cu_seqlens)
+    starts = {} if cu_seqlens is None else sequence_starts(cu_seqlens, T)
+    n_seq = B if cu_seqlens is None else len(cu_seqlens) - 1
+    dstate0 = np.zeros((n_seq, 4, d))
+    if g_final is not None:
+        g_final = np.asarray(g_final, dtype=np.float64)
+        if cu_seqlens is None:
+            g[:, T - 1] += g_final
+        else:
+            cu = [int(v) for v in cu_seqlens]
+            for s in range(n_seq):
+                if cu[s + 1] > cu[s]:
+                    g[0, cu[s + 1] - 1] += g_final[s]
+                else:
+                    dstate0[s] += g_final[s]
     dP = np.empty_like(P)
     dR = np.zeros((4, d))
     lam_all = np.empty_like(S)
@@ -408,13 +468,22 @@ def backward(P, R, state0, S, g, forget, return_adjoint=False):
         dP[:, t] = delta
         dR += np.sum(delta * prev[:, t, H][:, None, :], axis=0)
         lam_prev = np.einsum("bsjd,bsd->bjd", A, lam)
-        lam = g[:, t - 1] + lam_prev if t > 0 else lam_prev
+        if cu_seqlens is None:
+            if t == 0:
+                dstate0 += lam_prev
+            lam = g[:, t - 1] + lam_prev if t > 0 else lam_prev
+        else:
+            if t in starts:
+                dstate0[starts[t]] += lam_prev[0]
+                lam_prev = np.zeros_like(lam_prev)
+            if t > 0:
+                lam = g[:, t - 1] + lam_prev
     if return_adjoint:
-        return dP, dR, lam, lam_all
-    return dP, dR, lam
+        return dP, dR, dstate0, lam_all
+    return dP, dR, dstate0
 
 
-def branch_margin(P, R, state0, S, forget):
+def branch_margin(P, R, state0, S, forget, cu_seqlens=None):
     """Distance |a - i~| of every step from the tie of the running maximum m = max(a, i~), and
     the scale |l| + |m'| + |i~| of the operands that form it (a = l + m'), at the states S;
     each (B, T, d).
@@ -426,7 +495,7 @@ def branch_margin(P, R, state0, S, forget):
     """
     P = np.asarray(P, dtype=np.float64)
     R = np.asarray(R, dtype=np.float64)
-    prev = _shifted(np.asarray(S, dtype=np.float64), state0)
+    prev = _shifted(np.asarray(S, dtype=np.float64), state0, cu_seqlens)
     _, it, ft, _ = preactivations(prev, P, R)
     lf, _ = log_forget(ft, forget)
     a = lf + prev[..., M, :]
@@ -465,19 +534,22 @@ def newton_flags(e_final, tol):
     return converged, diverged, nonfinite
 
 
-def newton(P, R, state0, forget, max_iters, tol=0.0, init=INIT_WARM, return_history=False):
+def newton(P, R, state0, forget, max_iters, tol=0.0, init=INIT_WARM, return_history=False,
+           cu_seqlens=None):
     """Newton solve of the sLSTM recurrence over all T steps at once.
 
     For k = 0 .. max_iters-1: F, A at the current iterate; e_k = max|F|; stop before the
     solve when tol > 0 and e_k < tol; Delta from the block-bidiagonal system; S += Delta.
     Finally e = max|F| at the last iterate and the flags.
     Returns (S, NewtonStats) and, with return_history, the list of iterates S^0..S^iters.
+    Packed sequences (cu_seqlens) share one residual norm, so one stop decision and one set of
+    flags cover the whole pack.
     """
     P = np.asarray(P, dtype=np.float64)
     R = np.asarray(R, dtype=np.float64)
     B, T, _, d = P.shape
     if init == INIT_WARM:
-        S = warm_start(P, state0, forget)
+        S = warm_start(P, state0, forget, cu_seqlens)
     elif init == INIT_ZERO:
         S = np.zeros((B, T, 4, d))
     else:
@@ -487,7 +559,7 @@ def newton(P, R, state0, forget, max_iters, tol=0.0, init=INIT_WARM, return_hist
     with np.errstate(all="ignore"):
         stopped = False
         for _ in range(max_iters):
-            F, A = residual(S, P, R, state0, forget)
+            F, A = residual(S, P, R, state0, forget, cu_seqlens=cu_seqlens)
             e = max_abs(F)
             stats.max_abs_F.append(e)
             if tol > 0 and e < tol:
@@ -498,7 +570,7 @@ def newton(P, R, state0, forget, max_iters, tol=0.0, init=INIT_WARM, return_hist
             if return_history:
                 hist.append(S.copy())
         if not stopped:
-            F, _ = residual(S, P, R, state0, forget, with_jacobian=False)
+            F, _ = residual(S, P, R, state0, forget, with_jacobian=False, cu_seqlens=cu_seqlens)
             stats.max_abs_F.append(max_abs(F))
     e_final = stats.max_abs_F[-1]
     stats.converged, stats.diverged, stats.nonfinite = newton_flags(e_final, tol)

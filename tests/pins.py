@@ -450,6 +450,83 @@ def pin_backward_finite_differences(ref):
             assert abs(fd(2, idx) - ds0[idx]) < 1e-6 * scale, (forget, "state0", idx)
 
 
+def _packed_problem(seed, lengths, d=5, forget="exp"):
+    """A packed problem: sequences of the given lengths (empty and length-1 ones included) one
+    after the other along T, each with its own state0."""
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(int)
+    T = int(cu[-1])
+    P, R = small_problem(seed, B=1, T=T, d=d, forget=forget)
+    rng = np.random.default_rng(seed + 3)
+    n = len(lengths)
+    s0 = np.stack([rng.uniform(-0.5, 0.5, (n, d)), rng.uniform(0.5, 2.0, (n, d)),
+                   rng.uniform(-2.0, 2.0, (n, d)), rng.uniform(-0.9, 0.9, (n, d))], axis=1)
+    return P, R, s0, cu
+
+
+PACKED_LENGTHS = [7, 0, 1, 12, 3, 0, 9]
+
+
+def pin_packed_equals_separate(ref):
+    """Packed sequences ("sLSTM in this library", "Packed sequences") are independent problems:
+    the sequential forward, the warm start and a fixed-count Newton solve of the pack equal those
+    of each sequence alone from its own state0, concatenated; final states are each sequence's
+    last state (state0 for an empty one)."""
+    for forget in ("exp", "sigmoid"):
+        P, R, s0, cu = _packed_problem(71, PACKED_LENGTHS, forget=forget)
+        seq = ref.sequential(P, R, s0, forget, cu_seqlens=cu)
+        warm = ref.warm_start(P, s0, forget, cu_seqlens=cu)
+        newt, st = ref.newton(P, R, s0, forget, 3, cu_seqlens=cu)
+        fin = ref.final_states(seq, s0, cu)
+        for s in range(len(PACKED_LENGTHS)):
+            a, b = cu[s], cu[s + 1]
+            if a == b:
+                np.testing.assert_array_equal(fin[s], s0[s])
+                continue
+            one = ref.sequential(P[:, a:b], R, s0[s:s + 1], forget)
+            np.testing.assert_allclose(seq[:, a:b], one, rtol=1e-13, atol=1e-15)
+            np.testing.assert_allclose(warm[:, a:b], ref.warm_start(P[:, a:b], s0[s:s + 1], forget),
+                                       rtol=1e-13, atol=1e-15)
+            S1, _ = ref.newton(P[:, a:b], R, s0[s:s + 1], forget, 3)
+            np.testing.assert_allclose(newt[:, a:b], S1, rtol=1e-12, atol=1e-14)
+            np.testing.assert_array_equal(fin[s], seq[0, b - 1])
+
+
+def pin_packed_early_stop_is_global(ref):
+    """One residual norm covers the pack: each iterate's max|F| is the largest over the
+    sequences solved alone, and the stop comes when that maximum meets the tolerance."""
+    P, R, s0, cu = _packed_problem(73, [30, 5, 40], forget="sigmoid")
+    tol = 1e-6
+    _, st = ref.newton(P, R, s0, "sigmoid", 8, tol=tol, cu_seqlens=cu)
+    alone = [ref.newton(P[:, cu[s]:cu[s + 1]], R, s0[s:s + 1], "sigmoid", 8)[1].max_abs_F for s in range(3)]
+    glob = [max(h[k] for h in alone) for k in range(9)]
+    stop = next((k for k in range(9) if glob[k] < tol), None)
+    assert stop is not None and st.iters == stop and st.converged
+    np.testing.assert_allclose(st.max_abs_F, glob[:stop + 1], rtol=1e-6, atol=1e-15)
+
+
+def pin_packed_backward(ref):
+    """The packed backward is the backward of each sequence alone: dP concatenated, dR summed,
+    dstate0 per sequence (an empty sequence passes its final-state gradient to its state0),
+    with the final-state gradients added at each sequence's last step."""
+    P, R, s0, cu = _packed_problem(75, PACKED_LENGTHS)
+    S = ref.sequential(P, R, s0, "exp", cu_seqlens=cu)
+    rng = np.random.default_rng(76)
+    g = rng.standard_normal(S.shape)
+    gf = rng.standard_normal(s0.shape)
+    dP, dR, ds0 = ref.backward(P, R, s0, S, g, "exp", cu_seqlens=cu, g_final=gf)
+    dR_sum = np.zeros_like(dR)
+    for s in range(len(PACKED_LENGTHS)):
+        a, b = cu[s], cu[s + 1]
+        if a == b:
+            np.testing.assert_array_equal(ds0[s], gf[s])
+            continue
+        d1, r1, s1 = ref.backward(P[:, a:b], R, s0[s:s + 1], S[:, a:b], g[:, a:b], "exp", g_final=gf[s:s + 1])
+        np.testing.assert_allclose(dP[:, a:b], d1, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(ds0[s], s1[0], rtol=1e-12, atol=1e-14)
+        dR_sum += r1
+    np.testing.assert_allclose(dR, dR_sum, rtol=1e-12, atol=1e-13)
+
+
 def pin_backward_adjoint_dense(ref):
     """The reverse recurrence solves the transposed block-bidiagonal system: its adjoint equals a
     dense LAPACK solve of J^T lam = g for every lane (J the forward Newton matrix)."""

@@ -51,6 +51,10 @@ MUTATIONS = [
     ("floored read-out: m derivative dropped", "np.where(on_m, -em, 0.0)", "np.where(on_m, 0.0 * em, 0.0)"),
     ("floored read-out: n branch without the floor", "on_n = (an >= em) & (an >= READOUT_FLOOR)",
      "on_n = an >= READOUT_FLOOR"),
+    ("packed: no restart from state0", "            prev[:, t] = s0[s]\n", "            pass\n"),
+    ("packed: Jacobian not cut at starts", "                A[:, t] = 0.0\n", "                pass\n"),
+    ("packed backward: adjoint leaks across a start", "                lam_prev = np.zeros_like(lam_prev)\n",
+     "                pass\n"),
     ("weight gradient: transposed operand", "dW = (dP2.T @ x.reshape(B * T, d_in)).reshape(g, d_h, d_in)",
      "dW = (dP2.T @ x.reshape(B * T, d_in)[::-1]).reshape(g, d_h, d_in)"),
     ("input gradient: gate rows swapped", "dx = (dP2 @ W.reshape(g * d_h, d_in)).reshape(B, T, d_in)",
