@@ -283,6 +283,48 @@ slstm_status slstm_input_projection_backward(const void* x, const void* W_x, con
                                              size_t workspace_bytes, void* stream);
 
 /*
+ * Packed sequences ([SL] "Packed sequences"; "Scan backend" item 4): S ragged sequences laid
+ * end to end along time in one row, B = 1. Sequence s covers steps cu_seqlens[s] ..
+ * cu_seqlens[s+1] - 1 of P, states, h_out and the gradients (cu_seqlens: exclusive prefix sums
+ * of the lengths, S + 1 entries, cu_seqlens[0] = 0, non-decreasing, cu_seqlens[S] = T; empty
+ * sequences allowed). Each sequence starts from its own initial state: state0 is (S, 4, d_h)
+ * or NULL (zeros), and the step at each sequence's start does not depend on the step before
+ * it (the head flag of the segmented (J, r) scan: that step's Jacobian is zero).
+ *   cu_seqlens   device pointer to S + 1 int32 values, 4-byte aligned; its contents are read
+ *                by the kernels and not checked (a malformed array gives unspecified results,
+ *                every access staying in bounds). n_seqs = S, 1 .. 2^24.
+ *   final_state  (S, 4, d_h): each sequence's last state (its state0 for an empty one).
+ *   g_final      (S, 4, d_h): added at each sequence's last step (an empty sequence passes it
+ *                to its dstate0).  dstate0 (S, 4, d_h).
+ * Everything else is as in the entry point without the suffix, at B = 1. The packed forms run
+ * the scan kernels: SLSTM_SCHEDULE_FUSED means SLSTM_SCHEDULE_FUSED_SCAN (size the workspace
+ * with that schedule), SLSTM_SCHEDULE_LAYERED is accepted by the Newton solve and the warm
+ * start, and SLSTM_SCHEDULE_FUSED_CHAIN is rejected.
+ */
+slstm_status slstm_newton_forward_varlen(const void* P, slstm_dtype P_dtype, const float* R,
+                                         const float* state0, const int* cu_seqlens, int n_seqs,
+                                         float* states, float* h_out, float* final_state, int T,
+                                         int d_h, slstm_forget fmode, int max_iters, float tol,
+                                         slstm_init init, slstm_schedule schedule, void* workspace,
+                                         size_t workspace_bytes, void* stream,
+                                         slstm_newton_stats* stats);
+slstm_status slstm_sequential_forward_varlen(const void* P, slstm_dtype P_dtype, const float* R,
+                                             const float* state0, const int* cu_seqlens, int n_seqs,
+                                             float* states, float* h_out, float* final_state, int T,
+                                             int d_h, slstm_forget fmode, void* stream);
+slstm_status slstm_warm_start_varlen(const void* P, slstm_dtype P_dtype, const float* state0,
+                                     const int* cu_seqlens, int n_seqs, float* states, int T, int d_h,
+                                     slstm_forget fmode, slstm_schedule schedule, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+slstm_status slstm_backward_varlen(const void* P, slstm_dtype P_dtype, const float* R,
+                                   const float* state0, const int* cu_seqlens, int n_seqs,
+                                   const float* states, const float* g_states, const float* g_h,
+                                   const float* g_final, void* dP, slstm_dtype dP_dtype, float* dR,
+                                   float* dbias, float* dstate0, int T, int d_h, slstm_forget fmode,
+                                   slstm_schedule schedule, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
  * Kernel timing with HIP events recorded on the launching stream around every kernel the
  * library launches, for measurement. Off by default; process-wide; not thread-safe.
  * slstm_profile_read waits for the recorded events and returns the summed duration (ms) and

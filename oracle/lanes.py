@@ -140,3 +140,96 @@ def sequential_lanes(P, R, state0, forget, lanes=None, workers=None, block=2048)
     finally:
         _SHARED.clear()
     return np.concatenate(outs, axis=0)
+
+
+# ---- packed sequences by groups of whole sequences --------------------------------------------
+# Packed sequences ("sLSTM in this library", "Packed sequences") are independent problems: each
+# starts from its own state0 and nothing crosses a boundary, forward or backward. A long pack is
+# therefore cut into runs of whole sequences, each run solved by the oracle as a pack of its own
+# in a worker process, and the results laid back end to end (dR summed over the runs). Without
+# an early stop the Newton iterates are per lane and per sequence too.
+
+def packed_groups(cu_seqlens, n_groups):
+    """Cut S packed sequences into at most n_groups runs (s_begin, s_end) of whole sequences
+    with about equal step counts; every run holds at least one step."""
+    cu = [int(v) for v in cu_seqlens]
+    S, T = len(cu) - 1, cu[-1]
+    target = max(1, -(-T // max(1, n_groups)))
+    groups, a = [], 0
+    for s in range(S):
+        if cu[s + 1] - cu[a] >= target:
+            groups.append([a, s + 1])
+            a = s + 1
+    if a < S:
+        if groups and cu[S] == cu[a]:
+            groups[-1][1] = S    # trailing empty sequences join the run before them
+        else:
+            groups.append([a, S])
+    return [tuple(g) for g in groups]
+
+
+def _packed_part(s_a, s_b):
+    cu = _SHARED["cu"]
+    t0, t1 = cu[s_a], cu[s_b]
+    state0 = _SHARED["state0"]
+    s0 = None if state0 is None else state0[s_a:s_b]
+    return t0, t1, np.asarray(cu[s_a:s_b + 1]) - t0, s0
+
+
+def _packed_sequential_part(args):
+    s_a, s_b, forget = args
+    t0, t1, cu, s0 = _packed_part(s_a, s_b)
+    return ref.sequential(_SHARED["P"][:, t0:t1], _SHARED["R"], s0, forget, cu_seqlens=cu)
+
+
+def _packed_newton_part(args):
+    s_a, s_b, forget, K, init = args
+    t0, t1, cu, s0 = _packed_part(s_a, s_b)
+    S, st = ref.newton(_SHARED["P"][:, t0:t1], _SHARED["R"], s0, forget, K, tol=0.0, init=init, cu_seqlens=cu)
+    return S, st.max_abs_F
+
+
+def _packed_backward_part(args):
+    s_a, s_b, forget = args
+    t0, t1, cu, s0 = _packed_part(s_a, s_b)
+    gf = _SHARED["g_final"]
+    return ref.backward(_SHARED["P"][:, t0:t1], _SHARED["R"], s0, _SHARED["S"][:, t0:t1], _SHARED["g"][:, t0:t1],
+                        forget, cu_seqlens=cu, g_final=None if gf is None else gf[s_a:s_b])
+
+
+def _packed_run(fn, cu_seqlens, extra, workers, **arrays):
+    workers = default_workers() if workers is None else workers
+    groups = packed_groups(cu_seqlens, 4 * workers)
+    _SHARED.update(cu=[int(v) for v in cu_seqlens], **{k: (None if v is None else as_f64(v)) for k, v in arrays.items()})
+    try:
+        return groups, _run(fn, [(a, b, *extra) for a, b in groups], workers)
+    finally:
+        _SHARED.clear()
+
+
+def packed_sequential(P, R, state0, forget, cu_seqlens, workers=None):
+    """ref.sequential(P, R, state0, forget, cu_seqlens=...) computed by runs of sequences."""
+    _, outs = _packed_run(_packed_sequential_part, cu_seqlens, (forget,), workers, P=P, R=R, state0=state0)
+    return np.concatenate(outs, axis=1)
+
+
+def packed_newton(P, R, state0, forget, max_iters, cu_seqlens, init=ref.INIT_WARM, workers=None):
+    """ref.newton(..., tol=0, cu_seqlens=...) (fixed iteration count) computed by runs of
+    sequences; max|F| of each iterate is the largest over the runs."""
+    _, outs = _packed_run(_packed_newton_part, cu_seqlens, (forget, max_iters, init), workers,
+                          P=P, R=R, state0=state0)
+    hist = [max(h[k] for _, h in outs) for k in range(max_iters + 1)]
+    st = ref.NewtonStats(iters=max_iters, max_abs_F=hist)
+    st.converged, st.diverged, st.nonfinite = ref.newton_flags(hist[-1], 0.0)
+    return np.concatenate([S for S, _ in outs], axis=1), st
+
+
+def packed_backward(P, R, state0, S, g, forget, cu_seqlens, g_final=None, workers=None):
+    """ref.backward(..., cu_seqlens=..., g_final=...) computed by runs of sequences -> (dP, dR,
+    dstate0); dR is the sum of the runs' sums."""
+    groups, outs = _packed_run(_packed_backward_part, cu_seqlens, (forget,), workers, P=P, R=R, state0=state0,
+                               S=S, g=g, g_final=g_final)
+    dP = np.concatenate([o[0] for o in outs], axis=1)
+    dR = np.sum([o[1] for o in outs], axis=0)
+    dstate0 = np.concatenate([o[2] for o in outs], axis=0)
+    return dP, dR, dstate0

@@ -180,12 +180,13 @@ size_t warm_desc_words_for(int B, int T, int d, bool chain) {
 }
 
 hipError_t launch_warm(const void* P, bool bf16, const float* state0, float* S, int B, int T, int d,
-                       int cm, bool chain, unsigned long long* desc, Control* ctl, hipStream_t st) {
+                       int cm, bool chain, unsigned long long* desc, Control* ctl, hipStream_t st,
+                       slstm::Seqs seqs) {
   const uint32_t ep = next_epoch();
   unsigned int* tickets = slstm::spread_of(ctl)->ticket[slstm::kTicketWarm][0];
   return timed(SLSTM_KERNEL_WARM_START, st, [&] {
     return chain ? slstm::launch_warm_chain(P, bf16, state0, S, B, T, d, cm, desc, tickets, ep, st)
-                 : slstm::launch_warm_start(P, bf16, state0, S, B, T, d, cm, desc, tickets, ep, st);
+                 : slstm::launch_warm_start(P, bf16, state0, S, B, T, d, cm, desc, tickets, ep, st, seqs);
   });
 }
 
@@ -263,7 +264,7 @@ __global__ void store_u32_kernel(unsigned int* p, unsigned int v) { *p = v; }
 hipError_t iterate(const void* P, bool bf16, const float* R, const float* state0, float* states,
                    float* h_out, int B, int T, int d_h, int cm, int max_iters, float tol,
                    slstm_init init, Form form, const NewtonLayout& L, void* workspace, Control* ctl,
-                   unsigned int* tickets, hipStream_t st) {
+                   unsigned int* tickets, hipStream_t st, slstm::Seqs seqs) {
   auto* desc = at<unsigned long long>(workspace, L.desc);
   const i64 n_state = static_cast<i64>(B) * T * 4 * d_h;
   // iterate buffers: the layered schedule updates `states` in place; the fused one alternates
@@ -276,7 +277,7 @@ hipError_t iterate(const void* P, bool bf16, const float* R, const float* state0
     buf[1] = (max_iters % 2 == 0) ? other : states;
   }
   if (init == SLSTM_INIT_WARM) {
-    HIP_RET(launch_warm(P, bf16, state0, buf[0], B, T, d_h, cm, form == Form::kChain, desc, ctl, st));
+    HIP_RET(launch_warm(P, bf16, state0, buf[0], B, T, d_h, cm, form == Form::kChain, desc, ctl, st, seqs));
   } else {
     HIP_RET(slstm::launch_zero(buf[0], n_state, st));
   }
@@ -297,7 +298,7 @@ hipError_t iterate(const void* P, bool bf16, const float* R, const float* state0
       const uint32_t ep = next_epoch();
       HIP_RET(timed(SLSTM_KERNEL_NEWTON_ITERATION, st, [&] {
         return slstm::launch_newton_iteration(P, bf16, R, state0, buf[k % 2], buf[(k + 1) % 2], B, T, d_h,
-                                              cm, desc, tickets, ep, ctl, k, tol, st);
+                                              cm, desc, tickets, ep, ctl, k, tol, st, seqs);
       }));
     }
   } else {
@@ -306,7 +307,8 @@ hipError_t iterate(const void* P, bool bf16, const float* R, const float* state0
     for (int k = 0; k < max_iters; ++k) {
       HIP_RET(timed(SLSTM_KERNEL_RESIDUAL_JACOBIAN, st, [&] {
         return slstm::launch_residual(P, bf16, R, state0, states, A, rhs, B, T, d_h, cm, ctl,
-                                      &slstm::spread_of(ctl)->err[0][k], slstm::kErrSlotWords, slstm::ResidualMode::kSparse, -1, tol, st);
+                                      &slstm::spread_of(ctl)->err[0][k], slstm::kErrSlotWords,
+                                      slstm::ResidualMode::kSparse, -1, tol, st, nullptr, seqs);
       }));
       const uint32_t ep = next_epoch();
       HIP_RET(timed(SLSTM_KERNEL_SCAN_BLOCK4, st, [&] {
@@ -322,7 +324,7 @@ hipError_t iterate(const void* P, bool bf16, const float* R, const float* state0
     HIP_RET(timed(SLSTM_KERNEL_FINAL_RESIDUAL, st, [&] {
       return slstm::launch_residual(P, bf16, R, state0, buf[max_iters % 2], nullptr, nullptr, B, T, d_h, cm,
                                     ctl, &slstm::spread_of(ctl)->err[0][max_iters], slstm::kErrSlotWords,
-                                    slstm::ResidualMode::kNone, chk, tol, st, h_out);
+                                    slstm::ResidualMode::kNone, chk, tol, st, h_out, seqs);
     }));
   }
   if (form != Form::kLayered)
@@ -408,6 +410,146 @@ int look_back_anchor_stride(long long n_lane_groups, int wgs_per_cu) {
 
 }  // namespace slstm
 
+namespace {
+
+// packed sequences: the offsets array's contents stay on the device and are not checked here;
+// the kernels keep every access in bounds whatever they hold
+slstm_status check_seqs(const int* cu_seqlens, int n_seqs, slstm::Seqs& seqs) {
+  if (cu_seqlens == nullptr || !aligned(cu_seqlens, 4))
+    return fail(SLSTM_EINVAL, "cu_seqlens must be a non-NULL, 4-byte aligned device pointer");
+  if (n_seqs < 1 || n_seqs > (1 << 24)) return fail(SLSTM_EINVAL, "n_seqs must be in 1..16777216 (got %d)", n_seqs);
+  seqs.cu = cu_seqlens;
+  seqs.n = n_seqs;
+  return SLSTM_OK;
+}
+
+slstm_status newton_forward(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
+                            float* states, float* h_out, float* final_state, int B, int T, int d_h,
+                            slstm_forget fmode, int max_iters, float tol, slstm_init init,
+                            slstm_schedule schedule, void* workspace, size_t workspace_bytes,
+                            void* stream, slstm_newton_stats* stats, slstm::Seqs seqs) {
+  slstm_status s = check_common(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, fmode);
+  if (s != SLSTM_OK) return s;
+  if (max_iters < 1 || max_iters > SLSTM_MAX_ITERS)
+    return fail(SLSTM_EINVAL, "max_iters must be in 1..%d (got %d)", SLSTM_MAX_ITERS, max_iters);
+  if (!(tol >= 0.0f) || std::isinf(tol)) return fail(SLSTM_EINVAL, "tol must be finite and >= 0");
+  if (init != SLSTM_INIT_WARM && init != SLSTM_INIT_ZERO) return fail(SLSTM_EINVAL, "unknown init %d", (int)init);
+  if (!known_schedule(schedule)) return fail(SLSTM_EINVAL, "unknown schedule %d", (int)schedule);
+  if (workspace == nullptr || !aligned(workspace, kAlign))
+    return fail(SLSTM_EINVAL, "workspace must be non-NULL and 256-byte aligned");
+  if (seqs.cu != nullptr && schedule == SLSTM_SCHEDULE_FUSED_CHAIN)
+    return fail(SLSTM_EINVAL, "packed sequences run the scan and layered forms only (not FUSED_CHAIN)");
+  const Form form = seqs.cu != nullptr && schedule == SLSTM_SCHEDULE_FUSED ? Form::kScan : newton_form(B, d_h, schedule);
+  const NewtonLayout L = newton_layout(B, T, d_h, form);
+  if (workspace_bytes < L.total)
+    return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf16 = P_dtype == SLSTM_BF16;
+  const int cm = cell_mode_of(fmode);
+  Control* ctl = at<Control>(workspace, L.ctl);
+  auto* desc = at<unsigned long long>(workspace, L.desc);
+  const i64 n_state = static_cast<i64>(B) * T * 4 * d_h;
+
+  HIP_TRY(slstm::launch_init_control(ctl, st));
+  unsigned int* tickets = slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0];
+  if (seqs.cu == nullptr && pipe_solve(form, max_iters, tol)) {
+    // the whole fixed-count solve in one pass; it writes the final states, h and every residual
+    const uint32_t ep = next_epoch();
+    HIP_TRY(timed(SLSTM_KERNEL_NEWTON_SOLVE, st, [&] {
+      return slstm::launch_newton_pipe(P, bf16, R, state0, states, h_out, B, T, d_h, cm,
+                                       init == SLSTM_INIT_WARM, max_iters, desc, tickets, ep, ctl, st);
+    }));
+  } else {
+    HIP_TRY(iterate(P, bf16, R, state0, states, h_out, B, T, d_h, cm, max_iters, tol, init, form, L,
+                    workspace, ctl, tickets, st, seqs));
+  }
+  HIP_TRY(slstm::launch_finalize(ctl, tol, st));
+  if (h_out != nullptr || final_state != nullptr)
+    HIP_TRY(slstm::launch_outputs(states, h_out, final_state, B, T, d_h, ctl, st, state0, seqs));
+  if (stats == nullptr) return SLSTM_OK;
+  Control host;
+  HIP_TRY(hipMemcpyAsync(&host, ctl, sizeof(Control), hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipStreamSynchronize(st));
+  return stats_from_control(host, stats);
+}
+
+
+slstm_status sequential_forward(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
+                                float* states, float* h_out, float* final_state, int B, int T, int d_h,
+                                slstm_forget fmode, void* stream, slstm::Seqs seqs) {
+  slstm_status s = check_common(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, fmode);
+  if (s != SLSTM_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HIP_TRY(timed(SLSTM_KERNEL_SEQUENTIAL, st, [&] {
+    return slstm::launch_sequential(P, P_dtype == SLSTM_BF16, R, state0, states, h_out, final_state,
+                                    B, T, d_h, cell_mode_of(fmode), st, seqs);
+  }));
+  // packed: each sequence's final state is gathered from its last step
+  if (seqs.cu != nullptr && final_state != nullptr)
+    HIP_TRY(slstm::launch_outputs(states, nullptr, final_state, B, T, d_h, nullptr, st, state0, seqs));
+  return SLSTM_OK;
+}
+
+slstm_status warm_start(const void* P, slstm_dtype P_dtype, const float* state0, float* states, int B,
+                        int T, int d_h, slstm_forget fmode, slstm_schedule schedule, void* workspace,
+                        size_t workspace_bytes, void* stream, slstm::Seqs seqs) {
+  static const float kDummyR = 0.0f;  // R is not used by the warm start; the shared check wants one
+  slstm_status s = check_common(P, P_dtype, &kDummyR, state0, states, nullptr, nullptr, B, T, d_h, fmode);
+  if (s != SLSTM_OK) return s;
+  if (!known_schedule(schedule)) return fail(SLSTM_EINVAL, "unknown schedule %d", (int)schedule);
+  if (workspace == nullptr || !aligned(workspace, kAlign)) return fail(SLSTM_EINVAL, "workspace must be 256-byte aligned");
+  if (seqs.cu != nullptr && schedule == SLSTM_SCHEDULE_FUSED_CHAIN)
+    return fail(SLSTM_EINVAL, "packed sequences run the scan form only (not FUSED_CHAIN)");
+  const bool chain = seqs.cu == nullptr && warm_chain_form(B, d_h, schedule);
+  const ScanLayout L = scan_layout(warm_desc_words_for(B, T, d_h, chain));
+  if (workspace_bytes < L.total) return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Control* ctl = at<Control>(workspace, L.ctl);
+  HIP_TRY(slstm::launch_init_control(ctl, st));
+  HIP_TRY(launch_warm(P, P_dtype == SLSTM_BF16, state0, states, B, T, d_h, cell_mode_of(fmode),
+                      chain, at<unsigned long long>(workspace, L.desc), ctl, st, seqs));
+  return SLSTM_OK;
+}
+
+slstm_status backward(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
+                      const float* states, const float* g_states, const float* g_h, const float* g_final,
+                      void* dP, slstm_dtype dP_dtype, float* dR, float* dbias, float* dstate0, int B, int T,
+                      int d_h, slstm_forget fmode, slstm_schedule schedule, void* workspace,
+                      size_t workspace_bytes, void* stream, slstm::Seqs seqs) {
+  slstm_status s = check_common(P, P_dtype, R, state0, states, nullptr, nullptr, B, T, d_h, fmode);
+  if (s != SLSTM_OK) return s;
+  if (dP == nullptr || dR == nullptr) return fail(SLSTM_EINVAL, "dP and dR must not be NULL");
+  if (dP_dtype != SLSTM_F32 && dP_dtype != SLSTM_BF16) return fail(SLSTM_EINVAL, "unknown dP dtype %d", (int)dP_dtype);
+  if (!aligned(dP, 16) || !aligned(dR, 4) || !aligned(dbias, 4) || !aligned(dstate0, 4) ||
+      !aligned(g_states, 4) || !aligned(g_h, 4) || !aligned(g_final, 4))
+    return fail(SLSTM_EINVAL, "dP must be 16-byte aligned; gradients and dR, dbias, dstate0 4-byte aligned");
+  if (!known_schedule(schedule)) return fail(SLSTM_EINVAL, "unknown schedule %d", (int)schedule);
+  if (!backward_schedule(schedule))
+    return fail(SLSTM_EINVAL, "the backward pass has fused forms only: schedule FUSED, FUSED_SCAN or FUSED_CHAIN");
+  if (workspace == nullptr || !aligned(workspace, kAlign))
+    return fail(SLSTM_EINVAL, "workspace must be non-NULL and 256-byte aligned");
+  if (seqs.cu != nullptr && schedule == SLSTM_SCHEDULE_FUSED_CHAIN)
+    return fail(SLSTM_EINVAL, "packed sequences run the scan form only (not FUSED_CHAIN)");
+  const bool scan = backward_scan_form(B, d_h, schedule);
+  const BackwardLayout L = backward_layout(B, T, d_h, scan);
+  if (workspace_bytes < L.total)
+    return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Control* ctl = at<Control>(workspace, L.ctl);
+  HIP_TRY(slstm::launch_init_control(ctl, st));
+  const uint32_t ep = next_epoch();
+  HIP_TRY(timed(SLSTM_KERNEL_BACKWARD, st, [&] {
+    return slstm::launch_backward(P, P_dtype == SLSTM_BF16, R, state0, states, g_states, g_h, g_final, dP,
+                                  dP_dtype == SLSTM_BF16, dR, dbias, dstate0, at<float>(workspace, L.rows), B, T, d_h,
+                                  cell_mode_of(fmode), scan, at<unsigned long long>(workspace, L.desc),
+                                  slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0], ep, st, seqs);
+  }));
+  return SLSTM_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* slstm_status_string(slstm_status s) {
@@ -437,50 +579,24 @@ slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const floa
                                   slstm_schedule schedule, void* workspace,
                                   size_t workspace_bytes, void* stream, slstm_newton_stats* stats) {
   g_err[0] = '\0';
-  slstm_status s = check_common(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, fmode);
-  if (s != SLSTM_OK) return s;
-  if (max_iters < 1 || max_iters > SLSTM_MAX_ITERS)
-    return fail(SLSTM_EINVAL, "max_iters must be in 1..%d (got %d)", SLSTM_MAX_ITERS, max_iters);
-  if (!(tol >= 0.0f) || std::isinf(tol)) return fail(SLSTM_EINVAL, "tol must be finite and >= 0");
-  if (init != SLSTM_INIT_WARM && init != SLSTM_INIT_ZERO) return fail(SLSTM_EINVAL, "unknown init %d", (int)init);
-  if (!known_schedule(schedule)) return fail(SLSTM_EINVAL, "unknown schedule %d", (int)schedule);
-  if (workspace == nullptr || !aligned(workspace, kAlign))
-    return fail(SLSTM_EINVAL, "workspace must be non-NULL and 256-byte aligned");
-  const Form form = newton_form(B, d_h, schedule);
-  const NewtonLayout L = newton_layout(B, T, d_h, form);
-  if (workspace_bytes < L.total)
-    return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
-
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool bf16 = P_dtype == SLSTM_BF16;
-  const int cm = cell_mode_of(fmode);
-  Control* ctl = at<Control>(workspace, L.ctl);
-  auto* desc = at<unsigned long long>(workspace, L.desc);
-  const i64 n_state = static_cast<i64>(B) * T * 4 * d_h;
-
-  HIP_TRY(slstm::launch_init_control(ctl, st));
-  unsigned int* tickets = slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0];
-  if (pipe_solve(form, max_iters, tol)) {
-    // the whole fixed-count solve in one pass; it writes the final states, h and every residual
-    const uint32_t ep = next_epoch();
-    HIP_TRY(timed(SLSTM_KERNEL_NEWTON_SOLVE, st, [&] {
-      return slstm::launch_newton_pipe(P, bf16, R, state0, states, h_out, B, T, d_h, cm,
-                                       init == SLSTM_INIT_WARM, max_iters, desc, tickets, ep, ctl, st);
-    }));
-  } else {
-    HIP_TRY(iterate(P, bf16, R, state0, states, h_out, B, T, d_h, cm, max_iters, tol, init, form, L,
-                    workspace, ctl, tickets, st));
-  }
-  HIP_TRY(slstm::launch_finalize(ctl, tol, st));
-  if (h_out != nullptr || final_state != nullptr)
-    HIP_TRY(slstm::launch_outputs(states, h_out, final_state, B, T, d_h, ctl, st));
-  if (stats == nullptr) return SLSTM_OK;
-  Control host;
-  HIP_TRY(hipMemcpyAsync(&host, ctl, sizeof(Control), hipMemcpyDeviceToHost, st));
-  HIP_TRY(hipStreamSynchronize(st));
-  return stats_from_control(host, stats);
+  return newton_forward(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, fmode, max_iters, tol,
+                        init, schedule, workspace, workspace_bytes, stream, stats, {});
 }
 
+slstm_status slstm_newton_forward_varlen(const void* P, slstm_dtype P_dtype, const float* R,
+                                         const float* state0, const int* cu_seqlens, int n_seqs,
+                                         float* states, float* h_out, float* final_state, int T,
+                                         int d_h, slstm_forget fmode, int max_iters, float tol,
+                                         slstm_init init, slstm_schedule schedule, void* workspace,
+                                         size_t workspace_bytes, void* stream,
+                                         slstm_newton_stats* stats) {
+  g_err[0] = '\0';
+  slstm::Seqs seqs;
+  slstm_status s = check_seqs(cu_seqlens, n_seqs, seqs);
+  if (s != SLSTM_OK) return s;
+  return newton_forward(P, P_dtype, R, state0, states, h_out, final_state, 1, T, d_h, fmode, max_iters, tol,
+                        init, schedule, workspace, workspace_bytes, stream, stats, seqs);
+}
 
 slstm_status slstm_newton_read_stats(const void* workspace, size_t workspace_bytes, void* stream,
                                      slstm_newton_stats* stats) {
@@ -499,14 +615,18 @@ slstm_status slstm_sequential_forward(const void* P, slstm_dtype P_dtype, const 
                                       float* final_state, int B, int T, int d_h,
                                       slstm_forget fmode, void* stream) {
   g_err[0] = '\0';
-  slstm_status s = check_common(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, fmode);
+  return sequential_forward(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, fmode, stream, {});
+}
+
+slstm_status slstm_sequential_forward_varlen(const void* P, slstm_dtype P_dtype, const float* R,
+                                             const float* state0, const int* cu_seqlens, int n_seqs,
+                                             float* states, float* h_out, float* final_state, int T,
+                                             int d_h, slstm_forget fmode, void* stream) {
+  g_err[0] = '\0';
+  slstm::Seqs seqs;
+  slstm_status s = check_seqs(cu_seqlens, n_seqs, seqs);
   if (s != SLSTM_OK) return s;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  HIP_TRY(timed(SLSTM_KERNEL_SEQUENTIAL, st, [&] {
-    return slstm::launch_sequential(P, P_dtype == SLSTM_BF16, R, state0, states, h_out, final_state,
-                                    B, T, d_h, cell_mode_of(fmode), st);
-  }));
-  return SLSTM_OK;
+  return sequential_forward(P, P_dtype, R, state0, states, h_out, final_state, 1, T, d_h, fmode, stream, seqs);
 }
 
 slstm_status slstm_input_projection(const void* x, const void* W_x, const float* bias, float* P,
@@ -586,20 +706,19 @@ slstm_status slstm_warm_start(const void* P, slstm_dtype P_dtype, const float* s
                               slstm_schedule schedule, void* workspace, size_t workspace_bytes,
                               void* stream) {
   g_err[0] = '\0';
-  static const float kDummyR = 0.0f;  // R is not used by the warm start; the shared check wants one
-  slstm_status s = check_common(P, P_dtype, &kDummyR, state0, states, nullptr, nullptr, B, T, d_h, fmode);
+  return warm_start(P, P_dtype, state0, states, B, T, d_h, fmode, schedule, workspace, workspace_bytes, stream, {});
+}
+
+slstm_status slstm_warm_start_varlen(const void* P, slstm_dtype P_dtype, const float* state0,
+                                     const int* cu_seqlens, int n_seqs, float* states, int T, int d_h,
+                                     slstm_forget fmode, slstm_schedule schedule, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  g_err[0] = '\0';
+  slstm::Seqs seqs;
+  slstm_status s = check_seqs(cu_seqlens, n_seqs, seqs);
   if (s != SLSTM_OK) return s;
-  if (!known_schedule(schedule)) return fail(SLSTM_EINVAL, "unknown schedule %d", (int)schedule);
-  if (workspace == nullptr || !aligned(workspace, kAlign)) return fail(SLSTM_EINVAL, "workspace must be 256-byte aligned");
-  const bool chain = warm_chain_form(B, d_h, schedule);
-  const ScanLayout L = scan_layout(warm_desc_words_for(B, T, d_h, chain));
-  if (workspace_bytes < L.total) return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  Control* ctl = at<Control>(workspace, L.ctl);
-  HIP_TRY(slstm::launch_init_control(ctl, st));
-  HIP_TRY(launch_warm(P, P_dtype == SLSTM_BF16, state0, states, B, T, d_h, cell_mode_of(fmode),
-                      chain, at<unsigned long long>(workspace, L.desc), ctl, st));
-  return SLSTM_OK;
+  return warm_start(P, P_dtype, state0, states, 1, T, d_h, fmode, schedule, workspace, workspace_bytes, stream,
+                    seqs);
 }
 
 size_t slstm_backward_workspace_bytes(int B, int T, int d_h, slstm_schedule schedule) {
@@ -614,33 +733,23 @@ slstm_status slstm_backward(const void* P, slstm_dtype P_dtype, const float* R, 
                             slstm_schedule schedule, void* workspace, size_t workspace_bytes,
                             void* stream) {
   g_err[0] = '\0';
-  slstm_status s = check_common(P, P_dtype, R, state0, states, nullptr, nullptr, B, T, d_h, fmode);
+  return backward(P, P_dtype, R, state0, states, g_states, g_h, g_final, dP, dP_dtype, dR, dbias, dstate0, B, T,
+                  d_h, fmode, schedule, workspace, workspace_bytes, stream, {});
+}
+
+slstm_status slstm_backward_varlen(const void* P, slstm_dtype P_dtype, const float* R,
+                                   const float* state0, const int* cu_seqlens, int n_seqs,
+                                   const float* states, const float* g_states, const float* g_h,
+                                   const float* g_final, void* dP, slstm_dtype dP_dtype, float* dR,
+                                   float* dbias, float* dstate0, int T, int d_h, slstm_forget fmode,
+                                   slstm_schedule schedule, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  g_err[0] = '\0';
+  slstm::Seqs seqs;
+  slstm_status s = check_seqs(cu_seqlens, n_seqs, seqs);
   if (s != SLSTM_OK) return s;
-  if (dP == nullptr || dR == nullptr) return fail(SLSTM_EINVAL, "dP and dR must not be NULL");
-  if (dP_dtype != SLSTM_F32 && dP_dtype != SLSTM_BF16) return fail(SLSTM_EINVAL, "unknown dP dtype %d", (int)dP_dtype);
-  if (!aligned(dP, 16) || !aligned(dR, 4) || !aligned(dbias, 4) || !aligned(dstate0, 4) ||
-      !aligned(g_states, 4) || !aligned(g_h, 4) || !aligned(g_final, 4))
-    return fail(SLSTM_EINVAL, "dP must be 16-byte aligned; gradients and dR, dbias, dstate0 4-byte aligned");
-  if (!known_schedule(schedule)) return fail(SLSTM_EINVAL, "unknown schedule %d", (int)schedule);
-  if (!backward_schedule(schedule))
-    return fail(SLSTM_EINVAL, "the backward pass has fused forms only: schedule FUSED, FUSED_SCAN or FUSED_CHAIN");
-  if (workspace == nullptr || !aligned(workspace, kAlign))
-    return fail(SLSTM_EINVAL, "workspace must be non-NULL and 256-byte aligned");
-  const bool scan = backward_scan_form(B, d_h, schedule);
-  const BackwardLayout L = backward_layout(B, T, d_h, scan);
-  if (workspace_bytes < L.total)
-    return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  Control* ctl = at<Control>(workspace, L.ctl);
-  HIP_TRY(slstm::launch_init_control(ctl, st));
-  const uint32_t ep = next_epoch();
-  HIP_TRY(timed(SLSTM_KERNEL_BACKWARD, st, [&] {
-    return slstm::launch_backward(P, P_dtype == SLSTM_BF16, R, state0, states, g_states, g_h, g_final, dP,
-                                  dP_dtype == SLSTM_BF16, dR, dbias, dstate0, at<float>(workspace, L.rows), B, T, d_h,
-                                  cell_mode_of(fmode), scan, at<unsigned long long>(workspace, L.desc),
-                                  slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0], ep, st);
-  }));
-  return SLSTM_OK;
+  return backward(P, P_dtype, R, state0, states, g_states, g_h, g_final, dP, dP_dtype, dR, dbias, dstate0, 1, T,
+                  d_h, fmode, schedule, workspace, workspace_bytes, stream, seqs);
 }
 
 size_t slstm_input_projection_backward_workspace_bytes(int B, int T, int d_in, int d_h) {

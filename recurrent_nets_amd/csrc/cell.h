@@ -68,6 +68,13 @@ __device__ __forceinline__ Readout readout(float n, float m, bool floored) {
   return {rcp_fast(D), on_n ? copysignf(1.0f, n) : 0.0f, on_m ? -em : 0.0f};
 }
 
+// The state before the first step of sequence s (state0 (n_seqs, 4, d), zeros without one)
+__device__ __forceinline__ CellIn state0_of(const float* state0, int s, unsigned ud, unsigned j) {
+  if (state0 == nullptr) return {0.0f, 0.0f, 0.0f, 0.0f};
+  const float* s0 = state0 + static_cast<i64>(s) * 4 * static_cast<i64>(ud);
+  return {s0[j], s0[ud + j], s0[2 * ud + j], s0[3 * ud + j]};
+}
+
 // One step. Writes the next state s[4] = (c, n, m, h); with JAC also A[16] row-major
 // (A[4*row + col] = d s[row] / d prev[col]).
 //

@@ -37,6 +37,51 @@ __device__ __forceinline__ float load_p(const void* __restrict__ P, i64 idx) {
 constexpr int kCellSigmoid = 1;
 constexpr int kCellFloored = 2;
 
+// ---- packed sequences -------------------------------------------------------------------------
+// With packed sequences ("sLSTM in this library", "Packed sequences") the single batch row holds
+// n_seqs sequences one after the other along T, sequence s on steps cu[s] .. cu[s+1]-1 (cu: the
+// n_seqs + 1 exclusive prefix offsets), each started from its own state0[s]. Without them
+// (cu == nullptr) batch row b is sequence b and starts at t = 0. A cursor walks the steps of a
+// run in increasing order and names the sequence, if any, that starts at each. Every read of cu
+// stays within its n_seqs + 1 entries whatever they hold.
+// packed-sequence offsets as the launchers take them (cu == nullptr: one sequence per row)
+struct Seqs {
+  const int* cu = nullptr;
+  int n = 0;
+};
+
+struct SeqCursor {
+  const int* cu;
+  int n_seqs;
+  int s;      // the sequence holding the current step
+  int start;  // its first step
+  int end;    // one past its last step
+};
+
+// cursor at step t (t >= 0): the last sequence whose first step is <= t
+__device__ __forceinline__ SeqCursor seq_cursor(const int* cu, int n_seqs, int b, int t) {
+  if (cu == nullptr) return {nullptr, 0, b, 0, 0x7fffffff};
+  int lo = 0, hi = n_seqs - 1;  // largest s in [0, n_seqs) with cu[s] <= t (0 if none)
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  return {cu, n_seqs, lo, cu[lo], cu[lo + 1]};
+}
+
+// The sequence that starts at step t, or -1. Steps must be visited one by one in increasing
+// order (t = the cursor's step, then +1, ...).
+__device__ __forceinline__ int seq_begin(SeqCursor& c, int t) {
+  if (c.cu == nullptr) return t == 0 ? c.s : -1;
+  while (t >= c.end && c.s + 1 < c.n_seqs) {
+    ++c.s;
+    c.start = c.cu[c.s];
+    c.end = c.cu[c.s + 1];
+  }
+  return (t == c.start && t < c.end) ? c.s : -1;
+}
+
 // ---- buffer resources -------------------------------------------------------------------------
 // A buffer resource holds a wave-uniform base address in scalar registers; each access adds a
 // 32-bit per-lane byte offset (one VGPR) and a wave-uniform byte offset (an SGPR). Kernels that

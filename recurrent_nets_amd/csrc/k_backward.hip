@@ -19,7 +19,8 @@
 //   last in time first), compose their steps' maps y -> A_t^T (g_t + y) into one affine map,
 //   scan the maps across the quad and look back across tiles (quad_look_back, tiles in reverse
 //   order of time), then run their steps again from the y entering them. Parallel along T at
-//   any batch size.
+//   any batch size. With packed sequences (PACKED) the map of a sequence's first step is zero
+//   (nothing flows back across the boundary) and its A^T lam is that sequence's dstate0.
 // Each tile writes its lane's sums of dP_t h_{t-1} and of dP_t (a row of 8 d floats per batch
 // row and tile), and two small kernels add the rows in a fixed order into dR and dbias. dP is
 // written as float32 or, for the bf16 weight-gradient GEMMs, rounded to bfloat16. Every value
@@ -206,14 +207,14 @@ __global__ __launch_bounds__(kBackBlock, SLSTM_BACK_MIN_WAVES) void backward_cha
 constexpr int kBackScanBlock = 256;  // 4 waves x 16 features x 4 sub-chunks
 constexpr int kBackScanTSub = SLSTM_BACK_SCAN_TSUB;
 
-template <bool BF16, int CM, bool GS, int TSUB>
+template <bool BF16, int CM, bool GS, int TSUB, bool PACKED>
 __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void backward_scan_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S, const float* __restrict__ g, const float* __restrict__ g_h,
     const float* __restrict__ g_final, void* __restrict__ dP, int dp_bf16, float* __restrict__ dstate0,
     float* __restrict__ sum_rows, int T, int d, int n_jt, int n_lg, int n_tt, int anchor_stride,
     unsigned long long* __restrict__ desc, unsigned int* __restrict__ tickets, int n_ctr,
-    uint32_t epoch) {
+    uint32_t epoch, const int* __restrict__ cu, int n_seqs) {
   constexpr bool sig = (CM & kCellSigmoid) != 0;   // forget-gate form and read-out,
   constexpr bool floored = (CM & kCellFloored) != 0;  // fixed per instantiation
   __shared__ int s_tile[2];
@@ -250,6 +251,18 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
 
   const unsigned long long pf = quad_look_back_prefetch(desc, n_lanes_pad, my_lane, q, tr, anchor_stride);
 
+  // packed: the sequence starting at each step of the sub-chunk and the one ending there (-1: none)
+  int sq[TSUB], lq[TSUB];
+  if constexpr (PACKED) {
+    SeqCursor seq = seq_cursor(cu, n_seqs, b, t_start);
+#pragma unroll
+    for (int u = 0; u < TSUB; ++u) {
+      const int t = t_start + u;
+      sq[u] = t < T ? seq_begin(seq, t) : -1;
+      lq[u] = (t < T && t + 1 == seq.end) ? seq.s : -1;
+    }
+  }
+
   float pg[TSUB][4], sv[TSUB][4], gs[TSUB][4];
 #pragma unroll
   for (int u = 0; u < TSUB; ++u) {
@@ -272,8 +285,9 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
         for (int k = 0; k < 4; ++k) gs[u][k] = buf_ld(rsG, 4u * o, 4u * k * ud);
       }
       if (g_h != nullptr) gs[u][3] += buf_ld(rsH, 4u * (static_cast<unsigned>(sc * TSUB + u) * ud + j), 0);
-      if (g_final != nullptr && t == T - 1) {
-        const float* gf = g_final + static_cast<i64>(b) * 4 * static_cast<i64>(d);
+      const int fs = PACKED ? lq[u] : (t == T - 1 ? b : -1);  // the sequence that ends at t
+      if (g_final != nullptr && fs >= 0) {
+        const float* gf = g_final + static_cast<i64>(fs) * 4 * static_cast<i64>(d);
 #pragma unroll
         for (int k = 0; k < 4; ++k) gs[u][k] += gf[k * ud + j];
       }
@@ -313,7 +327,8 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
   for (int u = TSUB - 1; u >= 0; --u) {
     const int t = t_start + u;
     if (valid && t < T) {
-      const CellIn pv = (u == 0) ? pv0 : CellIn{sv[u - 1][0], sv[u - 1][1], sv[u - 1][2], sv[u - 1][3]};
+      CellIn pv = (u == 0) ? pv0 : CellIn{sv[u - 1][0], sv[u - 1][1], sv[u - 1][2], sv[u - 1][3]};
+      if (PACKED && sq[u] >= 0) pv = state0_of(state0, sq[u], ud, j);
       float f[4], A[16], At[16];
       cell_step<true>(pv, pg[u][0], pg[u][1], pg[u][2], pg[u][3], rz, ri, rf, ro, sig, floored, f, A);
 #pragma unroll
@@ -325,6 +340,13 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
       const float zero[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       mat4_vec(At, w, zero, v);
       mat4_mul_left(At, M);
+      if (PACKED && sq[u] >= 0) {
+        // a sequence start: nothing flows back to the step before it
+#pragma unroll
+        for (int e = 0; e < 16; ++e) M[e] = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = 0.0f;
+      }
     }
   }
 
@@ -354,7 +376,8 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
   for (int u = TSUB - 1; u >= 0; --u) {
     const int t = t_start + u;
     if (valid && t < T) {
-      const CellIn pv = (u == 0) ? pv0 : CellIn{sv[u - 1][0], sv[u - 1][1], sv[u - 1][2], sv[u - 1][3]};
+      CellIn pv = (u == 0) ? pv0 : CellIn{sv[u - 1][0], sv[u - 1][1], sv[u - 1][2], sv[u - 1][3]};
+      if (PACKED && sq[u] >= 0) pv = state0_of(state0, sq[u], ud, j);
       float lam[4], dx[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) lam[e] = gs[u][e] + y[e];
@@ -365,6 +388,15 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
         store_dp(dx[e], dpb, rsD, o, e * ud);
         dr[e] = fmaf(dx[e], pv.h, dr[e]);
         db[e] += dx[e];
+      }
+      if (PACKED && sq[u] >= 0) {
+        if (dstate0 != nullptr) {
+          float* ds = dstate0 + static_cast<i64>(sq[u]) * 4 * static_cast<i64>(d);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ds[e * ud + j] = y[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = 0.0f;
       }
     }
   }
@@ -380,7 +412,7 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
 #pragma unroll
     for (int e = 0; e < 8; ++e) rows[e * ud + j] = tot[e];
   }
-  if (valid && t_start == 0 && dstate0 != nullptr) {
+  if (!PACKED && valid && t_start == 0 && dstate0 != nullptr) {
     float* ds = dstate0 + static_cast<i64>(b) * 4 * static_cast<i64>(d);
 #pragma unroll
     for (int e = 0; e < 4; ++e) ds[e * ud + j] = y[e];
@@ -425,6 +457,19 @@ __global__ __launch_bounds__(256) void sum_chunks_kernel(const float* __restrict
   else out1[i - n0] = acc;
 }
 
+// dstate0 of the empty packed sequences: their final state is state0, so the gradient with
+// respect to state0 is g_final (zero without it)
+__global__ __launch_bounds__(256) void empty_seq_dstate0_kernel(const int* __restrict__ cu,
+                                                                const float* __restrict__ g_final,
+                                                                float* __restrict__ dstate0, int n_seqs,
+                                                                int d4) {
+  const i64 n = static_cast<i64>(n_seqs) * d4;  // (s, slot, j)
+  for (i64 o = static_cast<i64>(blockIdx.x) * 256 + threadIdx.x; o < n; o += static_cast<i64>(gridDim.x) * 256) {
+    const int s = static_cast<int>(o / d4);
+    if (cu[s] == cu[s + 1]) dstate0[o] = g_final != nullptr ? g_final[o] : 0.0f;
+  }
+}
+
 // ---- sizes and launch ---------------------------------------------------------------------------
 struct BackGrid {
   i64 n_jt, n_lg, n_tt, rows;
@@ -462,7 +507,9 @@ hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const flo
                            void* dP, bool dp_bf16, float* dR, float* dbias, float* dstate0,
                            float* rows, int B, int T, int d, int cell_mode, bool scan,
                            unsigned long long* desc, unsigned int* tickets, uint32_t epoch,
-                           hipStream_t stream) {
+                           hipStream_t stream, Seqs seqs) {
+  const bool packed = seqs.cu != nullptr;
+  if (packed && (!scan || B != 1)) return hipErrorInvalidValue;  // packed: the scan form, one row
   const BackGrid gr = back_grid(B, T, d, scan);
   const i64 blocks = gr.n_lg * gr.n_tt;
   const i64 chunk = row_chunk(gr.rows);
@@ -490,11 +537,28 @@ hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const flo
   } while (0)
   if (scan) {
     const int stride = look_back_anchor_stride(gr.n_lg, SLSTM_BACK_SCAN_MIN_WAVES);
-#define SLSTM_BACK_LAUNCH(BF, CM_, GS)                                                                             \
-  backward_scan_kernel<BF, CM_, GS, kBackScanTSub><<<grid, kBackScanBlock, 0, stream>>>(                           \
-      P, R, state0, S, g, g_h, g_final, dP, dpb, dstate0, rows, T, d, a, c, e, stride, desc, tickets, n_ctr, epoch)
-    SLSTM_BACK_DISPATCH;
+    if (packed) {
+#define SLSTM_BACK_LAUNCH(BF, CM_, GS)                                                                   \
+  backward_scan_kernel<BF, CM_, GS, kBackScanTSub, true><<<grid, kBackScanBlock, 0, stream>>>(           \
+      P, R, state0, S, g, g_h, g_final, dP, dpb, dstate0, rows, T, d, a, c, e, stride, desc, tickets, n_ctr, \
+      epoch, seqs.cu, seqs.n)
+      SLSTM_BACK_DISPATCH;
 #undef SLSTM_BACK_LAUNCH
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+      if (dstate0 != nullptr && seqs.n > 0) {
+        const i64 n = static_cast<i64>(seqs.n) * 4 * d;
+        const unsigned blocks_e = static_cast<unsigned>(std::min<i64>((n + 255) / 256, 4096));
+        empty_seq_dstate0_kernel<<<blocks_e, 256, 0, stream>>>(seqs.cu, g_final, dstate0, seqs.n, 4 * d);
+      }
+    } else {
+#define SLSTM_BACK_LAUNCH(BF, CM_, GS)                                                                   \
+  backward_scan_kernel<BF, CM_, GS, kBackScanTSub, false><<<grid, kBackScanBlock, 0, stream>>>(          \
+      P, R, state0, S, g, g_h, g_final, dP, dpb, dstate0, rows, T, d, a, c, e, stride, desc, tickets, n_ctr, \
+      epoch, nullptr, 0)
+      SLSTM_BACK_DISPATCH;
+#undef SLSTM_BACK_LAUNCH
+    }
   } else {
 #define SLSTM_BACK_LAUNCH(BF, CM_, GS)                                                                      \
   backward_chain_kernel<BF, CM_, GS><<<grid, kBackBlock, 0, stream>>>(P, R, state0, S, g, g_h, g_final, dP, \

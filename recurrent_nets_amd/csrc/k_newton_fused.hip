@@ -17,6 +17,11 @@
 // the residual and the write of the new iterate. The step before a sub-chunk comes from the
 // neighbouring thread of the quad or, for the first, from S_k, which this launch never writes.
 //
+// Packed sequences (PACKED): at the first step of each sequence the state before it is that
+// sequence's state0 and its Jacobian is zero, so the composed maps restart there (the head
+// flag of the segmented scan); every thread finds the sequences its steps belong to with a
+// SeqCursor.
+//
 // The residual maximum of S_k goes to the spread slots. Early stop is exact although the
 // update of iteration k is formed together with F_k: the next launch (or the final residual
 // pass) finds max|F_k| < tol and declares S_k final; S_k is still intact in the other buffer.
@@ -63,26 +68,26 @@ __device__ __forceinline__ void load_sub_chunk(rsrc_t rsP, rsrc_t rsS, unsigned 
   }
 }
 
-// residual r = f(s') - s and the 12 Jacobian entries of one step (zero map at t = 0: the
-// initial state is data, not an unknown)
+// residual r = f(s') - s and the 12 Jacobian entries of one step (zero map at a sequence
+// start: the state before it is data, not an unknown)
 __device__ __forceinline__ void step_terms(const CellIn& pv, const float pg[4], const float sv[4],
-                                           float rz, float ri, float rf, float ro, bool sig, bool floored, int t,
-                                           float a[12], float r[4]) {
+                                           float rz, float ri, float rf, float ro, bool sig, bool floored,
+                                           bool start, float a[12], float r[4]) {
   float f[4], Aj[16];
   cell_step<true>(pv, pg[0], pg[1], pg[2], pg[3], rz, ri, rf, ro, sig, floored, f, Aj);
 #pragma unroll
   for (int k = 0; k < 4; ++k) r[k] = f[k] - sv[k];
 #pragma unroll
-  for (int q = 0; q < 12; ++q) a[q] = (t == 0) ? 0.0f : Aj[kSpPlane[q]];
+  for (int q = 0; q < 12; ++q) a[q] = start ? 0.0f : Aj[kSpPlane[q]];
 }
 
-template <bool BF16, int TSUB>
+template <bool BF16, int TSUB, bool PACKED>
 __global__ __launch_bounds__(kFusedBlock, SLSTM_FUSED_MIN_WAVES) void newton_iter_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S_in, float* __restrict__ S_out, int T, int d, int n_jt, int n_lg,
     int n_tt, int anchor_stride, int cell_mode, unsigned long long* __restrict__ desc,
     unsigned int* __restrict__ tickets, int n_ctr, uint32_t epoch, Control* __restrict__ ctl,
-    int k_iter, float tol) {
+    int k_iter, float tol, const int* __restrict__ cu, int n_seqs) {
   if (ctl->stopped) return;
   if (k_iter > 0 && tol > 0.0f && err_reduced(ctl, k_iter - 1) < tol) {
     // the previous iterate already met the tolerance: it is the result
@@ -161,12 +166,20 @@ __global__ __launch_bounds__(kFusedBlock, SLSTM_FUSED_MIN_WAVES) void newton_ite
   float M[16], v[4];
   float fmax_local = 0.0f;
   CellIn pv = pv0;
+  SeqCursor seq;
+  if constexpr (PACKED) seq = seq_cursor(cu, n_seqs, b, t_start);
 #pragma unroll
   for (int u = 0; u < TSUB; ++u) {
     const int t = t_start + u;
     float a[12], r[4];
     if (valid && t < T) {
-      step_terms(pv, pg[u], sv[u], rz, ri, rf, ro, sig, floored, t, a, r);
+      bool start = t == 0;
+      if constexpr (PACKED) {
+        const int sq = seq_begin(seq, t);
+        start = sq >= 0;
+        if (start) pv = state0_of(state0, sq, ud, j);
+      }
+      step_terms(pv, pg[u], sv[u], rz, ri, rf, ro, sig, floored, start, a, r);
 #pragma unroll
       for (int k = 0; k < 4; ++k) fmax_local = fmaxf(fmax_local, abs_nan_inf(r[k]));
       pv = {sv[u][0], sv[u][1], sv[u][2], sv[u][3]};
@@ -260,7 +273,7 @@ hipError_t launch_newton_iteration(const void* P, bool p_bf16, const float* R, c
                                    const float* S_in, float* S_out, int B, int T, int d,
                                    int cell_mode, unsigned long long* desc, unsigned int* tickets,
                                    uint32_t epoch, Control* ctl, int k_iter, float tol,
-                                   hipStream_t stream) {
+                                   hipStream_t stream, Seqs seqs) {
   i64 n_jt, n_lg, n_tt;
   fused_grid(B, T, d, n_jt, n_lg, n_tt);
   const i64 blocks = n_lg * n_tt;
@@ -269,14 +282,19 @@ hipError_t launch_newton_iteration(const void* P, bool p_bf16, const float* R, c
   const int n_ctr = ticket_counters(n_lg);
   const dim3 grid(static_cast<unsigned>(blocks));
   const int sig = cell_mode;
-  if (p_bf16)
-    newton_iter_kernel<true, kFusedTSub><<<grid, kFusedBlock, 0, stream>>>(
-        P, R, state0, S_in, S_out, T, d, static_cast<int>(n_jt), static_cast<int>(n_lg),
-        static_cast<int>(n_tt), stride, sig, desc, tickets, n_ctr, epoch, ctl, k_iter, tol);
-  else
-    newton_iter_kernel<false, kFusedTSub><<<grid, kFusedBlock, 0, stream>>>(
-        P, R, state0, S_in, S_out, T, d, static_cast<int>(n_jt), static_cast<int>(n_lg),
-        static_cast<int>(n_tt), stride, sig, desc, tickets, n_ctr, epoch, ctl, k_iter, tol);
+#define SLSTM_FUSED_LAUNCH(BF, PK)                                                                   \
+  newton_iter_kernel<BF, kFusedTSub, PK><<<grid, kFusedBlock, 0, stream>>>(                          \
+      P, R, state0, S_in, S_out, T, d, static_cast<int>(n_jt), static_cast<int>(n_lg),                \
+      static_cast<int>(n_tt), stride, sig, desc, tickets, n_ctr, epoch, ctl, k_iter, tol, seqs.cu, seqs.n)
+  const bool packed = seqs.cu != nullptr;
+  if (p_bf16) {
+    if (packed) SLSTM_FUSED_LAUNCH(true, true);
+    else SLSTM_FUSED_LAUNCH(true, false);
+  } else {
+    if (packed) SLSTM_FUSED_LAUNCH(false, true);
+    else SLSTM_FUSED_LAUNCH(false, false);
+  }
+#undef SLSTM_FUSED_LAUNCH
   return hipGetLastError();
 }
 

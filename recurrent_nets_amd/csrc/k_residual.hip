@@ -39,7 +39,8 @@ __global__ __launch_bounds__(kResBlock, 2) void residual_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S, float* __restrict__ A, float* __restrict__ rhs, int T, int d,
     int n_chunks, int cell_mode, Control* __restrict__ ctl, unsigned int* __restrict__ err_base,
-    int err_stride, int stop_check_iter, float tol, float* __restrict__ h_out) {
+    int err_stride, int stop_check_iter, float tol, float* __restrict__ h_out,
+    const int* __restrict__ cu, int n_seqs) {
   if (ctl != nullptr) {
     if (ctl->stopped) return;
     if (stop_check_iter >= 0 && tol > 0.0f && err_reduced(ctl, stop_check_iter) < tol) {
@@ -65,18 +66,12 @@ __global__ __launch_bounds__(kResBlock, 2) void residual_kernel(
     const bool floored = (cell_mode & kCellFloored) != 0;
     const i64 row4 = 4 * static_cast<i64>(d);  // floats per (b, t) row of a state tensor
     const float* Sb = S + static_cast<i64>(b) * T * row4;
-    CellIn pv;
-    if (t0 == 0) {
-      if (state0 != nullptr) {
-        const float* s0 = state0 + static_cast<i64>(b) * row4;
-        pv = {s0[j], s0[ud + j], s0[2 * ud + j], s0[3 * ud + j]};
-      } else {
-        pv = {0.0f, 0.0f, 0.0f, 0.0f};
-      }
-    } else {
+    CellIn pv = {0.0f, 0.0f, 0.0f, 0.0f};  // a sequence start replaces it below
+    if (t0 > 0) {
       const float* sp = Sb + static_cast<i64>(t0 - 1) * row4;
       pv = {sp[j], sp[ud + j], sp[2 * ud + j], sp[3 * ud + j]};
     }
+    SeqCursor seq = seq_cursor(cu, n_seqs, b, t0);
     // next step's operands are loaded one step ahead
     float pn[4], sn[4];
     auto load_step = [&](int t, float (&pg)[4], float (&st)[4]) {
@@ -96,6 +91,10 @@ __global__ __launch_bounds__(kResBlock, 2) void residual_kernel(
         st[k] = sn[k];
       }
       if (t + 1 < t1) load_step(t + 1, pn, sn);
+      const int sq = seq_begin(seq, t);
+      if (sq >= 0) pv = state0_of(state0, sq, ud, j);
+      // packed: the step after a sequence boundary does not depend on the state before it
+      const bool cut = cu != nullptr && sq >= 0;
       float f[4], Aj[16];
       cell_step<JMODE != kJacNone>(pv, pg[0], pg[1], pg[2], pg[3], rz, ri, rf, ro, sig, floored, f, Aj);
       const i64 row = static_cast<i64>(b) * T + t;
@@ -108,11 +107,11 @@ __global__ __launch_bounds__(kResBlock, 2) void residual_kernel(
       if constexpr (JMODE == kJacDense) {
         float* Ap = A + row * 16 * static_cast<i64>(d);
 #pragma unroll
-        for (int e = 0; e < 16; ++e) Ap[e * ud + j] = Aj[e];
+        for (int e = 0; e < 16; ++e) Ap[e * ud + j] = cut ? 0.0f : Aj[e];
       } else if constexpr (JMODE == kJacSparse) {
         float* Ap = A + row * 16 * static_cast<i64>(d);
 #pragma unroll
-        for (int q = 0; q < 12; ++q) Ap[kSparsePlanes[q] * ud + j] = Aj[kSparsePlanes[q]];
+        for (int q = 0; q < 12; ++q) Ap[kSparsePlanes[q] * ud + j] = cut ? 0.0f : Aj[kSparsePlanes[q]];
       }
       if (h_out != nullptr) h_out[row * static_cast<i64>(d) + j] = st[3];
       pv = {st[0], st[1], st[2], st[3]};
@@ -135,23 +134,26 @@ template <bool BF16>
 static void launch_mode(int mode, dim3 grid, hipStream_t stream, const void* P, const float* R,
                         const float* state0, const float* S, float* A, float* rhs, int T, int d,
                         int n_chunks, int sig, Control* ctl, unsigned int* err_base, int err_stride,
-                        int chk, float tol, float* h_out) {
+                        int chk, float tol, float* h_out, Seqs seqs) {
   if (mode == kJacDense)
     residual_kernel<BF16, kJacDense><<<grid, kResBlock, 0, stream>>>(P, R, state0, S, A, rhs, T, d,
-                                                                      n_chunks, sig, ctl, err_base, err_stride, chk, tol, h_out);
+                                                                      n_chunks, sig, ctl, err_base, err_stride, chk, tol, h_out,
+                                                                      seqs.cu, seqs.n);
   else if (mode == kJacSparse)
     residual_kernel<BF16, kJacSparse><<<grid, kResBlock, 0, stream>>>(P, R, state0, S, A, rhs, T, d,
-                                                                       n_chunks, sig, ctl, err_base, err_stride, chk, tol, h_out);
+                                                                       n_chunks, sig, ctl, err_base, err_stride, chk, tol, h_out,
+                                                                       seqs.cu, seqs.n);
   else
     residual_kernel<BF16, kJacNone><<<grid, kResBlock, 0, stream>>>(P, R, state0, S, nullptr, nullptr,
-                                                                     T, d, n_chunks, sig, ctl, err_base, err_stride, chk, tol, h_out);
+                                                                     T, d, n_chunks, sig, ctl, err_base, err_stride, chk, tol, h_out,
+                                                                     seqs.cu, seqs.n);
 }
 
 hipError_t launch_residual(const void* P, bool p_bf16, const float* R, const float* state0,
                            const float* S, float* A, float* rhs, int B, int T, int d,
                            int cell_mode, Control* ctl, unsigned int* err_base, int err_stride,
                            ResidualMode mode, int stop_check_iter, float tol, hipStream_t stream,
-                           float* h_out) {
+                           float* h_out, Seqs seqs) {
   const int n_chunks = (T + kResChunk - 1) / kResChunk;
   const unsigned gx = static_cast<unsigned>((d + kWave - 1) / kWave);
   const unsigned gy = static_cast<unsigned>((n_chunks + kResWaves - 1) / kResWaves);
@@ -161,10 +163,10 @@ hipError_t launch_residual(const void* P, bool p_bf16, const float* R, const flo
   const int m = mode == ResidualMode::kDense ? kJacDense : (mode == ResidualMode::kSparse ? kJacSparse : kJacNone);
   if (p_bf16)
     launch_mode<true>(m, grid, stream, P, R, state0, S, A, rhs, T, d, n_chunks, sig, ctl, err_base, err_stride,
-                      stop_check_iter, tol, h_out);
+                      stop_check_iter, tol, h_out, seqs);
   else
     launch_mode<false>(m, grid, stream, P, R, state0, S, A, rhs, T, d, n_chunks, sig, ctl, err_base, err_stride,
-                       stop_check_iter, tol, h_out);
+                       stop_check_iter, tol, h_out, seqs);
   return hipGetLastError();
 }
 

@@ -96,6 +96,29 @@ __global__ __launch_bounds__(kUpdBlock) void final_state_kernel(const float* __r
   }
 }
 
+// packed sequences: out[s] = the last state of sequence s (steps cu[s] .. cu[s+1]-1 of the one
+// batch row), or state0[s] (zeros without one) for an empty sequence; cu is read only within
+// its n_seqs + 1 entries and the step is clamped into [0, T)
+__global__ __launch_bounds__(kUpdBlock) void packed_final_state_kernel(const float* __restrict__ S,
+                                                                       const float* __restrict__ state0,
+                                                                       const int* __restrict__ cu,
+                                                                       float* __restrict__ out,
+                                                                       int n_seqs, int T, int d) {
+  const i64 n = static_cast<i64>(n_seqs) * 4 * d;  // (s, slot, j)
+  for (i64 i = static_cast<i64>(blockIdx.x) * kUpdBlock + threadIdx.x; i < n;
+       i += static_cast<i64>(gridDim.x) * kUpdBlock) {
+    const int s = static_cast<int>(i / (4 * static_cast<i64>(d)));
+    const i64 rest = i - static_cast<i64>(s) * 4 * d;
+    const int a = cu[s], e = cu[s + 1];
+    if (e > a) {
+      const int t = e - 1 < 0 ? 0 : (e - 1 >= T ? T - 1 : e - 1);
+      out[i] = S[static_cast<i64>(t) * 4 * d + rest];
+    } else {
+      out[i] = state0 != nullptr ? state0[i] : 0.0f;
+    }
+  }
+}
+
 __global__ __launch_bounds__(kUpdBlock) void zero_kernel(float4* __restrict__ p, i64 n4) {
   const i64 stride = static_cast<i64>(gridDim.x) * kUpdBlock;
   for (i64 i = static_cast<i64>(blockIdx.x) * kUpdBlock + threadIdx.x; i < n4; i += stride)
@@ -142,14 +165,18 @@ hipError_t launch_settle(Control* ctl, int k, float tol, hipStream_t stream) {
 }
 
 hipError_t launch_outputs(const float* S, float* h, float* final_state, int B, int T, int d,
-                          const Control* ctl, hipStream_t stream) {
+                          const Control* ctl, hipStream_t stream, const float* state0, Seqs seqs) {
   if (h != nullptr) {
     const i64 rows = static_cast<i64>(B) * T;
     hidden_kernel<<<stream_grid(rows * d), kUpdBlock, 0, stream>>>(S, h, rows, d, ctl);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (final_state != nullptr) {
+  if (final_state != nullptr && seqs.cu != nullptr) {
+    if (seqs.n > 0)
+      packed_final_state_kernel<<<stream_grid(static_cast<i64>(seqs.n) * 4 * d), kUpdBlock, 0, stream>>>(
+          S, state0, seqs.cu, final_state, seqs.n, T, d);
+  } else if (final_state != nullptr) {
     final_state_kernel<<<stream_grid(static_cast<i64>(B) * 4 * d), kUpdBlock, 0, stream>>>(
         S, final_state, B, T, d);
   }

@@ -26,6 +26,12 @@
 // tile aggregates and carries staged in LDS, and a decoupled look-back across tiles along T
 // with the same fixed, anchored dataflow. The re-run from each carry writes the states
 // (c, n, m, h) with h = sigma(p_o) c / n (or the floored read-out, see cell.h).
+//
+// Packed sequences (PACKED): a run that contains a sequence start forgets whatever enters it;
+// it is held in absolute form, E = +inf marking it and (L, cz, nz) holding the (m, c, n) it
+// ends with (the start step applied to the sequence's state0, then the steps after it). A run
+// composed after an absolute one is applied to its state; an absolute run composed after any
+// run replaces it (the head flag of the segmented scan).
 #include "cell.h"
 #include "kernels.h"
 
@@ -45,8 +51,21 @@ __device__ __forceinline__ float exp_or_zero(float e, float x) {
   return (e == -INFINITY) ? 0.0f : exp_fast(x);
 }
 
+__device__ __forceinline__ bool absolute(const LogAgg& X) { return X.E == INFINITY; }
+
+__device__ __forceinline__ void apply_relative(const LogAgg& X, float& m, float& c, float& n);
+
 // X first, then Y
+template <bool PACKED = false>
 __device__ __forceinline__ LogAgg compose(const LogAgg& X, const LogAgg& Y) {
+  if constexpr (PACKED) {
+    if (absolute(Y)) return Y;
+    if (absolute(X)) {
+      float m = X.L, c = X.cz, n = X.nz;
+      apply_relative(Y, m, c, n);
+      return {m, INFINITY, c, n};
+    }
+  }
   LogAgg o;
   o.L = X.L + Y.L;
   const float ey = Y.E - X.L;
@@ -59,13 +78,24 @@ __device__ __forceinline__ LogAgg compose(const LogAgg& X, const LogAgg& Y) {
 }
 
 // apply a run to a carried (m, c, n)
-__device__ __forceinline__ void apply(const LogAgg& X, float& m, float& c, float& n) {
+__device__ __forceinline__ void apply_relative(const LogAgg& X, float& m, float& c, float& n) {
   const float x = fmaxf(m, X.E);
   const float wc = exp_fast(m - x);
   const float wz = exp_or_zero(X.E, X.E - x);
   c = fmaf(wc, c, wz * X.cz);
   n = fmaf(wc, n, wz * X.nz);
   m = X.L + x;
+}
+
+template <bool PACKED = false>
+__device__ __forceinline__ void apply(const LogAgg& X, float& m, float& c, float& n) {
+  if (PACKED && absolute(X)) {
+    m = X.L;
+    c = X.cz;
+    n = X.nz;
+    return;
+  }
+  apply_relative(X, m, c, n);
 }
 
 __device__ __forceinline__ LogAgg quad_perm_agg_m1(const LogAgg& X) {
@@ -77,11 +107,12 @@ __device__ __forceinline__ LogAgg quad_perm_agg_m2(const LogAgg& X) {
           quad_perm<0, 1, 0, 1>(X.nz)};
 }
 
-template <bool BF16>
+template <bool BF16, bool PACKED>
 __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
     const void* __restrict__ P, const float* __restrict__ state0, float* __restrict__ S, int T,
     int d, int cell_mode, int n_jt, int n_lg, int n_tt, int anchor_stride,
-    unsigned long long* __restrict__ desc, unsigned int* __restrict__ tickets, int n_ctr, uint32_t epoch) {
+    unsigned long long* __restrict__ desc, unsigned int* __restrict__ tickets, int n_ctr, uint32_t epoch,
+    const int* __restrict__ cu, int n_seqs) {
   __shared__ int s_tile[2];
   __shared__ LogAgg s_agg[64];
   __shared__ float s_carry[64][3];
@@ -133,20 +164,36 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
       lf[u] = 0.0f;
     }
   }
+  // the sequence starting at each step of the sub-chunk, or -1 (packed only)
+  int sq[kWarmTSub];
+  if constexpr (PACKED) {
+    SeqCursor seq = seq_cursor(cu, n_seqs, b, t_start);
+#pragma unroll
+    for (int u = 0; u < kWarmTSub; ++u) sq[u] = (t_start + u < T) ? seq_begin(seq, t_start + u) : -1;
+  }
   LogAgg agg = {0.0f, -INFINITY, 0.0f, 0.0f};
 #pragma unroll
   for (int u = 0; u < kWarmTSub; ++u) {
     // one step as a run: L = l, E = i~ - l, cz = z, nz = 1
-    const LogAgg stp = {lf[u], it[u] - lf[u], zz[u], 1.0f};
-    agg = compose(agg, stp);
+    LogAgg stp = {lf[u], it[u] - lf[u], zz[u], 1.0f};
+    if constexpr (PACKED) {
+      if (valid && sq[u] >= 0) {
+        // a sequence start: the step from the sequence's state0, in absolute form
+        const CellIn s0 = state0_of(state0, sq[u], ud, j);
+        float m = s0.m, c = s0.c, n = s0.n;
+        apply_relative(stp, m, c, n);
+        stp = {m, INFINITY, c, n};
+      }
+    }
+    agg = compose<PACKED>(agg, stp);
   }
 
   // ---- level 2: quad scan (DPP) ----
   {
     const LogAgg p1 = quad_perm_agg_m1(agg);
-    if (sc >= 1) agg = compose(p1, agg);
+    if (sc >= 1) agg = compose<PACKED>(p1, agg);
     const LogAgg p2 = quad_perm_agg_m2(agg);
-    if (sc >= 2) agg = compose(p2, agg);
+    if (sc >= 2) agg = compose<PACKED>(p2, agg);
   }
   if (sc == 3) s_agg[lane_in_tile] = agg;
   __syncthreads();
@@ -186,13 +233,13 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
         while (!(tag_load(word(p, 4), epoch, pa.L) & tag_load(word(p, 5), epoch, pa.E) &
                  tag_load(word(p, 6), epoch, pa.cz) & tag_load(word(p, 7), epoch, pa.nz)))
           __builtin_amdgcn_s_sleep(2);
-        acc = compose(pa, acc);
+        acc = compose<PACKED>(pa, acc);
       }
       float xm, xc, xn;
       while (!(tag_load(word(a, 0), epoch, xm) & tag_load(word(a, 1), epoch, xc) &
                tag_load(word(a, 2), epoch, xn)))
         __builtin_amdgcn_s_sleep(2);
-      apply(acc, xm, xc, xn);
+      apply<PACKED>(acc, xm, xc, xn);
       cm = xm;
       cc = xc;
       cn = xn;
@@ -202,7 +249,7 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
     s_carry[l][2] = cn;
     if (anchor) {
       float em = cm, ec = cc, en = cn;
-      apply(tile, em, ec, en);
+      apply<PACKED>(tile, em, ec, en);
       tag_store(word(tt, 0), em, epoch);
       tag_store(word(tt, 1), ec, epoch);
       tag_store(word(tt, 2), en, epoch);
@@ -215,7 +262,7 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
   const float cc = s_carry[lane_in_tile][1];
   const float cn = s_carry[lane_in_tile][2];
   float em = cm, ec = cc, en = cn;
-  apply(agg, em, ec, en);  // inclusive: end of this sub-chunk
+  apply<PACKED>(agg, em, ec, en);  // inclusive: end of this sub-chunk
   float m = quad_perm<0, 0, 1, 2>(em);
   float c = quad_perm<0, 0, 1, 2>(ec);
   float n = quad_perm<0, 0, 1, 2>(en);
@@ -228,6 +275,14 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
   for (int u = 0; u < kWarmTSub; ++u) {
     const int t = t_start + u;
     if (valid && t < T) {
+      if constexpr (PACKED) {
+        if (sq[u] >= 0) {
+          const CellIn s0 = state0_of(state0, sq[u], ud, j);
+          m = s0.m;
+          c = s0.c;
+          n = s0.n;
+        }
+      }
       const float a = lf[u] + m;
       const float mn = (a >= it[u]) ? a : it[u];
       const float ig = exp_fast(it[u] - mn);
@@ -258,7 +313,7 @@ size_t warm_desc_words(int B, int T, int d) {
 
 hipError_t launch_warm_start(const void* P, bool p_bf16, const float* state0, float* S, int B,
                              int T, int d, int cell_mode, unsigned long long* desc,
-                             unsigned int* tickets, uint32_t epoch, hipStream_t stream) {
+                             unsigned int* tickets, uint32_t epoch, hipStream_t stream, Seqs seqs) {
   i64 n_jt, n_lg, n_tt;
   warm_grid(B, T, d, n_jt, n_lg, n_tt);
   const i64 blocks = n_lg * n_tt;
@@ -267,14 +322,19 @@ hipError_t launch_warm_start(const void* P, bool p_bf16, const float* state0, fl
   const int sig = cell_mode;
   const int stride = look_back_anchor_stride(n_lg, 2);
   const int n_ctr = ticket_counters(n_lg);
-  if (p_bf16)
-    warm_start_kernel<true><<<grid, kWarmBlock, 0, stream>>>(P, state0, S, T, d, sig, static_cast<int>(n_jt),
-                                                             static_cast<int>(n_lg), static_cast<int>(n_tt),
-                                                             stride, desc, tickets, n_ctr, epoch);
-  else
-    warm_start_kernel<false><<<grid, kWarmBlock, 0, stream>>>(P, state0, S, T, d, sig, static_cast<int>(n_jt),
-                                                              static_cast<int>(n_lg), static_cast<int>(n_tt),
-                                                              stride, desc, tickets, n_ctr, epoch);
+#define SLSTM_WARM_SCAN_LAUNCH(BF, PK)                                                                    \
+  warm_start_kernel<BF, PK><<<grid, kWarmBlock, 0, stream>>>(P, state0, S, T, d, sig, static_cast<int>(n_jt), \
+                                                             static_cast<int>(n_lg), static_cast<int>(n_tt), \
+                                                             stride, desc, tickets, n_ctr, epoch, seqs.cu, seqs.n)
+  const bool packed = seqs.cu != nullptr;
+  if (p_bf16) {
+    if (packed) SLSTM_WARM_SCAN_LAUNCH(true, true);
+    else SLSTM_WARM_SCAN_LAUNCH(true, false);
+  } else {
+    if (packed) SLSTM_WARM_SCAN_LAUNCH(false, true);
+    else SLSTM_WARM_SCAN_LAUNCH(false, false);
+  }
+#undef SLSTM_WARM_SCAN_LAUNCH
   return hipGetLastError();
 }
 

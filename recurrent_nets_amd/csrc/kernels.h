@@ -22,14 +22,14 @@ hipError_t launch_residual(const void* P, bool p_bf16, const float* R, const flo
                            const float* S, float* A, float* rhs, int B, int T, int d,
                            int cell_mode, Control* ctl, unsigned int* err_base, int err_stride,
                            ResidualMode mode, int stop_check_iter, float tol, hipStream_t stream,
-                           float* h_out = nullptr);
+                           float* h_out = nullptr, Seqs seqs = {});
 
 size_t fused_desc_words(int B, int T, int d);
 hipError_t launch_newton_iteration(const void* P, bool p_bf16, const float* R, const float* state0,
                                    const float* S_in, float* S_out, int B, int T, int d,
                                    int cell_mode, unsigned long long* desc, unsigned int* tickets,
                                    uint32_t epoch, Control* ctl, int k_iter, float tol,
-                                   hipStream_t stream);
+                                   hipStream_t stream, Seqs seqs = {});
 // chain form of the fused iteration (256 features x 8 steps per tile); `last` also writes the
 // residual of the new iterate (slot k_iter + 1) and, if h_out is not NULL, its hidden slot
 long long chain_lane_groups(int B, int d);
@@ -63,7 +63,8 @@ hipError_t launch_scan_block4(const float* A, const float* rhs, float* x, int B,
 size_t warm_desc_words(int B, int T, int d);
 hipError_t launch_warm_start(const void* P, bool p_bf16, const float* state0, float* S, int B,
                              int T, int d, int cell_mode, unsigned long long* desc,
-                             unsigned int* tickets, uint32_t epoch, hipStream_t stream);
+                             unsigned int* tickets, uint32_t epoch, hipStream_t stream,
+                             Seqs seqs = {});
 
 size_t warm_chain_desc_words(int B, int T, int d);
 hipError_t launch_warm_chain(const void* P, bool p_bf16, const float* state0, float* S, int B,
@@ -79,21 +80,23 @@ hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const flo
                            void* dP, bool dp_bf16, float* dR, float* dbias, float* dstate0,
                            float* rows, int B, int T, int d, int cell_mode, bool scan,
                            unsigned long long* desc, unsigned int* tickets, uint32_t epoch,
-                           hipStream_t stream);
+                           hipStream_t stream, Seqs seqs = {});
 
 hipError_t launch_update(float* S, const float* D, i64 n_floats, Control* ctl, int k_iter,
                          hipStream_t stream);
 hipError_t launch_init_control(Control* ctl, hipStream_t stream);
 hipError_t launch_finalize(Control* ctl, float tol, hipStream_t stream);
 // hidden slot (unless the final residual pass already wrote it: then only after an early stop,
-// signalled by ctl) and final state
+// signalled by ctl) and final state; with packed sequences the final state of each sequence
+// (its state0 for an empty one)
 hipError_t launch_outputs(const float* S, float* h, float* final_state, int B, int T, int d,
-                          const Control* ctl, hipStream_t stream);
+                          const Control* ctl, hipStream_t stream, const float* state0 = nullptr,
+                          Seqs seqs = {});
 hipError_t launch_zero(float* p, i64 n_floats, hipStream_t stream);
 
 hipError_t launch_sequential(const void* P, bool p_bf16, const float* R, const float* state0,
                              float* S, float* h_out, float* final_state, int B, int T, int d,
-                             int cell_mode, hipStream_t stream);
+                             int cell_mode, hipStream_t stream, Seqs seqs = {});
 
 // C = X W^T (+ bias) in bf16 MFMA with float32 accumulation; X (M x K), W (N x K), both
 // K-contiguous. With splits > 1 the K range is split and split s writes its partial product to

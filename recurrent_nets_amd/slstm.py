@@ -35,6 +35,8 @@ EXPORTED = [
     "slstm_profile_enable", "slstm_profile_reset", "slstm_profile_read",
     "slstm_profile_durations", "slstm_backward_workspace_bytes", "slstm_backward",
     "slstm_input_projection_backward_workspace_bytes", "slstm_input_projection_backward",
+    "slstm_newton_forward_varlen", "slstm_sequential_forward_varlen", "slstm_warm_start_varlen",
+    "slstm_backward_varlen",
 ]
 
 
@@ -119,6 +121,17 @@ def load(path: str | None = None):
     L.slstm_input_projection_backward.restype = _i
     L.slstm_input_projection_backward.argtypes = [_vp, _vp, _vp, _i, _vp, _vp, _i, _i, _i, _i, _vp,
                                                   _sz, _vp]
+    L.slstm_newton_forward_varlen.restype = _i
+    L.slstm_newton_forward_varlen.argtypes = [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i,
+                                              _i, _f, _i, _i, _vp, _sz, _vp, ctypes.POINTER(_Stats)]
+    L.slstm_sequential_forward_varlen.restype = _i
+    L.slstm_sequential_forward_varlen.argtypes = [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i,
+                                                  _i, _vp]
+    L.slstm_warm_start_varlen.restype = _i
+    L.slstm_warm_start_varlen.argtypes = [_vp, _i, _vp, _vp, _i, _vp, _i, _i, _i, _i, _vp, _sz, _vp]
+    L.slstm_backward_varlen.restype = _i
+    L.slstm_backward_varlen.argtypes = [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp,
+                                        _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]
     L.slstm_profile_enable.restype = _i
     L.slstm_profile_enable.argtypes = [_i]
     L.slstm_profile_reset.restype = _i
@@ -168,15 +181,43 @@ def _p_dtype(P):
     return BF16 if P.dtype == torch.bfloat16 else F32
 
 
-def _shape_check(P, R, state0):
+def _shape_check(P, R, state0, n_states=None):
+    """(B, T, d_h) of P; state0 is (n_states, 4, d_h), n_states = B unless given."""
     if P.dim() != 4 or P.shape[2] != 4:
         raise ValueError(f"P must be (B, T, 4, d_h), got {tuple(P.shape)}")
     B, T, _, d = P.shape
-    if tuple(R.shape) != (4, d):
+    if R is not None and tuple(R.shape) != (4, d):
         raise ValueError(f"R must be (4, {d}), got {tuple(R.shape)}")
-    if state0 is not None and tuple(state0.shape) != (B, 4, d):
-        raise ValueError(f"state0 must be ({B}, 4, {d}), got {tuple(state0.shape)}")
+    n = B if n_states is None else n_states
+    if state0 is not None and tuple(state0.shape) != (n, 4, d):
+        raise ValueError(f"state0 must be ({n}, 4, {d}), got {tuple(state0.shape)}")
     return B, T, d
+
+
+def _shape(t, name, shape):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must be {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _seqs(cu_seqlens, P):
+    """Packed sequences: (device int32 offsets, S) or (None, None). A list, tuple or host tensor
+    is checked (cu[0] = 0, non-decreasing, cu[S] = T) and copied to P's device; a device tensor
+    must be int32 and is passed as it is. P must then have B = 1."""
+    if cu_seqlens is None:
+        return None, None
+    if P.shape[0] != 1:
+        raise ValueError(f"packed sequences take P of shape (1, T, 4, d_h), got {tuple(P.shape)}")
+    T = P.shape[1]
+    if not (isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda):
+        cu = [int(v) for v in (cu_seqlens.tolist() if isinstance(cu_seqlens, torch.Tensor) else cu_seqlens)]
+        if len(cu) < 2 or cu[0] != 0 or cu[-1] != T or any(b < a for a, b in zip(cu, cu[1:])):
+            raise ValueError(f"cu_seqlens must run from 0 to T = {T} without decreasing, got {cu}")
+        cu_seqlens = torch.tensor(cu, dtype=torch.int32, device=P.device)
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise TypeError("cu_seqlens must be a 1-D int32 tensor of S + 1 offsets")
+    if not cu_seqlens.is_contiguous():
+        raise ValueError("cu_seqlens must be contiguous")
+    return cu_seqlens, cu_seqlens.numel() - 1
 
 
 def newton_workspace_bytes(B: int, T: int, d_h: int, schedule: str = "fused") -> int:
@@ -191,19 +232,24 @@ def alloc_workspace(nbytes: int, device=None) -> torch.Tensor:
 def newton_forward(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, init="warm",
                    states=None, h_out=None, want_hidden=True, final_state=None, workspace=None,
                    stream=None, stats=True, raise_on_divergence=True, schedule="fused",
-                   readout="exact"):
+                   readout="exact", cu_seqlens=None):
     """Newton-parallel forward. Returns (states (B,T,4,d_h), h (B,T,d_h) or None, NewtonStats
     or None). With stats=False the call is asynchronous and returns no stats. A given
     ``final_state`` (B,4,d_h) tensor receives the last step's state. ``schedule`` is "fused"
     (one kernel per iteration; "fused_chain" when the lane groups cover the GPU, else
     "fused_scan"), "fused_scan", "fused_chain" or "layered" (residual + Jacobian, scan,
     update). ``readout`` is "exact" (h = o c / n) or "floored" (h = o c / max(|n|, e^{-m},
-    1e-6)); every function taking ``forget`` takes it too."""
+    1e-6)); every function taking ``forget`` takes it too.
+
+    ``cu_seqlens`` (S + 1 offsets) packs S sequences end to end along time in P (1, T, 4, d_h):
+    state0 and final_state are then (S, 4, d_h), and "fused" means "fused_scan" ("fused_chain"
+    is rejected); sequential_forward, warm_start and backward take it the same way."""
     L = load()
     _dev(P, "P", (torch.float32, torch.bfloat16))
     _dev(R, "R", (torch.float32,))
     _dev(state0, "state0", (torch.float32,))
-    B, T, d = _shape_check(P, R, state0)
+    cu, S = _seqs(cu_seqlens, P)
+    B, T, d = _shape_check(P, R, state0, S)
     if states is None:
         states = torch.empty((B, T, 4, d), dtype=torch.float32, device=P.device)
     if want_hidden and h_out is None:
@@ -211,16 +257,25 @@ def newton_forward(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, init="
     _dev(states, "states", (torch.float32,))
     _dev(h_out, "h_out", (torch.float32,))
     _dev(final_state, "final_state", (torch.float32,))
-    need = L.slstm_newton_workspace_bytes(B, T, d, SCHEDULE[schedule])
+    _shape(final_state, "final_state", (B if cu is None else S, 4, d))
+    sched = SCHEDULE["fused_scan" if cu is not None and schedule == "fused" else schedule]
+    need = L.slstm_newton_workspace_bytes(B, T, d, sched)
     if workspace is None:
         workspace = alloc_workspace(need, P.device)
     st = _Stats() if stats else None
-    status = L.slstm_newton_forward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
-                                    _ptr(h_out), _ptr(final_state), B, T, d, _fmode(forget, readout),
-                                    int(max_iters),
-                                    float(tol), INIT[init], SCHEDULE[schedule], _ptr(workspace),
-                                    workspace.numel() * workspace.element_size(), _stream(stream),
-                                    ctypes.byref(st) if st is not None else None)
+    nbytes = workspace.numel() * workspace.element_size()
+    st_ref = ctypes.byref(st) if st is not None else None
+    if cu is None:
+        status = L.slstm_newton_forward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
+                                        _ptr(h_out), _ptr(final_state), B, T, d, _fmode(forget, readout),
+                                        int(max_iters), float(tol), INIT[init], SCHEDULE[schedule],
+                                        _ptr(workspace), nbytes, _stream(stream), st_ref)
+    else:
+        status = L.slstm_newton_forward_varlen(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(cu), S,
+                                               _ptr(states), _ptr(h_out), _ptr(final_state), T, d,
+                                               _fmode(forget, readout), int(max_iters), float(tol),
+                                               INIT[init], SCHEDULE[schedule], _ptr(workspace), nbytes,
+                                               _stream(stream), st_ref)
     _check(status, "slstm_newton_forward")
     out_stats = NewtonStats._from(st, status) if st is not None else None
     if raise_on_divergence and status in (DIVERGED, NONFINITE):
@@ -239,14 +294,16 @@ def read_stats(workspace, stream=None) -> NewtonStats:
 
 
 def sequential_forward(P, R, state0=None, forget="exp", states=None, h_out=None,
-                       want_hidden=True, final_state=None, stream=None, readout="exact"):
+                       want_hidden=True, final_state=None, stream=None, readout="exact",
+                       cu_seqlens=None):
     """Step-by-step forward (also the T=1 decode step). Returns (states, h or None). A given
     ``final_state`` (B,4,d_h) tensor receives the last step's state."""
     L = load()
     _dev(P, "P", (torch.float32, torch.bfloat16))
     _dev(R, "R", (torch.float32,))
     _dev(state0, "state0", (torch.float32,))
-    B, T, d = _shape_check(P, R, state0)
+    cu, S = _seqs(cu_seqlens, P)
+    B, T, d = _shape_check(P, R, state0, S)
     if states is None:
         states = torch.empty((B, T, 4, d), dtype=torch.float32, device=P.device)
     if want_hidden and h_out is None:
@@ -254,9 +311,15 @@ def sequential_forward(P, R, state0=None, forget="exp", states=None, h_out=None,
     _dev(states, "states", (torch.float32,))
     _dev(h_out, "h_out", (torch.float32,))
     _dev(final_state, "final_state", (torch.float32,))
-    status = L.slstm_sequential_forward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
-                                        _ptr(h_out), _ptr(final_state), B, T, d, _fmode(forget, readout),
-                                        _stream(stream))
+    _shape(final_state, "final_state", (B if cu is None else S, 4, d))
+    if cu is None:
+        status = L.slstm_sequential_forward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
+                                            _ptr(h_out), _ptr(final_state), B, T, d,
+                                            _fmode(forget, readout), _stream(stream))
+    else:
+        status = L.slstm_sequential_forward_varlen(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(cu),
+                                                   S, _ptr(states), _ptr(h_out), _ptr(final_state), T, d,
+                                                   _fmode(forget, readout), _stream(stream))
     _check(status, "slstm_sequential_forward")
     return states, h_out
 
@@ -323,22 +386,30 @@ def scan_block4(A, rhs, out=None, workspace=None, stream=None):
 
 
 def warm_start(P, state0=None, forget="exp", out=None, workspace=None, stream=None,
-               schedule="fused", readout="exact"):
+               schedule="fused", readout="exact", cu_seqlens=None):
     """The R-free trajectory used as the initial Newton iterate. Returns states (B,T,4,d).
     ``schedule`` picks the kernel form as in newton_forward ("fused_chain": tile-serial
     recurrences; "fused_scan" / "layered": log-space scan with look-back)."""
     L = load()
     _dev(P, "P", (torch.float32, torch.bfloat16))
     _dev(state0, "state0", (torch.float32,))
-    B, T, _, d = P.shape
+    cu, S = _seqs(cu_seqlens, P)
+    B, T, d = _shape_check(P, None, state0, S)
     if out is None:
         out = torch.empty((B, T, 4, d), dtype=torch.float32, device=P.device)
-    need = L.slstm_warm_start_workspace_bytes(B, T, d, SCHEDULE[schedule])
+    _dev(out, "out", (torch.float32,))
+    sched = SCHEDULE["fused_scan" if cu is not None and schedule == "fused" else schedule]
+    need = L.slstm_warm_start_workspace_bytes(B, T, d, sched)
     if workspace is None:
         workspace = alloc_workspace(need, P.device)
-    status = L.slstm_warm_start(_ptr(P), _p_dtype(P), _ptr(state0), _ptr(out), B, T, d,
-                                _fmode(forget, readout), SCHEDULE[schedule], _ptr(workspace),
-                                workspace.numel(), _stream(stream))
+    if cu is None:
+        status = L.slstm_warm_start(_ptr(P), _p_dtype(P), _ptr(state0), _ptr(out), B, T, d,
+                                    _fmode(forget, readout), SCHEDULE[schedule], _ptr(workspace),
+                                    workspace.numel(), _stream(stream))
+    else:
+        status = L.slstm_warm_start_varlen(_ptr(P), _p_dtype(P), _ptr(state0), _ptr(cu), S, _ptr(out), T, d,
+                                           _fmode(forget, readout), SCHEDULE[schedule], _ptr(workspace),
+                                           workspace.numel(), _stream(stream))
     _check(status, "slstm_warm_start")
     return out
 
@@ -350,19 +421,21 @@ def backward_workspace_bytes(B: int, T: int, d_h: int, schedule: str = "fused") 
 def backward(P, R, states, state0=None, g_states=None, g_h=None, g_final=None, forget="exp",
              dP=None, dR=None, dstate0=None, want_dstate0=True, workspace=None, stream=None,
              schedule="fused", dP_dtype=torch.float32, dbias=None, want_dbias=False,
-             readout="exact"):
+             readout="exact", cu_seqlens=None):
     """Gradients through the recurrence at the forward solution ``states`` (B,T,4,d_h).
     g_states (B,T,4,d_h), g_h (B,T,d_h) and g_final (B,4,d_h) are the loss's direct gradients
     (None: zeros). dP is float32 or bfloat16 (``dP_dtype``). Returns (dP (B,T,4,d_h),
     dR (4,d_h), dstate0 (B,4,d_h) or None), and dbias (4,d_h) last when ``want_dbias`` or a
-    ``dbias`` tensor is given."""
+    ``dbias`` tensor is given. With ``cu_seqlens``, g_final and dstate0 are (S,4,d_h)."""
     L = load()
     _dev(P, "P", (torch.float32, torch.bfloat16))
     _dev(R, "R", (torch.float32,))
     _dev(state0, "state0", (torch.float32,))
-    B, T, d = _shape_check(P, R, state0)
+    cu, S = _seqs(cu_seqlens, P)
+    B, T, d = _shape_check(P, R, state0, S)
+    n0 = B if cu is None else S
     for name, t, shape in (("states", states, (B, T, 4, d)), ("g_states", g_states, (B, T, 4, d)),
-                           ("g_h", g_h, (B, T, d)), ("g_final", g_final, (B, 4, d))):
+                           ("g_h", g_h, (B, T, d)), ("g_final", g_final, (n0, 4, d))):
         _dev(t, name, (torch.float32,))
         if t is not None and tuple(t.shape) != shape:
             raise ValueError(f"{name} must be {shape}, got {tuple(t.shape)}")
@@ -373,7 +446,7 @@ def backward(P, R, states, state0=None, g_states=None, g_h=None, g_final=None, f
     if dR is None:
         dR = torch.empty((4, d), dtype=torch.float32, device=P.device)
     if want_dstate0 and dstate0 is None:
-        dstate0 = torch.empty((B, 4, d), dtype=torch.float32, device=P.device)
+        dstate0 = torch.empty((n0, 4, d), dtype=torch.float32, device=P.device)
     _dev(dP, "dP", (torch.float32, torch.bfloat16))
     _dev(dR, "dR", (torch.float32,))
     _dev(dbias, "dbias", (torch.float32,))
@@ -381,11 +454,18 @@ def backward(P, R, states, state0=None, g_states=None, g_h=None, g_final=None, f
     need = L.slstm_backward_workspace_bytes(B, T, d, SCHEDULE[schedule])
     if workspace is None:
         workspace = alloc_workspace(need, P.device)
-    status = L.slstm_backward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
-                              _ptr(g_states), _ptr(g_h), _ptr(g_final), _ptr(dP),
-                              BF16 if dP.dtype == torch.bfloat16 else F32, _ptr(dR), _ptr(dbias),
-                              _ptr(dstate0), B, T, d, _fmode(forget, readout), SCHEDULE[schedule],
-                              _ptr(workspace), workspace.numel(), _stream(stream))
+    dpt = BF16 if dP.dtype == torch.bfloat16 else F32
+    if cu is None:
+        status = L.slstm_backward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
+                                  _ptr(g_states), _ptr(g_h), _ptr(g_final), _ptr(dP), dpt, _ptr(dR),
+                                  _ptr(dbias), _ptr(dstate0), B, T, d, _fmode(forget, readout),
+                                  SCHEDULE[schedule], _ptr(workspace), workspace.numel(), _stream(stream))
+    else:
+        status = L.slstm_backward_varlen(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(cu), S,
+                                         _ptr(states), _ptr(g_states), _ptr(g_h), _ptr(g_final), _ptr(dP),
+                                         dpt, _ptr(dR), _ptr(dbias), _ptr(dstate0), T, d,
+                                         _fmode(forget, readout), SCHEDULE[schedule], _ptr(workspace),
+                                         workspace.numel(), _stream(stream))
     _check(status, "slstm_backward")
     if dbias is not None:
         return dP, dR, dstate0, dbias

@@ -148,3 +148,59 @@ def test_binding_refuses_host_tensors():
     R = torch.zeros((4, 3))
     with pytest.raises(ValueError):
         slstm.newton_forward(P, R)
+
+
+def _fwd_varlen(lib, **kw):
+    args = dict(P=ctypes.c_void_p(256), dt=0, R=ctypes.c_void_p(256), s0=None,
+                cu=ctypes.c_void_p(512), n=3, S=ctypes.c_void_p(256), h=None, fin=None, T=64, d=16,
+                fm=0, K=3, tol=0.0, init=0, sched=0, ws=ctypes.c_void_p(4096), wsb=1 << 30,
+                stream=None, stats=None)
+    args.update(kw)
+    return lib.slstm_newton_forward_varlen(*args.values())
+
+
+def _bwd_varlen(lib, **kw):
+    args = dict(P=ctypes.c_void_p(256), dt=0, R=ctypes.c_void_p(256), s0=None,
+                cu=ctypes.c_void_p(512), n=3, S=ctypes.c_void_p(256), gs=None, gh=None, gf=None,
+                dP=ctypes.c_void_p(256), dpt=0, dR=ctypes.c_void_p(256), db=None, ds0=None, T=64,
+                d=16, fm=0, sched=0, ws=ctypes.c_void_p(4096), wsb=1 << 30, stream=None)
+    args.update(kw)
+    return lib.slstm_backward_varlen(*args.values())
+
+
+def test_varlen_argument_checks(lib):
+    # packed sequences: the offsets pointer and count are checked, the chain forms refused;
+    # everything here returns on the host before any device work
+    assert _fwd_varlen(lib, cu=None) == slstm.EINVAL
+    assert "cu_seqlens" in lib.slstm_last_error().decode()
+    assert _fwd_varlen(lib, cu=ctypes.c_void_p(514)) == slstm.EINVAL   # not 4-byte aligned
+    assert _fwd_varlen(lib, n=0) == slstm.EINVAL
+    assert _fwd_varlen(lib, n=-2) == slstm.EINVAL
+    assert _fwd_varlen(lib, sched=3) == slstm.EINVAL
+    assert "FUSED_CHAIN" in lib.slstm_last_error().decode()
+    assert _fwd_varlen(lib, T=0) == slstm.EINVAL
+    for sched in (0, 1, 2):
+        assert _fwd_varlen(lib, sched=sched, wsb=100) == slstm.EWORKSPACE
+    assert _bwd_varlen(lib, cu=None) == slstm.EINVAL
+    assert _bwd_varlen(lib, n=0) == slstm.EINVAL
+    assert _bwd_varlen(lib, sched=3) == slstm.EINVAL
+    assert _bwd_varlen(lib, sched=1) == slstm.EINVAL
+    assert _bwd_varlen(lib, wsb=100) == slstm.EWORKSPACE
+    s = lib.slstm_warm_start_varlen(ctypes.c_void_p(256), 0, None, ctypes.c_void_p(512), 3,
+                                    ctypes.c_void_p(256), 64, 16, 0, 3, ctypes.c_void_p(4096), 1 << 30, None)
+    assert s == slstm.EINVAL
+    s = lib.slstm_warm_start_varlen(ctypes.c_void_p(256), 0, None, ctypes.c_void_p(512), 3,
+                                    ctypes.c_void_p(256), 64, 16, 0, 0, ctypes.c_void_p(4096), 10, None)
+    assert s == slstm.EWORKSPACE
+    s = lib.slstm_sequential_forward_varlen(ctypes.c_void_p(256), 0, ctypes.c_void_p(256), None, None, 3,
+                                            ctypes.c_void_p(256), None, None, 64, 16, 0, None)
+    assert s == slstm.EINVAL
+
+
+def test_binding_checks_offsets():
+    P = torch.zeros((1, 10, 4, 3))
+    for bad in ([0, 4, 3, 10], [1, 10], [0, 9], [0]):
+        with pytest.raises(ValueError):
+            slstm._seqs(bad, P)
+    with pytest.raises(ValueError):
+        slstm._seqs([0, 5, 10], torch.zeros((2, 10, 4, 3)))

@@ -41,6 +41,43 @@ def test_sequential_lanes_subset():
         np.testing.assert_array_equal(got[k], full[lb[k], :, :, lj[k]])
 
 
+def test_packed_groups_cover_every_sequence():
+    cu = [0, 0, 5, 5, 6, 20, 20, 21, 21]
+    for n in (1, 2, 3, 5, 50):
+        groups = lanes.packed_groups(cu, n)
+        assert groups[0][0] == 0 and groups[-1][1] == len(cu) - 1
+        assert all(a[1] == b[0] for a, b in zip(groups, groups[1:]))
+        assert all(cu[b] > cu[a] for a, b in groups)  # at least one step per run
+        assert len(groups) <= n
+
+
+def test_packed_runs_match_one_call():
+    """Runs of whole sequences solved apart reproduce the one-call packed oracle: forward,
+    fixed-count Newton (states and residual history) and backward (dR summed over the runs)."""
+    cu = gen.packed_offsets(5, 700, 60)
+    T, n, d = int(cu[-1]), len(cu) - 1, 5
+    rng = np.random.Generator(np.random.PCG64(9))
+    P = rng.standard_normal((1, T, 4, d))
+    P[:, :, 2] += 3.0
+    R = rng.uniform(-0.5, 0.5, (4, d))
+    s0 = np.stack([rng.uniform(-0.5, 0.5, (n, d)), rng.uniform(0.5, 2.0, (n, d)),
+                   rng.uniform(-2.0, 2.0, (n, d)), rng.uniform(-0.9, 0.9, (n, d))], axis=1)
+    for forget in ("exp", "sigmoid"):
+        seq = ref.sequential(P, R, s0, forget, cu_seqlens=cu)
+        np.testing.assert_array_equal(lanes.packed_sequential(P, R, s0, forget, cu, workers=3), seq)
+        S, st = ref.newton(P, R, s0, forget, 3, cu_seqlens=cu)
+        S2, st2 = lanes.packed_newton(P, R, s0, forget, 3, cu, workers=3)
+        np.testing.assert_allclose(S2, S, rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(st2.max_abs_F, st.max_abs_F, rtol=1e-12, atol=1e-300)
+        g = rng.standard_normal(seq.shape)
+        gf = rng.standard_normal((n, 4, d))
+        want = ref.backward(P, R, s0, seq, g, forget, cu_seqlens=cu, g_final=gf)
+        got = lanes.packed_backward(P, R, s0, seq, g, forget, cu, g_final=gf, workers=3)
+        np.testing.assert_allclose(got[0], want[0], rtol=1e-13, atol=1e-14)
+        np.testing.assert_allclose(got[1], want[1], rtol=1e-11)
+        np.testing.assert_allclose(got[2], want[2], rtol=1e-13, atol=1e-14)
+
+
 def test_workload_recipe():
     names = [w.name for w in WORKLOADS]
     assert len(set(names)) == 5

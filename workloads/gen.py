@@ -123,3 +123,26 @@ def random_cotangents_device(seed: int, B: int, T: int, d: int, device):
     g_h = torch.randn((B, T, d), generator=gen, device=device)
     g_final = torch.randn((B, 4, d), generator=gen, device=device)
     return g_states, g_h, g_final
+
+
+def packed_offsets(seed: int, total: int, max_len: int, share_empty: float = 0.05,
+                   share_one: float = 0.05) -> np.ndarray:
+    """Offsets cu_seqlens (S + 1 int64, from 0 to ``total``) of ragged sequences packed end to
+    end: lengths log-uniform in [1, max_len] (many short sequences, a few long ones), with a
+    share of empty and of length-1 sequences mixed in; the last length is cut so that the
+    lengths sum to ``total``."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lengths = []
+    left = total
+    while left > 0:
+        u = rng.uniform()
+        if u < share_empty:
+            n = 0
+        elif u < share_empty + share_one:
+            n = 1
+        else:
+            n = int(np.exp(rng.uniform(0.0, np.log(max_len))))
+        n = min(max(n, 0), left)
+        lengths.append(n)
+        left -= n
+    return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
