@@ -8,7 +8,8 @@ full-layer workload (B=128, T=2048, d_in=d_h=1024, bf16 x and W_x):
     T=1 sequential decode step at B=128 continuing from the final state (its own projection).
 For workloads whose solver input is P the step is the Newton forward alone. The Newton
 forward runs in the schedule the library picks for the shape (--schedule fused); the scan
-form of the fused iteration and the layered schedule are timed after it as context.
+form of the fused iteration, the layered schedule, the backward pass, the same tokens packed
+as ragged sequences (cu_seqlens) and the sequential forward are timed after it as context.
 
 Prints ONE JSON line on stdout. Timing: W untimed warm-up steps, then exactly K steps
 between two device synchronisations, wall clock. Per-kernel durations come from HIP events
@@ -210,6 +211,8 @@ def main():
                     help="skip the context runs of the scan form and the layered schedule")
     ap.add_argument("--no-backward-context", action="store_true",
                     help="skip the context run of the backward pass at the forward solution")
+    ap.add_argument("--no-packed-context", action="store_true",
+                    help="skip the context run on the same tokens packed as ragged sequences")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -449,6 +452,83 @@ def main():
                 log(f"[bench] backward {kind}: {kavg:.3f} ms, {tf:.0f} TFLOP/s (operand transposes included)")
             del dx, dW, pws
         del dP, dR, db, d0, bws, g_h, g_fin
+        torch.cuda.empty_cache()
+
+    if not args.no_packed_context:
+        # the same B*T tokens as ragged sequences packed end to end in one row (cu_seqlens:
+        # log-uniform lengths up to 8192 steps with empty and length-1 sequences mixed in), each
+        # from a zero state: the Newton solve in its scan form and the backward, not the metric
+        from workloads import packed_offsets, random_cotangents_device
+        cu_host = packed_offsets(w.seed, w.B * w.T, 8192)
+        n_seq = len(cu_host) - 1
+        cu = torch.as_tensor(cu_host, dtype=torch.int32, device=dev)
+        BT = w.B * w.T
+        Pp, Sp, Hp = P.view(1, BT, 4, w.d_h), S.view(1, BT, 4, w.d_h), H.view(1, BT, w.d_h)
+        fin = torch.empty((n_seq, 4, w.d_h), dtype=torch.float32, device=dev)
+        pws = slstm.alloc_workspace(slstm.newton_workspace_bytes(1, BT, w.d_h, "fused_scan"), dev)
+
+        def packed_fwd():
+            slstm.newton_forward(Pp, R, None, w.forget, w.max_iters, w.tol, "warm", states=Sp, h_out=Hp,
+                                 final_state=fin, workspace=pws, stats=False, cu_seqlens=cu)
+
+        packed_fwd()
+        torch.cuda.synchronize()
+        pst = slstm.read_stats(pws)
+        reps = max(3, args.steps // 2)
+        slstm.profile_reset()
+        slstm.profile_enable(True)
+        tp = time.perf_counter()
+        for _ in range(reps):
+            packed_fwd()
+        torch.cuda.synchronize()
+        p_ms = (time.perf_counter() - tp) * 1000.0 / reps
+        slstm.profile_enable(False)
+        pk = {}
+        for kind in ("warm_start", "newton_iteration", "final_residual"):
+            d = slstm.profile_durations(kind)
+            if d:
+                avg = sum(d) / len(d)
+                pk[kind] = {"launches_per_solve": len(d) // reps, "avg_ms": round(avg, 4),
+                            "GB_s": round(work[kind]["bytes"] / (avg * 1e-3) / 1e9, 1)}
+        it = pk["newton_iteration"]
+        log(f"[bench] packed ({n_seq} sequences): solve {p_ms:.3f} ms, iteration kernel {it['avg_ms']:.3f} ms, "
+            f"{it['GB_s']:.0f} GB/s algorithmic")
+        _, g_hp, _ = random_cotangents_device(w.seed + 98, 1, BT, w.d_h, dev)
+        g_fp = torch.randn((n_seq, 4, w.d_h), generator=torch.Generator(device=dev).manual_seed(w.seed + 97),
+                           device=dev)
+        dPp = torch.empty((1, BT, 4, w.d_h), dtype=torch.bfloat16, device=dev)
+        dRp = torch.empty((4, w.d_h), dtype=torch.float32, device=dev)
+        d0p = torch.empty((n_seq, 4, w.d_h), dtype=torch.float32, device=dev)
+        pbws = slstm.alloc_workspace(slstm.backward_workspace_bytes(1, BT, w.d_h), dev)
+
+        def packed_bwd():
+            slstm.backward(Pp, R, Sp, None, None, g_hp, g_fp, w.forget, dP=dPp, dR=dRp, dstate0=d0p,
+                           workspace=pbws, cu_seqlens=cu)
+
+        packed_bwd()
+        torch.cuda.synchronize()
+        slstm.profile_reset()
+        slstm.profile_enable(True)
+        for _ in range(reps):
+            packed_bwd()
+        torch.cuda.synchronize()
+        slstm.profile_enable(False)
+        bd = slstm.profile_durations("backward")
+        pb = sum(bd) / len(bd)
+        pb_gbs = work["backward"]["bytes"] / (pb * 1e-3) / 1e9
+        log(f"[bench] packed backward: recurrence kernels {pb:.3f} ms, {pb_gbs:.0f} GB/s algorithmic")
+        context["packed"] = {
+            "sequences": n_seq, "tokens": BT, "max_len": int(max(cu_host[1:] - cu_host[:-1])),
+            "form": "scan", "solve_ms": round(p_ms, 4), "state_elems_per_s": n_e / (p_ms * 1e-3),
+            "solver": {"iters": pst.iters, "max_abs_F": pst.max_abs_F[-1], "diverged": pst.diverged},
+            "kernels": pk,
+            "roofline": {"bound": "hbm", "kernel": "newton_iteration", "achieved": it["GB_s"],
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(it["GB_s"] / HBM_PEAK_GBS, 4)},
+            "backward": {"kernel_avg_ms": round(pb, 4), "gradients_in": "dL/dh, dL/d final states",
+                         "roofline": {"bound": "hbm", "kernel": "backward", "achieved": round(pb_gbs, 1),
+                                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": round(pb_gbs / HBM_PEAK_GBS, 4)}}}
+        del pws, pbws, dPp, dRp, d0p, g_hp, g_fp, fin
         torch.cuda.empty_cache()
 
     if not args.no_sequential_context:

@@ -140,7 +140,7 @@ Form newton_form(int B, int d, slstm_schedule s) {
 }
 
 struct NewtonLayout {
-  size_t ctl, desc, A, rhs, S2, total;
+  size_t ctl, desc, A, rhs, S2, tab, total;
 };
 
 // control block, look-back words, then either the second iterate buffer (fused) or the
@@ -167,6 +167,9 @@ NewtonLayout newton_layout(int B, int T, int d, Form form) {
     L.S2 = 0;
     L.total = align_up(L.rhs + n_state * sizeof(float));
   }
+  // the sequence table of packed calls (unused otherwise)
+  L.tab = L.total;
+  L.total = align_up(L.tab + slstm::seq_table_ints(T) * sizeof(int));
   return L;
 }
 
@@ -191,14 +194,16 @@ hipError_t launch_warm(const void* P, bool bf16, const float* state0, float* S, 
 }
 
 struct ScanLayout {
-  size_t ctl, desc, total;
+  size_t ctl, desc, tab, total;
 };
 
-ScanLayout scan_layout(size_t desc_words) {
+// control block, look-back words, then (table_T > 0) a sequence table for table_T steps
+ScanLayout scan_layout(size_t desc_words, int table_T = 0) {
   ScanLayout L;
   L.ctl = 0;
   L.desc = align_up(slstm::kControlBytes);
-  L.total = align_up(L.desc + desc_words * 8);
+  L.tab = align_up(L.desc + desc_words * 8);
+  L.total = table_T > 0 ? align_up(L.tab + slstm::seq_table_ints(table_T) * sizeof(int)) : L.tab;
   return L;
 }
 
@@ -340,7 +345,7 @@ bool pipe_solve(Form form, int max_iters, float tol) {
 
 // control block, the look-back words, then the dR rows and their chunk sums
 struct BackwardLayout {
-  size_t ctl, desc, rows, total;
+  size_t ctl, desc, rows, tab, total;
 };
 
 bool backward_schedule(slstm_schedule s) {
@@ -360,7 +365,8 @@ BackwardLayout backward_layout(int B, int T, int d, bool scan) {
   L.ctl = 0;
   L.desc = align_up(slstm::kControlBytes);
   L.rows = align_up(L.desc + slstm::backward_desc_words(B, T, d, scan) * 8);
-  L.total = align_up(L.rows + slstm::backward_row_floats(B, T, d, scan) * sizeof(float));
+  L.tab = align_up(L.rows + slstm::backward_row_floats(B, T, d, scan) * sizeof(float));
+  L.total = align_up(L.tab + slstm::seq_table_ints(T) * sizeof(int));  // packed calls only
   return L;
 }
 
@@ -452,6 +458,11 @@ slstm_status newton_forward(const void* P, slstm_dtype P_dtype, const float* R, 
   const i64 n_state = static_cast<i64>(B) * T * 4 * d_h;
 
   HIP_TRY(slstm::launch_init_control(ctl, st));
+  if (seqs.cu != nullptr) {  // the sequence table the packed kernels start their cursors from
+    int* tab = at<int>(workspace, L.tab);
+    HIP_TRY(slstm::launch_seq_table(seqs.cu, seqs.n, T, tab, st));
+    seqs.tab = tab;
+  }
   unsigned int* tickets = slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0];
   if (seqs.cu == nullptr && pipe_solve(form, max_iters, tol)) {
     // the whole fixed-count solve in one pass; it writes the final states, h and every residual
@@ -502,11 +513,16 @@ slstm_status warm_start(const void* P, slstm_dtype P_dtype, const float* state0,
   if (seqs.cu != nullptr && schedule == SLSTM_SCHEDULE_FUSED_CHAIN)
     return fail(SLSTM_EINVAL, "packed sequences run the scan form only (not FUSED_CHAIN)");
   const bool chain = seqs.cu == nullptr && warm_chain_form(B, d_h, schedule);
-  const ScanLayout L = scan_layout(warm_desc_words_for(B, T, d_h, chain));
+  const ScanLayout L = scan_layout(warm_desc_words_for(B, T, d_h, chain), T);
   if (workspace_bytes < L.total) return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
   hipStream_t st = static_cast<hipStream_t>(stream);
   Control* ctl = at<Control>(workspace, L.ctl);
   HIP_TRY(slstm::launch_init_control(ctl, st));
+  if (seqs.cu != nullptr) {  // the sequence table the packed kernels start their cursors from
+    int* tab = at<int>(workspace, L.tab);
+    HIP_TRY(slstm::launch_seq_table(seqs.cu, seqs.n, T, tab, st));
+    seqs.tab = tab;
+  }
   HIP_TRY(launch_warm(P, P_dtype == SLSTM_BF16, state0, states, B, T, d_h, cell_mode_of(fmode),
                       chain, at<unsigned long long>(workspace, L.desc), ctl, st, seqs));
   return SLSTM_OK;
@@ -538,6 +554,11 @@ slstm_status backward(const void* P, slstm_dtype P_dtype, const float* R, const 
   hipStream_t st = static_cast<hipStream_t>(stream);
   Control* ctl = at<Control>(workspace, L.ctl);
   HIP_TRY(slstm::launch_init_control(ctl, st));
+  if (seqs.cu != nullptr) {  // the sequence table the packed kernels start their cursors from
+    int* tab = at<int>(workspace, L.tab);
+    HIP_TRY(slstm::launch_seq_table(seqs.cu, seqs.n, T, tab, st));
+    seqs.tab = tab;
+  }
   const uint32_t ep = next_epoch();
   HIP_TRY(timed(SLSTM_KERNEL_BACKWARD, st, [&] {
     return slstm::launch_backward(P, P_dtype == SLSTM_BF16, R, state0, states, g_states, g_h, g_final, dP,
@@ -698,7 +719,7 @@ slstm_status slstm_scan_block4(const float* A, const float* rhs, float* x, int B
 
 size_t slstm_warm_start_workspace_bytes(int B, int T, int d_h, slstm_schedule schedule) {
   if (check_dims(B, T, d_h) != SLSTM_OK || !known_schedule(schedule)) return 0;
-  return scan_layout(warm_desc_words_for(B, T, d_h, warm_chain_form(B, d_h, schedule))).total;
+  return scan_layout(warm_desc_words_for(B, T, d_h, warm_chain_form(B, d_h, schedule)), T).total;
 }
 
 slstm_status slstm_warm_start(const void* P, slstm_dtype P_dtype, const float* state0,

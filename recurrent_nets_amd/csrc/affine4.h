@@ -126,6 +126,13 @@ __device__ __forceinline__ void quad_row_of_last(const float M[16], const float 
 // epoch-tagged (see tag_store); the word w of tile t for lane L sits at
 // desc[(t * kLookBackWords + w) * n_lanes_pad + L]: w = 0..3 the inclusive value, 4 + 4 i + k
 // the entry (i, k) of M, 20 + i the entry i of v.
+// With CUT (packed sequences only: the test costs the unpacked kernels' schedule), maps that
+// are exactly zero in every lane of the wave (a packed sequence starts inside them)
+// make everything before them irrelevant: the fold stops there and the anchor's value is not
+// waited for, and an anchor whose own maps are zero publishes its inclusive value (its v)
+// before its look-back, so a chain of anchors breaks at every sequence start. For finite values
+// the result is the one the full fold gives (0 * x = 0); a non-finite value is not carried
+// across such a map.
 //   pf_word: this thread's word of the anchor's inclusive value, loaded ahead of time
 //            (quad_look_back_prefetch); it costs no wait when it already carries the epoch.
 __device__ __forceinline__ unsigned long long quad_look_back_prefetch(
@@ -137,6 +144,7 @@ __device__ __forceinline__ unsigned long long quad_look_back_prefetch(
                            __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <bool CUT = false>
 __device__ __forceinline__ void quad_look_back(const float arow[4], float av, float carry[4],
                                                unsigned long long* __restrict__ desc,
                                                i64 n_lanes_pad, i64 my_lane, int q, int tt,
@@ -145,11 +153,20 @@ __device__ __forceinline__ void quad_look_back(const float arow[4], float av, fl
   auto word = [&](int tile, int w) {
     return desc + (static_cast<i64>(tile) * kLookBackWords + w) * n_lanes_pad + my_lane;
   };
+  // whether the maps of every lane of the wave are exactly zero (each thread holds one row of
+  // its lane's map): a wave-uniform answer, so the branches on it stay scalar
+  auto wave_zero = [&](const float r[4]) {
+    const bool z = r[0] == 0.0f && r[1] == 0.0f && r[2] == 0.0f && r[3] == 0.0f;
+    return __builtin_amdgcn_ballot_w64(z) == __builtin_amdgcn_read_exec();
+  };
   const bool anchor = (tt % anchor_stride) == 0;
+  const bool own_zero = CUT && wave_zero(arow);
   if (!anchor) {
 #pragma unroll
     for (int k = 0; k < 4; ++k) tag_store(word(tt, 4 + 4 * q + k), arow[k], epoch);
     tag_store(word(tt, 20 + q), av, epoch);
+  } else if (own_zero) {
+    tag_store(word(tt, q), av, epoch);  // the inclusive value does not depend on the carry
   }
   float cq = 0.0f;  // carry[q]
   if (tt > 0) {
@@ -158,7 +175,12 @@ __device__ __forceinline__ void quad_look_back(const float arow[4], float av, fl
     float mrow[4], vacc = 0.0f;
 #pragma unroll
     for (int k = 0; k < 4; ++k) mrow[k] = (k == q) ? 1.0f : 0.0f;
+    bool cut = false;  // the accumulated map is zero: tiles further back cannot change the carry
     for (int p = tt - 1; p > a; --p) {
+      if (CUT && wave_zero(mrow)) {
+        cut = true;
+        break;
+      }
       float prow[4], pv;
       while (true) {
         bool ok = true;
@@ -186,21 +208,26 @@ __device__ __forceinline__ void quad_look_back(const float arow[4], float av, fl
       for (int k = 0; k < 4; ++k) mrow[k] = nrow[k];
       vacc = nv;
     }
-    // the anchor's inclusive value, element q
-    float xq = __uint_as_float(static_cast<uint32_t>(pf_word));
-    bool ok = static_cast<uint32_t>(pf_word >> 32) == epoch;
-    while (!ok) {
-      ok = tag_load(word(a, q), epoch, xq);
-      if (ok) break;
-      __builtin_amdgcn_s_sleep(2);
+    cut = cut || (CUT && wave_zero(mrow));
+    if (cut) {
+      cq = vacc;
+    } else {
+      // the anchor's inclusive value, element q
+      float xq = __uint_as_float(static_cast<uint32_t>(pf_word));
+      bool ok = static_cast<uint32_t>(pf_word >> 32) == epoch;
+      while (!ok) {
+        ok = tag_load(word(a, q), epoch, xq);
+        if (ok) break;
+        __builtin_amdgcn_s_sleep(2);
+      }
+      cq = fmaf(mrow[0], quad_bcast<0>(xq), fmaf(mrow[1], quad_bcast<1>(xq), fmaf(mrow[2], quad_bcast<2>(xq), fmaf(mrow[3], quad_bcast<3>(xq), vacc))));
     }
-    cq = fmaf(mrow[0], quad_bcast<0>(xq), fmaf(mrow[1], quad_bcast<1>(xq), fmaf(mrow[2], quad_bcast<2>(xq), fmaf(mrow[3], quad_bcast<3>(xq), vacc))));
   }
   carry[0] = quad_bcast<0>(cq);
   carry[1] = quad_bcast<1>(cq);
   carry[2] = quad_bcast<2>(cq);
   carry[3] = quad_bcast<3>(cq);
-  if (anchor) {
+  if (anchor && !own_zero) {
     const float xe = fmaf(arow[0], carry[0], fmaf(arow[1], carry[1], fmaf(arow[2], carry[2], fmaf(arow[3], carry[3], av))));
     tag_store(word(tt, q), xe, epoch);
   }

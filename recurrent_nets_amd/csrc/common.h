@@ -48,7 +48,14 @@ constexpr int kCellFloored = 2;
 struct Seqs {
   const int* cu = nullptr;
   int n = 0;
+  const int* tab = nullptr;  // optional: seq_table entries (see build_seq_table)
 };
+
+// seq_table: entry k holds the sequence containing step k << kSeqTabShift, i.e. the s with
+// cu[s] <= 4k < cu[s+1] (the largest s with cu[s] <= 4k); ceil(T / 4) entries
+constexpr int kSeqTabShift = 2;
+// look-back anchor stride of the packed scan kernels
+constexpr int kPackedAnchorStride = 4;
 
 struct SeqCursor {
   const int* cu;
@@ -58,14 +65,25 @@ struct SeqCursor {
   int end;    // one past its last step
 };
 
-// cursor at step t (t >= 0): the last sequence whose first step is <= t
-__device__ __forceinline__ SeqCursor seq_cursor(const int* cu, int n_seqs, int b, int t) {
+// cursor at step t (t >= 0): the last sequence whose first step is <= t. With a sequence table
+// one load finds the sequence at the table step at or before t, then the cursor walks forward;
+// without one, a binary search over the offsets. Table entries are clamped into [0, n_seqs), so
+// every access stays in bounds whatever the offsets hold.
+__device__ __forceinline__ SeqCursor seq_cursor(const int* cu, int n_seqs, int b, int t,
+                                                const int* tab = nullptr) {
   if (cu == nullptr) return {nullptr, 0, b, 0, 0x7fffffff};
-  int lo = 0, hi = n_seqs - 1;  // largest s in [0, n_seqs) with cu[s] <= t (0 if none)
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (cu[mid] <= t) lo = mid;
-    else hi = mid - 1;
+  int lo;
+  if (tab != nullptr) {
+    lo = min(max(tab[t >> kSeqTabShift], 0), n_seqs - 1);
+    while (lo + 1 < n_seqs && cu[lo + 1] <= t) ++lo;
+  } else {
+    lo = 0;
+    int hi = n_seqs - 1;  // largest s in [0, n_seqs) with cu[s] <= t (0 if none)
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cu[mid] <= t) lo = mid;
+      else hi = mid - 1;
+    }
   }
   return {cu, n_seqs, lo, cu[lo], cu[lo + 1]};
 }

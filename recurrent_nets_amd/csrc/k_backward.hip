@@ -214,7 +214,8 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
     const float* __restrict__ g_final, void* __restrict__ dP, int dp_bf16, float* __restrict__ dstate0,
     float* __restrict__ sum_rows, int T, int d, int n_jt, int n_lg, int n_tt, int anchor_stride,
     unsigned long long* __restrict__ desc, unsigned int* __restrict__ tickets, int n_ctr,
-    uint32_t epoch, const int* __restrict__ cu, int n_seqs) {
+    uint32_t epoch, const int* __restrict__ cu, int n_seqs,
+    const int* __restrict__ seq_tab) {
   constexpr bool sig = (CM & kCellSigmoid) != 0;   // forget-gate form and read-out,
   constexpr bool floored = (CM & kCellFloored) != 0;  // fixed per instantiation
   __shared__ int s_tile[2];
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
   // packed: the sequence starting at each step of the sub-chunk and the one ending there (-1: none)
   int sq[TSUB], lq[TSUB];
   if constexpr (PACKED) {
-    SeqCursor seq = seq_cursor(cu, n_seqs, b, t_start);
+    SeqCursor seq = seq_cursor(cu, n_seqs, b, t_start, seq_tab);
 #pragma unroll
     for (int u = 0; u < TSUB; ++u) {
       const int t = t_start + u;
@@ -340,13 +341,14 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
       const float zero[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       mat4_vec(At, w, zero, v);
       mat4_mul_left(At, M);
-      if (PACKED && sq[u] >= 0) {
-        // a sequence start: nothing flows back to the step before it
+    }
+    if (PACKED && sq[u] >= 0) {
+      // a sequence start: nothing flows back to the step before it (padding lanes past d_h
+      // too, so that all lanes of a tile agree on where the maps restart)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) M[e] = 0.0f;
+      for (int e = 0; e < 16; ++e) M[e] = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = 0.0f;
-      }
+      for (int e = 0; e < 4; ++e) v[e] = 0.0f;
     }
   }
 
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
   {
     float arow[4], av;
     quad_row_of_last(M, v, q, arow, av);
-    quad_look_back(arow, av, carry, desc, n_lanes_pad, my_lane, q, tr, anchor_stride, epoch, pf);
+    quad_look_back<PACKED>(arow, av, carry, desc, n_lanes_pad, my_lane, q, tr, anchor_stride, epoch, pf);
   }
   // y entering the sub-chunk: the inclusive value of the thread before in the quad
   float y[4];
@@ -537,11 +539,14 @@ hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const flo
   } while (0)
   if (scan) {
     const int stride = look_back_anchor_stride(gr.n_lg, SLSTM_BACK_SCAN_MIN_WAVES);
+  // packed rows are few lane groups along a long T: anchors every 4 tiles (measured best
+  // between 1 and 8 over short and long sequence mixes)
+  const int stride_used = seqs.cu != nullptr ? kPackedAnchorStride : stride;
     if (packed) {
 #define SLSTM_BACK_LAUNCH(BF, CM_, GS)                                                                   \
   backward_scan_kernel<BF, CM_, GS, kBackScanTSub, true><<<grid, kBackScanBlock, 0, stream>>>(           \
-      P, R, state0, S, g, g_h, g_final, dP, dpb, dstate0, rows, T, d, a, c, e, stride, desc, tickets, n_ctr, \
-      epoch, seqs.cu, seqs.n)
+      P, R, state0, S, g, g_h, g_final, dP, dpb, dstate0, rows, T, d, a, c, e, stride_used, desc, tickets, n_ctr, \
+      epoch, seqs.cu, seqs.n, seqs.tab)
       SLSTM_BACK_DISPATCH;
 #undef SLSTM_BACK_LAUNCH
       hipError_t err = hipGetLastError();
@@ -554,8 +559,8 @@ hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const flo
     } else {
 #define SLSTM_BACK_LAUNCH(BF, CM_, GS)                                                                   \
   backward_scan_kernel<BF, CM_, GS, kBackScanTSub, false><<<grid, kBackScanBlock, 0, stream>>>(          \
-      P, R, state0, S, g, g_h, g_final, dP, dpb, dstate0, rows, T, d, a, c, e, stride, desc, tickets, n_ctr, \
-      epoch, nullptr, 0)
+      P, R, state0, S, g, g_h, g_final, dP, dpb, dstate0, rows, T, d, a, c, e, stride_used, desc, tickets, n_ctr, \
+      epoch, nullptr, 0, nullptr)
       SLSTM_BACK_DISPATCH;
 #undef SLSTM_BACK_LAUNCH
     }

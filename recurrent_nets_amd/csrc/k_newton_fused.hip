@@ -87,7 +87,8 @@ __global__ __launch_bounds__(kFusedBlock, SLSTM_FUSED_MIN_WAVES) void newton_ite
     const float* __restrict__ S_in, float* __restrict__ S_out, int T, int d, int n_jt, int n_lg,
     int n_tt, int anchor_stride, int cell_mode, unsigned long long* __restrict__ desc,
     unsigned int* __restrict__ tickets, int n_ctr, uint32_t epoch, Control* __restrict__ ctl,
-    int k_iter, float tol, const int* __restrict__ cu, int n_seqs) {
+    int k_iter, float tol, const int* __restrict__ cu, int n_seqs,
+    const int* __restrict__ seq_tab) {
   if (ctl->stopped) return;
   if (k_iter > 0 && tol > 0.0f && err_reduced(ctl, k_iter - 1) < tol) {
     // the previous iterate already met the tolerance: it is the result
@@ -167,26 +168,28 @@ __global__ __launch_bounds__(kFusedBlock, SLSTM_FUSED_MIN_WAVES) void newton_ite
   float fmax_local = 0.0f;
   CellIn pv = pv0;
   SeqCursor seq;
-  if constexpr (PACKED) seq = seq_cursor(cu, n_seqs, b, t_start);
+  if constexpr (PACKED) seq = seq_cursor(cu, n_seqs, b, t_start, seq_tab);
 #pragma unroll
   for (int u = 0; u < TSUB; ++u) {
     const int t = t_start + u;
     float a[12], r[4];
+    // packed: the sequence starting at t (every lane walks the offsets, padding lanes too, so
+    // that all lanes of a tile agree on where the maps restart)
+    int sq = -1;
+    if constexpr (PACKED) {
+      if (t < T) sq = seq_begin(seq, t);
+    }
     if (valid && t < T) {
-      bool start = t == 0;
-      if constexpr (PACKED) {
-        const int sq = seq_begin(seq, t);
-        start = sq >= 0;
-        if (start) pv = state0_of(state0, sq, ud, j);
-      }
+      const bool start = PACKED ? sq >= 0 : t == 0;
+      if (PACKED && start) pv = state0_of(state0, sq, ud, j);
       step_terms(pv, pg[u], sv[u], rz, ri, rf, ro, sig, floored, start, a, r);
 #pragma unroll
       for (int k = 0; k < 4; ++k) fmax_local = fmaxf(fmax_local, abs_nan_inf(r[k]));
       pv = {sv[u][0], sv[u][1], sv[u][2], sv[u][3]};
     } else {
-      // identity map
+      // identity map (zero at a sequence start)
 #pragma unroll
-      for (int q = 0; q < 12; ++q) a[q] = (kSpPlane[q] % 5 == 0) ? 1.0f : 0.0f;
+      for (int q = 0; q < 12; ++q) a[q] = (kSpPlane[q] % 5 == 0 && sq < 0) ? 1.0f : 0.0f;
 #pragma unroll
       for (int k = 0; k < 4; ++k) r[k] = 0.0f;
     }
@@ -226,7 +229,7 @@ __global__ __launch_bounds__(kFusedBlock, SLSTM_FUSED_MIN_WAVES) void newton_ite
   {
     float arow[4], av;
     quad_row_of_last(M, v, sc, arow, av);
-    quad_look_back(arow, av, carry, desc, n_lanes_pad, my_lane, sc, tt, anchor_stride, epoch, pf);
+    quad_look_back<PACKED>(arow, av, carry, desc, n_lanes_pad, my_lane, sc, tt, anchor_stride, epoch, pf);
   }
 
   // ---- re-run each sub-chunk from the value entering it and write the updated iterate ----
@@ -279,13 +282,16 @@ hipError_t launch_newton_iteration(const void* P, bool p_bf16, const float* R, c
   const i64 blocks = n_lg * n_tt;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const int stride = look_back_anchor_stride(n_lg, SLSTM_FUSED_MIN_WAVES);
+  // packed rows are few lane groups along a long T: anchors every 4 tiles (measured best
+  // between 1 and 8 over short and long sequence mixes)
+  const int stride_used = seqs.cu != nullptr ? kPackedAnchorStride : stride;
   const int n_ctr = ticket_counters(n_lg);
   const dim3 grid(static_cast<unsigned>(blocks));
   const int sig = cell_mode;
 #define SLSTM_FUSED_LAUNCH(BF, PK)                                                                   \
   newton_iter_kernel<BF, kFusedTSub, PK><<<grid, kFusedBlock, 0, stream>>>(                          \
       P, R, state0, S_in, S_out, T, d, static_cast<int>(n_jt), static_cast<int>(n_lg),                \
-      static_cast<int>(n_tt), stride, sig, desc, tickets, n_ctr, epoch, ctl, k_iter, tol, seqs.cu, seqs.n)
+      static_cast<int>(n_tt), stride_used, sig, desc, tickets, n_ctr, epoch, ctl, k_iter, tol, seqs.cu, seqs.n, seqs.tab)
   const bool packed = seqs.cu != nullptr;
   if (p_bf16) {
     if (packed) SLSTM_FUSED_LAUNCH(true, true);

@@ -40,7 +40,8 @@ __global__ __launch_bounds__(kResBlock, 2) void residual_kernel(
     const float* __restrict__ S, float* __restrict__ A, float* __restrict__ rhs, int T, int d,
     int n_chunks, int cell_mode, Control* __restrict__ ctl, unsigned int* __restrict__ err_base,
     int err_stride, int stop_check_iter, float tol, float* __restrict__ h_out,
-    const int* __restrict__ cu, int n_seqs) {
+    const int* __restrict__ cu, int n_seqs,
+    const int* __restrict__ seq_tab) {
   if (ctl != nullptr) {
     if (ctl->stopped) return;
     if (stop_check_iter >= 0 && tol > 0.0f && err_reduced(ctl, stop_check_iter) < tol) {
@@ -71,7 +72,7 @@ __global__ __launch_bounds__(kResBlock, 2) void residual_kernel(
       const float* sp = Sb + static_cast<i64>(t0 - 1) * row4;
       pv = {sp[j], sp[ud + j], sp[2 * ud + j], sp[3 * ud + j]};
     }
-    SeqCursor seq = seq_cursor(cu, n_seqs, b, t0);
+    SeqCursor seq = seq_cursor(cu, n_seqs, b, t0, seq_tab);
     // next step's operands are loaded one step ahead
     float pn[4], sn[4];
     auto load_step = [&](int t, float (&pg)[4], float (&st)[4]) {
@@ -138,15 +139,15 @@ static void launch_mode(int mode, dim3 grid, hipStream_t stream, const void* P, 
   if (mode == kJacDense)
     residual_kernel<BF16, kJacDense><<<grid, kResBlock, 0, stream>>>(P, R, state0, S, A, rhs, T, d,
                                                                       n_chunks, sig, ctl, err_base, err_stride, chk, tol, h_out,
-                                                                      seqs.cu, seqs.n);
+                                                                      seqs.cu, seqs.n, seqs.tab);
   else if (mode == kJacSparse)
     residual_kernel<BF16, kJacSparse><<<grid, kResBlock, 0, stream>>>(P, R, state0, S, A, rhs, T, d,
                                                                        n_chunks, sig, ctl, err_base, err_stride, chk, tol, h_out,
-                                                                       seqs.cu, seqs.n);
+                                                                       seqs.cu, seqs.n, seqs.tab);
   else
     residual_kernel<BF16, kJacNone><<<grid, kResBlock, 0, stream>>>(P, R, state0, S, nullptr, nullptr,
                                                                      T, d, n_chunks, sig, ctl, err_base, err_stride, chk, tol, h_out,
-                                                                     seqs.cu, seqs.n);
+                                                                     seqs.cu, seqs.n, seqs.tab);
 }
 
 hipError_t launch_residual(const void* P, bool p_bf16, const float* R, const float* state0,

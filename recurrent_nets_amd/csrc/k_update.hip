@@ -192,6 +192,23 @@ hipError_t launch_select_iterate(const Control* ctl, const float* buf0, const fl
   return hipGetLastError();
 }
 
+// entry k of the sequence table: the sequence holding step 4k (a binary search per entry, all
+// entries in parallel)
+__global__ __launch_bounds__(kUpdBlock) void seq_table_kernel(const int* __restrict__ cu, int n_seqs,
+                                                             int* __restrict__ tab, int n_tab) {
+  const int k = blockIdx.x * kUpdBlock + threadIdx.x;
+  if (k >= n_tab) return;
+  tab[k] = seq_cursor(cu, n_seqs, 0, k << kSeqTabShift).s;
+}
+
+size_t seq_table_ints(int T) { return (static_cast<size_t>(T) + (1u << kSeqTabShift) - 1) >> kSeqTabShift; }
+
+hipError_t launch_seq_table(const int* cu, int n_seqs, int T, int* tab, hipStream_t stream) {
+  const int n_tab = static_cast<int>(seq_table_ints(T));
+  seq_table_kernel<<<(n_tab + kUpdBlock - 1) / kUpdBlock, kUpdBlock, 0, stream>>>(cu, n_seqs, tab, n_tab);
+  return hipGetLastError();
+}
+
 hipError_t launch_zero(float* p, i64 n_floats, hipStream_t stream) {
   const i64 n4 = n_floats / 4;
   zero_kernel<<<stream_grid(n4), kUpdBlock, 0, stream>>>(reinterpret_cast<float4*>(p), n4);

@@ -112,7 +112,8 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
     const void* __restrict__ P, const float* __restrict__ state0, float* __restrict__ S, int T,
     int d, int cell_mode, int n_jt, int n_lg, int n_tt, int anchor_stride,
     unsigned long long* __restrict__ desc, unsigned int* __restrict__ tickets, int n_ctr, uint32_t epoch,
-    const int* __restrict__ cu, int n_seqs) {
+    const int* __restrict__ cu, int n_seqs,
+    const int* __restrict__ seq_tab) {
   __shared__ int s_tile[2];
   __shared__ LogAgg s_agg[64];
   __shared__ float s_carry[64][3];
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
   // the sequence starting at each step of the sub-chunk, or -1 (packed only)
   int sq[kWarmTSub];
   if constexpr (PACKED) {
-    SeqCursor seq = seq_cursor(cu, n_seqs, b, t_start);
+    SeqCursor seq = seq_cursor(cu, n_seqs, b, t_start, seq_tab);
 #pragma unroll
     for (int u = 0; u < kWarmTSub; ++u) sq[u] = (t_start + u < T) ? seq_begin(seq, t_start + u) : -1;
   }
@@ -177,9 +178,10 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
     // one step as a run: L = l, E = i~ - l, cz = z, nz = 1
     LogAgg stp = {lf[u], it[u] - lf[u], zz[u], 1.0f};
     if constexpr (PACKED) {
-      if (valid && sq[u] >= 0) {
-        // a sequence start: the step from the sequence's state0, in absolute form
-        const CellIn s0 = state0_of(state0, sq[u], ud, j);
+      if (sq[u] >= 0) {
+        // a sequence start: the step from the sequence's state0, in absolute form (a padding
+        // lane past d_h takes zeros, so that all lanes of a tile agree on where runs restart)
+        const CellIn s0 = valid ? state0_of(state0, sq[u], ud, j) : CellIn{0.0f, 0.0f, 0.0f, 0.0f};
         float m = s0.m, c = s0.c, n = s0.n;
         apply_relative(stp, m, c, n);
         stp = {m, INFINITY, c, n};
@@ -218,27 +220,43 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
     // fixed dataflow (results independent of scheduling): anchors publish their carry out,
     // the tiles in between their run aggregate before waiting; a tile folds the aggregates
     // down to the nearest anchor in a fixed order and applies it to the anchor's carry out
+    // packed: an absolute run does not depend on what enters it, so the fold stops at the first
+    // absolute one (tiles further back cannot change it) and the anchor's carry is not waited
+    // for, and an anchor whose own run is absolute publishes its carry out before its look-back:
+    // a chain of anchors breaks at every sequence start
+    // (wave-uniform tests: the branches on them stay scalar)
+    auto wave_abs = [&](const LogAgg& X) {
+      return __builtin_amdgcn_ballot_w64(absolute(X)) == __builtin_amdgcn_read_exec();
+    };
     const bool anchor = (tt % anchor_stride) == 0;
+    const bool own_abs = PACKED && wave_abs(tile);
     if (!anchor) {
       tag_store(word(tt, 4), tile.L, epoch);
       tag_store(word(tt, 5), tile.E, epoch);
       tag_store(word(tt, 6), tile.cz, epoch);
       tag_store(word(tt, 7), tile.nz, epoch);
+    } else if (own_abs) {
+      tag_store(word(tt, 0), tile.L, epoch);
+      tag_store(word(tt, 1), tile.cz, epoch);
+      tag_store(word(tt, 2), tile.nz, epoch);
     }
     if (tt > 0) {
       const int a = ((tt - 1) / anchor_stride) * anchor_stride;
       LogAgg acc = {0.0f, -INFINITY, 0.0f, 0.0f};  // runs a+1 .. tt-1, composed
       for (int p = tt - 1; p > a; --p) {
+        if (PACKED && wave_abs(acc)) break;
         LogAgg pa;
         while (!(tag_load(word(p, 4), epoch, pa.L) & tag_load(word(p, 5), epoch, pa.E) &
                  tag_load(word(p, 6), epoch, pa.cz) & tag_load(word(p, 7), epoch, pa.nz)))
           __builtin_amdgcn_s_sleep(2);
         acc = compose<PACKED>(pa, acc);
       }
-      float xm, xc, xn;
-      while (!(tag_load(word(a, 0), epoch, xm) & tag_load(word(a, 1), epoch, xc) &
-               tag_load(word(a, 2), epoch, xn)))
-        __builtin_amdgcn_s_sleep(2);
+      float xm = 0.0f, xc = 0.0f, xn = 0.0f;
+      if (!(PACKED && wave_abs(acc))) {
+        while (!(tag_load(word(a, 0), epoch, xm) & tag_load(word(a, 1), epoch, xc) &
+                 tag_load(word(a, 2), epoch, xn)))
+          __builtin_amdgcn_s_sleep(2);
+      }
       apply<PACKED>(acc, xm, xc, xn);
       cm = xm;
       cc = xc;
@@ -247,7 +265,7 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
     s_carry[l][0] = cm;
     s_carry[l][1] = cc;
     s_carry[l][2] = cn;
-    if (anchor) {
+    if (anchor && !own_abs) {
       float em = cm, ec = cc, en = cn;
       apply<PACKED>(tile, em, ec, en);
       tag_store(word(tt, 0), em, epoch);
@@ -321,11 +339,14 @@ hipError_t launch_warm_start(const void* P, bool p_bf16, const float* state0, fl
   const dim3 grid(static_cast<unsigned>(blocks));
   const int sig = cell_mode;
   const int stride = look_back_anchor_stride(n_lg, 2);
+  // packed rows are few lane groups along a long T: anchors every 4 tiles (measured best
+  // between 1 and 8 over short and long sequence mixes)
+  const int stride_used = seqs.cu != nullptr ? kPackedAnchorStride : stride;
   const int n_ctr = ticket_counters(n_lg);
 #define SLSTM_WARM_SCAN_LAUNCH(BF, PK)                                                                    \
   warm_start_kernel<BF, PK><<<grid, kWarmBlock, 0, stream>>>(P, state0, S, T, d, sig, static_cast<int>(n_jt), \
                                                              static_cast<int>(n_lg), static_cast<int>(n_tt), \
-                                                             stride, desc, tickets, n_ctr, epoch, seqs.cu, seqs.n)
+                                                             stride_used, desc, tickets, n_ctr, epoch, seqs.cu, seqs.n, seqs.tab)
   const bool packed = seqs.cu != nullptr;
   if (p_bf16) {
     if (packed) SLSTM_WARM_SCAN_LAUNCH(true, true);

@@ -93,6 +93,9 @@ hipError_t launch_outputs(const float* S, float* h, float* final_state, int B, i
                           const Control* ctl, hipStream_t stream, const float* state0 = nullptr,
                           Seqs seqs = {});
 hipError_t launch_zero(float* p, i64 n_floats, hipStream_t stream);
+// the sequence table of packed offsets (seq_table_ints(T) ints; see kSeqTabShift)
+size_t seq_table_ints(int T);
+hipError_t launch_seq_table(const int* cu, int n_seqs, int T, int* tab, hipStream_t stream);
 
 hipError_t launch_sequential(const void* P, bool p_bf16, const float* R, const float* state0,
                              float* S, float* h_out, float* final_state, int B, int T, int d,
