@@ -617,3 +617,144 @@ def input_projection_backward(x, W, dP):
 def hidden(S):
     """The hidden slot (B, T, d_h) of a state tensor (hidden slot 3)."""
     return np.asarray(S)[..., H, :]
+
+
+# ---------------------------------------------------------------------------------------
+# head mixing (mix='head'): block-diagonal recurrent matrices, one block per head and gate
+# ---------------------------------------------------------------------------------------
+# "sLSTM in this library", section "Cell" (mix table, row 'head'): R of shape
+# (4, n_heads, d_head, d_head), n_heads dividing d_h; the paper's sLSTM (summary card, "Method"
+# item 2 and the one-head step pseudocode under "Key equations") mixes memory through
+# recurrent matrices from the previous hidden state to every gate pre-activation, block-diagonal
+# with one block per head, so no mixing across heads. Feature j = a d_head + i is unit i of head
+# a; its pre-activation for gate g is p[g, j] + sum_k R[g, a, i, k] h'[a d_head + k] (R_g h' with
+# the row for unit i). Everything after the pre-activations is the channelwise cell: this
+# section calls ``cell`` with the full pre-activation as input and a zero channelwise weight.
+# The dense (4 d_head) x (4 d_head) Jacobian per head is assembled here (the dense-J oracle the
+# pages keep for this mode); state vectors of a head are ordered unit-major, index 4 i + slot.
+
+def head_recurrent(h, R):
+    """R_g h' per gate: h (..., d), R (4, n_heads, d_head, d_head) -> (..., 4, d) with
+    [..., g, a d_head + i] = sum_k R[g, a, i, k] h[..., a d_head + k]."""
+    R = np.asarray(R, dtype=np.float64)
+    _, nh, dh, _ = R.shape
+    hh = np.asarray(h, dtype=np.float64).reshape(h.shape[:-1] + (nh, dh))
+    y = np.einsum("gaik,...ak->...gai", R, hh)
+    return y.reshape(h.shape[:-1] + (4, nh * dh))
+
+
+def _head_shape(R, d):
+    R = np.asarray(R, dtype=np.float64)
+    if R.ndim != 4 or R.shape[0] != 4 or R.shape[2] != R.shape[3] or R.shape[1] * R.shape[2] != d:
+        raise ValueError(f"head-mixing R must be (4, n_heads, d_head, d_head) with n_heads * d_head = {d}")
+    return R, R.shape[1], R.shape[2]
+
+
+def head_vectors(X, nh):
+    """(..., 4, d) -> (..., nh, 4 dh) with index 4 i + slot for unit i of each head."""
+    d = X.shape[-1]
+    dh = d // nh
+    Y = np.moveaxis(X, -2, -1)                   # (..., d, 4)
+    return Y.reshape(X.shape[:-2] + (nh, dh * 4))
+
+
+def from_head_vectors(Y, nh):
+    """Inverse of head_vectors: (..., nh, 4 dh) -> (..., 4, d)."""
+    dh = Y.shape[-1] // 4
+    X = Y.reshape(Y.shape[:-2] + (nh * dh, 4))
+    return np.moveaxis(X, -1, -2)
+
+
+def cell_head(prev, p, R, forget, with_jacobian=False):
+    """One sLSTM step under head mixing.
+
+    prev, p (..., 4, d); R (4, n_heads, d_head, d_head). Returns the next state (..., 4, d)
+    and, if asked, the dense Jacobian J (..., n_heads, 4 d_head, 4 d_head) of the next state of
+    each head with respect to that head's previous state (unit-major ordering):
+      J[(i, slot), (i, col)] = d next[slot, i] / d prev[col, i] through the unit's own c', n', m'
+      J[(i, slot), (k, h)]  += sum_g G[slot, g, i] R[g, a, i, k]   (h' enters every gate of the
+    head), with G = d next / d x~ the gate Jacobian of the step.
+    """
+    p = np.asarray(p, dtype=np.float64)
+    d = p.shape[-1]
+    R, nh, dh = _head_shape(R, d)
+    pre = p + head_recurrent(prev[..., H, :], R)
+    zero_r = np.zeros((4, d))
+    if not with_jacobian:
+        return cell(prev, pre, zero_r, forget)
+    nxt, A0 = cell(prev, pre, zero_r, forget, with_jacobian=True)  # zero h' column
+    G = gate_jacobian(prev, pre, zero_r, forget)                     # (..., slot, gate, d)
+    lead = p.shape[:-2]
+    J = np.zeros(lead + (nh, dh, 4, dh, 4))
+    A0h = A0.reshape(lead + (4, 4, nh, dh))      # slot, col, a, i
+    Gh = G.reshape(lead + (4, 4, nh, dh))        # slot, gate, a, i
+    # own columns: unit i's next state from its own previous state
+    for i in range(dh):
+        J[..., :, i, :, i, :] = np.moveaxis(A0h[..., i], (-3, -2, -1), (-2, -1, -3))
+    # h' columns: sum over gates of G[slot, gate] R[gate, a, i, k]
+    J[..., :, :, :, :, H] += np.einsum("...sgai,gaik->...aisk", Gh, R)
+    return nxt, J.reshape(lead + (nh, 4 * dh, 4 * dh))
+
+
+def sequential_head(P, R, state0, forget):
+    """s_t = f(s_{t-1}) under head mixing, t = 1..T, from state0 (zeros when None)."""
+    P = np.asarray(P, dtype=np.float64)
+    B, T, _, d = P.shape
+    S = np.empty((B, T, 4, d))
+    prev = _state0(state0, B, d)
+    with np.errstate(all="ignore"):
+        for t in range(T):
+            prev = cell_head(prev, P[:, t], R, forget)
+            S[:, t] = prev
+    return S
+
+
+def residual_head(S, P, R, state0, forget, with_jacobian=True):
+    """F_t = s_t - f(s_{t-1}) and the dense per-head Jacobians J_t, t = 1..T."""
+    prev = _shifted(S, state0)
+    if with_jacobian:
+        fs, J = cell_head(prev, P, R, forget, with_jacobian=True)
+        return S - fs, J
+    return S - cell_head(prev, P, R, forget), None
+
+
+def forward_substitution_head(J, rhs, nh):
+    """x_1 = rhs_1, x_t = J_t x_{t-1} + rhs_t with dense per-head blocks (J_1 unused).
+    J (B, T, nh, 4 dh, 4 dh), rhs (B, T, 4, d) -> x (B, T, 4, d)."""
+    r = head_vectors(rhs, nh)
+    x = np.empty_like(r)
+    x[:, 0] = r[:, 0]
+    for t in range(1, r.shape[1]):
+        x[:, t] = np.einsum("bauv,bav->bau", J[:, t], x[:, t - 1]) + r[:, t]
+    return from_head_vectors(x, nh)
+
+
+def newton_head(P, R, state0, forget, max_iters, tol=0.0, init=INIT_WARM):
+    """Newton solve under head mixing: the steps of ``newton`` with the dense per-head
+    Jacobians (the warm start drops R h' and is the channelwise one)."""
+    P = np.asarray(P, dtype=np.float64)
+    B, T, _, d = P.shape
+    R, nh, _ = _head_shape(R, d)
+    if init == INIT_WARM:
+        S = warm_start(P, state0, forget)
+    elif init == INIT_ZERO:
+        S = np.zeros((B, T, 4, d))
+    else:
+        raise ValueError(f"unknown init {init!r}")
+    stats = NewtonStats()
+    with np.errstate(all="ignore"):
+        stopped = False
+        for _ in range(max_iters):
+            F, J = residual_head(S, P, R, state0, forget)
+            e = max_abs(F)
+            stats.max_abs_F.append(e)
+            stopped = tol > 0.0 and e < tol  # the stop rule of ``newton``
+            if stopped:
+                break
+            S = S + forward_substitution_head(J, -F, nh)
+            stats.iters += 1
+        if not stopped:
+            F, _ = residual_head(S, P, R, state0, forget, with_jacobian=False)
+            stats.max_abs_F.append(max_abs(F))
+    stats.converged, stats.diverged, stats.nonfinite = newton_flags(stats.max_abs_F[-1], tol)
+    return S, stats

@@ -553,4 +553,136 @@ def pin_gate_jacobian_h_column(ref):
         np.testing.assert_allclose(A[..., :, 3, :], np.einsum("btsgd,gd->btsd", G, R), rtol=1e-12, atol=1e-14)
 
 
+# ---- head mixing ("sLSTM in this library", "Cell": mix='head'; summary card "Method" item 2) ----
+def _head_problem(seed, B=2, T=7, nh=2, dh=3, forget="sigmoid"):
+    rng = np.random.default_rng(seed)
+    d = nh * dh
+    P = rng.standard_normal((B, T, 4, d))
+    P[:, :, 2] += 2.0
+    R = rng.uniform(-0.4, 0.4, (4, nh, dh, dh))
+    s0 = np.zeros((B, 4, d))
+    s0[:, 0] = rng.uniform(-0.5, 0.5, (B, d))
+    s0[:, 1] = rng.uniform(0.5, 2.0, (B, d))
+    s0[:, 2] = rng.uniform(-1.0, 1.0, (B, d))
+    s0[:, 3] = rng.uniform(-0.5, 0.5, (B, d))
+    return P, R, s0
+
+
+def pin_head_recurrent_worked_example(ref):
+    """R_g h' by hand for two heads of two units: row i of block (g, a) meets unit k of head a."""
+    R = np.zeros((4, 2, 2, 2))
+    R[0, 0, 0, 1] = 2.0    # gate z, head 0: unit 0 reads unit 1
+    R[2, 1, 1, 0] = -1.0   # gate f, head 1: unit 1 reads unit 0 (feature 2)
+    h = np.array([0.5, 3.0, 7.0, 11.0])
+    y = ref.head_recurrent(h, R)
+    want = np.zeros((4, 4))
+    want[0, 0] = 6.0
+    want[2, 3] = -7.0
+    np.testing.assert_array_equal(y, want)
+
+
+def pin_head_width_one_is_channelwise(ref):
+    """d_head = 1: block (g, j) is the channelwise weight r[g, j]; the step, its Jacobian and the
+    Newton solve are the channelwise ones."""
+    rng = np.random.default_rng(91)
+    B, T, d = 2, 6, 5
+    P = rng.standard_normal((B, T, 4, d))
+    P[:, :, 2] += 2.0
+    r = rng.uniform(-0.5, 0.5, (4, d))
+    Rh = r.reshape(4, d, 1, 1).copy()
+    np.testing.assert_array_equal(ref.sequential_head(P, Rh, None, "exp"), ref.sequential(P, r, None, "exp"))
+    S = ref.sequential(P, r, None, "exp")
+    _, A = ref.cell(S[:, 2], P[:, 3], r, "exp", with_jacobian=True)
+    _, J = ref.cell_head(S[:, 2], P[:, 3], Rh, "exp", with_jacobian=True)
+    np.testing.assert_allclose(J, np.moveaxis(A, -1, 1), rtol=1e-14, atol=1e-15)
+    Sd, _ = ref.newton(P, r, None, "exp", 3)
+    Sh, _ = ref.newton_head(P, Rh, None, "exp", 3)
+    np.testing.assert_allclose(Sh, Sd, rtol=1e-12, atol=1e-13)
+
+
+def pin_head_diagonal_blocks_are_channelwise(ref):
+    """Blocks that are diagonal (unit i reads only itself) give the channelwise recurrence."""
+    rng = np.random.default_rng(92)
+    B, T, nh, dh = 2, 6, 2, 3
+    d = nh * dh
+    P = rng.standard_normal((B, T, 4, d))
+    r = rng.uniform(-0.5, 0.5, (4, d))
+    R = np.zeros((4, nh, dh, dh))
+    for a in range(nh):
+        for i in range(dh):
+            R[:, a, i, i] = r[:, a * dh + i]
+    np.testing.assert_array_equal(ref.sequential_head(P, R, None, "sigmoid"), ref.sequential(P, r, None, "sigmoid"))
+
+
+def pin_head_jacobian_finite_differences(ref):
+    """Dense per-head Jacobian against central differences of the step, column by column; a
+    perturbation in one head leaves the other heads' next states unchanged."""
+    P, R, s0 = _head_problem(93)
+    B, T, _, d = P.shape
+    nh, dh = R.shape[1], R.shape[2]
+    S = ref.sequential_head(P, R, s0, "sigmoid")
+    prev, p = S[:, 2], P[:, 3]
+    _, J = ref.cell_head(prev, p, R, "sigmoid", with_jacobian=True)
+    eps = 1e-6
+    for col in range(4):
+        for j in range(d):
+            dp = np.zeros_like(prev)
+            dp[:, col, j] = eps
+            fd = (ref.cell_head(prev + dp, p, R, "sigmoid") - ref.cell_head(prev - dp, p, R, "sigmoid")) / (2 * eps)
+            a, k = divmod(j, dh)
+            got = J[:, a, :, 4 * k + col].reshape(B, dh, 4)
+            np.testing.assert_allclose(got, np.moveaxis(fd[:, :, a * dh:(a + 1) * dh], 1, 2), rtol=1e-6, atol=1e-8)
+            for o in range(nh):
+                if o != a:
+                    assert np.max(np.abs(fd[:, :, o * dh:(o + 1) * dh])) == 0.0
+
+
+def pin_head_newton_exact_at_k_equals_t(ref):
+    """From the zero iterate, T Newton steps give the sequential solution exactly (the first k
+    steps are exact after k iterations), and near the solution the residual falls
+    quadratically."""
+    P, R, s0 = _head_problem(94, T=5)
+    T = P.shape[1]
+    S, st = ref.newton_head(P, R, s0, "sigmoid", T, init=ref.INIT_ZERO)
+    np.testing.assert_allclose(S, ref.sequential_head(P, R, s0, "sigmoid"), rtol=1e-13, atol=1e-14)
+    _, st = ref.newton_head(P, R, s0, "sigmoid", 4)
+    e = st.max_abs_F
+    assert e[2] < 0.1 and e[3] < 4.0 * e[2] ** 2 and e[4] < 4.0 * e[3] ** 2 + 1e-14, e
+
+
+def pin_head_forward_substitution_vs_dense(ref):
+    """The block solve with dense per-head blocks against a LAPACK solve of the assembled
+    (T 4 d_head) system of one head."""
+    rng = np.random.default_rng(95)
+    B, T, nh, dh = 1, 5, 2, 2
+    J = rng.uniform(-0.5, 0.5, (B, T, nh, 4 * dh, 4 * dh))
+    rhs = rng.standard_normal((B, T, 4, nh * dh))
+    x = ref.forward_substitution_head(J, rhs, nh)
+    for a in range(nh):
+        n = 4 * dh
+        M = np.eye(T * n)
+        for t in range(1, T):
+            M[t * n:(t + 1) * n, (t - 1) * n:t * n] = -J[0, t, a]
+        rv = ref.head_vectors(rhs, nh)[0, :, a].reshape(-1)
+        want = np.linalg.solve(M, rv).reshape(T, n)
+        np.testing.assert_allclose(ref.head_vectors(x, nh)[0, :, a], want, rtol=1e-12, atol=1e-13)
+
+
+def pin_head_units_permute(ref):
+    """Renumbering the units of a head (columns of P and state0, rows and columns of its blocks)
+    renumbers the solution."""
+    P, R, s0 = _head_problem(96, T=6)
+    dh = R.shape[2]
+    perm = np.array([2, 0, 1])
+    full = np.concatenate([perm, dh + np.arange(dh)])      # permute head 0 only
+    Rp = R.copy()
+    Rp[:, 0] = R[:, 0][:, perm][:, :, perm]
+    S = ref.sequential_head(P, R, s0, "sigmoid")
+    Sp = ref.sequential_head(P[..., full], Rp, s0[..., full], "sigmoid")
+    np.testing.assert_allclose(Sp, S[..., full], rtol=1e-14, atol=1e-15)
+    Sn, _ = ref.newton_head(P, R, s0, "sigmoid", 2)
+    Snp, _ = ref.newton_head(P[..., full], Rp, s0[..., full], "sigmoid", 2)
+    np.testing.assert_allclose(Snp, Sn[..., full], rtol=1e-12, atol=1e-13)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

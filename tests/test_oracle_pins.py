@@ -61,6 +61,11 @@ MUTATIONS = [
      "dx = (dP2 @ W[::-1].reshape(g * d_h, d_in)).reshape(B, T, d_in)"),
     ("gate Jacobian: forget derivative", "dfg_df = fg * (dlf - dm_df)", "dfg_df = fg * (1.0 - dm_df)"),
     ("gate Jacobian: output-gate term", "dh[GO] = dh[GO] + (c / v[\"D\"]) * o * (1.0 - o)", "dh[GO] = dh[GO]"),
+    ("head mixing: transposed block", 'np.einsum("gaik,...ak->...gai", R, hh)', 'np.einsum("gaki,...ak->...gai", R, hh)'),
+    ("head Jacobian: transposed coupling", 'np.einsum("...sgai,gaik->...aisk", Gh, R)',
+     'np.einsum("...sgai,gaki->...aisk", Gh, R)'),
+    ("head solve: transposed block", 'np.einsum("bauv,bav->bau", J[:, t], x[:, t - 1])',
+     'np.einsum("bavu,bav->bau", J[:, t], x[:, t - 1])'),
 ]
 
 
