@@ -325,6 +325,37 @@ slstm_status slstm_backward_varlen(const void* P, slstm_dtype P_dtype, const flo
                                    void* stream);
 
 /*
+ * Head mixing ([SL] "Cell", the mix table's 'head' row; [XL] "Method" item 2 and the one-head
+ * step pseudocode: recurrent matrices from h' to every gate, block-diagonal with one block per
+ * head, no mixing across heads). R is (4, n_heads, d_head, d_head) float32, 16-byte aligned,
+ * n_heads * d_head = d_h, d_head one of 8, 16, 32, 64; unit i of head a (feature
+ * j = a d_head + i) has the pre-activations x~_g = P[.., g, j] + sum_k R[g, a, i, k] h'[a d_head + k].
+ * Every other argument is as for the channelwise calls (P, states, h_out, final_state, state0
+ * layouts, forget modes with the floored read-out flag, statuses, stream semantics).
+ *
+ * slstm_head_newton_forward: Newton as slstm_newton_forward (warm start with R h' dropped, the
+ * same stop rule, flags and stats), each iteration one kernel: one workgroup per (batch row,
+ * head) walks T, forms the residual at the iterate and solves the block-bidiagonal system with
+ * the Jacobian applied in factored form (the unit's own-state columns plus the gate Jacobian
+ * times R_g Delta h'), so no (4 d_head)^2 block is formed. The solve is a recurrence along T;
+ * parallelism comes from B * n_heads. Workspace: slstm_head_newton_workspace_bytes (0 if the
+ * sizes are invalid).
+ * slstm_head_sequential_forward: the step loop, one workgroup per (batch row, head); no
+ * workspace.
+ */
+size_t slstm_head_newton_workspace_bytes(int B, int T, int d_h, int n_heads);
+slstm_status slstm_head_newton_forward(const void* P, slstm_dtype P_dtype, const float* R,
+                                       const float* state0, float* states, float* h_out,
+                                       float* final_state, int B, int T, int d_h, int n_heads,
+                                       slstm_forget fmode, int max_iters, float tol, slstm_init init,
+                                       void* workspace, size_t workspace_bytes, void* stream,
+                                       slstm_newton_stats* stats);
+slstm_status slstm_head_sequential_forward(const void* P, slstm_dtype P_dtype, const float* R,
+                                           const float* state0, float* states, float* h_out,
+                                           float* final_state, int B, int T, int d_h, int n_heads,
+                                           slstm_forget fmode, void* stream);
+
+/*
  * Kernel timing with HIP events recorded on the launching stream around every kernel the
  * library launches, for measurement. Off by default; process-wide; not thread-safe.
  * slstm_profile_read waits for the recorded events and returns the summed duration (ms) and
@@ -343,7 +374,9 @@ typedef enum {
   SLSTM_KERNEL_BACKWARD = 9,     /* the adjoint and cell VJP pass of slstm_backward */
   SLSTM_KERNEL_WEIGHT_GRADIENT = 10, /* slstm_input_projection_backward's dW_x product */
   SLSTM_KERNEL_INPUT_GRADIENT = 11,  /* slstm_input_projection_backward's dx product */
-  SLSTM_KERNEL_KINDS = 12
+  SLSTM_KERNEL_HEAD_ITERATION = 12,  /* one Newton iteration under head mixing */
+  SLSTM_KERNEL_HEAD_SEQUENTIAL = 13, /* the sequential forward under head mixing */
+  SLSTM_KERNEL_KINDS = 14
 } slstm_kernel_kind;
 
 slstm_status slstm_profile_enable(int on);

@@ -569,6 +569,31 @@ slstm_status backward(const void* P, slstm_dtype P_dtype, const float* R, const 
   return SLSTM_OK;
 }
 
+// head mixing: control block, the warm start's look-back words, the second iterate buffer
+struct HeadLayout {
+  size_t ctl, desc, S2, total;
+};
+
+HeadLayout head_layout(int B, int T, int d) {
+  HeadLayout L;
+  L.ctl = 0;
+  L.desc = align_up(slstm::kControlBytes);
+  L.S2 = align_up(L.desc + slstm::warm_desc_words(B, T, d) * 8);
+  L.total = align_up(L.S2 + static_cast<size_t>(B) * T * 4 * d * sizeof(float));
+  return L;
+}
+
+bool head_shape_ok(int d, int n_heads) {
+  return n_heads >= 1 && d % n_heads == 0 && slstm::head_width_supported(d / n_heads);
+}
+
+slstm_status check_heads(int d, int n_heads, const float* R) {
+  if (!head_shape_ok(d, n_heads))
+    return fail(SLSTM_EINVAL, "n_heads (%d) must divide d_h (%d) into heads of 8, 16, 32 or 64 units", n_heads, d);
+  if (!aligned(R, 16)) return fail(SLSTM_EINVAL, "R must be 16-byte aligned");
+  return SLSTM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -830,6 +855,84 @@ slstm_status slstm_input_projection_backward(const void* x, const void* W_x, con
       return slstm::launch_gemm_bf16(A, WT, nullptr, dx, bt, d_in, static_cast<int>(L.k_4d), st, 1);
     }));
   }
+  return SLSTM_OK;
+}
+
+size_t slstm_head_newton_workspace_bytes(int B, int T, int d_h, int n_heads) {
+  if (check_dims(B, T, d_h) != SLSTM_OK || !head_shape_ok(d_h, n_heads)) return 0;
+  return head_layout(B, T, d_h).total;
+}
+
+slstm_status slstm_head_newton_forward(const void* P, slstm_dtype P_dtype, const float* R,
+                                       const float* state0, float* states, float* h_out,
+                                       float* final_state, int B, int T, int d_h, int n_heads,
+                                       slstm_forget fmode, int max_iters, float tol, slstm_init init,
+                                       void* workspace, size_t workspace_bytes, void* stream,
+                                       slstm_newton_stats* stats) {
+  g_err[0] = '\0';
+  slstm_status s = check_common(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, fmode);
+  if (s != SLSTM_OK) return s;
+  s = check_heads(d_h, n_heads, R);
+  if (s != SLSTM_OK) return s;
+  if (max_iters < 1 || max_iters > SLSTM_MAX_ITERS)
+    return fail(SLSTM_EINVAL, "max_iters must be in 1..%d (got %d)", SLSTM_MAX_ITERS, max_iters);
+  if (!(tol >= 0.0f) || std::isinf(tol)) return fail(SLSTM_EINVAL, "tol must be finite and >= 0");
+  if (init != SLSTM_INIT_WARM && init != SLSTM_INIT_ZERO) return fail(SLSTM_EINVAL, "unknown init %d", (int)init);
+  if (workspace == nullptr || !aligned(workspace, kAlign))
+    return fail(SLSTM_EINVAL, "workspace must be non-NULL and 256-byte aligned");
+  const HeadLayout L = head_layout(B, T, d_h);
+  if (workspace_bytes < L.total)
+    return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool bf16 = P_dtype == SLSTM_BF16;
+  const int cm = cell_mode_of(fmode);
+  Control* ctl = at<Control>(workspace, L.ctl);
+  auto* desc = at<unsigned long long>(workspace, L.desc);
+  const i64 n_state = static_cast<i64>(B) * T * 4 * d_h;
+  HIP_TRY(slstm::launch_init_control(ctl, st));
+  // iterate k lives in buf[k % 2], arranged so that iterate max_iters lands in `states`
+  float* other = at<float>(workspace, L.S2);
+  float* buf[2] = {(max_iters % 2 == 0) ? states : other, (max_iters % 2 == 0) ? other : states};
+  if (init == SLSTM_INIT_WARM) {
+    HIP_TRY(launch_warm(P, bf16, state0, buf[0], B, T, d_h, cm, false, desc, ctl, st, {}));
+  } else {
+    HIP_TRY(slstm::launch_zero(buf[0], n_state, st));
+  }
+  for (int k = 0; k < max_iters; ++k) {
+    const bool last = k + 1 == max_iters;
+    HIP_TRY(timed(SLSTM_KERNEL_HEAD_ITERATION, st, [&] {
+      return slstm::launch_head_iteration(P, bf16, R, state0, buf[k % 2], buf[(k + 1) % 2], last ? h_out : nullptr,
+                                          B, T, d_h, n_heads, cm, ctl, k, tol, last, st);
+    }));
+  }
+  // the last launch formed the final residual and h; what remains of the stop rule is the check
+  // of the iterate before it
+  HIP_TRY(slstm::launch_settle(ctl, max_iters - 1, tol, st));
+  HIP_TRY(slstm::launch_select_iterate(ctl, buf[0], buf[1], states, n_state, st));
+  HIP_TRY(slstm::launch_finalize(ctl, tol, st));
+  if (h_out != nullptr || final_state != nullptr)
+    HIP_TRY(slstm::launch_outputs(states, h_out, final_state, B, T, d_h, ctl, st));
+  if (stats == nullptr) return SLSTM_OK;
+  Control host;
+  HIP_TRY(hipMemcpyAsync(&host, ctl, sizeof(Control), hipMemcpyDeviceToHost, st));
+  HIP_TRY(hipStreamSynchronize(st));
+  return stats_from_control(host, stats);
+}
+
+slstm_status slstm_head_sequential_forward(const void* P, slstm_dtype P_dtype, const float* R,
+                                           const float* state0, float* states, float* h_out,
+                                           float* final_state, int B, int T, int d_h, int n_heads,
+                                           slstm_forget fmode, void* stream) {
+  g_err[0] = '\0';
+  slstm_status s = check_common(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, fmode);
+  if (s != SLSTM_OK) return s;
+  s = check_heads(d_h, n_heads, R);
+  if (s != SLSTM_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HIP_TRY(timed(SLSTM_KERNEL_HEAD_SEQUENTIAL, st, [&] {
+    return slstm::launch_head_sequential(P, P_dtype == SLSTM_BF16, R, state0, states, h_out, final_state, B, T,
+                                         d_h, n_heads, cell_mode_of(fmode), st);
+  }));
   return SLSTM_OK;
 }
 

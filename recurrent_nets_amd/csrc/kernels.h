@@ -101,6 +101,17 @@ hipError_t launch_sequential(const void* P, bool p_bf16, const float* R, const f
                              float* S, float* h_out, float* final_state, int B, int T, int d,
                              int cell_mode, hipStream_t stream, Seqs seqs = {});
 
+// head mixing (R of shape (4, n_heads, d_head, d_head), d_head in {8, 16, 32, 64}): the
+// sequential forward, and one Newton iteration (residual of S_in, the factored block solve,
+// S_out; `last` also the residual of S_out, slot k_iter + 1, and h into h_out if not NULL)
+bool head_width_supported(int d_head);
+hipError_t launch_head_sequential(const void* P, bool p_bf16, const float* R, const float* state0, float* S,
+                                  float* h_out, float* final_state, int B, int T, int d, int n_heads,
+                                  int cell_mode, hipStream_t stream);
+hipError_t launch_head_iteration(const void* P, bool p_bf16, const float* R, const float* state0, const float* S_in,
+                                 float* S_out, float* h_out, int B, int T, int d, int n_heads, int cell_mode,
+                                 Control* ctl, int k_iter, float tol, bool last, hipStream_t stream);
+
 // C = X W^T (+ bias) in bf16 MFMA with float32 accumulation; X (M x K), W (N x K), both
 // K-contiguous. With splits > 1 the K range is split and split s writes its partial product to
 // C + s * M * N (bias must then be null); gemm_splits_for gives an accepted split count.

@@ -25,7 +25,8 @@ SCHEDULE = {"fused": 0, "layered": 1, "fused_scan": 2, "fused_chain": 3}
 MAX_ITERS = 64
 KERNELS = {"warm_start": 0, "residual_jacobian": 1, "scan_block4": 2, "update": 3,
            "final_residual": 4, "input_projection": 5, "sequential": 6, "newton_iteration": 7,
-           "newton_solve": 8, "backward": 9, "weight_gradient": 10, "input_gradient": 11}
+           "newton_solve": 8, "backward": 9, "weight_gradient": 10, "input_gradient": 11,
+           "head_iteration": 12, "head_sequential": 13}
 
 EXPORTED = [
     "slstm_status_string", "slstm_last_error", "slstm_newton_workspace_bytes",
@@ -36,7 +37,8 @@ EXPORTED = [
     "slstm_profile_durations", "slstm_backward_workspace_bytes", "slstm_backward",
     "slstm_input_projection_backward_workspace_bytes", "slstm_input_projection_backward",
     "slstm_newton_forward_varlen", "slstm_sequential_forward_varlen", "slstm_warm_start_varlen",
-    "slstm_backward_varlen",
+    "slstm_backward_varlen", "slstm_head_newton_workspace_bytes", "slstm_head_newton_forward",
+    "slstm_head_sequential_forward",
 ]
 
 
@@ -132,6 +134,13 @@ def load(path: str | None = None):
     L.slstm_backward_varlen.restype = _i
     L.slstm_backward_varlen.argtypes = [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp,
                                         _vp, _vp, _i, _i, _i, _i, _vp, _sz, _vp]
+    L.slstm_head_newton_workspace_bytes.restype = _sz
+    L.slstm_head_newton_workspace_bytes.argtypes = [_i, _i, _i, _i]
+    L.slstm_head_newton_forward.restype = _i
+    L.slstm_head_newton_forward.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i, _f, _i,
+                                            _vp, _sz, _vp, ctypes.POINTER(_Stats)]
+    L.slstm_head_sequential_forward.restype = _i
+    L.slstm_head_sequential_forward.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
     L.slstm_profile_enable.restype = _i
     L.slstm_profile_enable.argtypes = [_i]
     L.slstm_profile_reset.restype = _i
@@ -470,6 +479,79 @@ def backward(P, R, states, state0=None, g_states=None, g_h=None, g_final=None, f
     if dbias is not None:
         return dP, dR, dstate0, dbias
     return dP, dR, dstate0
+
+
+# ---- head mixing (R of shape (4, n_heads, d_head, d_head)) ----------------------------------
+def _head_check(P, R, state0):
+    if P.dim() != 4 or P.shape[2] != 4:
+        raise ValueError(f"P must be (B, T, 4, d_h), got {tuple(P.shape)}")
+    B, T, _, d = P.shape
+    if R.dim() != 4 or R.shape[0] != 4 or R.shape[2] != R.shape[3] or R.shape[1] * R.shape[2] != d:
+        raise ValueError(f"R must be (4, n_heads, d_head, d_head) with n_heads * d_head = {d}, got {tuple(R.shape)}")
+    _shape(state0, "state0", (B, 4, d))
+    return B, T, d, int(R.shape[1])
+
+
+def head_newton_workspace_bytes(B: int, T: int, d_h: int, n_heads: int) -> int:
+    return int(load().slstm_head_newton_workspace_bytes(B, T, d_h, n_heads))
+
+
+def head_newton_forward(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, init="warm",
+                        states=None, h_out=None, want_hidden=True, final_state=None, workspace=None,
+                        stream=None, stats=True, raise_on_divergence=True, readout="exact"):
+    """Newton-parallel forward under head mixing (block-diagonal R, one block per head and
+    gate). Arguments and returns as newton_forward; R (4, n_heads, d_head, d_head) float32 with
+    d_head in {8, 16, 32, 64}."""
+    L = load()
+    _dev(P, "P", (torch.float32, torch.bfloat16))
+    _dev(R, "R", (torch.float32,))
+    _dev(state0, "state0", (torch.float32,))
+    B, T, d, nh = _head_check(P, R, state0)
+    if states is None:
+        states = torch.empty((B, T, 4, d), dtype=torch.float32, device=P.device)
+    if want_hidden and h_out is None:
+        h_out = torch.empty((B, T, d), dtype=torch.float32, device=P.device)
+    _dev(states, "states", (torch.float32,))
+    _dev(h_out, "h_out", (torch.float32,))
+    _dev(final_state, "final_state", (torch.float32,))
+    _shape(final_state, "final_state", (B, 4, d))
+    if workspace is None:
+        workspace = alloc_workspace(L.slstm_head_newton_workspace_bytes(B, T, d, nh), P.device)
+    st = _Stats() if stats else None
+    status = L.slstm_head_newton_forward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states), _ptr(h_out),
+                                         _ptr(final_state), B, T, d, nh, _fmode(forget, readout), int(max_iters),
+                                         float(tol), INIT[init], _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _stream(stream),
+                                         ctypes.byref(st) if st is not None else None)
+    _check(status, "slstm_head_newton_forward")
+    out_stats = NewtonStats._from(st, status) if st is not None else None
+    if raise_on_divergence and status in (DIVERGED, NONFINITE):
+        raise NewtonDivergenceError(
+            f"{L.slstm_status_string(status).decode()} (max|F| = {out_stats.max_abs_F[-1]:.3g})")
+    return states, h_out, out_stats
+
+
+def head_sequential_forward(P, R, state0=None, forget="exp", states=None, h_out=None, want_hidden=True,
+                            final_state=None, stream=None, readout="exact"):
+    """Step-by-step forward under head mixing (also the T=1 decode step). Returns (states, h)."""
+    L = load()
+    _dev(P, "P", (torch.float32, torch.bfloat16))
+    _dev(R, "R", (torch.float32,))
+    _dev(state0, "state0", (torch.float32,))
+    B, T, d, nh = _head_check(P, R, state0)
+    if states is None:
+        states = torch.empty((B, T, 4, d), dtype=torch.float32, device=P.device)
+    if want_hidden and h_out is None:
+        h_out = torch.empty((B, T, d), dtype=torch.float32, device=P.device)
+    _dev(states, "states", (torch.float32,))
+    _dev(h_out, "h_out", (torch.float32,))
+    _dev(final_state, "final_state", (torch.float32,))
+    _shape(final_state, "final_state", (B, 4, d))
+    status = L.slstm_head_sequential_forward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
+                                             _ptr(h_out), _ptr(final_state), B, T, d, nh, _fmode(forget, readout),
+                                             _stream(stream))
+    _check(status, "slstm_head_sequential_forward")
+    return states, h_out
 
 
 def input_projection_backward_workspace_bytes(B: int, T: int, d_in: int, d_h: int) -> int:

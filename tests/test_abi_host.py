@@ -204,3 +204,28 @@ def test_binding_checks_offsets():
             slstm._seqs(bad, P)
     with pytest.raises(ValueError):
         slstm._seqs([0, 5, 10], torch.zeros((2, 10, 4, 3)))
+
+
+def test_head_argument_checks(lib):
+    # head mixing: n_heads must split d_h into heads of 8, 16, 32 or 64 units; R 16-byte aligned
+    assert lib.slstm_head_newton_workspace_bytes(2, 64, 64, 2) > 0
+    for nh in (0, 3, 64, 128):
+        assert lib.slstm_head_newton_workspace_bytes(2, 64, 64, nh) == 0
+    args = dict(P=ctypes.c_void_p(256), dt=0, R=ctypes.c_void_p(256), s0=None, S=ctypes.c_void_p(256), h=None,
+                fin=None, B=2, T=64, d=64, nh=2, fm=0, K=3, tol=0.0, init=0, ws=ctypes.c_void_p(4096),
+                wsb=1 << 30, stream=None, stats=None)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return lib.slstm_head_newton_forward(*a.values())
+    assert call(nh=3) == slstm.EINVAL
+    assert "heads" in lib.slstm_last_error().decode()
+    assert call(nh=16) == slstm.EINVAL            # d_head = 4
+    assert call(R=ctypes.c_void_p(260)) == slstm.EINVAL
+    assert call(K=0) == slstm.EINVAL
+    assert call(wsb=100) == slstm.EWORKSPACE
+    assert call(ws=None) == slstm.EINVAL
+    s = lib.slstm_head_sequential_forward(ctypes.c_void_p(256), 0, ctypes.c_void_p(256), None, ctypes.c_void_p(256),
+                                          None, None, 2, 64, 64, 5, 0, None)
+    assert s == slstm.EINVAL

@@ -9,6 +9,7 @@ from .gen import (  # noqa: F401
     draw_layer_inputs,
     draw_preactivation_inputs,
     draw_decode_inputs,
+    draw_head_inputs,
     packed_offsets,
     random_cotangents,
     random_cotangents_device,

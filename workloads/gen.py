@@ -146,3 +146,26 @@ def packed_offsets(seed: int, total: int, max_len: int, share_empty: float = 0.0
         lengths.append(n)
         left -= n
     return np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+
+
+def draw_head_inputs(seed: int, B: int, T: int, d: int, n_heads: int, p_dtype: str = "f32",
+                     forget_bias: float = 3.0, with_state0: bool = False):
+    """Inputs for head mixing: P (B, T, 4, d) ~ N(0, 1) with the forget-gate row shifted by
+    ``forget_bias`` (the marginal law of x W^T + bias for x ~ N(0, 1), W ~ N(0, 1/d_in)), in
+    float32 or bf16; R (4, n_heads, d_head, d_head) ~ U(-0.5, 0.5) / sqrt(d_head), so that
+    R_g h' has the spread of the channelwise U(-0.5, 0.5) h'; optionally a plausible state0
+    (B, 4, d). Returns float32 torch tensors on the CPU (P in bf16 for p_dtype "bf16")."""
+    dh = d // n_heads
+    rng = np.random.Generator(np.random.PCG64(seed))
+    P = rng.standard_normal((B, T, 4, d))
+    P[:, :, 2] += forget_bias
+    R = rng.uniform(-0.5, 0.5, (4, n_heads, dh, dh)) / np.sqrt(dh)
+    s0 = None
+    if with_state0:
+        s0 = np.stack([rng.uniform(-0.5, 0.5, (B, d)), rng.uniform(0.5, 2.0, (B, d)),
+                       rng.uniform(-2.0, 2.0, (B, d)), rng.uniform(-0.9, 0.9, (B, d))], axis=1)
+        s0 = torch.from_numpy(s0.astype(np.float32))
+    Pt = torch.from_numpy(P.astype(np.float32))
+    if p_dtype == "bf16":
+        Pt = Pt.to(torch.bfloat16)
+    return dict(P=Pt, R=torch.from_numpy(R.astype(np.float32)), state0=s0)
