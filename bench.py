@@ -9,7 +9,8 @@ full-layer workload (B=128, T=2048, d_in=d_h=1024, bf16 x and W_x):
 For workloads whose solver input is P the step is the Newton forward alone. The Newton
 forward runs in the schedule the library picks for the shape (--schedule fused); the scan
 form of the fused iteration, the layered schedule, the backward pass, the same tokens packed
-as ragged sequences (cu_seqlens) and the sequential forward are timed after it as context.
+as ragged sequences (cu_seqlens), head mixing (block-diagonal R, its own seeded input) and
+the sequential forward are timed after it as context.
 
 Prints ONE JSON line on stdout. Timing: W untimed warm-up steps, then exactly K steps
 between two device synchronisations, wall clock. Per-kernel durations come from HIP events
@@ -84,6 +85,21 @@ def kernel_work(w, n_e, p_bytes):
                          "flops": n_e * solve_flops_per_elem(w.max_iters, w.forget == "sigmoid")},
         "backward": {"bound": "hbm", "bytes": n_e * (p_bytes + 16 + 4 + 8)},                  # P, S, dL/dh in; bf16 dP out
     }
+
+
+# Head mixing (block-diagonal R, 32 heads of 32 units) at the size of the sigmoid workload's
+# batch and width: a context line, not the metric.
+HEAD = dict(B=16, T=4096, d=1024, n_heads=32, forget="exp", K=3, seed=20265)
+
+
+def head_iter_flops_per_elem(d_head, sigmoid_forget):
+    """Floating-point operations of one state element (b, t, j) in one head-mixing Newton
+    iteration as the kernel forms them: the block products R_g h' and R_g Delta h' for the four
+    gates (2 x 4 x d_head FMAs), the cell step 34 and its own-state and gate Jacobians 31, the
+    residual and its maximum 8, the factored solve (3 own-state and 4 gate FMAs per slot) 56 and
+    the update 4; the sigmoid forget gate adds 6 and 5 as in solve_flops_per_elem."""
+    sig = 1 if sigmoid_forget else 0
+    return 16 * d_head + (34 + 6 * sig) + (31 + 5 * sig) + 8 + 56 + 4
 
 
 def source_sha(paths):
@@ -195,6 +211,66 @@ def cpu_baseline(w, host, lanes_wanted):
 
 
 # ---------------------------------------------------------------------------------------
+def head_context(slstm, torch, dev, steps):
+    """Head mixing: the Newton solve (warm start, K iterations of the per-head kernel) and the
+    per-head sequential forward on one seeded input, timed like the main step."""
+    from workloads import draw_head_inputs
+    B, T, d, nh, K = HEAD["B"], HEAD["T"], HEAD["d"], HEAD["n_heads"], HEAD["K"]
+    dh = d // nh
+    inp = draw_head_inputs(HEAD["seed"], B, T, d, nh)
+    P, R = inp["P"].to(dev), inp["R"].to(dev)
+    S = torch.empty((B, T, 4, d), dtype=torch.float32, device=dev)
+    H = torch.empty((B, T, d), dtype=torch.float32, device=dev)
+    ws = slstm.alloc_workspace(slstm.head_newton_workspace_bytes(B, T, d, nh), dev)
+
+    def solve():
+        slstm.head_newton_forward(P, R, None, HEAD["forget"], K, 0.0, "warm", states=S, h_out=H, workspace=ws,
+                                  stats=False)
+
+    solve()
+    torch.cuda.synchronize()
+    st = slstm.read_stats(ws)
+    reps = max(3, steps // 2)
+    slstm.profile_reset()
+    slstm.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        solve()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / reps
+    for _ in range(reps):
+        slstm.head_sequential_forward(P, R, None, HEAD["forget"], states=S, h_out=H)
+    torch.cuda.synchronize()
+    slstm.profile_enable(False)
+    it = slstm.profile_durations("head_iteration")
+    sq = slstm.profile_durations("head_sequential")
+    wm = slstm.profile_durations("warm_start")
+    it_ms, sq_ms = sum(it) / len(it), sum(sq) / len(sq)
+    n_e = B * T * d
+    it_bytes = n_e * (16 + 16 + 16)           # P, S_k in; S_k+1 out
+    it_flops = n_e * head_iter_flops_per_elem(dh, HEAD["forget"] == "sigmoid")
+    gbs, tfs = it_bytes / (it_ms * 1e-3) / 1e9, it_flops / (it_ms * 1e-3) / 1e12
+    log(f"[bench] head mixing ({nh} heads of {dh}): solve {ms:.3f} ms, iteration kernel {it_ms:.3f} ms "
+        f"({it_ms * 1e3 / T:.3f} us per step), sequential {sq_ms:.3f} ms")
+    del ws, S, H, P, R
+    torch.cuda.empty_cache()
+    return {
+        "B": B, "T": T, "d_h": d, "n_heads": nh, "d_head": dh, "forget_gate": HEAD["forget"], "newton_iters": K,
+        "preactivations": "f32", "solve_ms": round(ms, 4), "state_elems_per_s": n_e / (ms * 1e-3),
+        "solver": {"iters": st.iters, "max_abs_F": st.max_abs_F[-1], "diverged": st.diverged},
+        "kernels": {"warm_start": {"avg_ms": round(sum(wm) / len(wm), 4)},
+                    "head_iteration": {"avg_ms": round(it_ms, 4), "us_per_step": round(it_ms * 1e3 / T, 4),
+                                       "bytes_per_launch": it_bytes, "flops_per_launch": it_flops},
+                    "head_sequential": {"avg_ms": round(sq_ms, 4), "us_per_step": round(sq_ms * 1e3 / T, 4),
+                                        "state_elems_per_s": n_e / (sq_ms * 1e-3)}},
+        "roofline": {"bound": "latency", "kernel": "head_iteration",
+                     "note": "one workgroup per (batch row, head) walks T; a step's chain bounds it",
+                     "hbm_view": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(gbs / HBM_PEAK_GBS, 4)},
+                     "alu_view": {"achieved": round(tfs, 2), "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(tfs / FP32_VECTOR_PEAK_TFLOPS, 4)}}}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -213,6 +289,8 @@ def main():
                     help="skip the context run of the backward pass at the forward solution")
     ap.add_argument("--no-packed-context", action="store_true",
                     help="skip the context run on the same tokens packed as ragged sequences")
+    ap.add_argument("--no-head-context", action="store_true",
+                    help="skip the context run of head mixing (block-diagonal R)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -530,6 +608,9 @@ def main():
                                       "frac": round(pb_gbs / HBM_PEAK_GBS, 4)}}}
         del pws, pbws, dPp, dRp, d0p, g_hp, g_fp, fin
         torch.cuda.empty_cache()
+
+    if not args.no_head_context:
+        context["head"] = head_context(slstm, torch, dev, args.steps)
 
     if not args.no_sequential_context:
         # the lane-parallel sequential forward on the same P, for context (not the metric)

@@ -62,6 +62,19 @@ __device__ __forceinline__ void load_block_row(const float* __restrict__ R, int 
   }
 }
 
+// v[g] for the lane's gate g = 2 g1 + g0 (the bits held as loop-invariant lane masks): three
+// selects, where indexing a register array by g would select among every element
+struct GateSel {
+  bool g0, g1;
+  __device__ __forceinline__ explicit GateSel(int g) : g0((g & 1) != 0), g1((g & 2) != 0) {}
+  __device__ __forceinline__ float operator()(float v0, float v1, float v2, float v3) const {
+    const float lo = g0 ? v1 : v0;
+    const float hi = g0 ? v3 : v2;
+    return g1 ? hi : lo;
+  }
+  __device__ __forceinline__ float operator()(const float v[4]) const { return (*this)(v[0], v[1], v[2], v[3]); }
+};
+
 template <int DH>
 __device__ __forceinline__ float block_dot(const float row[DH], const float* __restrict__ v) {
   const float4* v4 = reinterpret_cast<const float4*>(v);
@@ -90,41 +103,51 @@ __global__ __launch_bounds__(4 * DH) void head_seq_kernel(const void* __restrict
   const int a = blockIdx.x, b = blockIdx.y;
   const int j = a * DH + i;
   const i64 dd = d;
+  const GateSel sel(g);
   float row[DH];
   load_block_row<DH>(R, nh, a, i, g, row);
   // previous state of the unit, slot g in this lane
   float prev = state0 != nullptr ? state0[(static_cast<i64>(b) * 4 + g) * dd + j] : 0.0f;
   if (g == 3) hbuf[0][i] = prev;
   const i64 base = static_cast<i64>(b) * T * 4 * dd + g * dd + j;  // (b, t = 0, slot/gate g, j)
+  // ring of the next kHeadPrefetch steps' pre-activations; loads past the end re-read step T-1
   float pr[kHeadPrefetch];
 #pragma unroll
-  for (int u = 0; u < kHeadPrefetch; ++u) pr[u] = u < T ? load_p<BF16>(P, base + u * 4 * dd) : 0.0f;
+  for (int u = 0; u < kHeadPrefetch; ++u) pr[u] = load_p<BF16>(P, base + static_cast<i64>(min(u, T - 1)) * 4 * dd);
   head_lds_barrier();
-  for (int t0 = 0; t0 < T; t0 += kHeadPrefetch) {
+  auto step = [&](int t, float p) {
+    const float x = p + block_dot<DH>(row, hbuf[t & 1]);
+    float xs[4], ps[4];
+    quad_gather(x, xs);
+    quad_gather(prev, ps);
+    float s[4], A[16];
+    cell_step<false>(CellIn{ps[0], ps[1], ps[2], 0.0f}, xs[0], xs[1], xs[2], xs[3], 0.0f, 0.0f, 0.0f, 0.0f, sig,
+                     floored, s, A);
+    const float v = sel(s);
+    S[base + static_cast<i64>(t) * 4 * dd] = v;
+    if (g == 3) {
+      hbuf[(t + 1) & 1][i] = v;
+      if (h_out != nullptr) h_out[(static_cast<i64>(b) * T + t) * dd + j] = v;
+    }
+    prev = v;
+    head_lds_barrier();
+  };
+  // whole blocks of kHeadPrefetch steps: every ring slot is refilled unconditionally, so no
+  // load has to complete before the step kHeadPrefetch later that reads it
+  int t0 = 0;
+  for (; t0 + kHeadPrefetch <= T; t0 += kHeadPrefetch) {
 #pragma unroll
     for (int u = 0; u < kHeadPrefetch; ++u) {
       const int t = t0 + u;
-      if (t < T) {
-        const float p = pr[u];
-        if (t + kHeadPrefetch < T) pr[u] = load_p<BF16>(P, base + static_cast<i64>(t + kHeadPrefetch) * 4 * dd);
-        const float x = p + block_dot<DH>(row, hbuf[t & 1]);
-        float xs[4], ps[4];
-        quad_gather(x, xs);
-        quad_gather(prev, ps);
-        float s[4], A[16];
-        cell_step<false>(CellIn{ps[0], ps[1], ps[2], 0.0f}, xs[0], xs[1], xs[2], xs[3], 0.0f, 0.0f, 0.0f, 0.0f, sig,
-                         floored, s, A);
-        const float v = g == 0 ? s[0] : (g == 1 ? s[1] : (g == 2 ? s[2] : s[3]));
-        S[base + static_cast<i64>(t) * 4 * dd] = v;
-        if (g == 3) {
-          hbuf[(t + 1) & 1][i] = v;
-          if (h_out != nullptr) h_out[(static_cast<i64>(b) * T + t) * dd + j] = v;
-        }
-        prev = v;
-        head_lds_barrier();
-      }
+      const float p = pr[u];
+      pr[u] = load_p<BF16>(P, base + static_cast<i64>(min(t + kHeadPrefetch, T - 1)) * 4 * dd);
+      step(t, p);
     }
   }
+  // the last T mod kHeadPrefetch steps, whose operands are in the ring
+#pragma unroll
+  for (int u = 0; u < kHeadPrefetch - 1; ++u)
+    if (t0 + u < T) step(t0 + u, pr[u]);
   if (final_state != nullptr) final_state[(static_cast<i64>(b) * 4 + g) * dd + j] = prev;
 }
 
@@ -172,6 +195,7 @@ __global__ __launch_bounds__(4 * DH) void head_iter_kernel(const void* __restric
     s_err[0] = 0u;
     s_err[1] = 0u;
   }
+  const GateSel sel(g);
   float row[DH];
   load_block_row<DH>(R, nh, a, i, g, row);
   float prev = state0 != nullptr ? state0[(static_cast<i64>(b) * 4 + g) * dd + j] : 0.0f;  // iterate at t-1
@@ -181,65 +205,74 @@ __global__ __launch_bounds__(4 * DH) void head_iter_kernel(const void* __restric
     dhbuf[0][i] = 0.0f;
   }
   const i64 base = static_cast<i64>(b) * T * 4 * dd + g * dd + j;
+  // rings of the next kHeadPrefetch steps' operands; loads past the end re-read step T-1
   float pr[kHeadPrefetch], sr[kHeadPrefetch];
 #pragma unroll
   for (int u = 0; u < kHeadPrefetch; ++u) {
-    pr[u] = u < T ? load_p<BF16>(P, base + u * 4 * dd) : 0.0f;
-    sr[u] = u < T ? S_in[base + u * 4 * dd] : 0.0f;
+    const i64 off = base + static_cast<i64>(min(u, T - 1)) * 4 * dd;
+    pr[u] = load_p<BF16>(P, off);
+    sr[u] = S_in[off];
   }
   unsigned int emax = 0u, emax_new = 0u;
   head_lds_barrier();
-  for (int t0 = 0; t0 < T; t0 += kHeadPrefetch) {
+  auto step = [&](int t, float p, float sin) {
+    // residual and factors at the iterate (independent of the solve)
+    const float x = p + block_dot<DH>(row, hbuf[t & 1]);
+    float xs[4], ps[4];
+    quad_gather(x, xs);
+    quad_gather(prev, ps);
+    float s[4], A[16], G[16];
+    cell_step_gates(CellIn{ps[0], ps[1], ps[2], 0.0f}, xs, sig, floored, s, A, G);
+    const float sg = sel(s);
+    const float F = sin - sg;
+    emax = res_max(emax, F);
+    // the solve: Delta_t = A_own Delta_{t-1} + G (R Delta h_{t-1}) - F
+    const float y = block_dot<DH>(row, dhbuf[t & 1]);
+    float ys[4], ds[4];
+    quad_gather(y, ys);
+    quad_gather(dprev, ds);
+    // row g of A_own and of G (rows are slots, 4 entries each)
+    float delta = sel(A[0], A[4], A[8], A[12]) * ds[0];
+    delta = fmaf(sel(A[1], A[5], A[9], A[13]), ds[1], delta);
+    delta = fmaf(sel(A[2], A[6], A[10], A[14]), ds[2], delta);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) delta = fmaf(sel(G[q], G[4 + q], G[8 + q], G[12 + q]), ys[q], delta);
+    delta -= F;
+    const float sout = sin + delta;
+    S_out[base + static_cast<i64>(t) * 4 * dd] = sout;
+    if constexpr (LAST) {
+      // residual of the new iterate: its pre-activations are x~ + R Delta h'
+      float sn[4], An[16];
+      cell_step<false>(CellIn{ps[0] + ds[0], ps[1] + ds[1], ps[2] + ds[2], 0.0f}, xs[0] + ys[0], xs[1] + ys[1],
+                       xs[2] + ys[2], xs[3] + ys[3], 0.0f, 0.0f, 0.0f, 0.0f, sig, floored, sn, An);
+      const float sng = sel(sn);
+      emax_new = res_max(emax_new, sout - sng);
+      if (g == 3 && h_out != nullptr) h_out[(static_cast<i64>(b) * T + t) * dd + j] = sout;
+    }
+    if (g == 3) {
+      hbuf[(t + 1) & 1][i] = sin;
+      dhbuf[(t + 1) & 1][i] = delta;
+    }
+    prev = sin;
+    dprev = delta;
+    head_lds_barrier();
+  };
+  // whole blocks of kHeadPrefetch steps with unconditional ring refills (see head_seq_kernel)
+  int t0 = 0;
+  for (; t0 + kHeadPrefetch <= T; t0 += kHeadPrefetch) {
 #pragma unroll
     for (int u = 0; u < kHeadPrefetch; ++u) {
       const int t = t0 + u;
-      if (t < T) {
-        const float p = pr[u], sin = sr[u];
-        if (t + kHeadPrefetch < T) {
-          pr[u] = load_p<BF16>(P, base + static_cast<i64>(t + kHeadPrefetch) * 4 * dd);
-          sr[u] = S_in[base + static_cast<i64>(t + kHeadPrefetch) * 4 * dd];
-        }
-        // residual and factors at the iterate (independent of the solve)
-        const float x = p + block_dot<DH>(row, hbuf[t & 1]);
-        float xs[4], ps[4];
-        quad_gather(x, xs);
-        quad_gather(prev, ps);
-        float s[4], A[16], G[16];
-        cell_step_gates(CellIn{ps[0], ps[1], ps[2], 0.0f}, xs, sig, floored, s, A, G);
-        const float sg = g == 0 ? s[0] : (g == 1 ? s[1] : (g == 2 ? s[2] : s[3]));
-        const float F = sin - sg;
-        emax = res_max(emax, F);
-        // the solve: Delta_t = A_own Delta_{t-1} + G (R Delta h_{t-1}) - F
-        const float y = block_dot<DH>(row, dhbuf[t & 1]);
-        float ys[4], ds[4];
-        quad_gather(y, ys);
-        quad_gather(dprev, ds);
-        const float* Ar = A + 4 * g;
-        const float* Gr = G + 4 * g;
-        float delta = fmaf(Ar[0], ds[0], fmaf(Ar[1], ds[1], Ar[2] * ds[2]));
-        delta = fmaf(Gr[0], ys[0], fmaf(Gr[1], ys[1], fmaf(Gr[2], ys[2], fmaf(Gr[3], ys[3], delta))));
-        delta -= F;
-        const float sout = sin + delta;
-        S_out[base + static_cast<i64>(t) * 4 * dd] = sout;
-        if constexpr (LAST) {
-          // residual of the new iterate: its pre-activations are x~ + R Delta h'
-          float sn[4], An[16];
-          cell_step<false>(CellIn{ps[0] + ds[0], ps[1] + ds[1], ps[2] + ds[2], 0.0f}, xs[0] + ys[0], xs[1] + ys[1],
-                           xs[2] + ys[2], xs[3] + ys[3], 0.0f, 0.0f, 0.0f, 0.0f, sig, floored, sn, An);
-          const float sng = g == 0 ? sn[0] : (g == 1 ? sn[1] : (g == 2 ? sn[2] : sn[3]));
-          emax_new = res_max(emax_new, sout - sng);
-          if (g == 3 && h_out != nullptr) h_out[(static_cast<i64>(b) * T + t) * dd + j] = sout;
-        }
-        if (g == 3) {
-          hbuf[(t + 1) & 1][i] = sin;
-          dhbuf[(t + 1) & 1][i] = delta;
-        }
-        prev = sin;
-        dprev = delta;
-        head_lds_barrier();
-      }
+      const float p = pr[u], sin = sr[u];
+      const i64 off = base + static_cast<i64>(min(t + kHeadPrefetch, T - 1)) * 4 * dd;
+      pr[u] = load_p<BF16>(P, off);
+      sr[u] = S_in[off];
+      step(t, p, sin);
     }
   }
+#pragma unroll
+  for (int u = 0; u < kHeadPrefetch - 1; ++u)
+    if (t0 + u < T) step(t0 + u, pr[u], sr[u]);
   // residual maxima: the workgroup's into LDS, then one device atomic per slot
   __hip_atomic_fetch_max(&s_err[0], emax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   if (LAST) __hip_atomic_fetch_max(&s_err[1], emax_new, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
