@@ -376,7 +376,8 @@ typedef enum {
   SLSTM_KERNEL_INPUT_GRADIENT = 11,  /* slstm_input_projection_backward's dx product */
   SLSTM_KERNEL_HEAD_ITERATION = 12,  /* one Newton iteration under head mixing */
   SLSTM_KERNEL_HEAD_SEQUENTIAL = 13, /* the sequential forward under head mixing */
-  SLSTM_KERNEL_KINDS = 14
+  SLSTM_KERNEL_HEAD_SOLVE = 14,      /* the whole Newton solve under head mixing, one sweep */
+  SLSTM_KERNEL_KINDS = 15
 } slstm_kernel_kind;
 
 slstm_status slstm_profile_enable(int on);

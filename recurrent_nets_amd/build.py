@@ -6,6 +6,7 @@ shared object, recurrent_nets_amd/lib/libslstm_mi355x.so.
 from __future__ import annotations
 
 import argparse
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -49,8 +50,7 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
     os.makedirs(LIBDIR, exist_ok=True)
     cc = hipcc()
     with tempfile.TemporaryDirectory(prefix="slstm_build_") as tmp:
-        objs = []
-        for src in sources():
+        def compile_one(src):
             obj = os.path.join(tmp, os.path.basename(src) + ".o")
             cmd = [cc, *HIPCC_FLAGS, "-c", src, "-o", obj]
             if resource_usage:
@@ -60,7 +60,15 @@ def build(verbose: bool = False, resource_usage: bool = False) -> str:
             res = subprocess.run(cmd, capture_output=True, text=True)
             # the host pass warns that it does not know the device-only feature; drop that line
             err = "\n".join(l for l in res.stderr.splitlines() if "packed-fp32-ops" not in l)
-            if res.returncode != 0:
+            return src, obj, res.returncode, err
+
+        # one hipcc process per source, a few at a time (the machine's CPU share is 16)
+        workers = max(1, min(8, os.cpu_count() or 1, len(sources())))
+        with concurrent.futures.ThreadPoolExecutor(max_workers=workers) as pool:
+            results = list(pool.map(compile_one, sources()))
+        objs = []
+        for src, obj, rc, err in results:
+            if rc != 0:
                 raise RuntimeError(f"hipcc failed on {src}:\n{err}")
             if err.strip() and (verbose or resource_usage):
                 print(err, file=sys.stderr)

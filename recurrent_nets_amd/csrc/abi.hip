@@ -336,7 +336,6 @@ hipError_t iterate(const void* P, bool bf16, const float* R, const float* state0
     HIP_RET(slstm::launch_select_iterate(ctl, buf[0], buf[1], states, n_state, st));
   return hipSuccess;
 }
-#undef HIP_RET
 
 // fixed-count solves of the chain form run as one pipelined kernel
 bool pipe_solve(Form form, int max_iters, float tol) {
@@ -570,6 +569,34 @@ slstm_status backward(const void* P, slstm_dtype P_dtype, const float* R, const 
 }
 
 // head mixing: control block, the warm start's look-back words, the second iterate buffer
+// head mixing with one launch per iteration (an early stop, or more iterations than the
+// one-sweep kernel holds): the warm start or zero iterate, then K iteration kernels; iterate k
+// lives in buf[k % 2], arranged so that iterate max_iters lands in `states`, and the early stop
+// leaves its iterate there through select_iterate
+hipError_t head_newton_iterations(const void* P, bool bf16, const float* R, const float* state0, float* states,
+                                  float* h_out, int B, int T, int d_h, int n_heads, int cm, int max_iters, float tol,
+                                  slstm_init init, Control* ctl, unsigned long long* desc, float* other,
+                                  hipStream_t st) {
+  const i64 n_state = static_cast<i64>(B) * T * 4 * d_h;
+  float* buf[2] = {(max_iters % 2 == 0) ? states : other, (max_iters % 2 == 0) ? other : states};
+  if (init == SLSTM_INIT_WARM) {
+    HIP_RET(launch_warm(P, bf16, state0, buf[0], B, T, d_h, cm, false, desc, ctl, st, {}));
+  } else {
+    HIP_RET(slstm::launch_zero(buf[0], n_state, st));
+  }
+  for (int k = 0; k < max_iters; ++k) {
+    const bool last = k + 1 == max_iters;
+    HIP_RET(timed(SLSTM_KERNEL_HEAD_ITERATION, st, [&] {
+      return slstm::launch_head_iteration(P, bf16, R, state0, buf[k % 2], buf[(k + 1) % 2], last ? h_out : nullptr,
+                                          B, T, d_h, n_heads, cm, ctl, k, tol, last, st);
+    }));
+  }
+  // the last launch formed the final residual and h; what remains of the stop rule is the check
+  // of the iterate before it
+  HIP_RET(slstm::launch_settle(ctl, max_iters - 1, tol, st));
+  return slstm::launch_select_iterate(ctl, buf[0], buf[1], states, n_state, st);
+}
+
 struct HeadLayout {
   size_t ctl, desc, S2, total;
 };
@@ -888,27 +915,17 @@ slstm_status slstm_head_newton_forward(const void* P, slstm_dtype P_dtype, const
   const int cm = cell_mode_of(fmode);
   Control* ctl = at<Control>(workspace, L.ctl);
   auto* desc = at<unsigned long long>(workspace, L.desc);
-  const i64 n_state = static_cast<i64>(B) * T * 4 * d_h;
   HIP_TRY(slstm::launch_init_control(ctl, st));
-  // iterate k lives in buf[k % 2], arranged so that iterate max_iters lands in `states`
-  float* other = at<float>(workspace, L.S2);
-  float* buf[2] = {(max_iters % 2 == 0) ? states : other, (max_iters % 2 == 0) ? other : states};
-  if (init == SLSTM_INIT_WARM) {
-    HIP_TRY(launch_warm(P, bf16, state0, buf[0], B, T, d_h, cm, false, desc, ctl, st, {}));
-  } else {
-    HIP_TRY(slstm::launch_zero(buf[0], n_state, st));
-  }
-  for (int k = 0; k < max_iters; ++k) {
-    const bool last = k + 1 == max_iters;
-    HIP_TRY(timed(SLSTM_KERNEL_HEAD_ITERATION, st, [&] {
-      return slstm::launch_head_iteration(P, bf16, R, state0, buf[k % 2], buf[(k + 1) % 2], last ? h_out : nullptr,
-                                          B, T, d_h, n_heads, cm, ctl, k, tol, last, st);
+  if (tol == 0.0f && max_iters <= slstm::kHeadSolveMaxIters) {
+    // a fixed count of iterations: the whole solve in one sweep over T
+    HIP_TRY(timed(SLSTM_KERNEL_HEAD_SOLVE, st, [&] {
+      return slstm::launch_head_solve(P, bf16, R, state0, states, h_out, B, T, d_h, n_heads, cm, max_iters,
+                                      init == SLSTM_INIT_ZERO, ctl, st);
     }));
+  } else {
+    HIP_TRY(head_newton_iterations(P, bf16, R, state0, states, h_out, B, T, d_h, n_heads, cm, max_iters, tol, init,
+                                   ctl, desc, at<float>(workspace, L.S2), st));
   }
-  // the last launch formed the final residual and h; what remains of the stop rule is the check
-  // of the iterate before it
-  HIP_TRY(slstm::launch_settle(ctl, max_iters - 1, tol, st));
-  HIP_TRY(slstm::launch_select_iterate(ctl, buf[0], buf[1], states, n_state, st));
   HIP_TRY(slstm::launch_finalize(ctl, tol, st));
   if (h_out != nullptr || final_state != nullptr)
     HIP_TRY(slstm::launch_outputs(states, h_out, final_state, B, T, d_h, ctl, st));
@@ -918,7 +935,6 @@ slstm_status slstm_head_newton_forward(const void* P, slstm_dtype P_dtype, const
   HIP_TRY(hipStreamSynchronize(st));
   return stats_from_control(host, stats);
 }
-
 slstm_status slstm_head_sequential_forward(const void* P, slstm_dtype P_dtype, const float* R,
                                            const float* state0, float* states, float* h_out,
                                            float* final_state, int B, int T, int d_h, int n_heads,

@@ -22,73 +22,11 @@
 //
 // Per-step operands are prefetched kHeadPrefetch steps ahead; the barrier between steps orders
 // LDS only, so those loads stay in flight across it.
-#include "affine4.h"
 #include "cell.h"
+#include "head.h"
 #include "kernels.h"
 
 namespace slstm {
-
-constexpr int kHeadPrefetch = 8;
-
-// barrier for the step-to-step LDS exchange: this thread's LDS accesses have completed
-// (lgkmcnt 0, the other counters left at their maxima); global loads stay in flight
-__device__ __forceinline__ void head_lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// the four values of a unit (one per lane of its quad), in every lane of the quad
-__device__ __forceinline__ void quad_gather(float v, float out[4]) {
-  out[0] = quad_bcast<0>(v);
-  out[1] = quad_bcast<1>(v);
-  out[2] = quad_bcast<2>(v);
-  out[3] = quad_bcast<3>(v);
-}
-
-// row i of gate g's block of head a, d_head floats (R is (4, n_heads, d_head, d_head))
-template <int DH>
-__device__ __forceinline__ void load_block_row(const float* __restrict__ R, int nh, int a, int i, int g,
-                                               float row[DH]) {
-  const float4* src = reinterpret_cast<const float4*>(R + ((static_cast<i64>(g) * nh + a) * DH + i) * DH);
-#pragma unroll
-  for (int k = 0; k < DH / 4; ++k) {
-    const float4 v = src[k];
-    row[4 * k] = v.x;
-    row[4 * k + 1] = v.y;
-    row[4 * k + 2] = v.z;
-    row[4 * k + 3] = v.w;
-  }
-}
-
-// v[g] for the lane's gate g = 2 g1 + g0 (the bits held as loop-invariant lane masks): three
-// selects, where indexing a register array by g would select among every element
-struct GateSel {
-  bool g0, g1;
-  __device__ __forceinline__ explicit GateSel(int g) : g0((g & 1) != 0), g1((g & 2) != 0) {}
-  __device__ __forceinline__ float operator()(float v0, float v1, float v2, float v3) const {
-    const float lo = g0 ? v1 : v0;
-    const float hi = g0 ? v3 : v2;
-    return g1 ? hi : lo;
-  }
-  __device__ __forceinline__ float operator()(const float v[4]) const { return (*this)(v[0], v[1], v[2], v[3]); }
-};
-
-template <int DH>
-__device__ __forceinline__ float block_dot(const float row[DH], const float* __restrict__ v) {
-  const float4* v4 = reinterpret_cast<const float4*>(v);
-  float acc0 = 0.0f, acc1 = 0.0f;
-#pragma unroll
-  for (int k = 0; k < DH / 4; ++k) {
-    const float4 x = v4[k];
-    acc0 = fmaf(row[4 * k], x.x, acc0);
-    acc1 = fmaf(row[4 * k + 1], x.y, acc1);
-    acc0 = fmaf(row[4 * k + 2], x.z, acc0);
-    acc1 = fmaf(row[4 * k + 3], x.w, acc1);
-  }
-  return acc0 + acc1;
-}
 
 template <int DH, bool BF16, int CM>
 __global__ __launch_bounds__(4 * DH) void head_seq_kernel(const void* __restrict__ P, const float* __restrict__ R,
@@ -287,23 +225,15 @@ __global__ __launch_bounds__(4 * DH) void head_iter_kernel(const void* __restric
 
 bool head_width_supported(int d_head) { return d_head == 8 || d_head == 16 || d_head == 32 || d_head == 64; }
 
-#define SLSTM_HEAD_DH_DISPATCH(DHV, BODY) \
-  switch (DHV) {                          \
-    case 8: { constexpr int DH = 8; BODY; break; }    \
-    case 16: { constexpr int DH = 16; BODY; break; }  \
-    case 32: { constexpr int DH = 32; BODY; break; }  \
-    case 64: { constexpr int DH = 64; BODY; break; }  \
-    default: return hipErrorInvalidValue;             \
-  }
-
 hipError_t launch_head_sequential(const void* P, bool p_bf16, const float* R, const float* state0, float* S,
                                   float* h_out, float* final_state, int B, int T, int d, int n_heads,
                                   int cell_mode, hipStream_t stream) {
   if (n_heads < 1 || d % n_heads != 0 || B > 65535) return hipErrorInvalidValue;
   const int dh = d / n_heads;
   const dim3 grid(static_cast<unsigned>(n_heads), static_cast<unsigned>(B));
+  const unsigned int lds = head_spread_lds(static_cast<long long>(n_heads) * B, 4096);
 #define SLSTM_HEAD_SEQ(BF, CM_) \
-  head_seq_kernel<DH, BF, CM_><<<grid, 4 * DH, 0, stream>>>(P, R, state0, S, h_out, final_state, T, d, n_heads)
+  head_seq_kernel<DH, BF, CM_><<<grid, 4 * DH, lds, stream>>>(P, R, state0, S, h_out, final_state, T, d, n_heads)
 #define SLSTM_HEAD_SEQ_T(CM_) SLSTM_HEAD_SEQ(true, CM_)
 #define SLSTM_HEAD_SEQ_F(CM_) SLSTM_HEAD_SEQ(false, CM_)
   SLSTM_HEAD_DH_DISPATCH(dh, {
@@ -322,8 +252,9 @@ hipError_t launch_head_iteration(const void* P, bool p_bf16, const float* R, con
   if (n_heads < 1 || d % n_heads != 0 || B > 65535) return hipErrorInvalidValue;
   const int dh = d / n_heads;
   const dim3 grid(static_cast<unsigned>(n_heads), static_cast<unsigned>(B));
+  const unsigned int lds = head_spread_lds(static_cast<long long>(n_heads) * B, 4096);
 #define SLSTM_HEAD_IT(BF, LS, CM_)                                                                             \
-  head_iter_kernel<DH, BF, CM_, LS><<<grid, 4 * DH, 0, stream>>>(P, R, state0, S_in, S_out, h_out, T, d, n_heads, \
+  head_iter_kernel<DH, BF, CM_, LS><<<grid, 4 * DH, lds, stream>>>(P, R, state0, S_in, S_out, h_out, T, d, n_heads, \
                                                                  ctl, k_iter, tol)
 #define SLSTM_HEAD_IT_TT(CM_) SLSTM_HEAD_IT(true, true, CM_)
 #define SLSTM_HEAD_IT_TF(CM_) SLSTM_HEAD_IT(true, false, CM_)
@@ -345,7 +276,5 @@ hipError_t launch_head_iteration(const void* P, bool p_bf16, const float* R, con
 #undef SLSTM_HEAD_IT
   return hipGetLastError();
 }
-
-#undef SLSTM_HEAD_DH_DISPATCH
 
 }  // namespace slstm

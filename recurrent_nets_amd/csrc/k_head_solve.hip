@@ -1,0 +1,192 @@
+// The whole Newton solve under head mixing in one sweep over T ("sLSTM in this library",
+// "Cell", the mix table's 'head' row; Newton's method on the recurrence, "ParaRNN", the
+// Newton-iteration section): a fixed count of K iterations (no early stop), pipelined along T.
+//
+// Iteration k's linear solve Delta^k_t = A^k_t Delta^k_{t-1} - F^k_t is a forward substitution:
+// at step t it needs only iterate k at t-1 and t and Delta^k_{t-1}. Iterate k at t is
+// S^{k-1}_t + Delta^{k-1}_t, formed by stage k-1 at the same step, and its pre-activations are
+// linear in h', so
+//   x~^k_t = x~^{k-1}_t + R Delta h^{k-1}_{t-1}        (x~^0_t = p_t + R h^0_{t-1})
+// and one block product per stage (R Delta h^k_{t-1}) serves both stage k's solve and stage
+// k+1's residual. Stage 0's iterate is the warm start (the channelwise cell with R h' dropped,
+// run step by step here) or zero. A step therefore costs K + 1 block products and K + 2 cell
+// evaluations (warm start, K residuals with their Jacobians, the final residual); nothing but P
+// is read and nothing but S^K and h is written. The iterates are those of one kernel per
+// iteration up to float32 rounding.
+//
+// Layout as in k_head.hip: a workgroup per (batch row, head), lane 4 i + g for unit i and
+// gate / state slot g, row i of gate g's block in registers, h of iterate 0 and Delta h of
+// every stage passed from step to step through double-buffered LDS.
+#include "cell.h"
+#include "head.h"
+#include "kernels.h"
+
+namespace slstm {
+
+template <int DH, bool BF16, int CM, int K>
+__global__ __launch_bounds__(4 * DH) void head_solve_kernel(const void* __restrict__ P, const float* __restrict__ R,
+                                                            const float* __restrict__ state0, float* __restrict__ S,
+                                                            float* __restrict__ h_out, int T, int d, int nh,
+                                                            Control* __restrict__ ctl, int zero_init) {
+  constexpr bool sig = (CM & kCellSigmoid) != 0;
+  constexpr bool floored = (CM & kCellFloored) != 0;
+  __shared__ __attribute__((aligned(16))) float h0buf[2][DH];     // h of iterate 0 at t - 1
+  __shared__ __attribute__((aligned(16))) float dhbuf[K][2][DH];  // Delta h of stage k at t - 1
+  __shared__ unsigned int s_err[K + 1];
+  __shared__ float junk[4 * DH];  // the LDS writes of lanes that do not hold h (see h_slot)
+  const int tid = threadIdx.x;
+  const int i = tid >> 2, g = tid & 3;
+  const int a = blockIdx.x, b = blockIdx.y;
+  const int j = a * DH + i;
+  const i64 dd = d;
+  const GateSel sel(g);
+  float row[DH];
+  load_block_row<DH>(R, nh, a, i, g, row);
+  const float s0 = state0 != nullptr ? state0[(static_cast<i64>(b) * 4 + g) * dd + j] : 0.0f;
+  // slot g of iterate k at t - 1 (k = 0..K; every iterate starts from state0) and of Delta^k
+  float sp[K + 1], dp[K];
+  unsigned int emax[K + 1];
+#pragma unroll
+  for (int k = 0; k <= K; ++k) {
+    sp[k] = s0;
+    emax[k] = 0u;
+  }
+#pragma unroll
+  for (int k = 0; k < K; ++k) dp[k] = 0.0f;
+  if (g == 3) {
+    h0buf[0][i] = s0;  // the state before step 0 is state0 for every iterate
+#pragma unroll
+    for (int k = 0; k < K; ++k) dhbuf[k][0][i] = 0.0f;
+  }
+  if (tid <= K) s_err[tid] = 0u;
+  // where this lane's value goes in an h exchange: the h lane's slot, the others a junk word;
+  // an address select keeps the step free of branches, so its stages can be interleaved
+  auto h_slot = [&](float* hdst) { return g == 3 ? hdst : &junk[tid]; };
+  const i64 base = static_cast<i64>(b) * T * 4 * dd + g * dd + j;  // (b, t = 0, slot/gate g, j)
+  float pr[kHeadPrefetch];
+#pragma unroll
+  for (int u = 0; u < kHeadPrefetch; ++u) pr[u] = load_p<BF16>(P, base + static_cast<i64>(min(u, T - 1)) * 4 * dd);
+  head_lds_barrier();
+
+  // a step at t >= T (the rest of the last block of kHeadPrefetch) runs on clamped operands and
+  // leaves no trace: no store, no residual maximum; its LDS exchange is never read for a real
+  // step. The step returns slot g of iterate K at t; the block stores them after its last step.
+  const float warm_scale = zero_init ? 0.0f : 1.0f;  // the warm start's state is finite
+  auto step = [&](int t, float p, bool real) -> float {
+    // the R Delta h' products of every stage depend on step t - 1 only
+    float y[K];
+#pragma unroll
+    for (int k = 0; k < K; ++k) y[k] = block_dot<DH>(row, dhbuf[k][t & 1]);
+    float xs[4], ps[4], pg[4];
+    quad_gather(p + block_dot<DH>(row, h0buf[t & 1]), xs);  // x~^0_t
+    quad_gather(sp[0], ps);                                  // iterate 0 at t - 1
+    // iterate 0 at t (formed also for a zero start, then discarded: no branch in the step)
+    float cur;
+    {
+      quad_gather(p, pg);
+      float s[4], A[16];
+      cell_step<false>(CellIn{ps[0], ps[1], ps[2], 0.0f}, pg[0], pg[1], pg[2], pg[3], 0.0f, 0.0f, 0.0f, 0.0f, sig,
+                       floored, s, A);
+      cur = sel(s) * warm_scale;
+    }
+    *h_slot(&h0buf[(t + 1) & 1][i]) = cur;
+#pragma unroll
+    for (int k = 0; k < K; ++k) {
+      if (k > 0) quad_gather(sp[k], ps);  // iterate k at t - 1
+      float s[4], A[16], G[16];
+      cell_step_gates(CellIn{ps[0], ps[1], ps[2], 0.0f}, xs, sig, floored, s, A, G);
+      const float F = cur - sel(s);
+      const unsigned int em = res_max(emax[k], F);
+      emax[k] = real ? em : emax[k];
+      float ys[4], ds[4];
+      quad_gather(y[k], ys);
+      quad_gather(dp[k], ds);
+      float delta = sel(A[0], A[4], A[8], A[12]) * ds[0];
+      delta = fmaf(sel(A[1], A[5], A[9], A[13]), ds[1], delta);
+      delta = fmaf(sel(A[2], A[6], A[10], A[14]), ds[2], delta);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) delta = fmaf(sel(G[q], G[4 + q], G[8 + q], G[12 + q]), ys[q], delta);
+      delta -= F;
+      *h_slot(&dhbuf[k][(t + 1) & 1][i]) = delta;
+      sp[k] = cur;
+      dp[k] = delta;
+      cur += delta;  // iterate k + 1 at t
+#pragma unroll
+      for (int q = 0; q < 4; ++q) xs[q] += ys[q];
+    }
+    // iterate K at t: the result, and its residual
+    quad_gather(sp[K], ps);
+    float sn[4], An[16];
+    cell_step<false>(CellIn{ps[0], ps[1], ps[2], 0.0f}, xs[0], xs[1], xs[2], xs[3], 0.0f, 0.0f, 0.0f, 0.0f, sig,
+                     floored, sn, An);
+    const unsigned int em = res_max(emax[K], cur - sel(sn));
+    emax[K] = real ? em : emax[K];
+    sp[K] = cur;
+    head_lds_barrier();
+    return cur;
+  };
+  // blocks of kHeadPrefetch steps; every ring slot is refilled unconditionally (clamped), so no
+  // load has to complete before the step kHeadPrefetch later that reads it
+  const bool h_lane = g == 3 && h_out != nullptr;
+  for (int t0 = 0; t0 < T; t0 += kHeadPrefetch) {
+    float out[kHeadPrefetch];
+#pragma unroll
+    for (int u = 0; u < kHeadPrefetch; ++u) {
+      const int t = t0 + u;
+      const float p = pr[u];
+      pr[u] = load_p<BF16>(P, base + static_cast<i64>(min(t + kHeadPrefetch, T - 1)) * 4 * dd);
+      out[u] = step(t, p, t < T);
+    }
+#pragma unroll
+    for (int u = 0; u < kHeadPrefetch; ++u) {
+      const int t = t0 + u;
+      if (t < T) {
+        S[base + static_cast<i64>(t) * 4 * dd] = out[u];
+        if (h_lane) h_out[(static_cast<i64>(b) * T + t) * dd + j] = out[u];
+      }
+    }
+  }
+
+  // residual maxima of iterates 0..K: the workgroup's into LDS, then one device atomic each
+#pragma unroll
+  for (int k = 0; k <= K; ++k) __hip_atomic_fetch_max(&s_err[k], emax[k], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned int slot = blockIdx.x + gridDim.x * blockIdx.y;
+#pragma unroll
+    for (int k = 0; k <= K; ++k) err_publish(&spread_of(ctl)->err[0][k], kErrSlotWords, slot, res_max_value(s_err[k]));
+    if (blockIdx.x == 0 && blockIdx.y == 0) ctl->iters = K;
+  }
+}
+
+hipError_t launch_head_solve(const void* P, bool p_bf16, const float* R, const float* state0, float* S,
+                             float* h_out, int B, int T, int d, int n_heads, int cell_mode, int K, bool zero_init,
+                             Control* ctl, hipStream_t stream) {
+  if (n_heads < 1 || d % n_heads != 0 || B > 65535 || K < 1 || K > kHeadSolveMaxIters) return hipErrorInvalidValue;
+  const int dh = d / n_heads;
+  const dim3 grid(static_cast<unsigned>(n_heads), static_cast<unsigned>(B));
+  const unsigned int lds = head_spread_lds(static_cast<long long>(n_heads) * B, 4096);
+  const int zi = zero_init ? 1 : 0;
+#define SLSTM_HEAD_SOLVE(BF, KK, CM_) \
+  head_solve_kernel<DH, BF, CM_, KK><<<grid, 4 * DH, lds, stream>>>(P, R, state0, S, h_out, T, d, n_heads, ctl, zi)
+#define SLSTM_HEAD_SOLVE_K(BF, CM_)              \
+  switch (K) {                                   \
+    case 1: SLSTM_HEAD_SOLVE(BF, 1, CM_); break; \
+    case 2: SLSTM_HEAD_SOLVE(BF, 2, CM_); break; \
+    case 3: SLSTM_HEAD_SOLVE(BF, 3, CM_); break; \
+    default: SLSTM_HEAD_SOLVE(BF, 4, CM_); break; \
+  }
+#define SLSTM_HEAD_SOLVE_T(CM_) SLSTM_HEAD_SOLVE_K(true, CM_)
+#define SLSTM_HEAD_SOLVE_F(CM_) SLSTM_HEAD_SOLVE_K(false, CM_)
+  SLSTM_HEAD_DH_DISPATCH(dh, {
+    if (p_bf16) { SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_HEAD_SOLVE_T) }
+    else { SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_HEAD_SOLVE_F) }
+  })
+#undef SLSTM_HEAD_SOLVE_T
+#undef SLSTM_HEAD_SOLVE_F
+#undef SLSTM_HEAD_SOLVE_K
+#undef SLSTM_HEAD_SOLVE
+  return hipGetLastError();
+}
+
+}  // namespace slstm

@@ -111,6 +111,14 @@ hipError_t launch_head_sequential(const void* P, bool p_bf16, const float* R, co
 hipError_t launch_head_iteration(const void* P, bool p_bf16, const float* R, const float* state0, const float* S_in,
                                  float* S_out, float* h_out, int B, int T, int d, int n_heads, int cell_mode,
                                  Control* ctl, int k_iter, float tol, bool last, hipStream_t stream);
+// The whole head-mixing Newton solve in one sweep over T: K (1..kHeadSolveMaxIters) iterations
+// pipelined stage by stage, the warm start (or zero_init's zero iterate) formed in the sweep;
+// writes S (iterate K), h_out (may be NULL), the residual maxima of iterates 0..K into ctl's
+// error slots and ctl->iters = K.
+constexpr int kHeadSolveMaxIters = 4;
+hipError_t launch_head_solve(const void* P, bool p_bf16, const float* R, const float* state0, float* S,
+                             float* h_out, int B, int T, int d, int n_heads, int cell_mode, int K, bool zero_init,
+                             Control* ctl, hipStream_t stream);
 
 // C = X W^T (+ bias) in bf16 MFMA with float32 accumulation; X (M x K), W (N x K), both
 // K-contiguous. With splits > 1 the K range is split and split s writes its partial product to

@@ -26,7 +26,7 @@ MAX_ITERS = 64
 KERNELS = {"warm_start": 0, "residual_jacobian": 1, "scan_block4": 2, "update": 3,
            "final_residual": 4, "input_projection": 5, "sequential": 6, "newton_iteration": 7,
            "newton_solve": 8, "backward": 9, "weight_gradient": 10, "input_gradient": 11,
-           "head_iteration": 12, "head_sequential": 13}
+           "head_iteration": 12, "head_sequential": 13, "head_solve": 14}
 
 EXPORTED = [
     "slstm_status_string", "slstm_last_error", "slstm_newton_workspace_bytes",

@@ -4,7 +4,8 @@ library", "Cell", the mix table; the paper's sLSTM memory mixing, summary card "
 the float64 oracle's dense per-head forms.
 
 Covered: the sequential forward and the Newton solve (warm and zero start, fixed count and early
-stop, state0 and final state) for every supported head width, both forget-gate forms, the
+stop, state0 and final state; the one-sweep kernel for a fixed count of up to 4 iterations and
+the per-iteration kernels otherwise) for every supported head width, both forget-gate forms, the
 floored read-out and bf16 pre-activations; T = 1 and T not a multiple of the kernels' 8-step
 prefetch; many narrow heads; diagonal blocks against the channelwise solver at a larger size;
 and the head-mixing benchmark workload at full size on sampled (batch row, head) pairs: each
@@ -141,6 +142,54 @@ def test_head_newton_stop_after_last_iterate(gpu_lib):
     assert st_ref.iters == 2 and st_ref.converged
     assert st.iters == 2 and st.converged
     assert h_rel_err(h, S_ref[..., 3, :]) < H_TOL_F32
+
+
+@pytest.mark.parametrize("K", [1, 2, 3, 4])
+@pytest.mark.parametrize("dh", [8, 64])
+def test_head_one_sweep_solve(gpu_lib, K, dh):
+    """tol = 0 and K <= 4: the whole solve is one launch of the one-sweep kernel (no iteration
+    kernel); a tolerance that is never met forces one iteration kernel per iteration instead.
+    Both match the oracle's iterate, residual maxima and flags."""
+    P, R, s0 = _inputs(1000 + K + dh, 2, 45, dh, 2)
+    Pd, Rd, s0d = _dev(P, R, s0)
+    case(f"head one-sweep solve vs iteration kernels d_head={dh} K={K}")
+    gpu_lib.profile_reset()
+    gpu_lib.profile_enable(True)
+    _, h1, st1 = gpu_lib.head_newton_forward(Pd, Rd, s0d, "exp", K, 0.0)
+    n_sweep = len(gpu_lib.profile_durations("head_solve"))
+    n_iter1 = len(gpu_lib.profile_durations("head_iteration"))
+    gpu_lib.profile_reset()
+    _, h2, st2 = gpu_lib.head_newton_forward(Pd, Rd, s0d, "exp", K, 1e-30)
+    n_iter2 = len(gpu_lib.profile_durations("head_iteration"))
+    gpu_lib.profile_enable(False)
+    torch.cuda.synchronize()
+    assert (n_sweep, n_iter1, n_iter2) == (1, 0, K)
+    S_ref, st_ref = ref.newton_head(to_np(P), to_np(R), to_np(s0), "exp", K)
+    for h, st in ((h1, st1), (h2, st2)):
+        assert h_rel_err(h, S_ref[..., 3, :]) < H_TOL_F32
+        assert st.iters == K and st.diverged == st_ref.diverged and not st.converged
+        assert len(st.max_abs_F) == K + 1
+        for e_gpu, e_ref in zip(st.max_abs_F, st_ref.max_abs_F):
+            if e_ref > 1e-3:
+                assert abs(e_gpu - e_ref) <= 1e-3 * e_ref
+    assert h_rel_err(h1, to_np(h2)) < H_TOL_F32
+
+
+def test_head_one_sweep_zero_init_exact(gpu_lib):
+    """The one-sweep kernel from a zero iterate: after K = T iterations the iterate is the exact
+    solution (the sequential one). Sigmoid forget gate: with the exponential one, this zero
+    start's intermediate iterates reach residuals of 3e3 and float32 keeps h only to 8e-4 of
+    it, on the one-sweep and the per-iteration kernels alike."""
+    T = 4
+    P, R, s0 = _inputs(1010, 3, T, 16, 2)
+    case(f"head one-sweep zero init K=T={T}")
+    _, h, st = gpu_lib.head_newton_forward(*_dev(P, R, s0), "sigmoid", T, 0.0, init="zero")
+    torch.cuda.synchronize()
+    seq = ref.sequential_head(to_np(P), to_np(R), to_np(s0), "sigmoid")
+    S_ref, _ = ref.newton_head(to_np(P), to_np(R), to_np(s0), "sigmoid", T, init=ref.INIT_ZERO)
+    assert h_rel_err(h, S_ref[..., 3, :]) < H_TOL_F32
+    assert h_rel_err(h, seq[..., 3, :]) < H_TOL_F32
+    assert st.iters == T
 
 
 @pytest.mark.parametrize("T", [1, 7, 8, 9])
