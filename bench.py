@@ -90,6 +90,7 @@ def kernel_work(w, n_e, p_bytes):
 # Head mixing (block-diagonal R, 32 heads of 32 units) at the size of the sigmoid workload's
 # batch and width: a context line, not the metric.
 HEAD = dict(B=16, T=4096, d=1024, n_heads=32, forget="exp", K=3, seed=20265)
+HEAD_WORKLOAD = "head_b16_t4096_d1024_h32"
 
 
 def head_solve_flops_per_elem(d_head, K, sigmoid_forget):
@@ -129,6 +130,9 @@ KERNEL_SOURCES = {
     "backward": ["recurrent_nets_amd/csrc/k_backward.hip", "recurrent_nets_amd/csrc/affine4.h",
                  "recurrent_nets_amd/csrc/cell.h", "recurrent_nets_amd/csrc/common.h",
                  "recurrent_nets_amd/csrc/kernels.h"],
+    "head_solve": ["recurrent_nets_amd/csrc/k_head_solve.hip", "recurrent_nets_amd/csrc/head.h",
+                   "recurrent_nets_amd/csrc/affine4.h", "recurrent_nets_amd/csrc/cell.h",
+                   "recurrent_nets_amd/csrc/common.h", "recurrent_nets_amd/csrc/kernels.h"],
 }
 
 
@@ -271,7 +275,8 @@ def head_context(slstm, torch, dev, steps):
                      "hbm_view": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": round(gbs / HBM_PEAK_GBS, 4)},
                      "alu_view": {"achieved": round(tfs, 2), "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                  "frac": round(tfs / FP32_VECTOR_PEAK_TFLOPS, 4)}}}
+                                  "frac": round(tfs / FP32_VECTOR_PEAK_TFLOPS, 4)},
+                     "traffic": measured_traffic("head_solve", HEAD_WORKLOAD)}}
 
 
 def main():
