@@ -758,3 +758,49 @@ def newton_head(P, R, state0, forget, max_iters, tol=0.0, init=INIT_WARM):
             stats.max_abs_F.append(max_abs(F))
     stats.converged, stats.diverged, stats.nonfinite = newton_flags(stats.max_abs_F[-1], tol)
     return S, stats
+
+
+def backward_head(P, R, state0, S, g, forget, g_final=None, return_adjoint=False):
+    """Gradients through the recurrence under head mixing, for a loss whose direct derivative
+    with respect to the states is g = dL/dS (and g_final = dL/d(final state), added at the last
+    step). P, S, g (B, T, 4, d); R (4, n_heads, d_head, d_head); state0 (B, 4, d) or None.
+    Returns dP (B, T, 4, d), dR (4, n_heads, d_head, d_head), dstate0 (B, 4, d) and, with
+    return_adjoint, the adjoint lam (B, T, 4, d).
+
+    The reverse recurrence of ``backward`` with the dense per-head Jacobians of ``cell_head``:
+      lam_T = g_T,  lam_t = g_t + J_{t+1}^T lam_{t+1}   (per head, unit-major vectors)
+    and per step the gate vector-Jacobian product dP_t = G_t^T lam_t (G_t = d s_t / d x~_t, the
+    same for every mixing, since x~ enters the cell the same way); h' enters x~ through R_g h',
+    so dR[g, a, i, k] = sum over b and t of dP_t[g, a d_head + i] h_{t-1}[a d_head + k], and
+    dstate0 = J_1^T lam_1.
+    """
+    P = np.asarray(P, dtype=np.float64)
+    S = np.asarray(S, dtype=np.float64)
+    g = np.array(g, dtype=np.float64)
+    B, T, _, d = P.shape
+    R, nh, dh = _head_shape(R, d)
+    prev = _shifted(S, state0)
+    if g_final is not None:
+        g[:, T - 1] += np.asarray(g_final, dtype=np.float64)
+    zero_r = np.zeros((4, d))
+    dP = np.empty_like(P)
+    dR = np.zeros((4, nh, dh, dh))
+    dstate0 = np.zeros((B, 4, d))
+    lam_all = np.empty_like(S)
+    lam = g[:, T - 1].copy()
+    for t in range(T - 1, -1, -1):
+        lam_all[:, t] = lam
+        _, J = cell_head(prev[:, t], P[:, t], R, forget, with_jacobian=True)
+        pre = P[:, t] + head_recurrent(prev[:, t, H], R)
+        G = gate_jacobian(prev[:, t], pre, zero_r, forget)
+        delta = (G * lam[:, :, None, :]).sum(axis=1)  # G^T lam: sum over the state slots
+        dP[:, t] = delta
+        dR += np.einsum("bgai,bak->gaik", delta.reshape(B, 4, nh, dh), prev[:, t, H].reshape(B, nh, dh))
+        lam_prev = from_head_vectors(np.einsum("bauv,bau->bav", J, head_vectors(lam, nh)), nh)
+        if t > 0:
+            lam = g[:, t - 1] + lam_prev
+        else:
+            dstate0 = lam_prev
+    if return_adjoint:
+        return dP, dR, dstate0, lam_all
+    return dP, dR, dstate0

@@ -685,4 +685,70 @@ def pin_head_units_permute(ref):
     np.testing.assert_allclose(Snp, Sn[..., full], rtol=1e-12, atol=1e-13)
 
 
+def pin_head_backward_finite_differences(ref):
+    """dP, dR and dstate0 of a loss L = sum g S + sum g_final S_T through the sequential head
+    recurrence, against central differences along random directions (both forget gates and the
+    floored read-out)."""
+    P, R, s0 = _head_problem(97, T=6)
+    rng = np.random.default_rng(98)
+    g = rng.standard_normal(P.shape)
+    gf = rng.standard_normal(s0.shape)
+    eps = 1e-6
+    for forget in ("exp", "sigmoid", "sigmoid" + ref.FLOORED):
+        S = ref.sequential_head(P, R, s0, forget)
+        dP, dR, d0 = ref.backward_head(P, R, s0, S, g, forget, g_final=gf)
+
+        def loss(P_, R_, s_):
+            S_ = ref.sequential_head(P_, R_, s_, forget)
+            return float(np.sum(g * S_) + np.sum(gf * S_[:, -1]))
+
+        for which, X, grad in (("P", P, dP), ("R", R, dR), ("state0", s0, d0)):
+            E = rng.standard_normal(X.shape)
+            plus = [P, R, s0]
+            minus = [P, R, s0]
+            k = ("P", "R", "state0").index(which)
+            plus[k], minus[k] = X + eps * E, X - eps * E
+            fd = (loss(*plus) - loss(*minus)) / (2 * eps)
+            assert abs(fd - float(np.sum(grad * E))) <= 1e-6 * max(1.0, abs(fd)), (forget, which)
+
+
+def pin_head_backward_diagonal_blocks_are_channelwise(ref):
+    """Diagonal blocks: dP and dstate0 are the channelwise backward's, and the diagonal of dR is
+    its dR (the off-diagonal entries are the gradients of weights that happen to be zero)."""
+    P, R, s0 = _head_problem(99, T=7)
+    nh, dh = R.shape[1], R.shape[2]
+    r = np.concatenate([np.stack([np.diag(R[q, a]) for a in range(nh)]).reshape(-1)[None] for q in range(4)])
+    Rd = np.zeros_like(R)
+    for q in range(4):
+        for a in range(nh):
+            Rd[q, a] = np.diag(r[q, a * dh:(a + 1) * dh])
+    rng = np.random.default_rng(100)
+    g = rng.standard_normal(P.shape)
+    for forget in ("exp", "sigmoid"):
+        S = ref.sequential_head(P, Rd, s0, forget)
+        dP, dR, d0 = ref.backward_head(P, Rd, s0, S, g, forget)
+        cP, cR, c0 = ref.backward(P, r, s0, S, g, forget)
+        np.testing.assert_allclose(dP, cP, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(d0, c0, rtol=1e-12, atol=1e-13)
+        diag = np.stack([np.concatenate([np.diag(dR[q, a]) for a in range(nh)]) for q in range(4)])
+        np.testing.assert_allclose(diag, cR, rtol=1e-12, atol=1e-13)
+
+
+def pin_head_backward_width_one_is_channelwise(ref):
+    """d_head = 1: every output of the head backward is the channelwise backward's."""
+    rng = np.random.default_rng(101)
+    B, T, d = 2, 8, 5
+    P = rng.standard_normal((B, T, 4, d))
+    P[:, :, 2] += 2.0
+    r = rng.uniform(-0.5, 0.5, (4, d))
+    g = rng.standard_normal(P.shape)
+    gf = rng.standard_normal((B, 4, d))
+    S = ref.sequential(P, r, None, "sigmoid")
+    dP, dR, d0 = ref.backward_head(P, r.reshape(4, d, 1, 1), None, S, g, "sigmoid", g_final=gf)
+    cP, cR, c0 = ref.backward(P, r, None, S, g, "sigmoid", g_final=gf)
+    np.testing.assert_allclose(dP, cP, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(dR.reshape(4, d), cR, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(d0, c0, rtol=1e-12, atol=1e-13)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -64,6 +64,12 @@ MUTATIONS = [
     ("head mixing: transposed block", 'np.einsum("gaik,...ak->...gai", R, hh)', 'np.einsum("gaki,...ak->...gai", R, hh)'),
     ("head Jacobian: transposed coupling", 'np.einsum("...sgai,gaik->...aisk", Gh, R)',
      'np.einsum("...sgai,gaki->...aisk", Gh, R)'),
+    ("head backward: transposed gate Jacobian", "(G * lam[:, :, None, :]).sum(axis=1)",
+     "(G * lam[:, None, :, :]).sum(axis=2)"),
+    ("head backward: untransposed Jacobian", 'np.einsum("bauv,bau->bav", J, head_vectors(lam, nh))',
+     'np.einsum("bauv,bav->bau", J, head_vectors(lam, nh))'),
+    ("head backward: transposed dR", 'np.einsum("bgai,bak->gaik", delta.reshape', 'np.einsum("bgai,bak->gaki", delta.reshape'),
+    ("head backward: dR against h_t", "prev[:, t, H].reshape(B, nh, dh))", "S[:, t, H].reshape(B, nh, dh))"),
     ("head solve: transposed block", 'np.einsum("bauv,bav->bau", J[:, t], x[:, t - 1])',
      'np.einsum("bavu,bav->bau", J[:, t], x[:, t - 1])'),
 ]
