@@ -334,14 +334,25 @@ slstm_status slstm_backward_varlen(const void* P, slstm_dtype P_dtype, const flo
  * layouts, forget modes with the floored read-out flag, statuses, stream semantics).
  *
  * slstm_head_newton_forward: Newton as slstm_newton_forward (warm start with R h' dropped, the
- * same stop rule, flags and stats), each iteration one kernel: one workgroup per (batch row,
- * head) walks T, forms the residual at the iterate and solves the block-bidiagonal system with
- * the Jacobian applied in factored form (the unit's own-state columns plus the gate Jacobian
- * times R_g Delta h'), so no (4 d_head)^2 block is formed. The solve is a recurrence along T;
- * parallelism comes from B * n_heads. Workspace: slstm_head_newton_workspace_bytes (0 if the
- * sizes are invalid).
+ * same stop rule, flags and stats). One workgroup per (batch row, head) walks T, forms the
+ * residual at the iterate and solves the block-bidiagonal system with the Jacobian applied in
+ * factored form (the unit's own-state columns plus the gate Jacobian times R_g Delta h'), so no
+ * (4 d_head)^2 block is formed; the solve is a recurrence along T and parallelism comes from
+ * B * n_heads. With tol = 0 and max_iters <= 4 the warm start and all iterations run as one
+ * kernel, pipelined along T; otherwise the warm start, then one kernel per iteration.
+ * Workspace: slstm_head_newton_workspace_bytes (0 if the sizes are invalid).
  * slstm_head_sequential_forward: the step loop, one workgroup per (batch row, head); no
  * workspace.
+ * slstm_head_backward: gradients through the head-mixing recurrence at the forward solution
+ * `states`, as slstm_backward ([SL] "Backward"): g_states (B, T, 4, d_h), g_h (B, T, d_h) and
+ * g_final (B, 4, d_h) are the loss's direct gradients (each may be NULL: zero); outputs dP
+ * (B, T, 4, d_h) in dP_dtype (F32 or BF16, rounded to nearest even), dR (4, n_heads, d_head,
+ * d_head), dbias (4, d_h; may be NULL), dstate0 (B, 4, d_h; may be NULL); d_head 8, 16 or 32
+ * (64 is rejected with SLSTM_EINVAL: a lane's block row, column and dR row would not fit in
+ * registers). One workgroup per
+ * (batch row, head) walks T backwards; dR and dbias are added over the batch in a fixed order
+ * from per-row partial sums in the workspace (slstm_head_backward_workspace_bytes; 0 if the
+ * sizes are invalid), so results are reproducible bit for bit.
  */
 size_t slstm_head_newton_workspace_bytes(int B, int T, int d_h, int n_heads);
 slstm_status slstm_head_newton_forward(const void* P, slstm_dtype P_dtype, const float* R,
@@ -354,6 +365,13 @@ slstm_status slstm_head_sequential_forward(const void* P, slstm_dtype P_dtype, c
                                            const float* state0, float* states, float* h_out,
                                            float* final_state, int B, int T, int d_h, int n_heads,
                                            slstm_forget fmode, void* stream);
+size_t slstm_head_backward_workspace_bytes(int B, int T, int d_h, int n_heads);
+slstm_status slstm_head_backward(const void* P, slstm_dtype P_dtype, const float* R,
+                                 const float* state0, const float* states, const float* g_states,
+                                 const float* g_h, const float* g_final, void* dP,
+                                 slstm_dtype dP_dtype, float* dR, float* dbias, float* dstate0, int B,
+                                 int T, int d_h, int n_heads, slstm_forget fmode, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 /*
  * Kernel timing with HIP events recorded on the launching stream around every kernel the
@@ -377,7 +395,8 @@ typedef enum {
   SLSTM_KERNEL_HEAD_ITERATION = 12,  /* one Newton iteration under head mixing */
   SLSTM_KERNEL_HEAD_SEQUENTIAL = 13, /* the sequential forward under head mixing */
   SLSTM_KERNEL_HEAD_SOLVE = 14,      /* the whole Newton solve under head mixing, one sweep */
-  SLSTM_KERNEL_KINDS = 15
+  SLSTM_KERNEL_HEAD_BACKWARD = 15,   /* the backward under head mixing (recurrence and sums) */
+  SLSTM_KERNEL_KINDS = 16
 } slstm_kernel_kind;
 
 slstm_status slstm_profile_enable(int on);

@@ -568,7 +568,6 @@ slstm_status backward(const void* P, slstm_dtype P_dtype, const float* R, const 
   return SLSTM_OK;
 }
 
-// head mixing: control block, the warm start's look-back words, the second iterate buffer
 // head mixing with one launch per iteration (an early stop, or more iterations than the
 // one-sweep kernel holds): the warm start or zero iterate, then K iteration kernels; iterate k
 // lives in buf[k % 2], arranged so that iterate max_iters lands in `states`, and the early stop
@@ -597,6 +596,7 @@ hipError_t head_newton_iterations(const void* P, bool bf16, const float* R, cons
   return slstm::launch_select_iterate(ctl, buf[0], buf[1], states, n_state, st);
 }
 
+// head mixing: control block, the warm start's look-back words, the second iterate buffer
 struct HeadLayout {
   size_t ctl, desc, S2, total;
 };
@@ -948,6 +948,43 @@ slstm_status slstm_head_sequential_forward(const void* P, slstm_dtype P_dtype, c
   HIP_TRY(timed(SLSTM_KERNEL_HEAD_SEQUENTIAL, st, [&] {
     return slstm::launch_head_sequential(P, P_dtype == SLSTM_BF16, R, state0, states, h_out, final_state, B, T,
                                          d_h, n_heads, cell_mode_of(fmode), st);
+  }));
+  return SLSTM_OK;
+}
+
+size_t slstm_head_backward_workspace_bytes(int B, int T, int d_h, int n_heads) {
+  if (check_dims(B, T, d_h) != SLSTM_OK || !head_shape_ok(d_h, n_heads) ||
+      !slstm::head_backward_width_supported(d_h / n_heads))
+    return 0;
+  return align_up(slstm::head_backward_part_floats(B, d_h, n_heads) * sizeof(float));
+}
+
+slstm_status slstm_head_backward(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
+                                 const float* states, const float* g_states, const float* g_h,
+                                 const float* g_final, void* dP, slstm_dtype dP_dtype, float* dR, float* dbias,
+                                 float* dstate0, int B, int T, int d_h, int n_heads, slstm_forget fmode,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = '\0';
+  slstm_status s = check_common(P, P_dtype, R, state0, states, nullptr, nullptr, B, T, d_h, fmode);
+  if (s != SLSTM_OK) return s;
+  s = check_heads(d_h, n_heads, R);
+  if (s != SLSTM_OK) return s;
+  if (!slstm::head_backward_width_supported(d_h / n_heads))
+    return fail(SLSTM_EINVAL, "the head-mixing backward takes heads of 8, 16 or 32 units (got %d)", d_h / n_heads);
+  if (dP == nullptr || dR == nullptr) return fail(SLSTM_EINVAL, "dP and dR must not be NULL");
+  if (dP_dtype != SLSTM_F32 && dP_dtype != SLSTM_BF16) return fail(SLSTM_EINVAL, "unknown dP dtype %d", (int)dP_dtype);
+  if (!aligned(dP, 4) || !aligned(dR, 4) || !aligned(dbias, 4) || !aligned(dstate0, 4) || !aligned(g_states, 4) ||
+      !aligned(g_h, 4) || !aligned(g_final, 4))
+    return fail(SLSTM_EINVAL, "dP, the gradients and dR, dbias, dstate0 must be 4-byte aligned");
+  if (workspace == nullptr || !aligned(workspace, kAlign))
+    return fail(SLSTM_EINVAL, "workspace must be non-NULL and 256-byte aligned");
+  const size_t need = slstm_head_backward_workspace_bytes(B, T, d_h, n_heads);
+  if (workspace_bytes < need) return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  HIP_TRY(timed(SLSTM_KERNEL_HEAD_BACKWARD, st, [&] {
+    return slstm::launch_head_backward(P, P_dtype == SLSTM_BF16, R, state0, states, g_states, g_h, g_final, dP,
+                                       dP_dtype == SLSTM_BF16, dR, dbias, dstate0, B, T, d_h, n_heads,
+                                       cell_mode_of(fmode), static_cast<float*>(workspace), st);
   }));
   return SLSTM_OK;
 }

@@ -26,7 +26,7 @@ MAX_ITERS = 64
 KERNELS = {"warm_start": 0, "residual_jacobian": 1, "scan_block4": 2, "update": 3,
            "final_residual": 4, "input_projection": 5, "sequential": 6, "newton_iteration": 7,
            "newton_solve": 8, "backward": 9, "weight_gradient": 10, "input_gradient": 11,
-           "head_iteration": 12, "head_sequential": 13, "head_solve": 14}
+           "head_iteration": 12, "head_sequential": 13, "head_solve": 14, "head_backward": 15}
 
 EXPORTED = [
     "slstm_status_string", "slstm_last_error", "slstm_newton_workspace_bytes",
@@ -38,7 +38,7 @@ EXPORTED = [
     "slstm_input_projection_backward_workspace_bytes", "slstm_input_projection_backward",
     "slstm_newton_forward_varlen", "slstm_sequential_forward_varlen", "slstm_warm_start_varlen",
     "slstm_backward_varlen", "slstm_head_newton_workspace_bytes", "slstm_head_newton_forward",
-    "slstm_head_sequential_forward",
+    "slstm_head_sequential_forward", "slstm_head_backward_workspace_bytes", "slstm_head_backward",
 ]
 
 
@@ -141,6 +141,11 @@ def load(path: str | None = None):
                                             _vp, _sz, _vp, ctypes.POINTER(_Stats)]
     L.slstm_head_sequential_forward.restype = _i
     L.slstm_head_sequential_forward.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _vp]
+    L.slstm_head_backward_workspace_bytes.restype = _sz
+    L.slstm_head_backward_workspace_bytes.argtypes = [_i, _i, _i, _i]
+    L.slstm_head_backward.restype = _i
+    L.slstm_head_backward.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i,
+                                      _i, _vp, _sz, _vp]
     L.slstm_profile_enable.restype = _i
     L.slstm_profile_enable.argtypes = [_i]
     L.slstm_profile_reset.restype = _i
@@ -552,6 +557,51 @@ def head_sequential_forward(P, R, state0=None, forget="exp", states=None, h_out=
                                              _stream(stream))
     _check(status, "slstm_head_sequential_forward")
     return states, h_out
+
+
+def head_backward_workspace_bytes(B: int, T: int, d_h: int, n_heads: int) -> int:
+    return int(load().slstm_head_backward_workspace_bytes(B, T, d_h, n_heads))
+
+
+def head_backward(P, R, states, state0=None, g_states=None, g_h=None, g_final=None, forget="exp",
+                  dP=None, dR=None, dstate0=None, want_dstate0=True, workspace=None, stream=None,
+                  dP_dtype=torch.float32, dbias=None, want_dbias=False, readout="exact"):
+    """Gradients through the head-mixing recurrence at the forward solution ``states``
+    (B,T,4,d_h); arguments as ``backward``, R (4, n_heads, d_head, d_head) with d_head 8, 16 or
+    32. Returns (dP, dR (4, n_heads, d_head, d_head), dstate0 or None), and dbias (4, d_h) last
+    when ``want_dbias`` or a ``dbias`` tensor is given."""
+    L = load()
+    _dev(P, "P", (torch.float32, torch.bfloat16))
+    _dev(R, "R", (torch.float32,))
+    _dev(state0, "state0", (torch.float32,))
+    B, T, d, nh = _head_check(P, R, state0)
+    for name, t, shape in (("states", states, (B, T, 4, d)), ("g_states", g_states, (B, T, 4, d)),
+                           ("g_h", g_h, (B, T, d)), ("g_final", g_final, (B, 4, d))):
+        _dev(t, name, (torch.float32,))
+        if t is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be {shape}, got {tuple(t.shape)}")
+    if dP is None:
+        dP = torch.empty((B, T, 4, d), dtype=dP_dtype, device=P.device)
+    if dR is None:
+        dR = torch.empty(tuple(R.shape), dtype=torch.float32, device=P.device)
+    if want_dbias and dbias is None:
+        dbias = torch.empty((4, d), dtype=torch.float32, device=P.device)
+    if want_dstate0 and dstate0 is None:
+        dstate0 = torch.empty((B, 4, d), dtype=torch.float32, device=P.device)
+    _dev(dP, "dP", (torch.float32, torch.bfloat16))
+    _dev(dR, "dR", (torch.float32,))
+    _dev(dbias, "dbias", (torch.float32,))
+    _dev(dstate0, "dstate0", (torch.float32,))
+    if workspace is None:
+        workspace = alloc_workspace(max(L.slstm_head_backward_workspace_bytes(B, T, d, nh), 256), P.device)
+    status = L.slstm_head_backward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states), _ptr(g_states),
+                                   _ptr(g_h), _ptr(g_final), _ptr(dP), BF16 if dP.dtype == torch.bfloat16 else F32,
+                                   _ptr(dR), _ptr(dbias), _ptr(dstate0), B, T, d, nh, _fmode(forget, readout),
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(status, "slstm_head_backward")
+    if want_dbias or dbias is not None:
+        return dP, dR, dstate0, dbias
+    return dP, dR, dstate0
 
 
 def input_projection_backward_workspace_bytes(B: int, T: int, d_in: int, d_h: int) -> int:
