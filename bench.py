@@ -220,7 +220,8 @@ def cpu_baseline(w, host, lanes_wanted):
 # ---------------------------------------------------------------------------------------
 def head_context(slstm, torch, dev, steps):
     """Head mixing: the Newton solve (one sweep over T with the warm start and K pipelined
-    iterations, no early stop) and the per-head sequential forward on one seeded input."""
+    iterations, no early stop), the per-head sequential forward and the backward at the
+    solution, on one seeded input."""
     from workloads import draw_head_inputs
     B, T, d, nh, K = HEAD["B"], HEAD["T"], HEAD["d"], HEAD["n_heads"], HEAD["K"]
     dh = d // nh
@@ -259,7 +260,31 @@ def head_context(slstm, torch, dev, steps):
     gbs, tfs = sv_bytes / (sv_ms * 1e-3) / 1e9, sv_flops / (sv_ms * 1e-3) / 1e12
     log(f"[bench] head mixing ({nh} heads of {dh}): solve {ms:.3f} ms, one-sweep kernel {sv_ms:.3f} ms "
         f"({sv_ms * 1e3 / T:.3f} us per step), sequential {sq_ms:.3f} ms")
-    del ws, S, H, P, R
+    # the backward at the solution for a loss on h (dL/dh ~ N(0, 1) and a final-state gradient):
+    # bf16 dP, dR per head, dbias, dstate0
+    from workloads import random_cotangents_device
+    _, g_h, g_fin = random_cotangents_device(HEAD["seed"] + 99, B, T, d, dev)
+    dP = torch.empty((B, T, 4, d), dtype=torch.bfloat16, device=dev)
+    bws = slstm.alloc_workspace(slstm.head_backward_workspace_bytes(B, T, d, nh), dev)
+
+    def bwd():
+        slstm.head_backward(P, R, S, None, None, g_h, g_fin, HEAD["forget"], dP=dP, workspace=bws, want_dbias=True)
+
+    bwd()
+    torch.cuda.synchronize()
+    slstm.profile_reset()
+    slstm.profile_enable(True)
+    for _ in range(reps):
+        bwd()
+    torch.cuda.synchronize()
+    slstm.profile_enable(False)
+    bw = slstm.profile_durations("head_backward")
+    bw_ms = sum(bw) / len(bw)
+    bw_bytes = n_e * (16 + 16 + 4 + 8)        # P, S, dL/dh in; bf16 dP out
+    bw_gbs = bw_bytes / (bw_ms * 1e-3) / 1e9
+    log(f"[bench] head mixing backward: {bw_ms:.3f} ms ({bw_ms * 1e3 / T:.3f} us per step), "
+        f"{bw_gbs:.0f} GB/s algorithmic")
+    del ws, S, H, P, R, dP, bws, g_h, g_fin
     torch.cuda.empty_cache()
     return {
         "B": B, "T": T, "d_h": d, "n_heads": nh, "d_head": dh, "forget_gate": HEAD["forget"], "newton_iters": K,
@@ -269,7 +294,13 @@ def head_context(slstm, torch, dev, steps):
         "kernels": {"head_solve": {"avg_ms": round(sv_ms, 4), "us_per_step": round(sv_ms * 1e3 / T, 4),
                                    "bytes_per_launch": sv_bytes, "flops_per_launch": sv_flops},
                     "head_sequential": {"avg_ms": round(sq_ms, 4), "us_per_step": round(sq_ms * 1e3 / T, 4),
-                                        "state_elems_per_s": n_e / (sq_ms * 1e-3)}},
+                                        "state_elems_per_s": n_e / (sq_ms * 1e-3)},
+                    "head_backward": {"avg_ms": round(bw_ms, 4), "us_per_step": round(bw_ms * 1e3 / T, 4),
+                                      "gradients_in": "dL/dh, dL/d final state", "dP": "bf16",
+                                      "bytes_per_launch": bw_bytes, "hbm_view": {"achieved": round(bw_gbs, 1),
+                                                                                  "peak": HBM_PEAK_GBS,
+                                                                                  "unit": "GB/s",
+                                                                                  "frac": round(bw_gbs / HBM_PEAK_GBS, 4)}}},
         "roofline": {"bound": "latency", "kernel": "head_solve",
                      "note": "one workgroup per (batch row, head) walks T; a step's chain bounds it",
                      "hbm_view": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
