@@ -44,6 +44,19 @@ namespace slstm {
 #endif
 constexpr int kFusedBlock = 256;
 constexpr int kFusedTSub = SLSTM_FUSED_TSUB;
+// Rows with few lane groups (packed sequences, or B * d_h of a few thousand lanes) have long
+// look-back chains along T: the scan advances one anchor per memory round trip, and a tile of
+// 4 * TSUB steps sets how far. There the sub-chunks are twice as long (the registers then
+// allow 2 workgroups per compute unit), which halves the chain.
+#ifndef SLSTM_FUSED_LONG_TSUB
+#define SLSTM_FUSED_LONG_TSUB 8
+#endif
+constexpr int kFusedLongTSub = SLSTM_FUSED_LONG_TSUB;
+constexpr int kFewLaneGroups = 64;
+static_assert(kFusedLongTSub >= kFusedTSub, "look-back words are sized for the shorter tiles");
+
+template <int TSUB>
+constexpr int fused_wgs_per_cu() { return TSUB > 4 ? 2 : SLSTM_FUSED_MIN_WAVES; }
 
 template <bool BF16, int TSUB>
 __device__ __forceinline__ void load_sub_chunk(rsrc_t rsP, rsrc_t rsS, unsigned lane_off, unsigned ud,
@@ -82,7 +95,7 @@ __device__ __forceinline__ void step_terms(const CellIn& pv, const float pg[4], 
 }
 
 template <bool BF16, int TSUB, bool PACKED>
-__global__ __launch_bounds__(kFusedBlock, SLSTM_FUSED_MIN_WAVES) void newton_iter_kernel(
+__global__ __launch_bounds__(kFusedBlock, fused_wgs_per_cu<TSUB>()) void newton_iter_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S_in, float* __restrict__ S_out, int T, int d, int n_jt, int n_lg,
     int n_tt, int anchor_stride, int cell_mode, unsigned long long* __restrict__ desc,
@@ -260,15 +273,21 @@ __global__ __launch_bounds__(kFusedBlock, SLSTM_FUSED_MIN_WAVES) void newton_ite
   if (blockIdx.x == 0 && tid == 0) ctl->iters = k_iter + 1;
 }
 
-static void fused_grid(int B, int T, int d, i64& n_jt, i64& n_lg, i64& n_tt) {
-  n_jt = (d + 63) / 64;
-  n_lg = static_cast<i64>(B) * n_jt;
-  n_tt = (T + 4 * kFusedTSub - 1) / (4 * kFusedTSub);
+static int fused_tsub(int B, int d, bool packed) {
+  const i64 n_lg = static_cast<i64>(B) * ((d + 63) / 64);
+  return packed || n_lg < kFewLaneGroups ? kFusedLongTSub : kFusedTSub;
 }
 
+static void fused_grid(int B, int T, int d, int tsub, i64& n_jt, i64& n_lg, i64& n_tt) {
+  n_jt = (d + 63) / 64;
+  n_lg = static_cast<i64>(B) * n_jt;
+  n_tt = (T + 4 * tsub - 1) / (4 * tsub);
+}
+
+// sized for the shorter tiles (the most tiles), whichever the launch picks
 size_t fused_desc_words(int B, int T, int d) {
   i64 n_jt, n_lg, n_tt;
-  fused_grid(B, T, d, n_jt, n_lg, n_tt);
+  fused_grid(B, T, d, kFusedTSub, n_jt, n_lg, n_tt);
   return static_cast<size_t>(n_tt * kLookBackWords * n_lg * 64);
 }
 
@@ -277,22 +296,29 @@ hipError_t launch_newton_iteration(const void* P, bool p_bf16, const float* R, c
                                    int cell_mode, unsigned long long* desc, unsigned int* tickets,
                                    uint32_t epoch, Control* ctl, int k_iter, float tol,
                                    hipStream_t stream, Seqs seqs) {
+  const bool packed = seqs.cu != nullptr;
+  const int tsub = fused_tsub(B, d, packed);
   i64 n_jt, n_lg, n_tt;
-  fused_grid(B, T, d, n_jt, n_lg, n_tt);
+  fused_grid(B, T, d, tsub, n_jt, n_lg, n_tt);
   const i64 blocks = n_lg * n_tt;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
-  const int stride = look_back_anchor_stride(n_lg, SLSTM_FUSED_MIN_WAVES);
+  const int stride = look_back_anchor_stride(
+      n_lg, tsub == kFusedTSub ? fused_wgs_per_cu<kFusedTSub>() : fused_wgs_per_cu<kFusedLongTSub>());
   // packed rows are few lane groups along a long T: anchors every 4 tiles (measured best
   // between 1 and 8 over short and long sequence mixes)
   const int stride_used = seqs.cu != nullptr ? kPackedAnchorStride : stride;
   const int n_ctr = ticket_counters(n_lg);
   const dim3 grid(static_cast<unsigned>(blocks));
   const int sig = cell_mode;
-#define SLSTM_FUSED_LAUNCH(BF, PK)                                                                   \
-  newton_iter_kernel<BF, kFusedTSub, PK><<<grid, kFusedBlock, 0, stream>>>(                          \
+#define SLSTM_FUSED_LAUNCH_T(BF, TS, PK)                                                             \
+  newton_iter_kernel<BF, TS, PK><<<grid, kFusedBlock, 0, stream>>>(                                  \
       P, R, state0, S_in, S_out, T, d, static_cast<int>(n_jt), static_cast<int>(n_lg),                \
       static_cast<int>(n_tt), stride_used, sig, desc, tickets, n_ctr, epoch, ctl, k_iter, tol, seqs.cu, seqs.n, seqs.tab)
-  const bool packed = seqs.cu != nullptr;
+#define SLSTM_FUSED_LAUNCH(BF, PK)                                         \
+  do {                                                                     \
+    if (tsub == kFusedTSub) SLSTM_FUSED_LAUNCH_T(BF, kFusedTSub, PK);      \
+    else SLSTM_FUSED_LAUNCH_T(BF, kFusedLongTSub, PK);                     \
+  } while (0)
   if (p_bf16) {
     if (packed) SLSTM_FUSED_LAUNCH(true, true);
     else SLSTM_FUSED_LAUNCH(true, false);
@@ -301,6 +327,7 @@ hipError_t launch_newton_iteration(const void* P, bool p_bf16, const float* R, c
     else SLSTM_FUSED_LAUNCH(false, false);
   }
 #undef SLSTM_FUSED_LAUNCH
+#undef SLSTM_FUSED_LAUNCH_T
   return hipGetLastError();
 }
 
