@@ -55,7 +55,10 @@ struct Seqs {
 // cu[s] <= 4k < cu[s+1] (the largest s with cu[s] <= 4k); ceil(T / 4) entries
 constexpr int kSeqTabShift = 2;
 // look-back anchor stride of the packed scan kernels
-constexpr int kPackedAnchorStride = 4;
+#ifndef SLSTM_PACKED_ANCHOR_STRIDE
+#define SLSTM_PACKED_ANCHOR_STRIDE 2
+#endif
+constexpr int kPackedAnchorStride = SLSTM_PACKED_ANCHOR_STRIDE;
 
 struct SeqCursor {
   const int* cu;
