@@ -304,9 +304,9 @@ hipError_t launch_newton_iteration(const void* P, bool p_bf16, const float* R, c
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const int stride = look_back_anchor_stride(
       n_lg, tsub == kFusedTSub ? fused_wgs_per_cu<kFusedTSub>() : fused_wgs_per_cu<kFusedLongTSub>());
-  // packed rows are few lane groups along a long T: anchors every 4 tiles (measured best
-  // between 1 and 8 over short and long sequence mixes)
-  const int stride_used = seqs.cu != nullptr ? kPackedAnchorStride : stride;
+  // packed rows and other rows of few lane groups along a long T (the long sub-chunks) take
+  // the packed anchor stride, measured best there
+  const int stride_used = packed || tsub != kFusedTSub ? kPackedAnchorStride : stride;
   const int n_ctr = ticket_counters(n_lg);
   const dim3 grid(static_cast<unsigned>(blocks));
   const int sig = cell_mode;
