@@ -229,3 +229,27 @@ def test_head_argument_checks(lib):
     s = lib.slstm_head_sequential_forward(ctypes.c_void_p(256), 0, ctypes.c_void_p(256), None, ctypes.c_void_p(256),
                                           None, None, 2, 64, 64, 5, 0, None)
     assert s == slstm.EINVAL
+
+
+def test_head_backward_argument_checks(lib):
+    # widths: 8, 16, 32 only (a block row, column and dR row per lane must fit in registers)
+    assert lib.slstm_head_backward_workspace_bytes(2, 64, 64, 2) > 0
+    assert lib.slstm_head_backward_workspace_bytes(2, 64, 128, 2) == 0      # d_head 64
+    assert lib.slstm_head_backward_workspace_bytes(2, 64, 64, 3) == 0
+    args = dict(P=ctypes.c_void_p(256), dt=0, R=ctypes.c_void_p(256), s0=None, S=ctypes.c_void_p(256), gs=None,
+                gh=None, gf=None, dP=ctypes.c_void_p(256), dpt=0, dR=ctypes.c_void_p(256), db=None, d0=None, B=2,
+                T=64, d=64, nh=2, fm=0, ws=ctypes.c_void_p(4096), wsb=1 << 30, stream=None)
+
+    def call(**kw):
+        a = dict(args)
+        a.update(kw)
+        return lib.slstm_head_backward(*a.values())
+    assert call(d=128) == slstm.EINVAL
+    assert "8, 16 or 32" in lib.slstm_last_error().decode()
+    assert call(nh=3) == slstm.EINVAL
+    assert call(dP=None) == slstm.EINVAL
+    assert call(dR=None) == slstm.EINVAL
+    assert call(dpt=7) == slstm.EINVAL
+    assert call(R=ctypes.c_void_p(260)) == slstm.EINVAL
+    assert call(ws=None) == slstm.EINVAL
+    assert call(wsb=100) == slstm.EWORKSPACE
