@@ -148,65 +148,6 @@ __device__ __forceinline__ void cell_step(const CellIn& pv, float pz, float pi, 
   }
 }
 
-// One step from full gate pre-activations x[4] = (z~, i~, f~, o~) (head mixing: the recurrent
-// term is already in them). Writes the next state s[4], the derivatives of the next state with
-// respect to the unit's own previous c, n, m in A[4*row + col] for col 0..2 (col 3 is not
-// written), and the gate Jacobian G[4*row + gate] = d s[row] / d x[gate]. These are the
-// coefficients of cell_step's Jacobian with its four recurrent weights left free: there the h'
-// column is G (r_z, r_i, r_f, r_o).
-__device__ __forceinline__ void cell_step_gates(const CellIn& pv, const float x[4], bool sig_forget,
-                                                bool floored, float s[4], float A[16], float G[16]) {
-  const float z = tanh_fast(x[0]);
-  const float it = x[1];
-  const float o = sigmoidf(x[3]);
-  float lf, dlf;
-  if (sig_forget) {
-    lf = log_sigmoidf(x[2]);
-    dlf = sigmoidf(-x[2]);
-  } else {
-    lf = x[2];
-    dlf = 1.0f;
-  }
-  const float a = lf + pv.m;
-  const bool beta = a >= it;
-  const float m = beta ? a : it;
-  const float e = exp_fast(-fabsf(a - it));
-  const float ig = beta ? e : 1.0f;
-  const float fg = beta ? 1.0f : e;
-  const float c = fmaf(fg, pv.c, ig * z);
-  const float n = fmaf(fg, pv.n, ig);
-  const Readout rdn = readout(n, m, floored);
-  const float rn = rdn.rD;
-  const float h = o * c * rn;
-  s[0] = c;
-  s[1] = n;
-  s[2] = m;
-  s[3] = h;
-  const float c_m = e * (beta ? -z : pv.c);
-  const float n_m = e * (beta ? -1.0f : pv.n);
-  const float q1 = o * rn;
-  const float q2 = h * rn;
-  const float qn = floored ? q2 * rdn.dn : q2;
-  const float qm = floored ? q2 * rdn.dm : 0.0f;
-  const float mm = beta ? 1.0f : 0.0f;  // dm/dm'
-  A[0] = fg;     A[1] = 0.0f;   A[2] = c_m;
-  A[4] = 0.0f;   A[5] = fg;     A[6] = n_m;
-  A[8] = 0.0f;   A[9] = 0.0f;   A[10] = mm;
-  A[12] = q1 * fg;
-  A[13] = -qn * fg;
-  A[14] = fmaf(q1, c_m, fmaf(-qn, n_m, -qm * mm));
-  // gate columns (z, i, f, o); the h row by the quotient rule through c, n and m
-  const float gc_z = ig * fmaf(-z, z, 1.0f);
-  const float gm_i = beta ? 0.0f : 1.0f, gm_f = beta ? dlf : 0.0f;
-  G[0] = gc_z;   G[1] = -c_m;   G[2] = c_m * dlf;   G[3] = 0.0f;
-  G[4] = 0.0f;   G[5] = -n_m;   G[6] = n_m * dlf;   G[7] = 0.0f;
-  G[8] = 0.0f;   G[9] = gm_i;   G[10] = gm_f;       G[11] = 0.0f;
-  G[12] = q1 * gc_z;
-  G[13] = fmaf(q1, G[1], fmaf(-qn, G[5], -qm * gm_i));
-  G[14] = fmaf(q1, G[2], fmaf(-qn, G[6], -qm * gm_f));
-  G[15] = (c * rn) * fmaf(-o, o, o);
-}
-
 // Vector-Jacobian product of one step at the state before it (pv) and its pre-activations:
 // given lam = dL/ds for the state the step produces, returns dx = dL/dx~ for the gate
 // pre-activations (z, i, f, o) (= dL/dP of the step) and lam_prev = dL/ds' = A^T lam. The

@@ -14,7 +14,7 @@
 // head_iter_kernel: one Newton iteration. Residual F_t = s_t - f(s_{t-1}) at the iterate and
 //   the linear solve Delta_t = A_t Delta_{t-1} - F_t with the Jacobian applied in factored form,
 //     A_t Delta = A_own (Delta c', Delta n', Delta m') + G (R_g Delta h')_g
-//   (A_own the unit's own-state columns, G = d s / d x~ the gate Jacobian; see cell_step_gates):
+//   (A_own the unit's own-state columns, G = d s / d x~ the gate Jacobian; see cell_step_lin):
 //   the (4 d_head)^2 block is never formed, and the block product costs d_head FMAs per lane.
 //   The solve is a recurrence along T for each (batch row, head), like the chain form of the
 //   channelwise solver; the iterates are those of the oracle's dense block forward
@@ -159,8 +159,9 @@ __global__ __launch_bounds__(4 * DH) void head_iter_kernel(const void* __restric
     float xs[4], ps[4];
     quad_gather(x, xs);
     quad_gather(prev, ps);
-    float s[4], A[16], G[16];
-    cell_step_gates(CellIn{ps[0], ps[1], ps[2], 0.0f}, xs, sig, floored, s, A, G);
+    float s[4];
+    CellLin L;
+    cell_step_lin(CellIn{ps[0], ps[1], ps[2], 0.0f}, xs, sig, floored, s, L);
     const float sg = sel(s);
     const float F = sin - sg;
     emax = res_max(emax, F);
@@ -169,13 +170,10 @@ __global__ __launch_bounds__(4 * DH) void head_iter_kernel(const void* __restric
     float ys[4], ds[4];
     quad_gather(y, ys);
     quad_gather(dprev, ds);
-    // row g of A_own and of G (rows are slots, 4 entries each)
-    float delta = sel(A[0], A[4], A[8], A[12]) * ds[0];
-    delta = fmaf(sel(A[1], A[5], A[9], A[13]), ds[1], delta);
-    delta = fmaf(sel(A[2], A[6], A[10], A[14]), ds[2], delta);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) delta = fmaf(sel(G[q], G[4 + q], G[8 + q], G[12 + q]), ys[q], delta);
-    delta -= F;
+    // slot g of A_own Delta' + G (R Delta h')
+    float dv[4];
+    cell_jvp(L, ds, ys, dv);
+    const float delta = sel(dv) - F;
     const float sout = sin + delta;
     S_out[base + static_cast<i64>(t) * 4 * dd] = sout;
     if constexpr (LAST) {

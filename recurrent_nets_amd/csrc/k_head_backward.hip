@@ -108,13 +108,11 @@ __global__ __launch_bounds__(4 * DH) void head_backward_kernel(
       quad_gather(p + block_dot<DH>(row, hb), xs);
       quad_gather(sp, ps);
       quad_gather(lam, ls);
-      float s[4], A[16], G[16];
-      cell_step_gates(CellIn{ps[0], ps[1], ps[2], 0.0f}, xs, sig, floored, s, A, G);
-      // dP_t for gate g: column g of G against lam
-      float dx = sel(G[0], G[1], G[2], G[3]) * ls[0];
-      dx = fmaf(sel(G[4], G[5], G[6], G[7]), ls[1], dx);
-      dx = fmaf(sel(G[8], G[9], G[10], G[11]), ls[2], dx);
-      dx = fmaf(sel(G[12], G[13], G[14], G[15]), ls[3], dx);
+      float s[4], dxv[4], dpv[3];
+      CellLin L;
+      cell_step_lin(CellIn{ps[0], ps[1], ps[2], 0.0f}, xs, sig, floored, s, L);
+      cell_vjp_lin(L, ls, dxv, dpv);
+      const float dx = sel(dxv);  // dP_t for gate g
       out[u] = dx;
       const float dxm = real ? dx : 0.0f;
       const float4* h4 = reinterpret_cast<const float4*>(hb);
@@ -127,11 +125,7 @@ __global__ __launch_bounds__(4 * DH) void head_backward_kernel(
         dr[4 * k + 3] = fmaf(dxm, hv.w, dr[4 * k + 3]);
       }
       db += dxm;
-      // own-state columns of J^T lam: column g of A_own (g < 3)
-      float la = sel(A[0], A[1], A[2], 0.0f) * ls[0];
-      la = fmaf(sel(A[4], A[5], A[6], 0.0f), ls[1], la);
-      la = fmaf(sel(A[8], A[9], A[10], 0.0f), ls[2], la);
-      la = fmaf(sel(A[12], A[13], A[14], 0.0f), ls[3], la);
+      const float la = sel(dpv[0], dpv[1], dpv[2], 0.0f);  // own-state columns of J^T lam (g < 3)
       dxbuf[r & 1][g][i] = dx;
       *h_slot(&hbuf[(r + 1) & 1][i]) = sp_next;
       head_lds_barrier();

@@ -23,8 +23,11 @@
 
 namespace slstm {
 
+// One wave per SIMD is this kernel's occupancy at the sizes it serves (a workgroup per batch
+// row and head); saying so lets the scheduler keep a step's LDS reads in flight together
+// instead of trading them for registers.
 template <int DH, bool BF16, int CM, int K>
-__global__ __launch_bounds__(4 * DH) void head_solve_kernel(const void* __restrict__ P, const float* __restrict__ R,
+__global__ __launch_bounds__(4 * DH) __attribute__((amdgpu_waves_per_eu(1, 1))) void head_solve_kernel(const void* __restrict__ P, const float* __restrict__ R,
                                                             const float* __restrict__ state0, float* __restrict__ S,
                                                             float* __restrict__ h_out, int T, int d, int nh,
                                                             Control* __restrict__ ctl, int zero_init) {
@@ -93,20 +96,18 @@ __global__ __launch_bounds__(4 * DH) void head_solve_kernel(const void* __restri
 #pragma unroll
     for (int k = 0; k < K; ++k) {
       if (k > 0) quad_gather(sp[k], ps);  // iterate k at t - 1
-      float s[4], A[16], G[16];
-      cell_step_gates(CellIn{ps[0], ps[1], ps[2], 0.0f}, xs, sig, floored, s, A, G);
+      float s[4];
+      CellLin L;
+      cell_step_lin(CellIn{ps[0], ps[1], ps[2], 0.0f}, xs, sig, floored, s, L);
       const float F = cur - sel(s);
       const unsigned int em = res_max(emax[k], F);
       emax[k] = real ? em : emax[k];
       float ys[4], ds[4];
       quad_gather(y[k], ys);
       quad_gather(dp[k], ds);
-      float delta = sel(A[0], A[4], A[8], A[12]) * ds[0];
-      delta = fmaf(sel(A[1], A[5], A[9], A[13]), ds[1], delta);
-      delta = fmaf(sel(A[2], A[6], A[10], A[14]), ds[2], delta);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) delta = fmaf(sel(G[q], G[4 + q], G[8 + q], G[12 + q]), ys[q], delta);
-      delta -= F;
+      float dv[4];
+      cell_jvp(L, ds, ys, dv);
+      const float delta = sel(dv) - F;
       *h_slot(&dhbuf[k][(t + 1) & 1][i]) = delta;
       sp[k] = cur;
       dp[k] = delta;
