@@ -696,24 +696,39 @@ def cell_head(prev, p, R, forget, with_jacobian=False):
     return nxt, J.reshape(lead + (nh, 4 * dh, 4 * dh))
 
 
-def sequential_head(P, R, state0, forget):
-    """s_t = f(s_{t-1}) under head mixing, t = 1..T, from state0 (zeros when None)."""
+def sequential_head(P, R, state0, forget, cu_seqlens=None):
+    """s_t = f(s_{t-1}) under head mixing, t = 1..T, from state0 (zeros when None). Packed
+    (cu_seqlens, B = 1, state0 (S, 4, d)): the state restarts from state0[s] at the first step
+    of sequence s, as in ``sequential``."""
     P = np.asarray(P, dtype=np.float64)
     B, T, _, d = P.shape
     S = np.empty((B, T, 4, d))
-    prev = _state0(state0, B, d)
+    if cu_seqlens is None:
+        starts, s0 = {}, None
+        prev = _state0(state0, B, d)
+    else:
+        starts = sequence_starts(cu_seqlens, T)
+        s0 = _state0(state0, len(cu_seqlens) - 1, d)
+        prev = np.zeros((B, 4, d))
     with np.errstate(all="ignore"):
         for t in range(T):
+            if t in starts:
+                prev = s0[starts[t]][None]
             prev = cell_head(prev, P[:, t], R, forget)
             S[:, t] = prev
     return S
 
 
-def residual_head(S, P, R, state0, forget, with_jacobian=True):
-    """F_t = s_t - f(s_{t-1}) and the dense per-head Jacobians J_t, t = 1..T."""
-    prev = _shifted(S, state0)
+def residual_head(S, P, R, state0, forget, with_jacobian=True, cu_seqlens=None):
+    """F_t = s_t - f(s_{t-1}) and the dense per-head Jacobians J_t, t = 1..T. Packed: the state
+    before a sequence start is that sequence's state0 (data, not an unknown), so J is zero there
+    (the head flag of the segmented scan)."""
+    prev = _shifted(S, state0, cu_seqlens)
     if with_jacobian:
         fs, J = cell_head(prev, P, R, forget, with_jacobian=True)
+        if cu_seqlens is not None:
+            for t in sequence_starts(cu_seqlens, S.shape[1]):
+                J[:, t] = 0.0
         return S - fs, J
     return S - cell_head(prev, P, R, forget), None
 
@@ -729,14 +744,15 @@ def forward_substitution_head(J, rhs, nh):
     return from_head_vectors(x, nh)
 
 
-def newton_head(P, R, state0, forget, max_iters, tol=0.0, init=INIT_WARM):
+def newton_head(P, R, state0, forget, max_iters, tol=0.0, init=INIT_WARM, cu_seqlens=None):
     """Newton solve under head mixing: the steps of ``newton`` with the dense per-head
-    Jacobians (the warm start drops R h' and is the channelwise one)."""
+    Jacobians (the warm start drops R h' and is the channelwise one). Packed: cu_seqlens as in
+    ``sequential_head``; one residual maximum over the whole pack decides the stop."""
     P = np.asarray(P, dtype=np.float64)
     B, T, _, d = P.shape
     R, nh, _ = _head_shape(R, d)
     if init == INIT_WARM:
-        S = warm_start(P, state0, forget)
+        S = warm_start(P, state0, forget, cu_seqlens)
     elif init == INIT_ZERO:
         S = np.zeros((B, T, 4, d))
     else:
@@ -745,7 +761,7 @@ def newton_head(P, R, state0, forget, max_iters, tol=0.0, init=INIT_WARM):
     with np.errstate(all="ignore"):
         stopped = False
         for _ in range(max_iters):
-            F, J = residual_head(S, P, R, state0, forget)
+            F, J = residual_head(S, P, R, state0, forget, cu_seqlens=cu_seqlens)
             e = max_abs(F)
             stats.max_abs_F.append(e)
             stopped = tol > 0.0 and e < tol  # the stop rule of ``newton``
@@ -754,13 +770,13 @@ def newton_head(P, R, state0, forget, max_iters, tol=0.0, init=INIT_WARM):
             S = S + forward_substitution_head(J, -F, nh)
             stats.iters += 1
         if not stopped:
-            F, _ = residual_head(S, P, R, state0, forget, with_jacobian=False)
+            F, _ = residual_head(S, P, R, state0, forget, with_jacobian=False, cu_seqlens=cu_seqlens)
             stats.max_abs_F.append(max_abs(F))
     stats.converged, stats.diverged, stats.nonfinite = newton_flags(stats.max_abs_F[-1], tol)
     return S, stats
 
 
-def backward_head(P, R, state0, S, g, forget, g_final=None, return_adjoint=False):
+def backward_head(P, R, state0, S, g, forget, g_final=None, return_adjoint=False, cu_seqlens=None):
     """Gradients through the recurrence under head mixing, for a loss whose direct derivative
     with respect to the states is g = dL/dS (and g_final = dL/d(final state), added at the last
     step). P, S, g (B, T, 4, d); R (4, n_heads, d_head, d_head); state0 (B, 4, d) or None.
@@ -772,20 +788,32 @@ def backward_head(P, R, state0, S, g, forget, g_final=None, return_adjoint=False
     and per step the gate vector-Jacobian product dP_t = G_t^T lam_t (G_t = d s_t / d x~_t, the
     same for every mixing, since x~ enters the cell the same way); h' enters x~ through R_g h',
     so dR[g, a, i, k] = sum over b and t of dP_t[g, a d_head + i] h_{t-1}[a d_head + k], and
-    dstate0 = J_1^T lam_1.
+    dstate0 = J_1^T lam_1. Packed (cu_seqlens, B = 1): as ``backward``, the adjoint of the state
+    before a sequence start is dstate0[s] and nothing crosses the start; g_final (S, 4, d) is
+    added at each sequence's last step, or passed to dstate0 by an empty sequence.
     """
     P = np.asarray(P, dtype=np.float64)
     S = np.asarray(S, dtype=np.float64)
     g = np.array(g, dtype=np.float64)
     B, T, _, d = P.shape
     R, nh, dh = _head_shape(R, d)
-    prev = _shifted(S, state0)
+    prev = _shifted(S, state0, cu_seqlens)
+    starts = {} if cu_seqlens is None else sequence_starts(cu_seqlens, T)
+    dstate0 = np.zeros((B if cu_seqlens is None else len(cu_seqlens) - 1, 4, d))
     if g_final is not None:
-        g[:, T - 1] += np.asarray(g_final, dtype=np.float64)
+        g_final = np.asarray(g_final, dtype=np.float64)
+        if cu_seqlens is None:
+            g[:, T - 1] += g_final
+        else:
+            cu = [int(v) for v in cu_seqlens]
+            for q in range(len(cu) - 1):
+                if cu[q + 1] > cu[q]:
+                    g[0, cu[q + 1] - 1] += g_final[q]
+                else:
+                    dstate0[q] += g_final[q]
     zero_r = np.zeros((4, d))
     dP = np.empty_like(P)
     dR = np.zeros((4, nh, dh, dh))
-    dstate0 = np.zeros((B, 4, d))
     lam_all = np.empty_like(S)
     lam = g[:, T - 1].copy()
     for t in range(T - 1, -1, -1):
@@ -797,10 +825,14 @@ def backward_head(P, R, state0, S, g, forget, g_final=None, return_adjoint=False
         dP[:, t] = delta
         dR += np.einsum("bgai,bak->gaik", delta.reshape(B, 4, nh, dh), prev[:, t, H].reshape(B, nh, dh))
         lam_prev = from_head_vectors(np.einsum("bauv,bau->bav", J, head_vectors(lam, nh)), nh)
+        if cu_seqlens is None:
+            if t == 0:
+                dstate0 += lam_prev
+        elif t in starts:
+            dstate0[starts[t]] += lam_prev[0]
+            lam_prev = np.zeros_like(lam_prev)
         if t > 0:
             lam = g[:, t - 1] + lam_prev
-        else:
-            dstate0 = lam_prev
     if return_adjoint:
         return dP, dR, dstate0, lam_all
     return dP, dR, dstate0

@@ -751,4 +751,67 @@ def pin_head_backward_width_one_is_channelwise(ref):
     np.testing.assert_allclose(d0, c0, rtol=1e-12, atol=1e-13)
 
 
+def _head_pack(seed, lengths, nh=2, dh=3):
+    rng = np.random.default_rng(seed)
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    T, n, d = int(cu[-1]), len(lengths), nh * dh
+    P = rng.standard_normal((1, T, 4, d))
+    P[:, :, 2] += 2.0
+    R = rng.uniform(-0.4, 0.4, (4, nh, dh, dh))
+    s0 = np.zeros((n, 4, d))
+    s0[:, 0] = rng.uniform(-0.5, 0.5, (n, d))
+    s0[:, 1] = rng.uniform(0.5, 2.0, (n, d))
+    s0[:, 2] = rng.uniform(-1.0, 1.0, (n, d))
+    s0[:, 3] = rng.uniform(-0.5, 0.5, (n, d))
+    return P, R, s0, cu
+
+
+def pin_head_packed_equals_separate(ref):
+    """Packed head mixing is the sequences solved one by one: the sequential forward, Newton at
+    a fixed count, final states; with an early stop the pack stops once for all, at the
+    iterate each sequence reaches in that many iterations."""
+    lengths = [3, 0, 5, 1, 4]
+    P, R, s0, cu = _head_pack(102, lengths)
+    for forget in ("exp", "sigmoid"):
+        S = ref.sequential_head(P, R, s0, forget, cu_seqlens=cu)
+        Sn, st = ref.newton_head(P, R, s0, forget, 3, cu_seqlens=cu)
+        Se, ste = ref.newton_head(P, R, s0, forget, 8, tol=1e-6, cu_seqlens=cu)
+        assert ste.converged and ste.iters < 8
+        for q in range(len(lengths)):
+            a, b = int(cu[q]), int(cu[q + 1])
+            if a == b:
+                continue
+            Pq = P[:, a:b]
+            np.testing.assert_allclose(S[:, a:b], ref.sequential_head(Pq, R, s0[q:q + 1], forget), rtol=1e-13, atol=1e-14)
+            Sq, _ = ref.newton_head(Pq, R, s0[q:q + 1], forget, 3)
+            np.testing.assert_allclose(Sn[:, a:b], Sq, rtol=1e-11, atol=1e-12)
+            Sq, _ = ref.newton_head(Pq, R, s0[q:q + 1], forget, ste.iters)
+            np.testing.assert_allclose(Se[:, a:b], Sq, rtol=1e-11, atol=1e-12)
+        fin = ref.final_states(S, s0, cu)
+        np.testing.assert_array_equal(fin[1], s0[1])   # the empty sequence keeps its state0
+
+
+def pin_head_packed_backward(ref):
+    """The packed head backward is the per-sequence backwards: dP and dstate0 per sequence, dR
+    summed; an empty sequence passes its final-state gradient to dstate0."""
+    lengths = [4, 0, 3, 6]
+    P, R, s0, cu = _head_pack(103, lengths)
+    rng = np.random.default_rng(104)
+    g = rng.standard_normal(P.shape)
+    gf = rng.standard_normal(s0.shape)
+    S = ref.sequential_head(P, R, s0, "sigmoid", cu_seqlens=cu)
+    dP, dR, d0 = ref.backward_head(P, R, s0, S, g, "sigmoid", g_final=gf, cu_seqlens=cu)
+    dR_sum = np.zeros_like(dR)
+    for q in range(len(lengths)):
+        a, b = int(cu[q]), int(cu[q + 1])
+        if a == b:
+            np.testing.assert_array_equal(d0[q], gf[q])
+            continue
+        pq, rq, dq = ref.backward_head(P[:, a:b], R, s0[q:q + 1], S[:, a:b], g[:, a:b], "sigmoid", g_final=gf[q:q + 1])
+        np.testing.assert_allclose(dP[:, a:b], pq, rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(d0[q], dq[0], rtol=1e-12, atol=1e-13)
+        dR_sum += rq
+    np.testing.assert_allclose(dR, dR_sum, rtol=1e-12, atol=1e-13)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -70,6 +70,9 @@ MUTATIONS = [
      'np.einsum("bauv,bav->bau", J, head_vectors(lam, nh))'),
     ("head backward: transposed dR", 'np.einsum("bgai,bak->gaik", delta.reshape', 'np.einsum("bgai,bak->gaki", delta.reshape'),
     ("head backward: dR against h_t", "prev[:, t, H].reshape(B, nh, dh))", "S[:, t, H].reshape(B, nh, dh))"),
+    ('head packed: no restart at a start', '            if t in starts:\n                prev = s0[starts[t]][None]\n', ''),
+    ('head packed: Jacobian not cut at a start', '                J[:, t] = 0.0\n', '                pass\n'),
+    ('head packed backward: adjoint leaks across a start', '        elif t in starts:\n            dstate0[starts[t]] += lam_prev[0]\n            lam_prev = np.zeros_like(lam_prev)\n', '        elif t in starts:\n            dstate0[starts[t]] += lam_prev[0]\n'),
     ("head solve: transposed block", 'np.einsum("bauv,bav->bau", J[:, t], x[:, t - 1])',
      'np.einsum("bavu,bav->bau", J[:, t], x[:, t - 1])'),
 ]
