@@ -353,6 +353,12 @@ slstm_status slstm_backward_varlen(const void* P, slstm_dtype P_dtype, const flo
  * (batch row, head) walks T backwards; dR and dbias are added over the batch in a fixed order
  * from per-row partial sums in the workspace (slstm_head_backward_workspace_bytes; 0 if the
  * sizes are invalid), so results are reproducible bit for bit.
+ * The _varlen forms take packed sequences as the channelwise _varlen calls do (one row of T steps,
+ * cu_seqlens (n_seqs + 1 device ints), state0, final_state, g_final and dstate0 per sequence):
+ * a sequence start takes state0[s] as the state before it, its Jacobian is zero for the Newton
+ * solve and the adjoint does not cross it. Packed Newton runs the warm start and one kernel per
+ * iteration (never the one-sweep kernel); the workspace sizes are those of the unpacked calls
+ * with B = 1.
  */
 size_t slstm_head_newton_workspace_bytes(int B, int T, int d_h, int n_heads);
 slstm_status slstm_head_newton_forward(const void* P, slstm_dtype P_dtype, const float* R,
@@ -365,6 +371,17 @@ slstm_status slstm_head_sequential_forward(const void* P, slstm_dtype P_dtype, c
                                            const float* state0, float* states, float* h_out,
                                            float* final_state, int B, int T, int d_h, int n_heads,
                                            slstm_forget fmode, void* stream);
+slstm_status slstm_head_newton_forward_varlen(const void* P, slstm_dtype P_dtype, const float* R,
+                                              const float* state0, const int* cu_seqlens, int n_seqs,
+                                              float* states, float* h_out, float* final_state, int T,
+                                              int d_h, int n_heads, slstm_forget fmode, int max_iters,
+                                              float tol, slstm_init init, void* workspace,
+                                              size_t workspace_bytes, void* stream,
+                                              slstm_newton_stats* stats);
+slstm_status slstm_head_sequential_forward_varlen(const void* P, slstm_dtype P_dtype, const float* R,
+                                                  const float* state0, const int* cu_seqlens, int n_seqs,
+                                                  float* states, float* h_out, float* final_state, int T,
+                                                  int d_h, int n_heads, slstm_forget fmode, void* stream);
 size_t slstm_head_backward_workspace_bytes(int B, int T, int d_h, int n_heads);
 slstm_status slstm_head_backward(const void* P, slstm_dtype P_dtype, const float* R,
                                  const float* state0, const float* states, const float* g_states,
@@ -372,6 +389,13 @@ slstm_status slstm_head_backward(const void* P, slstm_dtype P_dtype, const float
                                  slstm_dtype dP_dtype, float* dR, float* dbias, float* dstate0, int B,
                                  int T, int d_h, int n_heads, slstm_forget fmode, void* workspace,
                                  size_t workspace_bytes, void* stream);
+slstm_status slstm_head_backward_varlen(const void* P, slstm_dtype P_dtype, const float* R,
+                                        const float* state0, const int* cu_seqlens, int n_seqs,
+                                        const float* states, const float* g_states, const float* g_h,
+                                        const float* g_final, void* dP, slstm_dtype dP_dtype, float* dR,
+                                        float* dbias, float* dstate0, int T, int d_h, int n_heads,
+                                        slstm_forget fmode, void* workspace, size_t workspace_bytes,
+                                        void* stream);
 
 /*
  * Kernel timing with HIP events recorded on the launching stream around every kernel the

@@ -575,11 +575,11 @@ slstm_status backward(const void* P, slstm_dtype P_dtype, const float* R, const 
 hipError_t head_newton_iterations(const void* P, bool bf16, const float* R, const float* state0, float* states,
                                   float* h_out, int B, int T, int d_h, int n_heads, int cm, int max_iters, float tol,
                                   slstm_init init, Control* ctl, unsigned long long* desc, float* other,
-                                  hipStream_t st) {
+                                  hipStream_t st, slstm::Seqs seqs) {
   const i64 n_state = static_cast<i64>(B) * T * 4 * d_h;
   float* buf[2] = {(max_iters % 2 == 0) ? states : other, (max_iters % 2 == 0) ? other : states};
   if (init == SLSTM_INIT_WARM) {
-    HIP_RET(launch_warm(P, bf16, state0, buf[0], B, T, d_h, cm, false, desc, ctl, st, {}));
+    HIP_RET(launch_warm(P, bf16, state0, buf[0], B, T, d_h, cm, false, desc, ctl, st, seqs));
   } else {
     HIP_RET(slstm::launch_zero(buf[0], n_state, st));
   }
@@ -587,7 +587,7 @@ hipError_t head_newton_iterations(const void* P, bool bf16, const float* R, cons
     const bool last = k + 1 == max_iters;
     HIP_RET(timed(SLSTM_KERNEL_HEAD_ITERATION, st, [&] {
       return slstm::launch_head_iteration(P, bf16, R, state0, buf[k % 2], buf[(k + 1) % 2], last ? h_out : nullptr,
-                                          B, T, d_h, n_heads, cm, ctl, k, tol, last, st);
+                                          B, T, d_h, n_heads, cm, ctl, k, tol, last, st, seqs);
     }));
   }
   // the last launch formed the final residual and h; what remains of the stop rule is the check
@@ -598,7 +598,7 @@ hipError_t head_newton_iterations(const void* P, bool bf16, const float* R, cons
 
 // head mixing: control block, the warm start's look-back words, the second iterate buffer
 struct HeadLayout {
-  size_t ctl, desc, S2, total;
+  size_t ctl, desc, S2, tab, total;
 };
 
 HeadLayout head_layout(int B, int T, int d) {
@@ -606,7 +606,8 @@ HeadLayout head_layout(int B, int T, int d) {
   L.ctl = 0;
   L.desc = align_up(slstm::kControlBytes);
   L.S2 = align_up(L.desc + slstm::warm_desc_words(B, T, d) * 8);
-  L.total = align_up(L.S2 + static_cast<size_t>(B) * T * 4 * d * sizeof(float));
+  L.tab = align_up(L.S2 + static_cast<size_t>(B) * T * 4 * d * sizeof(float));  // packed: sequence table
+  L.total = align_up(L.tab + slstm::seq_table_ints(T) * sizeof(int));
   return L;
 }
 
@@ -890,13 +891,15 @@ size_t slstm_head_newton_workspace_bytes(int B, int T, int d_h, int n_heads) {
   return head_layout(B, T, d_h).total;
 }
 
-slstm_status slstm_head_newton_forward(const void* P, slstm_dtype P_dtype, const float* R,
-                                       const float* state0, float* states, float* h_out,
-                                       float* final_state, int B, int T, int d_h, int n_heads,
-                                       slstm_forget fmode, int max_iters, float tol, slstm_init init,
-                                       void* workspace, size_t workspace_bytes, void* stream,
-                                       slstm_newton_stats* stats) {
-  g_err[0] = '\0';
+}  // extern "C"
+
+namespace {
+
+slstm_status head_newton_forward(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
+                                 float* states, float* h_out, float* final_state, int B, int T, int d_h,
+                                 int n_heads, slstm_forget fmode, int max_iters, float tol, slstm_init init,
+                                 void* workspace, size_t workspace_bytes, void* stream, slstm_newton_stats* stats,
+                                 slstm::Seqs seqs) {
   slstm_status s = check_common(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, fmode);
   if (s != SLSTM_OK) return s;
   s = check_heads(d_h, n_heads, R);
@@ -916,7 +919,13 @@ slstm_status slstm_head_newton_forward(const void* P, slstm_dtype P_dtype, const
   Control* ctl = at<Control>(workspace, L.ctl);
   auto* desc = at<unsigned long long>(workspace, L.desc);
   HIP_TRY(slstm::launch_init_control(ctl, st));
-  if (tol == 0.0f && max_iters <= slstm::kHeadSolveMaxIters) {
+  if (seqs.cu != nullptr) {
+    int* tab = at<int>(workspace, L.tab);
+    HIP_TRY(slstm::launch_seq_table(seqs.cu, seqs.n, T, tab, st));
+    seqs.tab = tab;
+  }
+  // the one-sweep kernel serves fixed counts on unpacked rows; packed rows iterate kernel by kernel
+  if (seqs.cu == nullptr && tol == 0.0f && max_iters <= slstm::kHeadSolveMaxIters) {
     // a fixed count of iterations: the whole solve in one sweep over T
     HIP_TRY(timed(SLSTM_KERNEL_HEAD_SOLVE, st, [&] {
       return slstm::launch_head_solve(P, bf16, R, state0, states, h_out, B, T, d_h, n_heads, cm, max_iters,
@@ -924,47 +933,41 @@ slstm_status slstm_head_newton_forward(const void* P, slstm_dtype P_dtype, const
     }));
   } else {
     HIP_TRY(head_newton_iterations(P, bf16, R, state0, states, h_out, B, T, d_h, n_heads, cm, max_iters, tol, init,
-                                   ctl, desc, at<float>(workspace, L.S2), st));
+                                   ctl, desc, at<float>(workspace, L.S2), st, seqs));
   }
   HIP_TRY(slstm::launch_finalize(ctl, tol, st));
   if (h_out != nullptr || final_state != nullptr)
-    HIP_TRY(slstm::launch_outputs(states, h_out, final_state, B, T, d_h, ctl, st));
+    HIP_TRY(slstm::launch_outputs(states, h_out, final_state, B, T, d_h, ctl, st, state0, seqs));
   if (stats == nullptr) return SLSTM_OK;
   Control host;
   HIP_TRY(hipMemcpyAsync(&host, ctl, sizeof(Control), hipMemcpyDeviceToHost, st));
   HIP_TRY(hipStreamSynchronize(st));
   return stats_from_control(host, stats);
 }
-slstm_status slstm_head_sequential_forward(const void* P, slstm_dtype P_dtype, const float* R,
-                                           const float* state0, float* states, float* h_out,
-                                           float* final_state, int B, int T, int d_h, int n_heads,
-                                           slstm_forget fmode, void* stream) {
-  g_err[0] = '\0';
+slstm_status head_sequential_forward(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
+                                     float* states, float* h_out, float* final_state, int B, int T, int d_h,
+                                     int n_heads, slstm_forget fmode, void* stream, slstm::Seqs seqs) {
   slstm_status s = check_common(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, fmode);
   if (s != SLSTM_OK) return s;
   s = check_heads(d_h, n_heads, R);
   if (s != SLSTM_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   HIP_TRY(timed(SLSTM_KERNEL_HEAD_SEQUENTIAL, st, [&] {
-    return slstm::launch_head_sequential(P, P_dtype == SLSTM_BF16, R, state0, states, h_out, final_state, B, T,
-                                         d_h, n_heads, cell_mode_of(fmode), st);
+    return slstm::launch_head_sequential(P, P_dtype == SLSTM_BF16, R, state0, states, h_out,
+                                         seqs.cu != nullptr ? nullptr : final_state, B, T, d_h, n_heads,
+                                         cell_mode_of(fmode), st, seqs);
   }));
+  if (seqs.cu != nullptr && final_state != nullptr)  // each sequence's last state, or its state0 if empty
+    HIP_TRY(slstm::launch_outputs(states, nullptr, final_state, B, T, d_h, nullptr, st, state0, seqs));
   return SLSTM_OK;
 }
 
-size_t slstm_head_backward_workspace_bytes(int B, int T, int d_h, int n_heads) {
-  if (check_dims(B, T, d_h) != SLSTM_OK || !head_shape_ok(d_h, n_heads) ||
-      !slstm::head_backward_width_supported(d_h / n_heads))
-    return 0;
-  return align_up(slstm::head_backward_part_floats(B, d_h, n_heads) * sizeof(float));
-}
 
-slstm_status slstm_head_backward(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
-                                 const float* states, const float* g_states, const float* g_h,
-                                 const float* g_final, void* dP, slstm_dtype dP_dtype, float* dR, float* dbias,
-                                 float* dstate0, int B, int T, int d_h, int n_heads, slstm_forget fmode,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
-  g_err[0] = '\0';
+slstm_status head_backward(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
+                           const float* states, const float* g_states, const float* g_h, const float* g_final,
+                           void* dP, slstm_dtype dP_dtype, float* dR, float* dbias, float* dstate0, int B, int T,
+                           int d_h, int n_heads, slstm_forget fmode, void* workspace, size_t workspace_bytes,
+                           void* stream, slstm::Seqs seqs) {
   slstm_status s = check_common(P, P_dtype, R, state0, states, nullptr, nullptr, B, T, d_h, fmode);
   if (s != SLSTM_OK) return s;
   s = check_heads(d_h, n_heads, R);
@@ -984,9 +987,92 @@ slstm_status slstm_head_backward(const void* P, slstm_dtype P_dtype, const float
   HIP_TRY(timed(SLSTM_KERNEL_HEAD_BACKWARD, st, [&] {
     return slstm::launch_head_backward(P, P_dtype == SLSTM_BF16, R, state0, states, g_states, g_h, g_final, dP,
                                        dP_dtype == SLSTM_BF16, dR, dbias, dstate0, B, T, d_h, n_heads,
-                                       cell_mode_of(fmode), static_cast<float*>(workspace), st);
+                                       cell_mode_of(fmode), static_cast<float*>(workspace), st, seqs);
   }));
   return SLSTM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t slstm_head_backward_workspace_bytes(int B, int T, int d_h, int n_heads) {
+  if (check_dims(B, T, d_h) != SLSTM_OK || !head_shape_ok(d_h, n_heads) ||
+      !slstm::head_backward_width_supported(d_h / n_heads))
+    return 0;
+  return align_up(slstm::head_backward_part_floats(B, d_h, n_heads) * sizeof(float));
+}
+
+slstm_status slstm_head_newton_forward(const void* P, slstm_dtype P_dtype, const float* R,
+                                       const float* state0, float* states, float* h_out,
+                                       float* final_state, int B, int T, int d_h, int n_heads,
+                                       slstm_forget fmode, int max_iters, float tol, slstm_init init,
+                                       void* workspace, size_t workspace_bytes, void* stream,
+                                       slstm_newton_stats* stats) {
+  g_err[0] = '\0';
+  return head_newton_forward(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, n_heads, fmode, max_iters,
+                             tol, init, workspace, workspace_bytes, stream, stats, {});
+}
+
+slstm_status slstm_head_newton_forward_varlen(const void* P, slstm_dtype P_dtype, const float* R,
+                                              const float* state0, const int* cu_seqlens, int n_seqs,
+                                              float* states, float* h_out, float* final_state, int T,
+                                              int d_h, int n_heads, slstm_forget fmode, int max_iters,
+                                              float tol, slstm_init init, void* workspace,
+                                              size_t workspace_bytes, void* stream,
+                                              slstm_newton_stats* stats) {
+  g_err[0] = '\0';
+  slstm::Seqs seqs;
+  slstm_status s = check_seqs(cu_seqlens, n_seqs, seqs);
+  if (s != SLSTM_OK) return s;
+  return head_newton_forward(P, P_dtype, R, state0, states, h_out, final_state, 1, T, d_h, n_heads, fmode, max_iters,
+                             tol, init, workspace, workspace_bytes, stream, stats, seqs);
+}
+
+slstm_status slstm_head_sequential_forward(const void* P, slstm_dtype P_dtype, const float* R,
+                                           const float* state0, float* states, float* h_out,
+                                           float* final_state, int B, int T, int d_h, int n_heads,
+                                           slstm_forget fmode, void* stream) {
+  g_err[0] = '\0';
+  return head_sequential_forward(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, n_heads, fmode, stream,
+                                 {});
+}
+
+slstm_status slstm_head_sequential_forward_varlen(const void* P, slstm_dtype P_dtype, const float* R,
+                                                  const float* state0, const int* cu_seqlens, int n_seqs,
+                                                  float* states, float* h_out, float* final_state, int T,
+                                                  int d_h, int n_heads, slstm_forget fmode, void* stream) {
+  g_err[0] = '\0';
+  slstm::Seqs seqs;
+  slstm_status s = check_seqs(cu_seqlens, n_seqs, seqs);
+  if (s != SLSTM_OK) return s;
+  return head_sequential_forward(P, P_dtype, R, state0, states, h_out, final_state, 1, T, d_h, n_heads, fmode, stream,
+                                 seqs);
+}
+
+slstm_status slstm_head_backward(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
+                                 const float* states, const float* g_states, const float* g_h,
+                                 const float* g_final, void* dP, slstm_dtype dP_dtype, float* dR, float* dbias,
+                                 float* dstate0, int B, int T, int d_h, int n_heads, slstm_forget fmode,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  g_err[0] = '\0';
+  return head_backward(P, P_dtype, R, state0, states, g_states, g_h, g_final, dP, dP_dtype, dR, dbias, dstate0, B, T,
+                       d_h, n_heads, fmode, workspace, workspace_bytes, stream, {});
+}
+
+slstm_status slstm_head_backward_varlen(const void* P, slstm_dtype P_dtype, const float* R,
+                                        const float* state0, const int* cu_seqlens, int n_seqs,
+                                        const float* states, const float* g_states, const float* g_h,
+                                        const float* g_final, void* dP, slstm_dtype dP_dtype, float* dR,
+                                        float* dbias, float* dstate0, int T, int d_h, int n_heads,
+                                        slstm_forget fmode, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  g_err[0] = '\0';
+  slstm::Seqs seqs;
+  slstm_status s = check_seqs(cu_seqlens, n_seqs, seqs);
+  if (s != SLSTM_OK) return s;
+  return head_backward(P, P_dtype, R, state0, states, g_states, g_h, g_final, dP, dP_dtype, dR, dbias, dstate0, 1, T,
+                       d_h, n_heads, fmode, workspace, workspace_bytes, stream, seqs);
 }
 
 slstm_status slstm_profile_enable(int on) {

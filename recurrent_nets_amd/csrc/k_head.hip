@@ -28,11 +28,14 @@
 
 namespace slstm {
 
-template <int DH, bool BF16, int CM>
+// Packed sequences (PACKED, one batch row): at the first step of sequence s the state before
+// it is state0[s]; the workgroup stages that state's h for the block product behind an extra
+// barrier (at sequence starts only) and walks the offsets with a SeqCursor.
+template <int DH, bool BF16, int CM, bool PACKED>
 __global__ __launch_bounds__(4 * DH) void head_seq_kernel(const void* __restrict__ P, const float* __restrict__ R,
                                                           const float* __restrict__ state0, float* __restrict__ S,
                                                           float* __restrict__ h_out, float* __restrict__ final_state,
-                                                          int T, int d, int nh) {
+                                                          int T, int d, int nh, Seqs seqs) {
   constexpr bool sig = (CM & kCellSigmoid) != 0;
   constexpr bool floored = (CM & kCellFloored) != 0;
   __shared__ __attribute__((aligned(16))) float hbuf[2][DH];
@@ -53,7 +56,16 @@ __global__ __launch_bounds__(4 * DH) void head_seq_kernel(const void* __restrict
 #pragma unroll
   for (int u = 0; u < kHeadPrefetch; ++u) pr[u] = load_p<BF16>(P, base + static_cast<i64>(min(u, T - 1)) * 4 * dd);
   head_lds_barrier();
+  SeqCursor cur = seq_cursor(seqs.cu, seqs.n, 0, 0, seqs.tab);
   auto step = [&](int t, float p) {
+    if constexpr (PACKED) {
+      const int sq = seq_begin(cur, t);
+      if (sq >= 0) {  // a sequence start (uniform): the state before it is state0[sq]
+        prev = state0 != nullptr ? state0[(static_cast<i64>(sq) * 4 + g) * dd + j] : 0.0f;
+        if (g == 3) hbuf[t & 1][i] = prev;
+        head_lds_barrier();
+      }
+    }
     const float x = p + block_dot<DH>(row, hbuf[t & 1]);
     float xs[4], ps[4];
     quad_gather(x, xs);
@@ -86,7 +98,7 @@ __global__ __launch_bounds__(4 * DH) void head_seq_kernel(const void* __restrict
 #pragma unroll
   for (int u = 0; u < kHeadPrefetch - 1; ++u)
     if (t0 + u < T) step(t0 + u, pr[u]);
-  if (final_state != nullptr) final_state[(static_cast<i64>(b) * 4 + g) * dd + j] = prev;
+  if (!PACKED && final_state != nullptr) final_state[(static_cast<i64>(b) * 4 + g) * dd + j] = prev;
 }
 
 // The residual maximum of iterate k - 1 over the spread slots (read serially by one thread;
@@ -101,12 +113,13 @@ __device__ __forceinline__ float head_err_prev(const Control* ctl, int k, float*
   return *s_tmp;
 }
 
-template <int DH, bool BF16, int CM, bool LAST>
+template <int DH, bool BF16, int CM, bool LAST, bool PACKED>
 __global__ __launch_bounds__(4 * DH) void head_iter_kernel(const void* __restrict__ P, const float* __restrict__ R,
                                                            const float* __restrict__ state0,
                                                            const float* __restrict__ S_in, float* __restrict__ S_out,
                                                            float* __restrict__ h_out, int T, int d, int nh,
-                                                           Control* __restrict__ ctl, int k_iter, float tol) {
+                                                           Control* __restrict__ ctl, int k_iter, float tol,
+                                                           Seqs seqs) {
   constexpr bool sig = (CM & kCellSigmoid) != 0;
   constexpr bool floored = (CM & kCellFloored) != 0;
   __shared__ __attribute__((aligned(16))) float hbuf[2][DH];   // h of the iterate at t - 1
@@ -153,7 +166,20 @@ __global__ __launch_bounds__(4 * DH) void head_iter_kernel(const void* __restric
   }
   unsigned int emax = 0u, emax_new = 0u;
   head_lds_barrier();
+  SeqCursor cur = seq_cursor(seqs.cu, seqs.n, 0, 0, seqs.tab);
   auto step = [&](int t, float p, float sin) {
+    if constexpr (PACKED) {
+      const int sq = seq_begin(cur, t);
+      if (sq >= 0) {  // a sequence start: state0[sq] before it, a zero Jacobian (no Delta enters)
+        prev = state0 != nullptr ? state0[(static_cast<i64>(sq) * 4 + g) * dd + j] : 0.0f;
+        dprev = 0.0f;
+        if (g == 3) {
+          hbuf[t & 1][i] = prev;
+          dhbuf[t & 1][i] = 0.0f;
+        }
+        head_lds_barrier();
+      }
+    }
     // residual and factors at the iterate (independent of the solve)
     const float x = p + block_dot<DH>(row, hbuf[t & 1]);
     float xs[4], ps[4];
@@ -225,13 +251,21 @@ bool head_width_supported(int d_head) { return d_head == 8 || d_head == 16 || d_
 
 hipError_t launch_head_sequential(const void* P, bool p_bf16, const float* R, const float* state0, float* S,
                                   float* h_out, float* final_state, int B, int T, int d, int n_heads,
-                                  int cell_mode, hipStream_t stream) {
+                                  int cell_mode, hipStream_t stream, Seqs seqs) {
   if (n_heads < 1 || d % n_heads != 0 || B > 65535) return hipErrorInvalidValue;
   const int dh = d / n_heads;
   const dim3 grid(static_cast<unsigned>(n_heads), static_cast<unsigned>(B));
   const unsigned int lds = head_spread_lds(static_cast<long long>(n_heads) * B, 4096);
-#define SLSTM_HEAD_SEQ(BF, CM_) \
-  head_seq_kernel<DH, BF, CM_><<<grid, 4 * DH, lds, stream>>>(P, R, state0, S, h_out, final_state, T, d, n_heads)
+  const bool packed = seqs.cu != nullptr;
+#define SLSTM_HEAD_SEQ(BF, CM_)                                                                              \
+  do {                                                                                                       \
+    if (packed)                                                                                              \
+      head_seq_kernel<DH, BF, CM_, true><<<grid, 4 * DH, lds, stream>>>(P, R, state0, S, h_out, final_state, T, d, \
+                                                                        n_heads, seqs);                      \
+    else                                                                                                     \
+      head_seq_kernel<DH, BF, CM_, false><<<grid, 4 * DH, lds, stream>>>(P, R, state0, S, h_out, final_state, T, \
+                                                                         d, n_heads, seqs);                  \
+  } while (0)
 #define SLSTM_HEAD_SEQ_T(CM_) SLSTM_HEAD_SEQ(true, CM_)
 #define SLSTM_HEAD_SEQ_F(CM_) SLSTM_HEAD_SEQ(false, CM_)
   SLSTM_HEAD_DH_DISPATCH(dh, {
@@ -246,14 +280,21 @@ hipError_t launch_head_sequential(const void* P, bool p_bf16, const float* R, co
 
 hipError_t launch_head_iteration(const void* P, bool p_bf16, const float* R, const float* state0, const float* S_in,
                                  float* S_out, float* h_out, int B, int T, int d, int n_heads, int cell_mode,
-                                 Control* ctl, int k_iter, float tol, bool last, hipStream_t stream) {
+                                 Control* ctl, int k_iter, float tol, bool last, hipStream_t stream, Seqs seqs) {
   if (n_heads < 1 || d % n_heads != 0 || B > 65535) return hipErrorInvalidValue;
   const int dh = d / n_heads;
   const dim3 grid(static_cast<unsigned>(n_heads), static_cast<unsigned>(B));
   const unsigned int lds = head_spread_lds(static_cast<long long>(n_heads) * B, 4096);
-#define SLSTM_HEAD_IT(BF, LS, CM_)                                                                             \
-  head_iter_kernel<DH, BF, CM_, LS><<<grid, 4 * DH, lds, stream>>>(P, R, state0, S_in, S_out, h_out, T, d, n_heads, \
-                                                                 ctl, k_iter, tol)
+  const bool packed = seqs.cu != nullptr;
+#define SLSTM_HEAD_IT(BF, LS, CM_)                                                                              \
+  do {                                                                                                          \
+    if (packed)                                                                                                 \
+      head_iter_kernel<DH, BF, CM_, LS, true><<<grid, 4 * DH, lds, stream>>>(P, R, state0, S_in, S_out, h_out, T, d, \
+                                                                             n_heads, ctl, k_iter, tol, seqs);  \
+    else                                                                                                        \
+      head_iter_kernel<DH, BF, CM_, LS, false><<<grid, 4 * DH, lds, stream>>>(P, R, state0, S_in, S_out, h_out, T, \
+                                                                              d, n_heads, ctl, k_iter, tol, seqs); \
+  } while (0)
 #define SLSTM_HEAD_IT_TT(CM_) SLSTM_HEAD_IT(true, true, CM_)
 #define SLSTM_HEAD_IT_TF(CM_) SLSTM_HEAD_IT(true, false, CM_)
 #define SLSTM_HEAD_IT_FT(CM_) SLSTM_HEAD_IT(false, true, CM_)

@@ -32,12 +32,16 @@ __device__ __forceinline__ void load_block_col(const float* __restrict__ R, int 
   for (int k = 0; k < DH; ++k) col[k] = src[k * DH];
 }
 
-template <int DH, bool BF16, int CM, bool DP_BF16>
+// Packed sequences (PACKED, one batch row): walking T backwards, the kernel follows the sequence
+// holding each step; at a sequence's last step its final-state gradient joins the adjoint, and at
+// its first step the state before is state0[s] (staged behind an extra barrier), the adjoint
+// J^T lam there is dstate0[s], and nothing is carried into the previous sequence.
+template <int DH, bool BF16, int CM, bool DP_BF16, bool PACKED>
 __global__ __launch_bounds__(4 * DH) void head_backward_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S, const float* __restrict__ g_states, const float* __restrict__ g_h,
     const float* __restrict__ g_final, void* __restrict__ dP, float* __restrict__ dR_part,
-    float* __restrict__ db_part, float* __restrict__ dstate0, int T, int d, int nh) {
+    float* __restrict__ db_part, float* __restrict__ dstate0, int T, int d, int nh, Seqs seqs) {
   constexpr bool sig = (CM & kCellSigmoid) != 0;
   constexpr bool floored = (CM & kCellFloored) != 0;
   __shared__ __attribute__((aligned(16))) float hbuf[2][DH];      // h of the state before step t
@@ -82,8 +86,11 @@ __global__ __launch_bounds__(4 * DH) void head_backward_kernel(
     const float gsv = gs_src[base + tl * 4 * dd];
     const float ghv = gh_src[hbase + tl * dd];
     lam = (has_gs ? gsv : 0.0f) + (has_gh ? ghv : 0.0f);
-    if (g_final != nullptr) lam += g_final[(static_cast<i64>(b) * 4 + g) * dd + j];
+    if (!PACKED && g_final != nullptr) lam += g_final[(static_cast<i64>(b) * 4 + g) * dd + j];
   }
+  // the sequence holding the current step (packed), for steps visited in decreasing order
+  const SeqCursor c0 = seq_cursor(seqs.cu, seqs.n, 0, T - 1, seqs.tab);
+  int rs = c0.s, rstart = c0.start, rend = c0.end;
   float pr[kHeadPrefetch], sr[kHeadPrefetch], gr[kHeadPrefetch];
 #pragma unroll
   for (int u = 0; u < kHeadPrefetch; ++u) ld(u, pr[u], sr[u], gr[u]);
@@ -99,10 +106,28 @@ __global__ __launch_bounds__(4 * DH) void head_backward_kernel(
       const int r = r0 + u;
       const int t = T - 1 - r;
       const bool real = t >= 0;
-      const float p = pr[u], sp = sr[u], gd = gr[u];
+      const float p = pr[u], gd = gr[u];
+      float sp = sr[u];
       ld(r + kHeadPrefetch, pr[u], sr[u], gr[u]);
       const float sp_next = sr[(u + 1) % kHeadPrefetch];  // slot g of the state before step t-1
       const float* hb = hbuf[r & 1];
+      bool seq_first = false;
+      if constexpr (PACKED) {
+        if (real) {
+          while (t < rstart && rs > 0) {
+            --rs;
+            rstart = seqs.cu[rs];
+            rend = seqs.cu[rs + 1];
+          }
+          if (t == rend - 1 && g_final != nullptr) lam += g_final[(static_cast<i64>(rs) * 4 + g) * dd + j];
+          seq_first = t == rstart;
+          if (seq_first) {  // the state before this step is state0[rs]
+            sp = state0 != nullptr ? state0[(static_cast<i64>(rs) * 4 + g) * dd + j] : 0.0f;
+            if (g == 3) hbuf[r & 1][i] = sp;
+            head_lds_barrier();
+          }
+        }
+      }
       // the step's pre-activations and Jacobians at the stored state before it
       float xs[4], ps[4], ls[4];
       quad_gather(p + block_dot<DH>(row, hb), xs);
@@ -133,8 +158,17 @@ __global__ __launch_bounds__(4 * DH) void head_backward_kernel(
       float ys[4];
       quad_gather(block_dot<DH>(col, dxbuf[r & 1][g]), ys);
       const float lprev = g == 3 ? (ys[0] + ys[1]) + (ys[2] + ys[3]) : la;
-      d0 = t == 0 ? lprev : d0;
-      lam = gd + lprev;
+      if constexpr (PACKED) {
+        if (seq_first) {  // the adjoint of state0[rs]; nothing crosses into the previous sequence
+          if (dstate0 != nullptr) dstate0[(static_cast<i64>(rs) * 4 + g) * dd + j] = lprev;
+          lam = gd;
+        } else {
+          lam = gd + lprev;
+        }
+      } else {
+        d0 = t == 0 ? lprev : d0;
+        lam = gd + lprev;
+      }
     }
     // this block's dP, in order of the steps
 #pragma unroll
@@ -152,7 +186,18 @@ __global__ __launch_bounds__(4 * DH) void head_backward_kernel(
 #pragma unroll
   for (int k = 0; k < DH / 4; ++k) dst[k] = make_float4(dr[4 * k], dr[4 * k + 1], dr[4 * k + 2], dr[4 * k + 3]);
   db_part[(static_cast<i64>(b) * 4 + g) * dd + j] = db;
-  if (dstate0 != nullptr) dstate0[(static_cast<i64>(b) * 4 + g) * dd + j] = d0;
+  if (!PACKED && dstate0 != nullptr) dstate0[(static_cast<i64>(b) * 4 + g) * dd + j] = d0;
+}
+
+// packed: an empty sequence passes its final-state gradient (or zero) to dstate0
+__global__ __launch_bounds__(256) void head_empty_seq_dstate0_kernel(const int* __restrict__ cu, int n_seqs,
+                                                                     const float* __restrict__ g_final,
+                                                                     float* __restrict__ dstate0, int d) {
+  const i64 n = static_cast<i64>(n_seqs) * 4 * d;
+  for (i64 e = static_cast<i64>(blockIdx.x) * 256 + threadIdx.x; e < n; e += static_cast<i64>(gridDim.x) * 256) {
+    const int sq = static_cast<int>(e / (4 * static_cast<i64>(d)));
+    if (cu[sq] == cu[sq + 1]) dstate0[e] = g_final != nullptr ? g_final[e] : 0.0f;
+  }
 }
 
 // out[e] = sum over b = 0..B-1 of part[b n + e], added in order of b
@@ -184,16 +229,23 @@ bool head_backward_width_supported(int d_head) { return d_head == 8 || d_head ==
 hipError_t launch_head_backward(const void* P, bool p_bf16, const float* R, const float* state0, const float* S,
                                 const float* g_states, const float* g_h, const float* g_final, void* dP,
                                 bool dp_bf16, float* dR, float* dbias, float* dstate0, int B, int T, int d,
-                                int n_heads, int cell_mode, float* part, hipStream_t stream) {
+                                int n_heads, int cell_mode, float* part, hipStream_t stream, Seqs seqs) {
   if (n_heads < 1 || d % n_heads != 0 || B > 65535) return hipErrorInvalidValue;
   const int dh = d / n_heads;
   float* dR_part = part;
   float* db_part = part + static_cast<i64>(B) * 4 * d * dh;
   const dim3 grid(static_cast<unsigned>(n_heads), static_cast<unsigned>(B));
   const unsigned int lds = head_spread_lds(static_cast<long long>(n_heads) * B, 8192);
-#define SLSTM_HEAD_BWD(BF, DB, CM_)                                                                                \
-  head_backward_kernel<DH, BF, CM_, DB><<<grid, 4 * DH, lds, stream>>>(P, R, state0, S, g_states, g_h, g_final, dP, \
-                                                                       dR_part, db_part, dstate0, T, d, n_heads)
+  const bool packed = seqs.cu != nullptr;
+#define SLSTM_HEAD_BWD(BF, DB, CM_)                                                                             \
+  do {                                                                                                          \
+    if (packed)                                                                                                 \
+      head_backward_kernel<DH, BF, CM_, DB, true><<<grid, 4 * DH, lds, stream>>>(                               \
+          P, R, state0, S, g_states, g_h, g_final, dP, dR_part, db_part, dstate0, T, d, n_heads, seqs);         \
+    else                                                                                                        \
+      head_backward_kernel<DH, BF, CM_, DB, false><<<grid, 4 * DH, lds, stream>>>(                              \
+          P, R, state0, S, g_states, g_h, g_final, dP, dR_part, db_part, dstate0, T, d, n_heads, seqs);         \
+  } while (0)
 #define SLSTM_HEAD_BWD_TT(CM_) SLSTM_HEAD_BWD(true, true, CM_)
 #define SLSTM_HEAD_BWD_TF(CM_) SLSTM_HEAD_BWD(true, false, CM_)
 #define SLSTM_HEAD_BWD_FT(CM_) SLSTM_HEAD_BWD(false, true, CM_)
@@ -219,6 +271,11 @@ hipError_t launch_head_backward(const void* P, bool p_bf16, const float* R, cons
   const i64 n_dr = static_cast<i64>(4) * d * dh;
   batch_sum_kernel<<<static_cast<unsigned>(std::min<i64>((n_dr + 255) / 256, 2048)), 256, 0, stream>>>(dR_part, dR,
                                                                                                        n_dr, B);
+  if (packed && dstate0 != nullptr && seqs.n > 0) {
+    const i64 n0 = static_cast<i64>(seqs.n) * 4 * d;
+    head_empty_seq_dstate0_kernel<<<static_cast<unsigned>(std::min<i64>((n0 + 255) / 256, 2048)), 256, 0, stream>>>(
+        seqs.cu, seqs.n, g_final, dstate0, d);
+  }
   if (dbias != nullptr) {
     const i64 n_db = static_cast<i64>(4) * d;
     batch_sum_kernel<<<static_cast<unsigned>(std::min<i64>((n_db + 255) / 256, 2048)), 256, 0, stream>>>(db_part,

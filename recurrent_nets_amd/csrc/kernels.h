@@ -107,10 +107,11 @@ hipError_t launch_sequential(const void* P, bool p_bf16, const float* R, const f
 bool head_width_supported(int d_head);
 hipError_t launch_head_sequential(const void* P, bool p_bf16, const float* R, const float* state0, float* S,
                                   float* h_out, float* final_state, int B, int T, int d, int n_heads,
-                                  int cell_mode, hipStream_t stream);
+                                  int cell_mode, hipStream_t stream, Seqs seqs = {});
 hipError_t launch_head_iteration(const void* P, bool p_bf16, const float* R, const float* state0, const float* S_in,
                                  float* S_out, float* h_out, int B, int T, int d, int n_heads, int cell_mode,
-                                 Control* ctl, int k_iter, float tol, bool last, hipStream_t stream);
+                                 Control* ctl, int k_iter, float tol, bool last, hipStream_t stream,
+                                 Seqs seqs = {});
 // The whole head-mixing Newton solve in one sweep over T: K (1..kHeadSolveMaxIters) iterations
 // pipelined stage by stage, the warm start (or zero_init's zero iterate) formed in the sweep;
 // writes S (iterate K), h_out (may be NULL), the residual maxima of iterates 0..K into ctl's
@@ -129,7 +130,7 @@ bool head_backward_width_supported(int d_head);  // 8, 16, 32
 hipError_t launch_head_backward(const void* P, bool p_bf16, const float* R, const float* state0, const float* S,
                                 const float* g_states, const float* g_h, const float* g_final, void* dP,
                                 bool dp_bf16, float* dR, float* dbias, float* dstate0, int B, int T, int d,
-                                int n_heads, int cell_mode, float* part, hipStream_t stream);
+                                int n_heads, int cell_mode, float* part, hipStream_t stream, Seqs seqs = {});
 
 // C = X W^T (+ bias) in bf16 MFMA with float32 accumulation; X (M x K), W (N x K), both
 // K-contiguous. With splits > 1 the K range is split and split s writes its partial product to

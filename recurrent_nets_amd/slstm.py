@@ -39,6 +39,7 @@ EXPORTED = [
     "slstm_newton_forward_varlen", "slstm_sequential_forward_varlen", "slstm_warm_start_varlen",
     "slstm_backward_varlen", "slstm_head_newton_workspace_bytes", "slstm_head_newton_forward",
     "slstm_head_sequential_forward", "slstm_head_backward_workspace_bytes", "slstm_head_backward",
+    "slstm_head_newton_forward_varlen", "slstm_head_sequential_forward_varlen", "slstm_head_backward_varlen",
 ]
 
 
@@ -146,6 +147,15 @@ def load(path: str | None = None):
     L.slstm_head_backward.restype = _i
     L.slstm_head_backward.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i,
                                       _i, _vp, _sz, _vp]
+    L.slstm_head_newton_forward_varlen.restype = _i
+    L.slstm_head_newton_forward_varlen.argtypes = [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
+                                                   _i, _vp, _sz, _vp, ctypes.POINTER(_Stats)]
+    L.slstm_head_sequential_forward_varlen.restype = _i
+    L.slstm_head_sequential_forward_varlen.argtypes = [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _i, _i, _i, _i,
+                                                       _vp]
+    L.slstm_head_backward_varlen.restype = _i
+    L.slstm_head_backward_varlen.argtypes = [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp,
+                                             _i, _i, _i, _i, _vp, _sz, _vp]
     L.slstm_profile_enable.restype = _i
     L.slstm_profile_enable.argtypes = [_i]
     L.slstm_profile_reset.restype = _i
@@ -487,13 +497,14 @@ def backward(P, R, states, state0=None, g_states=None, g_h=None, g_final=None, f
 
 
 # ---- head mixing (R of shape (4, n_heads, d_head, d_head)) ----------------------------------
-def _head_check(P, R, state0):
+def _head_check(P, R, state0, n_seq=None):
+    """Shapes of a head-mixing call; n_seq (packed) makes state0 (n_seq, 4, d_h)."""
     if P.dim() != 4 or P.shape[2] != 4:
         raise ValueError(f"P must be (B, T, 4, d_h), got {tuple(P.shape)}")
     B, T, _, d = P.shape
     if R.dim() != 4 or R.shape[0] != 4 or R.shape[2] != R.shape[3] or R.shape[1] * R.shape[2] != d:
         raise ValueError(f"R must be (4, n_heads, d_head, d_head) with n_heads * d_head = {d}, got {tuple(R.shape)}")
-    _shape(state0, "state0", (B, 4, d))
+    _shape(state0, "state0", (B if n_seq is None else n_seq, 4, d))
     return B, T, d, int(R.shape[1])
 
 
@@ -503,15 +514,17 @@ def head_newton_workspace_bytes(B: int, T: int, d_h: int, n_heads: int) -> int:
 
 def head_newton_forward(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, init="warm",
                         states=None, h_out=None, want_hidden=True, final_state=None, workspace=None,
-                        stream=None, stats=True, raise_on_divergence=True, readout="exact"):
+                        stream=None, stats=True, raise_on_divergence=True, readout="exact", cu_seqlens=None):
     """Newton-parallel forward under head mixing (block-diagonal R, one block per head and
     gate). Arguments and returns as newton_forward; R (4, n_heads, d_head, d_head) float32 with
-    d_head in {8, 16, 32, 64}."""
+    d_head in {8, 16, 32, 64}. With cu_seqlens (packed, B = 1), state0 and final_state are
+    (S, 4, d_h)."""
     L = load()
     _dev(P, "P", (torch.float32, torch.bfloat16))
     _dev(R, "R", (torch.float32,))
     _dev(state0, "state0", (torch.float32,))
-    B, T, d, nh = _head_check(P, R, state0)
+    cu, n_seq = _seqs(cu_seqlens, P)
+    B, T, d, nh = _head_check(P, R, state0, n_seq)
     if states is None:
         states = torch.empty((B, T, 4, d), dtype=torch.float32, device=P.device)
     if want_hidden and h_out is None:
@@ -519,15 +532,22 @@ def head_newton_forward(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, i
     _dev(states, "states", (torch.float32,))
     _dev(h_out, "h_out", (torch.float32,))
     _dev(final_state, "final_state", (torch.float32,))
-    _shape(final_state, "final_state", (B, 4, d))
+    _shape(final_state, "final_state", (B if cu is None else n_seq, 4, d))
     if workspace is None:
         workspace = alloc_workspace(L.slstm_head_newton_workspace_bytes(B, T, d, nh), P.device)
     st = _Stats() if stats else None
-    status = L.slstm_head_newton_forward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states), _ptr(h_out),
-                                         _ptr(final_state), B, T, d, nh, _fmode(forget, readout), int(max_iters),
-                                         float(tol), INIT[init], _ptr(workspace),
-                                         workspace.numel() * workspace.element_size(), _stream(stream),
-                                         ctypes.byref(st) if st is not None else None)
+    wsb = workspace.numel() * workspace.element_size()
+    sref = ctypes.byref(st) if st is not None else None
+    if cu is None:
+        status = L.slstm_head_newton_forward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states), _ptr(h_out),
+                                             _ptr(final_state), B, T, d, nh, _fmode(forget, readout),
+                                             int(max_iters), float(tol), INIT[init], _ptr(workspace), wsb,
+                                             _stream(stream), sref)
+    else:
+        status = L.slstm_head_newton_forward_varlen(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(cu), n_seq,
+                                                    _ptr(states), _ptr(h_out), _ptr(final_state), T, d, nh,
+                                                    _fmode(forget, readout), int(max_iters), float(tol), INIT[init],
+                                                    _ptr(workspace), wsb, _stream(stream), sref)
     _check(status, "slstm_head_newton_forward")
     out_stats = NewtonStats._from(st, status) if st is not None else None
     if raise_on_divergence and status in (DIVERGED, NONFINITE):
@@ -537,13 +557,15 @@ def head_newton_forward(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, i
 
 
 def head_sequential_forward(P, R, state0=None, forget="exp", states=None, h_out=None, want_hidden=True,
-                            final_state=None, stream=None, readout="exact"):
-    """Step-by-step forward under head mixing (also the T=1 decode step). Returns (states, h)."""
+                            final_state=None, stream=None, readout="exact", cu_seqlens=None):
+    """Step-by-step forward under head mixing (also the T=1 decode step). Returns (states, h).
+    With cu_seqlens (packed, B = 1), state0 and final_state are (S, 4, d_h)."""
     L = load()
     _dev(P, "P", (torch.float32, torch.bfloat16))
     _dev(R, "R", (torch.float32,))
     _dev(state0, "state0", (torch.float32,))
-    B, T, d, nh = _head_check(P, R, state0)
+    cu, n_seq = _seqs(cu_seqlens, P)
+    B, T, d, nh = _head_check(P, R, state0, n_seq)
     if states is None:
         states = torch.empty((B, T, 4, d), dtype=torch.float32, device=P.device)
     if want_hidden and h_out is None:
@@ -551,10 +573,15 @@ def head_sequential_forward(P, R, state0=None, forget="exp", states=None, h_out=
     _dev(states, "states", (torch.float32,))
     _dev(h_out, "h_out", (torch.float32,))
     _dev(final_state, "final_state", (torch.float32,))
-    _shape(final_state, "final_state", (B, 4, d))
-    status = L.slstm_head_sequential_forward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
-                                             _ptr(h_out), _ptr(final_state), B, T, d, nh, _fmode(forget, readout),
-                                             _stream(stream))
+    _shape(final_state, "final_state", (B if cu is None else n_seq, 4, d))
+    if cu is None:
+        status = L.slstm_head_sequential_forward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
+                                                 _ptr(h_out), _ptr(final_state), B, T, d, nh,
+                                                 _fmode(forget, readout), _stream(stream))
+    else:
+        status = L.slstm_head_sequential_forward_varlen(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(cu),
+                                                        n_seq, _ptr(states), _ptr(h_out), _ptr(final_state), T, d,
+                                                        nh, _fmode(forget, readout), _stream(stream))
     _check(status, "slstm_head_sequential_forward")
     return states, h_out
 
@@ -565,18 +592,21 @@ def head_backward_workspace_bytes(B: int, T: int, d_h: int, n_heads: int) -> int
 
 def head_backward(P, R, states, state0=None, g_states=None, g_h=None, g_final=None, forget="exp",
                   dP=None, dR=None, dstate0=None, want_dstate0=True, workspace=None, stream=None,
-                  dP_dtype=torch.float32, dbias=None, want_dbias=False, readout="exact"):
+                  dP_dtype=torch.float32, dbias=None, want_dbias=False, readout="exact", cu_seqlens=None):
     """Gradients through the head-mixing recurrence at the forward solution ``states``
     (B,T,4,d_h); arguments as ``backward``, R (4, n_heads, d_head, d_head) with d_head 8, 16 or
     32. Returns (dP, dR (4, n_heads, d_head, d_head), dstate0 or None), and dbias (4, d_h) last
-    when ``want_dbias`` or a ``dbias`` tensor is given."""
+    when ``want_dbias`` or a ``dbias`` tensor is given. With cu_seqlens (packed, B = 1),
+    state0, g_final and dstate0 are (S, 4, d_h)."""
     L = load()
     _dev(P, "P", (torch.float32, torch.bfloat16))
     _dev(R, "R", (torch.float32,))
     _dev(state0, "state0", (torch.float32,))
-    B, T, d, nh = _head_check(P, R, state0)
+    cu, n_seq = _seqs(cu_seqlens, P)
+    B, T, d, nh = _head_check(P, R, state0, n_seq)
+    n0 = B if cu is None else n_seq
     for name, t, shape in (("states", states, (B, T, 4, d)), ("g_states", g_states, (B, T, 4, d)),
-                           ("g_h", g_h, (B, T, d)), ("g_final", g_final, (B, 4, d))):
+                           ("g_h", g_h, (B, T, d)), ("g_final", g_final, (n0, 4, d))):
         _dev(t, name, (torch.float32,))
         if t is not None and tuple(t.shape) != shape:
             raise ValueError(f"{name} must be {shape}, got {tuple(t.shape)}")
@@ -587,17 +617,24 @@ def head_backward(P, R, states, state0=None, g_states=None, g_h=None, g_final=No
     if want_dbias and dbias is None:
         dbias = torch.empty((4, d), dtype=torch.float32, device=P.device)
     if want_dstate0 and dstate0 is None:
-        dstate0 = torch.empty((B, 4, d), dtype=torch.float32, device=P.device)
+        dstate0 = torch.empty((n0, 4, d), dtype=torch.float32, device=P.device)
     _dev(dP, "dP", (torch.float32, torch.bfloat16))
     _dev(dR, "dR", (torch.float32,))
     _dev(dbias, "dbias", (torch.float32,))
     _dev(dstate0, "dstate0", (torch.float32,))
     if workspace is None:
         workspace = alloc_workspace(max(L.slstm_head_backward_workspace_bytes(B, T, d, nh), 256), P.device)
-    status = L.slstm_head_backward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states), _ptr(g_states),
-                                   _ptr(g_h), _ptr(g_final), _ptr(dP), BF16 if dP.dtype == torch.bfloat16 else F32,
-                                   _ptr(dR), _ptr(dbias), _ptr(dstate0), B, T, d, nh, _fmode(forget, readout),
-                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    dpt = BF16 if dP.dtype == torch.bfloat16 else F32
+    wsb = workspace.numel() * workspace.element_size()
+    if cu is None:
+        status = L.slstm_head_backward(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states), _ptr(g_states),
+                                       _ptr(g_h), _ptr(g_final), _ptr(dP), dpt, _ptr(dR), _ptr(dbias), _ptr(dstate0),
+                                       B, T, d, nh, _fmode(forget, readout), _ptr(workspace), wsb, _stream(stream))
+    else:
+        status = L.slstm_head_backward_varlen(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(cu), n_seq,
+                                              _ptr(states), _ptr(g_states), _ptr(g_h), _ptr(g_final), _ptr(dP), dpt,
+                                              _ptr(dR), _ptr(dbias), _ptr(dstate0), T, d, nh, _fmode(forget, readout),
+                                              _ptr(workspace), wsb, _stream(stream))
     _check(status, "slstm_head_backward")
     if want_dbias or dbias is not None:
         return dP, dR, dstate0, dbias
