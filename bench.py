@@ -334,9 +334,9 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU: this build runs the whole Newton solve on a single "
-              f"MI355X (requested --gpus {args.gpus}, WORLD_SIZE {world}). Multi-GPU runs are "
-              f"not part of it.", file=sys.stderr)
+        print(f"bench.py measures one GPU: the library runs the whole Newton solve on a single "
+              f"MI355X (requested --gpus {args.gpus}, WORLD_SIZE {world}); it has no multi-GPU path.",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -1,4 +1,4 @@
-// C ABI of the library: argument checks, workspace layout, the Newton driver and timing.
+// C ABI of the library: argument checks, workspace layout, the host-side Newton loop and timing.
 // The solver loop follows "Layout" (pararnn-torch docs), "Current surface (0.17)":
 // initial state prepended, residual early stop, flags after the last iterate.
 #include <hip/hip_runtime.h>
