@@ -160,6 +160,160 @@ __global__ __launch_bounds__(4 * DH) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   }
 }
 
+// The same solve with its stages on separate wave groups of one workgroup: group 0 forms the
+// warm start, group k + 1 runs Newton iteration k (its residual, Jacobian and substitution
+// step) and group K + 1 the final residual and the stores. At tick tau group r works on step
+// tau - r, so the K + 2 stages of a step run one after another on consecutive ticks while the
+// groups run side by side; a tick costs about one stage (one block product and one cell
+// evaluation) instead of all of them. Stage r hands its iterate at t and its pre-activations
+// x~ at t to stage r + 1 through a double-buffered LDS slot, one float of each per lane; every
+// group passes one barrier per tick. A group is 4 d_head lanes rounded up to a whole wave (at
+// d_head 8 the upper half of the wave repeats the lower: the same values to the same LDS words,
+// no global stores), so every branch on the group is uniform over a wave. Heads of up to 32
+// units: K + 2 groups of 128 lanes fit a workgroup, and a lane's block row fits its registers.
+constexpr int kHeadPipeMaxThreads = 1024;
+
+template <int DH>
+constexpr int head_pipe_group() {
+  return 4 * DH < 64 ? 64 : 4 * DH;
+}
+
+// WAVES: the waves per SIMD the register budget is cut for (1: no cut). Two workgroups that share
+// a CU stay resident together only at 6 (80 registers a lane).
+template <int DH, bool BF16, int CM, int WAVES>
+__global__ __launch_bounds__(kHeadPipeMaxThreads) __attribute__((amdgpu_waves_per_eu(WAVES))) void head_solve_pipe_kernel(
+    const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
+    float* __restrict__ S, float* __restrict__ h_out, int T, int d, int nh, Control* __restrict__ ctl,
+    int zero_init, int K) {
+  constexpr bool sig = (CM & kCellSigmoid) != 0;
+  constexpr bool floored = (CM & kCellFloored) != 0;
+  constexpr int GS = head_pipe_group<DH>();
+  constexpr int KM = kHeadSolveMaxIters;
+  __shared__ __attribute__((aligned(16))) float h0buf[2][DH];      // h of iterate 0 at t - 1
+  __shared__ __attribute__((aligned(16))) float dhbuf[KM][2][DH];  // Delta h of iteration k at t - 1
+  __shared__ float hand_s[KM + 1][2][GS];  // iterate r at t, slot g: from group r to group r + 1
+  __shared__ float hand_x[KM + 1][2][GS];  // x~ of iterate r at t, gate g
+  __shared__ unsigned int s_err[KM + 1];
+  __shared__ float junk[GS];  // the LDS writes of lanes that do not hold h (see h_slot)
+  const int tid = threadIdx.x;
+  const int grp = __builtin_amdgcn_readfirstlane(tid / GS);
+  const int tg = tid - grp * GS;
+  const int i = (tg >> 2) & (DH - 1), g = tg & 3;
+  const bool primary = tg < 4 * DH;
+  const int a = blockIdx.x, b = blockIdx.y;
+  const int j = a * DH + i;
+  const i64 dd = d;
+  const GateSel sel(g);
+  const float s0 = state0 != nullptr ? state0[(static_cast<i64>(b) * 4 + g) * dd + j] : 0.0f;
+  if (grp == 0 && g == 3) h0buf[0][i] = s0;  // the state before step 0 is state0 for every iterate
+  if (grp >= 1 && grp <= K && g == 3) dhbuf[grp - 1][0][i] = 0.0f;
+  if (tid <= K) s_err[tid] = 0u;
+  auto h_slot = [&](float* hdst, bool write) { return write ? hdst : &junk[tg]; };
+  const i64 base = static_cast<i64>(b) * T * 4 * dd + g * dd + j;  // (b, t = 0, slot/gate g, j)
+  // ticks 0 .. T + K, rounded up to whole blocks of kHeadPrefetch: every group passes the same
+  // number of barriers
+  const int n_ticks = (T + K + 1 + kHeadPrefetch - 1) / kHeadPrefetch * kHeadPrefetch;
+  head_lds_barrier();
+
+  if (grp == 0) {
+    // the warm start: the channelwise cell with R h' dropped, and x~ of iterate 0
+    float row[DH];
+    load_block_row<DH>(R, nh, a, i, g, row);
+    const float warm_scale = zero_init ? 0.0f : 1.0f;  // the warm start's state is finite
+    float sp = s0;
+    float pr[kHeadPrefetch];
+#pragma unroll
+    for (int u = 0; u < kHeadPrefetch; ++u) pr[u] = load_p<BF16>(P, base + static_cast<i64>(min(u, T - 1)) * 4 * dd);
+    for (int t0 = 0; t0 < n_ticks; t0 += kHeadPrefetch) {
+#pragma unroll
+      for (int u = 0; u < kHeadPrefetch; ++u) {
+        const int t = t0 + u;
+        const float p = pr[u];
+        pr[u] = load_p<BF16>(P, base + static_cast<i64>(min(t + kHeadPrefetch, T - 1)) * 4 * dd);
+        const float x = p + block_dot<DH>(row, h0buf[t & 1]);
+        float ps[4], pg[4], s[4], A[16];
+        quad_gather(sp, ps);
+        quad_gather(p, pg);
+        cell_step<false>(CellIn{ps[0], ps[1], ps[2], 0.0f}, pg[0], pg[1], pg[2], pg[3], 0.0f, 0.0f, 0.0f, 0.0f, sig,
+                         floored, s, A);
+        const float cur = sel(s) * warm_scale;
+        *h_slot(&h0buf[(t + 1) & 1][i], g == 3) = cur;
+        hand_s[0][t & 1][tg] = cur;
+        hand_x[0][t & 1][tg] = x;
+        sp = cur;  // past T the values run on unread
+        head_lds_barrier();
+      }
+    }
+  } else if (grp <= K) {
+    // Newton iteration k at step t: residual and Jacobian at iterate k, Delta^k_t, iterate k + 1
+    const int k = grp - 1;
+    float row[DH];
+    load_block_row<DH>(R, nh, a, i, g, row);
+    float sp = s0, dp = 0.0f;  // slot g of iterate k and of Delta^k at t - 1
+    unsigned int emax = 0u;
+    for (int tau = 0; tau < n_ticks; ++tau) {
+      const int t = tau - grp;
+      const bool real = t >= 0 && t < T;
+      const int rd = (tau - 1) & 1, wr = tau & 1;
+      const float cur = hand_s[k][rd][tg];  // iterate k at t
+      const float x = hand_x[k][rd][tg];
+      const float y = block_dot<DH>(row, dhbuf[k][t & 1]);  // R Delta h^k_{t-1}
+      float xs[4], ps[4], ys[4], ds[4], s[4], dv[4];
+      quad_gather(x, xs);
+      quad_gather(sp, ps);
+      CellLin L;
+      cell_step_lin(CellIn{ps[0], ps[1], ps[2], 0.0f}, xs, sig, floored, s, L);
+      const float F = cur - sel(s);
+      const unsigned int em = res_max(emax, F);
+      emax = real ? em : emax;
+      quad_gather(y, ys);
+      quad_gather(dp, ds);
+      cell_jvp(L, ds, ys, dv);
+      const float delta = sel(dv) - F;
+      // before step 0 the slot holds Delta h^k_{-1} = 0: ticks ahead of it write elsewhere
+      *h_slot(&dhbuf[k][(t + 1) & 1][i], g == 3 && real) = delta;
+      hand_s[grp][wr][tg] = cur + delta;
+      hand_x[grp][wr][tg] = x + y;
+      sp = real ? cur : sp;
+      dp = real ? delta : dp;
+      head_lds_barrier();
+    }
+    __hip_atomic_fetch_max(&s_err[k], emax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  } else {
+    // iterate K at step t: its residual, and the stores
+    float sp = s0;
+    unsigned int emax = 0u;
+    const bool h_lane = g == 3 && h_out != nullptr && primary;
+    for (int tau = 0; tau < n_ticks; ++tau) {
+      const int t = tau - grp;
+      const bool real = t >= 0 && t < T;
+      const int rd = (tau - 1) & 1;
+      const float cur = hand_s[K][rd][tg];
+      const float x = hand_x[K][rd][tg];
+      float xs[4], ps[4], sn[4], An[16];
+      quad_gather(x, xs);
+      quad_gather(sp, ps);
+      cell_step<false>(CellIn{ps[0], ps[1], ps[2], 0.0f}, xs[0], xs[1], xs[2], xs[3], 0.0f, 0.0f, 0.0f, 0.0f, sig,
+                       floored, sn, An);
+      const unsigned int em = res_max(emax, cur - sel(sn));
+      emax = real ? em : emax;
+      sp = real ? cur : sp;
+      if (real && primary) {
+        S[base + static_cast<i64>(t) * 4 * dd] = cur;
+        if (h_lane) h_out[(static_cast<i64>(b) * T + t) * dd + j] = cur;
+      }
+      head_lds_barrier();
+    }
+    __hip_atomic_fetch_max(&s_err[K], emax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned int slot = blockIdx.x + gridDim.x * blockIdx.y;
+    for (int k = 0; k <= K; ++k) err_publish(&spread_of(ctl)->err[0][k], kErrSlotWords, slot, res_max_value(s_err[k]));
+    if (blockIdx.x == 0 && blockIdx.y == 0) ctl->iters = K;
+  }
+}
+
 hipError_t launch_head_solve(const void* P, bool p_bf16, const float* R, const float* state0, float* S,
                              float* h_out, int B, int T, int d, int n_heads, int cell_mode, int K, bool zero_init,
                              Control* ctl, hipStream_t stream) {
@@ -168,6 +322,39 @@ hipError_t launch_head_solve(const void* P, bool p_bf16, const float* R, const f
   const dim3 grid(static_cast<unsigned>(n_heads), static_cast<unsigned>(B));
   const unsigned int lds = head_spread_lds(static_cast<long long>(n_heads) * B, 4096);
   const int zi = zero_init ? 1 : 0;
+  // Which form: the wave-group form runs a step in about half the single-group sweep's time
+  // while each CU holds one workgroup, and with two (at K >= 2 with the register cut that keeps
+  // both resident) about 15% faster; from three workgroups a CU on, the CU's issue rate bounds
+  // both and the sweep's fewer instructions win (measured at d_head 32, T 4096, K 1 and 3).
+  // Heads wider than 32 units always take the sweep.
+  const long long wg_per_cu = (static_cast<long long>(n_heads) * B + 255) / 256;
+  if (dh <= 32 && wg_per_cu <= 2) {
+    const unsigned int lds_p = head_spread_lds(static_cast<long long>(n_heads) * B, 24 * 1024);
+    const bool cut = wg_per_cu == 2 && K >= 2;
+#define SLSTM_HEAD_PIPE(CM_)                                                                                  \
+  if (cut)                                                                                                    \
+    head_solve_pipe_kernel<DH, BFV, CM_, 6><<<grid, (K + 2) * head_pipe_group<DH>(), lds_p, stream>>>(      \
+        P, R, state0, S, h_out, T, d, n_heads, ctl, zi, K);                                                   \
+  else                                                                                                        \
+    head_solve_pipe_kernel<DH, BFV, CM_, 1><<<grid, (K + 2) * head_pipe_group<DH>(), lds_p, stream>>>(      \
+        P, R, state0, S, h_out, T, d, n_heads, ctl, zi, K);
+#define SLSTM_HEAD_PIPE_DH(DHV)                                                              \
+  case DHV: {                                                                                \
+    constexpr int DH = DHV;                                                                  \
+    if (p_bf16) { constexpr bool BFV = true; SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_HEAD_PIPE) } \
+    else { constexpr bool BFV = false; SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_HEAD_PIPE) }       \
+    break;                                                                                   \
+  }
+    switch (dh) {
+      SLSTM_HEAD_PIPE_DH(8)
+      SLSTM_HEAD_PIPE_DH(16)
+      SLSTM_HEAD_PIPE_DH(32)
+      default: return hipErrorInvalidValue;
+    }
+#undef SLSTM_HEAD_PIPE_DH
+#undef SLSTM_HEAD_PIPE
+    return hipGetLastError();
+  }
 #define SLSTM_HEAD_SOLVE(BF, KK, CM_) \
   head_solve_kernel<DH, BF, CM_, KK><<<grid, 4 * DH, lds, stream>>>(P, R, state0, S, h_out, T, d, n_heads, ctl, zi)
 #define SLSTM_HEAD_SOLVE_K(BF, CM_)              \

@@ -175,6 +175,26 @@ def test_head_one_sweep_solve(gpu_lib, K, dh):
     assert h_rel_err(h1, to_np(h2)) < H_TOL_F32
 
 
+@pytest.mark.parametrize("K", [1, 3])
+@pytest.mark.parametrize("B,nh,dh", [(1, 3, 32), (2, 150, 8), (2, 300, 8)])
+def test_head_one_sweep_forms(gpu_lib, B, nh, dh, K):
+    """The one-sweep solve picks its kernel by the number of (batch row, head) workgroups per CU:
+    its stages on separate wave groups at one (3 heads) and two (300: with the register cut from
+    K = 2), the single-group sweep from three (600). Every form matches the oracle's states and
+    residual maxima."""
+    P, R, s0 = _inputs(1020 + nh + K, B, 21, dh, nh)
+    case(f"head one-sweep form B={B} heads={nh} d_head={dh} K={K}")
+    S, h, st = gpu_lib.head_newton_forward(*_dev(P, R, s0), "exp", K, 0.0)
+    torch.cuda.synchronize()
+    S_ref, st_ref = ref.newton_head(to_np(P), to_np(R), to_np(s0), "exp", K)
+    assert h_rel_err(h, S_ref[..., 3, :]) < H_TOL_F32
+    assert _state_err(S, S_ref) < 1e-4
+    assert st.iters == K and st.diverged == st_ref.diverged
+    for e_gpu, e_ref in zip(st.max_abs_F, st_ref.max_abs_F):
+        if e_ref > 1e-3:
+            assert abs(e_gpu - e_ref) <= 1e-3 * e_ref
+
+
 def test_head_one_sweep_zero_init_exact(gpu_lib):
     """The one-sweep kernel from a zero iterate: after K = T iterations the iterate is the exact
     solution (the sequential one). Sigmoid forget gate: with the exponential one, this zero
