@@ -290,7 +290,7 @@ def head_context(slstm, torch, dev, steps):
         "B": B, "T": T, "d_h": d, "n_heads": nh, "d_head": dh, "forget_gate": HEAD["forget"], "newton_iters": K,
         "preactivations": "f32", "solve_ms": round(ms, 4), "state_elems_per_s": n_e / (ms * 1e-3),
         "solver": {"iters": st.iters, "max_abs_F": st.max_abs_F[-1], "diverged": st.diverged},
-        "form": "one sweep (warm start and K iterations pipelined along T)",
+        "form": "one sweep (warm start, K iterations and the final residual pipelined along T, one wave group each)",
         "kernels": {"head_solve": {"avg_ms": round(sv_ms, 4), "us_per_step": round(sv_ms * 1e3 / T, 4),
                                    "bytes_per_launch": sv_bytes, "flops_per_launch": sv_flops},
                     "head_sequential": {"avg_ms": round(sq_ms, 4), "us_per_step": round(sq_ms * 1e3 / T, 4),
@@ -302,7 +302,7 @@ def head_context(slstm, torch, dev, steps):
                                                                                   "unit": "GB/s",
                                                                                   "frac": round(bw_gbs / HBM_PEAK_GBS, 4)}}},
         "roofline": {"bound": "latency", "kernel": "head_solve",
-                     "note": "one workgroup per (batch row, head) walks T; a step's chain bounds it",
+                     "note": "one workgroup per (batch row, head) walks T, its stages a tick apart on separate wave groups; the tick's chain and the CU's issue rate bound it",
                      "hbm_view": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": round(gbs / HBM_PEAK_GBS, 4)},
                      "alu_view": {"achieved": round(tfs, 2), "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
