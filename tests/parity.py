@@ -22,23 +22,33 @@ def to_np(t) -> np.ndarray:
     return np.asarray(t, dtype=np.float64)
 
 
-# Floor of the element-wise relative error. |h| < 1 always, and h = o c / n is formed through
-# cancellation in c, so float32 carries an absolute error of a few 1e-7 whatever the
-# algorithm: a plain float32 step loop reaches 1.2e-4 against the float64 oracle on the
-# sigmoid-forget workload when the floor is 1e-3, and 1.6e-5 when it is 1e-2
-# (tests/test_metric_calibration.py). Below |h| = 1e-2 the error is therefore measured
-# against 1e-2.
-H_FLOOR = 1e-2
+# Floor of the element-wise relative error: max over elements of |dh| / max(|h_ref|, floor).
+# |h| < 1 always and h crosses zero, so the metric needs a floor. The default is 1e-3. A plain
+# float32 step loop -- the most direct float32 evaluation there is -- meets the float32 bar
+# (1e-4) at that floor on the exponential-forget workloads (5.6e-7 tiny, 2.1e-5 mid, 7e-6 long
+# context; tests/test_metric_calibration.py), so those compare at 1e-3. With the sigmoid forget
+# gate the same loop reaches 1.2e-4 at 1e-3: h = o c / n is formed through cancellation in c,
+# and the float32 absolute error of a few 1e-7 is above 1e-4 of |h| for |h| near 1e-3. Cases
+# that hold the float32 bar with a sigmoid forget gate therefore compare at H_FLOOR_SIGMOID
+# (the same loop: 1.6e-5). Cases with bf16 inputs (bar 2e-2) use the default.
+H_FLOOR = 1e-3
+H_FLOOR_SIGMOID = 1e-2
 
 
-def h_rel_err(h_gpu, h_ref) -> float:
-    """max over elements of |h_gpu - h_ref| / max(|h_ref|, H_FLOOR)."""
+def h_floor(forget: str, tol: float) -> float:
+    """The floor a case compares h at: H_FLOOR_SIGMOID for the float32 bar with the sigmoid
+    forget gate, H_FLOOR otherwise."""
+    return H_FLOOR_SIGMOID if (tol <= H_TOL_F32 and str(forget).startswith("sigmoid")) else H_FLOOR
+
+
+def h_rel_err(h_gpu, h_ref, floor: float = H_FLOOR) -> float:
+    """max over elements of |h_gpu - h_ref| / max(|h_ref|, floor)."""
     g = to_np(h_gpu)
     r = to_np(h_ref)
     assert g.shape == r.shape, (g.shape, r.shape)
     if not np.all(np.isfinite(g)):
         return float("inf")
-    return float(np.max(np.abs(g - r) / np.maximum(np.abs(r), H_FLOOR)))
+    return float(np.max(np.abs(g - r) / np.maximum(np.abs(r), floor)))
 
 
 # Bar on the gradients of the backward pass (dP, dR, dstate0), float32 arithmetic in the kernel

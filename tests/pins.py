@@ -814,4 +814,67 @@ def pin_head_packed_backward(ref):
     np.testing.assert_allclose(dR, dR_sum, rtol=1e-12, atol=1e-13)
 
 
+# ---------------------------------------------------------------------------------------
+# branch margin (chooses the lanes the backward's parity compares)
+# ---------------------------------------------------------------------------------------
+def pin_branch_margin_worked_example(ref):
+    """|a - i~| and |l| + |m'| + |i~| at the state BEFORE each step, worked by hand.
+
+    One lane, two steps, R = (0.2, 0.5, -0.5, 0.1), state0 = (c, n, m, h) = (0.5, 1, 0.25, 0.5),
+    S_1 = (0.1, 2, -1.5, -0.25) (any S: the margin is defined at every iterate).
+      t = 1 (previous state = state0): i~ = 0.5 + 0.5*0.5 = 0.75, f~ = 1.5 - 0.5*0.5 = 1.25;
+        exponential gate: l = 1.25, a = l + m' = 1.5, margin 0.75, scale 1.25 + 0.25 + 0.75 = 2.25
+      t = 2 (previous state = S_1): i~ = 2 + 0.5*(-0.25) = 1.875, f~ = 1 + (-0.5)(-0.25) = 1.125;
+        a = 1.125 - 1.5 = -0.375, margin 2.25, scale 1.125 + 1.5 + 1.875 = 4.5
+    With the sigmoid gate l = -ln(1 + e^{-f~}) (log of the logistic function) at the same f~.
+    """
+    R = np.array([0.2, 0.5, -0.5, 0.1])[:, None]
+    s0 = np.array([0.5, 1.0, 0.25, 0.5])[None, :, None]
+    S = np.zeros((1, 2, 4, 1))
+    S[0, 0, :, 0] = [0.1, 2.0, -1.5, -0.25]
+    S[0, 1, :, 0] = [0.3, 0.7, 9.0, 0.9]
+    P = np.zeros((1, 2, 4, 1))
+    P[0, 0, :, 0] = [0.0, 0.5, 1.5, 0.0]
+    P[0, 1, :, 0] = [0.0, 2.0, 1.0, 0.0]
+    margin, scale = ref.branch_margin(P, R, s0, S, "exp")
+    np.testing.assert_allclose(margin[0, :, 0], [0.75, 2.25], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(scale[0, :, 0], [2.25, 4.5], rtol=0, atol=1e-15)
+    margin, scale = ref.branch_margin(P, R, s0, S, "sigmoid")
+    l1 = -math.log1p(math.exp(-1.25))
+    l2 = -math.log1p(math.exp(-1.125))
+    np.testing.assert_allclose(margin[0, :, 0], [abs(l1 + 0.25 - 0.75), abs(l2 - 1.5 - 1.875)],
+                               rtol=1e-14)
+    np.testing.assert_allclose(scale[0, :, 0], [abs(l1) + 0.25 + 0.75, abs(l2) + 1.5 + 1.875],
+                               rtol=1e-14)
+    # packed: a sequence starting at the second step takes its own state0 as the state before
+    # it, here state0[1] = (0, 1, -2, 0): i~ = 2, f~ = 1, a = 1 - 2 = -1, margin 3, scale 5
+    s0p = np.concatenate([s0, np.array([0.0, 1.0, -2.0, 0.0])[None, :, None]])
+    margin, scale = ref.branch_margin(P, R, s0p, S, "exp", cu_seqlens=np.array([0, 1, 2]))
+    np.testing.assert_allclose(margin[0, :, 0], [0.75, 3.0], rtol=0, atol=1e-15)
+    np.testing.assert_allclose(scale[0, :, 0], [2.25, 5.0], rtol=0, atol=1e-15)
+
+
+def pin_branch_margin_zero_at_ties(ref):
+    """An exact tie a = i~ has margin 0, and a step moved off the tie by a known amount in m'
+    has exactly that margin (a = l + m' moves with m', i~ does not)."""
+    for forget in ("exp", "sigmoid"):
+        rng = np.random.Generator(np.random.PCG64(31))
+        d = 16
+        s0 = np.stack([rng.uniform(-1, 1, d), np.exp(rng.uniform(0, 1, d)),
+                       rng.uniform(-3, 3, d), rng.uniform(-0.9, 0.9, d)])[None]
+        R = rng.uniform(-0.5, 0.5, (4, d))
+        R[1] = 0.0                      # i~ = p_i exactly
+        P = rng.standard_normal((1, 1, 4, d))
+        lf, _ = ref.log_forget(P[:, 0, 2] + R[2] * s0[:, 3], forget)
+        P[:, 0, 1] = lf + s0[:, 2]      # a == i~ bit for bit
+        S = np.zeros((1, 1, 4, d))
+        margin, _ = ref.branch_margin(P, R, s0, S, forget)
+        np.testing.assert_array_equal(margin, 0.0)
+        shift = 0.25 * np.arange(1, d + 1)      # exact in binary
+        s1 = s0.copy()
+        s1[:, 2] += shift
+        margin, _ = ref.branch_margin(P, R, s1, S, forget)
+        np.testing.assert_allclose(margin[0, 0], shift, rtol=1e-12, atol=1e-12)
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -12,12 +12,21 @@ import pytest
 import torch
 
 from oracle import lanes, slstm_ref as ref
-from parity import H_TOL_BF16, H_TOL_F32, case, h_rel_err, sample_lanes, to_np
-from workloads import by_name, draw_layer_inputs, draw_preactivation_inputs, random_states, to_bf16
+from parity import H_FLOOR_SIGMOID, H_TOL_BF16, H_TOL_F32, case, h_rel_err, sample_lanes, to_np
+from workloads import (by_name, draw_decode_inputs, draw_layer_inputs, draw_preactivation_inputs,
+                       random_states, to_bf16)
 
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
+
+# Regression guards for the workloads whose contract bar is the bf16 one (2e-2). The float32
+# path measures h errors of order 1e-5 there, so a bar of 2e-2 alone would let a thousandfold
+# regression pass. Each guard is about ten times the error measured on MI355X, at the same
+# floor; exceeding it means the kernels lost accuracy, not that the contract is broken.
+GUARD_SIGMOID_BF16 = 1e-3   # measured 8.6e-5 .. 9.1e-5 (all three schedules)
+GUARD_LAYER = 1e-4          # measured 1.06e-5
+GUARD_DECODE = 1e-4         # measured 1.0e-5 (decode from the forward's final state)
 
 
 @pytest.fixture(params=["fused_scan", "fused_chain", "layered"])
@@ -50,9 +59,13 @@ def test_sigmoid_bf16_workload_full_size(gpu_lib, schedule):
     assert st_ref.iters == st.iters and st_ref.converged == st.converged
     for k in range(st.iters):
         assert st.max_abs_F[k] == pytest.approx(st_ref.max_abs_F[k], rel=0.05, abs=2e-5)
-    err = h_rel_err(_gpu_h_at(h, lb, lj), S_ref[:, :, 3])
-    print(f"sigmoid bf16 full size: iters {st.iters}, h rel err {err:.2e}")
+    hg = _gpu_h_at(h, lb, lj)
+    err = h_rel_err(hg, S_ref[:, :, 3])
+    err_sig = h_rel_err(hg, S_ref[:, :, 3], H_FLOOR_SIGMOID)
+    print(f"sigmoid bf16 full size: iters {st.iters}, h rel err {err:.2e} (floor 1e-3), "
+          f"{err_sig:.2e} (floor 1e-2)")
     assert err < H_TOL_BF16
+    assert err < GUARD_SIGMOID_BF16
 
 
 def test_long_context_workload_full_size(gpu_lib, schedule):
@@ -90,9 +103,12 @@ def test_full_layer_workload_full_size(gpu_lib, schedule):
     bias = inp["bias"].to(DEV)
     R = inp["R"].to(DEV)
     P = gpu_lib.input_projection(x, W, bias)
-    S, h, st = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, schedule=schedule)
+    fin = torch.empty((w.B, 4, w.d_h), dtype=torch.float32, device=DEV)
+    S, h, st = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, final_state=fin,
+                                      schedule=schedule)
     torch.cuda.synchronize()
     assert st.iters == w.max_iters and not st.diverged
+    assert torch.equal(fin, S[:, -1])
     m_max = float(S[..., 2, :].abs().max())
     assert st.max_abs_F[-1] <= 64 * np.spacing(np.float32(m_max))
     lb, lj = sample_lanes(w.B, w.d_h, 64, seed=3)
@@ -110,11 +126,33 @@ def test_full_layer_workload_full_size(gpu_lib, schedule):
     S_ref, st_ref = ref.newton(P_lanes, to_np(inp["R"])[:, lj], None, w.forget, w.max_iters, tol=w.tol)
     assert not st_ref.diverged
     err = h_rel_err(_gpu_h_at(h, lb, lj), np.transpose(S_ref[0, :, 3, :], (1, 0)))
-    print(f"full layer: h rel err {err:.2e} (bar {H_TOL_BF16}; float32 bar {H_TOL_F32})")
+    print(f"full layer: h rel err {err:.2e} (bar {H_TOL_BF16}, guard {GUARD_LAYER})")
     assert err < H_TOL_BF16
+    assert err < GUARD_LAYER
+
+    # the T = 1 decode step continues each side's own forward: the GPU from the GPU's final
+    # state, the oracle from its own K-iteration final state of the sampled lanes, both with
+    # the benchmark's fresh bf16 input row projected by the same weights
+    case("decode: T=1 step at B=128 from the forward's final state")
+    del S, h
+    x_dec = draw_decode_inputs(w)
+    P_dec = gpu_lib.input_projection(x_dec.to(DEV), W, bias)
+    _, h_dec = gpu_lib.sequential_forward(P_dec, R, fin, w.forget)
+    torch.cuda.synchronize()
+    Pd_ref = ref.input_projection(to_np(x_dec), W64, b64)            # (B, 1, 4, d)
+    Pd_lanes = Pd_ref[lb, 0, :, lj].T                               # (4, n) at the sampled lanes
+    fin_ref = S_ref[0, -1]                                            # (4, n) at the sampled lanes
+    S_dec_ref = ref.sequential(Pd_lanes[None, None], to_np(inp["R"])[:, lj], fin_ref[None], w.forget)
+    hd = h_dec[torch.as_tensor(lb, device=DEV), 0, torch.as_tensor(lj, device=DEV)].cpu().double().numpy()
+    err_dec = h_rel_err(hd, S_dec_ref[0, 0, 3])
+    print(f"full layer decode from the forward's final state: h rel err {err_dec:.2e}")
+    assert err_dec < H_TOL_BF16
+    assert err_dec < GUARD_DECODE
 
 
 def test_full_layer_decode_step(gpu_lib):
+    """The decode step on every lane of the batch, from a drawn state (the chained case on
+    sampled lanes is part of the full-layer test)."""
     w = by_name("layer_b128_t2048_d1024")
     case("decode: T=1 sequential step at B=128 after the input projection")
     inp = draw_layer_inputs(w, B=1, T=1)

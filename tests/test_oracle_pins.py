@@ -73,6 +73,10 @@ MUTATIONS = [
     ('head packed: no restart at a start', '            if t in starts:\n                prev = s0[starts[t]][None]\n', ''),
     ('head packed: Jacobian not cut at a start', '                J[:, t] = 0.0\n', '                pass\n'),
     ('head packed backward: adjoint leaks across a start', '        elif t in starts:\n            dstate0[starts[t]] += lam_prev[0]\n            lam_prev = np.zeros_like(lam_prev)\n', '        elif t in starts:\n            dstate0[starts[t]] += lam_prev[0]\n'),
+    ("branch margin at s_t instead of s_{t-1}", "prev = _shifted(np.asarray(S, dtype=np.float64), state0, cu_seqlens)\n    _, it, ft, _ = preactivations(prev, P, R)",
+     "prev = np.asarray(S, dtype=np.float64)\n    _, it, ft, _ = preactivations(prev, P, R)"),
+    ("branch margin without the stabiliser", "a = lf + prev[..., M, :]\n    return np.abs(a - it)",
+     "a = lf\n    return np.abs(a - it)"),
     ("head solve: transposed block", 'np.einsum("bauv,bav->bau", J[:, t], x[:, t - 1])',
      'np.einsum("bavu,bav->bau", J[:, t], x[:, t - 1])'),
 ]
