@@ -160,6 +160,33 @@ slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const floa
 slstm_status slstm_newton_read_stats(const void* workspace, size_t workspace_bytes, void* stream,
                                      slstm_newton_stats* stats);
 
+/* Size of the library's fixed device scratch used by slstm_newton_forward_noalloc (64 MiB). */
+#define SLSTM_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+
+/*
+ * For callers that cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc): slstm_newton_forward without a workspace argument.
+ * Same arguments, semantics, layouts and results as slstm_newton_forward (the same kernels);
+ * the solver's workspace is a fixed array of SLSTM_NOALLOC_SCRATCH_BYTES inside the library,
+ * one per GPU, allocated when the library's code is loaded onto that GPU and held until the
+ * process ends. The call allocates nothing (no hipMalloc, hipFree or allocating library call)
+ * and records no profiling events.
+ *  - Problems whose workspace, slstm_newton_workspace_bytes(B, T, d_h, schedule), exceeds
+ *    SLSTM_NOALLOC_SCRATCH_BYTES are rejected with SLSTM_EWORKSPACE before any work is enqueued.
+ *  - The scratch lives on the device of `stream` (the current device for NULL); the solver's
+ *    control block is cleared by a kernel at the start of each call.
+ *  - Every call on one GPU shares that GPU's scratch: calls that overlap in time on one GPU
+ *    (on different streams, or from different threads) race and give undefined results;
+ *    serialise them. Solver statistics are only returned through `stats` (which waits for the
+ *    stream); slstm_newton_read_stats cannot address the scratch.
+ */
+slstm_status slstm_newton_forward_noalloc(const void* P, slstm_dtype P_dtype, const float* R,
+                                          const float* state0, float* states, float* h_out,
+                                          float* final_state, int B, int T, int d_h,
+                                          slstm_forget fmode, int max_iters, float tol,
+                                          slstm_init init, slstm_schedule schedule, void* stream,
+                                          slstm_newton_stats* stats);
+
 /*
  * Sequential forward ([SL] "API notes": solver='sequential'; at T = 1 the decode step):
  * s_t = f(s_{t-1}, P_t) for t = 1..T, one thread per lane (b, j). Same arguments and layouts

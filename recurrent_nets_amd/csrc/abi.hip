@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <random>
 #include <vector>
 
@@ -75,9 +76,12 @@ struct Profiler {
 };
 Profiler g_prof;
 
+// set for the duration of a call that must not create HIP objects (the no-allocation entry)
+thread_local bool g_no_timing = false;
+
 template <class F>
 hipError_t timed(slstm_kernel_kind kind, hipStream_t s, F&& launch) {
-  if (!g_prof.on) return launch();
+  if (!g_prof.on || g_no_timing) return launch();
   ProfRec r;
   hipError_t e = g_prof.acquire(r);
   if (e != hipSuccess) return e;
@@ -428,6 +432,43 @@ slstm_status check_seqs(const int* cu_seqlens, int n_seqs, slstm::Seqs& seqs) {
   return SLSTM_OK;
 }
 
+// ---- scratch of the no-allocation Newton entry point --------------------------------------------
+// One statically sized array per device, loaded with the code object and kept until the process
+// ends. Host code must never pass the array's name to a kernel (on the host it is only a stand-in
+// for the symbol): the device address comes from hipGetSymbolAddress, taken once per device with
+// that device current, and only that address is used.
+constexpr size_t kNoAllocScratchBytes = size_t(SLSTM_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// the scratch address on device `dev` (nullptr and the HIP error on failure)
+void* scratch_on_device(int dev, hipError_t& err) {
+  err = hipSuccess;
+  if (dev < 0 || dev >= kMaxScratchDevices) {
+    err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] != nullptr) return g_scratch_ptr[dev];
+  int cur = 0;
+  err = hipGetDevice(&cur);
+  if (err != hipSuccess) return nullptr;
+  if (cur != dev && (err = hipSetDevice(dev)) != hipSuccess) return nullptr;
+  void* p = nullptr;
+  err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  const hipError_t back = cur != dev ? hipSetDevice(cur) : hipSuccess;
+  if (err != hipSuccess) return nullptr;
+  if (back != hipSuccess) {
+    err = back;
+    return nullptr;
+  }
+  g_scratch_ptr[dev] = p;
+  return p;
+}
+
 slstm_status newton_forward(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
                             float* states, float* h_out, float* final_state, int B, int T, int d_h,
                             slstm_forget fmode, int max_iters, float tol, slstm_init init,
@@ -682,6 +723,40 @@ slstm_status slstm_newton_read_stats(const void* workspace, size_t workspace_byt
   HIP_TRY(hipMemcpyAsync(&host, workspace, sizeof(Control), hipMemcpyDeviceToHost, st));
   HIP_TRY(hipStreamSynchronize(st));
   return stats_from_control(host, stats);
+}
+
+slstm_status slstm_newton_forward_noalloc(const void* P, slstm_dtype P_dtype, const float* R,
+                                          const float* state0, float* states, float* h_out,
+                                          float* final_state, int B, int T, int d_h, slstm_forget fmode,
+                                          int max_iters, float tol, slstm_init init,
+                                          slstm_schedule schedule, void* stream,
+                                          slstm_newton_stats* stats) {
+  if (!known_schedule(schedule)) return fail(SLSTM_EINVAL, "unknown schedule %d", (int)schedule);
+  const size_t need = slstm_newton_workspace_bytes(B, T, d_h, schedule);
+  if (need == 0) {
+    const slstm_status s = check_dims(B, T, d_h);
+    return s != SLSTM_OK ? s : fail(SLSTM_EINVAL, "invalid sizes");
+  }
+  if (need > kNoAllocScratchBytes)
+    return fail(SLSTM_EWORKSPACE,
+                "slstm_newton_forward_noalloc: this problem needs %zu bytes of scratch, more than the "
+                "library's fixed %zu; call slstm_newton_forward with a workspace instead",
+                need, kNoAllocScratchBytes);
+  int dev = 0;
+  if (stream != nullptr) {
+    HIP_TRY(hipStreamGetDevice(static_cast<hipStream_t>(stream), &dev));
+  } else {
+    HIP_TRY(hipGetDevice(&dev));
+  }
+  hipError_t err;
+  void* ws = scratch_on_device(dev, err);
+  if (ws == nullptr) return fail(SLSTM_EHIP, "scratch address on device %d: %s", dev, hipGetErrorString(err));
+  g_no_timing = true;
+  const slstm_status s = newton_forward(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, fmode,
+                                        max_iters, tol, init, schedule, ws, kNoAllocScratchBytes, stream,
+                                        stats, {});
+  g_no_timing = false;
+  return s;
 }
 
 slstm_status slstm_sequential_forward(const void* P, slstm_dtype P_dtype, const float* R,

@@ -40,6 +40,7 @@ EXPORTED = [
     "slstm_backward_varlen", "slstm_head_newton_workspace_bytes", "slstm_head_newton_forward",
     "slstm_head_sequential_forward", "slstm_head_backward_workspace_bytes", "slstm_head_backward",
     "slstm_head_newton_forward_varlen", "slstm_head_sequential_forward_varlen", "slstm_head_backward_varlen",
+    "slstm_newton_forward_noalloc",
 ]
 
 
@@ -102,6 +103,9 @@ def load(path: str | None = None):
     L.slstm_newton_forward.restype = _i
     L.slstm_newton_forward.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
                                        _i, _i, _vp, _sz, _vp, ctypes.POINTER(_Stats)]
+    L.slstm_newton_forward_noalloc.restype = _i
+    L.slstm_newton_forward_noalloc.argtypes = [_vp, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f,
+                                               _i, _i, _vp, ctypes.POINTER(_Stats)]
     L.slstm_newton_read_stats.restype = _i
     L.slstm_newton_read_stats.argtypes = [_vp, _sz, _vp, ctypes.POINTER(_Stats)]
     L.slstm_sequential_forward.restype = _i
@@ -301,6 +305,42 @@ def newton_forward(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, init="
                                                INIT[init], SCHEDULE[schedule], _ptr(workspace), nbytes,
                                                _stream(stream), st_ref)
     _check(status, "slstm_newton_forward")
+    out_stats = NewtonStats._from(st, status) if st is not None else None
+    if raise_on_divergence and status in (DIVERGED, NONFINITE):
+        raise NewtonDivergenceError(
+            f"{L.slstm_status_string(status).decode()} (max|F| = {out_stats.max_abs_F[-1]:.3g})")
+    return states, h_out, out_stats
+
+
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024  # SLSTM_NOALLOC_SCRATCH_BYTES
+
+
+def newton_forward_noalloc(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, init="warm",
+                           states=None, h_out=None, final_state=None, stream=None, stats=True,
+                           raise_on_divergence=True, schedule="fused", readout="exact"):
+    """newton_forward through the entry point that allocates nothing: the solver works in the
+    library's fixed per-GPU scratch (NOALLOC_SCRATCH_BYTES), so the caller passes outputs but no
+    workspace. ``states`` (and ``h_out`` if wanted) must be given. Calls that overlap on one GPU
+    race on the shared scratch. Returns (states, h_out, NewtonStats or None)."""
+    L = load()
+    _dev(P, "P", (torch.float32, torch.bfloat16))
+    _dev(R, "R", (torch.float32,))
+    _dev(state0, "state0", (torch.float32,))
+    B, T, d = _shape_check(P, R, state0, None)
+    if states is None:
+        raise ValueError("newton_forward_noalloc needs a preallocated states tensor")
+    _dev(states, "states", (torch.float32,))
+    _dev(h_out, "h_out", (torch.float32,))
+    _dev(final_state, "final_state", (torch.float32,))
+    _shape(states, "states", (B, T, 4, d))
+    _shape(h_out, "h_out", (B, T, d))
+    _shape(final_state, "final_state", (B, 4, d))
+    st = _Stats() if stats else None
+    status = L.slstm_newton_forward_noalloc(_ptr(P), _p_dtype(P), _ptr(R), _ptr(state0), _ptr(states),
+                                            _ptr(h_out), _ptr(final_state), B, T, d, _fmode(forget, readout),
+                                            int(max_iters), float(tol), INIT[init], SCHEDULE[schedule],
+                                            _stream(stream), ctypes.byref(st) if st is not None else None)
+    _check(status, "slstm_newton_forward_noalloc")
     out_stats = NewtonStats._from(st, status) if st is not None else None
     if raise_on_divergence and status in (DIVERGED, NONFINITE):
         raise NewtonDivergenceError(
