@@ -40,7 +40,13 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, published
 # dual-rate fp32) x 2.4 GHz = 157.3 TFLOP/s. The library's kernels are built without packed
 # fp32 instructions, so 78.6 TFLOP/s is their ceiling for pure FMA streams.
 FP32_VECTOR_PEAK_TFLOPS = 157.3
+FP32_UNPACKED_PEAK_TFLOPS = 78.6
+# vector issue: a wave64 VALU instruction occupies a 16-lane SIMD for 4 cycles; 1024 SIMDs at
+# 2.4 GHz
+SIMDS = 1024
+CLOCK_GHZ = 2.4
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+VALU_FILE = os.path.join(ROOT, "profiles", "valu.json")
 
 
 def log(*a):
@@ -72,8 +78,8 @@ def kernel_work(w, n_e, p_bytes):
     """Algorithmic work per launch of each kernel kind. Bytes: every operand of every state
     element read once and every result written once (per element: P p_bytes, a state 16, a
     right-hand side / Newton step 16, the Jacobian JAC_BYTES, h 4). The one-kernel solve is
-    bound by its vector instructions, so its figure is the flop count of solve_flops_per_elem;
-    its bytes (P in; S_K and h out) are kept for the HBM view."""
+    reported against HBM on its bytes (P in; S_K and h out), with its flop count of
+    solve_flops_per_elem and its vector-issue share beside it."""
     return {
         "warm_start": {"bound": "hbm", "bytes": n_e * (p_bytes + 16)},                        # P in, S out
         "residual_jacobian": {"bound": "hbm", "bytes": n_e * (p_bytes + 16 + JAC_BYTES + 16)},  # P, S in; A, rhs out
@@ -81,7 +87,7 @@ def kernel_work(w, n_e, p_bytes):
         "update": {"bound": "hbm", "bytes": n_e * 48},                                        # S, Delta in; S out
         "final_residual": {"bound": "hbm", "bytes": n_e * (p_bytes + 16)},                    # P, S in
         "newton_iteration": {"bound": "hbm", "bytes": n_e * (p_bytes + 16 + 16)},             # P, S_k in; S_k+1 out
-        "newton_solve": {"bound": "alu", "bytes": n_e * (p_bytes + 16 + 4),                   # P in; S_K, h out
+        "newton_solve": {"bound": "hbm", "bytes": n_e * (p_bytes + 16 + 4),                   # P in; S_K, h out
                          "flops": n_e * solve_flops_per_elem(w.max_iters, w.forget == "sigmoid")},
         "backward": {"bound": "hbm", "bytes": n_e * (p_bytes + 16 + 4 + 8)},                  # P, S, dL/dh in; bf16 dP out
     }
@@ -143,12 +149,69 @@ def measured_traffic(kernel, workload):
         return None
     with open(TRAFFIC_FILE) as f:
         data = json.load(f)
-    rec = data.get(kernel)
+    rec = data.get(f"{kernel}@{workload}") or data.get(kernel)
     if not rec or rec.get("workload") != workload:
         return None
     if rec.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
         return None
     return rec.get("bytes_per_launch")
+
+
+def measured_valu(kernel, workload):
+    """VALU instructions per launch (SQ_INSTS_VALU, summed over the launch's waves) from a
+    committed rocprofv3 counter run, or None when it was taken on another workload or on an
+    older version of the kernel's source."""
+    if not os.path.exists(VALU_FILE):
+        return None
+    with open(VALU_FILE) as f:
+        data = json.load(f)
+    rec = data.get(f"{kernel}@{workload}") or data.get(kernel)
+    if not rec or rec.get("workload") != workload:
+        return None
+    if rec.get("source_sha") != source_sha(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("valu_insts_per_launch")
+
+
+def valu_issue_frac(insts, ms):
+    """Share of the GPU's vector issue slots a launch's VALU instructions fill: each wave64
+    instruction holds a 16-lane SIMD for 4 cycles."""
+    return insts * 4.0 / (SIMDS * CLOCK_GHZ * 1e9 * ms * 1e-3)
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def copy_bandwidth(torch, dev, nbytes=4 << 30, reps=5):
+    """Device-to-device copy bandwidth on this GPU (torch's copy of nbytes, read + write
+    counted), median of reps: the practical ceiling of a kernel that reads and writes HBM."""
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1.0)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        dst.copy_(src)
+        b.record()
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    del src, dst
+    torch.cuda.empty_cache()
+    times.sort()
+    return 2.0 * nbytes / (times[len(times) // 2] * 1e-3) / 1e9
 
 
 # ---------------------------------------------------------------------------------------
@@ -164,13 +227,19 @@ def _cpu_block(args):
     b, j0, j1 = args
     w = _CPU["w"]
     with threadpool_limits(1):
+        t0 = time.perf_counter()
         if "x" in _CPU:
             x = _CPU["x"][b:b + 1].astype(np.float64)
             P = ref.input_projection(x, _CPU["W"][:, j0:j1], _CPU["bias"][:, j0:j1])
         else:
             P = _CPU["P"][b:b + 1, :, :, j0:j1]
+        t1 = time.perf_counter()
         _, st = ref.newton(P, _CPU["R"][:, j0:j1], None, w.forget, w.max_iters, tol=w.tol)
-    return st.iters
+        t2 = time.perf_counter()
+        ref.sequential(P, _CPU["R"][:, j0:j1], None, w.forget)
+        t3 = time.perf_counter()
+    # per block: projection, Newton and sequential seconds
+    return t1 - t0, t2 - t1, t3 - t2
 
 
 def cpu_baseline(w, host, lanes_wanted):
@@ -203,18 +272,26 @@ def cpu_baseline(w, host, lanes_wanted):
     else:
         _CPU["P"] = host["P"].double().numpy()
     ctx = mp.get_context("fork")
-    t0 = time.perf_counter()
-    with ctx.Pool(processes=min(workers, len(tasks))) as pool:
-        pool.map(_cpu_block, tasks, chunksize=1)
-    dt = time.perf_counter() - t0
+    n_proc = min(workers, len(tasks))
+    with ctx.Pool(processes=n_proc) as pool:
+        parts = pool.map(_cpu_block, tasks, chunksize=1)
     _CPU.clear()
+    # every process works through its blocks one after another: the wall time of each leg is
+    # its summed process time spread over the processes
+    t_proj = sum(p[0] for p in parts) / n_proc
+    t_newton = sum(p[1] for p in parts) / n_proc
+    t_seq = sum(p[2] for p in parts) / n_proc
     elems = n_lanes * w.T
-    what = ("input projection + " if "x" in host else "") + f"Newton K={w.max_iters}"
-    return {"value": elems / dt, "unit": "state-elems/s", "cores": min(workers, len(tasks)),
-            "kind": "oracle",
-            "sample": f"{n_lanes} of {w.lanes} lanes (b, j) x full T={w.T}: float64 {what}, "
-                      f"{elems} state elements in {dt:.2f} s wall on {min(workers, len(tasks))} "
-                      f"single-threaded processes"}
+    proj = "input projection + " if "x" in host else ""
+    dt = t_proj + t_newton
+    return {"value": elems / dt, "unit": "state-elems/s", "cores": n_proc, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{n_lanes} of {w.lanes} lanes (b, j) x full T={w.T}: float64 {proj}Newton "
+                      f"K={w.max_iters}{' tol=%g' % w.tol if w.tol > 0 else ''}, {elems} state elements, "
+                      f"{dt:.2f} s on {n_proc} single-threaded processes",
+            "newton_only": {"value": elems / t_newton, "unit": "state-elems/s"},
+            "sequential": {"value": elems / t_seq, "unit": "state-elems/s",
+                           "sample": f"the float64 step loop on the same lanes, {t_seq:.2f} s"}}
 
 
 # ---------------------------------------------------------------------------------------
@@ -310,6 +387,72 @@ def head_context(slstm, torch, dev, steps):
                      "traffic": measured_traffic("head_solve", HEAD_WORKLOAD)}}
 
 
+def solver_context(slstm, torch, dev, name, steps, cpu_lanes, no_cpu):
+    """One of the workloads whose solver input is P, at its full size, in the schedule the
+    library picks for its shape: state-elems/s of the Newton solve, the iteration kernel's HBM
+    fraction, the solver's outcome and the float64 oracle on a lane sample. Not the metric."""
+    from workloads import by_name, draw_preactivation_inputs
+    w = by_name(name)
+    t_gen = time.perf_counter()
+    host = draw_preactivation_inputs(w, device=dev)
+    P = host["P"].to(dev)
+    R = host["R"].to(dev)
+    log(f"[bench] context {name}: inputs ready in {time.perf_counter() - t_gen:.1f} s")
+    p_bytes = 8 if w.p_dtype == "bf16" else 16
+    n_e = w.state_elems
+    S = torch.empty((w.B, w.T, 4, w.d_h), dtype=torch.float32, device=dev)
+    H = torch.empty((w.B, w.T, w.d_h), dtype=torch.float32, device=dev)
+    ws = slstm.alloc_workspace(slstm.newton_workspace_bytes(w.B, w.T, w.d_h, "fused"), dev)
+
+    def solve():
+        slstm.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, "warm", states=S, h_out=H, workspace=ws,
+                             stats=False, schedule="fused")
+
+    solve()
+    torch.cuda.synchronize()
+    st = slstm.read_stats(ws)
+    reps = max(3, steps // 2)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        solve()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1000.0 / reps
+    slstm.profile_reset()
+    slstm.profile_enable(True)
+    for _ in range(reps):
+        solve()
+    torch.cuda.synchronize()
+    slstm.profile_enable(False)
+    bytes_of = {"warm_start": n_e * (p_bytes + 16), "newton_iteration": n_e * (p_bytes + 32),
+                "final_residual": n_e * (p_bytes + 16 + 4), "newton_solve": n_e * (p_bytes + 16 + 4)}
+    kernels = {}
+    for kind, nb in bytes_of.items():
+        d = slstm.profile_durations(kind)
+        if d:
+            avg = sum(d) / len(d)
+            kernels[kind] = {"launches_per_solve": len(d) // reps, "avg_ms": round(avg, 4),
+                             "bytes_per_launch": nb, "GB_s": round(nb / (avg * 1e-3) / 1e9, 1)}
+    it = kernels.get("newton_iteration")
+    log(f"[bench] context {name}: solve {ms:.3f} ms ({n_e / (ms * 1e-3):.3e} state-elems/s), iters {st.iters}, "
+        f"converged {st.converged}, iteration kernel {it['avg_ms'] if it else float('nan'):.3f} ms")
+    out = {"B": w.B, "T": w.T, "d_h": w.d_h, "preactivations": w.p_dtype, "forget_gate": w.forget,
+           "max_iters": w.max_iters, "tol": w.tol, "schedule": "fused (scan form at this shape)",
+           "solve_ms": round(ms, 4), "state_elems_per_s": n_e / (ms * 1e-3),
+           "solver": {"iters": st.iters, "converged": st.converged, "diverged": st.diverged,
+                      "max_abs_F": st.max_abs_F},
+           "kernels": kernels}
+    if it:
+        out["roofline"] = {"bound": "hbm", "kernel": "newton_iteration", "achieved": it["GB_s"],
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(it["GB_s"] / HBM_PEAK_GBS, 4),
+                           "traffic": measured_traffic("newton_iteration", w.name)}
+    del ws, S, H, P, R
+    torch.cuda.empty_cache()
+    if not no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, {"P": host["P"], "R": host["R"]}, cpu_lanes)
+        log(f"[bench] context {name}: CPU oracle {out['cpu_baseline']['value']:.3e} state-elems/s")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -318,6 +461,8 @@ def main():
     ap.add_argument("--workload", default="layer_b128_t2048_d1024")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-lanes", type=int, default=40960)
+    ap.add_argument("--no-copy-bandwidth", action="store_true",
+                    help="skip the device-copy bandwidth measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run a plain device copy of 4 GiB (counter calibration runs)")
     ap.add_argument("--no-sequential-context", action="store_true")
@@ -330,6 +475,8 @@ def main():
                     help="skip the context run on the same tokens packed as ragged sequences")
     ap.add_argument("--no-head-context", action="store_true",
                     help="skip the context run of head mixing (block-diagonal R)")
+    ap.add_argument("--no-workload-contexts", action="store_true",
+                    help="skip the sigmoid/bf16 and long-context workloads at their full sizes")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -403,16 +550,31 @@ def main():
         log(f"[bench] {schedule}: solver iters {st.iters}, max|F| {['%.2e' % e for e in st.max_abs_F]}, "
             f"diverged {st.diverged}; device memory {torch.cuda.memory_allocated() / 2**30:.1f} GiB")
         torch.cuda.synchronize()
-        slstm.profile_reset()
-        slstm.profile_enable(True)
+        # the metric: exactly `steps` steps between two synchronisations, nothing recorded
         t0 = time.perf_counter()
         for _ in range(steps):
             step()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        slstm.profile_enable(False)
         ms = (t1 - t0) * 1000.0 / steps
         log(f"[bench] {schedule}: {steps} timed steps, {ms:.3f} ms/step")
+        # then the same number of steps again with the library's kernel events and one event
+        # pair per step on the stream: per-kernel durations and the spread of step times
+        slstm.profile_reset()
+        slstm.profile_enable(True)
+        evs = []
+        for _ in range(steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            step()
+            b.record()
+            evs.append((a, b))
+        torch.cuda.synchronize()
+        slstm.profile_enable(False)
+        step_ms = sorted(a.elapsed_time(b) for a, b in evs)
+        spread = {"median_ms": round(step_ms[len(step_ms) // 2], 4), "min_ms": round(step_ms[0], 4),
+                  "max_ms": round(step_ms[-1], 4), "steps": steps, "timing": "HIP events per step, second pass"}
         kernels = {}
         for kind, wk in work.items():
             d = slstm.profile_durations(kind)
@@ -441,28 +603,38 @@ def main():
                                  "total_ms_per_step": (sum(seqd) + sum(small)) / steps}
         del ws
         torch.cuda.empty_cache()
+        kernels["_spread"] = spread
         return ms, kernels, st
 
     def roofline_of(kernels, steps, ms):
-        dominant = max((k for k in kernels if k in work or k == "input_projection"),
+        dominant = max((k for k in kernels if (k in work or k == "input_projection") and not k.startswith("_")),
                        key=lambda k: kernels[k]["total_ms_per_step"])
         k = kernels[dominant]
         if dominant == "input_projection":
             roof = {"bound": "mfma", "kernel": dominant, "achieved": round(k["TFLOP_s"], 1),
                     "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": round(k["TFLOP_s"] / BF16_PEAK_TFLOPS, 4)}
-        elif work[dominant]["bound"] == "alu":
-            roof = {"bound": "alu", "kernel": dominant, "achieved": round(k["TFLOP_s"], 1),
-                    "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(k["TFLOP_s"] / FP32_VECTOR_PEAK_TFLOPS, 4),
-                    "hbm_view": {"achieved": round(k["GB_s"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                 "frac": round(k["GB_s"] / HBM_PEAK_GBS, 4)}}
         else:
             roof = {"bound": "hbm", "kernel": dominant, "achieved": round(k["GB_s"], 1), "peak": HBM_PEAK_GBS,
                     "unit": "GB/s", "frac": round(k["GB_s"] / HBM_PEAK_GBS, 4)}
+            if copy_gbs:
+                roof["copy_ceiling"] = {"achieved": round(copy_gbs, 1), "unit": "GB/s",
+                                        "frac_of_copy": round(k["GB_s"] / copy_gbs, 4)}
+            if "flops" in k:
+                # the kernel's arithmetic beside its bytes: flops against the ceiling of the build
+                # (no packed fp32), and the share of vector issue its instructions fill
+                roof["alu_view"] = {"achieved": round(k["TFLOP_s"], 2), "peak": FP32_UNPACKED_PEAK_TFLOPS,
+                                    "unit": "TFLOP/s", "frac": round(k["TFLOP_s"] / FP32_UNPACKED_PEAK_TFLOPS, 4)}
+            insts = measured_valu(dominant, w.name)
+            if insts:
+                roof["valu_issue"] = {"valu_insts_per_launch": insts,
+                                      "frac": round(valu_issue_frac(insts, k["avg_ms"]), 4),
+                                      "source": "profiles/valu.json (rocprofv3 SQ_INSTS_VALU)"}
         roof["traffic"] = measured_traffic(dominant, w.name)
         # whole-step roofline: every kernel at its own bound
         t_roof = 0.0
         for kind, kk in kernels.items():
+            if kind.startswith("_"):
+                continue
             per_step = kk["launches"] / steps
             if kind == "input_projection":
                 t_roof += per_step * max(kk["flops_per_launch"] / (BF16_PEAK_TFLOPS * 1e12),
@@ -471,18 +643,24 @@ def main():
                 wk = work[kind]
                 t = wk["bytes"] / (HBM_PEAK_GBS * 1e9)
                 if "flops" in wk:
-                    t = max(t, wk["flops"] / (FP32_VECTOR_PEAK_TFLOPS * 1e12))
+                    t = max(t, wk["flops"] / (FP32_UNPACKED_PEAK_TFLOPS * 1e12))
                 t_roof += per_step * t
         return roof, t_roof / (ms * 1e-3)
 
     def rounded(kernels):
         return {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-                for k, v in kernels.items()}
+                for k, v in kernels.items() if not k.startswith("_")}
+
+    copy_gbs = None
+    if not args.no_copy_bandwidth:
+        copy_gbs = copy_bandwidth(torch, dev)
+        log(f"[bench] device copy of 4 GiB: {copy_gbs:.0f} GB/s (read + write)")
 
     ms_per_step, kernels, st = timed_run(args.schedule, args.steps, args.warmup)
     roofline, step_frac = roofline_of(kernels, args.steps, ms_per_step)
     value = n_e / (ms_per_step * 1e-3)
     context = {"schedule": args.schedule, "step_roofline_frac": round(step_frac, 4),
+               "step_time": kernels["_spread"], "copy_GB_s": round(copy_gbs, 1) if copy_gbs else None,
                "kernels": rounded(kernels),
                "solver": {"iters": st.iters, "max_abs_F": st.max_abs_F, "diverged": st.diverged}}
     if w.on_gpu_gemm:
@@ -508,7 +686,10 @@ def main():
         context["layered"] = {"ms_per_step": round(lms, 4), "state_elems_per_s": n_e / (lms * 1e-3),
                               "roofline": lroof,
                               "residual_plus_scan": {"achieved": round(ab_gbs, 1), "peak": HBM_PEAK_GBS,
-                                                     "unit": "GB/s", "frac": round(ab_gbs / HBM_PEAK_GBS, 4)},
+                                                     "unit": "GB/s", "frac": round(ab_gbs / HBM_PEAK_GBS, 4),
+                                                     "frac_of_copy": round(ab_gbs / copy_gbs, 4) if copy_gbs else None,
+                                                     "traffic": {k: measured_traffic(k, w.name)
+                                                                 for k in ("residual_jacobian", "scan_block4", "update")}},
                               "kernels": rounded(lkernels)}
 
     if not args.no_backward_context:
@@ -650,6 +831,14 @@ def main():
 
     if not args.no_head_context:
         context["head"] = head_context(slstm, torch, dev, args.steps)
+
+    if not args.no_workload_contexts and w.on_gpu_gemm:
+        # the sigmoid/bf16 workload (early stop) and the long-context workload at full size,
+        # where lanes are few and the scan form's parallelism along T carries the solve
+        context["workloads"] = {}
+        for name, lanes_n in (("sigmoid_bf16p_b16_t4096_d1024", 4096), ("long_b4_t16384_d2048", 1024)):
+            context["workloads"][name] = solver_context(slstm, torch, dev, name, args.steps, lanes_n,
+                                                        args.no_cpu_baseline)
 
     if not args.no_sequential_context:
         # the lane-parallel sequential forward on the same P, for context (not the metric)

@@ -233,4 +233,147 @@ __device__ __forceinline__ void quad_look_back(const float arow[4], float av, fl
   }
 }
 
+// ---- tiles of 4 data waves and a coordinating wave ------------------------------------------
+// Wave-major scan tiles: wave w (w = 0..3) of a workgroup holds sub-chunk w (consecutive steps)
+// of the tile's features, one or two per thread, so every access of a wave covers whole
+// 256- or 512-byte rows; a fifth wave, which holds no data, does the look-back across tiles.
+constexpr int kRowsDataWaves = 4;
+constexpr int kRowsBlock = (kRowsDataWaves + 1) * kWave;  // 320
+
+// VEC consecutive floats at a byte offset (one 4- or 8-byte buffer access)
+template <int VEC>
+__device__ __forceinline__ void buf_ld_vec(rsrc_t r, unsigned voff, unsigned soff, float (&out)[VEC]) {
+  if constexpr (VEC == 1) {
+    out[0] = buf_ld(r, voff, soff);
+  } else {
+    const auto w = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    out[0] = __uint_as_float(static_cast<uint32_t>(w[0]));
+    out[1] = __uint_as_float(static_cast<uint32_t>(w[1]));
+  }
+}
+template <int VEC>
+__device__ __forceinline__ void buf_st_vec(const float (&v)[VEC], rsrc_t r, unsigned voff, unsigned soff) {
+  if constexpr (VEC == 1) {
+    buf_st(v[0], r, voff, soff);
+  } else {
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 w;
+    w[0] = __float_as_uint(v[0]);
+    w[1] = __float_as_uint(v[1]);
+    __builtin_amdgcn_raw_buffer_store_b64(w, r, voff, soff, 0);
+  }
+}
+
+// The coordinating wave of a scan tile, lane l = features VEC l .. VEC l + VEC - 1 of the
+// tile: between the two workgroup barriers of the data waves it publishes the tile's aggregate
+// (non-anchor tiles), looks back across tiles for the value entering the tile and writes the
+// value entering each sub-chunk to s_x. Look-back words: word w of tile t for feature lane L at
+// desc[(t * kLookBackWords + w) * n_lanes_pad + L]; w = 0..3 the tile's inclusive value
+// (anchors), 4 + 4 i + k the entry (i, k) of its aggregate map, 20 + i the entry i of its offset.
+template <int VEC>
+__device__ __forceinline__ void scan_coordinate(float (&s_map)[4][20][VEC * kWave], float (&s_x)[4][4][VEC * kWave],
+                                                unsigned long long* __restrict__ desc, i64 n_lanes_pad,
+                                                i64 lane0, int tt, int anchor_stride, uint32_t epoch,
+                                                int l) {
+  auto word = [&](int tile, int w, int f) {
+    return desc + (static_cast<i64>(tile) * kLookBackWords + w) * n_lanes_pad + lane0 + f;
+  };
+  const int anchor_a = tt > 0 ? ((tt - 1) / anchor_stride) * anchor_stride : 0;
+  const bool anchor = (tt % anchor_stride) == 0;
+  // the anchor's inclusive value, loaded now so that it arrives while the data waves load
+  unsigned long long pf[VEC][4];
+#pragma unroll
+  for (int f = 0; f < VEC; ++f)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      pf[f][e] = tt > 0 ? __hip_atomic_load(word(anchor_a, e, f), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+  __syncthreads();  // the data waves' maps are in LDS
+#pragma unroll
+  for (int f = 0; f < VEC; ++f) {
+    const int lf = VEC * l + f;  // the feature's column in LDS
+    auto load_map = [&](int w, float (&Mw)[16], float (&vw)[4]) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) Mw[e] = s_map[w][e][lf];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vw[e] = s_map[w][16 + e][lf];
+    };
+    if (!anchor) {
+      // the tile's aggregate: sub-chunk maps 3 o 2 o 1 o 0, published before any wait
+      float G[16], gv[4];
+      load_map(0, G, gv);
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        float Mw[16], vw[4];
+        load_map(w, Mw, vw);
+        compose_after(Mw, vw, G, gv);  // (Mw, vw) <- (Mw, vw) o (G, gv)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) G[e] = Mw[e];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) gv[e] = vw[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) tag_store(word(tt, 4 + e, f), G[e], epoch);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tag_store(word(tt, 20 + e, f), gv[e], epoch);
+    }
+  }
+#pragma unroll
+  for (int f = 0; f < VEC; ++f) {
+    const int lf = VEC * l + f;
+    float xs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (tt > 0) {
+      // accumulated map of the tiles anchor_a+1 .. tt-1, folded from the nearest one back
+      float Macc[16], vacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int e = 0; e < 16; ++e) Macc[e] = (e % 5 == 0) ? 1.0f : 0.0f;
+      for (int p = tt - 1; p > anchor_a; --p) {
+        float Mp[16], vp[4];
+        while (true) {
+          bool ok = true;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) ok &= tag_load(word(p, 4 + e, f), epoch, Mp[e]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ok &= tag_load(word(p, 20 + e, f), epoch, vp[e]);
+          if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
+          __builtin_amdgcn_s_sleep(2);
+        }
+        compose_after(Macc, vacc, Mp, vp);  // (Macc, vacc) <- (Macc, vacc) o (Mp, vp)
+      }
+      float xa[4];
+      bool ok = true;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xa[e] = __uint_as_float(static_cast<uint32_t>(pf[f][e]));
+        ok &= static_cast<uint32_t>(pf[f][e] >> 32) == epoch;
+      }
+      while (__builtin_amdgcn_ballot_w64(!ok) != 0) {
+        __builtin_amdgcn_s_sleep(2);
+        ok = true;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ok &= tag_load(word(anchor_a, e, f), epoch, xa[e]);
+      }
+      mat4_vec(Macc, xa, vacc, xs);
+    }
+    // start values of the sub-chunks, then the tile's inclusive value
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_x[w][e][lf] = xs[e];
+      float Mw[16], vw[4], xn[4];
+#pragma unroll
+      for (int e = 0; e < 16; ++e) Mw[e] = s_map[w][e][lf];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vw[e] = s_map[w][16 + e][lf];
+      mat4_vec(Mw, xs, vw, xn);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) xs[e] = xn[e];
+    }
+    if (anchor) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tag_store(word(tt, e, f), xs[e], epoch);
+    }
+  }
+  __syncthreads();  // start values in LDS
+}
+
 }  // namespace slstm

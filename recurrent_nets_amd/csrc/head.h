@@ -170,9 +170,22 @@ __device__ __forceinline__ void cell_vjp_lin(const CellLin& L, const float lam[4
 // workgroups spread evenly over the chip's 256 CUs (160 KiB of LDS each): a workgroup walks all
 // of T, so a CU that received more of them than its share would set the kernel's duration. At
 // most 64 KiB, the per-workgroup default limit.
+// compute units of the current device (256 on MI355X when the query fails)
+inline int head_device_cus() {
+  static int cus = [] {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0)
+      return v;
+    return 256;
+  }();
+  return cus;
+}
+
 inline unsigned int head_spread_lds(long long n_wg, unsigned int static_lds) {
-  constexpr long long kCUs = 256, kLdsPerCU = 160 * 1024, kMax = 64 * 1024;
-  const long long per_cu = (n_wg + kCUs - 1) / kCUs;
+  constexpr long long kLdsPerCU = 160 * 1024, kMax = 64 * 1024;
+  const long long cus = head_device_cus();
+  const long long per_cu = (n_wg + cus - 1) / cus;
   long long bytes = kLdsPerCU / (per_cu < 1 ? 1 : per_cu) - static_cast<long long>(static_lds) - 1024;
   if (bytes > kMax) bytes = kMax;
   return bytes > 0 ? static_cast<unsigned int>(bytes) : 0u;

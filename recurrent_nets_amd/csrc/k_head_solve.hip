@@ -178,8 +178,9 @@ constexpr int head_pipe_group() {
   return 4 * DH < 64 ? 64 : 4 * DH;
 }
 
-// WAVES: the waves per SIMD the register budget is cut for (1: no cut). Two workgroups that share
-// a CU stay resident together only at 6 (80 registers a lane).
+// WAVES: the waves per SIMD the register budget is cut for (1: no cut). Uncut, the kernel takes
+// at most 96 VGPRs a lane, so up to 5 waves share a SIMD; the launcher cuts to 6 (80 registers a
+// lane) only when two workgroups a CU need more (d_head 32 at K >= 3).
 template <int DH, bool BF16, int CM, int WAVES>
 __global__ __launch_bounds__(kHeadPipeMaxThreads) __attribute__((amdgpu_waves_per_eu(WAVES))) void head_solve_pipe_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
@@ -327,10 +328,15 @@ hipError_t launch_head_solve(const void* P, bool p_bf16, const float* R, const f
   // both resident) about 15% faster; from three workgroups a CU on, the CU's issue rate bounds
   // both and the sweep's fewer instructions win (measured at d_head 32, T 4096, K 1 and 3).
   // Heads wider than 32 units always take the sweep.
-  const long long wg_per_cu = (static_cast<long long>(n_heads) * B + 255) / 256;
+  const long long cus = head_device_cus();
+  const long long wg_per_cu = (static_cast<long long>(n_heads) * B + cus - 1) / cus;
   if (dh <= 32 && wg_per_cu <= 2) {
     const unsigned int lds_p = head_spread_lds(static_cast<long long>(n_heads) * B, 24 * 1024);
-    const bool cut = wg_per_cu == 2 && K >= 2;
+    // waves a SIMD must hold, counting each workgroup's K + 2 groups of ceil(4 d_head / 64)
+    // waves as spread over the 4 SIMDs in whole rounds: uncut (96 VGPRs) a SIMD takes 5
+    const long long waves_per_group = (4 * dh + kWave - 1) / kWave;
+    const long long waves_per_simd = ((K + 2) * waves_per_group + 3) / 4 * wg_per_cu;
+    const bool cut = waves_per_simd > 5;
 #define SLSTM_HEAD_PIPE(CM_)                                                                                  \
   if (cut)                                                                                                    \
     head_solve_pipe_kernel<DH, BFV, CM_, 6><<<grid, (K + 2) * head_pipe_group<DH>(), lds_p, stream>>>(      \

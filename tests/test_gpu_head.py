@@ -195,6 +195,39 @@ def test_head_one_sweep_forms(gpu_lib, B, nh, dh, K):
             assert abs(e_gpu - e_ref) <= 1e-3 * e_ref
 
 
+@pytest.mark.parametrize("K", [2, 3])
+@pytest.mark.parametrize("forget,p_dtype", [("sigmoid", "f32"), ("exp", "bf16"), ("sigmoid", "bf16")])
+@pytest.mark.parametrize("B,nh,dh", [(1, 3, 32), (2, 100, 16), (3, 200, 16), (17, 32, 32), (2, 300, 8)])
+def test_head_one_sweep_forms_gates(gpu_lib, B, nh, dh, forget, p_dtype, K):
+    """Both one-sweep forms with the sigmoid forget gate and bf16 pre-activations: the wave-group
+    form (3 and 200 workgroups: one per CU) and the single-group sweep (600, 544 and 600
+    workgroups: three a CU, d_head 8, 16 and 32), on sampled (batch row, head) pairs, each solved
+    alone by the oracle (heads are independent recurrences)."""
+    T = 33
+    x = draw_head_inputs(1100 + B + nh + dh + K, B, T, nh * dh, nh, p_dtype=p_dtype, with_state0=True)
+    P, R, s0 = x["P"], x["R"], x["state0"]
+    case(f"head one-sweep B={B} heads={nh} d_head={dh} {forget} {p_dtype} K={K}")
+    gpu_lib.profile_reset()
+    gpu_lib.profile_enable(True)
+    S, h, st = gpu_lib.head_newton_forward(*_dev(P, R, s0), forget, K, 0.0, raise_on_divergence=False)
+    n_sweep = len(gpu_lib.profile_durations("head_solve"))
+    gpu_lib.profile_enable(False)
+    torch.cuda.synchronize()
+    assert n_sweep == 1 and st.iters == K
+    S, h = S.cpu(), h.cpu()
+    bar = H_TOL_BF16 if p_dtype == "bf16" else H_TOL_F32
+    pairs = sorted({(0, 0), (B - 1, nh - 1), (B // 2, nh // 2)})
+    for b, a in pairs:
+        cols = slice(a * dh, (a + 1) * dh)
+        Pa = to_np(P[b:b + 1, :, :, cols])
+        Ra = to_np(R[:, a:a + 1])
+        s0a = to_np(s0[b:b + 1, :, cols])
+        S_ref, st_ref = ref.newton_head(Pa, Ra, s0a, forget, K)
+        err = h_rel_err(h[b:b + 1, :, cols], S_ref[..., 3, :], h_floor(forget, bar))
+        assert err < bar, (b, a, err)
+        assert _state_err(S[b:b + 1, :, :, cols], S_ref) < (2e-2 if p_dtype == "bf16" else 1e-4)
+
+
 def test_head_one_sweep_zero_init_exact(gpu_lib):
     """The one-sweep kernel from a zero iterate: after K = T iterations the iterate is the exact
     solution (the sequential one). Sigmoid forget gate: with the exponential one, this zero
