@@ -130,12 +130,19 @@ KERNEL_SOURCES = {
     "newton_solve": ["recurrent_nets_amd/csrc/k_newton_pipe.hip", "recurrent_nets_amd/csrc/cell.h",
                      "recurrent_nets_amd/csrc/common.h", "recurrent_nets_amd/csrc/kernels.h"],
     "update": ["recurrent_nets_amd/csrc/k_update.hip", "recurrent_nets_amd/csrc/common.h"],
+    "final_residual": ["recurrent_nets_amd/csrc/k_residual.hip", "recurrent_nets_amd/csrc/cell.h",
+                       "recurrent_nets_amd/csrc/common.h"],
     "warm_start": ["recurrent_nets_amd/csrc/k_warm.hip", "recurrent_nets_amd/csrc/cell.h",
                    "recurrent_nets_amd/csrc/common.h"],
     "input_projection": ["recurrent_nets_amd/csrc/k_gemm.hip", "recurrent_nets_amd/csrc/common.h"],
     "backward": ["recurrent_nets_amd/csrc/k_backward.hip", "recurrent_nets_amd/csrc/affine4.h",
                  "recurrent_nets_amd/csrc/cell.h", "recurrent_nets_amd/csrc/common.h",
                  "recurrent_nets_amd/csrc/kernels.h"],
+    "packed_iteration": ["recurrent_nets_amd/csrc/k_newton_fused.hip", "recurrent_nets_amd/csrc/affine4.h",
+                         "recurrent_nets_amd/csrc/cell.h", "recurrent_nets_amd/csrc/common.h"],
+    "packed_backward": ["recurrent_nets_amd/csrc/k_backward.hip", "recurrent_nets_amd/csrc/affine4.h",
+                        "recurrent_nets_amd/csrc/cell.h", "recurrent_nets_amd/csrc/common.h",
+                        "recurrent_nets_amd/csrc/kernels.h"],
     "head_solve": ["recurrent_nets_amd/csrc/k_head_solve.hip", "recurrent_nets_amd/csrc/head.h",
                    "recurrent_nets_amd/csrc/affine4.h", "recurrent_nets_amd/csrc/cell.h",
                    "recurrent_nets_amd/csrc/common.h", "recurrent_nets_amd/csrc/kernels.h"],
@@ -821,11 +828,13 @@ def main():
             "solver": {"iters": pst.iters, "max_abs_F": pst.max_abs_F[-1], "diverged": pst.diverged},
             "kernels": pk,
             "roofline": {"bound": "hbm", "kernel": "newton_iteration", "achieved": it["GB_s"],
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(it["GB_s"] / HBM_PEAK_GBS, 4)},
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(it["GB_s"] / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("packed_iteration", w.name)},
             "backward": {"kernel_avg_ms": round(pb, 4), "gradients_in": "dL/dh, dL/d final states",
                          "roofline": {"bound": "hbm", "kernel": "backward", "achieved": round(pb_gbs, 1),
                                       "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                      "frac": round(pb_gbs / HBM_PEAK_GBS, 4)}}}
+                                      "frac": round(pb_gbs / HBM_PEAK_GBS, 4),
+                                      "traffic": measured_traffic("packed_backward", w.name)}}}
         del pws, pbws, dPp, dRp, d0p, g_hp, g_fp, fin
         torch.cuda.empty_cache()
 
