@@ -355,7 +355,7 @@ slstm_status slstm_backward_varlen(const void* P, slstm_dtype P_dtype, const flo
  * Head mixing ([SL] "Cell", the mix table's 'head' row; [XL] "Method" item 2 and the one-head
  * step pseudocode: recurrent matrices from h' to every gate, block-diagonal with one block per
  * head, no mixing across heads). R is (4, n_heads, d_head, d_head) float32, 16-byte aligned,
- * n_heads * d_head = d_h, d_head one of 8, 16, 32, 64; unit i of head a (feature
+ * n_heads * d_head = d_h, d_head one of 8, 16, 32, 64, 128; unit i of head a (feature
  * j = a d_head + i) has the pre-activations x~_g = P[.., g, j] + sum_k R[g, a, i, k] h'[a d_head + k].
  * Every other argument is as for the channelwise calls (P, states, h_out, final_state, state0
  * layouts, forget modes with the floored read-out flag, statuses, stream semantics).
@@ -365,8 +365,9 @@ slstm_status slstm_backward_varlen(const void* P, slstm_dtype P_dtype, const flo
  * residual at the iterate and solves the block-bidiagonal system with the Jacobian applied in
  * factored form (the unit's own-state columns plus the gate Jacobian times R_g Delta h'), so no
  * (4 d_head)^2 block is formed; the solve is a recurrence along T and parallelism comes from
- * B * n_heads. With tol = 0 and max_iters <= 4 the warm start and all iterations run as one
- * kernel, pipelined along T; otherwise the warm start, then one kernel per iteration.
+ * B * n_heads. With tol = 0, max_iters <= 4 and d_head <= 64 the warm start and all iterations
+ * run as one kernel, pipelined along T; otherwise (and always for heads of 128 units, whose
+ * pipeline stages would not fit the register file) the warm start, then one kernel per iteration.
  * Workspace: slstm_head_newton_workspace_bytes (0 if the sizes are invalid).
  * slstm_head_sequential_forward: the step loop, one workgroup per (batch row, head); no
  * workspace.
@@ -374,9 +375,9 @@ slstm_status slstm_backward_varlen(const void* P, slstm_dtype P_dtype, const flo
  * `states`, as slstm_backward ([SL] "Backward"): g_states (B, T, 4, d_h), g_h (B, T, d_h) and
  * g_final (B, 4, d_h) are the loss's direct gradients (each may be NULL: zero); outputs dP
  * (B, T, 4, d_h) in dP_dtype (F32 or BF16, rounded to nearest even), dR (4, n_heads, d_head,
- * d_head), dbias (4, d_h; may be NULL), dstate0 (B, 4, d_h; may be NULL); d_head 8, 16 or 32
- * (64 is rejected with SLSTM_EINVAL: a lane's block row, column and dR row would not fit in
- * registers). One workgroup per
+ * d_head), dbias (4, d_h; may be NULL), dstate0 (B, 4, d_h; may be NULL); d_head 8, 16, 32 or
+ * 64 (128 is rejected with SLSTM_EINVAL: a lane's block row and dR row would not fit in
+ * registers, nor the head's transposed blocks in LDS). One workgroup per
  * (batch row, head) walks T backwards; dR and dbias are added over the batch in a fixed order
  * from per-row partial sums in the workspace (slstm_head_backward_workspace_bytes; 0 if the
  * sizes are invalid), so results are reproducible bit for bit.

@@ -658,7 +658,7 @@ bool head_shape_ok(int d, int n_heads) {
 
 slstm_status check_heads(int d, int n_heads, const float* R) {
   if (!head_shape_ok(d, n_heads))
-    return fail(SLSTM_EINVAL, "n_heads (%d) must divide d_h (%d) into heads of 8, 16, 32 or 64 units", n_heads, d);
+    return fail(SLSTM_EINVAL, "n_heads (%d) must divide d_h (%d) into heads of 8, 16, 32, 64 or 128 units", n_heads, d);
   if (!aligned(R, 16)) return fail(SLSTM_EINVAL, "R must be 16-byte aligned");
   return SLSTM_OK;
 }
@@ -999,8 +999,10 @@ slstm_status head_newton_forward(const void* P, slstm_dtype P_dtype, const float
     HIP_TRY(slstm::launch_seq_table(seqs.cu, seqs.n, T, tab, st));
     seqs.tab = tab;
   }
-  // the one-sweep kernel serves fixed counts on unpacked rows; packed rows iterate kernel by kernel
-  if (seqs.cu == nullptr && tol == 0.0f && max_iters <= slstm::kHeadSolveMaxIters) {
+  // the one-sweep kernel serves fixed counts on unpacked rows of heads up to 64 units; packed rows
+  // and 128-unit heads iterate kernel by kernel
+  if (seqs.cu == nullptr && tol == 0.0f && max_iters <= slstm::kHeadSolveMaxIters &&
+      d_h / n_heads <= slstm::kHeadSolveMaxWidth) {
     // a fixed count of iterations: the whole solve in one sweep over T
     HIP_TRY(timed(SLSTM_KERNEL_HEAD_SOLVE, st, [&] {
       return slstm::launch_head_solve(P, bf16, R, state0, states, h_out, B, T, d_h, n_heads, cm, max_iters,
@@ -1048,7 +1050,7 @@ slstm_status head_backward(const void* P, slstm_dtype P_dtype, const float* R, c
   s = check_heads(d_h, n_heads, R);
   if (s != SLSTM_OK) return s;
   if (!slstm::head_backward_width_supported(d_h / n_heads))
-    return fail(SLSTM_EINVAL, "the head-mixing backward takes heads of 8, 16 or 32 units (got %d)", d_h / n_heads);
+    return fail(SLSTM_EINVAL, "the head-mixing backward takes heads of 8, 16, 32 or 64 units (got %d)", d_h / n_heads);
   if (dP == nullptr || dR == nullptr) return fail(SLSTM_EINVAL, "dP and dR must not be NULL");
   if (dP_dtype != SLSTM_F32 && dP_dtype != SLSTM_BF16) return fail(SLSTM_EINVAL, "unknown dP dtype %d", (int)dP_dtype);
   if (!aligned(dP, 4) || !aligned(dR, 4) || !aligned(dbias, 4) || !aligned(dstate0, 4) || !aligned(g_states, 4) ||

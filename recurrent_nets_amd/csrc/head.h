@@ -83,7 +83,6 @@ __device__ __forceinline__ float block_dot(const float row[DH], const float* __r
   return acc0 + acc1;
 }
 
-
 // One cell step under head mixing in linearised form: the next state s (c, n, m, h) from the
 // previous state pv (its h enters only through the pre-activations x, which already hold R h')
 // and the coefficients of the step's Jacobian in the structure the cell gives it (the nonzero
@@ -193,6 +192,17 @@ inline unsigned int head_spread_lds(long long n_wg, unsigned int static_lds) {
 
 // DH = d_head as a compile-time constant for the widths the kernels are built for
 #define SLSTM_HEAD_DH_DISPATCH(DHV, BODY) \
+  switch (DHV) {                          \
+    case 8: { constexpr int DH = 8; BODY; break; }    \
+    case 16: { constexpr int DH = 16; BODY; break; }  \
+    case 32: { constexpr int DH = 32; BODY; break; }  \
+    case 64: { constexpr int DH = 64; BODY; break; }  \
+    case 128: { constexpr int DH = 128; BODY; break; } \
+    default: return hipErrorInvalidValue;             \
+  }
+// the widths of the one-sweep Newton kernel (a 128-unit head's K + 2 stages exceed the register
+// file; such heads iterate kernel by kernel)
+#define SLSTM_HEAD_SWEEP_DH_DISPATCH(DHV, BODY) \
   switch (DHV) {                          \
     case 8: { constexpr int DH = 8; BODY; break; }    \
     case 16: { constexpr int DH = 16; BODY; break; }  \

@@ -247,7 +247,9 @@ __global__ __launch_bounds__(4 * DH) void head_iter_kernel(const void* __restric
   }
 }
 
-bool head_width_supported(int d_head) { return d_head == 8 || d_head == 16 || d_head == 32 || d_head == 64; }
+bool head_width_supported(int d_head) {
+  return d_head == 8 || d_head == 16 || d_head == 32 || d_head == 64 || d_head == 128;
+}
 
 hipError_t launch_head_sequential(const void* P, bool p_bf16, const float* R, const float* state0, float* S,
                                   float* h_out, float* final_state, int B, int T, int d, int n_heads,

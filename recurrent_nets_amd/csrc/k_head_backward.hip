@@ -15,7 +15,9 @@
 // the head (staged in LDS from the states), the cell's gate and own-state Jacobians, dP, then
 // one LDS exchange of dP so each lane can form its column's share of R_g^T dP_g, summed over the
 // quad. The step is branch-free and the dP stores are batched per 8-step block, as in the
-// one-sweep forward. dR and dbias leave as per-row partial sums that a second kernel adds over
+// one-sweep forward. Heads of 64 units keep the block columns in LDS instead (the head's four
+// transposed blocks, 64 KiB, rows padded so that the 16 lanes the LDS serves together hit
+// distinct banks): a lane's row, column and dR row (192 floats) would not fit the register file. dR and dbias leave as per-row partial sums that a second kernel adds over
 // the batch in a fixed order.
 #include "cell.h"
 #include "head.h"
@@ -30,6 +32,42 @@ __device__ __forceinline__ void load_block_col(const float* __restrict__ R, int 
   const float* src = R + (static_cast<i64>(g) * nh + a) * DH * DH + i;
 #pragma unroll
   for (int k = 0; k < DH; ++k) col[k] = src[k * DH];
+}
+
+// Transposed blocks of head a in LDS for heads of 64 units: column i of gate g's block at
+// colT[g * kColGate + i * kColRow + k] = R[g, a, k, i]. Rows padded by 4 floats and gates by 16, so
+// lane 4 i' + g (i' = 0..3, the 16 lanes served together) reads banks 16 g + 4 i' + (0..3).
+template <int DH> struct ColLds {
+  static constexpr int kColRow = DH + 4;
+  static constexpr int kColGate = DH * kColRow + 16;
+  static constexpr int kFloats = 4 * kColGate;
+};
+
+template <int DH>
+__device__ __forceinline__ void fill_col_lds(const float* __restrict__ R, int nh, int a, float* colT) {
+  // thread e of the workgroup copies entries e, e + 4 DH, ...: consecutive threads read
+  // consecutive entries of a block row (coalesced) and write them down an LDS column
+  for (int e = threadIdx.x; e < 4 * DH * DH; e += 4 * DH) {
+    const int g = e / (DH * DH), rest = e - g * DH * DH, k = rest / DH, i = rest - k * DH;
+    colT[g * ColLds<DH>::kColGate + i * ColLds<DH>::kColRow + k] = R[(static_cast<i64>(g) * nh + a) * DH * DH + rest];
+  }
+}
+
+// sum over k of col[k] v[k], col and v both in LDS (float4 reads, two accumulators)
+template <int DH>
+__device__ __forceinline__ float lds_col_dot(const float* col, const float* v) {
+  const float4* c4 = reinterpret_cast<const float4*>(col);
+  const float4* v4 = reinterpret_cast<const float4*>(v);
+  float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+  for (int k = 0; k < DH / 4; ++k) {
+    const float4 c = c4[k], x = v4[k];
+    acc0 = fmaf(c.x, x.x, acc0);
+    acc1 = fmaf(c.y, x.y, acc1);
+    acc0 = fmaf(c.z, x.z, acc0);
+    acc1 = fmaf(c.w, x.w, acc1);
+  }
+  return acc0 + acc1;
 }
 
 // Packed sequences (PACKED, one batch row): walking T backwards, the kernel follows the sequence
@@ -47,15 +85,18 @@ __global__ __launch_bounds__(4 * DH) void head_backward_kernel(
   __shared__ __attribute__((aligned(16))) float hbuf[2][DH];      // h of the state before step t
   __shared__ __attribute__((aligned(16))) float dxbuf[2][4][DH];  // dP of step t, per gate
   __shared__ float junk[4 * DH];
+  constexpr bool kColLds = DH >= 64;
+  __shared__ __attribute__((aligned(16))) float colT[kColLds ? ColLds<DH>::kFloats : 4];
   const int tid = threadIdx.x;
   const int i = tid >> 2, g = tid & 3;
   const int a = blockIdx.x, b = blockIdx.y;
   const int j = a * DH + i;
   const i64 dd = d;
   const GateSel sel(g);
-  float row[DH], col[DH], dr[DH];
+  float row[DH], col[kColLds ? 1 : DH], dr[DH];
   load_block_row<DH>(R, nh, a, i, g, row);
-  load_block_col<DH>(R, nh, a, i, g, col);
+  if constexpr (kColLds) fill_col_lds<DH>(R, nh, a, colT);  // visible after the first barrier below
+  else load_block_col<DH>(R, nh, a, i, g, col);
 #pragma unroll
   for (int k = 0; k < DH; ++k) dr[k] = 0.0f;
   float db = 0.0f;
@@ -149,6 +190,12 @@ __global__ __launch_bounds__(4 * DH) void head_backward_kernel(
         dr[4 * k + 2] = fmaf(dxm, hv.z, dr[4 * k + 2]);
         dr[4 * k + 3] = fmaf(dxm, hv.w, dr[4 * k + 3]);
       }
+      if constexpr (kColLds) {
+        // keep the step's dR update here: left free, the compiler sinks all eight steps' updates
+        // to the end of the block and holds their h rows in scratch
+#pragma unroll
+        for (int k = 0; k < DH; ++k) asm volatile("" : "+v"(dr[k]));
+      }
       db += dxm;
       const float la = sel(dpv[0], dpv[1], dpv[2], 0.0f);  // own-state columns of J^T lam (g < 3)
       dxbuf[r & 1][g][i] = dx;
@@ -156,7 +203,10 @@ __global__ __launch_bounds__(4 * DH) void head_backward_kernel(
       head_lds_barrier();
       // h' column of J^T lam for unit i: sum over gates of (R_g^T dP_g)[i]
       float ys[4];
-      quad_gather(block_dot<DH>(col, dxbuf[r & 1][g]), ys);
+      if constexpr (kColLds)
+        quad_gather(lds_col_dot<DH>(&colT[g * ColLds<DH>::kColGate + i * ColLds<DH>::kColRow], dxbuf[r & 1][g]), ys);
+      else
+        quad_gather(block_dot<DH>(col, dxbuf[r & 1][g]), ys);
       const float lprev = g == 3 ? (ys[0] + ys[1]) + (ys[2] + ys[3]) : la;
       if constexpr (PACKED) {
         if (seq_first) {  // the adjoint of state0[rs]; nothing crosses into the previous sequence
@@ -216,13 +266,16 @@ size_t head_backward_part_floats(int B, int d, int n_heads) {
   return static_cast<size_t>(B) * 4 * d * dh + static_cast<size_t>(B) * 4 * d;
 }
 
-bool head_backward_width_supported(int d_head) { return d_head == 8 || d_head == 16 || d_head == 32; }
+bool head_backward_width_supported(int d_head) {
+  return d_head == 8 || d_head == 16 || d_head == 32 || d_head == 64;
+}
 
 #define SLSTM_HEAD_BWD_DH_DISPATCH(DHV, BODY)        \
   switch (DHV) {                                     \
     case 8: { constexpr int DH = 8; BODY; break; }   \
     case 16: { constexpr int DH = 16; BODY; break; } \
     case 32: { constexpr int DH = 32; BODY; break; } \
+    case 64: { constexpr int DH = 64; BODY; break; } \
     default: return hipErrorInvalidValue;            \
   }
 
@@ -235,7 +288,9 @@ hipError_t launch_head_backward(const void* P, bool p_bf16, const float* R, cons
   float* dR_part = part;
   float* db_part = part + static_cast<i64>(B) * 4 * d * dh;
   const dim3 grid(static_cast<unsigned>(n_heads), static_cast<unsigned>(B));
-  const unsigned int lds = head_spread_lds(static_cast<long long>(n_heads) * B, 8192);
+  // static LDS of a workgroup: the exchange buffers, and for 64-unit heads the transposed blocks
+  const unsigned int lds = head_spread_lds(static_cast<long long>(n_heads) * B,
+                                           8192 + (dh >= 64 ? ColLds<64>::kFloats * 4u : 0u));
   const bool packed = seqs.cu != nullptr;
 #define SLSTM_HEAD_BWD(BF, DB, CM_)                                                                             \
   do {                                                                                                          \
@@ -250,7 +305,6 @@ hipError_t launch_head_backward(const void* P, bool p_bf16, const float* R, cons
 #define SLSTM_HEAD_BWD_TF(CM_) SLSTM_HEAD_BWD(true, false, CM_)
 #define SLSTM_HEAD_BWD_FT(CM_) SLSTM_HEAD_BWD(false, true, CM_)
 #define SLSTM_HEAD_BWD_FF(CM_) SLSTM_HEAD_BWD(false, false, CM_)
-  // d_head 64 would hold its row, column and dR row (192 registers) past the register file
   SLSTM_HEAD_BWD_DH_DISPATCH(dh, {
     if (p_bf16) {
       if (dp_bf16) { SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_HEAD_BWD_TT) }

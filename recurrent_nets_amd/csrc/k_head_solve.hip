@@ -372,7 +372,7 @@ hipError_t launch_head_solve(const void* P, bool p_bf16, const float* R, const f
   }
 #define SLSTM_HEAD_SOLVE_T(CM_) SLSTM_HEAD_SOLVE_K(true, CM_)
 #define SLSTM_HEAD_SOLVE_F(CM_) SLSTM_HEAD_SOLVE_K(false, CM_)
-  SLSTM_HEAD_DH_DISPATCH(dh, {
+  SLSTM_HEAD_SWEEP_DH_DISPATCH(dh, {
     if (p_bf16) { SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_HEAD_SOLVE_T) }
     else { SLSTM_CELL_MODE_DISPATCH(cell_mode, SLSTM_HEAD_SOLVE_F) }
   })

@@ -117,6 +117,7 @@ hipError_t launch_head_iteration(const void* P, bool p_bf16, const float* R, con
 // writes S (iterate K), h_out (may be NULL), the residual maxima of iterates 0..K into ctl's
 // error slots and ctl->iters = K.
 constexpr int kHeadSolveMaxIters = 4;
+constexpr int kHeadSolveMaxWidth = 64;  // widest head the one-sweep kernel takes
 hipError_t launch_head_solve(const void* P, bool p_bf16, const float* R, const float* state0, float* S,
                              float* h_out, int B, int T, int d, int n_heads, int cell_mode, int K, bool zero_init,
                              Control* ctl, hipStream_t stream);

@@ -207,8 +207,10 @@ def test_binding_checks_offsets():
 
 
 def test_head_argument_checks(lib):
-    # head mixing: n_heads must split d_h into heads of 8, 16, 32 or 64 units; R 16-byte aligned
+    # head mixing: n_heads must split d_h into heads of 8, 16, 32, 64 or 128 units; R 16-byte aligned
     assert lib.slstm_head_newton_workspace_bytes(2, 64, 64, 2) > 0
+    assert lib.slstm_head_newton_workspace_bytes(2, 64, 128, 1) > 0       # d_head 128
+    assert lib.slstm_head_newton_workspace_bytes(2, 64, 512, 2) == 0      # d_head 256
     for nh in (0, 3, 64, 128):
         assert lib.slstm_head_newton_workspace_bytes(2, 64, 64, nh) == 0
     args = dict(P=ctypes.c_void_p(256), dt=0, R=ctypes.c_void_p(256), s0=None, S=ctypes.c_void_p(256), h=None,
@@ -232,9 +234,11 @@ def test_head_argument_checks(lib):
 
 
 def test_head_backward_argument_checks(lib):
-    # widths: 8, 16, 32 only (a block row, column and dR row per lane must fit in registers)
+    # widths: 8 to 64 (a lane's block row and dR row must fit in registers, the head's
+    # transposed blocks in LDS)
     assert lib.slstm_head_backward_workspace_bytes(2, 64, 64, 2) > 0
-    assert lib.slstm_head_backward_workspace_bytes(2, 64, 128, 2) == 0      # d_head 64
+    assert lib.slstm_head_backward_workspace_bytes(2, 64, 128, 2) > 0       # d_head 64
+    assert lib.slstm_head_backward_workspace_bytes(2, 64, 256, 2) == 0      # d_head 128
     assert lib.slstm_head_backward_workspace_bytes(2, 64, 64, 3) == 0
     args = dict(P=ctypes.c_void_p(256), dt=0, R=ctypes.c_void_p(256), s0=None, S=ctypes.c_void_p(256), gs=None,
                 gh=None, gf=None, dP=ctypes.c_void_p(256), dpt=0, dR=ctypes.c_void_p(256), db=None, d0=None, B=2,
@@ -244,8 +248,8 @@ def test_head_backward_argument_checks(lib):
         a = dict(args)
         a.update(kw)
         return lib.slstm_head_backward(*a.values())
-    assert call(d=128) == slstm.EINVAL
-    assert "8, 16 or 32" in lib.slstm_last_error().decode()
+    assert call(d=256) == slstm.EINVAL
+    assert "8, 16, 32 or 64" in lib.slstm_last_error().decode()
     assert call(nh=3) == slstm.EINVAL
     assert call(dP=None) == slstm.EINVAL
     assert call(dR=None) == slstm.EINVAL

@@ -5,7 +5,8 @@ the float64 oracle's dense per-head forms.
 
 Covered: the sequential forward and the Newton solve (warm and zero start, fixed count and early
 stop, state0 and final state; the one-sweep kernel for a fixed count of up to 4 iterations and
-the per-iteration kernels otherwise) for every supported head width, both forget-gate forms, the
+the per-iteration kernels otherwise, and always for heads of 128 units) for every supported
+head width, both forget-gate forms, the
 floored read-out and bf16 pre-activations; T = 1 and T not a multiple of the kernels' 8-step
 prefetch; many narrow heads; diagonal blocks against the channelwise solver at a larger size;
 and the head-mixing benchmark workload at full size on sampled (batch row, head) pairs: each
@@ -21,7 +22,7 @@ from workloads import draw_head_inputs
 pytestmark = pytest.mark.gpu
 
 DEV = "cuda"
-WIDTHS = [8, 16, 32, 64]
+WIDTHS = [8, 16, 32, 64, 128]
 
 
 def _dev(*ts):
@@ -116,7 +117,7 @@ def test_head_newton_floored(gpu_lib, forget):
     assert h_rel_err(h, S_ref[..., 3, :], h_floor(forget, H_TOL_F32)) < H_TOL_F32
 
 
-@pytest.mark.parametrize("dh", [16, 64])
+@pytest.mark.parametrize("dh", [16, 64, 128])
 def test_head_newton_early_stop(gpu_lib, dh):
     """tol > 0: the solve stops at the first iterate whose residual maximum is below tol; the
     stop is global over every (batch row, head)."""
