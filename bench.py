@@ -389,8 +389,8 @@ def head_context(slstm, torch, dev, steps):
                      "note": "one workgroup per (batch row, head) walks T, its stages a tick apart on separate wave groups; the tick's chain and the CU's issue rate bound it",
                      "hbm_view": {"achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                   "frac": round(gbs / HBM_PEAK_GBS, 4)},
-                     "alu_view": {"achieved": round(tfs, 2), "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                                  "frac": round(tfs / FP32_VECTOR_PEAK_TFLOPS, 4)},
+                     "alu_view": {"achieved": round(tfs, 2), "peak": FP32_UNPACKED_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                  "frac": round(tfs / FP32_UNPACKED_PEAK_TFLOPS, 4)},
                      "traffic": measured_traffic("head_solve", HEAD_WORKLOAD)}}
 
 
