@@ -35,8 +35,11 @@ __device__ __forceinline__ float exp_fast(float x) { return __builtin_amdgcn_exp
 __device__ __forceinline__ float rcp_fast(float x) { return __builtin_amdgcn_rcpf(x); }
 // sigma(x) = 1 / (1 + e^-x)
 __device__ __forceinline__ float sigmoidf(float x) { return rcp_fast(1.0f + exp_fast(-x)); }
-// tanh x = 1 - 2 / (1 + e^{2x})
-__device__ __forceinline__ float tanh_fast(float x) { return 1.0f - 2.0f * rcp_fast(1.0f + exp_fast(2.0f * x)); }
+// tanh x = 1 - 2 / (1 + e^{2x}), e^{2x} = 2^(x (2 log2 e)): the doubled constant is exact, so this
+// is bitwise exp_fast(2 x) with one multiply fewer
+__device__ __forceinline__ float tanh_fast(float x) {
+  return 1.0f - 2.0f * rcp_fast(1.0f + __builtin_amdgcn_exp2f(x * (2.0f * kLog2e)));
+}
 // log sigma(x) = -softplus(-x) = -(max(-x, 0) + ln(1 + e^{-|x|})), finite for any finite x
 __device__ __forceinline__ float log_sigmoidf(float x) {
   return -(fmaxf(-x, 0.0f) + kLn2 * __builtin_amdgcn_logf(1.0f + exp_fast(-fabsf(x))));
@@ -75,13 +78,63 @@ __device__ __forceinline__ CellIn state0_of(const float* state0, int s, unsigned
   return {s0[j], s0[ud + j], s0[2 * ud + j], s0[3 * ud + j]};
 }
 
-// One step. Writes the next state s[4] = (c, n, m, h); with JAC also A[16] row-major
-// (A[4*row + col] = d s[row] / d prev[col]).
+// The stabilised gates of a step from a = l + m' and i~: m = max(a, i~) (a tie takes a) and
+// (i', f') = (e^{i~ - m}, e^{a - m}), one of which is e^0 = 1 and the other e^{-|a - i~|}, so one
+// exponential gives both, bitwise.
+__device__ __forceinline__ void stab_gates(float a, float it, float& m, float& ig, float& fg) {
+  const bool beta = a >= it;
+  const float e = exp_fast(-fabsf(a - it));
+  m = beta ? a : it;
+  ig = beta ? e : 1.0f;
+  fg = beta ? 1.0f : e;
+}
+
+// The values of one step that the state, its Jacobian and its linearisation share.
 //
 // m = max(a, i~) makes one of the two gates exactly e^0 = 1: with beta = (a >= i~) and
 // e = e^{-|a - i~|}, (i', f') = (e, 1) when beta and (1, e) otherwise. Both are bitwise the
-// values e^{i~ - m} and e^{a - m}, from one exponential. On the branch the max takes, the
-// derivatives of the c and n rows reduce to (with l' = dl/df~ and D = l' r_f - r_i)
+// values e^{i~ - m} and e^{a - m}, from one exponential.
+struct CellCore {
+  float z, o, dlf, e, ig, fg, c, n, m, h, rn;
+  bool beta;
+  Readout rdn;
+};
+__device__ __forceinline__ CellCore cell_core(const CellIn& pv, float pz, float pi, float pf, float po, float rz,
+                                              float ri, float rf, float ro, bool sig_forget, bool floored) {
+  CellCore k;
+  const float zt = fmaf(rz, pv.h, pz);
+  const float it = fmaf(ri, pv.h, pi);
+  const float ft = fmaf(rf, pv.h, pf);
+  const float ot = fmaf(ro, pv.h, po);
+  k.z = tanh_fast(zt);
+  k.o = sigmoidf(ot);
+  float lf;
+  if (sig_forget) {
+    lf = log_sigmoidf(ft);
+    k.dlf = sigmoidf(-ft);
+  } else {
+    lf = ft;
+    k.dlf = 1.0f;
+  }
+  const float a = lf + pv.m;
+  k.beta = a >= it;
+  k.m = k.beta ? a : it;
+  k.e = exp_fast(-fabsf(a - it));
+  k.ig = k.beta ? k.e : 1.0f;
+  k.fg = k.beta ? 1.0f : k.e;
+  k.c = fmaf(k.fg, pv.c, k.ig * k.z);
+  k.n = fmaf(k.fg, pv.n, k.ig);
+  k.rdn = readout(k.n, k.m, floored);
+  k.rn = k.rdn.rD;
+  k.h = k.o * k.c * k.rn;
+  return k;
+}
+
+// One step. Writes the next state s[4] = (c, n, m, h); with JAC also A[16] row-major
+// (A[4*row + col] = d s[row] / d prev[col]).
+//
+// On the branch the max takes, the derivatives of the c and n rows reduce to (with
+// l' = dl/df~ and D = l' r_f - r_i)
 //   dc/dm' = e (beta ? -z : c'),   dn/dm' = e (beta ? -1 : n'),
 //   dc/dh' = D dc/dm' + i' dz/dh',  dn/dh' = D dn/dm',
 // and dm/dm' = beta, dm/dh' = beta ? l' r_f : r_i. The h row is the quotient rule through c
@@ -90,37 +143,15 @@ template <bool JAC>
 __device__ __forceinline__ void cell_step(const CellIn& pv, float pz, float pi, float pf, float po,
                                           float rz, float ri, float rf, float ro, bool sig_forget,
                                           bool floored, float s[4], float A[16]) {
-  const float zt = fmaf(rz, pv.h, pz);
-  const float it = fmaf(ri, pv.h, pi);
-  const float ft = fmaf(rf, pv.h, pf);
-  const float ot = fmaf(ro, pv.h, po);
-  const float z = tanh_fast(zt);
-  const float o = sigmoidf(ot);
-  float lf, dlf;
-  if (sig_forget) {
-    lf = log_sigmoidf(ft);
-    dlf = sigmoidf(-ft);
-  } else {
-    lf = ft;
-    dlf = 1.0f;
-  }
-  const float a = lf + pv.m;
-  const bool beta = a >= it;
-  const float m = beta ? a : it;
-  const float e = exp_fast(-fabsf(a - it));
-  const float ig = beta ? e : 1.0f;
-  const float fg = beta ? 1.0f : e;
-  const float c = fmaf(fg, pv.c, ig * z);
-  const float n = fmaf(fg, pv.n, ig);
-  const Readout rdn = readout(n, m, floored);
-  const float rn = rdn.rD;
-  const float h = o * c * rn;
-  s[0] = c;
-  s[1] = n;
-  s[2] = m;
-  s[3] = h;
+  const CellCore k = cell_core(pv, pz, pi, pf, po, rz, ri, rf, ro, sig_forget, floored);
+  s[0] = k.c;
+  s[1] = k.n;
+  s[2] = k.m;
+  s[3] = k.h;
   if constexpr (JAC) {
-    const float lrf = dlf * rf;
+    const float z = k.z, o = k.o, e = k.e, ig = k.ig, fg = k.fg, c = k.c, h = k.h, rn = k.rn;
+    const bool beta = k.beta;
+    const float lrf = k.dlf * rf;
     const float D = lrf - ri;
     const float c_m = e * (beta ? -z : pv.c);
     const float n_m = e * (beta ? -1.0f : pv.n);
@@ -140,12 +171,63 @@ __device__ __forceinline__ void cell_step(const CellIn& pv, float pz, float pi, 
       A[14] = fmaf(q1, c_m, -q2 * n_m);
       A[15] = fmaf(q1, c_h, fmaf(-q2, n_h, (c * rn) * do_dh));
     } else {
-      const float qn = q2 * rdn.dn, qm = q2 * rdn.dm;
+      const float qn = q2 * k.rdn.dn, qm = q2 * k.rdn.dm;
       A[13] = -qn * fg;
       A[14] = fmaf(q1, c_m, fmaf(-qn, n_m, -qm * A[10]));
       A[15] = fmaf(q1, c_h, fmaf(-qn, n_h, fmaf(-qm, A[11], (c * rn) * do_dh)));
     }
   }
+}
+
+// The Jacobian of one step in factored form, for recurrences that apply it to one vector per
+// step (Delta_t = A_t Delta_{t-1} + rhs_t) rather than compose it: with Delta' = (c', n', m', h')
+// and y = m' + D h' (the direction the gates see through a = l + m' and i~), the rows of A
+// above give
+//   A_c Delta' = f' c' + c_m y + g h'        (g = i' dz/dh')
+//   A_n Delta' = f' n' + n_m y
+//   A_m Delta' = r_i h' + (beta ? y : 0)
+//   A_h Delta' = q1 A_c Delta' - qn A_n Delta' - qm A_m Delta' + dov h'
+// (q1 = o / D, qn = (h / D) D_n, qm = (h / D) D_m, dov = (c / D) do/dh' = h (1 - o) r_o), which
+// reuses the c, n and m rows instead of forming the h row's four entries.
+struct DiagLin {
+  float fg, c_m, n_m, g, D, ri, q1, qn, qm, dov;
+  bool beta;
+};
+__device__ __forceinline__ void cell_step_diag(const CellIn& pv, float pz, float pi, float pf, float po, float rz,
+                                               float ri, float rf, float ro, bool sig_forget, bool floored,
+                                               float s[4], DiagLin& L) {
+  const CellCore k = cell_core(pv, pz, pi, pf, po, rz, ri, rf, ro, sig_forget, floored);
+  s[0] = k.c;
+  s[1] = k.n;
+  s[2] = k.m;
+  s[3] = k.h;
+  L.beta = k.beta;
+  L.fg = k.fg;
+  L.c_m = k.e * (k.beta ? -k.z : pv.c);
+  L.n_m = k.e * (k.beta ? -1.0f : pv.n);
+  L.g = k.ig * (fmaf(-k.z, k.z, 1.0f) * rz);
+  L.D = fmaf(k.dlf, rf, -ri);
+  L.ri = ri;
+  L.q1 = k.o * k.rn;
+  const float q2 = k.h * k.rn;
+  L.qn = floored ? q2 * k.rdn.dn : q2;
+  L.qm = floored ? q2 * k.rdn.dm : 0.0f;
+  L.dov = k.h * (1.0f - k.o) * ro;
+}
+
+// x <- A x + rhs for the step L linearises (x holds Delta_{t-1} on entry, Delta_t on return)
+__device__ __forceinline__ void diag_jvp(const DiagLin& L, bool floored, const float rhs[4], float x[4]) {
+  const float y = fmaf(L.D, x[3], x[2]);
+  const float u0 = fmaf(L.fg, x[0], fmaf(L.c_m, y, L.g * x[3]));
+  const float u1 = fmaf(L.fg, x[1], L.n_m * y);
+  const float u2 = fmaf(L.ri, x[3], L.beta ? y : 0.0f);
+  const float tail = fmaf(L.dov, x[3], rhs[3]);
+  const float x3 = floored ? fmaf(L.q1, u0, fmaf(-L.qn, u1, fmaf(-L.qm, u2, tail)))
+                           : fmaf(L.q1, u0, fmaf(-L.qn, u1, tail));
+  x[0] = u0 + rhs[0];
+  x[1] = u1 + rhs[1];
+  x[2] = u2 + rhs[2];
+  x[3] = x3;
 }
 
 // Vector-Jacobian product of one step at the state before it (pv) and its pre-activations:

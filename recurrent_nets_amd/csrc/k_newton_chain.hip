@@ -130,8 +130,9 @@ __global__ __launch_bounds__(kChainBlock, SLSTM_CHAIN_MIN_WAVES) void newton_cha
     for (int u = 0; u < TC; ++u) {
       const int t = t0 + u;
       if (t < T) {
-        float f[4], A[16];
-        cell_step<true>(pv, pg[u][0], pg[u][1], pg[u][2], pg[u][3], rz, ri, rf, ro, sig, floored, f, A);
+        float f[4];
+        DiagLin L;
+        cell_step_diag(pv, pg[u][0], pg[u][1], pg[u][2], pg[u][3], rz, ri, rf, ro, sig, floored, f, L);
         float r[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -159,15 +160,7 @@ __global__ __launch_bounds__(kChainBlock, SLSTM_CHAIN_MIN_WAVES) void newton_cha
 #pragma unroll
           for (int k = 0; k < 4; ++k) x[k] = r[k];  // s_0 is data: Delta_1 = rhs_1
         } else {
-          // Delta_t = A_t Delta_t-1 + rhs_t over the 12 entries that are not structural zeros
-          const float x0 = fmaf(A[0], x[0], fmaf(A[2], x[2], fmaf(A[3], x[3], r[0])));
-          const float x1 = fmaf(A[5], x[1], fmaf(A[6], x[2], fmaf(A[7], x[3], r[1])));
-          const float x2 = fmaf(A[10], x[2], fmaf(A[11], x[3], r[2]));
-          const float x3 = fmaf(A[12], x[0], fmaf(A[13], x[1], fmaf(A[14], x[2], fmaf(A[15], x[3], r[3]))));
-          x[0] = x0;
-          x[1] = x1;
-          x[2] = x2;
-          x[3] = x3;
+          diag_jvp(L, floored, r, x);  // Delta_t = A_t Delta_t-1 + rhs_t, A_t in factored form
         }
         float sn[4];
         const unsigned o = u * 4u * ud + j;

@@ -124,10 +124,8 @@ __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_
     float c = hv[0], n = hv[1], m = hv[2];
 #pragma unroll
     for (int u = 0; u < TC; ++u) {
-      const float a = s[u][1] + m;
-      const float mn = (a >= s[u][2]) ? a : s[u][2];  // a tie takes a
-      const float ig = exp_fast(s[u][2] - mn);
-      const float fg = exp_fast(a - mn);
+      float mn, ig, fg;
+      stab_gates(s[u][1] + m, s[u][2], mn, ig, fg);
       c = fmaf(fg, c, ig * s[u][0]);
       n = fmaf(fg, n, ig);
       m = mn;
@@ -160,8 +158,9 @@ __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_
       for (int u = 0; u < TC; ++u) {
         const int t = t0 + u;
         if (t < T) {
-          float f[4], A[16], r[4];
-          cell_step<true>(pv, p[u][0], p[u][1], p[u][2], p[u][3], rz, ri, rf, ro, sig, floored, f, A);
+          float f[4], r[4];
+          DiagLin L;
+          cell_step_diag(pv, p[u][0], p[u][1], p[u][2], p[u][3], rz, ri, rf, ro, sig, floored, f, L);
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             r[e] = f[e] - s[u][e];
@@ -177,14 +176,7 @@ __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = r[e];  // s_0 is data: Delta_1 = rhs_1
           } else {
-            const float x0 = fmaf(A[0], x[0], fmaf(A[2], x[2], fmaf(A[3], x[3], r[0])));
-            const float x1 = fmaf(A[5], x[1], fmaf(A[6], x[2], fmaf(A[7], x[3], r[1])));
-            const float x2 = fmaf(A[10], x[2], fmaf(A[11], x[3], r[2]));
-            const float x3 = fmaf(A[12], x[0], fmaf(A[13], x[1], fmaf(A[14], x[2], fmaf(A[15], x[3], r[3]))));
-            x[0] = x0;
-            x[1] = x1;
-            x[2] = x2;
-            x[3] = x3;
+            diag_jvp(L, floored, r, x);  // Delta_t = A_t Delta_t-1 + rhs_t, A_t in factored form
           }
           pv = {s[u][0], s[u][1], s[u][2], s[u][3]};
 #pragma unroll

@@ -301,10 +301,8 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
           n = s0.n;
         }
       }
-      const float a = lf[u] + m;
-      const float mn = (a >= it[u]) ? a : it[u];
-      const float ig = exp_fast(it[u] - mn);
-      const float fg = exp_fast(a - mn);
+      float mn, ig, fg;
+      stab_gates(lf[u] + m, it[u], mn, ig, fg);
       c = fmaf(fg, c, ig * zz[u]);
       n = fmaf(fg, n, ig);
       m = mn;

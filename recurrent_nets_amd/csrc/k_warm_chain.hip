@@ -104,10 +104,8 @@ __global__ __launch_bounds__(kWarmChainBlock, SLSTM_WARM_CHAIN_MIN_WAVES) void w
 #pragma unroll
   for (int u = 0; u < TC; ++u) {
     if (t0 + u < T) {
-      const float a = lf[u] + m;
-      const float mn = (a >= it[u]) ? a : it[u];  // a tie takes a
-      const float ig = exp_fast(it[u] - mn);
-      const float fg = exp_fast(a - mn);
+      float mn, ig, fg;
+      stab_gates(lf[u] + m, it[u], mn, ig, fg);
       c = fmaf(fg, c, ig * zz[u]);
       n = fmaf(fg, n, ig);
       m = mn;
