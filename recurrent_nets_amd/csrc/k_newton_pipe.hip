@@ -84,16 +84,17 @@ __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_
   // ---- the tile's pre-activations, held for the whole solve ----
   const i64 tile_row = (static_cast<i64>(b) * T + t0) * 4 * static_cast<i64>(d);
   const rsrc_t rsP = make_rsrc(static_cast<const char*>(P) + tile_row * (BF16 ? 2 : 4));
+  // lane part j in the vector offset, step and gate parts in the scalar offset; lanes past d_h
+  // and steps past T read the last feature and step (every load in bounds, no zero fill): what
+  // they compute is never counted, stored or published
   float p[TC][4];
+  const unsigned jc = valid ? j : ud - 1u;
+  const int u_last = T - 1 - t0;
 #pragma unroll
   for (int u = 0; u < TC; ++u) {
+    const unsigned uc = static_cast<unsigned>(u < u_last ? u : u_last);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) p[u][k] = 0.0f;
-    if (valid && t0 + u < T) {
-      // lane part j in the vector offset, step and gate parts in the scalar offset
-#pragma unroll
-      for (int k = 0; k < 4; ++k) p[u][k] = buf_ld_p<BF16>(rsP, j, (4u * u + k) * ud);
-    }
+    for (int k = 0; k < 4; ++k) p[u][k] = buf_ld_p<BF16>(rsP, jc, (4u * uc + k) * ud);
   }
   float rz = 0.0f, ri = 0.0f, rf = 0.0f, ro = 0.0f;
   float hv[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // the iterate at step t0 - 1 (state0 before the sequence)
@@ -150,50 +151,65 @@ __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_
   // ---- K Newton iterations on the registers ----
   const int l = tid & (kWave - 1);
   for (int k = 0; k < K; ++k) {
-    CellIn pv = {hv[0], hv[1], hv[2], hv[3]};
+    const CellIn pv0 = {hv[0], hv[1], hv[2], hv[3]};  // iterate k before the tile
     float x[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    unsigned int fmax = 0u;
+    ResMax2 fmax;
     if (valid) {
+      // Step u reads iterate k at step u - 1 as its previous state, then completes that step's
+      // update (s[u-1] += Delta_{u-1}): the old value is read in place, never copied.
 #pragma unroll
       for (int u = 0; u < TC; ++u) {
         const int t = t0 + u;
         if (t < T) {
           float f[4], r[4];
           DiagLin L;
+          const CellIn pv = u == 0 ? pv0 : CellIn{s[u - 1][0], s[u - 1][1], s[u - 1][2], s[u - 1][3]};
           cell_step_diag(pv, p[u][0], p[u][1], p[u][2], p[u][3], rz, ri, rf, ro, sig, floored, f, L);
+          if (u > 0) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            r[e] = f[e] - s[u][e];
-            fmax = res_max(fmax, r[e]);
+            for (int e = 0; e < 4; ++e) s[u - 1][e] = s[u - 1][e] + x[e];
           }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) r[e] = f[e] - s[u][e];
+          res_max2(fmax, r[0], r[1]);
+          res_max2(fmax, r[2], r[3]);
           if (u == 0 && wait) {
             // the Newton step entering the tile; the state before the tile in iterate k+1
             wait_words(4 + 4 * k, x);
 #pragma unroll
             for (int e = 0; e < 4; ++e) hv[e] = hv[e] + x[e];
           }
-          if (t == 0) {
+          if (u == 0 && tt == 0) {  // t = 0
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = r[e];  // s_0 is data: Delta_1 = rhs_1
           } else {
             diag_jvp(L, floored, r, x);  // Delta_t = A_t Delta_t-1 + rhs_t, A_t in factored form
           }
-          pv = {s[u][0], s[u][1], s[u][2], s[u][3]};
-#pragma unroll
-          for (int e = 0; e < 4; ++e) s[u][e] = s[u][e] + x[e];
         }
+      }
+      // the update of the tile's last step
+      if (t0 + TC <= T) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) s[TC - 1][e] = s[TC - 1][e] + x[e];
+      } else {
+#pragma unroll
+        for (int u = 0; u < TC - 1; ++u)
+          if (u == T - 1 - t0) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s[u][e] = s[u][e] + x[e];
+          }
       }
       if (publish) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) tag_store(word(tt, 4 + 4 * k + e), x[e], epoch);
       }
     }
-    const unsigned int wm = wave_max_u32(fmax);
+    const unsigned int wm = wave_max_u32(res_max2_bits(fmax));
     if (l == 0) __hip_atomic_fetch_max(&s_err[k], wm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 
   // ---- residual of S_K, and the outputs ----
-  unsigned int fmax = 0u;
+  ResMax2 fmax;
   if (valid) {
     const rsrc_t rsO = make_rsrc(S_out + tile_row);
     const rsrc_t rsH = make_rsrc(h_out != nullptr ? h_out + (static_cast<i64>(b) * T + t0) * static_cast<i64>(d) : S_out);
@@ -203,17 +219,16 @@ __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_
       if (t0 + u < T) {
         float f[4];
         cell_step<false>(pv, p[u][0], p[u][1], p[u][2], p[u][3], rz, ri, rf, ro, sig, floored, f, nullptr);
+        res_max2(fmax, s[u][0] - f[0], s[u][1] - f[1]);
+        res_max2(fmax, s[u][2] - f[2], s[u][3] - f[3]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          fmax = res_max(fmax, s[u][e] - f[e]);
-          buf_st(s[u][e], rsO, 4u * j, 4u * (4u * u + e) * ud);
-        }
+        for (int e = 0; e < 4; ++e) buf_st(s[u][e], rsO, 4u * j, 4u * (4u * u + e) * ud);
         if (h_out != nullptr) buf_st(s[u][3], rsH, 4u * j, 4u * u * ud);
         pv = {s[u][0], s[u][1], s[u][2], s[u][3]};
       }
     }
   }
-  const unsigned int wm = wave_max_u32(fmax);
+  const unsigned int wm = wave_max_u32(res_max2_bits(fmax));
   if (l == 0) __hip_atomic_fetch_max(&s_err[K], wm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   __syncthreads();
   if (tid <= K) err_publish(&spread_of(ctl)->err[0][tid], kErrSlotWords, blockIdx.x, res_max_value(s_err[tid]));
