@@ -188,7 +188,7 @@ __device__ __forceinline__ void quad_look_back(const float arow[4], float av, fl
         for (int k = 0; k < 4; ++k) ok &= tag_load(word(p, 4 + 4 * q + k), epoch, prow[k]);
         ok &= tag_load(word(p, 20 + q), epoch, pv);
         if (ok) break;
-        __builtin_amdgcn_s_sleep(2);
+        poll_pause();
       }
       // (Macc, vacc) <- (Macc, vacc) o (Mp, vp), row q: sum_k Macc[q][k] (Mp[k][.], vp[k])
       float nrow[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -218,7 +218,7 @@ __device__ __forceinline__ void quad_look_back(const float arow[4], float av, fl
       while (!ok) {
         ok = tag_load(word(a, q), epoch, xq);
         if (ok) break;
-        __builtin_amdgcn_s_sleep(2);
+        poll_pause();
       }
       cq = fmaf(mrow[0], quad_bcast<0>(xq), fmaf(mrow[1], quad_bcast<1>(xq), fmaf(mrow[2], quad_bcast<2>(xq), fmaf(mrow[3], quad_bcast<3>(xq), vacc))));
     }
@@ -335,7 +335,7 @@ __device__ __forceinline__ void scan_coordinate(float (&s_map)[4][20][VEC * kWav
 #pragma unroll
           for (int e = 0; e < 4; ++e) ok &= tag_load(word(p, 20 + e, f), epoch, vp[e]);
           if (__builtin_amdgcn_ballot_w64(!ok) == 0) break;
-          __builtin_amdgcn_s_sleep(2);
+          poll_pause();
         }
         compose_after(Macc, vacc, Mp, vp);  // (Macc, vacc) <- (Macc, vacc) o (Mp, vp)
       }
@@ -347,7 +347,7 @@ __device__ __forceinline__ void scan_coordinate(float (&s_map)[4][20][VEC * kWav
         ok &= static_cast<uint32_t>(pf[f][e] >> 32) == epoch;
       }
       while (__builtin_amdgcn_ballot_w64(!ok) != 0) {
-        __builtin_amdgcn_s_sleep(2);
+        poll_pause();
         ok = true;
 #pragma unroll
         for (int e = 0; e < 4; ++e) ok &= tag_load(word(anchor_a, e, f), epoch, xa[e]);

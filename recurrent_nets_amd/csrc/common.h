@@ -205,6 +205,12 @@ __device__ __forceinline__ bool tag_load(const unsigned long long* p, uint32_t e
   return static_cast<uint32_t>(w >> 32) == epoch;
 }
 
+// Pause between two polls of a look-back word (s_sleep units of 64 cycles)
+#ifndef SLSTM_POLL_SLEEP
+#define SLSTM_POLL_SLEEP 2
+#endif
+__device__ __forceinline__ void poll_pause() { __builtin_amdgcn_s_sleep(SLSTM_POLL_SLEEP); }
+
 // Anchor stride of the look-back along T: tiles of one lane group are n_lg work tickets
 // apart, so when the lane groups outnumber the workgroups resident on the GPU a predecessor
 // has finished before its successor starts and a plain chain (stride 1) never waits. With few

@@ -146,7 +146,7 @@ __global__ __launch_bounds__(kBackBlock, SLSTM_BACK_MIN_WAVES) void backward_cha
     }
     while (!ok) {
       // the tile after holds an earlier ticket of the same counter, so it runs
-      __builtin_amdgcn_s_sleep(2);
+      poll_pause();
       ok = true;
 #pragma unroll
       for (int e = 0; e < kBackWords; ++e) ok &= tag_load(word(tt + 1, e), epoch, v[e]);

@@ -149,7 +149,7 @@ __global__ __launch_bounds__(kChainBlock, SLSTM_CHAIN_MIN_WAVES) void newton_cha
             ok &= static_cast<uint32_t>(pf[e] >> 32) == epoch;
           }
           while (!ok) {
-            __builtin_amdgcn_s_sleep(2);
+            poll_pause();
             ok = true;
 #pragma unroll
             for (int e = 0; e < 4; ++e) ok &= tag_load(carry_word(tt - 1, e), epoch, x[e]);

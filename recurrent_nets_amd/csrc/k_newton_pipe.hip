@@ -75,7 +75,7 @@ __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_
       ok = tag_load(word(tt - 1, w0), epoch, v[0]) & tag_load(word(tt - 1, w0 + 1), epoch, v[1]) &
            tag_load(word(tt - 1, w0 + 2), epoch, v[2]) & tag_load(word(tt - 1, w0 + 3), epoch, v[3]);
       if (ok) break;
-      __builtin_amdgcn_s_sleep(2);
+      poll_pause();
     }
   };
   constexpr bool sig = (CM & kCellSigmoid) != 0;   // forget-gate form and read-out,

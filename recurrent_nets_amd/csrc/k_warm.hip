@@ -248,14 +248,14 @@ __global__ __launch_bounds__(kWarmBlock) void warm_start_kernel(
         LogAgg pa;
         while (!(tag_load(word(p, 4), epoch, pa.L) & tag_load(word(p, 5), epoch, pa.E) &
                  tag_load(word(p, 6), epoch, pa.cz) & tag_load(word(p, 7), epoch, pa.nz)))
-          __builtin_amdgcn_s_sleep(2);
+          poll_pause();
         acc = compose<PACKED>(pa, acc);
       }
       float xm = 0.0f, xc = 0.0f, xn = 0.0f;
       if (!(PACKED && wave_abs(acc))) {
         while (!(tag_load(word(a, 0), epoch, xm) & tag_load(word(a, 1), epoch, xc) &
                  tag_load(word(a, 2), epoch, xn)))
-          __builtin_amdgcn_s_sleep(2);
+          poll_pause();
       }
       apply<PACKED>(acc, xm, xc, xn);
       cm = xm;

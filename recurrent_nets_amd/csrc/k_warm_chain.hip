@@ -95,7 +95,7 @@ __global__ __launch_bounds__(kWarmChainBlock, SLSTM_WARM_CHAIN_MIN_WAVES) void w
     n = __uint_as_float(static_cast<uint32_t>(pf[2]));
     while (!ok) {
       // the tile before holds an earlier ticket of the same counter, so it runs
-      __builtin_amdgcn_s_sleep(2);
+      poll_pause();
       ok = tag_load(carry_word(tt - 1, 0), epoch, m) & tag_load(carry_word(tt - 1, 1), epoch, c) &
            tag_load(carry_word(tt - 1, 2), epoch, n);
     }
