@@ -62,16 +62,17 @@ JAC_BYTES = 12 * 4
 
 
 def solve_flops_per_elem(K, sigmoid_forget):
-    """Floating-point operations of one state element of a whole Newton solve as the kernels
-    form them (an add, multiply, compare-select or max counts 1, an FMA 2, an exp2, log2 or
-    reciprocal 1): warm-start step 26, cell step 34, its Jacobian 31, residual and its maximum
-    8, the 4x4 recurrence (11 FMA) 22, the update 4; the sigmoid forget gate adds a log-sigmoid
-    to every step (6) and its derivative to every Jacobian (5)."""
+    """Floating-point operations of one state element of a whole Newton solve as the one-kernel
+    solve forms them (an add, multiply, compare-select or max counts 1, an FMA 2, an exp2, log2
+    or reciprocal 1): warm-start step 25, cell step 34, the coefficients of its Jacobian in
+    factored form 13, residual and its maximum 8, the Newton step through the factored Jacobian
+    22, the update 4; the sigmoid forget gate adds a log-sigmoid to every step (6) and its
+    derivative to every linearisation (5)."""
     sig = 1 if sigmoid_forget else 0
-    warm = 26 + 6 * sig
+    warm = 25 + 6 * sig
     cell = 34 + 6 * sig
-    jac = 31 + 5 * sig
-    return warm + K * (cell + jac + 8 + 22 + 4) + (cell + 8)
+    lin = 13 + 5 * sig
+    return warm + K * (cell + lin + 8 + 22 + 4) + (cell + 8)
 
 
 def kernel_work(w, n_e, p_bytes):
