@@ -384,9 +384,10 @@ slstm_status slstm_backward_varlen(const void* P, slstm_dtype P_dtype, const flo
  * The _varlen forms take packed sequences as the channelwise _varlen calls do (one row of T steps,
  * cu_seqlens (n_seqs + 1 device ints), state0, final_state, g_final and dstate0 per sequence):
  * a sequence start takes state0[s] as the state before it, its Jacobian is zero for the Newton
- * solve and the adjoint does not cross it. Packed Newton runs the warm start and one kernel per
- * iteration (never the one-sweep kernel); the workspace sizes are those of the unpacked calls
- * with B = 1.
+ * solve and the adjoint does not cross it. Packed Newton with tol = 0, max_iters <= 4 and d_head <= 64
+ * runs the one-sweep kernel in its single-group form (one workgroup per head along the row),
+ * otherwise the warm start and one kernel per iteration; the workspace sizes are those of the
+ * unpacked calls with B = 1.
  */
 size_t slstm_head_newton_workspace_bytes(int B, int T, int d_h, int n_heads);
 slstm_status slstm_head_newton_forward(const void* P, slstm_dtype P_dtype, const float* R,

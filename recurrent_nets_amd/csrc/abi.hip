@@ -999,14 +999,13 @@ slstm_status head_newton_forward(const void* P, slstm_dtype P_dtype, const float
     HIP_TRY(slstm::launch_seq_table(seqs.cu, seqs.n, T, tab, st));
     seqs.tab = tab;
   }
-  // the one-sweep kernel serves fixed counts on unpacked rows of heads up to 64 units; packed rows
-  // and 128-unit heads iterate kernel by kernel
-  if (seqs.cu == nullptr && tol == 0.0f && max_iters <= slstm::kHeadSolveMaxIters &&
-      d_h / n_heads <= slstm::kHeadSolveMaxWidth) {
+  // the one-sweep kernel serves fixed counts on heads up to 64 units (packed rows in its
+  // single-group form); 128-unit heads and solves with a tolerance iterate kernel by kernel
+  if (tol == 0.0f && max_iters <= slstm::kHeadSolveMaxIters && d_h / n_heads <= slstm::kHeadSolveMaxWidth) {
     // a fixed count of iterations: the whole solve in one sweep over T
     HIP_TRY(timed(SLSTM_KERNEL_HEAD_SOLVE, st, [&] {
       return slstm::launch_head_solve(P, bf16, R, state0, states, h_out, B, T, d_h, n_heads, cm, max_iters,
-                                      init == SLSTM_INIT_ZERO, ctl, st);
+                                      init == SLSTM_INIT_ZERO, ctl, st, seqs);
     }));
   } else {
     HIP_TRY(head_newton_iterations(P, bf16, R, state0, states, h_out, B, T, d_h, n_heads, cm, max_iters, tol, init,

@@ -17,6 +17,12 @@
 // Layout as in k_head.hip: a workgroup per (batch row, head), lane 4 i + g for unit i and
 // gate / state slot g, row i of gate g's block in registers, h of iterate 0 and Delta h of
 // every stage passed from step to step through double-buffered LDS.
+//
+// Packed sequences (PACKED, one batch row, single-group form): at the first step of sequence s
+// the state before it is state0[s] in every iterate and no Newton step enters it (a zero
+// Jacobian), so every stage restarts there from the same data; the workgroup stages that h
+// and zero Delta h for the block products behind an extra barrier (at sequence starts only) and
+// walks the offsets with a SeqCursor.
 #include "cell.h"
 #include "head.h"
 #include "kernels.h"
@@ -26,11 +32,11 @@ namespace slstm {
 // One wave per SIMD is this kernel's occupancy at the sizes it serves (a workgroup per batch
 // row and head); saying so lets the scheduler keep a step's LDS reads in flight together
 // instead of trading them for registers.
-template <int DH, bool BF16, int CM, int K>
+template <int DH, bool BF16, int CM, int K, bool PACKED>
 __global__ __launch_bounds__(4 * DH) __attribute__((amdgpu_waves_per_eu(1, 1))) void head_solve_kernel(const void* __restrict__ P, const float* __restrict__ R,
                                                             const float* __restrict__ state0, float* __restrict__ S,
                                                             float* __restrict__ h_out, int T, int d, int nh,
-                                                            Control* __restrict__ ctl, int zero_init) {
+                                                            Control* __restrict__ ctl, int zero_init, Seqs seqs) {
   constexpr bool sig = (CM & kCellSigmoid) != 0;
   constexpr bool floored = (CM & kCellFloored) != 0;
   __shared__ __attribute__((aligned(16))) float h0buf[2][DH];     // h of iterate 0 at t - 1
@@ -75,7 +81,24 @@ __global__ __launch_bounds__(4 * DH) __attribute__((amdgpu_waves_per_eu(1, 1))) 
   // leaves no trace: no store, no residual maximum; its LDS exchange is never read for a real
   // step. The step returns slot g of iterate K at t; the block stores them after its last step.
   const float warm_scale = zero_init ? 0.0f : 1.0f;  // the warm start's state is finite
+  SeqCursor seq = seq_cursor(seqs.cu, seqs.n, 0, 0, seqs.tab);
   auto step = [&](int t, float p, bool real) -> float {
+    if constexpr (PACKED) {
+      const int sq = real ? seq_begin(seq, t) : -1;
+      if (sq >= 0) {  // a sequence start (uniform): every iterate restarts from state0[sq]
+        const float v0 = state0 != nullptr ? state0[(static_cast<i64>(sq) * 4 + g) * dd + j] : 0.0f;
+#pragma unroll
+        for (int k = 0; k <= K; ++k) sp[k] = v0;
+#pragma unroll
+        for (int k = 0; k < K; ++k) dp[k] = 0.0f;
+        if (g == 3) {
+          h0buf[t & 1][i] = v0;
+#pragma unroll
+          for (int k = 0; k < K; ++k) dhbuf[k][t & 1][i] = 0.0f;
+        }
+        head_lds_barrier();
+      }
+    }
     // the R Delta h' products of every stage depend on step t - 1 only
     float y[K];
 #pragma unroll
@@ -317,7 +340,7 @@ __global__ __launch_bounds__(kHeadPipeMaxThreads) __attribute__((amdgpu_waves_pe
 
 hipError_t launch_head_solve(const void* P, bool p_bf16, const float* R, const float* state0, float* S,
                              float* h_out, int B, int T, int d, int n_heads, int cell_mode, int K, bool zero_init,
-                             Control* ctl, hipStream_t stream) {
+                             Control* ctl, hipStream_t stream, Seqs seqs) {
   if (n_heads < 1 || d % n_heads != 0 || B > 65535 || K < 1 || K > kHeadSolveMaxIters) return hipErrorInvalidValue;
   const int dh = d / n_heads;
   const dim3 grid(static_cast<unsigned>(n_heads), static_cast<unsigned>(B));
@@ -330,7 +353,9 @@ hipError_t launch_head_solve(const void* P, bool p_bf16, const float* R, const f
   // Heads wider than 32 units always take the sweep.
   const long long cus = head_device_cus();
   const long long wg_per_cu = (static_cast<long long>(n_heads) * B + cus - 1) / cus;
-  if (dh <= 32 && wg_per_cu <= 2) {
+  const bool packed = seqs.cu != nullptr;
+  if (packed && B != 1) return hipErrorInvalidValue;
+  if (dh <= 32 && wg_per_cu <= 2 && !packed) {
     const unsigned int lds_p = head_spread_lds(static_cast<long long>(n_heads) * B, 24 * 1024);
     // waves a SIMD must hold, counting each workgroup's K + 2 groups of ceil(4 d_head / 64)
     // waves as spread over the 4 SIMDs in whole rounds: uncut (96 VGPRs) a SIMD takes 5
@@ -361,8 +386,15 @@ hipError_t launch_head_solve(const void* P, bool p_bf16, const float* R, const f
 #undef SLSTM_HEAD_PIPE
     return hipGetLastError();
   }
-#define SLSTM_HEAD_SOLVE(BF, KK, CM_) \
-  head_solve_kernel<DH, BF, CM_, KK><<<grid, 4 * DH, lds, stream>>>(P, R, state0, S, h_out, T, d, n_heads, ctl, zi)
+#define SLSTM_HEAD_SOLVE(BF, KK, CM_)                                                                           \
+  do {                                                                                                          \
+    if (packed)                                                                                                 \
+      head_solve_kernel<DH, BF, CM_, KK, true><<<grid, 4 * DH, lds, stream>>>(P, R, state0, S, h_out, T, d,    \
+                                                                              n_heads, ctl, zi, seqs);          \
+    else                                                                                                        \
+      head_solve_kernel<DH, BF, CM_, KK, false><<<grid, 4 * DH, lds, stream>>>(P, R, state0, S, h_out, T, d,   \
+                                                                               n_heads, ctl, zi, seqs);         \
+  } while (0)
 #define SLSTM_HEAD_SOLVE_K(BF, CM_)              \
   switch (K) {                                   \
     case 1: SLSTM_HEAD_SOLVE(BF, 1, CM_); break; \

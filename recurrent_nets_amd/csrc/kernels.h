@@ -115,12 +115,12 @@ hipError_t launch_head_iteration(const void* P, bool p_bf16, const float* R, con
 // The whole head-mixing Newton solve in one sweep over T: K (1..kHeadSolveMaxIters) iterations
 // pipelined stage by stage, the warm start (or zero_init's zero iterate) formed in the sweep;
 // writes S (iterate K), h_out (may be NULL), the residual maxima of iterates 0..K into ctl's
-// error slots and ctl->iters = K.
+// error slots and ctl->iters = K. Packed rows (seqs, B = 1) run the single-group form.
 constexpr int kHeadSolveMaxIters = 4;
 constexpr int kHeadSolveMaxWidth = 64;  // widest head the one-sweep kernel takes
 hipError_t launch_head_solve(const void* P, bool p_bf16, const float* R, const float* state0, float* S,
                              float* h_out, int B, int T, int d, int n_heads, int cell_mode, int K, bool zero_init,
-                             Control* ctl, hipStream_t stream);
+                             Control* ctl, hipStream_t stream, Seqs seqs = {});
 
 // Backward under head mixing at the stored states S: dP (float32 or bf16), dR (4, n_heads,
 // d_head, d_head), dbias (4, d; may be NULL), dstate0 (B, 4, d; may be NULL); g_states, g_h and

@@ -1,9 +1,10 @@
 """GPU parity of packed sequences under head mixing: ragged sequences laid end to end in one row,
 each from its own state0 ("sLSTM in this library", "Packed sequences"; the head-mixing cell of the
 "Cell" section's mix table), against the float64 oracle's packed head forms. Covered: the
-sequential forward with per-sequence final states, the Newton solve (which runs the warm start
-and one kernel per iteration on a pack) at a fixed count and with an early stop, and the backward
-with a gradient at each sequence's final state. Lengths mix empty and length-1 sequences with
+sequential forward with per-sequence final states, the Newton solve at a fixed count (up to 4
+iterations in the single-group one-sweep kernel, more by the warm start and one kernel per
+iteration) and with an early stop, and the backward with a gradient at each sequence's final
+state. Lengths mix empty and length-1 sequences with
 ones that cross the kernels' 8-step prefetch blocks; one case starts a sequence at every step,
 one holds a single sequence."""
 import numpy as np
@@ -93,6 +94,32 @@ def test_head_packed_newton_early_stop(gpu_lib):
     assert st_ref.converged and st.converged
     assert st.iters == st_ref.iters < 8
     assert h_rel_err(h, S_ref[..., 3, :]) < H_TOL_BF16
+
+
+@pytest.mark.parametrize("layout,dh,K,init", [(lay, dh, K, "warm") for lay in ("mixed", "all_ones", "empty_ends")
+                                               for dh, K in ((8, 1), (16, 2), (32, 4), (64, 3))]
+                         + [("all_ones", 16, 2, "zero")])
+def test_head_packed_one_sweep(gpu_lib, layout, dh, K, init):
+    """The packed one-sweep solve (fixed K <= 4) against the oracle, and against the same pack run
+    iteration by iteration (a tolerance no residual meets keeps the per-iteration kernels)."""
+    lengths = LAYOUTS[layout]
+    P, R, s0, cu = _problem(1340 + dh + K, lengths, dh, 2)
+    case(f"head packed one-sweep {layout} d_head={dh} K={K} {init}")
+    fin = torch.empty_like(s0).to(DEV)
+    S, h, st = gpu_lib.head_newton_forward(*_on(P, R, s0), "exp", K, 0.0, init=init, final_state=fin,
+                                           cu_seqlens=cu, raise_on_divergence=False)
+    _, h_it, _ = gpu_lib.head_newton_forward(*_on(P, R, s0), "exp", K, 1e-30, init=init, cu_seqlens=cu,
+                                             raise_on_divergence=False)
+    torch.cuda.synchronize()
+    S_ref, st_ref = ref.newton_head(to_np(P), to_np(R), to_np(s0), "exp", K, init=init, cu_seqlens=cu)
+    err = h_rel_err(h, S_ref[..., 3, :])
+    print(f"head packed one-sweep {layout} d_head={dh} K={K} {init}: h rel err {err:.2e}, "
+          f"per-iteration form {h_rel_err(h_it, S_ref[..., 3, :]):.2e}")
+    assert not st_ref.diverged and not st.diverged
+    assert err < H_TOL_F32
+    assert h_rel_err(h_it, to_np(h)) < H_TOL_F32
+    assert st.iters == st_ref.iters == K
+    assert _state_err(fin, ref.final_states(S_ref, to_np(s0), cu)) < 1e-4
 
 
 def test_head_packed_single_sequence_matches_unpacked(gpu_lib):
