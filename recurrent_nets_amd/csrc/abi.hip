@@ -144,7 +144,7 @@ Form newton_form(int B, int d, slstm_schedule s) {
 }
 
 struct NewtonLayout {
-  size_t ctl, desc, A, rhs, S2, tab, total;
+  size_t ctl, desc, A, rhs, S2, tab, tiles, total;
 };
 
 // control block, look-back words, then either the second iterate buffer (fused) or the
@@ -171,10 +171,18 @@ NewtonLayout newton_layout(int B, int T, int d, Form form) {
     L.S2 = 0;
     L.total = align_up(L.rhs + n_state * sizeof(float));
   }
-  // the sequence table of packed calls (unused otherwise)
+  // the sequence table of packed calls and their aligned tiles (unused otherwise)
   L.tab = L.total;
-  L.total = align_up(L.tab + slstm::seq_table_ints(T) * sizeof(int));
+  L.tiles = align_up(L.tab + slstm::seq_table_ints(T) * sizeof(int));
+  L.total = align_up(L.tiles + slstm::aligned_tile_ints(slstm::fused_aligned_cap(T)) * sizeof(int));
   return L;
+}
+
+// whether a pack of n_seqs sequences over T steps fits the aligned tiles of the scan-form
+// iteration (at most one tile per sequence beyond the row's own count)
+bool aligned_tiles_fit(int T, int n_seqs) {
+  const long long steps = slstm::fused_aligned_steps();
+  return (T + steps - 1) / steps + static_cast<long long>(n_seqs) <= slstm::fused_aligned_cap(T);
 }
 
 // the warm start's kernel for a schedule: chains where the solver would use them
@@ -502,6 +510,13 @@ slstm_status newton_forward(const void* P, slstm_dtype P_dtype, const float* R, 
     int* tab = at<int>(workspace, L.tab);
     HIP_TRY(slstm::launch_seq_table(seqs.cu, seqs.n, T, tab, st));
     seqs.tab = tab;
+    if (form == Form::kScan && aligned_tiles_fit(T, seqs.n)) {
+      // the scan-form iterations on tiles aligned to the sequences
+      int* tiles = at<int>(workspace, L.tiles);
+      seqs.tile_cap = slstm::fused_aligned_cap(T);
+      HIP_TRY(slstm::launch_aligned_tiles(seqs.cu, seqs.n, T, slstm::fused_aligned_steps(), seqs.tile_cap, tiles, st));
+      seqs.tiles = tiles;
+    }
   }
   unsigned int* tickets = slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0];
   if (seqs.cu == nullptr && pipe_solve(form, max_iters, tol)) {

@@ -49,6 +49,11 @@ struct Seqs {
   const int* cu = nullptr;
   int n = 0;
   const int* tab = nullptr;  // optional: seq_table entries (see build_seq_table)
+  // optional: tiles aligned to the sequences (see launch_aligned_tiles), for the scan-form
+  // iteration: tiles[0] the number of tiles, then the order they are handed out in, each
+  // tile's sequence and each tile's position in it (tile_cap entries each)
+  const int* tiles = nullptr;
+  int tile_cap = 0;
 };
 
 // seq_table: entry k holds the sequence containing step k << kSeqTabShift, i.e. the s with

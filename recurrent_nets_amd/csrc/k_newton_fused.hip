@@ -22,6 +22,13 @@
 // flag of the segmented scan); every thread finds the sequences its steps belong to with a
 // SeqCursor.
 //
+// Aligned tiles (ALIGNED, packed sequences with a tile table, see launch_aligned_tiles): a tile
+// covers steps of one sequence only, starting at a multiple of the tile length from its first
+// step, so the look-back chains are per sequence (position p of sequence s takes the look-back
+// words of tile id - p + 0..p) and only position 0 starts a sequence. Tiles are handed out by
+// position, then sequence: the tiles in flight at once belong to many sequences, which advance
+// side by side instead of one after another.
+//
 // The residual maximum of S_k goes to the spread slots. Early stop is exact although the
 // update of iteration k is formed together with F_k: the next launch (or the final residual
 // pass) finds max|F_k| < tol and declares S_k final; S_k is still intact in the other buffer.
@@ -99,14 +106,14 @@ __device__ __forceinline__ void step_terms(const CellIn& pv, const float pg[4], 
   for (int q = 0; q < 12; ++q) a[q] = start ? 0.0f : Aj[kSpPlane[q]];
 }
 
-template <bool BF16, int TSUB, bool PACKED>
+template <bool BF16, int TSUB, bool PACKED, bool ALIGNED>
 __global__ __launch_bounds__(kFusedBlock, fused_wgs_per_cu<TSUB>()) void newton_iter_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S_in, float* __restrict__ S_out, int T, int d, int n_jt, int n_lg,
     int n_tt, int anchor_stride, int cell_mode, unsigned long long* __restrict__ desc,
     unsigned int* __restrict__ tickets, int n_ctr, uint32_t epoch, Control* __restrict__ ctl,
     int k_iter, float tol, const int* __restrict__ cu, int n_seqs,
-    const int* __restrict__ seq_tab) {
+    const int* __restrict__ seq_tab, const int* __restrict__ tiles, int tile_cap) {
   if (ctl->stopped) return;
   if (k_iter > 0 && tol > 0.0f && err_reduced(ctl, k_iter - 1) < tol) {
     // the previous iterate already met the tolerance: it is the result
@@ -125,10 +132,28 @@ __global__ __launch_bounds__(kFusedBlock, fused_wgs_per_cu<TSUB>()) void newton_
     s_arrived = 0u;
   }
   __syncthreads();
-  const int tt = __builtin_amdgcn_readfirstlane(s_tile[0]);
+  const int tk = __builtin_amdgcn_readfirstlane(s_tile[0]);
   const int lg = __builtin_amdgcn_readfirstlane(s_tile[1]);
   const int b = lg / n_jt;
   const int jt = lg - b * n_jt;
+  const i64 n_lanes_pad = static_cast<i64>(n_lg) * 64;
+  // the tile's position along its look-back chain, its first step, the end of its steps
+  int tt = tk, t_tile = tk * 4 * TSUB, t_end = T, aseq = 0;
+  unsigned long long* dsc = desc;  // the look-back words of the chain
+  if constexpr (ALIGNED) {
+    const int n_real = __builtin_amdgcn_readfirstlane(tiles[0]);
+    if (tk >= n_real) {  // a ticket past the last tile
+      if (blockIdx.x == 0 && tid == 0) ctl->iters = k_iter + 1;
+      return;
+    }
+    const int id = __builtin_amdgcn_readfirstlane(tiles[1 + tk]);
+    aseq = __builtin_amdgcn_readfirstlane(tiles[1 + tile_cap + id]);
+    tt = __builtin_amdgcn_readfirstlane(tiles[1 + 2 * tile_cap + id]);
+    const int a0 = min(max(cu[aseq], 0), T);
+    t_end = min(max(cu[aseq + 1], a0), T);
+    t_tile = a0 + tt * 4 * TSUB;
+    dsc = desc + static_cast<i64>(id - tt) * kLookBackWords * n_lanes_pad;
+  }
 
   // lane layout: the four threads of a quad hold the four consecutive sub-chunks of one feature
   const int l = tid & 63;
@@ -137,9 +162,7 @@ __global__ __launch_bounds__(kFusedBlock, fused_wgs_per_cu<TSUB>()) void newton_
   const unsigned ud = static_cast<unsigned>(d);
   const unsigned j = static_cast<unsigned>(jt * 64 + lane_in_tile);
   const bool valid = j < ud;
-  const int t_tile = tt * 4 * TSUB;
   const int t_start = t_tile + sc * TSUB;
-  const i64 n_lanes_pad = static_cast<i64>(n_lg) * 64;
   const i64 my_lane = static_cast<i64>(lg) * 64 + lane_in_tile;
   const bool sig = (cell_mode & kCellSigmoid) != 0;
   const bool floored = (cell_mode & kCellFloored) != 0;
@@ -151,10 +174,10 @@ __global__ __launch_bounds__(kFusedBlock, fused_wgs_per_cu<TSUB>()) void newton_
   const unsigned lane_off = static_cast<unsigned>(sc * TSUB) * 4u * ud + j;
 
   // this thread's word of the look-back anchor, loaded now so that it arrives meanwhile
-  const unsigned long long pf = quad_look_back_prefetch(desc, n_lanes_pad, my_lane, sc, tt, anchor_stride);
+  const unsigned long long pf = quad_look_back_prefetch(dsc, n_lanes_pad, my_lane, sc, tt, anchor_stride);
 
   float pg[TSUB][4], sv[TSUB][4];
-  load_sub_chunk<BF16, TSUB>(rsP, rsS, lane_off, ud, t_start, T, valid, pg, sv);
+  load_sub_chunk<BF16, TSUB>(rsP, rsS, lane_off, ud, t_start, t_end, valid, pg, sv);
 
   float rz = 0.0f, ri = 0.0f, rf = 0.0f, ro = 0.0f;
   // the state before the sub-chunk: the previous sub-chunk's last step (from the neighbouring
@@ -197,9 +220,10 @@ __global__ __launch_bounds__(kFusedBlock, fused_wgs_per_cu<TSUB>()) void newton_
     if constexpr (PACKED) {
       if (t < T) sq = seq_begin(seq, t);
     }
-    if (valid && t < T) {
-      const bool start = PACKED ? sq >= 0 : t == 0;
-      if (PACKED && start) pv = state0_of(state0, sq, ud, j);
+    if constexpr (ALIGNED) sq = (tt == 0 && t == t_tile && t < t_end) ? aseq : -1;
+    if (valid && t < t_end) {
+      const bool start = (PACKED || ALIGNED) ? sq >= 0 : t == 0;
+      if ((PACKED || ALIGNED) && start) pv = state0_of(state0, sq, ud, j);
       step_terms(pv, pg[u], sv[u], rz, ri, rf, ro, sig, floored, start, a, r);
 #pragma unroll
       for (int k = 0; k < 4; ++k) fmax_local = fmaxf(fmax_local, abs_nan_inf(r[k]));
@@ -247,7 +271,7 @@ __global__ __launch_bounds__(kFusedBlock, fused_wgs_per_cu<TSUB>()) void newton_
   {
     float arow[4], av;
     quad_row_of_last(M, v, sc, arow, av);
-    quad_look_back<PACKED>(arow, av, carry, desc, n_lanes_pad, my_lane, sc, tt, anchor_stride, epoch, pf);
+    quad_look_back<PACKED>(arow, av, carry, dsc, n_lanes_pad, my_lane, sc, tt, anchor_stride, epoch, pf);
   }
 
   // ---- re-run each sub-chunk from the value entering it and write the updated iterate ----
@@ -264,7 +288,7 @@ __global__ __launch_bounds__(kFusedBlock, fused_wgs_per_cu<TSUB>()) void newton_
 #pragma unroll
   for (int u = 0; u < TSUB; ++u) {
     const int t = t_start + u;
-    if (valid && t < T) {
+    if (valid && t < t_end) {
       float xn[4];
       sp_vec(keep_a[u], xs, keep_r[u], xn);
       const unsigned o = lane_off + u * 4u * ud;
@@ -296,35 +320,52 @@ size_t fused_desc_words(int B, int T, int d) {
   return static_cast<size_t>(n_tt * kLookBackWords * n_lg * 64);
 }
 
+// aligned tiles: the long sub-chunks, as many tiles as the words of the shorter tiles hold
+int fused_aligned_steps() { return 4 * kFusedLongTSub; }
+int fused_aligned_cap(int T) { return (T + 4 * kFusedTSub - 1) / (4 * kFusedTSub); }
+#ifndef SLSTM_ALIGNED_ANCHOR_STRIDE
+#define SLSTM_ALIGNED_ANCHOR_STRIDE 2
+#endif
+
 hipError_t launch_newton_iteration(const void* P, bool p_bf16, const float* R, const float* state0,
                                    const float* S_in, float* S_out, int B, int T, int d,
                                    int cell_mode, unsigned long long* desc, unsigned int* tickets,
                                    uint32_t epoch, Control* ctl, int k_iter, float tol,
                                    hipStream_t stream, Seqs seqs) {
   const bool packed = seqs.cu != nullptr;
+  const bool aligned = packed && seqs.tiles != nullptr;
   const int tsub = fused_tsub(B, d, packed);
   i64 n_jt, n_lg, n_tt;
   fused_grid(B, T, d, tsub, n_jt, n_lg, n_tt);
+  if (aligned) {  // at most one tile more than the row's per sequence; the tickets past the last exit
+    n_tt += seqs.n;
+    if (B != 1 || tsub != kFusedLongTSub || n_tt > seqs.tile_cap) return hipErrorInvalidValue;
+  }
   const i64 blocks = n_lg * n_tt;
   if (blocks > 0x7fffffffLL) return hipErrorInvalidValue;
   const int stride = look_back_anchor_stride(
       n_lg, tsub == kFusedTSub ? fused_wgs_per_cu<kFusedTSub>() : fused_wgs_per_cu<kFusedLongTSub>());
   // packed rows and other rows of few lane groups along a long T (the long sub-chunks) take
   // the packed anchor stride, measured best there
-  const int stride_used = packed || tsub != kFusedTSub ? kPackedAnchorStride : stride;
+  const int stride_used =
+      aligned ? SLSTM_ALIGNED_ANCHOR_STRIDE : (packed || tsub != kFusedTSub ? kPackedAnchorStride : stride);
   const int n_ctr = ticket_counters(n_lg);
   const dim3 grid(static_cast<unsigned>(blocks));
   const int sig = cell_mode;
-#define SLSTM_FUSED_LAUNCH_T(BF, TS, PK)                                                             \
-  newton_iter_kernel<BF, TS, PK><<<grid, kFusedBlock, 0, stream>>>(                                  \
+#define SLSTM_FUSED_LAUNCH_T(BF, TS, PK, AL)                                                         \
+  newton_iter_kernel<BF, TS, PK, AL><<<grid, kFusedBlock, 0, stream>>>(                              \
       P, R, state0, S_in, S_out, T, d, static_cast<int>(n_jt), static_cast<int>(n_lg),                \
-      static_cast<int>(n_tt), stride_used, sig, desc, tickets, n_ctr, epoch, ctl, k_iter, tol, seqs.cu, seqs.n, seqs.tab)
-#define SLSTM_FUSED_LAUNCH(BF, PK)                                         \
-  do {                                                                     \
-    if (tsub == kFusedTSub) SLSTM_FUSED_LAUNCH_T(BF, kFusedTSub, PK);      \
-    else SLSTM_FUSED_LAUNCH_T(BF, kFusedLongTSub, PK);                     \
+      static_cast<int>(n_tt), stride_used, sig, desc, tickets, n_ctr, epoch, ctl, k_iter, tol, seqs.cu, seqs.n, seqs.tab, \
+      seqs.tiles, seqs.tile_cap)
+#define SLSTM_FUSED_LAUNCH(BF, PK)                                                \
+  do {                                                                            \
+    if (tsub == kFusedTSub) SLSTM_FUSED_LAUNCH_T(BF, kFusedTSub, PK, false);      \
+    else SLSTM_FUSED_LAUNCH_T(BF, kFusedLongTSub, PK, false);                     \
   } while (0)
-  if (p_bf16) {
+  if (aligned) {
+    if (p_bf16) SLSTM_FUSED_LAUNCH_T(true, kFusedLongTSub, false, true);
+    else SLSTM_FUSED_LAUNCH_T(false, kFusedLongTSub, false, true);
+  } else if (p_bf16) {
     if (packed) SLSTM_FUSED_LAUNCH(true, true);
     else SLSTM_FUSED_LAUNCH(true, false);
   } else {

@@ -213,6 +213,53 @@ hipError_t launch_seq_table(const int* cu, int n_seqs, int T, int* tab, hipStrea
   return hipGetLastError();
 }
 
+// Tiles aligned to packed sequences: sequence s gets ceil(len_s / tile_steps) tiles, numbered
+// consecutively (tile id = the sequence's first tile + its position p), none straddling a start.
+// The order they are handed out in is by position, then sequence, so every tile comes after the
+// tiles before it in its sequence (the only ones it waits on) while the tiles in flight at once
+// belong to many sequences. One thread builds it (a few thousand entries, once per solve); at
+// most cap tiles are made, whatever the offsets hold (offsets are clamped into [0, T]).
+// Layout of tiles: [0] count, [1, 1 + cap) order, then cap sequence ids, cap positions, and
+// cap counters of scratch.
+__global__ __launch_bounds__(64) void aligned_tiles_kernel(const int* __restrict__ cu, int n_seqs, int T,
+                                                          int tile_steps, int cap, int* __restrict__ tiles) {
+  if (threadIdx.x != 0) return;
+  int* order = tiles + 1;
+  int* seq = tiles + 1 + cap;
+  int* pos = tiles + 1 + 2 * cap;
+  int* cnt = tiles + 1 + 3 * cap;  // tiles per position, then the next slot per position
+  int n = 0, max_nt = 0;
+  for (int s = 0; s < n_seqs && n < cap; ++s) {
+    const int a = min(max(cu[s], 0), T);
+    const int e = min(max(cu[s + 1], a), T);
+    const int nt = min((e - a + tile_steps - 1) / tile_steps, cap - n);
+    for (int p = 0; p < nt; ++p) {
+      seq[n + p] = s;
+      pos[n + p] = p;
+    }
+    n += nt;
+    max_nt = max(max_nt, nt);
+  }
+  for (int p = 0; p < max_nt; ++p) cnt[p] = 0;
+  for (int id = 0; id < n; ++id) ++cnt[pos[id]];
+  int run = 0;  // exclusive prefix: the first slot of each position
+  for (int p = 0; p < max_nt; ++p) {
+    const int c = cnt[p];
+    cnt[p] = run;
+    run += c;
+  }
+  for (int id = 0; id < n; ++id) order[cnt[pos[id]]++] = id;  // ids ascend with the sequence
+  tiles[0] = n;
+}
+
+size_t aligned_tile_ints(int cap) { return 1 + 4 * static_cast<size_t>(cap); }
+
+hipError_t launch_aligned_tiles(const int* cu, int n_seqs, int T, int tile_steps, int cap, int* tiles,
+                                hipStream_t stream) {
+  aligned_tiles_kernel<<<1, 64, 0, stream>>>(cu, n_seqs, T, tile_steps, cap, tiles);
+  return hipGetLastError();
+}
+
 hipError_t launch_zero(float* p, i64 n_floats, hipStream_t stream) {
   const i64 n4 = n_floats / 4;
   zero_kernel<<<stream_grid(n4), kUpdBlock, 0, stream>>>(reinterpret_cast<float4*>(p), n4);

@@ -96,6 +96,15 @@ hipError_t launch_zero(float* p, i64 n_floats, hipStream_t stream);
 // the sequence table of packed offsets (seq_table_ints(T) ints; see kSeqTabShift)
 size_t seq_table_ints(int T);
 hipError_t launch_seq_table(const int* cu, int n_seqs, int T, int* tab, hipStream_t stream);
+// tiles aligned to packed sequences for the scan-form iteration (see Seqs::tiles):
+// aligned_tile_ints(cap) ints; fused_aligned_cap(T) tiles fit the iteration's look-back words,
+// and a pack of n_seqs sequences over T steps needs at most ceil(T / fused_aligned_steps()) +
+// n_seqs of them
+size_t aligned_tile_ints(int cap);
+hipError_t launch_aligned_tiles(const int* cu, int n_seqs, int T, int tile_steps, int cap, int* tiles,
+                                hipStream_t stream);
+int fused_aligned_cap(int T);
+int fused_aligned_steps();
 
 hipError_t launch_sequential(const void* P, bool p_bf16, const float* R, const float* state0,
                              float* S, float* h_out, float* final_state, int B, int T, int d,

@@ -24,6 +24,9 @@ LAYOUTS = {
     "empty_ends": [0, 0, 150, 0, 1, 0],               # leading and trailing empties
     "single": [333],                                  # the unpacked problem
     "many": list(np.diff(packed_offsets(11, 3000, 40))),  # ~300 short sequences
+    # lengths at and around the 32-step tiles of the scan form's aligned tiles (which serve packs
+    # of at most about T / 32 sequences: this one, "mixed" and "single")
+    "tile_edges": [32, 0, 33, 31, 1, 64, 0, 96, 2, 65, 127, 1, 300],
 }
 
 
@@ -127,6 +130,18 @@ def test_packed_newton_early_stop(gpu_lib, schedule):
     assert st_ref.converged and st.converged
     assert st.iters == st_ref.iters
     assert h_rel_err(h, S_ref[..., 3, :]) < H_TOL_BF16
+
+
+def test_packed_aligned_tiles_reproducible(gpu_lib):
+    """The scan form on tiles aligned to the sequences: two solves give the same bits (the
+    tiles of many sequences run at once, in whatever order the hardware schedules them)."""
+    P, R, s0, cu = _problem(815, LAYOUTS["tile_edges"], 200, "exp")
+    case("packed aligned tiles reproducible")
+    Pd, Rd, s0d = _dev(P, R, s0)
+    a = gpu_lib.newton_forward(Pd, Rd, s0d, "exp", 3, 0.0, schedule="fused_scan", cu_seqlens=cu)[0].clone()
+    b = gpu_lib.newton_forward(Pd, Rd, s0d, "exp", 3, 0.0, schedule="fused_scan", cu_seqlens=cu)[0]
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
 
 
 def test_packed_single_sequence_matches_unpacked(gpu_lib):
