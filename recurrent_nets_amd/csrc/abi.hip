@@ -356,7 +356,7 @@ bool pipe_solve(Form form, int max_iters, float tol) {
 
 // control block, the look-back words, then the dR rows and their chunk sums
 struct BackwardLayout {
-  size_t ctl, desc, rows, tab, total;
+  size_t ctl, desc, rows, tab, tiles, total;
 };
 
 bool backward_schedule(slstm_schedule s) {
@@ -377,7 +377,9 @@ BackwardLayout backward_layout(int B, int T, int d, bool scan) {
   L.desc = align_up(slstm::kControlBytes);
   L.rows = align_up(L.desc + slstm::backward_desc_words(B, T, d, scan) * 8);
   L.tab = align_up(L.rows + slstm::backward_row_floats(B, T, d, scan) * sizeof(float));
-  L.total = align_up(L.tab + slstm::seq_table_ints(T) * sizeof(int));  // packed calls only
+  // packed calls only: the sequence table, then the aligned tiles
+  L.tiles = align_up(L.tab + slstm::seq_table_ints(T) * sizeof(int));
+  L.total = align_up(L.tiles + slstm::aligned_tile_ints(slstm::backward_aligned_cap(T)) * sizeof(int));
   return L;
 }
 
@@ -613,6 +615,15 @@ slstm_status backward(const void* P, slstm_dtype P_dtype, const float* R, const 
     int* tab = at<int>(workspace, L.tab);
     HIP_TRY(slstm::launch_seq_table(seqs.cu, seqs.n, T, tab, st));
     seqs.tab = tab;
+    const long long steps = slstm::backward_aligned_steps();
+    if (scan && (T + steps - 1) / steps + static_cast<long long>(seqs.n) <= slstm::backward_aligned_cap(T)) {
+      // the reverse scan on tiles aligned to the sequences (each chain runs from a sequence's
+      // last tile to its first)
+      int* tiles = at<int>(workspace, L.tiles);
+      seqs.tile_cap = slstm::backward_aligned_cap(T);
+      HIP_TRY(slstm::launch_aligned_tiles(seqs.cu, seqs.n, T, static_cast<int>(steps), seqs.tile_cap, tiles, st));
+      seqs.tiles = tiles;
+    }
   }
   const uint32_t ep = next_epoch();
   HIP_TRY(timed(SLSTM_KERNEL_BACKWARD, st, [&] {

@@ -206,8 +206,21 @@ __global__ __launch_bounds__(kBackBlock, SLSTM_BACK_MIN_WAVES) void backward_cha
 #endif
 constexpr int kBackScanBlock = 256;  // 4 waves x 16 features x 4 sub-chunks
 constexpr int kBackScanTSub = SLSTM_BACK_SCAN_TSUB;
+// Packed rows on tiles aligned to the sequences (see launch_aligned_tiles): the sub-chunks are
+// longer, so that a pack's tiles (at most one more per sequence than the row's) fit the
+// look-back words and rows of sums sized for the shorter tiles. 48-step tiles with every tile
+// an anchor measured fastest on MI355X (292-sequence pack of 262,144 steps at d_h = 1024:
+// 5.18 ms against 5.26 for 40-step tiles, 5.42 with anchors every other tile, 6.56 unaligned)
+#ifndef SLSTM_BACK_ALIGNED_TSUB
+#define SLSTM_BACK_ALIGNED_TSUB 12
+#endif
+constexpr int kBackAlignedTSub = SLSTM_BACK_ALIGNED_TSUB;
+static_assert(kBackAlignedTSub >= kBackScanTSub, "look-back words are sized for the shorter tiles");
+#ifndef SLSTM_BACK_ALIGNED_ANCHOR_STRIDE
+#define SLSTM_BACK_ALIGNED_ANCHOR_STRIDE 1
+#endif
 
-template <bool BF16, int CM, bool GS, int TSUB, bool PACKED>
+template <bool BF16, int CM, bool GS, int TSUB, bool PACKED, bool ALIGNED>
 __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void backward_scan_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S, const float* __restrict__ g, const float* __restrict__ g_h,
@@ -215,7 +228,7 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
     float* __restrict__ sum_rows, int T, int d, int n_jt, int n_lg, int n_tt, int anchor_stride,
     unsigned long long* __restrict__ desc, unsigned int* __restrict__ tickets, int n_ctr,
     uint32_t epoch, const int* __restrict__ cu, int n_seqs,
-    const int* __restrict__ seq_tab) {
+    const int* __restrict__ seq_tab, const int* __restrict__ tiles, int tile_cap) {
   constexpr bool sig = (CM & kCellSigmoid) != 0;   // forget-gate form and read-out,
   constexpr bool floored = (CM & kCellFloored) != 0;  // fixed per instantiation
   __shared__ int s_tile[2];
@@ -223,11 +236,38 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
   if (tid == 0) take_ticket(tickets, n_ctr, n_lg, n_tt, s_tile[0], s_tile[1]);
   __syncthreads();
   // tickets (and the look-back) run from the last tile along T to the first
-  const int tr = __builtin_amdgcn_readfirstlane(s_tile[0]);
+  int tr = __builtin_amdgcn_readfirstlane(s_tile[0]);
   const int lg = __builtin_amdgcn_readfirstlane(s_tile[1]);
-  const int tt = n_tt - 1 - tr;
   const int b = lg / n_jt;
   const int jt = lg - b * n_jt;
+  // the tile's row of sums, its first step, the end of its steps, the look-back words of its chain
+  int tt = n_tt - 1 - tr, row = b * n_tt + tt, t_tile = tt * 4 * TSUB, t_end = T, aseq = -1, a_start = 0;
+  unsigned long long* dsc = desc;
+  if constexpr (ALIGNED) {
+    // tile id order[tr] is position tr of its sequence's chain, counted from the sequence's last
+    // tile (tiles[1 + 2 cap + id]); it covers time position nt - 1 - tr of the sequence
+    const int n_real = __builtin_amdgcn_readfirstlane(tiles[0]);
+    row = tr;
+    if (tr >= n_real) {  // a ticket past the last tile: its row of sums is zero
+      const unsigned jz = static_cast<unsigned>(jt * 64) + (threadIdx.x >> 2);
+      if ((threadIdx.x & 3) == 0 && jz < static_cast<unsigned>(d)) {
+        float* rows = sum_rows + static_cast<i64>(tr) * 8 * static_cast<i64>(d);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rows[e * d + jz] = 0.0f;
+      }
+      return;
+    }
+    const int id = __builtin_amdgcn_readfirstlane(tiles[1 + tr]);
+    aseq = __builtin_amdgcn_readfirstlane(tiles[1 + tile_cap + id]);
+    const int pos = __builtin_amdgcn_readfirstlane(tiles[1 + 2 * tile_cap + id]);
+    a_start = min(max(cu[aseq], 0), T);
+    t_end = min(max(cu[aseq + 1], a_start), T);
+    const int nt = (t_end - a_start + 4 * TSUB - 1) / (4 * TSUB);
+    t_tile = a_start + (nt - 1 - pos) * 4 * TSUB;
+    dsc = desc + static_cast<i64>(id - pos) * kLookBackWords * static_cast<i64>(n_lg) * 64;
+    row = id;
+    tr = pos;
+  }
 
   // quad position q holds sub-chunk 3 - q: the quad scans in reverse order of time
   const int l = tid & 63;
@@ -237,7 +277,6 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
   const unsigned ud = static_cast<unsigned>(d);
   const unsigned j = static_cast<unsigned>(jt * 64 + lane_in_tile);
   const bool valid = j < ud;
-  const int t_tile = tt * 4 * TSUB;
   const int t_start = t_tile + sc * TSUB;
   const i64 n_lanes_pad = static_cast<i64>(n_lg) * 64;
   const i64 my_lane = static_cast<i64>(lg) * 64 + lane_in_tile;
@@ -250,11 +289,19 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
   const rsrc_t rsH = make_rsrc(g_h != nullptr ? g_h + (static_cast<i64>(b) * T + t_tile) * static_cast<i64>(d) : g_h);
   const unsigned lane_off = static_cast<unsigned>(sc * TSUB) * 4u * ud + j;  // elements
 
-  const unsigned long long pf = quad_look_back_prefetch(desc, n_lanes_pad, my_lane, q, tr, anchor_stride);
+  const unsigned long long pf = quad_look_back_prefetch(dsc, n_lanes_pad, my_lane, q, tr, anchor_stride);
 
   // packed: the sequence starting at each step of the sub-chunk and the one ending there (-1: none)
   int sq[TSUB], lq[TSUB];
-  if constexpr (PACKED) {
+  if constexpr (ALIGNED) {
+    // a tile holds steps of one sequence: its start is the first step of the first tile
+#pragma unroll
+    for (int u = 0; u < TSUB; ++u) {
+      const int t = t_start + u;
+      sq[u] = (t < t_end && t == a_start) ? aseq : -1;
+      lq[u] = (t < t_end && t + 1 == t_end) ? aseq : -1;
+    }
+  } else if constexpr (PACKED) {
     SeqCursor seq = seq_cursor(cu, n_seqs, b, t_start, seq_tab);
 #pragma unroll
     for (int u = 0; u < TSUB; ++u) {
@@ -274,7 +321,7 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
       gs[u][k] = 0.0f;
     }
     const int t = t_start + u;
-    if (valid && t < T) {
+    if (valid && t < t_end) {
       const unsigned o = lane_off + u * 4u * ud;
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -286,7 +333,7 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
         for (int k = 0; k < 4; ++k) gs[u][k] = buf_ld(rsG, 4u * o, 4u * k * ud);
       }
       if (g_h != nullptr) gs[u][3] += buf_ld(rsH, 4u * (static_cast<unsigned>(sc * TSUB + u) * ud + j), 0);
-      const int fs = PACKED ? lq[u] : (t == T - 1 ? b : -1);  // the sequence that ends at t
+      const int fs = (PACKED || ALIGNED) ? lq[u] : (t == T - 1 ? b : -1);  // the sequence that ends at t
       if (g_final != nullptr && fs >= 0) {
         const float* gf = g_final + static_cast<i64>(fs) * 4 * static_cast<i64>(d);
 #pragma unroll
@@ -311,7 +358,7 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
           const float* s0 = state0 + static_cast<i64>(b) * 4 * static_cast<i64>(d);
           pv0 = {s0[j], s0[ud + j], s0[2 * ud + j], s0[3 * ud + j]};
         }
-      } else if (t_start < T) {
+      } else if (t_start < t_end) {
         const float* sp = S + (static_cast<i64>(b) * T + t_start - 1) * 4 * static_cast<i64>(d);
         pv0 = {sp[j], sp[ud + j], sp[2 * ud + j], sp[3 * ud + j]};
       }
@@ -327,9 +374,9 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
 #pragma unroll
   for (int u = TSUB - 1; u >= 0; --u) {
     const int t = t_start + u;
-    if (valid && t < T) {
+    if (valid && t < t_end) {
       CellIn pv = (u == 0) ? pv0 : CellIn{sv[u - 1][0], sv[u - 1][1], sv[u - 1][2], sv[u - 1][3]};
-      if (PACKED && sq[u] >= 0) pv = state0_of(state0, sq[u], ud, j);
+      if ((PACKED || ALIGNED) && sq[u] >= 0) pv = state0_of(state0, sq[u], ud, j);
       float f[4], A[16], At[16];
       cell_step<true>(pv, pg[u][0], pg[u][1], pg[u][2], pg[u][3], rz, ri, rf, ro, sig, floored, f, A);
 #pragma unroll
@@ -342,7 +389,7 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
       mat4_vec(At, w, zero, v);
       mat4_mul_left(At, M);
     }
-    if (PACKED && sq[u] >= 0) {
+    if ((PACKED || ALIGNED) && sq[u] >= 0) {
       // a sequence start: nothing flows back to the step before it (padding lanes past d_h
       // too, so that all lanes of a tile agree on where the maps restart)
 #pragma unroll
@@ -358,7 +405,7 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
   {
     float arow[4], av;
     quad_row_of_last(M, v, q, arow, av);
-    quad_look_back<PACKED>(arow, av, carry, desc, n_lanes_pad, my_lane, q, tr, anchor_stride, epoch, pf);
+    quad_look_back<PACKED>(arow, av, carry, dsc, n_lanes_pad, my_lane, q, tr, anchor_stride, epoch, pf);
   }
   // y entering the sub-chunk: the inclusive value of the thread before in the quad
   float y[4];
@@ -377,9 +424,9 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
 #pragma unroll
   for (int u = TSUB - 1; u >= 0; --u) {
     const int t = t_start + u;
-    if (valid && t < T) {
+    if (valid && t < t_end) {
       CellIn pv = (u == 0) ? pv0 : CellIn{sv[u - 1][0], sv[u - 1][1], sv[u - 1][2], sv[u - 1][3]};
-      if (PACKED && sq[u] >= 0) pv = state0_of(state0, sq[u], ud, j);
+      if ((PACKED || ALIGNED) && sq[u] >= 0) pv = state0_of(state0, sq[u], ud, j);
       float lam[4], dx[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) lam[e] = gs[u][e] + y[e];
@@ -391,7 +438,7 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
         dr[e] = fmaf(dx[e], pv.h, dr[e]);
         db[e] += dx[e];
       }
-      if (PACKED && sq[u] >= 0) {
+      if ((PACKED || ALIGNED) && sq[u] >= 0) {
         if (dstate0 != nullptr) {
           float* ds = dstate0 + static_cast<i64>(sq[u]) * 4 * static_cast<i64>(d);
 #pragma unroll
@@ -410,11 +457,11 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
     tot[4 + e] = ((quad_bcast<0>(db[e]) + quad_bcast<1>(db[e])) + quad_bcast<2>(db[e])) + quad_bcast<3>(db[e]);
   }
   if (valid && q == 0) {
-    float* rows = sum_rows + (static_cast<i64>(b) * n_tt + tt) * 8 * static_cast<i64>(d);
+    float* rows = sum_rows + static_cast<i64>(row) * 8 * static_cast<i64>(d);
 #pragma unroll
     for (int e = 0; e < 8; ++e) rows[e * ud + j] = tot[e];
   }
-  if (!PACKED && valid && t_start == 0 && dstate0 != nullptr) {
+  if (!PACKED && !ALIGNED && valid && t_start == 0 && dstate0 != nullptr) {
     float* ds = dstate0 + static_cast<i64>(b) * 4 * static_cast<i64>(d);
 #pragma unroll
     for (int e = 0; e < 4; ++e) ds[e * ud + j] = y[e];
@@ -497,6 +544,9 @@ size_t backward_desc_words(int B, int T, int d, bool scan) {
   return static_cast<size_t>(scan ? g.n_tt * kLookBackWords * g.n_lg * 64 : g.n_tt * kBackWords * g.n_lg * kBackBlock);
 }
 
+int backward_aligned_steps() { return 4 * kBackAlignedTSub; }
+int backward_aligned_cap(int T) { return static_cast<int>(back_grid(1, T, 1, true).n_tt); }
+
 size_t backward_row_floats(int B, int T, int d, bool scan) {
   const BackGrid g = back_grid(B, T, d, scan);
   const i64 chunk = row_chunk(g.rows);
@@ -513,6 +563,9 @@ hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const flo
   const bool packed = seqs.cu != nullptr;
   if (packed && (!scan || B != 1)) return hipErrorInvalidValue;  // packed: the scan form, one row
   const BackGrid gr = back_grid(B, T, d, scan);
+  const bool aligned = packed && seqs.tiles != nullptr;
+  // aligned: one ticket per slot of the tile table (the rows and words hold that many tiles)
+  if (aligned && seqs.tile_cap != gr.n_tt) return hipErrorInvalidValue;
   const i64 blocks = gr.n_lg * gr.n_tt;
   const i64 chunk = row_chunk(gr.rows);
   const i64 chunks = (gr.rows + chunk - 1) / chunk;
@@ -539,30 +592,38 @@ hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const flo
   } while (0)
   if (scan) {
     const int stride = look_back_anchor_stride(gr.n_lg, SLSTM_BACK_SCAN_MIN_WAVES);
-  // packed rows are few lane groups along a long T: anchors every 4 tiles (measured best
-  // between 1 and 8 over short and long sequence mixes)
-  const int stride_used = seqs.cu != nullptr ? kPackedAnchorStride : stride;
-    if (packed) {
-#define SLSTM_BACK_LAUNCH(BF, CM_, GS)                                                                   \
-  backward_scan_kernel<BF, CM_, GS, kBackScanTSub, true><<<grid, kBackScanBlock, 0, stream>>>(           \
+    // packed rows are few lane groups along a long T: anchors every 4 tiles (measured best
+    // between 1 and 8 over short and long sequence mixes); on aligned tiles every tile is an
+    // anchor, one plain chain per sequence, as in the iteration
+    const int stride_used = aligned ? SLSTM_BACK_ALIGNED_ANCHOR_STRIDE : (packed ? kPackedAnchorStride : stride);
+    if (aligned) {
+#define SLSTM_BACK_LAUNCH(BF, CM_, GS)                                                                        \
+  backward_scan_kernel<BF, CM_, GS, kBackAlignedTSub, false, true><<<grid, kBackScanBlock, 0, stream>>>(      \
       P, R, state0, S, g, g_h, g_final, dP, dpb, dstate0, rows, T, d, a, c, e, stride_used, desc, tickets, n_ctr, \
-      epoch, seqs.cu, seqs.n, seqs.tab)
+      epoch, seqs.cu, seqs.n, seqs.tab, seqs.tiles, seqs.tile_cap)
       SLSTM_BACK_DISPATCH;
 #undef SLSTM_BACK_LAUNCH
+    } else if (packed) {
+#define SLSTM_BACK_LAUNCH(BF, CM_, GS)                                                                        \
+  backward_scan_kernel<BF, CM_, GS, kBackScanTSub, true, false><<<grid, kBackScanBlock, 0, stream>>>(         \
+      P, R, state0, S, g, g_h, g_final, dP, dpb, dstate0, rows, T, d, a, c, e, stride_used, desc, tickets, n_ctr, \
+      epoch, seqs.cu, seqs.n, seqs.tab, nullptr, 0)
+      SLSTM_BACK_DISPATCH;
+#undef SLSTM_BACK_LAUNCH
+    } else {
+#define SLSTM_BACK_LAUNCH(BF, CM_, GS)                                                                        \
+  backward_scan_kernel<BF, CM_, GS, kBackScanTSub, false, false><<<grid, kBackScanBlock, 0, stream>>>(        \
+      P, R, state0, S, g, g_h, g_final, dP, dpb, dstate0, rows, T, d, a, c, e, stride_used, desc, tickets, n_ctr, \
+      epoch, nullptr, 0, nullptr, nullptr, 0)
+      SLSTM_BACK_DISPATCH;
+#undef SLSTM_BACK_LAUNCH
+    }
+    if (packed && dstate0 != nullptr && seqs.n > 0) {
       hipError_t err = hipGetLastError();
       if (err != hipSuccess) return err;
-      if (dstate0 != nullptr && seqs.n > 0) {
-        const i64 n = static_cast<i64>(seqs.n) * 4 * d;
-        const unsigned blocks_e = static_cast<unsigned>(std::min<i64>((n + 255) / 256, 4096));
-        empty_seq_dstate0_kernel<<<blocks_e, 256, 0, stream>>>(seqs.cu, g_final, dstate0, seqs.n, 4 * d);
-      }
-    } else {
-#define SLSTM_BACK_LAUNCH(BF, CM_, GS)                                                                   \
-  backward_scan_kernel<BF, CM_, GS, kBackScanTSub, false><<<grid, kBackScanBlock, 0, stream>>>(          \
-      P, R, state0, S, g, g_h, g_final, dP, dpb, dstate0, rows, T, d, a, c, e, stride_used, desc, tickets, n_ctr, \
-      epoch, nullptr, 0, nullptr)
-      SLSTM_BACK_DISPATCH;
-#undef SLSTM_BACK_LAUNCH
+      const i64 n = static_cast<i64>(seqs.n) * 4 * d;
+      const unsigned blocks_e = static_cast<unsigned>(std::min<i64>((n + 255) / 256, 4096));
+      empty_seq_dstate0_kernel<<<blocks_e, 256, 0, stream>>>(seqs.cu, g_final, dstate0, seqs.n, 4 * d);
     }
   } else {
 #define SLSTM_BACK_LAUNCH(BF, CM_, GS)                                                                      \

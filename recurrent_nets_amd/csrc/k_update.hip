@@ -215,48 +215,114 @@ hipError_t launch_seq_table(const int* cu, int n_seqs, int T, int* tab, hipStrea
 
 // Tiles aligned to packed sequences: sequence s gets ceil(len_s / tile_steps) tiles, numbered
 // consecutively (tile id = the sequence's first tile + its position p), none straddling a start.
-// The order they are handed out in is by position, then sequence, so every tile comes after the
-// tiles before it in its sequence (the only ones it waits on) while the tiles in flight at once
-// belong to many sequences. One thread builds it (a few thousand entries, once per solve); at
-// most cap tiles are made, whatever the offsets hold (offsets are clamped into [0, T]).
+// The order they are handed out in is by position (any order among the tiles of one position):
+// every tile comes after the tiles before it in its sequence (the only ones it waits on), while
+// the tiles in flight at once belong to many sequences. One workgroup builds it, once per solve:
+// block scans give each sequence its first id; a histogram of the tile counts, summed from the
+// top, gives the tiles at each position and its exclusive prefix the first slot of each
+// position; each tile then takes the next slot of its position. At most cap tiles are made,
+// whatever the offsets hold (offsets are clamped into [0, T]).
 // Layout of tiles: [0] count, [1, 1 + cap) order, then cap sequence ids, cap positions, and
 // cap counters of scratch.
-__global__ __launch_bounds__(64) void aligned_tiles_kernel(const int* __restrict__ cu, int n_seqs, int T,
-                                                          int tile_steps, int cap, int* __restrict__ tiles) {
-  if (threadIdx.x != 0) return;
+constexpr int kTileBlock = 1024;
+
+// inclusive sum over the workgroup's threads in thread order; *total receives the sum of all
+template <class V>
+__device__ V block_inclusive_sum(V v, V* s_wave, V* total) {
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const V u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) s_wave[w] = v;
+  __syncthreads();
+  if (w == 0) {
+    V t = lane < kTileBlock / 64 ? s_wave[lane] : V(0);
+#pragma unroll
+    for (int o = 1; o < kTileBlock / 64; o <<= 1) {
+      const V u = __shfl_up(t, o, 64);
+      if (lane >= o) t += u;
+    }
+    if (lane < kTileBlock / 64) s_wave[lane] = t;
+  }
+  __syncthreads();
+  if (w > 0) v += s_wave[w - 1];
+  *total = s_wave[kTileBlock / 64 - 1];
+  __syncthreads();  // s_wave is free again
+  return v;
+}
+
+__global__ __launch_bounds__(kTileBlock) void aligned_tiles_kernel(const int* __restrict__ cu, int n_seqs, int T,
+                                                                  int tile_steps, int cap, int* __restrict__ tiles) {
+  __shared__ long long s_wave[kTileBlock / 64];  // 64-bit: tile counts of clamped offsets may be large
+  __shared__ int s_max;
   int* order = tiles + 1;
   int* seq = tiles + 1 + cap;
   int* pos = tiles + 1 + 2 * cap;
-  int* cnt = tiles + 1 + 3 * cap;  // tiles per position, then the next slot per position
-  int n = 0, max_nt = 0;
-  for (int s = 0; s < n_seqs && n < cap; ++s) {
-    const int a = min(max(cu[s], 0), T);
-    const int e = min(max(cu[s + 1], a), T);
-    const int nt = min((e - a + tile_steps - 1) / tile_steps, cap - n);
-    for (int p = 0; p < nt; ++p) {
-      seq[n + p] = s;
-      pos[n + p] = p;
+  int* cnt = tiles + 1 + 3 * cap;  // histogram, then tiles per position, then next slot per position
+  const int tid = threadIdx.x;
+  for (int i = tid; i < cap; i += kTileBlock) cnt[i] = 0;
+  if (tid == 0) s_max = 0;
+  __syncthreads();
+  // each sequence's tiles: ids first .. first + nt - 1 (cut at cap), positions 0 .. nt - 1
+  int made = 0;  // ids handed out so far (uniform)
+  for (int base = 0; base < n_seqs; base += kTileBlock) {
+    const int s = base + tid;
+    long long nt = 0;
+    if (s < n_seqs) {
+      const int a = min(max(cu[s], 0), T);
+      const int e = min(max(cu[s + 1], a), T);
+      nt = (e - a + tile_steps - 1) / tile_steps;
     }
-    n += nt;
-    max_nt = max(max_nt, nt);
+    long long chunk = 0;
+    const long long first = made + block_inclusive_sum(nt, s_wave, &chunk) - nt;
+    const int kept = static_cast<int>(max(0LL, min(nt, cap - first)));
+    for (int p = 0; p < kept; ++p) {
+      seq[first + p] = s;
+      pos[first + p] = p;
+    }
+    if (kept > 0) {
+      atomicAdd(&cnt[kept - 1], 1);  // sequences with exactly `kept` tiles
+      atomicMax(&s_max, kept);
+    }
+    made = static_cast<int>(min(made + chunk, static_cast<long long>(cap)));
   }
-  for (int p = 0; p < max_nt; ++p) cnt[p] = 0;
-  for (int id = 0; id < n; ++id) ++cnt[pos[id]];
-  int run = 0;  // exclusive prefix: the first slot of each position
-  for (int p = 0; p < max_nt; ++p) {
-    const int c = cnt[p];
-    cnt[p] = run;
-    run += c;
+  __syncthreads();
+  const int n = made;
+  const int max_nt = s_max;
+  // tiles at position p = sequences with more than p tiles: the histogram summed from the top
+  long long carry = 0;
+  for (int top = max_nt; top > 0; top -= kTileBlock) {
+    const int i = top - 1 - tid;
+    const long long v = i >= 0 ? cnt[i] : 0;
+    long long chunk = 0;
+    const long long incl = block_inclusive_sum(v, s_wave, &chunk);
+    if (i >= 0) cnt[i] = static_cast<int>(carry + incl);
+    carry += chunk;
   }
-  for (int id = 0; id < n; ++id) order[cnt[pos[id]]++] = id;  // ids ascend with the sequence
-  tiles[0] = n;
+  __syncthreads();
+  // the first slot of each position: exclusive prefix of the tiles per position
+  carry = 0;
+  for (int base = 0; base < max_nt; base += kTileBlock) {
+    const int i = base + tid;
+    const long long v = i < max_nt ? cnt[i] : 0;
+    long long chunk = 0;
+    const long long incl = block_inclusive_sum(v, s_wave, &chunk);
+    if (i < max_nt) cnt[i] = static_cast<int>(carry + incl - v);
+    carry += chunk;
+  }
+  __syncthreads();
+  for (int id = tid; id < n; id += kTileBlock) order[atomicAdd(&cnt[pos[id]], 1)] = id;
+  if (tid == 0) tiles[0] = n;
 }
 
 size_t aligned_tile_ints(int cap) { return 1 + 4 * static_cast<size_t>(cap); }
 
 hipError_t launch_aligned_tiles(const int* cu, int n_seqs, int T, int tile_steps, int cap, int* tiles,
                                 hipStream_t stream) {
-  aligned_tiles_kernel<<<1, 64, 0, stream>>>(cu, n_seqs, T, tile_steps, cap, tiles);
+  aligned_tiles_kernel<<<1, kTileBlock, 0, stream>>>(cu, n_seqs, T, tile_steps, cap, tiles);
   return hipGetLastError();
 }
 

@@ -75,6 +75,11 @@ hipError_t launch_warm_chain(const void* P, bool p_bf16, const float* state0, fl
 // dR and dbias over the tiles' rows; rows holds backward_row_floats floats
 size_t backward_desc_words(int B, int T, int d, bool scan);
 size_t backward_row_floats(int B, int T, int d, bool scan);
+// packed rows on aligned tiles (Seqs::tiles, positions counted from each sequence's last tile):
+// a table of backward_aligned_cap(T) slots of backward_aligned_steps() steps, which the words
+// and rows of the scan form hold
+int backward_aligned_steps();
+int backward_aligned_cap(int T);
 hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const float* state0,
                            const float* S, const float* g, const float* g_h, const float* g_final,
                            void* dP, bool dp_bf16, float* dR, float* dbias, float* dstate0,

@@ -27,6 +27,10 @@ LAYOUTS = {
     # lengths at and around the 32-step tiles of the scan form's aligned tiles (which serve packs
     # of at most about T / 32 sequences: this one, "mixed" and "single")
     "tile_edges": [32, 0, 33, 31, 1, 64, 0, 96, 2, 65, 127, 1, 300],
+    # lengths at and around multiples of 96 steps, i.e. of the backward's 48-step aligned tiles
+    # (which serve packs of at most about T / 96 sequences: this one, "single" and the
+    # full-size pack) and of the iteration's 32-step ones
+    "wide_tile_edges": [96, 0, 97, 95, 1, 192, 0, 288, 2, 193, 383, 1, 4000],
 }
 
 
@@ -132,11 +136,12 @@ def test_packed_newton_early_stop(gpu_lib, schedule):
     assert h_rel_err(h, S_ref[..., 3, :]) < H_TOL_BF16
 
 
-def test_packed_aligned_tiles_reproducible(gpu_lib):
+@pytest.mark.parametrize("layout", ["tile_edges", "wide_tile_edges"])
+def test_packed_aligned_tiles_reproducible(gpu_lib, layout):
     """The scan form on tiles aligned to the sequences: two solves give the same bits (the
     tiles of many sequences run at once, in whatever order the hardware schedules them)."""
-    P, R, s0, cu = _problem(815, LAYOUTS["tile_edges"], 200, "exp")
-    case("packed aligned tiles reproducible")
+    P, R, s0, cu = _problem(815, LAYOUTS[layout], 200, "exp")
+    case(f"packed aligned tiles reproducible {layout}")
     Pd, Rd, s0d = _dev(P, R, s0)
     a = gpu_lib.newton_forward(Pd, Rd, s0d, "exp", 3, 0.0, schedule="fused_scan", cu_seqlens=cu)[0].clone()
     b = gpu_lib.newton_forward(Pd, Rd, s0d, "exp", 3, 0.0, schedule="fused_scan", cu_seqlens=cu)[0]
@@ -198,6 +203,24 @@ def test_packed_backward(gpu_lib, schedule, layout, forget):
     for s in range(len(lengths)):  # an empty sequence passes g_final to its dstate0 unchanged
         if cu[s] == cu[s + 1]:
             assert torch.equal(ds0[s].cpu(), gf[s])
+
+
+def test_packed_backward_aligned_reproducible(gpu_lib):
+    """The backward on sequence-aligned tiles (taken for this pack) forms every value in one
+    fixed order: two calls agree bitwise."""
+    lengths = LAYOUTS["wide_tile_edges"]
+    P, R, s0, cu = _problem(870, lengths, 130, "exp")
+    S = torch.from_numpy(ref.sequential(to_np(P), to_np(R), to_np(s0), "exp", cu_seqlens=cu).astype(np.float32))
+    gen = torch.Generator().manual_seed(871)
+    gh = torch.randn((1, P.shape[1], 130), generator=gen)
+    gf = torch.randn((len(lengths), 4, 130), generator=gen)
+    case("packed backward on aligned tiles, twice")
+    args = _dev(P, R, S, s0) + [None] + _dev(gh, gf)
+    a = [t.clone() for t in gpu_lib.backward(*args, "exp", want_dbias=True, cu_seqlens=cu)]
+    b = gpu_lib.backward(*args, "exp", want_dbias=True, cu_seqlens=cu)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
 
 
 def test_packed_backward_bf16_dp(gpu_lib):
