@@ -375,12 +375,13 @@ slstm_status slstm_backward_varlen(const void* P, slstm_dtype P_dtype, const flo
  * `states`, as slstm_backward ([SL] "Backward"): g_states (B, T, 4, d_h), g_h (B, T, d_h) and
  * g_final (B, 4, d_h) are the loss's direct gradients (each may be NULL: zero); outputs dP
  * (B, T, 4, d_h) in dP_dtype (F32 or BF16, rounded to nearest even), dR (4, n_heads, d_head,
- * d_head), dbias (4, d_h; may be NULL), dstate0 (B, 4, d_h; may be NULL); d_head 8, 16, 32 or
- * 64 (128 is rejected with SLSTM_EINVAL: a lane's block row and dR row would not fit in
- * registers, nor the head's transposed blocks in LDS). One workgroup per
+ * d_head), dbias (4, d_h; may be NULL), dstate0 (B, 4, d_h; may be NULL); d_head 8, 16, 32, 64
+ * or 128 (heads of 128 units read their blocks of R from memory at every step: a lane's block
+ * row and dR row would not fit in registers, nor the head's blocks in LDS). One workgroup per
  * (batch row, head) walks T backwards; dR and dbias are added over the batch in a fixed order
  * from per-row partial sums in the workspace (slstm_head_backward_workspace_bytes; 0 if the
- * sizes are invalid), so results are reproducible bit for bit.
+ * sizes are invalid; for heads of 128 units it also holds the transposed blocks of R), so
+ * results are reproducible bit for bit.
  * The _varlen forms take packed sequences as the channelwise _varlen calls do (one row of T steps,
  * cu_seqlens (n_seqs + 1 device ints), state0, final_state, g_final and dstate0 per sequence):
  * a sequence start takes state0[s] as the state before it, its Jacobian is zero for the Newton

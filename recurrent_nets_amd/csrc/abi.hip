@@ -1075,7 +1075,7 @@ slstm_status head_backward(const void* P, slstm_dtype P_dtype, const float* R, c
   s = check_heads(d_h, n_heads, R);
   if (s != SLSTM_OK) return s;
   if (!slstm::head_backward_width_supported(d_h / n_heads))
-    return fail(SLSTM_EINVAL, "the head-mixing backward takes heads of 8, 16, 32 or 64 units (got %d)", d_h / n_heads);
+    return fail(SLSTM_EINVAL, "the head-mixing backward takes heads of 8, 16, 32, 64 or 128 units (got %d)", d_h / n_heads);
   if (dP == nullptr || dR == nullptr) return fail(SLSTM_EINVAL, "dP and dR must not be NULL");
   if (dP_dtype != SLSTM_F32 && dP_dtype != SLSTM_BF16) return fail(SLSTM_EINVAL, "unknown dP dtype %d", (int)dP_dtype);
   if (!aligned(dP, 4) || !aligned(dR, 4) || !aligned(dbias, 4) || !aligned(dstate0, 4) || !aligned(g_states, 4) ||

@@ -17,8 +17,13 @@
 // quad. The step is branch-free and the dP stores are batched per 8-step block, as in the
 // one-sweep forward. Heads of 64 units keep the block columns in LDS instead (the head's four
 // transposed blocks, 64 KiB, rows padded so that the 16 lanes the LDS serves together hit
-// distinct banks): a lane's row, column and dR row (192 floats) would not fit the register file. dR and dbias leave as per-row partial sums that a second kernel adds over
-// the batch in a fixed order.
+// distinct banks): a lane's row, column and dR row (192 floats) would not fit the register file.
+// Heads of 128 units stream R: the four blocks (256 KiB) fit neither the LDS nor, beside the
+// lane's dR row, the registers, so each step reads the lane's row of its block and its column
+// (a row of the transposed blocks, written to the workspace first) from memory, as float4
+// loads a few at a time (the L2 holds them; every batch row of the head reads the same blocks).
+// dR and dbias leave as per-row partial sums that a second kernel adds over the batch in a fixed
+// order.
 #include "cell.h"
 #include "head.h"
 #include "kernels.h"
@@ -70,6 +75,51 @@ __device__ __forceinline__ float lds_col_dot(const float* col, const float* v) {
   return acc0 + acc1;
 }
 
+// Heads of 128 units: row i of gate g's block of M (R, or its transposed blocks) times v (in
+// LDS), M read from memory SLSTM_HEAD_STREAM_CHUNK float4 loads at a time
+// (4 measured fastest on MI355X, 62 ms for B = 16, T = 4096, 8 heads of 128, against 64 and 67
+// for 8 and 16: the walk waits on the L2 for every chunk)
+#ifndef SLSTM_HEAD_STREAM_CHUNK
+#define SLSTM_HEAD_STREAM_CHUNK 4
+#endif
+template <int DH>
+__device__ __forceinline__ float stream_row_dot(const float* __restrict__ M, int nh, int a, int i, int g,
+                                                const float* v) {
+  constexpr int kChunk = SLSTM_HEAD_STREAM_CHUNK;
+  const float4* src = reinterpret_cast<const float4*>(M + ((static_cast<i64>(g) * nh + a) * DH + i) * DH);
+  const float4* v4 = reinterpret_cast<const float4*>(v);
+  float acc0 = 0.0f, acc1 = 0.0f;
+  // a loop kept rolled: unrolled, the compiler hoists the step-invariant loads out of the walk
+  // along T and spills what it hoisted
+#pragma unroll 1
+  for (int k0 = 0; k0 < DH / 4; k0 += kChunk) {
+    float4 r[kChunk];
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) r[k] = src[k0 + k];
+#pragma unroll
+    for (int k = 0; k < kChunk; ++k) {
+      const float4 x = v4[k0 + k];
+      acc0 = fmaf(r[k].x, x.x, acc0);
+      acc1 = fmaf(r[k].y, x.y, acc1);
+      acc0 = fmaf(r[k].z, x.z, acc0);
+      acc1 = fmaf(r[k].w, x.w, acc1);
+    }
+  }
+  return acc0 + acc1;
+}
+
+// RT[g, a, i, k] = R[g, a, k, i]: the transposed blocks
+__global__ __launch_bounds__(256) void transpose_blocks_kernel(const float* __restrict__ R, float* __restrict__ RT,
+                                                               int nh, int dh) {
+  const i64 n = static_cast<i64>(4) * nh * dh * dh;
+  for (i64 e = static_cast<i64>(blockIdx.x) * 256 + threadIdx.x; e < n; e += static_cast<i64>(gridDim.x) * 256) {
+    const i64 blk = e / (static_cast<i64>(dh) * dh);
+    const int rest = static_cast<int>(e - blk * dh * dh);
+    const int k = rest / dh, i = rest - k * dh;
+    RT[blk * dh * dh + static_cast<i64>(i) * dh + k] = R[e];
+  }
+}
+
 // Packed sequences (PACKED, one batch row): walking T backwards, the kernel follows the sequence
 // holding each step; at a sequence's last step its final-state gradient joins the adjoint, and at
 // its first step the state before is state0[s] (staged behind an extra barrier), the adjoint
@@ -79,13 +129,15 @@ __global__ __launch_bounds__(4 * DH) void head_backward_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S, const float* __restrict__ g_states, const float* __restrict__ g_h,
     const float* __restrict__ g_final, void* __restrict__ dP, float* __restrict__ dR_part,
-    float* __restrict__ db_part, float* __restrict__ dstate0, int T, int d, int nh, Seqs seqs) {
+    float* __restrict__ db_part, float* __restrict__ dstate0, int T, int d, int nh, Seqs seqs,
+    const float* __restrict__ RT) {
   constexpr bool sig = (CM & kCellSigmoid) != 0;
   constexpr bool floored = (CM & kCellFloored) != 0;
   __shared__ __attribute__((aligned(16))) float hbuf[2][DH];      // h of the state before step t
   __shared__ __attribute__((aligned(16))) float dxbuf[2][4][DH];  // dP of step t, per gate
   __shared__ float junk[4 * DH];
-  constexpr bool kColLds = DH >= 64;
+  constexpr bool kStream = DH >= 128;  // R read from memory every step
+  constexpr bool kColLds = DH == 64;   // block columns in LDS
   __shared__ __attribute__((aligned(16))) float colT[kColLds ? ColLds<DH>::kFloats : 4];
   const int tid = threadIdx.x;
   const int i = tid >> 2, g = tid & 3;
@@ -93,10 +145,10 @@ __global__ __launch_bounds__(4 * DH) void head_backward_kernel(
   const int j = a * DH + i;
   const i64 dd = d;
   const GateSel sel(g);
-  float row[DH], col[kColLds ? 1 : DH], dr[DH];
-  load_block_row<DH>(R, nh, a, i, g, row);
+  float row[kStream ? 1 : DH], col[(kColLds || kStream) ? 1 : DH], dr[DH];
+  if constexpr (!kStream) load_block_row<DH>(R, nh, a, i, g, row);
   if constexpr (kColLds) fill_col_lds<DH>(R, nh, a, colT);  // visible after the first barrier below
-  else load_block_col<DH>(R, nh, a, i, g, col);
+  else if constexpr (!kStream) load_block_col<DH>(R, nh, a, i, g, col);
 #pragma unroll
   for (int k = 0; k < DH; ++k) dr[k] = 0.0f;
   float db = 0.0f;
@@ -171,7 +223,8 @@ __global__ __launch_bounds__(4 * DH) void head_backward_kernel(
       }
       // the step's pre-activations and Jacobians at the stored state before it
       float xs[4], ps[4], ls[4];
-      quad_gather(p + block_dot<DH>(row, hb), xs);
+      if constexpr (kStream) quad_gather(p + stream_row_dot<DH>(R, nh, a, i, g, hb), xs);
+      else quad_gather(p + block_dot<DH>(row, hb), xs);
       quad_gather(sp, ps);
       quad_gather(lam, ls);
       float s[4], dxv[4], dpv[3];
@@ -190,7 +243,7 @@ __global__ __launch_bounds__(4 * DH) void head_backward_kernel(
         dr[4 * k + 2] = fmaf(dxm, hv.z, dr[4 * k + 2]);
         dr[4 * k + 3] = fmaf(dxm, hv.w, dr[4 * k + 3]);
       }
-      if constexpr (kColLds) {
+      if constexpr (DH >= 64) {
         // keep the step's dR update here: left free, the compiler sinks all eight steps' updates
         // to the end of the block and holds their h rows in scratch
 #pragma unroll
@@ -205,6 +258,8 @@ __global__ __launch_bounds__(4 * DH) void head_backward_kernel(
       float ys[4];
       if constexpr (kColLds)
         quad_gather(lds_col_dot<DH>(&colT[g * ColLds<DH>::kColGate + i * ColLds<DH>::kColRow], dxbuf[r & 1][g]), ys);
+      else if constexpr (kStream)
+        quad_gather(stream_row_dot<DH>(RT, nh, a, i, g, dxbuf[r & 1][g]), ys);
       else
         quad_gather(block_dot<DH>(col, dxbuf[r & 1][g]), ys);
       const float lprev = g == 3 ? (ys[0] + ys[1]) + (ys[2] + ys[3]) : la;
@@ -263,11 +318,12 @@ __global__ __launch_bounds__(256) void batch_sum_kernel(const float* __restrict_
 
 size_t head_backward_part_floats(int B, int d, int n_heads) {
   const i64 dh = d / n_heads;
-  return static_cast<size_t>(B) * 4 * d * dh + static_cast<size_t>(B) * 4 * d;
+  const size_t rt = dh >= 128 ? static_cast<size_t>(4) * d * dh : 0;  // transposed blocks, streamed heads
+  return static_cast<size_t>(B) * 4 * d * dh + static_cast<size_t>(B) * 4 * d + rt;
 }
 
 bool head_backward_width_supported(int d_head) {
-  return d_head == 8 || d_head == 16 || d_head == 32 || d_head == 64;
+  return d_head == 8 || d_head == 16 || d_head == 32 || d_head == 64 || d_head == 128;
 }
 
 #define SLSTM_HEAD_BWD_DH_DISPATCH(DHV, BODY)        \
@@ -276,6 +332,7 @@ bool head_backward_width_supported(int d_head) {
     case 16: { constexpr int DH = 16; BODY; break; } \
     case 32: { constexpr int DH = 32; BODY; break; } \
     case 64: { constexpr int DH = 64; BODY; break; } \
+    case 128: { constexpr int DH = 128; BODY; break; } \
     default: return hipErrorInvalidValue;            \
   }
 
@@ -287,19 +344,26 @@ hipError_t launch_head_backward(const void* P, bool p_bf16, const float* R, cons
   const int dh = d / n_heads;
   float* dR_part = part;
   float* db_part = part + static_cast<i64>(B) * 4 * d * dh;
+  float* RT = nullptr;
+  if (dh >= 128) {  // the transposed blocks the streamed heads read their columns from
+    RT = db_part + static_cast<i64>(B) * 4 * d;
+    const i64 n = static_cast<i64>(4) * d * dh;
+    transpose_blocks_kernel<<<static_cast<unsigned>(std::min<i64>((n + 255) / 256, 4096)), 256, 0, stream>>>(
+        R, RT, n_heads, dh);
+  }
   const dim3 grid(static_cast<unsigned>(n_heads), static_cast<unsigned>(B));
   // static LDS of a workgroup: the exchange buffers, and for 64-unit heads the transposed blocks
   const unsigned int lds = head_spread_lds(static_cast<long long>(n_heads) * B,
-                                           8192 + (dh >= 64 ? ColLds<64>::kFloats * 4u : 0u));
+                                           8192 + (dh == 64 ? ColLds<64>::kFloats * 4u : 0u));
   const bool packed = seqs.cu != nullptr;
 #define SLSTM_HEAD_BWD(BF, DB, CM_)                                                                             \
   do {                                                                                                          \
     if (packed)                                                                                                 \
       head_backward_kernel<DH, BF, CM_, DB, true><<<grid, 4 * DH, lds, stream>>>(                               \
-          P, R, state0, S, g_states, g_h, g_final, dP, dR_part, db_part, dstate0, T, d, n_heads, seqs);         \
+          P, R, state0, S, g_states, g_h, g_final, dP, dR_part, db_part, dstate0, T, d, n_heads, seqs, RT);     \
     else                                                                                                        \
       head_backward_kernel<DH, BF, CM_, DB, false><<<grid, 4 * DH, lds, stream>>>(                              \
-          P, R, state0, S, g_states, g_h, g_final, dP, dR_part, db_part, dstate0, T, d, n_heads, seqs);         \
+          P, R, state0, S, g_states, g_h, g_final, dP, dR_part, db_part, dstate0, T, d, n_heads, seqs, RT);     \
   } while (0)
 #define SLSTM_HEAD_BWD_TT(CM_) SLSTM_HEAD_BWD(true, true, CM_)
 #define SLSTM_HEAD_BWD_TF(CM_) SLSTM_HEAD_BWD(true, false, CM_)

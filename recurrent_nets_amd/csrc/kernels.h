@@ -138,10 +138,11 @@ hipError_t launch_head_solve(const void* P, bool p_bf16, const float* R, const f
 
 // Backward under head mixing at the stored states S: dP (float32 or bf16), dR (4, n_heads,
 // d_head, d_head), dbias (4, d; may be NULL), dstate0 (B, 4, d; may be NULL); g_states, g_h and
-// g_final may be NULL. `part` holds head_backward_part_floats(B, d, n_heads) floats of per-row
-// partial sums, added over the batch in a fixed order.
+// g_final may be NULL. `part` holds head_backward_part_floats(B, d, n_heads) floats: per-row
+// partial sums, added over the batch in a fixed order, and for heads of 128 units the
+// transposed blocks of R.
 size_t head_backward_part_floats(int B, int d, int n_heads);
-bool head_backward_width_supported(int d_head);  // 8, 16, 32
+bool head_backward_width_supported(int d_head);  // 8, 16, 32, 64, 128
 hipError_t launch_head_backward(const void* P, bool p_bf16, const float* R, const float* state0, const float* S,
                                 const float* g_states, const float* g_h, const float* g_final, void* dP,
                                 bool dp_bf16, float* dR, float* dbias, float* dstate0, int B, int T, int d,

@@ -634,8 +634,8 @@ def head_backward(P, R, states, state0=None, g_states=None, g_h=None, g_final=No
                   dP=None, dR=None, dstate0=None, want_dstate0=True, workspace=None, stream=None,
                   dP_dtype=torch.float32, dbias=None, want_dbias=False, readout="exact", cu_seqlens=None):
     """Gradients through the head-mixing recurrence at the forward solution ``states``
-    (B,T,4,d_h); arguments as ``backward``, R (4, n_heads, d_head, d_head) with d_head 8, 16, 32
-    or 64. Returns (dP, dR (4, n_heads, d_head, d_head), dstate0 or None), and dbias (4, d_h) last
+    (B,T,4,d_h); arguments as ``backward``, R (4, n_heads, d_head, d_head) with d_head 8, 16, 32,
+    64 or 128. Returns (dP, dR (4, n_heads, d_head, d_head), dstate0 or None), and dbias (4, d_h) last
     when ``want_dbias`` or a ``dbias`` tensor is given. With cu_seqlens (packed, B = 1),
     state0, g_final and dstate0 are (S, 4, d_h)."""
     L = load()

@@ -238,7 +238,8 @@ def test_head_backward_argument_checks(lib):
     # transposed blocks in LDS)
     assert lib.slstm_head_backward_workspace_bytes(2, 64, 64, 2) > 0
     assert lib.slstm_head_backward_workspace_bytes(2, 64, 128, 2) > 0       # d_head 64
-    assert lib.slstm_head_backward_workspace_bytes(2, 64, 256, 2) == 0      # d_head 128
+    assert lib.slstm_head_backward_workspace_bytes(2, 64, 256, 2) > 0       # d_head 128
+    assert lib.slstm_head_backward_workspace_bytes(2, 64, 512, 2) == 0      # d_head 256
     assert lib.slstm_head_backward_workspace_bytes(2, 64, 64, 3) == 0
     args = dict(P=ctypes.c_void_p(256), dt=0, R=ctypes.c_void_p(256), s0=None, S=ctypes.c_void_p(256), gs=None,
                 gh=None, gf=None, dP=ctypes.c_void_p(256), dpt=0, dR=ctypes.c_void_p(256), db=None, d0=None, B=2,
@@ -248,8 +249,8 @@ def test_head_backward_argument_checks(lib):
         a = dict(args)
         a.update(kw)
         return lib.slstm_head_backward(*a.values())
-    assert call(d=256) == slstm.EINVAL
-    assert "8, 16, 32 or 64" in lib.slstm_last_error().decode()
+    assert call(d=512) == slstm.EINVAL
+    assert "8, 16, 32, 64 or 128" in lib.slstm_last_error().decode()
     assert call(nh=3) == slstm.EINVAL
     assert call(dP=None) == slstm.EINVAL
     assert call(dR=None) == slstm.EINVAL

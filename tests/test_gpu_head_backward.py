@@ -76,7 +76,7 @@ def _check(got, want, tol=GRAD_TOL, label=""):
     return errs
 
 
-@pytest.mark.parametrize("dh", [8, 16, 32, 64])
+@pytest.mark.parametrize("dh", [8, 16, 32, 64, 128])
 @pytest.mark.parametrize("forget", ["exp", "sigmoid"])
 def test_head_backward_matches_oracle(gpu_lib, dh, forget):
     # seed 1132 with the sigmoid gate has a step within the tie margin; 1200 is the next clear one
@@ -164,9 +164,9 @@ def test_head_backward_reproducible(gpu_lib):
 
 
 def test_head_backward_rejects_wide_heads(gpu_lib):
-    P, R, s0, S = _problem(1170, 1, 4, 128, 1, "exp")
-    case("head backward rejects d_head 128")
-    with pytest.raises(gpu_lib.SlstmError, match="8, 16, 32 or 64"):
+    P, R, s0, S = _problem(1170, 1, 4, 256, 1, "exp")
+    case("head backward rejects d_head 256")
+    with pytest.raises(gpu_lib.SlstmError, match="8, 16, 32, 64 or 128"):
         gpu_lib.head_backward(_on(P), _on(R), _on(S), _on(s0), None, None, None, "exp")
 
 

@@ -133,8 +133,7 @@ def test_head_packed_single_sequence_matches_unpacked(gpu_lib):
     assert h_rel_err(hu3, S_ref[..., 3, :]) < H_TOL_F32
 
 
-@pytest.mark.parametrize("layout", list(LAYOUTS))
-@pytest.mark.parametrize("dh", [8, 32])
+@pytest.mark.parametrize("layout,dh", [(lay, dh) for lay in LAYOUTS for dh in (8, 32)] + [("mixed", 128)])
 def test_head_packed_backward(gpu_lib, layout, dh):
     """At the oracle's packed trajectory (exponential forget gate: every step clear of the
     running maximum's tie), a loss on the states, h and each sequence's final state."""
