@@ -244,9 +244,15 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
   int tt = n_tt - 1 - tr, row = b * n_tt + tt, t_tile = tt * 4 * TSUB, t_end = T, aseq = -1, a_start = 0;
   unsigned long long* dsc = desc;
   if constexpr (ALIGNED) {
-    // tile id order[tr] is position tr of its sequence's chain, counted from the sequence's last
-    // tile (tiles[1 + 2 cap + id]); it covers time position nt - 1 - tr of the sequence
+    // slot tr of the table: tile id at position pos of its sequence's chain, counted from the
+    // sequence's last tile, so it covers time position nt - 1 - pos of the sequence; the slot's
+    // values are read all at once (tr < tile_cap)
     const int n_real = __builtin_amdgcn_readfirstlane(tiles[0]);
+    const int id = __builtin_amdgcn_readfirstlane(tiles[1 + tr]);
+    const int sq = __builtin_amdgcn_readfirstlane(tiles[1 + tile_cap + tr]);
+    const int pos = __builtin_amdgcn_readfirstlane(tiles[1 + 2 * tile_cap + tr]);
+    const int a0 = __builtin_amdgcn_readfirstlane(tiles[1 + 3 * tile_cap + tr]);
+    const int e0 = __builtin_amdgcn_readfirstlane(tiles[1 + 4 * tile_cap + tr]);
     row = tr;
     if (tr >= n_real) {  // a ticket past the last tile: its row of sums is zero
       const unsigned jz = static_cast<unsigned>(jt * 64) + (threadIdx.x >> 2);
@@ -257,11 +263,9 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
       }
       return;
     }
-    const int id = __builtin_amdgcn_readfirstlane(tiles[1 + tr]);
-    aseq = __builtin_amdgcn_readfirstlane(tiles[1 + tile_cap + id]);
-    const int pos = __builtin_amdgcn_readfirstlane(tiles[1 + 2 * tile_cap + id]);
-    a_start = min(max(cu[aseq], 0), T);
-    t_end = min(max(cu[aseq + 1], a_start), T);
+    aseq = sq;
+    a_start = a0;
+    t_end = e0;
     const int nt = (t_end - a_start + 4 * TSUB - 1) / (4 * TSUB);
     t_tile = a_start + (nt - 1 - pos) * 4 * TSUB;
     dsc = desc + static_cast<i64>(id - pos) * kLookBackWords * static_cast<i64>(n_lg) * 64;

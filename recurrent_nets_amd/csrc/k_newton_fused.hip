@@ -141,16 +141,20 @@ __global__ __launch_bounds__(kFusedBlock, fused_wgs_per_cu<TSUB>()) void newton_
   int tt = tk, t_tile = tk * 4 * TSUB, t_end = T, aseq = 0;
   unsigned long long* dsc = desc;  // the look-back words of the chain
   if constexpr (ALIGNED) {
+    // this ticket's slot of the table, all six values at once (tk < tile_cap)
     const int n_real = __builtin_amdgcn_readfirstlane(tiles[0]);
+    const int id = __builtin_amdgcn_readfirstlane(tiles[1 + tk]);
+    const int sq = __builtin_amdgcn_readfirstlane(tiles[1 + tile_cap + tk]);
+    const int ps = __builtin_amdgcn_readfirstlane(tiles[1 + 2 * tile_cap + tk]);
+    const int a0 = __builtin_amdgcn_readfirstlane(tiles[1 + 3 * tile_cap + tk]);
+    const int e0 = __builtin_amdgcn_readfirstlane(tiles[1 + 4 * tile_cap + tk]);
     if (tk >= n_real) {  // a ticket past the last tile
       if (blockIdx.x == 0 && tid == 0) ctl->iters = k_iter + 1;
       return;
     }
-    const int id = __builtin_amdgcn_readfirstlane(tiles[1 + tk]);
-    aseq = __builtin_amdgcn_readfirstlane(tiles[1 + tile_cap + id]);
-    tt = __builtin_amdgcn_readfirstlane(tiles[1 + 2 * tile_cap + id]);
-    const int a0 = min(max(cu[aseq], 0), T);
-    t_end = min(max(cu[aseq + 1], a0), T);
+    aseq = sq;
+    tt = ps;
+    t_end = e0;
     t_tile = a0 + tt * 4 * TSUB;
     dsc = desc + static_cast<i64>(id - tt) * kLookBackWords * n_lanes_pad;
   }

@@ -222,8 +222,10 @@ hipError_t launch_seq_table(const int* cu, int n_seqs, int T, int* tab, hipStrea
 // top, gives the tiles at each position and its exclusive prefix the first slot of each
 // position; each tile then takes the next slot of its position. At most cap tiles are made,
 // whatever the offsets hold (offsets are clamped into [0, T]).
-// Layout of tiles: [0] count, [1, 1 + cap) order, then cap sequence ids, cap positions, and
-// cap counters of scratch.
+// Layout of tiles: [0] count, then per slot of the hand-out order (cap each): the tile id, its
+// sequence, its position, the sequence's first step and its end (a tile reads its five values
+// in one round of independent loads); then cap each of scratch: sequence and position by id,
+// counters.
 constexpr int kTileBlock = 1024;
 
 // inclusive sum over the workgroup's threads in thread order; *total receives the sum of all
@@ -259,9 +261,13 @@ __global__ __launch_bounds__(kTileBlock) void aligned_tiles_kernel(const int* __
   __shared__ long long s_wave[kTileBlock / 64];  // 64-bit: tile counts of clamped offsets may be large
   __shared__ int s_max;
   int* order = tiles + 1;
-  int* seq = tiles + 1 + cap;
-  int* pos = tiles + 1 + 2 * cap;
-  int* cnt = tiles + 1 + 3 * cap;  // histogram, then tiles per position, then next slot per position
+  int* slot_seq = tiles + 1 + cap;
+  int* slot_pos = tiles + 1 + 2 * cap;
+  int* slot_start = tiles + 1 + 3 * cap;
+  int* slot_end = tiles + 1 + 4 * cap;
+  int* seq = tiles + 1 + 5 * cap;
+  int* pos = tiles + 1 + 6 * cap;
+  int* cnt = tiles + 1 + 7 * cap;  // histogram, then tiles per position, then next slot per position
   const int tid = threadIdx.x;
   for (int i = tid; i < cap; i += kTileBlock) cnt[i] = 0;
   if (tid == 0) s_max = 0;
@@ -314,11 +320,20 @@ __global__ __launch_bounds__(kTileBlock) void aligned_tiles_kernel(const int* __
     carry += chunk;
   }
   __syncthreads();
-  for (int id = tid; id < n; id += kTileBlock) order[atomicAdd(&cnt[pos[id]], 1)] = id;
+  for (int id = tid; id < n; id += kTileBlock) {
+    const int s = seq[id], p = pos[id];
+    const int slot = atomicAdd(&cnt[p], 1);
+    const int a = min(max(cu[s], 0), T);
+    order[slot] = id;
+    slot_seq[slot] = s;
+    slot_pos[slot] = p;
+    slot_start[slot] = a;
+    slot_end[slot] = min(max(cu[s + 1], a), T);
+  }
   if (tid == 0) tiles[0] = n;
 }
 
-size_t aligned_tile_ints(int cap) { return 1 + 4 * static_cast<size_t>(cap); }
+size_t aligned_tile_ints(int cap) { return 1 + 8 * static_cast<size_t>(cap); }
 
 hipError_t launch_aligned_tiles(const int* cu, int n_seqs, int T, int tile_steps, int cap, int* tiles,
                                 hipStream_t stream) {
