@@ -206,22 +206,28 @@ __global__ __launch_bounds__(kBackBlock, SLSTM_BACK_MIN_WAVES) void backward_cha
 #endif
 constexpr int kBackScanBlock = 256;  // 4 waves x 16 features x 4 sub-chunks
 constexpr int kBackScanTSub = SLSTM_BACK_SCAN_TSUB;
-// Packed rows on tiles aligned to the sequences (see launch_aligned_tiles): the sub-chunks are
-// longer, so that a pack's tiles (at most one more per sequence than the row's) fit the
-// look-back words and rows of sums sized for the shorter tiles. 48-step tiles with every tile
-// an anchor measured fastest on MI355X (292-sequence pack of 262,144 steps at d_h = 1024:
-// 5.18 ms against 5.26 for 40-step tiles, 5.42 with anchors every other tile, 6.56 unaligned)
+// Packed rows on tiles aligned to the sequences (see launch_aligned_tiles): one row's look-back
+// words and rows of sums are sized for tiles of kBackAlignedLayoutSteps steps, so that a pack's
+// aligned tiles (at most one more per sequence than the row's) fit them. 32-step tiles at three
+// workgroups per CU (a few registers spilled), every tile an anchor, measured fastest on MI355X
+// (292-sequence pack of 262,144 steps at d_h = 1024: 4.14 ms, against 4.65 at two workgroups per
+// CU, 5.13 with 48-step tiles at two, 5.42 with anchors every other tile, 6.56 unaligned)
 #ifndef SLSTM_BACK_ALIGNED_TSUB
-#define SLSTM_BACK_ALIGNED_TSUB 12
+#define SLSTM_BACK_ALIGNED_TSUB 8
 #endif
 constexpr int kBackAlignedTSub = SLSTM_BACK_ALIGNED_TSUB;
-static_assert(kBackAlignedTSub >= kBackScanTSub, "look-back words are sized for the shorter tiles");
+constexpr int kBackAlignedLayoutSteps = 24;
+static_assert(kBackAlignedLayoutSteps < 4 * kBackAlignedTSub, "room for one extra tile per sequence");
+static_assert(kBackAlignedLayoutSteps <= 4 * kBackScanTSub, "the row's own tiles fit the layout");
+#ifndef SLSTM_BACK_ALIGNED_MIN_WAVES
+#define SLSTM_BACK_ALIGNED_MIN_WAVES 3
+#endif
 #ifndef SLSTM_BACK_ALIGNED_ANCHOR_STRIDE
 #define SLSTM_BACK_ALIGNED_ANCHOR_STRIDE 1
 #endif
 
 template <bool BF16, int CM, bool GS, int TSUB, bool PACKED, bool ALIGNED>
-__global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void backward_scan_kernel(
+__global__ __launch_bounds__(kBackScanBlock, (ALIGNED ? SLSTM_BACK_ALIGNED_MIN_WAVES : SLSTM_BACK_SCAN_MIN_WAVES)) void backward_scan_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     const float* __restrict__ S, const float* __restrict__ g, const float* __restrict__ g_h,
     const float* __restrict__ g_final, void* __restrict__ dP, int dp_bf16, float* __restrict__ dstate0,
@@ -296,15 +302,14 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
   const unsigned long long pf = quad_look_back_prefetch(dsc, n_lanes_pad, my_lane, q, tr, anchor_stride);
 
   // packed: the sequence starting at each step of the sub-chunk and the one ending there (-1: none)
-  int sq[TSUB], lq[TSUB];
+  // (aligned: a tile holds steps of one sequence from a multiple of the tile length on, so only
+  // the first step of a sub-chunk can start it and at most one step ends it)
+  int sq[PACKED ? TSUB : 1], lq[PACKED ? TSUB : 1];
+  bool starts = false;  // aligned: the sub-chunk's first step starts the sequence
+  int eu = -1;          // aligned: the sub-chunk's step that ends the sequence
   if constexpr (ALIGNED) {
-    // a tile holds steps of one sequence: its start is the first step of the first tile
-#pragma unroll
-    for (int u = 0; u < TSUB; ++u) {
-      const int t = t_start + u;
-      sq[u] = (t < t_end && t == a_start) ? aseq : -1;
-      lq[u] = (t < t_end && t + 1 == t_end) ? aseq : -1;
-    }
+    starts = t_start == a_start && a_start < t_end;
+    if (t_end - 1 >= t_start && t_end - 1 < t_start + TSUB) eu = t_end - 1 - t_start;
   } else if constexpr (PACKED) {
     SeqCursor seq = seq_cursor(cu, n_seqs, b, t_start, seq_tab);
 #pragma unroll
@@ -315,6 +320,17 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
     }
   }
 
+  // the sequence starting / ending at step u of the sub-chunk (-1: none)
+  auto seq_start = [&](int u) -> int {
+    if constexpr (ALIGNED) return (u == 0 && starts) ? aseq : -1;
+    else if constexpr (PACKED) return sq[u];
+    else return -1;
+  };
+  auto seq_end = [&](int u) -> int {
+    if constexpr (ALIGNED) return u == eu ? aseq : -1;
+    else if constexpr (PACKED) return lq[u];
+    else return -1;
+  };
   float pg[TSUB][4], sv[TSUB][4], gs[TSUB][4];
 #pragma unroll
   for (int u = 0; u < TSUB; ++u) {
@@ -337,7 +353,7 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
         for (int k = 0; k < 4; ++k) gs[u][k] = buf_ld(rsG, 4u * o, 4u * k * ud);
       }
       if (g_h != nullptr) gs[u][3] += buf_ld(rsH, 4u * (static_cast<unsigned>(sc * TSUB + u) * ud + j), 0);
-      const int fs = (PACKED || ALIGNED) ? lq[u] : (t == T - 1 ? b : -1);  // the sequence that ends at t
+      const int fs = (PACKED || ALIGNED) ? seq_end(u) : (t == T - 1 ? b : -1);  // the sequence that ends at t
       if (g_final != nullptr && fs >= 0) {
         const float* gf = g_final + static_cast<i64>(fs) * 4 * static_cast<i64>(d);
 #pragma unroll
@@ -380,7 +396,7 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
     const int t = t_start + u;
     if (valid && t < t_end) {
       CellIn pv = (u == 0) ? pv0 : CellIn{sv[u - 1][0], sv[u - 1][1], sv[u - 1][2], sv[u - 1][3]};
-      if ((PACKED || ALIGNED) && sq[u] >= 0) pv = state0_of(state0, sq[u], ud, j);
+      if ((PACKED || ALIGNED) && seq_start(u) >= 0) pv = state0_of(state0, seq_start(u), ud, j);
       float f[4], A[16], At[16];
       cell_step<true>(pv, pg[u][0], pg[u][1], pg[u][2], pg[u][3], rz, ri, rf, ro, sig, floored, f, A);
 #pragma unroll
@@ -393,7 +409,7 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
       mat4_vec(At, w, zero, v);
       mat4_mul_left(At, M);
     }
-    if ((PACKED || ALIGNED) && sq[u] >= 0) {
+    if ((PACKED || ALIGNED) && seq_start(u) >= 0) {
       // a sequence start: nothing flows back to the step before it (padding lanes past d_h
       // too, so that all lanes of a tile agree on where the maps restart)
 #pragma unroll
@@ -430,7 +446,7 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
     const int t = t_start + u;
     if (valid && t < t_end) {
       CellIn pv = (u == 0) ? pv0 : CellIn{sv[u - 1][0], sv[u - 1][1], sv[u - 1][2], sv[u - 1][3]};
-      if ((PACKED || ALIGNED) && sq[u] >= 0) pv = state0_of(state0, sq[u], ud, j);
+      if ((PACKED || ALIGNED) && seq_start(u) >= 0) pv = state0_of(state0, seq_start(u), ud, j);
       float lam[4], dx[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) lam[e] = gs[u][e] + y[e];
@@ -442,9 +458,9 @@ __global__ __launch_bounds__(kBackScanBlock, SLSTM_BACK_SCAN_MIN_WAVES) void bac
         dr[e] = fmaf(dx[e], pv.h, dr[e]);
         db[e] += dx[e];
       }
-      if ((PACKED || ALIGNED) && sq[u] >= 0) {
+      if ((PACKED || ALIGNED) && seq_start(u) >= 0) {
         if (dstate0 != nullptr) {
-          float* ds = dstate0 + static_cast<i64>(sq[u]) * 4 * static_cast<i64>(d);
+          float* ds = dstate0 + static_cast<i64>(seq_start(u)) * 4 * static_cast<i64>(d);
 #pragma unroll
           for (int e = 0; e < 4; ++e) ds[e * ud + j] = y[e];
         }
@@ -526,6 +542,7 @@ __global__ __launch_bounds__(256) void empty_seq_dstate0_kernel(const int* __res
 // ---- sizes and launch ---------------------------------------------------------------------------
 struct BackGrid {
   i64 n_jt, n_lg, n_tt, rows;
+  i64 layout_tt;  // tiles per row the words and rows of sums hold
 };
 
 static BackGrid back_grid(int B, int T, int d, bool scan) {
@@ -540,22 +557,25 @@ static BackGrid back_grid(int B, int T, int d, bool scan) {
     g.rows = static_cast<i64>(B) * g.n_tt;
   }
   g.n_lg = static_cast<i64>(B) * g.n_jt;
+  // one row of the scan form (every packed call): room for the aligned tiles
+  g.layout_tt = (scan && B == 1) ? (T + kBackAlignedLayoutSteps - 1) / kBackAlignedLayoutSteps : g.n_tt;
   return g;
 }
 
 size_t backward_desc_words(int B, int T, int d, bool scan) {
   const BackGrid g = back_grid(B, T, d, scan);
-  return static_cast<size_t>(scan ? g.n_tt * kLookBackWords * g.n_lg * 64 : g.n_tt * kBackWords * g.n_lg * kBackBlock);
+  return static_cast<size_t>(scan ? g.layout_tt * kLookBackWords * g.n_lg * 64 : g.n_tt * kBackWords * g.n_lg * kBackBlock);
 }
 
 int backward_aligned_steps() { return 4 * kBackAlignedTSub; }
-int backward_aligned_cap(int T) { return static_cast<int>(back_grid(1, T, 1, true).n_tt); }
+int backward_aligned_cap(int T) { return static_cast<int>(back_grid(1, T, 1, true).layout_tt); }
 
 size_t backward_row_floats(int B, int T, int d, bool scan) {
   const BackGrid g = back_grid(B, T, d, scan);
-  const i64 chunk = row_chunk(g.rows);
-  const i64 chunks = (g.rows + chunk - 1) / chunk;
-  return static_cast<size_t>((g.rows + chunks) * 8 * static_cast<i64>(d));
+  const i64 rows = static_cast<i64>(B) * g.layout_tt;  // at least g.rows
+  const i64 chunk = row_chunk(rows);
+  const i64 chunks = (rows + chunk - 1) / chunk;
+  return static_cast<size_t>((rows + chunks) * 8 * static_cast<i64>(d));
 }
 
 hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const float* state0,
@@ -566,10 +586,15 @@ hipError_t launch_backward(const void* P, bool p_bf16, const float* R, const flo
                            hipStream_t stream, Seqs seqs) {
   const bool packed = seqs.cu != nullptr;
   if (packed && (!scan || B != 1)) return hipErrorInvalidValue;  // packed: the scan form, one row
-  const BackGrid gr = back_grid(B, T, d, scan);
+  BackGrid gr = back_grid(B, T, d, scan);
   const bool aligned = packed && seqs.tiles != nullptr;
-  // aligned: one ticket per slot of the tile table (the rows and words hold that many tiles)
-  if (aligned && seqs.tile_cap != gr.n_tt) return hipErrorInvalidValue;
+  // aligned: one ticket, and one row of sums, per slot of the tile table (the rows and words
+  // hold that many tiles)
+  if (aligned) {
+    if (seqs.tile_cap != gr.layout_tt) return hipErrorInvalidValue;
+    gr.n_tt = gr.layout_tt;
+    gr.rows = gr.layout_tt;
+  }
   const i64 blocks = gr.n_lg * gr.n_tt;
   const i64 chunk = row_chunk(gr.rows);
   const i64 chunks = (gr.rows + chunk - 1) / chunk;

@@ -27,9 +27,9 @@ LAYOUTS = {
     # lengths at and around the 32-step tiles of the scan form's aligned tiles (which serve packs
     # of at most about T / 32 sequences: this one, "mixed" and "single")
     "tile_edges": [32, 0, 33, 31, 1, 64, 0, 96, 2, 65, 127, 1, 300],
-    # lengths at and around multiples of 96 steps, i.e. of the backward's 48-step aligned tiles
-    # (which serve packs of at most about T / 96 sequences: this one, "single" and the
-    # full-size pack) and of the iteration's 32-step ones
+    # lengths at and around multiples of 96 steps, and so of the 32-step aligned tiles of both the
+    # iteration and the backward (the backward's serve packs of at most about T / 96 sequences:
+    # this one, "single" and the full-size pack)
     "wide_tile_edges": [96, 0, 97, 95, 1, 192, 0, 288, 2, 193, 383, 1, 4000],
 }
 
@@ -223,9 +223,10 @@ def test_packed_backward_aligned_reproducible(gpu_lib):
         assert torch.equal(x, y)
 
 
-def test_packed_backward_bf16_dp(gpu_lib):
-    P, R, s0, cu = _problem(860, MIXED, 70, "exp")
-    case("packed backward, bf16 dP")
+@pytest.mark.parametrize("layout", ["mixed", "wide_tile_edges"])  # along the row; on aligned tiles
+def test_packed_backward_bf16_dp(gpu_lib, layout):
+    P, R, s0, cu = _problem(860, LAYOUTS[layout], 70, "exp")
+    case(f"packed backward, bf16 dP, {layout}")
     errs, _, _, _ = _backward_case(gpu_lib, P, R, s0, cu, "exp", "fused", 861, dP_dtype=torch.bfloat16)
     assert errs[0] < 1e-2            # dP rounded to bfloat16
     assert max(errs[1:]) < GRAD_TOL  # dR, dbias and dstate0 from the float32 values
