@@ -75,11 +75,12 @@ def solve_flops_per_elem(K, sigmoid_forget):
     return warm + K * (cell + lin + 8 + 22 + 4) + (cell + 8)
 
 
-def kernel_work(w, n_e, p_bytes):
+def kernel_work(w, n_e, p_bytes, states_out=True):
     """Algorithmic work per launch of each kernel kind. Bytes: every operand of every state
     element read once and every result written once (per element: P p_bytes, a state 16, a
     right-hand side / Newton step 16, the Jacobian JAC_BYTES, h 4). The one-kernel solve is
-    reported against HBM on its bytes (P in; S_K and h out), with its flop count of
+    reported against HBM on its bytes (P in; S_K, if the caller asks for the states, and h out;
+    the final state's B·4·d_h floats are negligible), with its flop count of
     solve_flops_per_elem and its vector-issue share beside it."""
     return {
         "warm_start": {"bound": "hbm", "bytes": n_e * (p_bytes + 16)},                        # P in, S out
@@ -88,7 +89,7 @@ def kernel_work(w, n_e, p_bytes):
         "update": {"bound": "hbm", "bytes": n_e * 48},                                        # S, Delta in; S out
         "final_residual": {"bound": "hbm", "bytes": n_e * (p_bytes + 16)},                    # P, S in
         "newton_iteration": {"bound": "hbm", "bytes": n_e * (p_bytes + 16 + 16)},             # P, S_k in; S_k+1 out
-        "newton_solve": {"bound": "hbm", "bytes": n_e * (p_bytes + 16 + 4),                   # P in; S_K, h out
+        "newton_solve": {"bound": "hbm", "bytes": n_e * (p_bytes + (16 if states_out else 0) + 4),  # P in; (S_K,) h out
                          "flops": n_e * solve_flops_per_elem(w.max_iters, w.forget == "sigmoid")},
         "backward": {"bound": "hbm", "bytes": n_e * (p_bytes + 16 + 4 + 8)},                  # P, S, dL/dh in; bf16 dP out
     }
@@ -408,13 +409,17 @@ def solver_context(slstm, torch, dev, name, steps, cpu_lanes, no_cpu):
     log(f"[bench] context {name}: inputs ready in {time.perf_counter() - t_gen:.1f} s")
     p_bytes = 8 if w.p_dtype == "bf16" else 16
     n_e = w.state_elems
-    S = torch.empty((w.B, w.T, 4, w.d_h), dtype=torch.float32, device=dev)
+    # the library runs a fixed-count solve on 32 or more lane groups of 256 features as one
+    # kernel, which needs no state tensor: the layer's default output, h and the final state
+    one_kernel = w.tol == 0.0 and w.max_iters <= 4 and w.B * -(-w.d_h // 256) >= 32
+    S = None if one_kernel else torch.empty((w.B, w.T, 4, w.d_h), dtype=torch.float32, device=dev)
     H = torch.empty((w.B, w.T, w.d_h), dtype=torch.float32, device=dev)
+    FS = torch.empty((w.B, 4, w.d_h), dtype=torch.float32, device=dev)
     ws = slstm.alloc_workspace(slstm.newton_workspace_bytes(w.B, w.T, w.d_h, "fused"), dev)
 
     def solve():
-        slstm.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, "warm", states=S, h_out=H, workspace=ws,
-                             stats=False, schedule="fused")
+        slstm.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, "warm", states=S, h_out=H, final_state=FS,
+                             workspace=ws, stats=False, schedule="fused", output_states=not one_kernel)
 
     solve()
     torch.cuda.synchronize()
@@ -432,7 +437,8 @@ def solver_context(slstm, torch, dev, name, steps, cpu_lanes, no_cpu):
     torch.cuda.synchronize()
     slstm.profile_enable(False)
     bytes_of = {"warm_start": n_e * (p_bytes + 16), "newton_iteration": n_e * (p_bytes + 32),
-                "final_residual": n_e * (p_bytes + 16 + 4), "newton_solve": n_e * (p_bytes + 16 + 4)}
+                "final_residual": n_e * (p_bytes + 16 + 4),
+                "newton_solve": n_e * (p_bytes + (0 if one_kernel else 16) + 4)}
     kernels = {}
     for kind, nb in bytes_of.items():
         d = slstm.profile_durations(kind)
@@ -444,7 +450,9 @@ def solver_context(slstm, torch, dev, name, steps, cpu_lanes, no_cpu):
     log(f"[bench] context {name}: solve {ms:.3f} ms ({n_e / (ms * 1e-3):.3e} state-elems/s), iters {st.iters}, "
         f"converged {st.converged}, iteration kernel {it['avg_ms'] if it else float('nan'):.3f} ms")
     out = {"B": w.B, "T": w.T, "d_h": w.d_h, "preactivations": w.p_dtype, "forget_gate": w.forget,
-           "max_iters": w.max_iters, "tol": w.tol, "schedule": "fused (scan form at this shape)",
+           "max_iters": w.max_iters, "tol": w.tol,
+           "schedule": "fused (one-kernel form at this shape)" if one_kernel else "fused (scan form at this shape)",
+           "outputs": "hidden slot and final state" if one_kernel else "states, hidden slot",
            "solve_ms": round(ms, 4), "state_elems_per_s": n_e / (ms * 1e-3),
            "solver": {"iters": st.iters, "converged": st.converged, "diverged": st.diverged,
                       "max_abs_F": st.max_abs_F},
@@ -453,7 +461,15 @@ def solver_context(slstm, torch, dev, name, steps, cpu_lanes, no_cpu):
         out["roofline"] = {"bound": "hbm", "kernel": "newton_iteration", "achieved": it["GB_s"],
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(it["GB_s"] / HBM_PEAK_GBS, 4),
                            "traffic": measured_traffic("newton_iteration", w.name)}
-    del ws, S, H, P, R
+    sv = kernels.get("newton_solve")
+    if sv:
+        # few lane groups: the wavefront along T waits on each tile's predecessor in turn
+        n_tt = -(-w.T // 14)
+        out["roofline"] = {"bound": "latency", "kernel": "newton_solve", "achieved": sv["GB_s"],
+                           "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(sv["GB_s"] / HBM_PEAK_GBS, 4),
+                           "tiles_along_T": n_tt, "us_per_tile": round(sv["avg_ms"] * 1e3 / n_tt, 3),
+                           "traffic": measured_traffic("newton_solve", w.name)}
+    del ws, S, H, FS, P, R
     torch.cuda.empty_cache()
     if not no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, {"P": host["P"], "R": host["R"]}, cpu_lanes)
@@ -475,6 +491,10 @@ def main():
                     help="first run a plain device copy of 4 GiB (counter calibration runs)")
     ap.add_argument("--no-sequential-context", action="store_true")
     ap.add_argument("--schedule", default="fused", choices=["fused", "fused_scan", "fused_chain", "layered"])
+    ap.add_argument("--outputs", default="hidden", choices=["hidden", "states"],
+                    help="what the timed forward writes: the layer's default output, the hidden slot and "
+                         "the final state (where the solve is the one-kernel form; other forms also write "
+                         "the states they iterate on), or the full states beside them")
     ap.add_argument("--no-layered-context", action="store_true",
                     help="skip the context runs of the scan form and the layered schedule")
     ap.add_argument("--no-backward-context", action="store_true",
@@ -537,15 +557,26 @@ def main():
 
     n_e = w.state_elems
     work = kernel_work(w, n_e, p_bytes)
+    n_cus = torch.cuda.get_device_properties(dev).multi_processor_count
 
-    def timed_run(schedule, steps, warmup):
+    def one_kernel_form(schedule):
+        """Whether the solve resolves to the one-kernel form, which needs no state tensor."""
+        if w.tol != 0.0 or w.max_iters > 4:
+            return False
+        return schedule == "fused_chain" or (schedule == "fused" and w.B * -(-w.d_h // 256) >= n_cus)
+
+    def timed_run(schedule, steps, warmup, states_out=None):
+        if states_out is None:
+            states_out = args.outputs == "states" or not one_kernel_form(schedule)
+        run_work = kernel_work(w, n_e, p_bytes, states_out)
         ws = slstm.alloc_workspace(slstm.newton_workspace_bytes(w.B, w.T, w.d_h, schedule), dev)
 
         def step():
             if w.on_gpu_gemm:
                 slstm.input_projection(x, W, bias, out=P)
-            slstm.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, "warm", states=S, h_out=H,
-                                 final_state=FS, workspace=ws, stats=False, schedule=schedule)
+            slstm.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, "warm", states=S if states_out else None,
+                                 h_out=H, final_state=FS, workspace=ws, stats=False, schedule=schedule,
+                                 output_states=states_out)
             if w.on_gpu_gemm:
                 slstm.input_projection(x_dec, W, bias, out=P_dec)
                 slstm.sequential_forward(P_dec, R, FS, w.forget, states=S_dec, h_out=H_dec)
@@ -583,8 +614,8 @@ def main():
         step_ms = sorted(a.elapsed_time(b) for a, b in evs)
         spread = {"median_ms": round(step_ms[len(step_ms) // 2], 4), "min_ms": round(step_ms[0], 4),
                   "max_ms": round(step_ms[-1], 4), "steps": steps, "timing": "HIP events per step, second pass"}
-        kernels = {}
-        for kind, wk in work.items():
+        kernels = {"_work": run_work, "_states_out": states_out}
+        for kind, wk in run_work.items():
             d = slstm.profile_durations(kind)
             if not d:
                 continue
@@ -615,6 +646,7 @@ def main():
         return ms, kernels, st
 
     def roofline_of(kernels, steps, ms):
+        work = kernels["_work"]
         dominant = max((k for k in kernels if (k in work or k == "input_projection") and not k.startswith("_")),
                        key=lambda k: kernels[k]["total_ms_per_step"])
         k = kernels[dominant]
@@ -627,11 +659,17 @@ def main():
             if copy_gbs:
                 roof["copy_ceiling"] = {"achieved": round(copy_gbs, 1), "unit": "GB/s",
                                         "frac_of_copy": round(k["GB_s"] / copy_gbs, 4)}
-            if "flops" in k:
+            if "TFLOP_s" in k:
                 # the kernel's arithmetic beside its bytes: flops against the ceiling of the build
-                # (no packed fp32), and the share of vector issue its instructions fill
-                roof["alu_view"] = {"achieved": round(k["TFLOP_s"], 2), "peak": FP32_UNPACKED_PEAK_TFLOPS,
-                                    "unit": "TFLOP/s", "frac": round(k["TFLOP_s"] / FP32_UNPACKED_PEAK_TFLOPS, 4)}
+                # (no packed fp32), and the share of vector issue its instructions fill; the roof
+                # nearer to its peak is the bound, the other its view
+                alu = {"achieved": round(k["TFLOP_s"], 2), "peak": FP32_UNPACKED_PEAK_TFLOPS,
+                       "unit": "TFLOP/s", "frac": round(k["TFLOP_s"] / FP32_UNPACKED_PEAK_TFLOPS, 4)}
+                if alu["frac"] > roof["frac"]:
+                    hbm_view = {kk: roof[kk] for kk in ("achieved", "peak", "unit", "frac", "copy_ceiling") if kk in roof}
+                    roof = {"bound": "alu", "kernel": dominant, **alu, "hbm_view": hbm_view}
+                else:
+                    roof["alu_view"] = alu
             insts = measured_valu(dominant, w.name)
             if insts:
                 roof["valu_issue"] = {"valu_insts_per_launch": insts,
@@ -671,6 +709,14 @@ def main():
                "step_time": kernels["_spread"], "copy_GB_s": round(copy_gbs, 1) if copy_gbs else None,
                "kernels": rounded(kernels),
                "solver": {"iters": st.iters, "max_abs_F": st.max_abs_F, "diverged": st.diverged}}
+    if not kernels["_states_out"]:
+        # the same step writing the full states beside the hidden slot (output_hidden=False on
+        # the pages' layer)
+        fsteps = max(2, args.steps // 2)
+        fms, fkernels, _ = timed_run(args.schedule, fsteps, 1, states_out=True)
+        froof, _ = roofline_of(fkernels, fsteps, fms)
+        context["full_states"] = {"ms_per_step": round(fms, 4), "state_elems_per_s": n_e / (fms * 1e-3),
+                                  "roofline": froof, "kernels": rounded(fkernels)}
     if w.on_gpu_gemm:
         gk = kernels["input_projection"]
         context["gemm"] = {"TFLOP_s": round(gk["TFLOP_s"], 1), "peak": BF16_PEAK_TFLOPS,
@@ -715,6 +761,12 @@ def main():
             dx = torch.empty((w.B, w.T, w.d_in), dtype=torch.float32, device=dev)
             dW = torch.empty((4, w.d_h, w.d_in), dtype=torch.float32, device=dev)
             pws = slstm.alloc_workspace(slstm.input_projection_backward_workspace_bytes(w.B, w.T, w.d_in, w.d_h), dev)
+
+        # the states of the forward solution, which the backward reads
+        if w.on_gpu_gemm:
+            slstm.input_projection(x, W, bias, out=P)
+        slstm.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, "warm", states=S, h_out=H,
+                             final_state=FS, stats=False)
 
         def bwd():
             slstm.backward(P, R, S, None, None, g_h, g_fin, w.forget, dP=dP, dR=dR, dstate0=d0, dbias=db,
@@ -872,7 +924,9 @@ def main():
     config = {"workload": w.name, "B": w.B, "T": w.T, "d_in": w.d_in, "d_h": w.d_h,
               "newton_iters": w.max_iters, "tol": w.tol, "forget_gate": w.forget,
               "preactivations": ("bf16 x, W_x -> float32 P on MFMA" if w.on_gpu_gemm else w.p_dtype),
-              "decode_batch": w.decode_batch, "init": "warm", "state_dtype": "f32"}
+              "decode_batch": w.decode_batch, "init": "warm", "state_dtype": "f32",
+              "outputs": ("states (B,T,4,d_h), hidden slot (B,T,d_h), final state" if kernels["_states_out"]
+                          else "hidden slot (B,T,d_h) and final state (the layer's default output)")}
     line = {"metric": METRIC, "value": value, "unit": "state-elems/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",

@@ -132,14 +132,26 @@ bool known_schedule(slstm_schedule s) {
          s == SLSTM_SCHEDULE_FUSED_CHAIN;
 }
 
-Form newton_form(int B, int d, slstm_schedule s) {
+// Lane groups from which FUSED runs a fixed-count solve (tol = 0, max_iters <= 4) as the
+// one-kernel form even when they do not cover every compute unit: its wavefront along T then
+// waits on each tile's predecessor (a few microseconds a tile), yet reads P once where the scan
+// form makes K + 2 passes over HBM. Measured on MI355X (K = 3 and 4): 32 lane groups at
+// T = 16384 (B = 4, d_h = 2048) 4.2 ms against 9.3 ms; 64 at T = 2048 (B = 16, d_h = 1024)
+// 0.73 ms against 1.95 ms.
+constexpr long long kOneKernelMinLaneGroups = 32;
+
+// one_kernel_ok: the call is a fixed-count, unpacked solve that the one-kernel form can run
+Form newton_form(int B, int d, slstm_schedule s, bool one_kernel_ok = false) {
   switch (s) {
     case SLSTM_SCHEDULE_LAYERED: return Form::kLayered;
     case SLSTM_SCHEDULE_FUSED_SCAN: return Form::kScan;
     case SLSTM_SCHEDULE_FUSED_CHAIN: return Form::kChain;
-    default:
+    default: {
       // chains along T cost no waiting once the lane groups cover every compute unit
-      return slstm::chain_lane_groups(B, d) >= device_cus() ? Form::kChain : Form::kScan;
+      const long long lg = slstm::chain_lane_groups(B, d);
+      if (lg >= device_cus()) return Form::kChain;
+      return one_kernel_ok && lg >= kOneKernelMinLaneGroups ? Form::kChain : Form::kScan;
+    }
   }
 }
 
@@ -239,10 +251,10 @@ int cell_mode_of(slstm_forget f) {
 
 slstm_status check_common(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
                           const float* states, const float* h_out, const float* final_state, int B,
-                          int T, int d, slstm_forget fmode) {
+                          int T, int d, slstm_forget fmode, bool states_required = true) {
   slstm_status s = check_dims(B, T, d);
   if (s != SLSTM_OK) return s;
-  if (P == nullptr || R == nullptr || states == nullptr)
+  if (P == nullptr || R == nullptr || (states_required && states == nullptr))
     return fail(SLSTM_EINVAL, "P, R and states must not be NULL");
   if (P_dtype != SLSTM_F32 && P_dtype != SLSTM_BF16) return fail(SLSTM_EINVAL, "unknown P dtype %d", (int)P_dtype);
   if (!known_cell_mode(fmode)) return fail(SLSTM_EINVAL, "unknown forget mode %d", (int)fmode);
@@ -484,7 +496,7 @@ slstm_status newton_forward(const void* P, slstm_dtype P_dtype, const float* R, 
                             slstm_forget fmode, int max_iters, float tol, slstm_init init,
                             slstm_schedule schedule, void* workspace, size_t workspace_bytes,
                             void* stream, slstm_newton_stats* stats, slstm::Seqs seqs) {
-  slstm_status s = check_common(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, fmode);
+  slstm_status s = check_common(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, fmode, false);
   if (s != SLSTM_OK) return s;
   if (max_iters < 1 || max_iters > SLSTM_MAX_ITERS)
     return fail(SLSTM_EINVAL, "max_iters must be in 1..%d (got %d)", SLSTM_MAX_ITERS, max_iters);
@@ -495,7 +507,15 @@ slstm_status newton_forward(const void* P, slstm_dtype P_dtype, const float* R, 
     return fail(SLSTM_EINVAL, "workspace must be non-NULL and 256-byte aligned");
   if (seqs.cu != nullptr && schedule == SLSTM_SCHEDULE_FUSED_CHAIN)
     return fail(SLSTM_EINVAL, "packed sequences run the scan and layered forms only (not FUSED_CHAIN)");
-  const Form form = seqs.cu != nullptr && schedule == SLSTM_SCHEDULE_FUSED ? Form::kScan : newton_form(B, d_h, schedule);
+  const bool one_kernel_ok = seqs.cu == nullptr && tol == 0.0f && max_iters <= slstm::kPipeMaxIters;
+  const Form form = seqs.cu != nullptr && schedule == SLSTM_SCHEDULE_FUSED ? Form::kScan
+                                                                          : newton_form(B, d_h, schedule, one_kernel_ok);
+  const bool one_kernel = seqs.cu == nullptr && pipe_solve(form, max_iters, tol);
+  // only the one-kernel solve keeps its iterate on chip; every other form keeps it in `states`
+  if (states == nullptr && !one_kernel)
+    return fail(SLSTM_EINVAL, "states may be NULL only for a fixed-count solve (tol = 0, max_iters <= %d) "
+                "that resolves to the one-kernel form (FUSED_CHAIN, or FUSED on enough lanes), unpacked",
+                slstm::kPipeMaxIters);
   const NewtonLayout L = newton_layout(B, T, d_h, form);
   if (workspace_bytes < L.total)
     return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
@@ -521,20 +541,22 @@ slstm_status newton_forward(const void* P, slstm_dtype P_dtype, const float* R, 
     }
   }
   unsigned int* tickets = slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0];
-  if (seqs.cu == nullptr && pipe_solve(form, max_iters, tol)) {
-    // the whole fixed-count solve in one pass; it writes the final states, h and every residual
+  if (one_kernel) {
+    // the whole fixed-count solve in one pass; it writes the states (if asked for), h, the
+    // final state and every residual
     const uint32_t ep = next_epoch();
     HIP_TRY(timed(SLSTM_KERNEL_NEWTON_SOLVE, st, [&] {
-      return slstm::launch_newton_pipe(P, bf16, R, state0, states, h_out, B, T, d_h, cm,
+      return slstm::launch_newton_pipe(P, bf16, R, state0, states, h_out, final_state, B, T, d_h, cm,
                                        init == SLSTM_INIT_WARM, max_iters, desc, tickets, ep, ctl, st);
     }));
+    HIP_TRY(slstm::launch_finalize(ctl, tol, st));
   } else {
     HIP_TRY(iterate(P, bf16, R, state0, states, h_out, B, T, d_h, cm, max_iters, tol, init, form, L,
                     workspace, ctl, tickets, st, seqs));
+    HIP_TRY(slstm::launch_finalize(ctl, tol, st));
+    if (h_out != nullptr || final_state != nullptr)
+      HIP_TRY(slstm::launch_outputs(states, h_out, final_state, B, T, d_h, ctl, st, state0, seqs));
   }
-  HIP_TRY(slstm::launch_finalize(ctl, tol, st));
-  if (h_out != nullptr || final_state != nullptr)
-    HIP_TRY(slstm::launch_outputs(states, h_out, final_state, B, T, d_h, ctl, st, state0, seqs));
   if (stats == nullptr) return SLSTM_OK;
   Control host;
   HIP_TRY(hipMemcpyAsync(&host, ctl, sizeof(Control), hipMemcpyDeviceToHost, st));
@@ -710,7 +732,9 @@ const char* slstm_last_error(void) { return g_err; }
 size_t slstm_newton_workspace_bytes(int B, int T, int d_h, slstm_schedule schedule) {
   if (check_dims(B, T, d_h) != SLSTM_OK) return 0;
   if (!known_schedule(schedule)) return 0;
-  return newton_layout(B, T, d_h, newton_form(B, d_h, schedule)).total;
+  // FUSED may resolve differently for fixed-count solves: room for either form
+  return std::max(newton_layout(B, T, d_h, newton_form(B, d_h, schedule, false)).total,
+                  newton_layout(B, T, d_h, newton_form(B, d_h, schedule, true)).total);
 }
 
 slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const float* R,

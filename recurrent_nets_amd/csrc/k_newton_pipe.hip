@@ -10,8 +10,9 @@
 // tile needs the tile's own iterate S_k, which is in its registers, and the Newton step
 // entering the tile, which tile tt-1 publishes as soon as its iteration k is done. So a tile
 // runs all K iterations on registers: tile tt works on iteration k while tile tt-1 is already on
-// iteration k+1, a wavefront along T. P is read once and only S_K (and h) is written: 36 bytes
-// per state element for the whole solve instead of 32 + 48 K + 20 for per-iteration passes.
+// iteration k+1, a wavefront along T. P is read once and only S_K (when the caller wants the
+// states), h and the final state are written: 36 bytes per state element for the whole solve
+// (20 with the hidden slot alone) instead of 32 + 48 K + 20 for per-iteration passes.
 //
 // Published per lane and tile, as epoch-tagged words (see tag_store): the initial iterate at
 // the tile's last step (c, n, m, h), and the Newton step of each iteration at the last step.
@@ -44,7 +45,8 @@ __host__ __device__ constexpr int pipe_words(int K) { return 4 + 4 * K; }
 template <bool BF16, bool WARM, int CM>
 __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_kernel(
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
-    float* __restrict__ S_out, float* __restrict__ h_out, int T, int d, int n_jt, int n_lg,
+    float* __restrict__ S_out, float* __restrict__ h_out, float* __restrict__ fs_out, int T, int d,
+    int n_jt, int n_lg,
     int n_tt, int K, unsigned long long* __restrict__ carry,
     unsigned int* __restrict__ tickets, int n_ctr, uint32_t epoch, Control* __restrict__ ctl) {
   constexpr int TC = kPipeSteps;
@@ -208,11 +210,12 @@ __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_
     if (l == 0) __hip_atomic_fetch_max(&s_err[k], wm, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 
-  // ---- residual of S_K, and the outputs ----
+  // ---- residual of S_K, and the outputs: the states (when asked for), h, the final state ----
   ResMax2 fmax;
   if (valid) {
-    const rsrc_t rsO = make_rsrc(S_out + tile_row);
-    const rsrc_t rsH = make_rsrc(h_out != nullptr ? h_out + (static_cast<i64>(b) * T + t0) * static_cast<i64>(d) : S_out);
+    // a descriptor over a null base is never used: each store below tests its own pointer
+    const rsrc_t rsO = make_rsrc(S_out != nullptr ? S_out + tile_row : nullptr);
+    const rsrc_t rsH = make_rsrc(h_out != nullptr ? h_out + (static_cast<i64>(b) * T + t0) * static_cast<i64>(d) : nullptr);
     CellIn pv = {hv[0], hv[1], hv[2], hv[3]};
 #pragma unroll
     for (int u = 0; u < TC; ++u) {
@@ -221,9 +224,16 @@ __global__ __launch_bounds__(kPipeBlock, SLSTM_PIPE_MIN_WAVES) void newton_pipe_
         cell_step<false>(pv, p[u][0], p[u][1], p[u][2], p[u][3], rz, ri, rf, ro, sig, floored, f, nullptr);
         res_max2(fmax, s[u][0] - f[0], s[u][1] - f[1]);
         res_max2(fmax, s[u][2] - f[2], s[u][3] - f[3]);
+        if (S_out != nullptr) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) buf_st(s[u][e], rsO, 4u * j, 4u * (4u * u + e) * ud);
+          for (int e = 0; e < 4; ++e) buf_st(s[u][e], rsO, 4u * j, 4u * (4u * u + e) * ud);
+        }
         if (h_out != nullptr) buf_st(s[u][3], rsH, 4u * j, 4u * u * ud);
+        if (fs_out != nullptr && t0 + u == T - 1) {
+          float* fs = fs_out + static_cast<i64>(b) * 4 * static_cast<i64>(d) + j;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) fs[e * ud] = s[u][e];
+        }
         pv = {s[u][0], s[u][1], s[u][2], s[u][3]};
       }
     }
@@ -248,7 +258,7 @@ size_t pipe_desc_words(int B, int T, int d, int K) {
 }
 
 hipError_t launch_newton_pipe(const void* P, bool p_bf16, const float* R, const float* state0,
-                              float* S_out, float* h_out, int B, int T, int d, int cell_mode,
+                              float* S_out, float* h_out, float* fs_out, int B, int T, int d, int cell_mode,
                               bool warm, int K, unsigned long long* carry, unsigned int* tickets,
                               uint32_t epoch, Control* ctl, hipStream_t stream) {
   i64 n_jt, n_lg, n_tt;
@@ -259,7 +269,7 @@ hipError_t launch_newton_pipe(const void* P, bool p_bf16, const float* R, const 
   const dim3 grid(static_cast<unsigned>(blocks));
   const int a = static_cast<int>(n_jt), c = static_cast<int>(n_lg), e = static_cast<int>(n_tt);
 #define SLSTM_PIPE_LAUNCH(BF, WM, CM_)                                                                   \
-  newton_pipe_kernel<BF, WM, CM_><<<grid, kPipeBlock, 0, stream>>>(P, R, state0, S_out, h_out, T, d, a, \
+  newton_pipe_kernel<BF, WM, CM_><<<grid, kPipeBlock, 0, stream>>>(P, R, state0, S_out, h_out, fs_out, T, d, a, \
                                                                    c, e, K, carry, tickets, n_ctr,      \
                                                                    epoch, ctl)
 #define SLSTM_PIPE_TT(CM_) SLSTM_PIPE_LAUNCH(true, true, CM_)

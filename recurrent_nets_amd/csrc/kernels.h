@@ -44,7 +44,7 @@ hipError_t launch_newton_chain(const void* P, bool p_bf16, const float* R, const
 constexpr int kPipeMaxIters = 4;
 size_t pipe_desc_words(int B, int T, int d, int K);
 hipError_t launch_newton_pipe(const void* P, bool p_bf16, const float* R, const float* state0,
-                              float* S_out, float* h_out, int B, int T, int d, int cell_mode,
+                              float* S_out, float* h_out, float* fs_out, int B, int T, int d, int cell_mode,
                               bool warm, int K, unsigned long long* carry, unsigned int* tickets,
                               uint32_t epoch, Control* ctl, hipStream_t stream);
 // after the last chain iteration: declares iterate k final when its residual met tol

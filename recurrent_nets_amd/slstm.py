@@ -260,12 +260,15 @@ def alloc_workspace(nbytes: int, device=None) -> torch.Tensor:
 def newton_forward(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, init="warm",
                    states=None, h_out=None, want_hidden=True, final_state=None, workspace=None,
                    stream=None, stats=True, raise_on_divergence=True, schedule="fused",
-                   readout="exact", cu_seqlens=None):
+                   readout="exact", cu_seqlens=None, output_states=True):
     """Newton-parallel forward. Returns (states (B,T,4,d_h), h (B,T,d_h) or None, NewtonStats
-    or None). With stats=False the call is asynchronous and returns no stats. A given
+    or None). ``output_states=False`` asks for the hidden slot and the final state only (the
+    pages' default layer output): states is then None and the library writes no state tensor,
+    which it allows where the solve resolves to the one-kernel form (tol = 0, max_iters <= 4,
+    unpacked; "fused_chain", or "fused" on enough lanes). With stats=False the call is asynchronous and returns no stats. A given
     ``final_state`` (B,4,d_h) tensor receives the last step's state. ``schedule`` is "fused"
-    (one kernel per iteration; "fused_chain" when the lane groups cover the GPU, else
-    "fused_scan"), "fused_scan", "fused_chain" or "layered" (residual + Jacobian, scan,
+    ("fused_chain" when the lane groups cover the GPU, or number at least 32 for a fixed-count
+    solve that runs as one kernel, else "fused_scan"), "fused_scan", "fused_chain" or "layered" (residual + Jacobian, scan,
     update). ``readout`` is "exact" (h = o c / n) or "floored" (h = o c / max(|n|, e^{-m},
     1e-6)); every function taking ``forget`` takes it too.
 
@@ -278,7 +281,7 @@ def newton_forward(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, init="
     _dev(state0, "state0", (torch.float32,))
     cu, S = _seqs(cu_seqlens, P)
     B, T, d = _shape_check(P, R, state0, S)
-    if states is None:
+    if states is None and output_states:
         states = torch.empty((B, T, 4, d), dtype=torch.float32, device=P.device)
     if want_hidden and h_out is None:
         h_out = torch.empty((B, T, d), dtype=torch.float32, device=P.device)

@@ -103,6 +103,15 @@ def test_argument_checks_return_einval(lib):
     assert "256-byte" in lib.slstm_last_error().decode()
     assert _fwd(lib, wsb=100) == slstm.EWORKSPACE
     assert "needed" in lib.slstm_last_error().decode()
+    # no state tensor: only where the solve is the one-kernel form, which keeps its iterate on
+    # chip (fixed count, tol = 0, max_iters <= 4, unpacked)
+    assert _fwd(lib, S=None, sched=1) == slstm.EINVAL            # layered
+    assert "one-kernel" in lib.slstm_last_error().decode()
+    assert _fwd(lib, S=None, sched=2) == slstm.EINVAL            # scan form
+    assert _fwd(lib, S=None, sched=0) == slstm.EINVAL            # fused on 2 lane groups: scan form
+    assert _fwd(lib, S=None, sched=3, tol=1e-5) == slstm.EINVAL  # early stop: per-iteration kernels
+    assert _fwd(lib, S=None, sched=3, K=5) == slstm.EINVAL
+    assert _fwd(lib, S=None, sched=3, wsb=100) == slstm.EWORKSPACE  # accepted, then sized
     s = lib.slstm_input_projection(ctypes.c_void_p(256), ctypes.c_void_p(256), None,
                                    ctypes.c_void_p(256), 2, 3, 12, 4, 1, None)
     assert s == slstm.EINVAL and "multiple of 8" in lib.slstm_last_error().decode()

@@ -262,3 +262,53 @@ def test_one_kernel_solve_matches_iteration_kernels(gpu_lib, init):
             assert torch.equal(nan, torch.isnan(b))
             assert torch.equal(a[~nan], b[~nan])
         assert np.array_equal(np.array(sta.max_abs_F), np.array(stb.max_abs_F), equal_nan=True)
+
+
+@pytest.mark.parametrize("name,readout", [("mid_b8_t1024_d256", "exact"), ("sigmoid_bf16p_b16_t4096_d1024", "exact"),
+                                          ("mid_b8_t1024_d256", "floored")])
+def test_hidden_only_output(gpu_lib, name, readout):
+    """The layer's default output, the hidden slot and the final state without the state tensor
+    ("sLSTM in this library", "Outputs"): the one-kernel solve writes h and the final state
+    itself. Both equal, bit for bit, what the same solve writes beside the states, and match the
+    oracle (ragged T and d; a random initial state on the float32 workload, none on the
+    sigmoid/bf16 one; warm and zero guesses; K = 4 at its limit)."""
+    w = by_name(name)
+    forget = w.forget
+    p_dtype = w.p_dtype
+    inp = draw_preactivation_inputs(w, B=3, T=999)
+    P = inp["P"][..., :200].contiguous()
+    R = inp["R"][:, :200].contiguous()
+    s0 = (torch.from_numpy(random_states(w.seed + 11, 3, 1, 200)[:, 0].astype(np.float32))
+          if p_dtype == "f32" else None)
+    dev = lambda t: None if t is None else t.to(DEV)  # noqa: E731
+    for init, K in (("warm", 3), ("warm", 4), ("zero", 2)):
+        case(f"hidden-only output {p_dtype}/{forget}/{readout}, init={init}, K={K}")
+        fs_a = torch.empty(3, 4, 200, device=DEV)
+        fs_b = torch.full((3, 4, 200), float("nan"), device=DEV)
+        Sa, ha, sta = gpu_lib.newton_forward(P.to(DEV), R.to(DEV), dev(s0), forget, K, 0.0, init,
+                                             final_state=fs_a, raise_on_divergence=False,
+                                             schedule="fused_chain", readout=readout)
+        Sb, hb, stb = gpu_lib.newton_forward(P.to(DEV), R.to(DEV), dev(s0), forget, K, 0.0, init,
+                                             final_state=fs_b, raise_on_divergence=False,
+                                             schedule="fused_chain", readout=readout, output_states=False)
+        torch.cuda.synchronize()
+        assert Sb is None
+        # the zero guess diverges: compare NaN positions, values elsewhere
+        for a, b in ((fs_a, Sa[:, -1]), (ha, hb), (fs_a, fs_b)):
+            nan = torch.isnan(a)
+            assert torch.equal(nan, torch.isnan(b))
+            assert torch.equal(a[~nan], b[~nan])
+        assert sta.iters == stb.iters == K
+        assert np.array_equal(np.array(sta.max_abs_F), np.array(stb.max_abs_F), equal_nan=True)
+        if init == "warm":
+            mode = forget if readout == "exact" else forget + "/floored"
+            S_ref, st_ref = ref.newton(to_np(P), to_np(R), None if s0 is None else to_np(s0), mode, K,
+                                       init=init)
+            bar = H_TOL_BF16 if p_dtype == "bf16" else H_TOL_F32
+            fl = h_floor(forget, bar)
+            assert h_rel_err(hb, S_ref[..., 3, :], fl) < bar
+            assert h_rel_err(fs_b[:, 3], S_ref[:, -1, 3], fl) < bar
+            for slot in range(3):  # c, n, m of the final state, normwise per slot
+                ref_s = S_ref[:, -1, slot]
+                assert np.max(np.abs(to_np(fs_b[:, slot]) - ref_s)) <= bar * np.max(np.abs(ref_s))
+            assert stb.diverged == st_ref.diverged
