@@ -145,6 +145,8 @@ KERNEL_SOURCES = {
     "packed_backward": ["recurrent_nets_amd/csrc/k_backward.hip", "recurrent_nets_amd/csrc/affine4.h",
                         "recurrent_nets_amd/csrc/cell.h", "recurrent_nets_amd/csrc/common.h",
                         "recurrent_nets_amd/csrc/kernels.h"],
+    "newton_solve_states": ["recurrent_nets_amd/csrc/k_newton_pipe.hip", "recurrent_nets_amd/csrc/cell.h",
+                            "recurrent_nets_amd/csrc/common.h", "recurrent_nets_amd/csrc/kernels.h"],
     "head_solve": ["recurrent_nets_amd/csrc/k_head_solve.hip", "recurrent_nets_amd/csrc/head.h",
                    "recurrent_nets_amd/csrc/affine4.h", "recurrent_nets_amd/csrc/cell.h",
                    "recurrent_nets_amd/csrc/common.h", "recurrent_nets_amd/csrc/kernels.h"],
@@ -670,12 +672,15 @@ def main():
                     roof = {"bound": "alu", "kernel": dominant, **alu, "hbm_view": hbm_view}
                 else:
                     roof["alu_view"] = alu
-            insts = measured_valu(dominant, w.name)
+            # the one-kernel solve's counters are recorded apart for the step that writes the states
+            rec = dominant + ("_states" if dominant == "newton_solve" and kernels.get("_states_out") else "")
+            insts = measured_valu(rec, w.name)
             if insts:
                 roof["valu_issue"] = {"valu_insts_per_launch": insts,
                                       "frac": round(valu_issue_frac(insts, k["avg_ms"]), 4),
                                       "source": "profiles/valu.json (rocprofv3 SQ_INSTS_VALU)"}
-        roof["traffic"] = measured_traffic(dominant, w.name)
+        rec = dominant + ("_states" if dominant == "newton_solve" and kernels.get("_states_out") else "")
+        roof["traffic"] = measured_traffic(rec, w.name)
         # whole-step roofline: every kernel at its own bound
         t_roof = 0.0
         for kind, kk in kernels.items():

@@ -547,7 +547,8 @@ slstm_status newton_forward(const void* P, slstm_dtype P_dtype, const float* R, 
     const uint32_t ep = next_epoch();
     HIP_TRY(timed(SLSTM_KERNEL_NEWTON_SOLVE, st, [&] {
       return slstm::launch_newton_pipe(P, bf16, R, state0, states, h_out, final_state, B, T, d_h, cm,
-                                       init == SLSTM_INIT_WARM, max_iters, desc, tickets, ep, ctl, st);
+                                       init == SLSTM_INIT_WARM, max_iters,
+                                       slstm::pipe_tile_steps(B, d_h, device_cus()), desc, tickets, ep, ctl, st);
     }));
     HIP_TRY(slstm::launch_finalize(ctl, tol, st));
   } else {

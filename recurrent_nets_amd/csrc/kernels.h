@@ -45,8 +45,10 @@ constexpr int kPipeMaxIters = 4;
 size_t pipe_desc_words(int B, int T, int d, int K);
 hipError_t launch_newton_pipe(const void* P, bool p_bf16, const float* R, const float* state0,
                               float* S_out, float* h_out, float* fs_out, int B, int T, int d, int cell_mode,
-                              bool warm, int K, unsigned long long* carry, unsigned int* tickets,
-                              uint32_t epoch, Control* ctl, hipStream_t stream);
+                              bool warm, int K, int tile_steps, unsigned long long* carry,
+                              unsigned int* tickets, uint32_t epoch, Control* ctl, hipStream_t stream);
+// steps per tile of the one-kernel solve for a shape on a GPU of n_cus compute units
+int pipe_tile_steps(int B, int d, int n_cus);
 // after the last chain iteration: declares iterate k final when its residual met tol
 hipError_t launch_settle(Control* ctl, int k, float tol, hipStream_t stream);
 // copies the final iterate into `states` when it ended in the other buffer (iterate k lives in
