@@ -150,6 +150,51 @@ def test_full_layer_workload_full_size(gpu_lib, schedule):
     assert err_dec < GUARD_DECODE
 
 
+def test_full_layer_hidden_only_as_benchmarked(gpu_lib):
+    """The full-layer forward in the launch the benchmark times: schedule "fused" (the one-kernel
+    solve at this shape) writing the layer's default output, h and the final state, without a
+    state tensor. h and the final state equal, bit for bit, those of the same solve writing the
+    states, and h matches the oracle on sampled lanes."""
+    w = by_name("layer_b128_t2048_d1024")
+    case(f"full size {w.name}: hidden-only one-kernel solve as the benchmark launches it")
+    inp = draw_layer_inputs(w)
+    W = inp["W"].to(DEV)
+    bias = inp["bias"].to(DEV)
+    R = inp["R"].to(DEV)
+    P = gpu_lib.input_projection(inp["x"].to(DEV), W, bias)
+    ws = gpu_lib.alloc_workspace(gpu_lib.newton_workspace_bytes(w.B, w.T, w.d_h, "fused"), P.device)
+    H = torch.empty((w.B, w.T, w.d_h), dtype=torch.float32, device=DEV)
+    fin = torch.empty((w.B, 4, w.d_h), dtype=torch.float32, device=DEV)
+    gpu_lib.profile_reset()
+    gpu_lib.profile_enable(True)
+    Sn, _, st = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, "warm", states=None, h_out=H,
+                                       final_state=fin, workspace=ws, schedule="fused", output_states=False)
+    n_solve = len(gpu_lib.profile_durations("newton_solve"))
+    gpu_lib.profile_enable(False)
+    torch.cuda.synchronize()
+    assert Sn is None and n_solve == 1  # the one-kernel form ran
+    assert st.iters == w.max_iters and not st.diverged
+    S, h, st2 = gpu_lib.newton_forward(P, R, None, w.forget, w.max_iters, w.tol, workspace=ws, schedule="fused")
+    torch.cuda.synchronize()
+    assert torch.equal(H, h) and torch.equal(fin, S[:, -1])
+    assert np.array_equal(np.array(st.max_abs_F), np.array(st2.max_abs_F))
+    del S, h
+    lb, lj = sample_lanes(w.B, w.d_h, 32, seed=5)
+    x64 = to_np(inp["x"][torch.as_tensor(np.unique(lb))])
+    rows = {int(b): k for k, b in enumerate(np.unique(lb))}
+    W64 = to_np(inp["W"])
+    b64 = to_np(inp["bias"])
+    P_lanes = np.empty((1, w.T, 4, len(lb)))
+    for k, (b, j) in enumerate(zip(lb, lj)):
+        P_lanes[0, :, :, k] = ref.input_projection(x64[rows[int(b)]][None], W64[:, j:j + 1], b64[:, j:j + 1])[0, :, :, 0]
+    S_ref, st_ref = ref.newton(P_lanes, to_np(inp["R"])[:, lj], None, w.forget, w.max_iters, tol=w.tol)
+    err = h_rel_err(_gpu_h_at(H, lb, lj), np.transpose(S_ref[0, :, 3, :], (1, 0)))
+    print(f"full layer, hidden-only: h rel err {err:.2e}")
+    assert err < H_TOL_BF16 and err < GUARD_LAYER
+    fin_gpu = fin[torch.as_tensor(lb, device=DEV), 3, torch.as_tensor(lj, device=DEV)]
+    assert h_rel_err(fin_gpu, S_ref[0, -1, 3]) < GUARD_LAYER
+
+
 def test_full_layer_decode_step(gpu_lib):
     """The decode step on every lane of the batch, from a drawn state (the chained case on
     sampled lanes is part of the full-layer test)."""
