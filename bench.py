@@ -64,14 +64,15 @@ JAC_BYTES = 12 * 4
 def solve_flops_per_elem(K, sigmoid_forget):
     """Floating-point operations of one state element of a whole Newton solve as the one-kernel
     solve forms them (an add, multiply, compare-select or max counts 1, an FMA 2, an exp2, log2
-    or reciprocal 1): warm-start step 25, cell step 34, the coefficients of its Jacobian in
-    factored form 13, residual and its maximum 8, the Newton step through the factored Jacobian
+    or reciprocal 1): warm-start step 25 (with the scaling of the z and o pre-activations for
+    their exponentials, done once per step), cell step 32, the coefficients of its Jacobian in
+    factored form 12, residual and its maximum 8, the Newton step through the factored Jacobian
     22, the update 4; the sigmoid forget gate adds a log-sigmoid to every step (6) and its
     derivative to every linearisation (5)."""
     sig = 1 if sigmoid_forget else 0
     warm = 25 + 6 * sig
-    cell = 34 + 6 * sig
-    lin = 13 + 5 * sig
+    cell = 32 + 6 * sig
+    lin = 12 + 5 * sig
     return warm + K * (cell + lin + 8 + 22 + 4) + (cell + 8)
 
 
@@ -105,13 +106,13 @@ def head_solve_flops_per_elem(d_head, K, sigmoid_forget):
     """Floating-point operations of one state element (b, t, j) in the one-sweep head-mixing
     Newton solve as the kernel forms them: K + 1 block products (R h' of the warm start, then
     R Delta h' of each iteration) for the four gates, 8 d_head each; the warm-start step 34; per
-    iteration the cell step 34, its own-state and gate Jacobians 31, the residual and its maximum
+    iteration the cell step 34, its own-state and gate Jacobians 30, the residual and its maximum
     8, the factored solve (3 own-state and 4 gate FMAs per slot) 56, the update 4 and the
     pre-activation update 4; the final residual 34 + 8. The sigmoid forget gate adds 6 to every
     cell step and 5 to every Jacobian, as in solve_flops_per_elem."""
     sig = 1 if sigmoid_forget else 0
     cell = 34 + 6 * sig
-    return 8 * d_head * (K + 1) + cell + K * (cell + 31 + 5 * sig + 8 + 56 + 4 + 4) + cell + 8
+    return 8 * d_head * (K + 1) + cell + K * (cell + 30 + 5 * sig + 8 + 56 + 4 + 4) + cell + 8
 
 
 def source_sha(paths):

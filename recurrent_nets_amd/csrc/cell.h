@@ -40,6 +40,15 @@ __device__ __forceinline__ float sigmoidf(float x) { return rcp_fast(1.0f + exp_
 __device__ __forceinline__ float tanh_fast(float x) {
   return 1.0f - 2.0f * rcp_fast(1.0f + __builtin_amdgcn_exp2f(x * (2.0f * kLog2e)));
 }
+// The same two from their exponent arguments already scaled: tanh_scaled(x * kTanhScale) and
+// sigmoid_scaled(x * kSigScale) are bitwise tanh_fast(x) and sigmoidf(x). A kernel that keeps a
+// step's pre-activations in registers through several evaluations scales them once.
+constexpr float kTanhScale = 2.0f * kLog2e;
+constexpr float kSigScale = -kLog2e;
+__device__ __forceinline__ float tanh_scaled(float xs) {
+  return 1.0f - 2.0f * rcp_fast(1.0f + __builtin_amdgcn_exp2f(xs));
+}
+__device__ __forceinline__ float sigmoid_scaled(float xs) { return rcp_fast(1.0f + __builtin_amdgcn_exp2f(xs)); }
 // log sigma(x) = -softplus(-x) = -(max(-x, 0) + ln(1 + e^{-|x|})), finite for any finite x
 __device__ __forceinline__ float log_sigmoidf(float x) {
   return -(fmaxf(-x, 0.0f) + kLn2 * __builtin_amdgcn_logf(1.0f + exp_fast(-fabsf(x))));
@@ -94,20 +103,26 @@ __device__ __forceinline__ void stab_gates(float a, float it, float& m, float& i
 // m = max(a, i~) makes one of the two gates exactly e^0 = 1: with beta = (a >= i~) and
 // e = e^{-|a - i~|}, (i', f') = (e, 1) when beta and (1, e) otherwise. Both are bitwise the
 // values e^{i~ - m} and e^{a - m}, from one exponential.
+//
+// The z and o pre-activations enter their exponentials scaled: z~ kTanhScale = r_z kTanhScale h'
+// + p_z kTanhScale as one FMA (likewise o with kSigScale). With PRE the caller passes p_z and p_o
+// already scaled (the same float32 products, so the same bits); r_z and r_o are always raw.
+// h = (o / D) c, the product the Jacobian's h row reuses.
 struct CellCore {
-  float z, o, dlf, e, ig, fg, c, n, m, h, rn;
+  float z, o, dlf, e, ig, fg, c, n, m, h, rn, q1;
   bool beta;
   Readout rdn;
 };
+template <bool PRE = false>
 __device__ __forceinline__ CellCore cell_core(const CellIn& pv, float pz, float pi, float pf, float po, float rz,
                                               float ri, float rf, float ro, bool sig_forget, bool floored) {
   CellCore k;
-  const float zt = fmaf(rz, pv.h, pz);
+  const float zs = fmaf(rz * kTanhScale, pv.h, PRE ? pz : pz * kTanhScale);
   const float it = fmaf(ri, pv.h, pi);
   const float ft = fmaf(rf, pv.h, pf);
-  const float ot = fmaf(ro, pv.h, po);
-  k.z = tanh_fast(zt);
-  k.o = sigmoidf(ot);
+  const float os = fmaf(ro * kSigScale, pv.h, PRE ? po : po * kSigScale);
+  k.z = tanh_scaled(zs);
+  k.o = sigmoid_scaled(os);
   float lf;
   if (sig_forget) {
     lf = log_sigmoidf(ft);
@@ -126,7 +141,8 @@ __device__ __forceinline__ CellCore cell_core(const CellIn& pv, float pz, float 
   k.n = fmaf(k.fg, pv.n, k.ig);
   k.rdn = readout(k.n, k.m, floored);
   k.rn = k.rdn.rD;
-  k.h = k.o * k.c * k.rn;
+  k.q1 = k.o * k.rn;
+  k.h = k.q1 * k.c;
   return k;
 }
 
@@ -139,11 +155,11 @@ __device__ __forceinline__ CellCore cell_core(const CellIn& pv, float pz, float 
 //   dc/dh' = D dc/dm' + i' dz/dh',  dn/dh' = D dn/dm',
 // and dm/dm' = beta, dm/dh' = beta ? l' r_f : r_i. The h row is the quotient rule through c
 // and through the read-out's denominator D(n, m).
-template <bool JAC>
+template <bool JAC, bool PRE = false>
 __device__ __forceinline__ void cell_step(const CellIn& pv, float pz, float pi, float pf, float po,
                                           float rz, float ri, float rf, float ro, bool sig_forget,
                                           bool floored, float s[4], float A[16]) {
-  const CellCore k = cell_core(pv, pz, pi, pf, po, rz, ri, rf, ro, sig_forget, floored);
+  const CellCore k = cell_core<PRE>(pv, pz, pi, pf, po, rz, ri, rf, ro, sig_forget, floored);
   s[0] = k.c;
   s[1] = k.n;
   s[2] = k.m;
@@ -160,7 +176,7 @@ __device__ __forceinline__ void cell_step(const CellIn& pv, float pz, float pi, 
     const float c_h = fmaf(c_m, D, ig * dz_dh);
     const float n_h = n_m * D;
     // row h = o c / D: (o/D) dc - (o c / D^2) (D_n dn + D_m dm), plus (c/D) do on h'
-    const float q1 = o * rn;
+    const float q1 = k.q1;
     const float q2 = h * rn;
     A[0] = fg;     A[1] = 0.0f;   A[2] = c_m;   A[3] = c_h;
     A[4] = 0.0f;   A[5] = fg;     A[6] = n_m;   A[7] = n_h;
@@ -187,16 +203,17 @@ __device__ __forceinline__ void cell_step(const CellIn& pv, float pz, float pi, 
 //   A_n Delta' = f' n' + n_m y
 //   A_m Delta' = r_i h' + (beta ? y : 0)
 //   A_h Delta' = q1 A_c Delta' - qn A_n Delta' - qm A_m Delta' + dov h'
-// (q1 = o / D, qn = (h / D) D_n, qm = (h / D) D_m, dov = (c / D) do/dh' = h (1 - o) r_o), which
-// reuses the c, n and m rows instead of forming the h row's four entries.
+// (q1 = o / D, qn = (h / D) D_n, qm = (h / D) D_m, dov = (c / D) do/dh' = (h - h o) r_o), which
+// reuses the c, n and m rows instead of forming the h row's four entries. PRE as in cell_core.
 struct DiagLin {
   float fg, c_m, n_m, g, D, ri, q1, qn, qm, dov;
   bool beta;
 };
+template <bool PRE = false>
 __device__ __forceinline__ void cell_step_diag(const CellIn& pv, float pz, float pi, float pf, float po, float rz,
                                                float ri, float rf, float ro, bool sig_forget, bool floored,
                                                float s[4], DiagLin& L) {
-  const CellCore k = cell_core(pv, pz, pi, pf, po, rz, ri, rf, ro, sig_forget, floored);
+  const CellCore k = cell_core<PRE>(pv, pz, pi, pf, po, rz, ri, rf, ro, sig_forget, floored);
   s[0] = k.c;
   s[1] = k.n;
   s[2] = k.m;
@@ -208,11 +225,11 @@ __device__ __forceinline__ void cell_step_diag(const CellIn& pv, float pz, float
   L.g = k.ig * (fmaf(-k.z, k.z, 1.0f) * rz);
   L.D = fmaf(k.dlf, rf, -ri);
   L.ri = ri;
-  L.q1 = k.o * k.rn;
+  L.q1 = k.q1;
   const float q2 = k.h * k.rn;
   L.qn = floored ? q2 * k.rdn.dn : q2;
   L.qm = floored ? q2 * k.rdn.dm : 0.0f;
-  L.dov = k.h * (1.0f - k.o) * ro;
+  L.dov = fmaf(-k.h, k.o, k.h) * ro;
 }
 
 // x <- A x + rhs for the step L linearises (x holds Delta_{t-1} on entry, Delta_t on return)

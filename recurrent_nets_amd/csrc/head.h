@@ -118,7 +118,8 @@ __device__ __forceinline__ void cell_step_lin(const CellIn& pv, const float x[4]
   const float n = fmaf(fg, pv.n, ig);
   const Readout rdn = readout(n, m, floored);
   const float rn = rdn.rD;
-  const float h = o * c * rn;
+  const float q1 = o * rn;  // h = (o / D) c, as the channelwise cell forms it
+  const float h = q1 * c;
   s[0] = c;
   s[1] = n;
   s[2] = m;
@@ -131,7 +132,7 @@ __device__ __forceinline__ void cell_step_lin(const CellIn& pv, const float x[4]
   L.gm_i = beta ? 0.0f : 1.0f;
   L.gm_f = beta ? dlf : 0.0f;
   L.dlf = dlf;
-  L.q1 = o * rn;
+  L.q1 = q1;
   const float q2 = h * rn;
   L.qn = floored ? q2 * rdn.dn : q2;
   L.qm = floored ? q2 * rdn.dm : 0.0f;

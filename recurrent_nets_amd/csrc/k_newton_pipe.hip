@@ -99,6 +99,9 @@ __global__ __launch_bounds__(kPipeBlock, pipe_min_waves(TC)) void newton_pipe_ke
     const unsigned uc = static_cast<unsigned>(u < u_last ? u : u_last);
 #pragma unroll
     for (int k = 0; k < 4; ++k) p[u][k] = buf_ld_p<BF16>(rsP, jc, (4u * uc + k) * ud);
+    // z and o enter only their exponentials: scaled once here for all K + 2 evaluations
+    p[u][0] *= kTanhScale;
+    p[u][3] *= kSigScale;
   }
   float rz = 0.0f, ri = 0.0f, rf = 0.0f, ro = 0.0f;
   float hv[4] = {0.0f, 0.0f, 0.0f, 0.0f};  // the iterate at step t0 - 1 (state0 before the sequence)
@@ -120,10 +123,10 @@ __global__ __launch_bounds__(kPipeBlock, pipe_min_waves(TC)) void newton_pipe_ke
     // gate terms first (they need P only): z, l, i~, sigma(p_o) in the slots of s[u]
 #pragma unroll
     for (int u = 0; u < TC; ++u) {
-      s[u][0] = tanh_fast(p[u][0]);
+      s[u][0] = tanh_scaled(p[u][0]);
       s[u][1] = sig ? log_sigmoidf(p[u][2]) : p[u][2];
       s[u][2] = p[u][1];
-      s[u][3] = sigmoidf(p[u][3]);
+      s[u][3] = sigmoid_scaled(p[u][3]);
     }
     if (wait) wait_words(0, hv);
     float c = hv[0], n = hv[1], m = hv[2];
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(kPipeBlock, pipe_min_waves(TC)) void newton_pipe_ke
           float f[4], r[4];
           DiagLin L;
           const CellIn pv = u == 0 ? pv0 : CellIn{s[u - 1][0], s[u - 1][1], s[u - 1][2], s[u - 1][3]};
-          cell_step_diag(pv, p[u][0], p[u][1], p[u][2], p[u][3], rz, ri, rf, ro, sig, floored, f, L);
+          cell_step_diag<true>(pv, p[u][0], p[u][1], p[u][2], p[u][3], rz, ri, rf, ro, sig, floored, f, L);
           if (u > 0) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) s[u - 1][e] = s[u - 1][e] + x[e];
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(kPipeBlock, pipe_min_waves(TC)) void newton_pipe_ke
     for (int u = 0; u < TC; ++u) {
       if (t0 + u < T) {
         float f[4];
-        cell_step<false>(pv, p[u][0], p[u][1], p[u][2], p[u][3], rz, ri, rf, ro, sig, floored, f, nullptr);
+        cell_step<false, true>(pv, p[u][0], p[u][1], p[u][2], p[u][3], rz, ri, rf, ro, sig, floored, f, nullptr);
         res_max2(fmax, s[u][0] - f[0], s[u][1] - f[1]);
         res_max2(fmax, s[u][2] - f[2], s[u][3] - f[3]);
         if (S_out != nullptr) {
