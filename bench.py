@@ -911,17 +911,25 @@ def main():
                                                         args.no_cpu_baseline)
 
     if not args.no_sequential_context:
-        # the lane-parallel sequential forward on the same P, for context (not the metric)
-        slstm.sequential_forward(P, R, None, w.forget, states=S, h_out=H)
-        torch.cuda.synchronize()
-        reps = 5
-        ts = time.perf_counter()
-        for _ in range(reps):
-            slstm.sequential_forward(P, R, None, w.forget, states=S, h_out=H)
-        torch.cuda.synchronize()
-        seq_ms = (time.perf_counter() - ts) * 1000.0 / reps
-        context["sequential_forward"] = {"ms": round(seq_ms, 3),
-                                         "state_elems_per_s": n_e / (seq_ms * 1e-3)}
+        # the lane-parallel sequential forward on the same P, for context (not the metric): the
+        # layer's default output (h and the final state) like the timed step, then with the states
+        def seq_ms_of(states_out):
+            run = lambda: slstm.sequential_forward(P, R, None, w.forget, states=S if states_out else None,  # noqa: E731
+                                                   h_out=H, final_state=FS, output_states=states_out)
+            run()
+            torch.cuda.synchronize()
+            reps = 5
+            ts = time.perf_counter()
+            for _ in range(reps):
+                run()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - ts) * 1000.0 / reps
+        seq_ms = seq_ms_of(False)
+        seq_ms_states = seq_ms_of(True)
+        context["sequential_forward"] = {"ms": round(seq_ms, 3), "state_elems_per_s": n_e / (seq_ms * 1e-3),
+                                         "outputs": "hidden slot and final state",
+                                         "with_states": {"ms": round(seq_ms_states, 3),
+                                                         "state_elems_per_s": n_e / (seq_ms_states * 1e-3)}}
 
     cpu = None
     if not args.no_cpu_baseline:

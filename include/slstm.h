@@ -197,7 +197,8 @@ slstm_status slstm_newton_forward_noalloc(const void* P, slstm_dtype P_dtype, co
 /*
  * Sequential forward ([SL] "API notes": solver='sequential'; at T = 1 the decode step):
  * s_t = f(s_{t-1}, P_t) for t = 1..T, one thread per lane (b, j). Same arguments and layouts
- * as slstm_newton_forward; needs no workspace.
+ * as slstm_newton_forward; needs no workspace. states may be NULL (unpacked calls): h_out and
+ * final_state are then the outputs, the layer's default output ([SL] "Outputs").
  */
 slstm_status slstm_sequential_forward(const void* P, slstm_dtype P_dtype, const float* R,
                                       const float* state0, float* states, float* h_out,

@@ -569,8 +569,11 @@ slstm_status newton_forward(const void* P, slstm_dtype P_dtype, const float* R, 
 slstm_status sequential_forward(const void* P, slstm_dtype P_dtype, const float* R, const float* state0,
                                 float* states, float* h_out, float* final_state, int B, int T, int d_h,
                                 slstm_forget fmode, void* stream, slstm::Seqs seqs) {
-  slstm_status s = check_common(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, fmode);
+  slstm_status s = check_common(P, P_dtype, R, state0, states, h_out, final_state, B, T, d_h, fmode, false);
   if (s != SLSTM_OK) return s;
+  // packed final states are gathered from the state tensor afterwards
+  if (states == nullptr && seqs.cu != nullptr)
+    return fail(SLSTM_EINVAL, "states may be NULL only for unpacked sequences");
   hipStream_t st = static_cast<hipStream_t>(stream);
   HIP_TRY(timed(SLSTM_KERNEL_SEQUENTIAL, st, [&] {
     return slstm::launch_sequential(P, P_dtype == SLSTM_BF16, R, state0, states, h_out, final_state,

@@ -54,11 +54,13 @@ __global__ __launch_bounds__(kSeqBlock) void sequential_kernel(
         float s[4];
         cell_step<false>(pv, cur[u][0], cur[u][1], cur[u][2], cur[u][3], rz, ri, rf, ro, sig, floored, s,
                          nullptr);
-        float* sp = S + lane_base + static_cast<i64>(t) * d4;
-        sp[0] = s[0];
-        sp[dd] = s[1];
-        sp[2 * dd] = s[2];
-        sp[3 * dd] = s[3];
+        if (S != nullptr) {  // the states are an output only when asked for
+          float* sp = S + lane_base + static_cast<i64>(t) * d4;
+          sp[0] = s[0];
+          sp[dd] = s[1];
+          sp[2 * dd] = s[2];
+          sp[3 * dd] = s[3];
+        }
         if (h_out != nullptr) h_out[(static_cast<i64>(b) * T + t) * dd + j] = s[3];
         pv = {s[0], s[1], s[2], s[3]};
       }

@@ -362,16 +362,18 @@ def read_stats(workspace, stream=None) -> NewtonStats:
 
 def sequential_forward(P, R, state0=None, forget="exp", states=None, h_out=None,
                        want_hidden=True, final_state=None, stream=None, readout="exact",
-                       cu_seqlens=None):
+                       cu_seqlens=None, output_states=True):
     """Step-by-step forward (also the T=1 decode step). Returns (states, h or None). A given
-    ``final_state`` (B,4,d_h) tensor receives the last step's state."""
+    ``final_state`` (B,4,d_h) tensor receives the last step's state. ``output_states=False``
+    (unpacked only) writes no state tensor and returns None for it: h and the final state are
+    the outputs, as in the layer's default output."""
     L = load()
     _dev(P, "P", (torch.float32, torch.bfloat16))
     _dev(R, "R", (torch.float32,))
     _dev(state0, "state0", (torch.float32,))
     cu, S = _seqs(cu_seqlens, P)
     B, T, d = _shape_check(P, R, state0, S)
-    if states is None:
+    if states is None and output_states:
         states = torch.empty((B, T, 4, d), dtype=torch.float32, device=P.device)
     if want_hidden and h_out is None:
         h_out = torch.empty((B, T, d), dtype=torch.float32, device=P.device)

@@ -124,6 +124,11 @@ def test_argument_checks_return_einval(lib):
     s = lib.slstm_sequential_forward(None, 0, ctypes.c_void_p(256), None, ctypes.c_void_p(256),
                                      None, None, 2, 64, 16, 0, None)
     assert s == slstm.EINVAL
+    # the packed sequential forward gathers its final states from the state tensor
+    cu = ctypes.c_void_p(1024)
+    s = lib.slstm_sequential_forward_varlen(ctypes.c_void_p(256), 0, ctypes.c_void_p(256), None, cu, 2,
+                                            None, None, None, 64, 16, 0, None)
+    assert s == slstm.EINVAL and "unpacked" in lib.slstm_last_error().decode()
 
 
 def _bwd(lib, **kw):

@@ -312,3 +312,24 @@ def test_hidden_only_output(gpu_lib, name, readout):
                 ref_s = S_ref[:, -1, slot]
                 assert np.max(np.abs(to_np(fs_b[:, slot]) - ref_s)) <= bar * np.max(np.abs(ref_s))
             assert stb.diverged == st_ref.diverged
+
+
+@pytest.mark.parametrize("p_dtype", ["f32", "bf16"])
+def test_sequential_hidden_only_output(gpu_lib, p_dtype):
+    """The sequential forward writing only h and the final state (no state tensor) gives, bit
+    for bit, what it writes beside the states (ragged d, a random initial state)."""
+    w = by_name("mid_b8_t1024_d256")
+    inp = draw_preactivation_inputs(w, B=3, T=333)
+    P = inp["P"][..., :200].contiguous()
+    if p_dtype == "bf16":
+        P = P.to(torch.bfloat16)
+    R = inp["R"][:, :200].contiguous().to(DEV)
+    s0 = torch.from_numpy(random_states(w.seed + 13, 3, 1, 200)[:, 0].astype(np.float32)).to(DEV)
+    case(f"sequential hidden-only output {p_dtype}")
+    fa = torch.empty(3, 4, 200, device=DEV)
+    fb = torch.empty(3, 4, 200, device=DEV)
+    Sa, ha = gpu_lib.sequential_forward(P.to(DEV), R, s0, w.forget, final_state=fa)
+    Sb, hb = gpu_lib.sequential_forward(P.to(DEV), R, s0, w.forget, final_state=fb, output_states=False)
+    torch.cuda.synchronize()
+    assert Sb is None
+    assert torch.equal(ha, hb) and torch.equal(fa, fb) and torch.equal(fa, Sa[:, -1])
