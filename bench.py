@@ -467,9 +467,9 @@ def solver_context(slstm, torch, dev, name, steps, cpu_lanes, no_cpu):
     sv = kernels.get("newton_solve")
     if sv:
         # few lane groups: the wavefront along T waits on each tile's predecessor in turn; the
-        # library's tiles are 14 steps where the lane groups cover the CUs, 24 otherwise
+        # library's tiles are 15 steps where the lane groups cover the CUs, 24 otherwise
         n_cus = torch.cuda.get_device_properties(dev).multi_processor_count
-        n_tt = -(-w.T // (14 if w.B * -(-w.d_h // 256) >= n_cus else 24))
+        n_tt = -(-w.T // (15 if w.B * -(-w.d_h // 256) >= n_cus else 24))
         out["roofline"] = {"bound": "latency", "kernel": "newton_solve", "achieved": sv["GB_s"],
                            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(sv["GB_s"] / HBM_PEAK_GBS, 4),
                            "tiles_along_T": n_tt, "us_per_tile": round(sv["avg_ms"] * 1e3 / n_tt, 3),

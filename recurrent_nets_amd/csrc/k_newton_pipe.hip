@@ -32,14 +32,15 @@
 namespace slstm {
 
 constexpr int kPipeBlock = 256;  // one feature per thread
-// Steps per tile. Short tiles (14 steps, P and the iterate in 167 registers, three workgroups a
-// CU) where the lane groups cover every CU: the solve is bound by vector issue there, and more
-// resident waves hide the latency of each step's dependent chain. Long tiles (24 steps, 235
-// registers, two workgroups a CU) where they do not: the wavefront along T then waits on each
-// tile's predecessor in turn, and longer tiles mean fewer hand-offs. Measured on MI355X (K = 3,
-// d_h = 1024): 512 lane groups 2.46 against 2.52 ms, 256 the same, 128 0.87 against 0.73 ms,
-// 32 (B = 4, T = 16384, d_h = 2048, K = 4) 3.91 against 3.21 ms; the results are bitwise equal.
-constexpr int kPipeStepsShort = 14;
+// Steps per tile. Short tiles (15 steps, P and the iterate in 166 registers, the most that keep
+// three workgroups a CU) where the lane groups cover every CU: the solve is bound by vector issue
+// there, and more resident waves hide the latency of each step's dependent chain. Long tiles (24
+// steps, 238 registers, two workgroups a CU) where they do not: the wavefront along T then waits
+// on each tile's predecessor in turn, and longer tiles mean fewer hand-offs. Measured on MI355X
+// (K = 3, d_h = 1024): 512 lane groups 2.46 ms at 14 steps against 2.52 at 24 (15 steps: 2.37
+// against 2.40 at 14), 256 the same, 128 0.87 against 0.73 ms, 32 (B = 4, T = 16384, d_h = 2048,
+// K = 4) 3.91 against 3.21 ms; the results are bitwise equal.
+constexpr int kPipeStepsShort = 15;
 constexpr int kPipeStepsLong = 24;
 
 __host__ __device__ constexpr int pipe_words(int K) { return 4 + 4 * K; }
