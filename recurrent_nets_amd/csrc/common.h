@@ -148,24 +148,17 @@ __device__ __forceinline__ float abs_nan_inf(float x) {
 __device__ __forceinline__ unsigned int res_max(unsigned int acc, float x) {
   return max(acc, __float_as_uint(x) & 0x7fffffffu);
 }
-// The same maximum kept as two running maxima of the raw bit patterns, one max3 per two values
-// and order instead of a mask per value: as unsigned integers every negative value lies above
-// every non-negative one and negatives order by magnitude; as signed integers every negative
-// lies below every non-negative value and non-negatives order by magnitude. So the unsigned
-// maximum holds the largest negative magnitude when there is a negative value, the signed one
-// the largest non-negative magnitude when there is a non-negative value, and the larger of the
-// two with the sign cleared is the largest |x|, NaN (either sign) above +inf as before.
+// The same maximum for a kernel that folds many values in: a float running maximum of |x| with
+// the NaN-propagating maximum (IEEE 754-2019 maximum, one v_maximum3_f32 per two values, the
+// absolute values as operand modifiers). Its bit pattern is then that of the largest |x|, or of
+// a quiet NaN, which lies above +inf like the patterns res_max keeps.
 struct ResMax2 {
-  unsigned int u = 0u;
-  int i = 0;
+  float v = 0.0f;
 };
 __device__ __forceinline__ void res_max2(ResMax2& acc, float a, float b) {
-  acc.u = max(max(acc.u, __float_as_uint(a)), __float_as_uint(b));
-  acc.i = max(max(acc.i, __float_as_int(a)), __float_as_int(b));
+  acc.v = __builtin_elementwise_maximum(__builtin_elementwise_maximum(acc.v, fabsf(a)), fabsf(b));
 }
-__device__ __forceinline__ unsigned int res_max2_bits(const ResMax2& acc) {
-  return max(acc.u & 0x7fffffffu, static_cast<unsigned int>(acc.i) & 0x7fffffffu);
-}
+__device__ __forceinline__ unsigned int res_max2_bits(const ResMax2& acc) { return __float_as_uint(acc.v); }
 __device__ __forceinline__ float res_max_value(unsigned int acc) {
   return acc > 0x7f800000u ? __int_as_float(0x7f800000) : __uint_as_float(acc);
 }
