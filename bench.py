@@ -412,9 +412,10 @@ def solver_context(slstm, torch, dev, name, steps, cpu_lanes, no_cpu):
     log(f"[bench] context {name}: inputs ready in {time.perf_counter() - t_gen:.1f} s")
     p_bytes = 8 if w.p_dtype == "bf16" else 16
     n_e = w.state_elems
-    # the library runs a fixed-count solve on 32 or more lane groups of 256 features as one
-    # kernel, which needs no state tensor: the layer's default output, h and the final state
-    one_kernel = w.tol == 0.0 and w.max_iters <= 4 and w.B * -(-w.d_h // 256) >= 32
+    # the library runs a fixed-count solve (K <= 4) on 32 or more lane groups of 256 features
+    # as one kernel, and an early stop (K <= 8) as two passes of it; neither needs a state
+    # tensor: the layer's default output, h and the final state
+    one_kernel = (w.max_iters <= 4 if w.tol == 0.0 else w.max_iters <= 8) and w.B * -(-w.d_h // 256) >= 32
     S = None if one_kernel else torch.empty((w.B, w.T, 4, w.d_h), dtype=torch.float32, device=dev)
     H = torch.empty((w.B, w.T, w.d_h), dtype=torch.float32, device=dev)
     FS = torch.empty((w.B, 4, w.d_h), dtype=torch.float32, device=dev)
@@ -454,7 +455,9 @@ def solver_context(slstm, torch, dev, name, steps, cpu_lanes, no_cpu):
         f"converged {st.converged}, iteration kernel {it['avg_ms'] if it else float('nan'):.3f} ms")
     out = {"B": w.B, "T": w.T, "d_h": w.d_h, "preactivations": w.p_dtype, "forget_gate": w.forget,
            "max_iters": w.max_iters, "tol": w.tol,
-           "schedule": "fused (one-kernel form at this shape)" if one_kernel else "fused (scan form at this shape)",
+           "schedule": ("fused (scan form at this shape)" if not one_kernel else
+                        "fused (one-kernel form at this shape)" if w.tol == 0.0 else
+                        "fused (one-kernel form at this shape: the budget, the stop test, then the count it chose)"),
            "outputs": "hidden slot and final state" if one_kernel else "states, hidden slot",
            "solve_ms": round(ms, 4), "state_elems_per_s": n_e / (ms * 1e-3),
            "solver": {"iters": st.iters, "converged": st.converged, "diverged": st.diverged,

@@ -90,7 +90,14 @@ typedef enum { SLSTM_INIT_WARM = 0, SLSTM_INIT_ZERO = 1 } slstm_init;
  *  SLSTM_SCHEDULE_FUSED        FUSED_CHAIN when B * ceil(d_h / 256) is at least the GPU's
  *                              compute-unit count, or at least 32 for a fixed-count solve
  *                              (tol = 0, max_iters <= 4, unpacked: the one-kernel form, which
- *                              reads P once); FUSED_SCAN otherwise;
+ *                              reads P once; under FUSED max_iters <= 8) or an early-stop
+ *                              solve (tol > 0, max_iters <= 8, unpacked); FUSED_SCAN
+ *                              otherwise. Under FUSED a fixed count up to 8 on the chain form
+ *                              runs as the one-kernel solve, and an early stop on
+ *                              the chain form runs the one-kernel form twice: max_iters
+ *                              iterations with every iterate's residual, then, if an iterate k
+ *                              met tol first, k iterations again, so that the outputs are the
+ *                              iterate the stop returns;
  *  SLSTM_SCHEDULE_LAYERED      three kernels per iteration: (a) residual + Jacobian to HBM in
  *                              the scan_block4 layout, (b) the 4x4 affine scan, (c) the update.
  * Each schedule's results are bitwise reproducible on a given device. */
@@ -138,11 +145,12 @@ size_t slstm_newton_workspace_bytes(int B, int T, int d_h, slstm_schedule schedu
  *  P, P_dtype   gate pre-activations (B, T, 4, d_h), float32 or bf16
  *  R            (4, d_h); state0 (B, 4, d_h) or NULL
  *  states       output (B, T, 4, d_h); also the Newton iterate while solving. May be NULL
- *               when the call resolves to the one-kernel solve (tol = 0, max_iters <= 4,
- *               FUSED_CHAIN, or FUSED where it picks FUSED_CHAIN): that form keeps its iterate
- *               on chip, and h_out and final_state are then the outputs, as in the layer's
- *               default output, the hidden slot ([SL] "Outputs"). NULL for any other form is
- *               SLSTM_EINVAL.
+ *               when the call resolves to the one-kernel solve (unpacked; tol = 0 and
+ *               max_iters <= 4 with FUSED_CHAIN; max_iters <= 8 with FUSED where it picks
+ *               FUSED_CHAIN, with or without a tolerance): that form keeps its
+ *               iterate on chip, and h_out and final_state are then the outputs, as in the
+ *               layer's default output, the hidden slot ([SL] "Outputs"). NULL for any other
+ *               form is SLSTM_EINVAL.
  *  h_out        optional output (B, T, d_h); final_state optional output (B, 4, d_h)
  *  fmode        forget-gate form; max_iters in 1..64; tol >= 0 (0: fixed iteration count)
  *  init         SLSTM_INIT_WARM (default reading) or SLSTM_INIT_ZERO

@@ -140,7 +140,8 @@ bool known_schedule(slstm_schedule s) {
 // 0.73 ms against 1.95 ms.
 constexpr long long kOneKernelMinLaneGroups = 32;
 
-// one_kernel_ok: the call is a fixed-count, unpacked solve that the one-kernel form can run
+// one_kernel_ok: the call is an unpacked solve that the one-kernel form can run (a fixed count
+// up to kPipeMaxIters; under FUSED up to kPipeMaxItersStop, an early stop in two passes)
 Form newton_form(int B, int d, slstm_schedule s, bool one_kernel_ok = false) {
   switch (s) {
     case SLSTM_SCHEDULE_LAYERED: return Form::kLayered;
@@ -175,7 +176,7 @@ NewtonLayout newton_layout(int B, int T, int d, Form form) {
     L.A = L.rhs = 0;
     L.total = align_up(L.S2 + n_state * sizeof(float));
     if (chain)  // the one-kernel solve keeps its words from L.desc on, in place of S2
-      L.total = std::max(L.total, align_up(L.desc + slstm::pipe_desc_words(B, T, d, slstm::kPipeMaxIters) * 8));
+      L.total = std::max(L.total, align_up(L.desc + slstm::pipe_desc_words(B, T, d, slstm::kPipeMaxItersStop) * 8));
   } else {
     const size_t desc_words = std::max(slstm::scan_desc_words(B, T, d, true), slstm::warm_desc_words(B, T, d));
     L.A = align_up(L.desc + desc_words * 8);
@@ -361,10 +362,6 @@ hipError_t iterate(const void* P, bool bf16, const float* R, const float* state0
   return hipSuccess;
 }
 
-// fixed-count solves of the chain form run as one pipelined kernel
-bool pipe_solve(Form form, int max_iters, float tol) {
-  return form == Form::kChain && tol == 0.0f && max_iters <= slstm::kPipeMaxIters;
-}
 
 // control block, the look-back words, then the dR rows and their chunk sums
 struct BackwardLayout {
@@ -507,15 +504,21 @@ slstm_status newton_forward(const void* P, slstm_dtype P_dtype, const float* R, 
     return fail(SLSTM_EINVAL, "workspace must be non-NULL and 256-byte aligned");
   if (seqs.cu != nullptr && schedule == SLSTM_SCHEDULE_FUSED_CHAIN)
     return fail(SLSTM_EINVAL, "packed sequences run the scan and layered forms only (not FUSED_CHAIN)");
-  const bool one_kernel_ok = seqs.cu == nullptr && tol == 0.0f && max_iters <= slstm::kPipeMaxIters;
-  const Form form = seqs.cu != nullptr && schedule == SLSTM_SCHEDULE_FUSED ? Form::kScan
-                                                                          : newton_form(B, d_h, schedule, one_kernel_ok);
-  const bool one_kernel = seqs.cu == nullptr && pipe_solve(form, max_iters, tol);
+  // The one-kernel (pipelined) solve of the chain form: a fixed count up to kPipeMaxIters, and
+  // under FUSED any count up to kPipeMaxItersStop, an early stop as two passes of it
+  const bool fused = schedule == SLSTM_SCHEDULE_FUSED;
+  const bool one_kernel_ok =
+      seqs.cu == nullptr &&
+      (tol == 0.0f ? max_iters <= (fused ? slstm::kPipeMaxItersStop : slstm::kPipeMaxIters)
+                   : fused && max_iters <= slstm::kPipeMaxItersStop);
+  const Form form = seqs.cu != nullptr && fused ? Form::kScan : newton_form(B, d_h, schedule, one_kernel_ok);
+  const bool one_kernel = one_kernel_ok && form == Form::kChain;
+  const bool stop_passes = one_kernel && tol > 0.0f;
   // only the one-kernel solve keeps its iterate on chip; every other form keeps it in `states`
   if (states == nullptr && !one_kernel)
-    return fail(SLSTM_EINVAL, "states may be NULL only for a fixed-count solve (tol = 0, max_iters <= %d) "
-                "that resolves to the one-kernel form (FUSED_CHAIN, or FUSED on enough lanes), unpacked",
-                slstm::kPipeMaxIters);
+    return fail(SLSTM_EINVAL, "states may be NULL only for a solve that resolves to the one-kernel form "
+                "(unpacked; tol = 0 and max_iters <= %d with FUSED_CHAIN; max_iters <= %d with FUSED on "
+                "enough lanes)", slstm::kPipeMaxIters, slstm::kPipeMaxItersStop);
   const NewtonLayout L = newton_layout(B, T, d_h, form);
   if (workspace_bytes < L.total)
     return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
@@ -543,13 +546,23 @@ slstm_status newton_forward(const void* P, slstm_dtype P_dtype, const float* R, 
   unsigned int* tickets = slstm::spread_of(ctl)->ticket[slstm::kTicketTiles][0];
   if (one_kernel) {
     // the whole fixed-count solve in one pass; it writes the states (if asked for), h, the
-    // final state and every residual
-    const uint32_t ep = next_epoch();
-    HIP_TRY(timed(SLSTM_KERNEL_NEWTON_SOLVE, st, [&] {
-      return slstm::launch_newton_pipe(P, bf16, R, state0, states, h_out, final_state, B, T, d_h, cm,
-                                       init == SLSTM_INIT_WARM, max_iters,
-                                       slstm::pipe_tile_steps(B, d_h, device_cus()), desc, tickets, ep, ctl, st);
-    }));
+    // final state and every residual. An early stop runs it for max_iters iterations, finds
+    // the first iterate below tol, and runs it again for that count (skipped on the device when
+    // none is), so the outputs are the iterate the stop returns
+    const int tile = slstm::pipe_tile_steps(B, d_h, device_cus());
+    auto pass = [&](bool k_from_ctl) {
+      const uint32_t ep = next_epoch();
+      return timed(SLSTM_KERNEL_NEWTON_SOLVE, st, [&] {
+        return slstm::launch_newton_pipe(P, bf16, R, state0, states, h_out, final_state, B, T, d_h, cm,
+                                         init == SLSTM_INIT_WARM, max_iters, k_from_ctl, tile, desc, tickets,
+                                         ep, ctl, st);
+      });
+    };
+    HIP_TRY(pass(false));
+    if (stop_passes) {
+      HIP_TRY(slstm::launch_pipe_stop(ctl, max_iters, tol, st));
+      HIP_TRY(pass(true));
+    }
     HIP_TRY(slstm::launch_finalize(ctl, tol, st));
   } else {
     HIP_TRY(iterate(P, bf16, R, state0, states, h_out, B, T, d_h, cm, max_iters, tol, init, form, L,

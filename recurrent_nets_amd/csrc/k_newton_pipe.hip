@@ -51,13 +51,19 @@ __global__ __launch_bounds__(kPipeBlock, pipe_min_waves(TC)) void newton_pipe_ke
     const void* __restrict__ P, const float* __restrict__ R, const float* __restrict__ state0,
     float* __restrict__ S_out, float* __restrict__ h_out, float* __restrict__ fs_out, int T, int d,
     int n_jt, int n_lg,
-    int n_tt, int K, unsigned long long* __restrict__ carry,
+    int n_tt, int K, int k_from_ctl, unsigned long long* __restrict__ carry,
     unsigned int* __restrict__ tickets, int n_ctr, uint32_t epoch, Control* __restrict__ ctl) {
   __shared__ int s_tile[2];
-  __shared__ unsigned int s_err[kPipeMaxIters + 1];  // block residual maxima per iterate
+  __shared__ unsigned int s_err[kPipeMaxItersStop + 1];  // block residual maxima per iterate
+  if (k_from_ctl) {
+    // the second pass of an early-stop solve: the iteration count the stop test chose; nothing
+    // to redo when no iterate met the tolerance (every workgroup leaves before taking a ticket)
+    if (!ctl->stopped) return;
+    K = ctl->iters;
+  }
   const int tid = threadIdx.x;
   if (tid == 0) take_ticket(tickets, n_ctr, n_lg, n_tt, s_tile[0], s_tile[1]);
-  if (tid <= kPipeMaxIters) s_err[tid] = 0u;
+  if (tid <= kPipeMaxItersStop) s_err[tid] = 0u;
   __syncthreads();
   const int tt = __builtin_amdgcn_readfirstlane(s_tile[0]);
   const int lg = __builtin_amdgcn_readfirstlane(s_tile[1]);
@@ -270,19 +276,20 @@ size_t pipe_desc_words(int B, int T, int d, int K) {
 
 hipError_t launch_newton_pipe(const void* P, bool p_bf16, const float* R, const float* state0,
                               float* S_out, float* h_out, float* fs_out, int B, int T, int d, int cell_mode,
-                              bool warm, int K, int tile_steps, unsigned long long* carry,
+                              bool warm, int K, bool k_from_ctl, int tile_steps, unsigned long long* carry,
                               unsigned int* tickets, uint32_t epoch, Control* ctl, hipStream_t stream) {
   if (tile_steps != kPipeStepsShort && tile_steps != kPipeStepsLong) return hipErrorInvalidValue;
   i64 n_jt, n_lg, n_tt;
   pipe_grid(B, T, d, tile_steps, n_jt, n_lg, n_tt);
   const i64 blocks = n_lg * n_tt;
-  if (blocks > 0x7fffffffLL || K < 1 || K > kPipeMaxIters) return hipErrorInvalidValue;
+  if (blocks > 0x7fffffffLL || K < 1 || K > kPipeMaxItersStop) return hipErrorInvalidValue;
+  const int kc = k_from_ctl ? 1 : 0;
   const int n_ctr = ticket_counters(n_lg);
   const dim3 grid(static_cast<unsigned>(blocks));
   const int a = static_cast<int>(n_jt), c = static_cast<int>(n_lg), e = static_cast<int>(n_tt);
 #define SLSTM_PIPE_LAUNCH_TC(BF, WM, CM_, TC_)                                                         \
   newton_pipe_kernel<BF, WM, CM_, TC_><<<grid, kPipeBlock, 0, stream>>>(P, R, state0, S_out, h_out, fs_out, T, d, \
-                                                                        a, c, e, K, carry, tickets, n_ctr,   \
+                                                                        a, c, e, K, kc, carry, tickets, n_ctr, \
                                                                         epoch, ctl)
 #define SLSTM_PIPE_LAUNCH(BF, WM, CM_)                                                    \
   if (tile_steps == kPipeStepsShort) {                                                    \
@@ -307,6 +314,28 @@ hipError_t launch_newton_pipe(const void* P, bool p_bf16, const float* R, const 
 #undef SLSTM_PIPE_FF
 #undef SLSTM_PIPE_LAUNCH
 #undef SLSTM_PIPE_LAUNCH_TC
+  return hipGetLastError();
+}
+
+// The stop test of an early-stop solve run as two one-kernel passes: after the first pass (a
+// fixed count of K iterations, every iterate's residual maximum in the spread slots), the first
+// iterate k < K whose max|F| is below tol is where the per-iteration solve would have stopped
+// before solving; it is recorded as the stop and the iteration count for the second pass.
+__global__ __launch_bounds__(kWave) void pipe_stop_kernel(Control* __restrict__ ctl, int K, float tol) {
+  for (int k = 0; k < K; ++k) {
+    const float e = err_reduced(ctl, k);  // the whole wave takes part
+    if (e < tol) {
+      if (threadIdx.x == 0) {
+        ctl->stopped = 1;
+        ctl->iters = k;
+      }
+      return;
+    }
+  }
+}
+
+hipError_t launch_pipe_stop(Control* ctl, int K, float tol, hipStream_t stream) {
+  pipe_stop_kernel<<<1, kWave, 0, stream>>>(ctl, K, tol);
   return hipGetLastError();
 }
 

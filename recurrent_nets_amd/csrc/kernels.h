@@ -42,11 +42,15 @@ hipError_t launch_newton_chain(const void* P, bool p_bf16, const float* R, const
 // a whole fixed-count solve of the chain form in one pipelined pass (warm or zero initial
 // iterate, 1 <= K <= kPipeMaxIters iterations, final residual and h); writes S_K to S_out
 constexpr int kPipeMaxIters = 4;
+// an early-stop solve (tol > 0) of at most this many iterations runs as two one-kernel passes:
+// K iterations with every iterate's residual maximum, the stop test, then the count it chose
+constexpr int kPipeMaxItersStop = 8;
 size_t pipe_desc_words(int B, int T, int d, int K);
 hipError_t launch_newton_pipe(const void* P, bool p_bf16, const float* R, const float* state0,
                               float* S_out, float* h_out, float* fs_out, int B, int T, int d, int cell_mode,
-                              bool warm, int K, int tile_steps, unsigned long long* carry,
+                              bool warm, int K, bool k_from_ctl, int tile_steps, unsigned long long* carry,
                               unsigned int* tickets, uint32_t epoch, Control* ctl, hipStream_t stream);
+hipError_t launch_pipe_stop(Control* ctl, int K, float tol, hipStream_t stream);
 // steps per tile of the one-kernel solve for a shape on a GPU of n_cus compute units
 int pipe_tile_steps(int B, int d, int n_cus);
 // after the last chain iteration: declares iterate k final when its residual met tol

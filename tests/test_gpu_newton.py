@@ -333,3 +333,59 @@ def test_sequential_hidden_only_output(gpu_lib, p_dtype):
     torch.cuda.synchronize()
     assert Sb is None
     assert torch.equal(ha, hb) and torch.equal(fa, fb) and torch.equal(fa, Sa[:, -1])
+
+
+def test_early_stop_as_two_one_kernel_passes(gpu_lib):
+    """FUSED on 32 lane groups with a tolerance runs the one-kernel solve for the budget, finds
+    the first iterate below tol and runs it again for that count. Iteration count, flags, every
+    residual maximum, h and the final state equal, bit for bit, those of the per-iteration chain
+    kernels with the same early stop (the stop landing before, at and past the budget, and no
+    stop), and match the oracle; with no state tensor the same h and final state come out."""
+    w = by_name("sigmoid_bf16p_b16_t4096_d1024")
+    inp = draw_preactivation_inputs(w, B=32, T=256)
+    P = inp["P"][..., :256].contiguous()
+    R = inp["R"][:, :256].contiguous()
+    n = ref.newton(to_np(P), to_np(R), None, w.forget, 8, tol=w.tol)[1].iters
+    assert 2 <= n < 8
+    Pd, Rd = P.to(DEV), R.to(DEV)
+    for K in sorted({n - 1, n, n + 1, 8}):
+        case(f"early stop at {n} as two one-kernel passes, budget K={K}")
+        gpu_lib.profile_reset()
+        gpu_lib.profile_enable(True)
+        fa = torch.empty(32, 4, 256, device=DEV)
+        Sa, ha, sta = gpu_lib.newton_forward(Pd, Rd, None, w.forget, K, w.tol, final_state=fa,
+                                             raise_on_divergence=False, schedule="fused")
+        n_solve = len(gpu_lib.profile_durations("newton_solve"))
+        n_iter = len(gpu_lib.profile_durations("newton_iteration"))
+        gpu_lib.profile_enable(False)
+        fb = torch.empty(32, 4, 256, device=DEV)
+        Sb, hb, stb = gpu_lib.newton_forward(Pd, Rd, None, w.forget, K, w.tol, final_state=fb,
+                                             raise_on_divergence=False, schedule="fused_chain")
+        fc = torch.empty(32, 4, 256, device=DEV)
+        _, hc, stc = gpu_lib.newton_forward(Pd, Rd, None, w.forget, K, w.tol, final_state=fc,
+                                            raise_on_divergence=False, schedule="fused", output_states=False)
+        torch.cuda.synchronize()
+        assert n_solve == 2 and n_iter == 0  # both passes of the one-kernel form, no iteration kernels
+        for st in (sta, stc):
+            assert (st.iters, st.converged, st.diverged, st.nonfinite) == \
+                (stb.iters, stb.converged, stb.diverged, stb.nonfinite)
+            assert np.array_equal(np.array(st.max_abs_F), np.array(stb.max_abs_F))
+        assert torch.equal(ha, hb) and torch.equal(hc, hb) and torch.equal(Sa, Sb)
+        assert torch.equal(fa, fb) and torch.equal(fc, fb)
+        S_ref, st_ref = ref.newton(to_np(P), to_np(R), None, w.forget, K, tol=w.tol)
+        assert sta.iters == st_ref.iters == min(n, K) and sta.converged == st_ref.converged
+        assert h_rel_err(ha, S_ref[..., 3, :]) < H_TOL_BF16
+    # a fixed count past the single-pass limit of FUSED_CHAIN (4) but within FUSED's (8): one
+    # launch of the one-kernel form, bitwise the per-iteration chain kernels
+    case("fused fixed count K=6 as one kernel")
+    gpu_lib.profile_reset()
+    gpu_lib.profile_enable(True)
+    Sa, ha, sta = gpu_lib.newton_forward(Pd, Rd, None, w.forget, 6, 0.0, raise_on_divergence=False, schedule="fused")
+    n_solve = len(gpu_lib.profile_durations("newton_solve"))
+    gpu_lib.profile_enable(False)
+    Sb, hb, stb = gpu_lib.newton_forward(Pd, Rd, None, w.forget, 6, 0.0, raise_on_divergence=False,
+                                         schedule="fused_chain")
+    torch.cuda.synchronize()
+    assert n_solve == 1 and sta.iters == stb.iters == 6
+    assert np.array_equal(np.array(sta.max_abs_F), np.array(stb.max_abs_F))
+    assert torch.equal(ha, hb) and torch.equal(Sa, Sb)
