@@ -193,6 +193,11 @@ NewtonLayout newton_layout(int B, int T, int d, Form form) {
 
 // whether a pack of n_seqs sequences over T steps fits the aligned tiles of the scan-form
 // iteration (at most one tile per sequence beyond the row's own count)
+// whether the one-kernel solve's tiles of `steps` steps, aligned to the sequences, fit the table
+bool pipe_aligned_fit(int T, int n_seqs, int steps) {
+  return (T + steps - 1) / steps + static_cast<long long>(n_seqs) <= slstm::fused_aligned_cap(T);
+}
+
 bool aligned_tiles_fit(int T, int n_seqs) {
   const long long steps = slstm::fused_aligned_steps();
   return (T + steps - 1) / steps + static_cast<long long>(n_seqs) <= slstm::fused_aligned_cap(T);
@@ -507,18 +512,23 @@ slstm_status newton_forward(const void* P, slstm_dtype P_dtype, const float* R, 
   // The one-kernel (pipelined) solve of the chain form: a fixed count up to kPipeMaxIters, and
   // under FUSED any count up to kPipeMaxItersStop, an early stop as two passes of it
   const bool fused = schedule == SLSTM_SCHEDULE_FUSED;
-  const bool one_kernel_ok =
-      seqs.cu == nullptr &&
-      (tol == 0.0f ? max_iters <= (fused ? slstm::kPipeMaxItersStop : slstm::kPipeMaxIters)
-                   : fused && max_iters <= slstm::kPipeMaxItersStop);
-  const Form form = seqs.cu != nullptr && fused ? Form::kScan : newton_form(B, d_h, schedule, one_kernel_ok);
-  const bool one_kernel = one_kernel_ok && form == Form::kChain;
+  const bool count_ok = tol == 0.0f ? max_iters <= (fused ? slstm::kPipeMaxItersStop : slstm::kPipeMaxIters)
+                                    : fused && max_iters <= slstm::kPipeMaxItersStop;
+  const bool one_kernel_ok = seqs.cu == nullptr && count_ok;
+  // A packed row under FUSED runs it on tiles aligned to the sequence starts when the tile table
+  // holds them and the sequences give enough chains (each lane group of each sequence is one)
+  const int pipe_tile = slstm::pipe_tile_steps(B, d_h, device_cus());
+  const bool packed_pipe = seqs.cu != nullptr && fused && count_ok && B == 1 && pipe_aligned_fit(T, seqs.n, pipe_tile) &&
+                           slstm::chain_lane_groups(B, d_h) * seqs.n >= kOneKernelMinLaneGroups;
+  const Form form = packed_pipe ? Form::kChain
+                                : (seqs.cu != nullptr && fused ? Form::kScan : newton_form(B, d_h, schedule, one_kernel_ok));
+  const bool one_kernel = (one_kernel_ok && form == Form::kChain) || packed_pipe;
   const bool stop_passes = one_kernel && tol > 0.0f;
   // only the one-kernel solve keeps its iterate on chip; every other form keeps it in `states`
   if (states == nullptr && !one_kernel)
     return fail(SLSTM_EINVAL, "states may be NULL only for a solve that resolves to the one-kernel form "
-                "(unpacked; tol = 0 and max_iters <= %d with FUSED_CHAIN; max_iters <= %d with FUSED on "
-                "enough lanes)", slstm::kPipeMaxIters, slstm::kPipeMaxItersStop);
+                "(tol = 0 and max_iters <= %d with FUSED_CHAIN, unpacked; max_iters <= %d with FUSED on "
+                "enough lanes or sequences)", slstm::kPipeMaxIters, slstm::kPipeMaxItersStop);
   const NewtonLayout L = newton_layout(B, T, d_h, form);
   if (workspace_bytes < L.total)
     return fail(SLSTM_EWORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, L.total);
@@ -535,7 +545,13 @@ slstm_status newton_forward(const void* P, slstm_dtype P_dtype, const float* R, 
     int* tab = at<int>(workspace, L.tab);
     HIP_TRY(slstm::launch_seq_table(seqs.cu, seqs.n, T, tab, st));
     seqs.tab = tab;
-    if (form == Form::kScan && aligned_tiles_fit(T, seqs.n)) {
+    if (packed_pipe) {
+      // the one-kernel solve's tiles aligned to the sequences, of its own length
+      int* tiles = at<int>(workspace, L.tiles);
+      seqs.tile_cap = slstm::fused_aligned_cap(T);
+      HIP_TRY(slstm::launch_aligned_tiles(seqs.cu, seqs.n, T, pipe_tile, seqs.tile_cap, tiles, st));
+      seqs.tiles = tiles;
+    } else if (form == Form::kScan && aligned_tiles_fit(T, seqs.n)) {
       // the scan-form iterations on tiles aligned to the sequences
       int* tiles = at<int>(workspace, L.tiles);
       seqs.tile_cap = slstm::fused_aligned_cap(T);
@@ -549,13 +565,13 @@ slstm_status newton_forward(const void* P, slstm_dtype P_dtype, const float* R, 
     // final state and every residual. An early stop runs it for max_iters iterations, finds
     // the first iterate below tol, and runs it again for that count (skipped on the device when
     // none is), so the outputs are the iterate the stop returns
-    const int tile = slstm::pipe_tile_steps(B, d_h, device_cus());
     auto pass = [&](bool k_from_ctl) {
       const uint32_t ep = next_epoch();
       return timed(SLSTM_KERNEL_NEWTON_SOLVE, st, [&] {
         return slstm::launch_newton_pipe(P, bf16, R, state0, states, h_out, final_state, B, T, d_h, cm,
-                                         init == SLSTM_INIT_WARM, max_iters, k_from_ctl, tile, desc, tickets,
-                                         ep, ctl, st);
+                                         init == SLSTM_INIT_WARM, max_iters, k_from_ctl, pipe_tile, desc,
+                                         tickets, ep, ctl, packed_pipe ? seqs.tiles : nullptr,
+                                         packed_pipe ? seqs.tile_cap : 0, st);
       });
     };
     HIP_TRY(pass(false));
@@ -564,6 +580,8 @@ slstm_status newton_forward(const void* P, slstm_dtype P_dtype, const float* R, 
       HIP_TRY(pass(true));
     }
     HIP_TRY(slstm::launch_finalize(ctl, tol, st));
+    if (packed_pipe && final_state != nullptr)  // sequences without steps keep their state0
+      HIP_TRY(slstm::launch_empty_seq_final(seqs.cu, seqs.n, T, state0, final_state, d_h, st));
   } else {
     HIP_TRY(iterate(P, bf16, R, state0, states, h_out, B, T, d_h, cm, max_iters, tol, init, form, L,
                     workspace, ctl, tickets, st, seqs));
@@ -749,9 +767,12 @@ const char* slstm_last_error(void) { return g_err; }
 size_t slstm_newton_workspace_bytes(int B, int T, int d_h, slstm_schedule schedule) {
   if (check_dims(B, T, d_h) != SLSTM_OK) return 0;
   if (!known_schedule(schedule)) return 0;
-  // FUSED may resolve differently for fixed-count solves: room for either form
-  return std::max(newton_layout(B, T, d_h, newton_form(B, d_h, schedule, false)).total,
-                  newton_layout(B, T, d_h, newton_form(B, d_h, schedule, true)).total);
+  // FUSED may resolve differently by iteration count and tolerance, and a packed row (B = 1) may
+  // take the chain form's one-kernel solve whatever its lanes: room for each form it can pick
+  size_t need = std::max(newton_layout(B, T, d_h, newton_form(B, d_h, schedule, false)).total,
+                         newton_layout(B, T, d_h, newton_form(B, d_h, schedule, true)).total);
+  if (schedule == SLSTM_SCHEDULE_FUSED && B == 1) need = std::max(need, newton_layout(B, T, d_h, Form::kChain).total);
+  return need;
 }
 
 slstm_status slstm_newton_forward(const void* P, slstm_dtype P_dtype, const float* R,

@@ -24,8 +24,12 @@
 //
 // Waits follow tickets as in the other look-back kernels: a tile waits only on tile tt-1 of
 // the same lanes, which holds an earlier ticket of the same counter and never waits on tile
-// tt. There is no early stop: the residual maxima of every iterate go to the spread slots, and
-// the solver uses this kernel only for a fixed iteration count.
+// tt. There is no early stop inside a launch: the residual maxima of every iterate go to the
+// spread slots, and an early stop runs the kernel twice (the budget, then the count the stop
+// test chose, read from the control block). Packed sequences (one batch row) run on tiles
+// aligned to the sequence starts, from the table of the aligned scan-form tiles: a tile at a
+// sequence start begins from that sequence's state0 and waits on nothing, so the sequences'
+// chains advance side by side.
 #include "cell.h"
 #include "kernels.h"
 
@@ -52,7 +56,8 @@ __global__ __launch_bounds__(kPipeBlock, pipe_min_waves(TC)) void newton_pipe_ke
     float* __restrict__ S_out, float* __restrict__ h_out, float* __restrict__ fs_out, int T, int d,
     int n_jt, int n_lg,
     int n_tt, int K, int k_from_ctl, unsigned long long* __restrict__ carry,
-    unsigned int* __restrict__ tickets, int n_ctr, uint32_t epoch, Control* __restrict__ ctl) {
+    unsigned int* __restrict__ tickets, int n_ctr, uint32_t epoch, Control* __restrict__ ctl,
+    const int* __restrict__ tiles, int tile_cap) {
   __shared__ int s_tile[2];
   __shared__ unsigned int s_err[kPipeMaxItersStop + 1];  // block residual maxima per iterate
   if (k_from_ctl) {
@@ -69,13 +74,37 @@ __global__ __launch_bounds__(kPipeBlock, pipe_min_waves(TC)) void newton_pipe_ke
   const int lg = __builtin_amdgcn_readfirstlane(s_tile[1]);
   const int b = lg / n_jt;
   const int jt = lg - b * n_jt;
+  // The tile: its words' index, its predecessor's, its first step, the end of its sequence (or
+  // of the row), whether it starts that sequence and which sequence it is. Packed sequences take
+  // tiles aligned to their starts from a table (one batch row; slots ordered by position, then
+  // sequence, so a tile's predecessor, the id before it, holds an earlier ticket).
+  int wid = tt, pred = tt - 1, t0 = tt * TC, t_end = T, seq = b;
+  bool first = tt == 0, has_next = tt + 1 < n_tt;
+  if (tiles != nullptr) {
+    const int n_real = __builtin_amdgcn_readfirstlane(tiles[0]);
+    if (tt >= n_real) {  // a ticket past the last tile
+      if (blockIdx.x == 0 && tid == 0) ctl->iters = K;
+      return;
+    }
+    const int id = __builtin_amdgcn_readfirstlane(tiles[1 + tt]);
+    const int sq = __builtin_amdgcn_readfirstlane(tiles[1 + tile_cap + tt]);
+    const int ps = __builtin_amdgcn_readfirstlane(tiles[1 + 2 * tile_cap + tt]);
+    const int a0 = __builtin_amdgcn_readfirstlane(tiles[1 + 3 * tile_cap + tt]);
+    const int e0 = __builtin_amdgcn_readfirstlane(tiles[1 + 4 * tile_cap + tt]);
+    wid = id;
+    pred = id - 1;
+    t0 = a0 + ps * TC;
+    t_end = e0;
+    seq = sq;
+    first = ps == 0;
+    has_next = t0 + TC < e0;
+  }
 
   const unsigned ud = static_cast<unsigned>(d);
   const unsigned j = static_cast<unsigned>(jt * kPipeBlock + tid);
   const bool valid = j < ud;
-  const int t0 = tt * TC;
-  const bool publish = valid && tt + 1 < n_tt;  // the tile after waits on these words
-  const bool wait = valid && tt > 0;
+  const bool publish = valid && has_next;  // the tile after waits on these words
+  const bool wait = valid && !first;
   const int W = pipe_words(K);
   const i64 n_lanes = static_cast<i64>(n_lg) * kPipeBlock;
   const i64 lane = static_cast<i64>(lg) * kPipeBlock + tid;
@@ -83,8 +112,8 @@ __global__ __launch_bounds__(kPipeBlock, pipe_min_waves(TC)) void newton_pipe_ke
   auto wait_words = [&](int w0, float v[4]) {
     bool ok = false;
     while (true) {
-      ok = tag_load(word(tt - 1, w0), epoch, v[0]) & tag_load(word(tt - 1, w0 + 1), epoch, v[1]) &
-           tag_load(word(tt - 1, w0 + 2), epoch, v[2]) & tag_load(word(tt - 1, w0 + 3), epoch, v[3]);
+      ok = tag_load(word(pred, w0), epoch, v[0]) & tag_load(word(pred, w0 + 1), epoch, v[1]) &
+           tag_load(word(pred, w0 + 2), epoch, v[2]) & tag_load(word(pred, w0 + 3), epoch, v[3]);
       if (ok) break;
       poll_pause();
     }
@@ -96,11 +125,11 @@ __global__ __launch_bounds__(kPipeBlock, pipe_min_waves(TC)) void newton_pipe_ke
   const i64 tile_row = (static_cast<i64>(b) * T + t0) * 4 * static_cast<i64>(d);
   const rsrc_t rsP = make_rsrc(static_cast<const char*>(P) + tile_row * (BF16 ? 2 : 4));
   // lane part j in the vector offset, step and gate parts in the scalar offset; lanes past d_h
-  // and steps past T read the last feature and step (every load in bounds, no zero fill): what
-  // they compute is never counted, stored or published
+  // and steps past the tile's end read the last feature and step (every load in bounds, no zero
+  // fill): what they compute is never counted, stored or published
   float p[TC][4];
   const unsigned jc = valid ? j : ud - 1u;
-  const int u_last = T - 1 - t0;
+  const int u_last = t_end - 1 - t0;
 #pragma unroll
   for (int u = 0; u < TC; ++u) {
     const unsigned uc = static_cast<unsigned>(u < u_last ? u : u_last);
@@ -117,8 +146,8 @@ __global__ __launch_bounds__(kPipeBlock, pipe_min_waves(TC)) void newton_pipe_ke
     ri = R[ud + j];
     rf = R[2 * ud + j];
     ro = R[3 * ud + j];
-    if (tt == 0 && state0 != nullptr) {
-      const float* s0 = state0 + static_cast<i64>(b) * 4 * static_cast<i64>(d);
+    if (first && state0 != nullptr) {
+      const float* s0 = state0 + static_cast<i64>(seq) * 4 * static_cast<i64>(d);
 #pragma unroll
       for (int k = 0; k < 4; ++k) hv[k] = s0[k * ud + j];
     }
@@ -152,7 +181,7 @@ __global__ __launch_bounds__(kPipeBlock, pipe_min_waves(TC)) void newton_pipe_ke
     }
     if (publish) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) tag_store(word(tt, e), s[TC - 1][e], epoch);
+      for (int e = 0; e < 4; ++e) tag_store(word(wid, e), s[TC - 1][e], epoch);
     }
   } else {
     // zero initial iterate: the state before the tile is zero too, except state0 before t = 0
@@ -174,7 +203,7 @@ __global__ __launch_bounds__(kPipeBlock, pipe_min_waves(TC)) void newton_pipe_ke
 #pragma unroll
       for (int u = 0; u < TC; ++u) {
         const int t = t0 + u;
-        if (t < T) {
+        if (t < t_end) {
           float f[4], r[4];
           DiagLin L;
           const CellIn pv = u == 0 ? pv0 : CellIn{s[u - 1][0], s[u - 1][1], s[u - 1][2], s[u - 1][3]};
@@ -193,7 +222,7 @@ __global__ __launch_bounds__(kPipeBlock, pipe_min_waves(TC)) void newton_pipe_ke
 #pragma unroll
             for (int e = 0; e < 4; ++e) hv[e] = hv[e] + x[e];
           }
-          if (u == 0 && tt == 0) {  // t = 0
+          if (u == 0 && first) {  // the first step of the sequence
 #pragma unroll
             for (int e = 0; e < 4; ++e) x[e] = r[e];  // s_0 is data: Delta_1 = rhs_1
           } else {
@@ -202,20 +231,20 @@ __global__ __launch_bounds__(kPipeBlock, pipe_min_waves(TC)) void newton_pipe_ke
         }
       }
       // the update of the tile's last step
-      if (t0 + TC <= T) {
+      if (t0 + TC <= t_end) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) s[TC - 1][e] = s[TC - 1][e] + x[e];
       } else {
 #pragma unroll
         for (int u = 0; u < TC - 1; ++u)
-          if (u == T - 1 - t0) {
+          if (u == t_end - 1 - t0) {
 #pragma unroll
             for (int e = 0; e < 4; ++e) s[u][e] = s[u][e] + x[e];
           }
       }
       if (publish) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) tag_store(word(tt, 4 + 4 * k + e), x[e], epoch);
+        for (int e = 0; e < 4; ++e) tag_store(word(wid, 4 + 4 * k + e), x[e], epoch);
       }
     }
     const unsigned int wm = wave_max_u32(res_max2_bits(fmax));
@@ -231,7 +260,7 @@ __global__ __launch_bounds__(kPipeBlock, pipe_min_waves(TC)) void newton_pipe_ke
     CellIn pv = {hv[0], hv[1], hv[2], hv[3]};
 #pragma unroll
     for (int u = 0; u < TC; ++u) {
-      if (t0 + u < T) {
+      if (t0 + u < t_end) {
         float f[4];
         cell_step<false, true>(pv, p[u][0], p[u][1], p[u][2], p[u][3], rz, ri, rf, ro, sig, floored, f, nullptr);
         res_max2(fmax, s[u][0] - f[0], s[u][1] - f[1]);
@@ -241,8 +270,8 @@ __global__ __launch_bounds__(kPipeBlock, pipe_min_waves(TC)) void newton_pipe_ke
           for (int e = 0; e < 4; ++e) buf_st(s[u][e], rsO, 4u * j, 4u * (4u * u + e) * ud);
         }
         if (h_out != nullptr) buf_st(s[u][3], rsH, 4u * j, 4u * u * ud);
-        if (fs_out != nullptr && t0 + u == T - 1) {
-          float* fs = fs_out + static_cast<i64>(b) * 4 * static_cast<i64>(d) + j;
+        if (fs_out != nullptr && t0 + u == t_end - 1) {  // the last step of the row or sequence
+          float* fs = fs_out + static_cast<i64>(seq) * 4 * static_cast<i64>(d) + j;
 #pragma unroll
           for (int e = 0; e < 4; ++e) fs[e * ud] = s[u][e];
         }
@@ -277,10 +306,15 @@ size_t pipe_desc_words(int B, int T, int d, int K) {
 hipError_t launch_newton_pipe(const void* P, bool p_bf16, const float* R, const float* state0,
                               float* S_out, float* h_out, float* fs_out, int B, int T, int d, int cell_mode,
                               bool warm, int K, bool k_from_ctl, int tile_steps, unsigned long long* carry,
-                              unsigned int* tickets, uint32_t epoch, Control* ctl, hipStream_t stream) {
+                              unsigned int* tickets, uint32_t epoch, Control* ctl, const int* tiles,
+                              int tile_cap, hipStream_t stream) {
   if (tile_steps != kPipeStepsShort && tile_steps != kPipeStepsLong) return hipErrorInvalidValue;
   i64 n_jt, n_lg, n_tt;
   pipe_grid(B, T, d, tile_steps, n_jt, n_lg, n_tt);
+  if (tiles != nullptr) {  // aligned tiles of one packed row: a ticket per table slot
+    if (B != 1 || tile_cap < 1) return hipErrorInvalidValue;
+    n_tt = tile_cap;
+  }
   const i64 blocks = n_lg * n_tt;
   if (blocks > 0x7fffffffLL || K < 1 || K > kPipeMaxItersStop) return hipErrorInvalidValue;
   const int kc = k_from_ctl ? 1 : 0;
@@ -290,7 +324,7 @@ hipError_t launch_newton_pipe(const void* P, bool p_bf16, const float* R, const 
 #define SLSTM_PIPE_LAUNCH_TC(BF, WM, CM_, TC_)                                                         \
   newton_pipe_kernel<BF, WM, CM_, TC_><<<grid, kPipeBlock, 0, stream>>>(P, R, state0, S_out, h_out, fs_out, T, d, \
                                                                         a, c, e, K, kc, carry, tickets, n_ctr, \
-                                                                        epoch, ctl)
+                                                                        epoch, ctl, tiles, tile_cap)
 #define SLSTM_PIPE_LAUNCH(BF, WM, CM_)                                                    \
   if (tile_steps == kPipeStepsShort) {                                                    \
     SLSTM_PIPE_LAUNCH_TC(BF, WM, CM_, kPipeStepsShort);                                   \
@@ -332,6 +366,31 @@ __global__ __launch_bounds__(kWave) void pipe_stop_kernel(Control* __restrict__ 
       return;
     }
   }
+}
+
+// the one-kernel solve writes each sequence's final state at its last step; an empty sequence
+// has none, and its final state is its state0 (zeros without one); cu is read within its
+// n_seqs + 1 entries
+__global__ __launch_bounds__(256) void empty_seq_final_kernel(const int* __restrict__ cu, int n_seqs, int T,
+                                                              const float* __restrict__ state0,
+                                                              float* __restrict__ out, int d) {
+  const i64 n = static_cast<i64>(n_seqs) * 4 * d;  // (s, slot, j)
+  for (i64 i = static_cast<i64>(blockIdx.x) * 256 + threadIdx.x; i < n; i += static_cast<i64>(gridDim.x) * 256) {
+    const int s = static_cast<int>(i / (4 * static_cast<i64>(d)));
+    // offsets clamped as the tile table clamps them: a sequence with no steps has no tile
+    const int a = min(max(cu[s], 0), T);
+    const int e = min(max(cu[s + 1], a), T);
+    if (e == a) out[i] = state0 != nullptr ? state0[i] : 0.0f;
+  }
+}
+
+hipError_t launch_empty_seq_final(const int* cu, int n_seqs, int T, const float* state0, float* final_state, int d,
+                                  hipStream_t stream) {
+  const i64 n = static_cast<i64>(n_seqs) * 4 * d;
+  if (n <= 0) return hipSuccess;
+  const i64 blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+  empty_seq_final_kernel<<<dim3(static_cast<unsigned>(blocks)), 256, 0, stream>>>(cu, n_seqs, T, state0, final_state, d);
+  return hipGetLastError();
 }
 
 hipError_t launch_pipe_stop(Control* ctl, int K, float tol, hipStream_t stream) {

@@ -49,7 +49,11 @@ size_t pipe_desc_words(int B, int T, int d, int K);
 hipError_t launch_newton_pipe(const void* P, bool p_bf16, const float* R, const float* state0,
                               float* S_out, float* h_out, float* fs_out, int B, int T, int d, int cell_mode,
                               bool warm, int K, bool k_from_ctl, int tile_steps, unsigned long long* carry,
-                              unsigned int* tickets, uint32_t epoch, Control* ctl, hipStream_t stream);
+                              unsigned int* tickets, uint32_t epoch, Control* ctl, const int* tiles,
+                              int tile_cap, hipStream_t stream);
+// final states of the empty sequences of a pack: state0, or zeros without one
+hipError_t launch_empty_seq_final(const int* cu, int n_seqs, int T, const float* state0, float* final_state, int d,
+                                  hipStream_t stream);
 hipError_t launch_pipe_stop(Control* ctl, int K, float tol, hipStream_t stream);
 // steps per tile of the one-kernel solve for a shape on a GPU of n_cus compute units
 int pipe_tile_steps(int B, int d, int n_cus);

@@ -273,8 +273,10 @@ def newton_forward(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, init="
     1e-6)); every function taking ``forget`` takes it too.
 
     ``cu_seqlens`` (S + 1 offsets) packs S sequences end to end along time in P (1, T, 4, d_h):
-    state0 and final_state are then (S, 4, d_h), and "fused" means "fused_scan" ("fused_chain"
-    is rejected); sequential_forward, warm_start and backward take it the same way."""
+    state0 and final_state are then (S, 4, d_h); "fused" runs the one-kernel solve on tiles
+    aligned to the sequences where it can (up to 8 iterations; enough sequences), else
+    "fused_scan" ("fused_chain" is rejected); sequential_forward, warm_start and backward take
+    it the same way."""
     L = load()
     _dev(P, "P", (torch.float32, torch.bfloat16))
     _dev(R, "R", (torch.float32,))
@@ -289,8 +291,7 @@ def newton_forward(P, R, state0=None, forget="exp", max_iters=3, tol=0.0, init="
     _dev(h_out, "h_out", (torch.float32,))
     _dev(final_state, "final_state", (torch.float32,))
     _shape(final_state, "final_state", (B if cu is None else S, 4, d))
-    sched = SCHEDULE["fused_scan" if cu is not None and schedule == "fused" else schedule]
-    need = L.slstm_newton_workspace_bytes(B, T, d, sched)
+    need = L.slstm_newton_workspace_bytes(B, T, d, SCHEDULE[schedule])
     if workspace is None:
         workspace = alloc_workspace(need, P.device)
     st = _Stats() if stats else None

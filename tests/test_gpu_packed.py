@@ -303,3 +303,64 @@ def test_packed_workload_full_size_backward(gpu_lib):
             grad_rel_err(ds0[..., jt], ds0_ref, keep)]
     print(f"full-size packed backward: rel err dP dR dstate0 {['%.2e' % e for e in errs]}, kept {keep.sum()}")
     assert max(errs) < GRAD_TOL
+
+
+# lengths around the one-kernel solve's 24-step aligned tiles, empties and single steps, enough
+# sequences for its chains (two lane groups of 256 features times 40 sequences)
+PIPE_LENGTHS = [24, 0, 25, 23, 1, 48, 0, 72, 2, 49, 95, 1, 300, 7, 120, 0, 24, 200, 33, 3,
+                96, 17, 0, 250, 64, 1, 47, 180, 5, 90, 26, 140, 0, 71, 9, 160, 24, 13, 110, 55]
+
+
+@pytest.mark.parametrize("forget", ["exp", "sigmoid"])
+@pytest.mark.parametrize("K", [3, 6])
+def test_packed_one_kernel_solve(gpu_lib, forget, K):
+    """FUSED on a pack with enough sequences runs the one-kernel solve on tiles aligned to the
+    sequence starts: h, each sequence's final state (state0 for the empty ones), the iteration
+    count and the flags match the oracle; without the state tensor h and the final states are
+    bitwise the same."""
+    P, R, s0, cu = _problem(870 + K, PIPE_LENGTHS, 300, forget)
+    case(f"packed one-kernel solve {forget} K={K} T={P.shape[1]} S={len(PIPE_LENGTHS)}")
+    Pd, Rd, s0d = _dev(P, R, s0)
+    fin = torch.empty_like(s0).to(DEV)
+    gpu_lib.profile_reset()
+    gpu_lib.profile_enable(True)
+    S, h, st = gpu_lib.newton_forward(Pd, Rd, s0d, forget, K, 0.0, final_state=fin, raise_on_divergence=False,
+                                      schedule="fused", cu_seqlens=cu)
+    n_solve = len(gpu_lib.profile_durations("newton_solve"))
+    n_iter = len(gpu_lib.profile_durations("newton_iteration"))
+    gpu_lib.profile_enable(False)
+    fin2 = torch.full_like(fin, float("nan"))
+    S2, h2, st2 = gpu_lib.newton_forward(Pd, Rd, s0d, forget, K, 0.0, final_state=fin2, raise_on_divergence=False,
+                                         schedule="fused", cu_seqlens=cu, output_states=False)
+    torch.cuda.synchronize()
+    assert n_solve == 1 and n_iter == 0
+    assert S2 is None and torch.equal(h, h2) and torch.equal(fin, fin2)
+    assert np.array_equal(np.array(st.max_abs_F), np.array(st2.max_abs_F))
+    S_ref, st_ref = ref.newton(to_np(P), to_np(R), to_np(s0), forget, K, cu_seqlens=cu)
+    err = h_rel_err(h, S_ref[..., 3, :], h_floor(forget, H_TOL_F32))
+    print(f"packed one-kernel {forget} K={K}: h rel err {err:.2e}")
+    assert err < H_TOL_F32
+    assert _state_err(S, S_ref) < 1e-4
+    assert st.iters == st_ref.iters and st.diverged == st_ref.diverged
+    assert _state_err(fin, ref.final_states(S_ref, to_np(s0), cu)) < 1e-4
+    for s in range(len(PIPE_LENGTHS)):
+        if cu[s] == cu[s + 1]:
+            assert torch.equal(fin[s].cpu(), s0[s])
+
+
+def test_packed_one_kernel_early_stop(gpu_lib):
+    """The early stop on a pack as two one-kernel passes: the stop is global, so the count and
+    flags equal the oracle's, and h is within the bf16 bar."""
+    P, R, s0, cu = _problem(880, PIPE_LENGTHS, 300, "sigmoid")
+    Pb = P.to(torch.bfloat16)
+    case("packed one-kernel early stop")
+    gpu_lib.profile_reset()
+    gpu_lib.profile_enable(True)
+    _, h, st = gpu_lib.newton_forward(*_dev(Pb, R, s0), "sigmoid", 8, 1e-5, schedule="fused", cu_seqlens=cu)
+    n_solve = len(gpu_lib.profile_durations("newton_solve"))
+    gpu_lib.profile_enable(False)
+    torch.cuda.synchronize()
+    S_ref, st_ref = ref.newton(to_np(Pb), to_np(R), to_np(s0), "sigmoid", 8, tol=1e-5, cu_seqlens=cu)
+    assert n_solve == 2
+    assert st_ref.converged and st.converged and st.iters == st_ref.iters
+    assert h_rel_err(h, S_ref[..., 3, :]) < H_TOL_BF16
