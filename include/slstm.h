@@ -339,10 +339,15 @@ slstm_status slstm_input_projection_backward(const void* x, const void* W_x, con
  *   final_state  (S, 4, d_h): each sequence's last state (its state0 for an empty one).
  *   g_final      (S, 4, d_h): added at each sequence's last step (an empty sequence passes it
  *                to its dstate0).  dstate0 (S, 4, d_h).
- * Everything else is as in the entry point without the suffix, at B = 1. The packed forms run
- * the scan kernels: SLSTM_SCHEDULE_FUSED means SLSTM_SCHEDULE_FUSED_SCAN (size the workspace
- * with that schedule), SLSTM_SCHEDULE_LAYERED is accepted by the Newton solve and the warm
- * start, and SLSTM_SCHEDULE_FUSED_CHAIN is rejected.
+ * Everything else is as in the entry point without the suffix, at B = 1. Packed Newton solves
+ * under SLSTM_SCHEDULE_FUSED (max_iters <= 8; an early stop in two passes) run the one-kernel
+ * solve on tiles aligned to the sequence starts, each sequence's chain beside the others, when
+ * the tile table holds the pack (about T / 48 sequences or fewer) and ceil(d_h / 256) times S
+ * is at least 32; otherwise, and for the other packed calls, SLSTM_SCHEDULE_FUSED means
+ * SLSTM_SCHEDULE_FUSED_SCAN. Size the Newton workspace with SLSTM_SCHEDULE_FUSED, which covers
+ * both (B = 1). SLSTM_SCHEDULE_LAYERED is accepted by the Newton solve and the warm start, and
+ * SLSTM_SCHEDULE_FUSED_CHAIN is rejected. states may be NULL for a packed solve that runs the
+ * one-kernel form.
  */
 slstm_status slstm_newton_forward_varlen(const void* P, slstm_dtype P_dtype, const float* R,
                                          const float* state0, const int* cu_seqlens, int n_seqs,
