@@ -7,10 +7,12 @@ full-layer workload (B=128, T=2048, d_in=d_h=1024, bf16 x and W_x):
     block-bidiagonal solve, update], final residual, flags, h and final-state outputs) -> a
     T=1 sequential decode step at B=128 continuing from the final state (its own projection).
 For workloads whose solver input is P the step is the Newton forward alone. The Newton
-forward runs in the schedule the library picks for the shape (--schedule fused); the scan
-form of the fused iteration, the layered schedule, the backward pass, the same tokens packed
-as ragged sequences (cu_seqlens), head mixing (block-diagonal R, its own seeded input) and
-the sequential forward are timed after it as context.
+forward runs in the schedule the library picks for the shape (--schedule fused) and writes
+the layer's default output, h and the final state (--outputs states writes the state tensor
+too); the same step writing the states, the scan form of the fused iteration, the layered
+schedule, the backward pass, the same tokens packed as ragged sequences (cu_seqlens), head
+mixing (block-diagonal R, its own seeded input), the sigmoid/bf16 and long-context
+workloads and the sequential forward are timed after it as context.
 
 Prints ONE JSON line on stdout. Timing: W untimed warm-up steps, then exactly K steps
 between two device synchronisations, wall clock. Per-kernel durations come from HIP events
@@ -828,7 +830,8 @@ def main():
     if not args.no_packed_context:
         # the same B*T tokens as ragged sequences packed end to end in one row (cu_seqlens:
         # log-uniform lengths up to 8192 steps with empty and length-1 sequences mixed in), each
-        # from a zero state: the Newton solve in its scan form and the backward, not the metric
+        # from a zero state: the Newton solve (the one-kernel form on tiles aligned to the
+        # sequences, and the scan form) and the backward, not the metric
         from workloads import packed_offsets, random_cotangents_device
         cu_host = packed_offsets(w.seed, w.B * w.T, 8192)
         n_seq = len(cu_host) - 1
