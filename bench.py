@@ -572,10 +572,14 @@ def main():
     n_cus = torch.cuda.get_device_properties(dev).multi_processor_count
 
     def one_kernel_form(schedule):
-        """Whether the solve resolves to the one-kernel form, which needs no state tensor."""
-        if w.tol != 0.0 or w.max_iters > 4:
-            return False
-        return schedule == "fused_chain" or (schedule == "fused" and w.B * -(-w.d_h // 256) >= n_cus)
+        """Whether the solve resolves to the one-kernel form, which needs no state tensor: under
+        fused_chain a fixed count up to 4; under fused up to 8 iterations (an early stop in two
+        passes) on 32 or more lane groups of 256 features, or on every lane group once they
+        cover the CUs."""
+        lanes = w.B * -(-w.d_h // 256)
+        if schedule == "fused_chain":
+            return w.tol == 0.0 and w.max_iters <= 4
+        return schedule == "fused" and w.max_iters <= 8 and (lanes >= 32 or lanes >= n_cus)
 
     def timed_run(schedule, steps, warmup, states_out=None):
         if states_out is None:
