@@ -574,12 +574,11 @@ def main():
     def one_kernel_form(schedule):
         """Whether the solve resolves to the one-kernel form, which needs no state tensor: under
         fused_chain a fixed count up to 4; under fused up to 8 iterations (an early stop in two
-        passes) on 32 or more lane groups of 256 features, or on every lane group once they
-        cover the CUs."""
+        passes) on 32 or more lane groups of 256 features."""
         lanes = w.B * -(-w.d_h // 256)
         if schedule == "fused_chain":
             return w.tol == 0.0 and w.max_iters <= 4
-        return schedule == "fused" and w.max_iters <= 8 and (lanes >= 32 or lanes >= n_cus)
+        return schedule == "fused" and w.max_iters <= 8 and lanes >= 32
 
     def timed_run(schedule, steps, warmup, states_out=None):
         if states_out is None:
